@@ -1,0 +1,213 @@
+/*
+ * qtip_moe.h -- C ABI of the MI355X (gfx950) trellis-quantized MoE expert matmul.
+ *
+ * One MoE layer whose experts are gate/up/down matrices stored as 2-bit
+ * bitshift-trellis codes.  Pairs (token, expert) are routed and binned by
+ * expert into m-tiles; every woken expert's packed bytes are decoded inside the
+ * multiply, so dense weights never exist in memory.
+ *
+ * Sources (the pages this library implements):
+ *  - m-tile occupancy page, PR #167 "gate the trellis grouped GEMM on m-tile
+ *    occupancy, not token count": pair binning and the m-tile walk, the fill
+ *    formula, the dispatch predicate, the decode-regime floor and the arm pin
+ *    (sections "The cause is a threshold", "The fix", "Post-merge note").
+ *  - arch-specialise page, PR #99 "arch-specialise the trellis grouped GEMM
+ *    (D16) + close the silent-failure holes (D18)": packed 2-bit bytes decoded
+ *    in-kernel, contiguous-run decode, status on every launch, empty grid is an
+ *    error, unsupported arch is an error, one source of truth for the m-tile
+ *    height, an arch witness that never caches a non-answer and declines under
+ *    graph capture (sections "The two levers", "D18", "The arch witness").
+ *  - prefill page, PR #196: per-arm launch counters and the variant knob where
+ *    an unknown value warns and keeps the default ("Two things that were built,
+ *    correct, and switched off").
+ *
+ * Conventions.
+ *  - Every pointer is a DEVICE pointer unless the comment says "host".
+ *    All device buffers are owned by the caller; the library never allocates,
+ *    frees or synchronises inside qtip_moe_forward / qtip_moe_route /
+ *    qtip_expert_matmul.  Work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream) and completes asynchronously.
+ *  - Every call returns a qtip_status.  A call that returns QTIP_OK has
+ *    enqueued work that writes every element of its outputs; no call returns
+ *    QTIP_OK after a failed launch (launch status is read back with
+ *    hipGetLastError after each launch, mapped to QTIP_ERR_HIP, and the HIP
+ *    error text is available from qtip_last_error_detail()).
+ *  - bf16 and fp16 values are passed as their 16-bit patterns.
+ *
+ * Weight format (reading of the pages, which give only "packed 2-bit bytes"):
+ *  - A matrix with `rows` outputs and `cols` inputs is `rows` independent rows
+ *    of cols/4 bytes.  Symbol c of a row = bits [2(c%4), 2(c%4)+2) of byte c/4.
+ *  - The 16-bit state of weight (r, c) is the 8-symbol window starting at c,
+ *    read circularly within the row: state = sum_j sym((c+j) mod cols) * 4^j.
+ *  - weight(r, c) = bf16(lut[state]) * scale[r]: the fp16 LUT value is rounded
+ *    to bf16 (nearest-even), the dot product accumulates in fp32, and the fp16
+ *    per-output-row scale multiplies the fp32 sum.
+ *  - Layer: h = silu(x Wg^T) * (x Wu^T) rounded to bf16; y = h Wd^T;
+ *    out[t] = sum_{j<k} w[t,j] * y(t, j) in fp32 (j ascending), then cast.
+ *  - Routing: the k largest logits of a token in descending order (ties go to
+ *    the lower expert index); weights = softmax over those k logits (fp32).
+ *    Logits must be finite (not checked).
+ */
+#ifndef QTIP_MOE_H
+#define QTIP_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qtip_status {
+  QTIP_OK = 0,
+  QTIP_ERR_INVALID_ARG = 1,    /* a null pointer, a bad shape, a too-small workspace */
+  QTIP_ERR_INVALID_CONFIG = 2, /* an empty or oversized launch (n <= 0, n > max_tokens, ...) */
+  QTIP_ERR_NOT_SUPPORTED = 3,  /* device is not gfx950, or its code object is not in the library */
+  QTIP_ERR_HIP = 4,            /* a HIP runtime or launch error; see qtip_last_error_detail() */
+  QTIP_ERR_CAPTURING = 5       /* the arch witness cannot be taken on a capturing stream */
+} qtip_status;
+
+enum { QTIP_ARM_AUTO = 0, QTIP_ARM_GEMV = 1, QTIP_ARM_GROUPED = 2 };
+enum { QTIP_OUT_BF16 = 0, QTIP_OUT_F32 = 1 };
+
+/* Decode-regime floor: n <= 8 tokens always take the GEMV arm (m-tile page, "The fix"). */
+#define QTIP_DECODE_REGIME_MAX_TOKENS 8
+/* Default m-tile height: the M of one bf16 MFMA (v_mfma_f32_16x16x32_bf16). */
+#define QTIP_DEFAULT_TILE_M 16
+/* One decode of an expert's weights is shared by up to this many binned pairs. */
+#define QTIP_UNIT_MAX_PAIRS 64
+/* Inputs per K block: H and I must be multiples of this; rows a multiple of 16. */
+#define QTIP_K_BLOCK 128
+
+typedef struct qtip_moe_desc {
+  int32_t num_experts;  /* E >= 1 (<= 1024) */
+  int32_t top_k;        /* k, 1 <= k <= E (<= 32) */
+  int32_t hidden;       /* H: gate/up inputs and down outputs; multiple of 128 */
+  int32_t inter;        /* I: gate/up outputs and down inputs; multiple of 128 */
+  int32_t max_tokens;   /* largest n a forward accepts (sizes the workspace), >= 1 */
+  int32_t arm_override; /* QTIP_ARM_AUTO (predicate), _GEMV or _GROUPED (pins the arm) */
+  int32_t variant;      /* kernel variant; 0 = default.  Unknown: warning, default kept */
+  int32_t out_dtype;    /* QTIP_OUT_BF16 or QTIP_OUT_F32 */
+  int32_t tile_m;       /* 0 = default (16); else 16, 32 or 64 */
+} qtip_moe_desc;
+
+typedef struct qtip_moe_plan_s* qtip_moe_plan_t;
+
+typedef struct qtip_moe_weights {
+  const uint8_t* codes_gate;  /* [E][I][H/4] packed 2-bit codes */
+  const uint8_t* codes_up;    /* [E][I][H/4] */
+  const uint8_t* codes_down;  /* [E][H][I/4] */
+  const uint16_t* scale_gate; /* [E][I] fp16, one per output row */
+  const uint16_t* scale_up;   /* [E][I] fp16 */
+  const uint16_t* scale_down; /* [E][H] fp16 */
+  const uint16_t* lut;        /* [65536] fp16, finite values */
+} qtip_moe_weights;
+
+typedef struct qtip_moe_stats {
+  uint64_t forward_calls;     /* successful qtip_moe_forward calls */
+  uint64_t gemv_launches;     /* expert-matrix kernel launches on the GEMV arm */
+  uint64_t grouped_launches;  /* expert-matrix kernel launches on the grouped arm */
+  uint64_t route_launches;    /* routing / binning kernel launches */
+  uint64_t combine_launches;  /* combine kernel launches */
+  int32_t last_arm;           /* arm taken by the last forward (QTIP_ARM_GEMV / _GROUPED) */
+  int32_t last_n_tokens;      /* n of the last forward */
+} qtip_moe_stats;
+
+/* ---- plan -------------------------------------------------------------------------
+ * qtip_moe_plan: validate `desc` (host) for `device`, fix the m-tile height and the
+ * workspace size, and return a plan (host memory only; launches nothing, so it is safe
+ * inside graph capture).  Checks: 1 <= k <= E <= 1024, k <= 32, H and I multiples of
+ * 128, max_tokens >= 1, a known arm/out_dtype, tile_m in {0,16,32,64}, and the device
+ * arch reported by HIP is gfx950 (else QTIP_ERR_NOT_SUPPORTED).  Free with
+ * qtip_moe_plan_destroy.  Not thread-safe per plan object (counters). */
+qtip_status qtip_moe_plan(const qtip_moe_desc* desc /*host*/, int device, qtip_moe_plan_t* out /*host*/);
+
+/* Same as qtip_moe_plan for an explicit arch name (e.g. "gfx950:sramecc+:xnack-"),
+ * without querying a device: lets host-only callers validate a configuration. */
+qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc /*host*/, const char* gcn_arch_name /*host*/,
+                                   qtip_moe_plan_t* out /*host*/);
+
+qtip_status qtip_moe_plan_destroy(qtip_moe_plan_t plan);
+
+/* What the kernels will use: the m-tile height, the workspace bytes a forward needs at
+ * max_tokens, and the smallest n for which the predicate selects the grouped arm.  Any
+ * output pointer may be NULL. */
+qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m /*host*/, size_t* workspace_bytes /*host*/,
+                               int32_t* min_tokens_grouped /*host*/);
+
+/* The arm a forward of n tokens takes: the override if one is set, else the closed-form
+ * predicate.  Returns QTIP_ARM_GEMV or QTIP_ARM_GROUPED, or -1 for a bad plan/n. */
+int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens);
+
+/* ---- closed-form fill model (m-tile page, "The cause is a threshold" and "The fix") --
+ * Uniform routing of n tokens to k of E experts wakes E(1-(1-k/E)^n) experts on average;
+ * pairs per woken expert = n k / that.  The grouped arm is selected iff n > 8 and pairs
+ * per woken expert >= tile_m.  Pure host functions of their arguments. */
+double qtip_fill_woken_experts(int32_t n, int32_t k, int32_t E);
+double qtip_fill_pairs_per_woken_expert(int32_t n, int32_t k, int32_t E);
+int32_t qtip_fill_select_grouped(int32_t n, int32_t k, int32_t E, int32_t tile_m); /* 1 / 0, -1 bad args */
+int32_t qtip_fill_min_tokens(int32_t k, int32_t E, int32_t tile_m);                /* smallest n selected */
+
+/* ---- forward ----------------------------------------------------------------------
+ * One MoE layer for n tokens: route, bin, gate+up (SwiGLU), down, combine.
+ *   x        [n][H] bf16 activations;   logits [n][E] fp32 router logits
+ *   out      [n][H] bf16 or fp32 (plan's out_dtype); every element is written
+ *   workspace >= qtip_moe_plan_info(...).workspace_bytes bytes, 256-byte aligned,
+ *            contents need no initialisation; must not overlap inputs or out.
+ * Errors: NULL plan/weights/x/logits/out/workspace -> INVALID_ARG; n <= 0 or
+ * n > max_tokens -> INVALID_CONFIG (an empty launch is an error, not a no-op);
+ * workspace too small or misaligned -> INVALID_ARG; device not gfx950 or witness
+ * failed -> NOT_SUPPORTED; first call on a device while `stream` is capturing ->
+ * CAPTURING; launch failure -> HIP.  Bumps the per-arm launch counters. */
+qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w /*host struct of device ptrs*/,
+                             const void* x_bf16, const float* logits, int32_t n_tokens, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- routing and binning alone (bit-exact testing of the routing launcher) ----------
+ *   topk_idx [n][k] int32, topk_w [n][k] fp32, counts [E], offsets [E+1] (exclusive
+ *   scan, offsets[E] = n k), sorted_pair [n k] (pair ids p = t k + j grouped by expert,
+ *   ascending p inside each expert), tile_map [n k][3] int32 (expert, start, len) tiles
+ *   in ascending expert order, len <= tile_m; n_tiles [1] = sum_e ceil(count_e/tile_m).
+ *   Rows of tile_map past n_tiles are left unwritten.  Errors as qtip_moe_forward. */
+qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_tokens, int32_t* topk_idx,
+                           float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                           int32_t* tile_map, int32_t* n_tiles, void* stream);
+
+/* ---- one trellis matrix times binned activation rows ------------------------------
+ * For each unit u < n_units of unit_map [n_units][3] = (expert e, start s, len L):
+ *   y[s+i][r] = scale[e][r] * sum_c a[s+i][c] * bf16(lut[state_e(r, c)])   (i < L, r < rows)
+ *   codes [E][rows][cols/4], scales [E][rows] fp16, lut [65536] fp16,
+ *   a [n_rows_a][cols] bf16, y [n_rows_a][rows] fp32.
+ * `arm` is QTIP_ARM_GEMV or QTIP_ARM_GROUPED.  Constraints: rows % 16 == 0, cols % 128
+ * == 0, 1 <= L <= 64, 0 <= e < num_experts, 0 <= s, s + L <= n_rows_a.  A unit that
+ * violates them on the device is skipped (its rows of y are not written), so device-side
+ * garbage cannot cause out-of-bounds access.  Rows of y no unit covers are not written.
+ * n_units == 0 is INVALID_CONFIG. */
+qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t* codes, const uint16_t* scales,
+                               const uint16_t* lut, int32_t num_experts, int32_t rows, int32_t cols,
+                               const void* a_bf16, int32_t n_rows_a, const int32_t* unit_map, int32_t n_units,
+                               float* y, void* stream);
+
+/* ---- observability ----------------------------------------------------------------- */
+qtip_status qtip_moe_stats_get(qtip_moe_plan_t plan, qtip_moe_stats* out /*host*/);
+qtip_status qtip_moe_stats_reset(qtip_moe_plan_t plan);
+
+/* One line naming the arm the plan takes for n tokens, the mean m-tile fill, pairs per
+ * woken expert and the boundary n (the engagement line of the m-tile page,
+ * "Re-measurement on this branch").  Writes at most buf_len bytes including the NUL. */
+qtip_status qtip_moe_engaged_line(qtip_moe_plan_t plan, int32_t n_tokens, char* buf /*host*/, size_t buf_len);
+
+/* Take (once per device, cached only on success) the arch witness: a one-thread kernel
+ * from this library's gfx950 code object writes a known value that is read back.  Fails
+ * with CAPTURING if `stream` is capturing, NOT_SUPPORTED if the value is wrong or the
+ * kernel cannot run.  qtip_moe_forward / _route / qtip_expert_matmul call it on first use. */
+qtip_status qtip_arch_witness(int device, void* stream);
+
+const char* qtip_status_string(qtip_status s);
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* qtip_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QTIP_MOE_H */

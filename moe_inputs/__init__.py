@@ -128,6 +128,12 @@ def make_workload(name: str, seed: int = 0, n_tokens: Optional[int] = None) -> M
     return make_inputs(WORKLOADS[name], seed=seed, n_tokens=n_tokens)
 
 
+def draw_logits(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    """Router logits alone (own stream), for routing-only tests at the workload's sizes."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0x10617]))
+    return _draw_logits(rng, shape)
+
+
 def redraw_tokens(inp: MoEInputs, n_tokens: int, seed: int) -> MoEInputs:
     """Keep the weights, draw a fresh batch of n_tokens activations and logits."""
     s = dataclasses.replace(inp.shape, n_tokens=n_tokens)

@@ -1,0 +1,127 @@
+"""CPU-side checks of the HIP library: it loads, exports every declared entry point, and its
+host logic (plan validation, the closed-form predicate, argument errors) behaves as documented.
+No test here launches GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import trellis_quantized_moe_expert_amd as q
+from oracle import fill
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+V4 = dict(num_experts=256, top_k=6, hidden=4096, inter=2048, max_tokens=1024)
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "qtip_moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qtip_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 17
+    lib = q.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_plan_for_arch_accepts_gfx950_and_reports_schedule():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950:sramecc+:xnack-")
+    info = q.qtip_moe_plan_info(plan)
+    assert info["tile_m"] == 16
+    assert info["min_tokens_grouped"] == 683
+    assert info["workspace_bytes"] > 1024 * 6 * (4096 * 4 + 2048 * 2)
+    assert q.qtip_moe_select_arm(plan, 682) == q.QTIP_ARM_GEMV
+    assert q.qtip_moe_select_arm(plan, 683) == q.QTIP_ARM_GROUPED
+    assert q.qtip_moe_select_arm(plan, 8) == q.QTIP_ARM_GEMV
+    line = q.qtip_moe_engaged_line(plan, 1572)
+    assert "grouped" in line and "230.3%" in line and "36.84" in line and "683" in line
+    q.qtip_moe_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("tile_m,expect", [(32, 1366), (64, 2731)])
+def test_tile_m_is_one_source_for_the_predicate(tile_m, expect):
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, tile_m=tile_m), "gfx950")
+    assert q.qtip_moe_plan_info(plan)["tile_m"] == tile_m
+    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == expect == fill.min_tokens_grouped(6, 256, tile_m)
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_override_pins_the_arm():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_GROUPED), "gfx950")
+    assert q.qtip_moe_select_arm(plan, 1) == q.QTIP_ARM_GROUPED
+    assert "pinned" in q.qtip_moe_engaged_line(plan, 1)
+    q.qtip_moe_plan_destroy(plan)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_GEMV), "gfx950")
+    assert q.qtip_moe_select_arm(plan, 5000) == q.QTIP_ARM_GEMV
+    q.qtip_moe_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("arch", ["gfx942", "gfx90a", "gfx9500", "sm_90", ""])
+def test_unsupported_arch_is_refused(arch):
+    with pytest.raises(q.QtipError) as ei:
+        q.qtip_moe_plan_for_arch(q.make_desc(**V4), arch)
+    assert ei.value.status == q.QTIP_ERR_NOT_SUPPORTED
+
+
+@pytest.mark.parametrize("bad", [dict(num_experts=0), dict(top_k=0), dict(top_k=300), dict(hidden=4000),
+                                 dict(inter=64), dict(max_tokens=0), dict(arm_override=7), dict(out_dtype=3),
+                                 dict(tile_m=8), dict(num_experts=2048, top_k=6), dict(top_k=33)])
+def test_invalid_desc_is_refused(bad):
+    with pytest.raises(q.QtipError) as ei:
+        q.qtip_moe_plan_for_arch(q.make_desc(**{**V4, **bad}), "gfx950")
+    assert ei.value.status == q.QTIP_ERR_INVALID_ARG
+
+
+def test_unknown_variant_warns_and_keeps_default(capfd):
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, variant=9), "gfx950")
+    assert "unknown kernel variant 9" in capfd.readouterr().err
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_fill_functions_match_the_pages_and_the_oracle():
+    assert f"{q.qtip_fill_woken_experts(32, 6, 256):.1f}" == "136.1"
+    assert f"{q.qtip_fill_pairs_per_woken_expert(128, 6, 256):.2f}" == "3.15"
+    assert f"{q.qtip_fill_pairs_per_woken_expert(683, 6, 256):.2f}" == "16.01"
+    assert q.qtip_fill_min_tokens(6, 256, 16) == 683
+    for n in (1, 8, 9, 32, 512, 682, 683, 1024, 1572, 2000):
+        assert q.qtip_fill_select_grouped(n, 6, 256, 16) == int(fill.select_grouped(n, 6, 256, 16))
+        assert q.qtip_fill_pairs_per_woken_expert(n, 6, 256) == pytest.approx(fill.pairs_per_woken_expert(n, 6, 256), rel=1e-12)
+    for k, E in [(1, 4), (2, 8), (6, 64), (8, 256), (6, 8), (1, 1024)]:
+        for tm in (16, 32, 64):
+            assert q.qtip_fill_min_tokens(k, E, tm) == fill.min_tokens_grouped(k, E, tm)
+    assert q.qtip_fill_select_grouped(0, 6, 256, 16) == -1
+    assert q.qtip_fill_min_tokens(7, 6, 16) == -1
+
+
+def test_forward_argument_errors_return_before_any_launch():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    ws = q.qtip_moe_plan_info(plan)["workspace_bytes"]
+    w = q.qtip_moe_weights(256, 256, 256, 256, 256, 256, 256)
+    lib = q.lib()
+    fwd = lambda wp, x, lg, n, out, wsp, wsb: lib.qtip_moe_forward(plan, wp, x, lg, n, out, wsp, wsb, None)
+    W = ctypes.byref(w)
+    assert fwd(W, 256, 256, 0, 256, 256, ws) == q.QTIP_ERR_INVALID_CONFIG          # empty launch
+    assert fwd(W, 256, 256, -3, 256, 256, ws) == q.QTIP_ERR_INVALID_CONFIG
+    assert fwd(W, 256, 256, 1025, 256, 256, ws) == q.QTIP_ERR_INVALID_CONFIG       # above max_tokens
+    assert fwd(W, None, 256, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG
+    assert fwd(None, 256, 256, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG
+    assert fwd(W, 256, 256, 4, 256, 256, ws - 1) == q.QTIP_ERR_INVALID_ARG         # workspace too small
+    assert fwd(W, 256, 256, 4, 256, 384, ws) == q.QTIP_ERR_INVALID_ARG             # misaligned workspace
+    assert fwd(W, 264, 256, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG             # misaligned x
+    w.lut = None
+    assert fwd(W, 256, 256, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG
+    assert "NULL weight" in q.last_error_detail()
+    assert lib.qtip_expert_matmul(plan, 1, 256, 256, 256, 4, 32, 256, 256, 8, 256, 0, 256, None) == q.QTIP_ERR_INVALID_CONFIG
+    assert lib.qtip_expert_matmul(plan, 5, 256, 256, 256, 4, 32, 256, 256, 8, 256, 1, 256, None) == q.QTIP_ERR_INVALID_ARG
+    assert lib.qtip_expert_matmul(plan, 1, 256, 256, 256, 4, 30, 256, 256, 8, 256, 1, 256, None) == q.QTIP_ERR_INVALID_ARG
+    assert lib.qtip_moe_route(plan, 256, 0, 256, 256, 256, 256, 256, 256, 256, None) == q.QTIP_ERR_INVALID_CONFIG
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_status_strings():
+    assert q.status_name(0) == "QTIP_OK"
+    assert q.status_name(5) == "QTIP_ERR_CAPTURING"

@@ -1,0 +1,229 @@
+"""ctypes binding of the C ABI in include/qtip_moe.h (argument marshalling only).
+
+Every function keeps its C name.  Pointer arguments accept an int address, None (NULL)
+or any object with a `data_ptr()` method (a torch tensor); device memory and streams
+come from PyTorch, all computation happens in the HIP library.  The binding never
+falls back to anything else: if the library is missing, `lib()` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libqtip_moe.so"
+LIB_PATH = os.path.join(_HERE, LIB_NAME)
+
+QTIP_OK = 0
+QTIP_ERR_INVALID_ARG = 1
+QTIP_ERR_INVALID_CONFIG = 2
+QTIP_ERR_NOT_SUPPORTED = 3
+QTIP_ERR_HIP = 4
+QTIP_ERR_CAPTURING = 5
+
+QTIP_ARM_AUTO = 0
+QTIP_ARM_GEMV = 1
+QTIP_ARM_GROUPED = 2
+QTIP_OUT_BF16 = 0
+QTIP_OUT_F32 = 1
+
+
+class qtip_moe_desc(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("arm_override", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32)]
+
+
+class qtip_moe_weights(ctypes.Structure):
+    _fields_ = [("codes_gate", ctypes.c_void_p), ("codes_up", ctypes.c_void_p), ("codes_down", ctypes.c_void_p),
+                ("scale_gate", ctypes.c_void_p), ("scale_up", ctypes.c_void_p), ("scale_down", ctypes.c_void_p),
+                ("lut", ctypes.c_void_p)]
+
+
+class qtip_moe_stats(ctypes.Structure):
+    _fields_ = [("forward_calls", ctypes.c_uint64), ("gemv_launches", ctypes.c_uint64),
+                ("grouped_launches", ctypes.c_uint64), ("route_launches", ctypes.c_uint64),
+                ("combine_launches", ctypes.c_uint64), ("last_arm", ctypes.c_int32),
+                ("last_n_tokens", ctypes.c_int32)]
+
+
+class QtipError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{fn} -> {status_name(status)}: {detail}")
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGS = {
+    "qtip_moe_plan": (_I32, [ctypes.POINTER(qtip_moe_desc), ctypes.c_int, ctypes.POINTER(_P)]),
+    "qtip_moe_plan_for_arch": (_I32, [ctypes.POINTER(qtip_moe_desc), ctypes.c_char_p, ctypes.POINTER(_P)]),
+    "qtip_moe_plan_destroy": (_I32, [_P]),
+    "qtip_moe_plan_info": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_I32)]),
+    "qtip_moe_select_arm": (_I32, [_P, _I32]),
+    "qtip_fill_woken_experts": (ctypes.c_double, [_I32, _I32, _I32]),
+    "qtip_fill_pairs_per_woken_expert": (ctypes.c_double, [_I32, _I32, _I32]),
+    "qtip_fill_select_grouped": (_I32, [_I32, _I32, _I32, _I32]),
+    "qtip_fill_min_tokens": (_I32, [_I32, _I32, _I32]),
+    "qtip_moe_forward": (_I32, [_P, ctypes.POINTER(qtip_moe_weights), _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+    "qtip_moe_route": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "qtip_expert_matmul": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _P]),
+    "qtip_moe_stats_get": (_I32, [_P, ctypes.POINTER(qtip_moe_stats)]),
+    "qtip_moe_stats_reset": (_I32, [_P]),
+    "qtip_moe_engaged_line": (_I32, [_P, _I32, ctypes.c_char_p, ctypes.c_size_t]),
+    "qtip_arch_witness": (_I32, [ctypes.c_int, _P]),
+    "qtip_status_string": (ctypes.c_char_p, [_I32]),
+    "qtip_last_error_detail": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it first (python -m "
+                              f"trellis_quantized_moe_expert_amd.build or __graft_entry__.build())")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return lib().qtip_status_string(status).decode()
+
+
+def last_error_detail() -> str:
+    return lib().qtip_last_error_detail().decode()
+
+
+def _ptr(obj):
+    if obj is None:
+        return None
+    if hasattr(obj, "data_ptr"):
+        return obj.data_ptr()
+    return int(obj)
+
+
+def _stream(stream):
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return torch.cuda.current_stream().cuda_stream
+        except ImportError:
+            pass
+        return None
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(fn: str, status: int):
+    if status != QTIP_OK:
+        raise QtipError(fn, status, last_error_detail())
+
+
+def make_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override=QTIP_ARM_AUTO, variant=0,
+              out_dtype=QTIP_OUT_F32, tile_m=0) -> qtip_moe_desc:
+    return qtip_moe_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override, variant, out_dtype, tile_m)
+
+
+def make_weights(codes_gate, codes_up, codes_down, scale_gate, scale_up, scale_down, lut) -> qtip_moe_weights:
+    return qtip_moe_weights(*(_ptr(a) for a in (codes_gate, codes_up, codes_down, scale_gate, scale_up,
+                                                scale_down, lut)))
+
+
+# ---- the C entry points, same names --------------------------------------------------------
+def qtip_moe_plan(desc: qtip_moe_desc, device: int = 0) -> int:
+    out = _P()
+    _check("qtip_moe_plan", lib().qtip_moe_plan(ctypes.byref(desc), device, ctypes.byref(out)))
+    return out.value
+
+
+def qtip_moe_plan_for_arch(desc: qtip_moe_desc, arch: str) -> int:
+    out = _P()
+    _check("qtip_moe_plan_for_arch", lib().qtip_moe_plan_for_arch(ctypes.byref(desc), arch.encode(), ctypes.byref(out)))
+    return out.value
+
+
+def qtip_moe_plan_destroy(plan: int) -> None:
+    _check("qtip_moe_plan_destroy", lib().qtip_moe_plan_destroy(plan))
+
+
+def qtip_moe_plan_info(plan: int) -> dict:
+    tm, mt, ws = _I32(), _I32(), ctypes.c_size_t()
+    _check("qtip_moe_plan_info", lib().qtip_moe_plan_info(plan, ctypes.byref(tm), ctypes.byref(ws), ctypes.byref(mt)))
+    return {"tile_m": tm.value, "workspace_bytes": ws.value, "min_tokens_grouped": mt.value}
+
+
+def qtip_moe_select_arm(plan: int, n_tokens: int) -> int:
+    return lib().qtip_moe_select_arm(plan, n_tokens)
+
+
+def qtip_fill_woken_experts(n, k, E) -> float:
+    return lib().qtip_fill_woken_experts(n, k, E)
+
+
+def qtip_fill_pairs_per_woken_expert(n, k, E) -> float:
+    return lib().qtip_fill_pairs_per_woken_expert(n, k, E)
+
+
+def qtip_fill_select_grouped(n, k, E, tile_m) -> int:
+    return lib().qtip_fill_select_grouped(n, k, E, tile_m)
+
+
+def qtip_fill_min_tokens(k, E, tile_m) -> int:
+    return lib().qtip_fill_min_tokens(k, E, tile_m)
+
+
+def qtip_moe_forward(plan, weights: qtip_moe_weights, x_bf16, logits, n_tokens, out, workspace, workspace_bytes,
+                     stream=None) -> None:
+    _check("qtip_moe_forward", lib().qtip_moe_forward(plan, ctypes.byref(weights), _ptr(x_bf16), _ptr(logits),
+                                                      n_tokens, _ptr(out), _ptr(workspace), workspace_bytes,
+                                                      _stream(stream)))
+
+
+def qtip_moe_route(plan, logits, n_tokens, topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles,
+                   stream=None) -> None:
+    _check("qtip_moe_route", lib().qtip_moe_route(plan, _ptr(logits), n_tokens, _ptr(topk_idx), _ptr(topk_w),
+                                                  _ptr(counts), _ptr(offsets), _ptr(sorted_pair), _ptr(tile_map),
+                                                  _ptr(n_tiles), _stream(stream)))
+
+
+def qtip_expert_matmul(plan, arm, codes, scales, lut, num_experts, rows, cols, a_bf16, n_rows_a, unit_map, n_units,
+                       y, stream=None) -> None:
+    _check("qtip_expert_matmul", lib().qtip_expert_matmul(plan, arm, _ptr(codes), _ptr(scales), _ptr(lut),
+                                                          num_experts, rows, cols, _ptr(a_bf16), n_rows_a,
+                                                          _ptr(unit_map), n_units, _ptr(y), _stream(stream)))
+
+
+def qtip_moe_stats_get(plan) -> dict:
+    s = qtip_moe_stats()
+    _check("qtip_moe_stats_get", lib().qtip_moe_stats_get(plan, ctypes.byref(s)))
+    return {name: getattr(s, name) for name, _ in qtip_moe_stats._fields_}
+
+
+def qtip_moe_stats_reset(plan) -> None:
+    _check("qtip_moe_stats_reset", lib().qtip_moe_stats_reset(plan))
+
+
+def qtip_moe_engaged_line(plan, n_tokens) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check("qtip_moe_engaged_line", lib().qtip_moe_engaged_line(plan, n_tokens, buf, len(buf)))
+    return buf.value.decode()
+
+
+def qtip_arch_witness(device: int = 0, stream=None) -> None:
+    _check("qtip_arch_witness", lib().qtip_arch_witness(device, _stream(stream)))
+
+
+def raw_status(fn_name: str, *args) -> int:
+    """Call a C entry point with raw arguments and return its status (for error-path tests)."""
+    return getattr(lib(), fn_name)(*args)

@@ -1,0 +1,465 @@
+// C ABI of the trellis MoE expert path: plans, dispatch, status mapping, witness, counters.
+//
+// Interface rules follow the arch-specialise page (PR #99, section "D18 -- this path had
+// no launch-status check anywhere" and "The arch witness"): every launch's status is read
+// back and mapped to an error, an empty grid is an error rather than a silent no-op, an
+// unsupported device is refused instead of running compiled-out code, the m-tile height
+// comes from one place (the plan) for the router, the kernels and the predicate, and the
+// witness declines under graph capture and caches only a successful answer.  The variant
+// knob follows the prefill page (PR #196): an unknown value warns and keeps the default.
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/qtip_moe.h"
+#include "fill_predicate.h"
+#include "qtip_internal.h"
+
+using namespace qtip;
+
+struct qtip_moe_plan_s {
+  qtip_moe_desc d;
+  int32_t tile_m;
+  int32_t device;  // -1: created from an arch name; the current device is used at call time
+  int32_t min_tokens_grouped;
+  size_t ws_bytes;
+  qtip_moe_stats stats;
+};
+
+namespace {
+
+thread_local std::string g_detail;
+
+qtip_status fail(qtip_status s, const std::string& what) {
+  g_detail = what;
+  return s;
+}
+
+qtip_status hip_fail(hipError_t e, const char* where) {
+  g_detail = std::string(where) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+  return QTIP_ERR_HIP;
+}
+
+bool arch_is_supported(const char* name) { return name != nullptr && std::strncmp(name, "gfx950", 6) == 0 &&
+                                                  (name[6] == '\0' || name[6] == ':'); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, h, y, total;
+};
+
+WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens) {
+  const size_t P = (size_t)n_tokens * d.top_k;
+  const size_t woken_max = P < (size_t)d.num_experts ? P : (size_t)d.num_experts;
+  const size_t max_tiles = P / tile_m + woken_max + 1;
+  const size_t max_units = P / kUnitMaxPairs + woken_max + 1;
+  WsLayout L{};
+  size_t o = 0;
+  L.topk_idx = o;     o = align256(o + P * 4);
+  L.topk_w = o;       o = align256(o + P * 4);
+  L.counts = o;       o = align256(o + (size_t)d.num_experts * 4);
+  L.offsets = o;      o = align256(o + ((size_t)d.num_experts + 1) * 4);
+  L.sorted_pair = o;  o = align256(o + P * 4);
+  L.tile_map = o;     o = align256(o + max_tiles * 12);
+  L.n_tiles = o;      o = align256(o + 4);
+  L.unit_map = o;     o = align256(o + max_units * 12);
+  L.n_units = o;      o = align256(o + 4);
+  L.h = o;            o = align256(o + P * (size_t)d.inter * 2);
+  L.y = o;            o = align256(o + P * (size_t)d.hidden * 4);
+  L.total = o;
+  return L;
+}
+
+size_t max_units_for(const qtip_moe_desc& d, int32_t n_tokens) {
+  const size_t P = (size_t)n_tokens * d.top_k;
+  const size_t woken_max = P < (size_t)d.num_experts ? P : (size_t)d.num_experts;
+  return P / kUnitMaxPairs + woken_max;
+}
+
+// --- per-device state: CU count and the witness ---------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_witness_ok[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
+std::mutex g_witness_mutex;
+
+qtip_status current_device(int* dev) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (*dev < 0 || *dev >= kMaxDevices) return fail(QTIP_ERR_NOT_SUPPORTED, "device index out of range");
+  return QTIP_OK;
+}
+
+qtip_status witness_on(int dev, hipStream_t stream) {
+  if (g_witness_ok[dev].load(std::memory_order_acquire)) return QTIP_OK;
+  std::lock_guard<std::mutex> lock(g_witness_mutex);
+  if (g_witness_ok[dev].load(std::memory_order_acquire)) return QTIP_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(QTIP_ERR_CAPTURING, "arch witness not taken yet and the stream is capturing; call "
+                                    "qtip_arch_witness outside capture first");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (!arch_is_supported(prop.gcnArchName))
+    return fail(QTIP_ERR_NOT_SUPPORTED, std::string("device arch ") + prop.gcnArchName + " is not gfx950");
+  int32_t* buf = nullptr;
+  e = hipMalloc(&buf, sizeof(int32_t));
+  if (e != hipSuccess) return hip_fail(e, "witness hipMalloc");
+  int32_t host = 0;
+  e = launch_witness(buf, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(&host, buf, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  (void)hipFree(buf);
+  if (e != hipSuccess) {
+    g_detail = std::string("arch witness could not run: ") + hipGetErrorName(e);
+    return QTIP_ERR_NOT_SUPPORTED;
+  }
+  if (host != kWitnessValue) return fail(QTIP_ERR_NOT_SUPPORTED, "arch witness returned a wrong value");
+  g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_release);
+  g_witness_ok[dev].store(1, std::memory_order_release);
+  return QTIP_OK;
+}
+
+qtip_status ensure_device(qtip_moe_plan_t plan, hipStream_t stream, int* dev_out) {
+  int dev = 0;
+  qtip_status s = current_device(&dev);
+  if (s != QTIP_OK) return s;
+  if (plan->device >= 0 && plan->device != dev)
+    return fail(QTIP_ERR_INVALID_ARG, "current device differs from the plan's device");
+  s = witness_on(dev, stream);
+  if (s != QTIP_OK) return s;
+  *dev_out = dev;
+  return QTIP_OK;
+}
+
+int persistent_grid(int dev, size_t max_tasks) {
+  const size_t cus = (size_t)g_cu_count[dev].load(std::memory_order_acquire);
+  size_t need = (max_tasks + kExpertWaves - 1) / kExpertWaves;
+  if (need < 1) need = 1;
+  return (int)(need < cus ? need : cus);
+}
+
+qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
+  if (!d) return fail(QTIP_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_experts < 1 || d->num_experts > kMaxExperts)
+    return fail(QTIP_ERR_INVALID_ARG, "num_experts must be in [1, 1024]");
+  if (d->top_k < 1 || d->top_k > d->num_experts || d->top_k > kMaxTopK)
+    return fail(QTIP_ERR_INVALID_ARG, "top_k must be in [1, min(num_experts, 32)]");
+  if (d->hidden < kKBlock || d->hidden % kKBlock) return fail(QTIP_ERR_INVALID_ARG, "hidden must be a positive multiple of 128");
+  if (d->inter < kKBlock || d->inter % kKBlock) return fail(QTIP_ERR_INVALID_ARG, "inter must be a positive multiple of 128");
+  if (d->max_tokens < 1) return fail(QTIP_ERR_INVALID_ARG, "max_tokens must be >= 1");
+  if ((int64_t)d->max_tokens * d->top_k > (1 << 24)) return fail(QTIP_ERR_INVALID_ARG, "max_tokens * top_k exceeds 2^24");
+  if (d->arm_override != QTIP_ARM_AUTO && d->arm_override != QTIP_ARM_GEMV && d->arm_override != QTIP_ARM_GROUPED)
+    return fail(QTIP_ERR_INVALID_ARG, "unknown arm_override");
+  if (d->out_dtype != QTIP_OUT_BF16 && d->out_dtype != QTIP_OUT_F32) return fail(QTIP_ERR_INVALID_ARG, "unknown out_dtype");
+  const int32_t tm = d->tile_m == 0 ? QTIP_DEFAULT_TILE_M : d->tile_m;
+  if (tm != 16 && tm != 32 && tm != 64) return fail(QTIP_ERR_INVALID_ARG, "tile_m must be 0, 16, 32 or 64");
+  *tile_m = tm;
+  return QTIP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qtip_status_string(qtip_status s) {
+  switch (s) {
+    case QTIP_OK: return "QTIP_OK";
+    case QTIP_ERR_INVALID_ARG: return "QTIP_ERR_INVALID_ARG";
+    case QTIP_ERR_INVALID_CONFIG: return "QTIP_ERR_INVALID_CONFIG";
+    case QTIP_ERR_NOT_SUPPORTED: return "QTIP_ERR_NOT_SUPPORTED";
+    case QTIP_ERR_HIP: return "QTIP_ERR_HIP";
+    case QTIP_ERR_CAPTURING: return "QTIP_ERR_CAPTURING";
+  }
+  return "QTIP_ERR_UNKNOWN";
+}
+
+const char* qtip_last_error_detail(void) { return g_detail.c_str(); }
+
+double qtip_fill_woken_experts(int32_t n, int32_t k, int32_t E) {
+  if (!fill_args_ok(n, k, E, 1)) return -1.0;
+  return fill_woken_experts(n, k, E);
+}
+
+double qtip_fill_pairs_per_woken_expert(int32_t n, int32_t k, int32_t E) {
+  if (!fill_args_ok(n, k, E, 1)) return -1.0;
+  return fill_pairs_per_woken_expert(n, k, E);
+}
+
+int32_t qtip_fill_select_grouped(int32_t n, int32_t k, int32_t E, int32_t tile_m) {
+  if (!fill_args_ok(n, k, E, tile_m)) return -1;
+  return fill_select_grouped(n, k, E, tile_m) ? 1 : 0;
+}
+
+int32_t qtip_fill_min_tokens(int32_t k, int32_t E, int32_t tile_m) {
+  if (!fill_args_ok(1, k, E, tile_m)) return -1;
+  return fill_min_tokens(k, E, tile_m);
+}
+
+qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc, const char* gcn_arch_name, qtip_moe_plan_t* out) {
+  g_detail.clear();
+  if (!out) return fail(QTIP_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int32_t tm = 0;
+  qtip_status s = validate_desc(desc, &tm);
+  if (s != QTIP_OK) return s;
+  if (!arch_is_supported(gcn_arch_name))
+    return fail(QTIP_ERR_NOT_SUPPORTED, std::string("arch '") + (gcn_arch_name ? gcn_arch_name : "(null)") +
+                                            "' is not supported; this library carries gfx950 code only");
+  if (desc->variant != 0)
+    std::fprintf(stderr, "qtip_moe: unknown kernel variant %d; keeping the default (0)\n", desc->variant);
+  auto* p = new (std::nothrow) qtip_moe_plan_s{};
+  if (!p) return fail(QTIP_ERR_INVALID_ARG, "out of host memory");
+  p->d = *desc;
+  p->d.variant = 0;
+  p->d.tile_m = tm;
+  p->tile_m = tm;
+  p->device = -1;
+  p->min_tokens_grouped = fill_min_tokens(desc->top_k, desc->num_experts, tm);
+  p->ws_bytes = ws_layout(p->d, tm, desc->max_tokens).total;
+  *out = p;
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_plan(const qtip_moe_desc* desc, int device, qtip_moe_plan_t* out) {
+  g_detail.clear();
+  if (!out) return fail(QTIP_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int32_t tm = 0;
+  qtip_status s = validate_desc(desc, &tm);
+  if (s != QTIP_OK) return s;
+  if (device < 0 || device >= kMaxDevices) return fail(QTIP_ERR_INVALID_ARG, "device index out of range");
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  s = qtip_moe_plan_for_arch(desc, prop.gcnArchName, out);
+  if (s == QTIP_OK) (*out)->device = device;
+  return s;
+}
+
+qtip_status qtip_moe_plan_destroy(qtip_moe_plan_t plan) {
+  delete plan;
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m, size_t* workspace_bytes,
+                               int32_t* min_tokens_grouped) {
+  if (!plan) return fail(QTIP_ERR_INVALID_ARG, "plan is NULL");
+  if (tile_m) *tile_m = plan->tile_m;
+  if (workspace_bytes) *workspace_bytes = plan->ws_bytes;
+  if (min_tokens_grouped) *min_tokens_grouped = plan->min_tokens_grouped;
+  return QTIP_OK;
+}
+
+int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens) {
+  if (!plan || n_tokens < 1) return -1;
+  if (plan->d.arm_override != QTIP_ARM_AUTO) return plan->d.arm_override;
+  return fill_select_grouped(n_tokens, plan->d.top_k, plan->d.num_experts, plan->tile_m) ? QTIP_ARM_GROUPED
+                                                                                       : QTIP_ARM_GEMV;
+}
+
+qtip_status qtip_arch_witness(int device, void* stream) {
+  g_detail.clear();
+  if (device < 0 || device >= kMaxDevices) return fail(QTIP_ERR_INVALID_ARG, "device index out of range");
+  int cur = 0;
+  qtip_status s = current_device(&cur);
+  if (s != QTIP_OK) return s;
+  if (cur != device) {
+    hipError_t e = hipSetDevice(device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  }
+  s = witness_on(device, (hipStream_t)stream);
+  if (cur != device) (void)hipSetDevice(cur);
+  return s;
+}
+
+qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_tokens, int32_t* topk_idx,
+                           float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                           int32_t* tile_map, int32_t* n_tiles, void* stream) {
+  g_detail.clear();
+  if (!plan || !logits || !topk_idx || !topk_w || !counts || !offsets || !sorted_pair || !tile_map || !n_tiles)
+    return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (n_tokens <= 0 || n_tokens > plan->d.max_tokens)
+    return fail(QTIP_ERR_INVALID_CONFIG, "n_tokens must be in [1, max_tokens]");
+  const hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  qtip_status s = ensure_device(plan, st, &dev);
+  if (s != QTIP_OK) return s;
+  const qtip_moe_desc& d = plan->d;
+  hipError_t e = launch_route_topk(logits, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
+  if (e != hipSuccess) return hip_fail(e, "route_topk launch");
+  plan->stats.route_launches++;
+  e = launch_bin(topk_idx, n_tokens * d.top_k, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets,
+                 sorted_pair, tile_map, n_tiles, nullptr, nullptr, st);
+  if (e != hipSuccess) return hip_fail(e, "bin launch");
+  plan->stats.route_launches++;
+  return QTIP_OK;
+}
+
+qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t* codes, const uint16_t* scales,
+                               const uint16_t* lut, int32_t num_experts, int32_t rows, int32_t cols,
+                               const void* a_bf16, int32_t n_rows_a, const int32_t* unit_map, int32_t n_units,
+                               float* y, void* stream) {
+  g_detail.clear();
+  if (!plan || !codes || !scales || !lut || !a_bf16 || !unit_map || !y) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (arm != QTIP_ARM_GEMV && arm != QTIP_ARM_GROUPED) return fail(QTIP_ERR_INVALID_ARG, "arm must be GEMV or GROUPED");
+  if (num_experts < 1 || rows < 16 || rows % 16 || cols < kKBlock || cols % kKBlock || n_rows_a < 1)
+    return fail(QTIP_ERR_INVALID_ARG, "bad shape: rows % 16, cols % 128, num_experts >= 1, n_rows_a >= 1");
+  if ((reinterpret_cast<uintptr_t>(lut) & 15) || (reinterpret_cast<uintptr_t>(a_bf16) & 15) ||
+      (reinterpret_cast<uintptr_t>(codes) & 7))
+    return fail(QTIP_ERR_INVALID_ARG, "lut and a_bf16 must be 16-byte aligned, codes 8-byte aligned");
+  if (n_units <= 0) return fail(QTIP_ERR_INVALID_CONFIG, "n_units must be >= 1 (an empty launch is an error)");
+  const hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  qtip_status s = ensure_device(plan, st, &dev);
+  if (s != QTIP_OK) return s;
+  ExpertParams p{};
+  p.codes0 = codes;
+  p.scale0 = scales;
+  p.lut = lut;
+  p.act = reinterpret_cast<const uint16_t*>(a_bf16);
+  p.act_row_div = 1;
+  p.units = unit_map;
+  p.n_units_host = n_units;
+  p.num_experts = num_experts;
+  p.rows = rows;
+  p.cols = cols;
+  p.n_pos = n_rows_a;
+  p.n_act_rows = n_rows_a;
+  p.out = y;
+  p.n_out_rows = n_rows_a;
+  const int grid = persistent_grid(dev, (size_t)n_units * (rows / kRowsPerTask));
+  hipError_t e = launch_expert(kModeSingle, arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv, p, grid, st);
+  if (e != hipSuccess) return hip_fail(e, "expert kernel launch");
+  if (arm == QTIP_ARM_GROUPED) plan->stats.grouped_launches++; else plan->stats.gemv_launches++;
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, const void* x_bf16, const float* logits,
+                             int32_t n_tokens, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_detail.clear();
+  if (!plan || !w || !x_bf16 || !logits || !out || !workspace) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (!w->codes_gate || !w->codes_up || !w->codes_down || !w->scale_gate || !w->scale_up || !w->scale_down || !w->lut)
+    return fail(QTIP_ERR_INVALID_ARG, "NULL weight pointer");
+  if ((reinterpret_cast<uintptr_t>(w->lut) & 15) || (reinterpret_cast<uintptr_t>(x_bf16) & 15) ||
+      (reinterpret_cast<uintptr_t>(out) & 15) || (reinterpret_cast<uintptr_t>(w->codes_gate) & 7) ||
+      (reinterpret_cast<uintptr_t>(w->codes_up) & 7) || (reinterpret_cast<uintptr_t>(w->codes_down) & 7))
+    return fail(QTIP_ERR_INVALID_ARG, "lut, x and out must be 16-byte aligned, codes 8-byte aligned");
+  if (n_tokens <= 0 || n_tokens > plan->d.max_tokens)
+    return fail(QTIP_ERR_INVALID_CONFIG, "n_tokens must be in [1, max_tokens] (an empty launch is an error)");
+  if (workspace_bytes < plan->ws_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(QTIP_ERR_INVALID_ARG, "workspace too small or not 256-byte aligned");
+  const hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  qtip_status s = ensure_device(plan, st, &dev);
+  if (s != QTIP_OK) return s;
+
+  const qtip_moe_desc& d = plan->d;
+  const int32_t arm = qtip_moe_select_arm(plan, n_tokens);
+  const int karm = arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv;
+  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens);
+  char* ws = reinterpret_cast<char*>(workspace);
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
+  float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted_pair = reinterpret_cast<int32_t*>(ws + L.sorted_pair);
+  int32_t* tile_map = reinterpret_cast<int32_t*>(ws + L.tile_map);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + L.n_tiles);
+  int32_t* unit_map = reinterpret_cast<int32_t*>(ws + L.unit_map);
+  int32_t* n_units = reinterpret_cast<int32_t*>(ws + L.n_units);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  float* y = reinterpret_cast<float*>(ws + L.y);
+  const int32_t P = n_tokens * d.top_k;
+
+  hipError_t e = launch_route_topk(logits, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
+  if (e != hipSuccess) return hip_fail(e, "route_topk launch");
+  e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets, sorted_pair, tile_map,
+                 n_tiles, unit_map, n_units, st);
+  if (e != hipSuccess) return hip_fail(e, "bin launch");
+  plan->stats.route_launches += 2;
+
+  const size_t max_units = max_units_for(d, n_tokens);
+  ExpertParams gu{};
+  gu.codes0 = w->codes_gate;
+  gu.codes1 = w->codes_up;
+  gu.scale0 = w->scale_gate;
+  gu.scale1 = w->scale_up;
+  gu.lut = w->lut;
+  gu.act = reinterpret_cast<const uint16_t*>(x_bf16);
+  gu.act_row_map = sorted_pair;
+  gu.act_row_div = d.top_k;
+  gu.units = unit_map;
+  gu.n_units_dev = n_units;
+  gu.num_experts = d.num_experts;
+  gu.rows = d.inter;
+  gu.cols = d.hidden;
+  gu.n_pos = P;
+  gu.n_act_rows = n_tokens;
+  gu.out = h;
+  gu.n_out_rows = P;
+  e = launch_expert(kModeGateUp, karm, gu, persistent_grid(dev, max_units * (d.inter / kRowsPerTask)), st);
+  if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
+
+  ExpertParams dn{};
+  dn.codes0 = w->codes_down;
+  dn.scale0 = w->scale_down;
+  dn.lut = w->lut;
+  dn.act = h;
+  dn.act_row_div = 1;
+  dn.units = unit_map;
+  dn.n_units_dev = n_units;
+  dn.num_experts = d.num_experts;
+  dn.rows = d.hidden;
+  dn.cols = d.inter;
+  dn.n_pos = P;
+  dn.n_act_rows = P;
+  dn.out = y;
+  dn.out_row_map = sorted_pair;
+  dn.n_out_rows = P;
+  e = launch_expert(kModeSingle, karm, dn, persistent_grid(dev, max_units * (d.hidden / kRowsPerTask)), st);
+  if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
+  if (karm == kArmGrouped) plan->stats.grouped_launches += 2; else plan->stats.gemv_launches += 2;
+
+  e = launch_combine(y, topk_w, n_tokens, d.top_k, d.hidden, out, d.out_dtype == QTIP_OUT_BF16, st);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  plan->stats.combine_launches++;
+  plan->stats.forward_calls++;
+  plan->stats.last_arm = arm;
+  plan->stats.last_n_tokens = n_tokens;
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_stats_get(qtip_moe_plan_t plan, qtip_moe_stats* out) {
+  if (!plan || !out) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  *out = plan->stats;
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_stats_reset(qtip_moe_plan_t plan) {
+  if (!plan) return fail(QTIP_ERR_INVALID_ARG, "plan is NULL");
+  plan->stats = qtip_moe_stats{};
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_engaged_line(qtip_moe_plan_t plan, int32_t n_tokens, char* buf, size_t buf_len) {
+  if (!plan || !buf || buf_len == 0) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (n_tokens < 1) return fail(QTIP_ERR_INVALID_CONFIG, "n_tokens must be >= 1");
+  const qtip_moe_desc& d = plan->d;
+  const int32_t arm = qtip_moe_select_arm(plan, n_tokens);
+  const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
+  std::snprintf(buf, buf_len,
+                "qtip_moe: %s arm for %d tokens x top-%d of %d experts; mean m-tile fill %.1f%% "
+                "(%.2f pairs per woken expert, tile_m=%d); grouped from %d tokens%s",
+                arm == QTIP_ARM_GROUPED ? "grouped" : "GEMV", n_tokens, d.top_k, d.num_experts,
+                100.0 * ppe / plan->tile_m, ppe, plan->tile_m, plan->min_tokens_grouped,
+                d.arm_override != QTIP_ARM_AUTO ? " (arm pinned by the plan)" : "");
+  return QTIP_OK;
+}
+
+}  // extern "C"

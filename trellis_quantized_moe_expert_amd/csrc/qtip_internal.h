@@ -1,0 +1,63 @@
+// Internal declarations shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace qtip {
+
+constexpr int kLutEntries = 65536;     // 16-bit trellis state -> one LUT entry
+constexpr int kExpertThreads = 1024;   // 16 wave64 per workgroup; the LUT fills 128 KiB of LDS,
+constexpr int kExpertWaves = 16;       // so one workgroup per CU is resident
+constexpr int kRowsPerTask = 16;       // output rows per wave task (the MFMA N)
+constexpr int kKBlock = 128;           // inputs per K block: 4 lane groups x 32-symbol runs
+constexpr int kUnitMaxPairs = 64;      // pairs sharing one decode (4 MFMA row blocks of 16)
+constexpr int kGemvPairs = 8;          // pairs per decode on the GEMV arm (VALU accumulators)
+constexpr int kRouteWaves = 4;         // tokens per route workgroup (one wave each)
+constexpr int kBinThreads = 1024;      // binning runs in one workgroup
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kWitnessValue = 0x950950;
+
+// One pass of one (or two fused) trellis matrices over binned activation rows.
+struct ExpertParams {
+  const uint8_t* codes0;        // [E][rows][cols/4]  gate (fused pass) or the single matrix
+  const uint8_t* codes1;        // [E][rows][cols/4]  up (fused pass only)
+  const uint16_t* scale0;       // [E][rows] fp16
+  const uint16_t* scale1;       // [E][rows] fp16 (fused pass only)
+  const uint16_t* lut;          // [65536] fp16
+  const uint16_t* act;          // [n_act_rows][cols] bf16
+  const int32_t* act_row_map;   // activation row of binned position s = map[s] / act_row_div (NULL: s)
+  int32_t act_row_div;
+  const int32_t* units;         // [n_units][3] (expert, start, len)
+  const int32_t* n_units_dev;   // device count of units (NULL: use n_units_host)
+  int32_t n_units_host;
+  int32_t num_experts;
+  int32_t rows, cols;
+  int32_t n_pos;                // binned positions are [0, n_pos)
+  int32_t n_act_rows;
+  void* out;                    // fused: bf16 h [n_pos][rows]; single: fp32 y [n_out_rows][rows]
+  const int32_t* out_row_map;   // single pass: output row of position s = map[s] (NULL: s)
+  int32_t n_out_rows;
+};
+
+enum ExpertMode { kModeGateUp = 0, kModeSingle = 1 };
+enum ExpertArm { kArmGemv = 0, kArmGrouped = 1 };
+
+hipError_t launch_expert(int mode, int arm, const ExpertParams& p, int grid, hipStream_t stream);
+
+hipError_t launch_route_topk(const float* logits, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
+                             float* topk_w, hipStream_t stream);
+
+hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
+                      int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map,
+                      int32_t* n_tiles, int32_t* unit_map, int32_t* n_units, hipStream_t stream);
+
+hipError_t launch_combine(const float* y, const float* topk_w, int32_t n, int32_t k, int32_t H, void* out,
+                          int out_bf16, hipStream_t stream);
+
+hipError_t launch_witness(int32_t* out, hipStream_t stream);
+
+}  // namespace qtip

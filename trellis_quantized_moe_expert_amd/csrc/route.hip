@@ -1,0 +1,209 @@
+// Routing and binning kernels.
+//
+// Source: m-tile occupancy page, PR #167, section "The cause is a threshold, not a kernel
+// defect": pairs are sorted by expert and the grouped kernel walks sum_e ceil(count_e /
+// tile_m) m-tiles.  The arch-specialise page (PR #99, section "D18") requires the tile map
+// to come from the same m-tile height the GEMM uses; here both read the plan's value.
+//
+// Readings fixed by the C ABI: top-k in descending logit order with ties to the lower
+// expert index; router weights = softmax over the k selected logits; within an expert's
+// bin pairs keep ascending pair id p = t*k + j (a stable counting sort), so the binning
+// is unique and can be compared bit for bit.
+#include "qtip_internal.h"
+
+#include <cmath>
+
+namespace qtip {
+
+namespace {
+
+__device__ inline bool beats(float v, int e, float bv, int be) {
+  return v > bv || (v == bv && e < be);
+}
+
+// One wave per token.  Each lane holds up to 16 logits (E <= 1024); k rounds of a wave-wide
+// argmax under the order (value descending, index ascending) pick the experts in order.
+__global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const float* __restrict__ logits, int32_t n,
+                                                                    int32_t E, int32_t k,
+                                                                    int32_t* __restrict__ topk_idx,
+                                                                    float* __restrict__ topk_w) {
+  __shared__ float sel[kRouteWaves][kMaxTopK];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * kRouteWaves + wv;
+  if (t >= n) return;  // whole wave leaves together; no barrier follows
+  const float* row = logits + (size_t)t * E;
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = (e < E) ? row[e] : 0.0f;
+  }
+  uint32_t taken = 0;
+  for (int jj = 0; jj < k; ++jj) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E && !((taken >> q) & 1u) && beats(v[q], e, bv, be)) {
+        bv = v[q];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      if (beats(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    // non-finite logits can leave no winner (be stays out of range); the pair is then
+    // recorded with an out-of-range expert id, which binning ignores
+    if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == 0) {
+      topk_idx[(size_t)t * k + jj] = be;
+      sel[wv][jj] = bv;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // softmax over the k selected logits, max subtracted first (sel[0] is the largest)
+  float ex = 0.0f;
+  if (lane < k) ex = expf(sel[wv][lane] - sel[wv][0]);
+  float z = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  if (lane < k) topk_w[(size_t)t * k + lane] = ex / z;
+}
+
+// Inclusive scan of one value per thread across a 1024-thread workgroup.
+__device__ inline int block_inclusive_scan(int x, int* wave_tot) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wave_tot[wv] = x;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wv; ++w) add += wave_tot[w];
+  __syncthreads();
+  return x + add;
+}
+
+// Stable counting sort of the n*k pairs by expert, plus the m-tile map and the unit map
+// (units = runs of up to unit_pairs pairs of one expert; each unit is one decode of the
+// expert's weights in the expert kernels; unit_map/n_units may be NULL to skip them).
+// One workgroup of 1024 threads.
+__global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restrict__ topk_idx, int32_t P, int32_t E,
+                                                          int32_t tile_m, int32_t unit_pairs,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_pair,
+                                                          int32_t* __restrict__ tile_map, int32_t* __restrict__ n_tiles,
+                                                          int32_t* __restrict__ unit_map,
+                                                          int32_t* __restrict__ n_units) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int running[kMaxExperts];
+  __shared__ int wave_cnt[kExpertWaves][kMaxExperts];
+  __shared__ int wave_tot[kExpertWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+
+  for (int e = tid; e < E; e += kBinThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kBinThreads) {
+    const int e = topk_idx[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // exclusive scans of counts, tiles per expert and units per expert (E <= 1024 = threads)
+  const int c = (tid < E) ? cnt[tid] : 0;
+  const int nt = (c + tile_m - 1) / tile_m;
+  const int nu = (c + unit_pairs - 1) / unit_pairs;
+  const int c_incl = block_inclusive_scan(c, wave_tot);
+  const int t_incl = block_inclusive_scan(nt, wave_tot);
+  const int u_incl = block_inclusive_scan(nu, wave_tot);
+  if (tid < E) {
+    const int off = c_incl - c;
+    counts[tid] = c;
+    offsets[tid] = off;
+    running[tid] = off;
+    int tb = t_incl - nt;
+    for (int q = 0; q < nt; ++q) {
+      tile_map[3 * (tb + q) + 0] = tid;
+      tile_map[3 * (tb + q) + 1] = off + q * tile_m;
+      tile_map[3 * (tb + q) + 2] = min(tile_m, c - q * tile_m);
+    }
+    int ub = u_incl - nu;
+    for (int q = 0; unit_map && q < nu; ++q) {
+      unit_map[3 * (ub + q) + 0] = tid;
+      unit_map[3 * (ub + q) + 1] = off + q * unit_pairs;
+      unit_map[3 * (ub + q) + 2] = min(unit_pairs, c - q * unit_pairs);
+    }
+  }
+  if (tid == E - 1) {
+    offsets[E] = c_incl;
+    *n_tiles = t_incl;
+    if (n_units) *n_units = u_incl;
+  }
+  __syncthreads();
+
+  // stable scatter, 1024 pairs per round: rank inside the wave from a bitwise match of
+  // the expert id, then the counts of earlier waves and earlier rounds
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < P; base += kBinThreads) {
+    for (int i = tid; i < kExpertWaves * E; i += kBinThreads) (&wave_cnt[0][0])[(i / E) * kMaxExperts + (i % E)] = 0;
+    const int p = base + tid;
+    const int ep = (p < P) ? topk_idx[p] : E;
+    const bool valid = ep >= 0 && ep < E;
+    const int e = valid ? ep : E;  // E: one bucket for idle lanes and out-of-range ids
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot((e >> b) & 1);
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    __syncthreads();
+    if (valid && rank == 0) wave_cnt[wv][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = running[e] + rank;
+      for (int w = 0; w < wv; ++w) pos += wave_cnt[w][e];
+      sorted_pair[pos] = p;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kBinThreads) {
+      int add = 0;
+      for (int w = 0; w < kExpertWaves; ++w) add += wave_cnt[w][ee];
+      running[ee] += add;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const float* logits, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
+                             float* topk_w, hipStream_t stream) {
+  const int grid = (n + kRouteWaves - 1) / kRouteWaves;
+  hipLaunchKernelGGL(route_topk_kernel, dim3(grid), dim3(kRouteWaves * 64), 0, stream, logits, n, E, k, topk_idx,
+                     topk_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
+                      int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
+                      int32_t* unit_map, int32_t* n_units, hipStream_t stream) {
+  hipLaunchKernelGGL(bin_kernel, dim3(1), dim3(kBinThreads), 0, stream, topk_idx, n_pairs, E, tile_m, unit_pairs,
+                     counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units);
+  return hipGetLastError();
+}
+
+}  // namespace qtip
