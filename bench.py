@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the trellis-quantized MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--arm auto|gemv|grouped]
+
+A step is one qtip_moe_forward (route, bin, gate+up, down, combine) over one batch of the
+workload, with weights and inputs already resident in HBM.  The default workload is the
+V4-shaped decode layer (E=256, top-6, hidden 4096, expert intermediate 2048, n=32 tokens,
+uniform routing, seed 0).  Prints ONE JSON line: tokens/s over the timed steps, the
+roofline of the dominant kernel (gate+up, packed-weight bytes per launch over its
+HIP-event-measured duration, against 8 TB/s), and the CPU oracle timed on a bounded sample.
+
+Other modes (not used by the driver):
+  --sweep PATH        both arms forced at n in {8,16,32,64,128,256,512,683,1024}; JSON lines to PATH
+  --calibrate-copy    run one device copy of known size first (for scaling PMC byte counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + packed-weight HBM GB/s (% peak) vs token count n"
+HBM_PEAK_GBS = 8000.0
+# VALU decode ceiling: 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-ops/s at 2 ops per symbol.
+DECODE_VALU_PEAK_SYMS = 256 * 64 * 2.4e9 / 2
+SWEEP_N = [8, 16, 32, 64, 128, 256, 512, 683, 1024]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["trellis_quantized_moe_expert_amd/csrc/expert.hip",
+                  "trellis_quantized_moe_expert_amd/csrc/qtip_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Runner:
+    """Plan + device weights + workspace; forwards one batch through the C ABI."""
+
+    def __init__(self, inp, arm, max_tokens, out_dtype, weights=None):
+        import torch
+        import trellis_quantized_moe_expert_amd as q
+        from moe_inputs.device import weights_to_device
+        self.q = q
+        s = inp.shape
+        self.shape = s
+        arm_code = {"auto": q.QTIP_ARM_AUTO, "gemv": q.QTIP_ARM_GEMV, "grouped": q.QTIP_ARM_GROUPED}[arm]
+        od = q.QTIP_OUT_BF16 if out_dtype == "bf16" else q.QTIP_OUT_F32
+        self.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens, arm_code, 0,
+                                                od, 0), 0)
+        self.info = q.qtip_moe_plan_info(self.plan)
+        self.ws = torch.empty(self.info["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
+        self.dw = weights if weights is not None else weights_to_device(inp)
+        d = self.dw
+        self.w = q.make_weights(d.codes_gate, d.codes_up, d.codes_down, d.scale_gate, d.scale_up, d.scale_down, d.lut)
+        self.out_dtype = torch.int16 if out_dtype == "bf16" else torch.float32
+        self.stream = torch.cuda.current_stream()
+
+    def bind(self, inp):
+        import torch
+        from moe_inputs.device import tokens_to_device
+        self.n = inp.logits.shape[0]
+        self.tok = tokens_to_device(inp)
+        self.out = torch.empty((self.n, self.shape.hidden), dtype=self.out_dtype, device="cuda:0")
+
+    def step(self):
+        self.q.qtip_moe_forward(self.plan, self.w, self.tok.x, self.tok.logits, self.n, self.out, self.ws,
+                                self.ws.numel(), self.stream)
+
+    def routing_counts(self):
+        """Per-expert pair counts of the bound batch, from the GPU router."""
+        import torch
+        q, s, n = self.q, self.shape, self.n
+        dev = lambda *shape, dt=torch.int32: torch.empty(shape, dtype=dt, device="cuda:0")
+        idx, w = dev(n, s.top_k), dev(n, s.top_k, dt=torch.float32)
+        counts, offs, sp, tm, nt = dev(s.num_experts), dev(s.num_experts + 1), dev(n * s.top_k), dev(n * s.top_k, 3), dev(1)
+        q.qtip_moe_route(self.plan, self.tok.logits, n, idx, w, counts, offs, sp, tm, nt, self.stream)
+        torch.cuda.synchronize()
+        return counts.cpu().numpy(), int(nt.cpu().numpy()[0])
+
+    def close(self):
+        self.q.qtip_moe_plan_destroy(self.plan)
+
+
+def timed(runner, steps, warmup, profile=True):
+    import torch
+    q = runner.q
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    if profile:
+        q.qtip_moe_profile_enable(runner.plan, min(steps, 4096))
+    q.qtip_moe_stats_reset(runner.plan)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()          # single process: the barrier is this synchronisation
+    t0 = time.perf_counter()
+    ev0.record(runner.stream)
+    for _ in range(steps):
+        runner.step()
+    ev1.record(runner.stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stats = q.qtip_moe_stats_get(runner.plan)
+    prof = q.qtip_moe_profile_read(runner.plan) if profile else None
+    if profile:
+        q.qtip_moe_profile_enable(runner.plan, 0)
+    return {"wall_s": t1 - t0, "gpu_ms": ev0.elapsed_time(ev1), "stats": stats, "prof": prof}
+
+
+def schedule_figures(counts, shape, arm):
+    """Algorithmic bytes and symbols of one forward, from the router's per-expert counts."""
+    import numpy as np
+    E, H, I = shape.num_experts, shape.hidden, shape.inter
+    woken = int((counts > 0).sum())
+    per_expert_bytes = {"gate_up": 2 * I * H // 4 + 2 * I * 2, "down": H * I // 4 + H * 2}
+    # decodes per expert: the grouped arm decodes once per unit of up to 64 pairs, the GEMV
+    # arm once per 8 pairs of a unit
+    units = [(c + 63) // 64 for c in counts.tolist()]
+    if arm == "grouped":
+        decodes = sum(units)
+    else:
+        decodes = 0
+        for c in counts.tolist():
+            while c > 0:
+                L = min(64, c)
+                decodes += (L + 7) // 8
+                c -= L
+    return {"woken": woken, "units": int(sum(units)), "decodes": int(decodes),
+            "bytes": {k: woken * v for k, v in per_expert_bytes.items()},
+            "symbols_min": {"gate_up": woken * 2 * I * H, "down": woken * H * I},
+            "symbols_sched": {"gate_up": decodes * 2 * I * H, "down": decodes * H * I},
+            "max_count": int(np.max(counts))}
+
+
+def read_traffic(workload, arm):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{workload}/{arm}/gate_up"
+    ent = rec.get(key)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
+        return None       # counters were taken on another version of the kernel
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, n_sample):
+    """The oracle as it stands, one BLAS thread, on the first n_sample tokens of the batch."""
+    from threadpoolctl import threadpool_limits
+    from oracle import moe
+    toks = list(range(n_sample))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        moe.moe_forward(inp, tokens=toks)
+        dt = time.perf_counter() - t0
+    return {"value": n_sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_sample} of the {inp.shape.n_tokens} tokens of this batch: routing and binning of the "
+                      f"whole batch, then the declared-mode layer for those tokens (decode of every expert they "
+                      f"use), numpy float64, 1 thread, {dt:.1f} s"}
+
+
+def calibrate_copy():
+    import torch
+    nbytes = 1 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"calibrate-copy: copied {nbytes} bytes device to device")
+    del a, b
+
+
+def run_sweep(path, steps, warmup):
+    import moe_inputs
+    shape = moe_inputs.WORKLOADS["v4_decode_n32"]
+    log("sweep: drawing V4-shaped weights once")
+    inps = moe_inputs.make_inputs_multi(shape, SWEEP_N, seed=0)
+    base = None
+    with open(path, "w") as f:
+        for arm in ("gemv", "grouped"):
+            r = Runner(inps[SWEEP_N[0]], arm, max(SWEEP_N), "bf16", weights=base)
+            base = r.dw
+            for n in SWEEP_N:
+                r.bind(inps[n])
+                res = timed(r, steps, warmup)
+                counts, _ = r.routing_counts()
+                fig = schedule_figures(counts, r.shape, arm)
+                ms = res["wall_s"] * 1e3 / steps
+                rec = {"arm": arm, "n": n, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+                       "stage_ms": {k: v / res["prof"]["n_forwards"] for k, v in res["prof"].items() if k != "n_forwards"},
+                       "launches": {k: res["stats"][k] for k in ("gemv_launches", "grouped_launches")},
+                       "woken": fig["woken"], "decodes": fig["decodes"],
+                       "predicate_grouped": r.q.qtip_fill_select_grouped(n, 6, 256, 16)}
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                log(json.dumps(rec))
+            r.close()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="v4_decode_n32")
+    ap.add_argument("--arm", choices=["auto", "gemv", "grouped"], default="auto")
+    ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
+    ap.add_argument("--cpu-sample", type=int, default=2, help="tokens the CPU oracle is timed on (0: skip)")
+    ap.add_argument("--sweep", metavar="PATH", default=None)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the path has no multi-GPU mode); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_inputs
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+    if args.sweep:
+        run_sweep(args.sweep, args.steps, args.warmup)
+        return
+
+    log(f"bench: drawing workload {args.workload}")
+    inp = moe_inputs.make_workload(args.workload, seed=0)
+    s = inp.shape
+    runner = Runner(inp, args.arm, s.n_tokens, args.out_dtype)
+    runner.bind(inp)
+    arm_code = runner.q.qtip_moe_select_arm(runner.plan, s.n_tokens)
+    arm = "grouped" if arm_code == runner.q.QTIP_ARM_GROUPED else "gemv"
+    log(runner.q.qtip_moe_engaged_line(runner.plan, s.n_tokens))
+    res = timed(runner, args.steps, args.warmup)
+    counts, n_tiles = runner.routing_counts()
+    runner.close()
+
+    if res["wall_s"] <= 0 or res["prof"]["n_forwards"] <= 0:
+        print("bench: no time or no profiled forwards recorded", file=sys.stderr)
+        sys.exit(2)
+    fig = schedule_figures(counts, s, arm)
+    nf = res["prof"]["n_forwards"]
+    stage_ms = {k: v / nf for k, v in res["prof"].items() if k != "n_forwards"}
+    ms_per_step = res["wall_s"] * 1e3 / args.steps
+    tokens_per_s = s.n_tokens * args.steps / res["wall_s"]
+    gu_s = stage_ms["gate_up"] * 1e-3
+    achieved = fig["bytes"]["gate_up"] / gu_s / 1e9
+    layer_bytes = fig["bytes"]["gate_up"] + fig["bytes"]["down"]
+    layer_gpu_s = res["gpu_ms"] * 1e-3 / args.steps
+    counters = res["stats"]
+    if (arm == "grouped" and counters["grouped_launches"] != 2 * args.steps) or \
+       (arm == "gemv" and counters["gemv_launches"] != 2 * args.steps):
+        print(f"bench: launch counters do not show the {arm} arm: {counters}", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = cpu_baseline(inp, args.cpu_sample) if args.cpu_sample > 0 else None
+    line = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "experts": s.num_experts, "top_k": s.top_k, "hidden": s.hidden,
+                   "inter": s.inter, "n_tokens": s.n_tokens, "routing": s.routing, "seed": 0, "arm": arm,
+                   "out_dtype": args.out_dtype},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(args.workload, arm)},
+        "cpu_baseline": cpu,
+        "detail": {
+            "dominant_kernel": f"expert_kernel gate+up ({arm} arm)",
+            "stage_ms": stage_ms,
+            "layer_packed_gbs": layer_bytes / layer_gpu_s / 1e9,
+            "layer_packed_frac": layer_bytes / layer_gpu_s / 1e9 / HBM_PEAK_GBS,
+            "gate_up_packed_bytes": fig["bytes"]["gate_up"], "down_packed_bytes": fig["bytes"]["down"],
+            "woken_experts": fig["woken"], "max_pairs_per_expert": fig["max_count"], "m_tiles": n_tiles,
+            "decode_units": fig["units"], "decodes": fig["decodes"],
+            "gate_up_symbols_per_s": fig["symbols_sched"]["gate_up"] / gu_s,
+            "gate_up_decode_valu_frac": fig["symbols_sched"]["gate_up"] / gu_s / DECODE_VALU_PEAK_SYMS,
+            "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "route_launches",
+                                                         "combine_launches")},
+            "kernel_source_sha": kernel_source_sha(),
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -203,6 +203,17 @@ qtip_status qtip_moe_engaged_line(qtip_moe_plan_t plan, int32_t n_tokens, char* 
  * kernel cannot run.  qtip_moe_forward / _route / qtip_expert_matmul call it on first use. */
 qtip_status qtip_arch_witness(int device, void* stream);
 
+/* Per-stage timing.  qtip_moe_profile_enable(plan, capacity) creates capacity x 6 HIP events
+ * (capacity <= 4096; 0 disables and frees them); every later forward on the plan records an
+ * event before its first kernel and after each of its five kernels (route, bin, gate+up,
+ * down, combine) on the forward's stream, cycling through `capacity` slots.
+ * qtip_moe_profile_read waits for the recorded events, writes the summed milliseconds per
+ * stage over the last min(forwards, capacity) forwards into stage_ms[5] (host), their count
+ * into n_forwards, and clears the record.  Enabling creates events, so do it outside capture. */
+#define QTIP_PROFILE_STAGES 5
+qtip_status qtip_moe_profile_enable(qtip_moe_plan_t plan, int32_t capacity);
+qtip_status qtip_moe_profile_read(qtip_moe_plan_t plan, double* stage_ms /*host [5]*/, int32_t* n_forwards /*host*/);
+
 const char* qtip_status_string(qtip_status s);
 /* Text of the last error raised on the calling thread ("" if none). */
 const char* qtip_last_error_detail(void);

@@ -124,6 +124,24 @@ def make_inputs(shape: MoEShape, seed: int = 0, n_tokens: Optional[int] = None) 
     return MoEInputs(s, seed, lut, cg, cu, cd, sg, su, sd, x, logits)
 
 
+def make_inputs_multi(shape: MoEShape, n_list, seed: int = 0) -> dict:
+    """One set of weights and, for each n in n_list, the activations and logits that
+    make_inputs(shape, seed, n) would draw (the generator state after the weights is
+    replayed for each n).  Returns {n: MoEInputs}, all sharing the weight arrays."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lut = rng.standard_normal(LUT_SIZE).astype(np.float16)
+    weights = _draw_experts(rng, shape)
+    state = rng.bit_generator.state
+    out = {}
+    for n in n_list:
+        s = dataclasses.replace(shape, n_tokens=n)
+        r = np.random.Generator(np.random.PCG64(seed))
+        r.bit_generator.state = state
+        x = f32_to_bf16_bits(r.standard_normal((n, s.hidden)).astype(np.float32))
+        out[n] = MoEInputs(s, seed, lut, *weights, x, _draw_logits(r, s))
+    return out
+
+
 def make_workload(name: str, seed: int = 0, n_tokens: Optional[int] = None) -> MoEInputs:
     return make_inputs(WORKLOADS[name], seed=seed, n_tokens=n_tokens)
 

@@ -72,6 +72,8 @@ _SIGS = {
     "qtip_moe_stats_reset": (_I32, [_P]),
     "qtip_moe_engaged_line": (_I32, [_P, _I32, ctypes.c_char_p, ctypes.c_size_t]),
     "qtip_arch_witness": (_I32, [ctypes.c_int, _P]),
+    "qtip_moe_profile_enable": (_I32, [_P, _I32]),
+    "qtip_moe_profile_read": (_I32, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)]),
     "qtip_status_string": (ctypes.c_char_p, [_I32]),
     "qtip_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -222,6 +224,20 @@ def qtip_moe_engaged_line(plan, n_tokens) -> str:
 
 def qtip_arch_witness(device: int = 0, stream=None) -> None:
     _check("qtip_arch_witness", lib().qtip_arch_witness(device, _stream(stream)))
+
+
+PROFILE_STAGES = ("route", "bin", "gate_up", "down", "combine")
+
+
+def qtip_moe_profile_enable(plan, capacity: int) -> None:
+    _check("qtip_moe_profile_enable", lib().qtip_moe_profile_enable(plan, capacity))
+
+
+def qtip_moe_profile_read(plan) -> dict:
+    ms = (ctypes.c_double * 5)()
+    n = _I32()
+    _check("qtip_moe_profile_read", lib().qtip_moe_profile_read(plan, ms, ctypes.byref(n)))
+    return {"n_forwards": n.value, **{name: ms[i] for i, name in enumerate(PROFILE_STAGES)}}
 
 
 def raw_status(fn_name: str, *args) -> int:

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/qtip_moe.h"
 #include "fill_predicate.h"
@@ -26,7 +27,29 @@ struct qtip_moe_plan_s {
   int32_t min_tokens_grouped;
   size_t ws_bytes;
   qtip_moe_stats stats;
+  // per-stage timing ring (qtip_moe_profile_enable)
+  std::vector<hipEvent_t> prof_events;  // capacity x (kStages + 1)
+  int32_t prof_capacity = 0;
+  int64_t prof_recorded = 0;            // forwards recorded since the last read
 };
+
+namespace {
+constexpr int kStages = QTIP_PROFILE_STAGES;
+
+void prof_free(qtip_moe_plan_s* p) {
+  for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
+  p->prof_events.clear();
+  p->prof_capacity = 0;
+  p->prof_recorded = 0;
+}
+
+// Records boundary `b` (0 = before the first kernel, 1..5 = after stage b) of this forward.
+inline hipError_t prof_mark(qtip_moe_plan_s* p, int b, hipStream_t st) {
+  if (p->prof_capacity == 0) return hipSuccess;
+  const int64_t slot = p->prof_recorded % p->prof_capacity;
+  return hipEventRecord(p->prof_events[slot * (kStages + 1) + b], st);
+}
+}  // namespace
 
 namespace {
 
@@ -243,6 +266,7 @@ qtip_status qtip_moe_plan(const qtip_moe_desc* desc, int device, qtip_moe_plan_t
 }
 
 qtip_status qtip_moe_plan_destroy(qtip_moe_plan_t plan) {
+  if (plan) prof_free(plan);
   delete plan;
   return QTIP_OK;
 }
@@ -377,12 +401,16 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
   float* y = reinterpret_cast<float*>(ws + L.y);
   const int32_t P = n_tokens * d.top_k;
 
-  hipError_t e = launch_route_topk(logits, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
+  hipError_t e = prof_mark(plan, 0, st);
+  if (e != hipSuccess) return hip_fail(e, "profile event");
+  e = launch_route_topk(logits, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
   if (e != hipSuccess) return hip_fail(e, "route_topk launch");
+  if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
   e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets, sorted_pair, tile_map,
                  n_tiles, unit_map, n_units, st);
   if (e != hipSuccess) return hip_fail(e, "bin launch");
   plan->stats.route_launches += 2;
+  if ((e = prof_mark(plan, 2, st)) != hipSuccess) return hip_fail(e, "profile event");
 
   const size_t max_units = max_units_for(d, n_tokens);
   ExpertParams gu{};
@@ -405,6 +433,7 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
   gu.n_out_rows = P;
   e = launch_expert(kModeGateUp, karm, gu, persistent_grid(dev, max_units * (d.inter / kRowsPerTask)), st);
   if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
+  if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
 
   ExpertParams dn{};
   dn.codes0 = w->codes_down;
@@ -424,14 +453,58 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
   dn.n_out_rows = P;
   e = launch_expert(kModeSingle, karm, dn, persistent_grid(dev, max_units * (d.hidden / kRowsPerTask)), st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
+  if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
   if (karm == kArmGrouped) plan->stats.grouped_launches += 2; else plan->stats.gemv_launches += 2;
 
   e = launch_combine(y, topk_w, n_tokens, d.top_k, d.hidden, out, d.out_dtype == QTIP_OUT_BF16, st);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if ((e = prof_mark(plan, 5, st)) != hipSuccess) return hip_fail(e, "profile event");
+  if (plan->prof_capacity) plan->prof_recorded++;
   plan->stats.combine_launches++;
   plan->stats.forward_calls++;
   plan->stats.last_arm = arm;
   plan->stats.last_n_tokens = n_tokens;
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_profile_enable(qtip_moe_plan_t plan, int32_t capacity) {
+  g_detail.clear();
+  if (!plan) return fail(QTIP_ERR_INVALID_ARG, "plan is NULL");
+  if (capacity < 0 || capacity > 4096) return fail(QTIP_ERR_INVALID_ARG, "capacity must be in [0, 4096]");
+  prof_free(plan);
+  if (capacity == 0) return QTIP_OK;
+  plan->prof_events.assign((size_t)capacity * (kStages + 1), nullptr);
+  for (auto& ev : plan->prof_events) {
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      prof_free(plan);
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  plan->prof_capacity = capacity;
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_profile_read(qtip_moe_plan_t plan, double* stage_ms, int32_t* n_forwards) {
+  g_detail.clear();
+  if (!plan || !stage_ms || !n_forwards) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  for (int b = 0; b < kStages; ++b) stage_ms[b] = 0.0;
+  *n_forwards = 0;
+  if (plan->prof_capacity == 0) return fail(QTIP_ERR_INVALID_CONFIG, "profiling is not enabled");
+  const int64_t n = plan->prof_recorded < plan->prof_capacity ? plan->prof_recorded : plan->prof_capacity;
+  for (int64_t slot = 0; slot < n; ++slot) {
+    hipEvent_t* ev = &plan->prof_events[slot * (kStages + 1)];
+    hipError_t e = hipEventSynchronize(ev[kStages]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    for (int b = 0; b < kStages; ++b) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, ev[b], ev[b + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      stage_ms[b] += ms;
+    }
+  }
+  *n_forwards = (int32_t)n;
+  plan->prof_recorded = 0;
   return QTIP_OK;
 }
 
