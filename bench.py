@@ -51,7 +51,7 @@ def kernel_source_sha() -> str:
 class Runner:
     """Plan + device weights + workspace; forwards one batch through the C ABI."""
 
-    def __init__(self, inp, arm, max_tokens, out_dtype, weights=None):
+    def __init__(self, inp, arm, max_tokens, out_dtype, weights=None, variant=0):
         import torch
         import trellis_quantized_moe_expert_amd as q
         from moe_inputs.device import weights_to_device
@@ -60,8 +60,8 @@ class Runner:
         self.shape = s
         arm_code = {"auto": q.QTIP_ARM_AUTO, "gemv": q.QTIP_ARM_GEMV, "grouped": q.QTIP_ARM_GROUPED}[arm]
         od = q.QTIP_OUT_BF16 if out_dtype == "bf16" else q.QTIP_OUT_F32
-        self.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens, arm_code, 0,
-                                                od, 0), 0)
+        self.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens, arm_code,
+                                                variant, od, 0), 0)
         self.info = q.qtip_moe_plan_info(self.plan)
         self.ws = torch.empty(self.info["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
         self.dw = weights if weights is not None else weights_to_device(inp)
@@ -121,24 +121,21 @@ def timed(runner, steps, warmup, profile=True):
     return {"wall_s": t1 - t0, "gpu_ms": ev0.elapsed_time(ev1), "stats": stats, "prof": prof}
 
 
-def schedule_figures(counts, shape, arm):
-    """Algorithmic bytes and symbols of one forward, from the router's per-expert counts."""
+def schedule_figures(counts, shape, arm, sched):
+    """Algorithmic bytes and symbols of one forward, from the router's per-expert counts and the
+    plan's schedule (how many binned pairs share one decode of an expert's rows)."""
     import numpy as np
     E, H, I = shape.num_experts, shape.hidden, shape.inter
     woken = int((counts > 0).sum())
     per_expert_bytes = {"gate_up": 2 * I * H // 4 + 2 * I * 2, "down": H * I // 4 + H * 2}
-    # decodes per expert: the grouped arm decodes once per unit of up to 64 pairs, the GEMV
-    # arm once per 8 pairs of a unit
-    units = [(c + 63) // 64 for c in counts.tolist()]
-    if arm == "grouped":
-        decodes = sum(units)
-    else:
-        decodes = 0
-        for c in counts.tolist():
-            while c > 0:
-                L = min(64, c)
-                decodes += (L + 7) // 8
-                c -= L
+    per = sched["pairs_per_decode_grouped"] if arm == "grouped" else sched["pairs_per_decode_gemv"]
+    units = [(c + 63) // 64 for c in counts.tolist()]      # the router's units hold <= 64 pairs
+    decodes = 0
+    for c in counts.tolist():
+        while c > 0:
+            L = min(64, c)
+            decodes += (L + per - 1) // per
+            c -= L
     return {"woken": woken, "units": int(sum(units)), "decodes": int(decodes),
             "bytes": {k: woken * v for k, v in per_expert_bytes.items()},
             "symbols_min": {"gate_up": woken * 2 * I * H, "down": woken * H * I},
@@ -188,7 +185,7 @@ def calibrate_copy():
     del a, b
 
 
-def run_sweep(path, steps, warmup):
+def run_sweep(path, steps, warmup, variant=0):
     import moe_inputs
     shape = moe_inputs.WORKLOADS["v4_decode_n32"]
     log("sweep: drawing V4-shaped weights once")
@@ -196,13 +193,13 @@ def run_sweep(path, steps, warmup):
     base = None
     with open(path, "w") as f:
         for arm in ("gemv", "grouped"):
-            r = Runner(inps[SWEEP_N[0]], arm, max(SWEEP_N), "bf16", weights=base)
+            r = Runner(inps[SWEEP_N[0]], arm, max(SWEEP_N), "bf16", weights=base, variant=variant)
             base = r.dw
             for n in SWEEP_N:
                 r.bind(inps[n])
                 res = timed(r, steps, warmup)
                 counts, _ = r.routing_counts()
-                fig = schedule_figures(counts, r.shape, arm)
+                fig = schedule_figures(counts, r.shape, arm, r.q.qtip_moe_plan_schedule(r.plan))
                 ms = res["wall_s"] * 1e3 / steps
                 rec = {"arm": arm, "n": n, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
                        "stage_ms": {k: v / res["prof"]["n_forwards"] for k, v in res["prof"].items() if k != "n_forwards"},
@@ -223,6 +220,7 @@ def main():
     ap.add_argument("--workload", default="v4_decode_n32")
     ap.add_argument("--arm", choices=["auto", "gemv", "grouped"], default="auto")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
+    ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 default, 1 W16, 2 W8)")
     ap.add_argument("--cpu-sample", type=int, default=2, help="tokens the CPU oracle is timed on (0: skip)")
     ap.add_argument("--sweep", metavar="PATH", default=None)
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -244,25 +242,26 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
     if args.sweep:
-        run_sweep(args.sweep, args.steps, args.warmup)
+        run_sweep(args.sweep, args.steps, args.warmup, args.variant)
         return
 
     log(f"bench: drawing workload {args.workload}")
     inp = moe_inputs.make_workload(args.workload, seed=0)
     s = inp.shape
-    runner = Runner(inp, args.arm, s.n_tokens, args.out_dtype)
+    runner = Runner(inp, args.arm, s.n_tokens, args.out_dtype, variant=args.variant)
     runner.bind(inp)
     arm_code = runner.q.qtip_moe_select_arm(runner.plan, s.n_tokens)
     arm = "grouped" if arm_code == runner.q.QTIP_ARM_GROUPED else "gemv"
     log(runner.q.qtip_moe_engaged_line(runner.plan, s.n_tokens))
     res = timed(runner, args.steps, args.warmup)
     counts, n_tiles = runner.routing_counts()
+    sched = runner.q.qtip_moe_plan_schedule(runner.plan)
     runner.close()
 
     if res["wall_s"] <= 0 or res["prof"]["n_forwards"] <= 0:
         print("bench: no time or no profiled forwards recorded", file=sys.stderr)
         sys.exit(2)
-    fig = schedule_figures(counts, s, arm)
+    fig = schedule_figures(counts, s, arm, sched)
     nf = res["prof"]["n_forwards"]
     stage_ms = {k: v / nf for k, v in res["prof"].items() if k != "n_forwards"}
     ms_per_step = res["wall_s"] * 1e3 / args.steps
@@ -284,7 +283,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "experts": s.num_experts, "top_k": s.top_k, "hidden": s.hidden,
                    "inter": s.inter, "n_tokens": s.n_tokens, "routing": s.routing, "seed": 0, "arm": arm,
-                   "out_dtype": args.out_dtype},
+                   "out_dtype": args.out_dtype, "variant": sched["variant"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(args.workload, arm)},
         "cpu_baseline": cpu,
@@ -298,6 +297,7 @@ def main():
             "decode_units": fig["units"], "decodes": fig["decodes"],
             "gate_up_symbols_per_s": fig["symbols_sched"]["gate_up"] / gu_s,
             "gate_up_decode_valu_frac": fig["symbols_sched"]["gate_up"] / gu_s / DECODE_VALU_PEAK_SYMS,
+            "schedule": sched,
             "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "route_launches",
                                                          "combine_launches")},
             "kernel_source_sha": kernel_source_sha(),

@@ -86,7 +86,7 @@ typedef struct qtip_moe_desc {
   int32_t inter;        /* I: gate/up outputs and down inputs; multiple of 128 */
   int32_t max_tokens;   /* largest n a forward accepts (sizes the workspace), >= 1 */
   int32_t arm_override; /* QTIP_ARM_AUTO (predicate), _GEMV or _GROUPED (pins the arm) */
-  int32_t variant;      /* kernel variant; 0 = default.  Unknown: warning, default kept */
+  int32_t variant;      /* expert kernel variant 0/1/2 (qtip_moe_plan_schedule); unknown: warning, 0 kept */
   int32_t out_dtype;    /* QTIP_OUT_BF16 or QTIP_OUT_F32 */
   int32_t tile_m;       /* 0 = default (16); else 16, 32 or 64 */
 } qtip_moe_desc;
@@ -134,6 +134,15 @@ qtip_status qtip_moe_plan_destroy(qtip_moe_plan_t plan);
  * output pointer may be NULL. */
 qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m /*host*/, size_t* workspace_bytes /*host*/,
                                int32_t* min_tokens_grouped /*host*/);
+
+/* The expert-kernel schedule the plan launches.  variant: the plan's variant (1 = 16 waves
+ * per workgroup with 32 pairs per grouped decode and 2 per GEMV decode; 2 = 8 waves with 64
+ * and 4; 0 = per arm the faster of the two: 1 on the grouped arm, 2 on the GEMV arm).
+ * waves_per_workgroup[2] (host): {grouped arm, GEMV arm}; pairs_per_decode_*: how many binned
+ * pairs share one decode of an expert's rows on each arm.  Any output pointer may be NULL. */
+qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t* variant /*host*/,
+                                   int32_t* waves_per_workgroup /*host [2]*/,
+                                   int32_t* pairs_per_decode_grouped /*host*/, int32_t* pairs_per_decode_gemv /*host*/);
 
 /* The arm a forward of n tokens takes: the override if one is set, else the closed-form
  * predicate.  Returns QTIP_ARM_GEMV or QTIP_ARM_GROUPED, or -1 for a bad plan/n. */

@@ -135,3 +135,22 @@ def test_forward_rejects_empty_and_oversized_batches_on_device():
             q.qtip_moe_forward(layer.plan, layer.w, 256, 256, n, out, layer.ws, layer.ws.numel())
         assert ei.value.status == q.QTIP_ERR_INVALID_CONFIG
     layer.close()
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("arm", [q.QTIP_ARM_GEMV, q.QTIP_ARM_GROUPED])
+def test_kernel_variants_full_parity(variant, arm):
+    """Both kernel configurations (16 waves / 32-pair decodes, 8 waves / 64-pair decodes) on a
+    batch whose experts need several decodes per unit on either arm."""
+    inp = moe_inputs.make_inputs(MID, seed=8, n_tokens=260)
+    say(f"forward variant={variant} arm={arm}")
+    s = inp.shape
+    layer = Layer(inp, arm=arm)
+    q.qtip_moe_plan_destroy(layer.plan)
+    layer.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, 260, arm, variant,
+                                             q.QTIP_OUT_F32, 0), 0)
+    got = layer.forward(inp)
+    layer.close()
+    ref = moe.moe_forward(inp)
+    assert ref["bins"]["counts"].max() > 64
+    check(got, ref, "f32")

@@ -61,6 +61,7 @@ _SIGS = {
     "qtip_moe_plan_destroy": (_I32, [_P]),
     "qtip_moe_plan_info": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_I32)]),
     "qtip_moe_select_arm": (_I32, [_P, _I32]),
+    "qtip_moe_plan_schedule": (_I32, [_P] + [ctypes.POINTER(_I32)] * 4),
     "qtip_fill_woken_experts": (ctypes.c_double, [_I32, _I32, _I32]),
     "qtip_fill_pairs_per_woken_expert": (ctypes.c_double, [_I32, _I32, _I32]),
     "qtip_fill_select_grouped": (_I32, [_I32, _I32, _I32, _I32]),
@@ -163,6 +164,15 @@ def qtip_moe_plan_info(plan: int) -> dict:
     tm, mt, ws = _I32(), _I32(), ctypes.c_size_t()
     _check("qtip_moe_plan_info", lib().qtip_moe_plan_info(plan, ctypes.byref(tm), ctypes.byref(ws), ctypes.byref(mt)))
     return {"tile_m": tm.value, "workspace_bytes": ws.value, "min_tokens_grouped": mt.value}
+
+
+def qtip_moe_plan_schedule(plan: int) -> dict:
+    variant, g, m = _I32(), _I32(), _I32()
+    waves = (_I32 * 2)()
+    _check("qtip_moe_plan_schedule", lib().qtip_moe_plan_schedule(plan, ctypes.byref(variant), waves,
+                                                                  ctypes.byref(g), ctypes.byref(m)))
+    return {"variant": variant.value, "waves_grouped": waves[0], "waves_gemv": waves[1],
+            "pairs_per_decode_grouped": g.value, "pairs_per_decode_gemv": m.value}
 
 
 def qtip_moe_select_arm(plan: int, n_tokens: int) -> int:

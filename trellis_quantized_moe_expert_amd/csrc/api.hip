@@ -24,6 +24,8 @@ struct qtip_moe_plan_s {
   qtip_moe_desc d;
   int32_t tile_m;
   int32_t device;  // -1: created from an arch name; the current device is used at call time
+  int32_t kvariant_grouped;  // expert kernel configuration launched on each arm (kVariantW16 / kVariantW8)
+  int32_t kvariant_gemv;
   int32_t min_tokens_grouped;
   size_t ws_bytes;
   qtip_moe_stats stats;
@@ -53,6 +55,10 @@ inline hipError_t prof_mark(qtip_moe_plan_s* p, int b, hipStream_t st) {
 
 namespace {
 
+// The default variant takes, per arm, the configuration measured fastest on MI355X: 16 waves
+// with 32 pairs per decode on the grouped arm, 8 waves with 4 pairs per decode on the GEMV arm.
+constexpr int kDefaultGroupedVariant = kVariantW16;
+constexpr int kDefaultGemvVariant = kVariantW8;
 thread_local std::string g_detail;
 
 qtip_status fail(qtip_status s, const std::string& what) {
@@ -160,9 +166,9 @@ qtip_status ensure_device(qtip_moe_plan_t plan, hipStream_t stream, int* dev_out
   return QTIP_OK;
 }
 
-int persistent_grid(int dev, size_t max_tasks) {
+int persistent_grid(int dev, size_t max_tasks, int waves) {
   const size_t cus = (size_t)g_cu_count[dev].load(std::memory_order_acquire);
-  size_t need = (max_tasks + kExpertWaves - 1) / kExpertWaves;
+  size_t need = (max_tasks + waves - 1) / waves;
   if (need < 1) need = 1;
   return (int)(need < cus ? need : cus);
 }
@@ -234,12 +240,17 @@ qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc, const char* gcn_ar
   if (!arch_is_supported(gcn_arch_name))
     return fail(QTIP_ERR_NOT_SUPPORTED, std::string("arch '") + (gcn_arch_name ? gcn_arch_name : "(null)") +
                                             "' is not supported; this library carries gfx950 code only");
-  if (desc->variant != 0)
+  int32_t variant = desc->variant;
+  if (variant < 0 || variant >= kVariantCount) {
     std::fprintf(stderr, "qtip_moe: unknown kernel variant %d; keeping the default (0)\n", desc->variant);
+    variant = 0;
+  }
   auto* p = new (std::nothrow) qtip_moe_plan_s{};
   if (!p) return fail(QTIP_ERR_INVALID_ARG, "out of host memory");
   p->d = *desc;
-  p->d.variant = 0;
+  p->d.variant = variant;
+  p->kvariant_grouped = variant == kVariantDefault ? kDefaultGroupedVariant : variant;
+  p->kvariant_gemv = variant == kVariantDefault ? kDefaultGemvVariant : variant;
   p->d.tile_m = tm;
   p->tile_m = tm;
   p->device = -1;
@@ -277,6 +288,19 @@ qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m, size_t* wo
   if (tile_m) *tile_m = plan->tile_m;
   if (workspace_bytes) *workspace_bytes = plan->ws_bytes;
   if (min_tokens_grouped) *min_tokens_grouped = plan->min_tokens_grouped;
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t* variant, int32_t* waves_per_workgroup,
+                                   int32_t* pairs_per_decode_grouped, int32_t* pairs_per_decode_gemv) {
+  if (!plan) return fail(QTIP_ERR_INVALID_ARG, "plan is NULL");
+  if (variant) *variant = plan->d.variant;
+  if (waves_per_workgroup) {
+    waves_per_workgroup[0] = expert_waves(plan->kvariant_grouped);
+    waves_per_workgroup[1] = expert_waves(plan->kvariant_gemv);
+  }
+  if (pairs_per_decode_grouped) *pairs_per_decode_grouped = expert_pairs_per_decode(plan->kvariant_grouped, kArmGrouped);
+  if (pairs_per_decode_gemv) *pairs_per_decode_gemv = expert_pairs_per_decode(plan->kvariant_gemv, kArmGemv);
   return QTIP_OK;
 }
 
@@ -357,8 +381,9 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
   p.n_act_rows = n_rows_a;
   p.out = y;
   p.n_out_rows = n_rows_a;
-  const int grid = persistent_grid(dev, (size_t)n_units * (rows / kRowsPerTask));
-  hipError_t e = launch_expert(kModeSingle, arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv, p, grid, st);
+  const int kv = arm == QTIP_ARM_GROUPED ? plan->kvariant_grouped : plan->kvariant_gemv;
+  const int grid = persistent_grid(dev, (size_t)n_units * (rows / kRowsPerTask), expert_waves(kv));
+  hipError_t e = launch_expert(kModeSingle, arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv, kv, p, grid, st);
   if (e != hipSuccess) return hip_fail(e, "expert kernel launch");
   if (arm == QTIP_ARM_GROUPED) plan->stats.grouped_launches++; else plan->stats.gemv_launches++;
   return QTIP_OK;
@@ -431,7 +456,9 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
   gu.n_act_rows = n_tokens;
   gu.out = h;
   gu.n_out_rows = P;
-  e = launch_expert(kModeGateUp, karm, gu, persistent_grid(dev, max_units * (d.inter / kRowsPerTask)), st);
+  const int kv = karm == kArmGrouped ? plan->kvariant_grouped : plan->kvariant_gemv;
+  const int waves = expert_waves(kv);
+  e = launch_expert(kModeGateUp, karm, kv, gu, persistent_grid(dev, max_units * (d.inter / kRowsPerTask), waves), st);
   if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
   if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
 
@@ -451,7 +478,7 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
   dn.out = y;
   dn.out_row_map = sorted_pair;
   dn.n_out_rows = P;
-  e = launch_expert(kModeSingle, karm, dn, persistent_grid(dev, max_units * (d.hidden / kRowsPerTask)), st);
+  e = launch_expert(kModeSingle, karm, kv, dn, persistent_grid(dev, max_units * (d.hidden / kRowsPerTask), waves), st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
   if (karm == kArmGrouped) plan->stats.grouped_launches += 2; else plan->stats.gemv_launches += 2;

@@ -72,25 +72,19 @@ __device__ inline uint32_t lut_pair(const uint16_t* lut, uint32_t s0, uint32_t s
   return (uint32_t)lut[s0] | ((uint32_t)lut[s1] << 16);
 }
 
-// `win` holds 30 valid stream bits: bits [2t, 2t+16) are the state of symbol t, t = 0..7.
-// Returns the 8 bf16 weights packed two per dword (symbol 2q low, 2q+1 high).
-__device__ inline u32x4 decode8(const uint16_t* lut, uint32_t win) {
-  u32x4 r;
-  r[0] = lut_pair(lut, win & 0xFFFFu, (win >> 2) & 0xFFFFu);
-  r[1] = lut_pair(lut, (win >> 4) & 0xFFFFu, (win >> 6) & 0xFFFFu);
-  r[2] = lut_pair(lut, (win >> 8) & 0xFFFFu, (win >> 10) & 0xFFFFu);
-  r[3] = lut_pair(lut, (win >> 12) & 0xFFFFu, (win >> 14) & 0xFFFFu);
-  return r;
-}
-
-// Window of step s (symbols 8s..8s+7 of the lane's 32-symbol run): d0, d1 are the run's
-// two dwords, la the look-ahead dword (the following 16 symbols).
-__device__ inline uint32_t run_window(int s, uint32_t d0, uint32_t d1, uint32_t la) {
-  switch (s) {
-    case 0: return d0;
-    case 1: return __builtin_amdgcn_alignbit(d1, d0, 16);
-    case 2: return d1;
-    default: return __builtin_amdgcn_alignbit(la, d1, 16);
+// Decode 16 consecutive symbols of a run.  `lo` holds the stream bits of the 16 symbols,
+// `hi` the 16 symbols after them (the look-ahead).  The 32-bit window alignbit(hi, lo, 2t)
+// holds the state of symbol t in its low half and of symbol t+8 in its high half, so one
+// funnel shift serves two symbols.  Returns the 8 bf16 weights of symbols 0..7 in `first`
+// and of symbols 8..15 in `second`, packed two per dword (lower symbol in the low half).
+__device__ inline void decode16(const uint16_t* lut, uint32_t lo, uint32_t hi, u32x4& first, u32x4& second) {
+  uint32_t x[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) x[t] = (t == 0) ? lo : __builtin_amdgcn_alignbit(hi, lo, 2 * t);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    first[q] = lut_pair(lut, x[2 * q] & 0xFFFFu, x[2 * q + 1] & 0xFFFFu);
+    second[q] = lut_pair(lut, x[2 * q] >> 16, x[2 * q + 1] >> 16);
   }
 }
 
@@ -164,7 +158,38 @@ __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int
   }
 }
 
-template <int MODE>
+// Loads the A fragments of one K block: for each 16-pair row block m < NS, the 16 bytes of
+// each of the 4 MFMA steps (K slots 8g..8g+7 <-> inputs kb*128 + 32g + 8s + 0..7).  Loads
+// are unconditional (rows past the unit read a valid row and are discarded later), so the
+// compiler can count outstanding memory operations exactly.
+template <int NS>
+__device__ inline void load_a_block(u32x4 (&a)[NS][4], const uint16_t* const (&abase)[NS], int kb) {
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) a[m][st] = *reinterpret_cast<const u32x4*>(abase[m] + kb * kKBlock + st * 8);
+  }
+}
+
+// Activation row pointers of this lane for NS entries; entry m is the binned position
+// first + m*stride.  Positions past the unit, and rows out of range, read the unit's first
+// row (always valid); their results are never stored.
+template <int NS>
+__device__ inline void act_rows(const ExpertParams& p, const Unit& un, int first, int stride, int g,
+                                const uint16_t* (&base)[NS]) {
+  int r_first = act_row(p, un.start);
+  if (r_first < 0) r_first = 0;
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+    const int pi = first + m * stride;
+    int ar = (pi < un.len) ? act_row(p, un.start + pi) : -1;
+    if (ar < 0) ar = r_first;
+    base[m] = p.act + (size_t)ar * p.cols + g * 32;
+  }
+}
+
+// Grouped arm: NS row blocks of 16 pairs share one decode of 16 output rows.
+template <int MODE, int NS>
 __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -172,47 +197,46 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
   const int row_bytes = p.cols >> 2;
   const int kblocks = p.cols / kKBlock;
   const uint8_t* row0 = p.codes0 + ((size_t)un.e * p.rows + r) * row_bytes;
-  const uint8_t* row1 = (MODE == kModeGateUp) ? p.codes1 + ((size_t)un.e * p.rows + r) * row_bytes : nullptr;
-  const int nsub = (un.len + 15) >> 4;
+  const uint8_t* row1 = (MODE == kModeGateUp) ? p.codes1 + ((size_t)un.e * p.rows + r) * row_bytes : row0;
 
-  // A operand rows of this lane (row i = lane%16 of each 16-pair block)
-  const uint16_t* abase[4];
-  bool aval[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int pi = m * 16 + j;
-    int ar = (pi < un.len) ? act_row(p, un.start + pi) : -1;
-    aval[m] = ar >= 0;
-    abase[m] = p.act + (size_t)(ar >= 0 ? ar : 0) * p.cols + g * 32;
-  }
+  const uint16_t* abase[NS];  // A operand row i = lane%16 of each 16-pair block
+  act_rows<NS>(p, un, j, 16, g, abase);
 
-  f32x4 acc0[4], acc1[4];
+  f32x4 acc0[NS], acc1[NS];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < NS; ++m) {
     acc0[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // Per block: the block's activations are requested first, then the next block's codes
+  // (the block after the last wraps to block 0 and is not used), so waiting for the
+  // activations never waits for those codes (memory counters retire in order) and the
+  // codes have the whole block's decode to arrive.
+  RunCodes n0 = load_run(row0, g * 8, row_bytes);
+  RunCodes n1 = (MODE == kModeGateUp) ? load_run(row1, g * 8, row_bytes) : n0;
   for (int kb = 0; kb < kblocks; ++kb) {
-    const int ob = kb * 32 + g * 8;
-    const RunCodes c0 = load_run(row0, ob, row_bytes);
-    RunCodes c1{};
-    if (MODE == kModeGateUp) c1 = load_run(row1, ob, row_bytes);
+    u32x4 a[NS][4];
+    load_a_block<NS>(a, abase, kb);
+    const RunCodes c0 = n0, c1 = n1;
+    const int ob = (kb + 1 < kblocks ? kb + 1 : 0) * 32 + g * 8;
+    n0 = load_run(row0, ob, row_bytes);
+    if (MODE == kModeGateUp) n1 = load_run(row1, ob, row_bytes);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 b0 = decode8(lut, run_window(s, c0.d0, c0.d1, c0.la));
-      u32x4 b1{};
-      if (MODE == kModeGateUp) b1 = decode8(lut, run_window(s, c1.d0, c1.d1, c1.la));
+    for (int h = 0; h < 2; ++h) {
+      u32x4 b0[2], b1[2];
+      decode16(lut, h ? c0.d1 : c0.d0, h ? c0.la : c0.d1, b0[0], b0[1]);
+      if (MODE == kModeGateUp) decode16(lut, h ? c1.d1 : c1.d0, h ? c1.la : c1.d1, b1[0], b1[1]);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (m < nsub) {
-          u32x4 a = u32x4{0u, 0u, 0u, 0u};
-          if (aval[m]) a = *reinterpret_cast<const u32x4*>(abase[m] + kb * kKBlock + s * 8);
-          acc0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                            __builtin_bit_cast(bf16x8, b0), acc0[m], 0, 0, 0);
+      for (int hs = 0; hs < 2; ++hs) {
+        const int st = 2 * h + hs;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+          acc0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
+                                                            __builtin_bit_cast(bf16x8, b0[hs]), acc0[m], 0, 0, 0);
           if (MODE == kModeGateUp)
-            acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                              __builtin_bit_cast(bf16x8, b1), acc1[m], 0, 0, 0);
+            acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
+                                                              __builtin_bit_cast(bf16x8, b1[hs]), acc1[m], 0, 0, 0);
         }
       }
     }
@@ -222,18 +246,17 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
   const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
   const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m < nsub) {
+  for (int m = 0; m < NS; ++m) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int pi = m * 16 + 4 * g + t;
-        if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][t], acc1[m][t], s0, s1);
-      }
+    for (int t = 0; t < 4; ++t) {
+      const int pi = m * 16 + 4 * g + t;
+      if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][t], acc1[m][t], s0, s1);
     }
   }
 }
 
-template <int MODE>
+// GEMV arm: NQ pairs share one decode of 16 output rows; VALU bf16 dot products.
+template <int MODE, int NQ>
 __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -241,79 +264,112 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
   const int row_bytes = p.cols >> 2;
   const int kblocks = p.cols / kKBlock;
   const uint8_t* row0 = p.codes0 + ((size_t)un.e * p.rows + r) * row_bytes;
-  const uint8_t* row1 = (MODE == kModeGateUp) ? p.codes1 + ((size_t)un.e * p.rows + r) * row_bytes : nullptr;
-  const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
-  const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
+  const uint8_t* row1 = (MODE == kModeGateUp) ? p.codes1 + ((size_t)un.e * p.rows + r) * row_bytes : row0;
 
-  for (int q0 = 0; q0 < un.len; q0 += kGemvPairs) {
-    const int nq = min(kGemvPairs, un.len - q0);
-    const uint16_t* xb[kGemvPairs];
-    bool xv[kGemvPairs];
+  const uint16_t* xb[NQ];  // every lane of group g reads the same 16 bytes of pair q
+  act_rows<NQ>(p, un, 0, 1, g, xb);
+  float acc0[NQ], acc1[NQ];
 #pragma unroll
-    for (int q = 0; q < kGemvPairs; ++q) {
-      const int ar = (q < nq) ? act_row(p, un.start + q0 + q) : -1;
-      xv[q] = ar >= 0;
-      xb[q] = p.act + (size_t)(ar >= 0 ? ar : 0) * p.cols + g * 32;
-    }
-    float acc0[kGemvPairs], acc1[kGemvPairs];
-#pragma unroll
-    for (int q = 0; q < kGemvPairs; ++q) acc0[q] = acc1[q] = 0.f;
+  for (int q = 0; q < NQ; ++q) acc0[q] = acc1[q] = 0.f;
 
-    for (int kb = 0; kb < kblocks; ++kb) {
-      const int ob = kb * 32 + g * 8;
-      const RunCodes c0 = load_run(row0, ob, row_bytes);
-      RunCodes c1{};
-      if (MODE == kModeGateUp) c1 = load_run(row1, ob, row_bytes);
+  RunCodes n0 = load_run(row0, g * 8, row_bytes);
+  RunCodes n1 = (MODE == kModeGateUp) ? load_run(row1, g * 8, row_bytes) : n0;
+  for (int kb = 0; kb < kblocks; ++kb) {
+    u32x4 x[NQ][4];
+    load_a_block<NQ>(x, xb, kb);
+    const RunCodes c0 = n0, c1 = n1;
+    const int ob = (kb + 1 < kblocks ? kb + 1 : 0) * 32 + g * 8;
+    n0 = load_run(row0, ob, row_bytes);
+    if (MODE == kModeGateUp) n1 = load_run(row1, ob, row_bytes);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 b0 = decode8(lut, run_window(s, c0.d0, c0.d1, c0.la));
-        u32x4 b1{};
-        if (MODE == kModeGateUp) b1 = decode8(lut, run_window(s, c1.d0, c1.d1, c1.la));
+    for (int h = 0; h < 2; ++h) {
+      u32x4 b0[2], b1[2];
+      decode16(lut, h ? c0.d1 : c0.d0, h ? c0.la : c0.d1, b0[0], b0[1]);
+      if (MODE == kModeGateUp) decode16(lut, h ? c1.d1 : c1.d0, h ? c1.la : c1.d1, b1[0], b1[1]);
 #pragma unroll
-        for (int q = 0; q < kGemvPairs; ++q) {
-          if (q < nq && xv[q]) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(xb[q] + kb * kKBlock + s * 8);
-            acc0[q] = dot8(b0, x, acc0[q]);
-            if (MODE == kModeGateUp) acc1[q] = dot8(b1, x, acc1[q]);
-          }
+      for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          acc0[q] = dot8(b0[hs], x[q][2 * h + hs], acc0[q]);
+          if (MODE == kModeGateUp) acc1[q] = dot8(b1[hs], x[q][2 * h + hs], acc1[q]);
         }
       }
     }
-    // sum the four lane groups (lanes j, j+16, j+32, j+48 hold one row's partial sums)
+  }
+  const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
+  const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
+  // sum the four lane groups (lanes j, j+16, j+32, j+48 hold one row's partial sums)
 #pragma unroll
-    for (int q = 0; q < kGemvPairs; ++q) {
-      float a0 = acc0[q];
-      a0 += __shfl_xor(a0, 16, 64);
-      a0 += __shfl_xor(a0, 32, 64);
-      float a1 = 0.f;
-      if (MODE == kModeGateUp) {
-        a1 = acc1[q];
-        a1 += __shfl_xor(a1, 16, 64);
-        a1 += __shfl_xor(a1, 32, 64);
+  for (int q = 0; q < NQ; ++q) {
+    float a0 = acc0[q];
+    a0 += __shfl_xor(a0, 16, 64);
+    a0 += __shfl_xor(a0, 32, 64);
+    float a1 = 0.f;
+    if (MODE == kModeGateUp) {
+      a1 = acc1[q];
+      a1 += __shfl_xor(a1, 16, 64);
+      a1 += __shfl_xor(a1, 32, 64);
+    }
+    if (q < un.len && (q & 3) == g) epilogue_store<MODE>(p, un, r, q, a0, a1, s0, s1);
+  }
+}
+
+// Kernel configurations (the plan's `variant`): waves per workgroup, pairs per decode on the
+// grouped arm (in 16-pair MFMA row blocks) and on the GEMV arm.  Fewer waves leave each wave
+// more registers for activation and code prefetch; more pairs per decode mean fewer decodes.
+template <int WAVES, int NSUB, int GPAIRS>
+struct ExpertCfg {
+  static constexpr int kWaves = WAVES, kNSub = NSUB, kGPairs = GPAIRS;
+};
+using CfgW16 = ExpertCfg<16, 2, 2>;
+using CfgW8 = ExpertCfg<8, 4, 4>;
+
+// A unit may hold more pairs than one decode serves; it is then processed in chunks, each
+// chunk decoding the rows again.  Each chunk runs the body specialised for its exact number
+// of 16-pair row blocks (grouped) or pairs (GEMV), chosen by a wave-uniform switch.
+template <int MODE, int ARM, class CFG>
+__device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
+  constexpr int kChunk = (ARM == kArmGrouped) ? CFG::kNSub * 16 : CFG::kGPairs;
+  static_assert(CFG::kNSub >= 1 && CFG::kNSub <= 4 && CFG::kGPairs >= 1 && CFG::kGPairs <= 4, "config");
+  for (int c0 = 0; c0 < un.len; c0 += kChunk) {
+    const Unit part{un.e, un.start + c0, min(kChunk, un.len - c0)};
+    if (ARM == kArmGrouped) {
+      switch ((part.len + 15) >> 4) {
+        case 1: task_grouped<MODE, 1>(p, lut, part, r0); break;
+        case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1)>(p, lut, part, r0); break;
+        case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1)>(p, lut, part, r0); break;
+        default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1)>(p, lut, part, r0); break;
       }
-      if (q < nq && (q & 3) == g) epilogue_store<MODE>(p, un, r, q0 + q, a0, a1, s0, s1);
+    } else {
+      switch (part.len) {
+        case 1: task_gemv<MODE, 1>(p, lut, part, r0); break;
+        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1)>(p, lut, part, r0); break;
+        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1)>(p, lut, part, r0); break;
+        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1)>(p, lut, part, r0); break;
+      }
     }
   }
 }
 
-template <int MODE, int ARM>
-__global__ __launch_bounds__(kExpertThreads, 1) void expert_kernel(ExpertParams p) {
+template <int MODE, int ARM, class CFG>
+__global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
   fill_lut(lut_s, p.lut);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = p.n_units_dev ? __builtin_amdgcn_readfirstlane(*p.n_units_dev) : p.n_units_host;
   const int nblocks = p.rows / kRowsPerTask;
   const long total = (long)n_units * nblocks;
-  const long stride = (long)gridDim.x * kExpertWaves;
-  for (long task = (long)blockIdx.x * kExpertWaves + wave; task < total; task += stride) {
+  // Each workgroup (one per CU) owns a contiguous, equal share of the tasks (+-1), so the
+  // CUs finish together; its waves take the share's tasks in turn, so neighbouring waves
+  // work on neighbouring row blocks of the same unit and share its activation rows in L1.
+  const long share_lo = total * blockIdx.x / gridDim.x;
+  const long share_hi = total * (blockIdx.x + 1) / gridDim.x;
+  for (long task = share_lo + wave; task < share_hi; task += CFG::kWaves) {
     const int u = (int)(task / nblocks);
     const int nb = (int)(task - (long)u * nblocks);
     Unit un;
     if (!read_unit(p, u, un)) continue;
-    if (ARM == kArmGrouped)
-      task_grouped<MODE>(p, lut_s, un, nb * kRowsPerTask);
-    else
-      task_gemv<MODE>(p, lut_s, un, nb * kRowsPerTask);
+    run_task<MODE, ARM, CFG>(p, lut_s, un, nb * kRowsPerTask);
   }
 }
 
@@ -348,16 +404,31 @@ __global__ void witness_kernel(int32_t* out) { out[0] = kWitnessValue; }
 
 }  // namespace
 
-hipError_t launch_expert(int mode, int arm, const ExpertParams& p, int grid, hipStream_t stream) {
-  const dim3 g(grid), b(kExpertThreads);
+template <class CFG>
+static void launch_cfg(int mode, int arm, const ExpertParams& p, int grid, hipStream_t stream) {
+  const dim3 g(grid), b(CFG::kWaves * 64);
   if (mode == kModeGateUp && arm == kArmGrouped)
-    hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped>), g, b, 0, stream, p);
+    hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG>), g, b, 0, stream, p);
   else if (mode == kModeGateUp)
-    hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv>), g, b, 0, stream, p);
+    hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG>), g, b, 0, stream, p);
   else if (arm == kArmGrouped)
-    hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped>), g, b, 0, stream, p);
+    hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped, CFG>), g, b, 0, stream, p);
   else
-    hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGemv>), g, b, 0, stream, p);
+    hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGemv, CFG>), g, b, 0, stream, p);
+}
+
+int expert_waves(int variant) { return variant == kVariantW8 ? CfgW8::kWaves : CfgW16::kWaves; }
+
+int expert_pairs_per_decode(int variant, int arm) {
+  if (variant == kVariantW8) return arm == kArmGrouped ? CfgW8::kNSub * 16 : CfgW8::kGPairs;
+  return arm == kArmGrouped ? CfgW16::kNSub * 16 : CfgW16::kGPairs;
+}
+
+hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, hipStream_t stream) {
+  if (variant == kVariantW8)
+    launch_cfg<CfgW8>(mode, arm, p, grid, stream);
+  else
+    launch_cfg<CfgW16>(mode, arm, p, grid, stream);
   return hipGetLastError();
 }
 

@@ -9,14 +9,15 @@
 namespace qtip {
 
 constexpr int kLutEntries = 65536;     // 16-bit trellis state -> one LUT entry
-constexpr int kExpertThreads = 1024;   // 16 wave64 per workgroup; the LUT fills 128 KiB of LDS,
-constexpr int kExpertWaves = 16;       // so one workgroup per CU is resident
+// The LUT fills 128 KiB of LDS, so one expert workgroup per CU is resident; the kernel
+// variant fixes its size (16 or 8 wave64).
+enum ExpertVariant { kVariantDefault = 0, kVariantW16 = 1, kVariantW8 = 2, kVariantCount = 3 };
+constexpr int kExpertWaves = 16;       // waves of the binning workgroup
 constexpr int kRowsPerTask = 16;       // output rows per wave task (the MFMA N)
 constexpr int kKBlock = 128;           // inputs per K block: 4 lane groups x 32-symbol runs
 constexpr int kUnitMaxPairs = 64;      // pairs sharing one decode (4 MFMA row blocks of 16)
-constexpr int kGemvPairs = 8;          // pairs per decode on the GEMV arm (VALU accumulators)
 constexpr int kRouteWaves = 4;         // tokens per route workgroup (one wave each)
-constexpr int kBinThreads = 1024;      // binning runs in one workgroup
+constexpr int kBinThreads = 1024;      // binning runs in one workgroup (16 waves)
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kWitnessValue = 0x950950;
@@ -46,7 +47,10 @@ struct ExpertParams {
 enum ExpertMode { kModeGateUp = 0, kModeSingle = 1 };
 enum ExpertArm { kArmGemv = 0, kArmGrouped = 1 };
 
-hipError_t launch_expert(int mode, int arm, const ExpertParams& p, int grid, hipStream_t stream);
+// `variant` must be kVariantW16 or kVariantW8 (the plan resolves kVariantDefault).
+hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, hipStream_t stream);
+int expert_waves(int variant);
+int expert_pairs_per_decode(int variant, int arm);
 
 hipError_t launch_route_topk(const float* logits, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
                              float* topk_w, hipStream_t stream);
