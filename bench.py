@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -128,18 +129,23 @@ def schedule_figures(counts, shape, arm, sched):
     E, H, I = shape.num_experts, shape.hidden, shape.inter
     woken = int((counts > 0).sum())
     per_expert_bytes = {"gate_up": 2 * I * H // 4 + 2 * I * 2, "down": H * I // 4 + H * 2}
-    per = sched["pairs_per_decode_grouped"] if arm == "grouped" else sched["pairs_per_decode_gemv"]
     units = [(c + 63) // 64 for c in counts.tolist()]      # the router's units hold <= 64 pairs
-    decodes = 0
-    for c in counts.tolist():
-        while c > 0:
-            L = min(64, c)
-            decodes += (L + per - 1) // per
-            c -= L
-    return {"woken": woken, "units": int(sum(units)), "decodes": int(decodes),
+
+    def decodes_for(per):
+        d = 0
+        for c in counts.tolist():
+            while c > 0:
+                L = min(64, c)
+                d += (L + per - 1) // per
+                c -= L
+        return d
+
+    dec = {"gate_up": decodes_for(sched["gate_up"]["pairs_per_decode"]),
+           "down": decodes_for(sched["down"]["pairs_per_decode"])}
+    return {"woken": woken, "units": int(sum(units)), "decodes": dec,
             "bytes": {k: woken * v for k, v in per_expert_bytes.items()},
             "symbols_min": {"gate_up": woken * 2 * I * H, "down": woken * H * I},
-            "symbols_sched": {"gate_up": decodes * 2 * I * H, "down": decodes * H * I},
+            "symbols_sched": {"gate_up": dec["gate_up"] * 2 * I * H, "down": dec["down"] * H * I},
             "max_count": int(np.max(counts))}
 
 
@@ -156,6 +162,44 @@ def read_traffic(workload, arm):
     if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
         return None       # counters were taken on another version of the kernel
     return ent.get("hbm_bytes_per_launch")
+
+
+def summarize_traffic(fetch_csv, write_csv, workload, arm, command):
+    """HBM bytes per launch of the gate+up kernel from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch), each scaled by what the counter reads for the 1 GiB device copy
+    that --calibrate-copy runs in the same process.  Writes an entry of profiles/traffic.json."""
+    import csv
+    copy_bytes = 1 << 30
+
+    def read(path, counter):
+        calib, vals = 0.0, []
+        mode_digit = "1" if arm == "grouped" else "0"
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name:
+                calib = max(calib, v)
+            elif re.search(rf"expert_kernel<0, {mode_digit}[,>]", name):
+                vals.append(v)
+        if calib <= 0 or not vals:
+            raise SystemExit(f"{path}: no calibration copy or no gate+up dispatch for {counter}")
+        return sum(vals) / len(vals), copy_bytes / (calib * 1024.0), len(vals)
+
+    fetch, f_fetch, nf = read(fetch_csv, "FETCH_SIZE")
+    write, f_write, nw = read(write_csv, "WRITE_SIZE")
+    ent = {"kernel_source_sha": kernel_source_sha(), "fetch_kib": fetch, "write_kib": write,
+           "fetch_factor": f_fetch, "write_factor": f_write, "dispatches": [nf, nw],
+           "hbm_bytes_per_launch": fetch * 1024.0 * f_fetch + write * 1024.0 * f_write, "command": command}
+    rec = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    rec[f"{workload}/{arm}/gate_up"] = ent
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    log(json.dumps(ent))
 
 
 def cpu_baseline(inp, n_sample):
@@ -185,26 +229,28 @@ def calibrate_copy():
     del a, b
 
 
-def run_sweep(path, steps, warmup, variant=0):
+def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=None):
     import moe_inputs
     shape = moe_inputs.WORKLOADS["v4_decode_n32"]
     log("sweep: drawing V4-shaped weights once")
-    inps = moe_inputs.make_inputs_multi(shape, SWEEP_N, seed=0)
+    n_list = n_list or SWEEP_N
+    inps = moe_inputs.make_inputs_multi(shape, n_list, seed=0)
     base = None
-    with open(path, "w") as f:
-        for arm in ("gemv", "grouped"):
-            r = Runner(inps[SWEEP_N[0]], arm, max(SWEEP_N), "bf16", weights=base, variant=variant)
+    with open(path, "a") as f:
+        for arm in arms:
+            r = Runner(inps[n_list[0]], arm, max(n_list), "bf16", weights=base, variant=variant)
             base = r.dw
-            for n in SWEEP_N:
+            for n in n_list:
                 r.bind(inps[n])
                 res = timed(r, steps, warmup)
                 counts, _ = r.routing_counts()
-                fig = schedule_figures(counts, r.shape, arm, r.q.qtip_moe_plan_schedule(r.plan))
+                sched = r.q.qtip_moe_plan_schedule(r.plan, n)
+                fig = schedule_figures(counts, r.shape, arm, sched)
                 ms = res["wall_s"] * 1e3 / steps
-                rec = {"arm": arm, "n": n, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+                rec = {"arm": arm, "n": n, "variant_requested": variant, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
                        "stage_ms": {k: v / res["prof"]["n_forwards"] for k, v in res["prof"].items() if k != "n_forwards"},
                        "launches": {k: res["stats"][k] for k in ("gemv_launches", "grouped_launches")},
-                       "woken": fig["woken"], "decodes": fig["decodes"],
+                       "woken": fig["woken"], "decodes": fig["decodes"], "schedule": sched,
                        "predicate_grouped": r.q.qtip_fill_select_grouped(n, 6, 256, 16)}
                 f.write(json.dumps(rec) + "\n")
                 f.flush()
@@ -220,12 +266,21 @@ def main():
     ap.add_argument("--workload", default="v4_decode_n32")
     ap.add_argument("--arm", choices=["auto", "gemv", "grouped"], default="auto")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
-    ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 default, 1 W16, 2 W8)")
+    ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 = the plan's choice, 1..5 fixed; see qtip_moe_plan_schedule)")
     ap.add_argument("--cpu-sample", type=int, default=2, help="tokens the CPU oracle is timed on (0: skip)")
     ap.add_argument("--sweep", metavar="PATH", default=None)
+    ap.add_argument("--sweep-arms", default="gemv,grouped")
+    ap.add_argument("--sweep-n", default=None, help="comma-separated token counts (default: the fixed list)")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection files")
+    ap.add_argument("--traffic-command", default="", help="the profiling command, recorded with --traffic-from")
     args = ap.parse_args()
 
+    if args.traffic_from:
+        summarize_traffic(args.traffic_from[0], args.traffic_from[1], args.workload,
+                          "grouped" if args.arm == "grouped" else args.arm, args.traffic_command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -242,7 +297,8 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
     if args.sweep:
-        run_sweep(args.sweep, args.steps, args.warmup, args.variant)
+        n_list = [int(x) for x in args.sweep_n.split(",")] if args.sweep_n else None
+        run_sweep(args.sweep, args.steps, args.warmup, args.variant, tuple(args.sweep_arms.split(",")), n_list)
         return
 
     log(f"bench: drawing workload {args.workload}")
@@ -255,7 +311,7 @@ def main():
     log(runner.q.qtip_moe_engaged_line(runner.plan, s.n_tokens))
     res = timed(runner, args.steps, args.warmup)
     counts, n_tiles = runner.routing_counts()
-    sched = runner.q.qtip_moe_plan_schedule(runner.plan)
+    sched = runner.q.qtip_moe_plan_schedule(runner.plan, s.n_tokens)
     runner.close()
 
     if res["wall_s"] <= 0 or res["prof"]["n_forwards"] <= 0:
@@ -283,7 +339,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "experts": s.num_experts, "top_k": s.top_k, "hidden": s.hidden,
                    "inter": s.inter, "n_tokens": s.n_tokens, "routing": s.routing, "seed": 0, "arm": arm,
-                   "out_dtype": args.out_dtype, "variant": sched["variant"]},
+                   "out_dtype": args.out_dtype,
+                   "variant": {"gate_up": sched["gate_up"]["variant"], "down": sched["down"]["variant"]}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(args.workload, arm)},
         "cpu_baseline": cpu,

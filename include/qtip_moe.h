@@ -74,6 +74,11 @@ enum { QTIP_OUT_BF16 = 0, QTIP_OUT_F32 = 1 };
 #define QTIP_DECODE_REGIME_MAX_TOKENS 8
 /* Default m-tile height: the M of one bf16 MFMA (v_mfma_f32_16x16x32_bf16). */
 #define QTIP_DEFAULT_TILE_M 16
+/* The fill threshold re-derived for these kernels on MI355X.  The grouped arm decodes each
+ * expert once per up to 64 binned pairs (not once per m-tile), so tile fill does not amortise
+ * anything; the measured GEMV/grouped crossover lies between 4 and 8 tokens at V4 routing,
+ * i.e. at the decode-regime floor, which a threshold of 1 pair per woken expert reproduces. */
+#define QTIP_DEFAULT_DISPATCH_TILE_M 1
 /* One decode of an expert's weights is shared by up to this many binned pairs. */
 #define QTIP_UNIT_MAX_PAIRS 64
 /* Inputs per K block: H and I must be multiples of this; rows a multiple of 16. */
@@ -86,9 +91,14 @@ typedef struct qtip_moe_desc {
   int32_t inter;        /* I: gate/up outputs and down inputs; multiple of 128 */
   int32_t max_tokens;   /* largest n a forward accepts (sizes the workspace), >= 1 */
   int32_t arm_override; /* QTIP_ARM_AUTO (predicate), _GEMV or _GROUPED (pins the arm) */
-  int32_t variant;      /* expert kernel variant 0/1/2 (qtip_moe_plan_schedule); unknown: warning, 0 kept */
+  int32_t variant;      /* expert kernel configuration 1..5 for both passes, or 0 = chosen per arm,
+                           pass and n by the plan (qtip_moe_plan_schedule reports it);
+                           unknown: warning, 0 kept */
   int32_t out_dtype;    /* QTIP_OUT_BF16 or QTIP_OUT_F32 */
-  int32_t tile_m;       /* 0 = default (16); else 16, 32 or 64 */
+  int32_t tile_m;       /* m-tile height of the tile map: 0 = default (16, the MFMA M); else 16, 32, 64 */
+  int32_t dispatch_tile_m; /* the fill predicate's threshold in pairs per woken expert: 0 = the value
+                              re-derived for these gfx950 kernels (QTIP_DEFAULT_DISPATCH_TILE_M);
+                              16 reproduces the pages' sm80 gate; 1..1024 accepted */
 } qtip_moe_desc;
 
 typedef struct qtip_moe_plan_s* qtip_moe_plan_t;
@@ -130,28 +140,37 @@ qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc /*host*/, const cha
 qtip_status qtip_moe_plan_destroy(qtip_moe_plan_t plan);
 
 /* What the kernels will use: the m-tile height, the workspace bytes a forward needs at
- * max_tokens, and the smallest n for which the predicate selects the grouped arm.  Any
- * output pointer may be NULL. */
+ * max_tokens, and the smallest n for which the predicate (with the plan's dispatch_tile_m)
+ * selects the grouped arm.  Any output pointer may be NULL. */
 qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m /*host*/, size_t* workspace_bytes /*host*/,
                                int32_t* min_tokens_grouped /*host*/);
 
-/* The expert-kernel schedule the plan launches.  variant: the plan's variant (1 = 16 waves
- * per workgroup with 32 pairs per grouped decode and 2 per GEMV decode; 2 = 8 waves with 64
- * and 4; 0 = per arm the faster of the two: 1 on the grouped arm, 2 on the GEMV arm).
- * waves_per_workgroup[2] (host): {grouped arm, GEMV arm}; pairs_per_decode_*: how many binned
- * pairs share one decode of an expert's rows on each arm.  Any output pointer may be NULL. */
-qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t* variant /*host*/,
-                                   int32_t* waves_per_workgroup /*host [2]*/,
-                                   int32_t* pairs_per_decode_grouped /*host*/, int32_t* pairs_per_decode_gemv /*host*/);
+/* The expert-kernel schedule a forward of n tokens launches (the arm and, for each of the two
+ * expert passes, the kernel configuration and its shape): the pages' schedule query, so
+ * callers and benchmarks read what runs. */
+typedef struct qtip_moe_kernel_shape {
+  int32_t variant;             /* kernel configuration 1..5 actually launched */
+  int32_t waves_per_workgroup; /* wave64 per (persistent, one-per-CU) workgroup */
+  int32_t rows_per_task;       /* output rows each wave decodes per task (16, 32 or 64) */
+  int32_t pairs_per_decode;    /* binned pairs of one expert that share one decode of its rows */
+} qtip_moe_kernel_shape;
+typedef struct qtip_moe_schedule {
+  int32_t arm;                  /* QTIP_ARM_GEMV or QTIP_ARM_GROUPED */
+  int32_t tile_m;               /* m-tile height of the tile map and the predicate */
+  qtip_moe_kernel_shape gate_up; /* the fused gate+up pass */
+  qtip_moe_kernel_shape down;    /* the down pass */
+} qtip_moe_schedule;
+qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_moe_schedule* out /*host*/);
 
 /* The arm a forward of n tokens takes: the override if one is set, else the closed-form
- * predicate.  Returns QTIP_ARM_GEMV or QTIP_ARM_GROUPED, or -1 for a bad plan/n. */
+ * predicate with the plan's dispatch_tile_m.  Returns QTIP_ARM_GEMV or QTIP_ARM_GROUPED, or -1
+ * for a bad plan/n. */
 int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens);
 
 /* ---- closed-form fill model (m-tile page, "The cause is a threshold" and "The fix") --
  * Uniform routing of n tokens to k of E experts wakes E(1-(1-k/E)^n) experts on average;
  * pairs per woken expert = n k / that.  The grouped arm is selected iff n > 8 and pairs
- * per woken expert >= tile_m.  Pure host functions of their arguments. */
+ * per woken expert >= tile_m (the threshold).  Pure host functions of their arguments. */
 double qtip_fill_woken_experts(int32_t n, int32_t k, int32_t E);
 double qtip_fill_pairs_per_woken_expert(int32_t n, int32_t k, int32_t E);
 int32_t qtip_fill_select_grouped(int32_t n, int32_t k, int32_t E, int32_t tile_m); /* 1 / 0, -1 bad args */

@@ -29,7 +29,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_plan_for_arch_accepts_gfx950_and_reports_schedule():
-    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950:sramecc+:xnack-")
+    # dispatch_tile_m=16 reproduces the pages' sm80 gate exactly
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, dispatch_tile_m=16), "gfx950:sramecc+:xnack-")
     info = q.qtip_moe_plan_info(plan)
     assert info["tile_m"] == 16
     assert info["min_tokens_grouped"] == 683
@@ -42,11 +43,31 @@ def test_plan_for_arch_accepts_gfx950_and_reports_schedule():
     q.qtip_moe_plan_destroy(plan)
 
 
-@pytest.mark.parametrize("tile_m,expect", [(32, 1366), (64, 2731)])
-def test_tile_m_is_one_source_for_the_predicate(tile_m, expect):
+@pytest.mark.parametrize("thr,expect", [(32, 1366), (64, 2731), (16, 683)])
+def test_dispatch_threshold_drives_the_predicate(thr, expect):
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, dispatch_tile_m=thr), "gfx950")
+    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == expect == fill.min_tokens_grouped(6, 256, thr)
+    assert q.qtip_moe_select_arm(plan, expect - 1) == q.QTIP_ARM_GEMV
+    assert q.qtip_moe_select_arm(plan, expect) == q.QTIP_ARM_GROUPED
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_default_dispatch_threshold_is_the_rederived_value():
+    # one pair per woken expert: the grouped arm from the decode-regime floor on
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == 9 == fill.min_tokens_grouped(6, 256, 1)
+    assert q.qtip_moe_select_arm(plan, 8) == q.QTIP_ARM_GEMV
+    assert q.qtip_moe_select_arm(plan, 9) == q.QTIP_ARM_GROUPED
+    assert "threshold 1 pairs" in q.qtip_moe_engaged_line(plan, 32)
+    q.qtip_moe_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("tile_m", [16, 32, 64])
+def test_tile_m_is_reported_and_drives_the_tile_fill(tile_m):
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, tile_m=tile_m), "gfx950")
     assert q.qtip_moe_plan_info(plan)["tile_m"] == tile_m
-    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == expect == fill.min_tokens_grouped(6, 256, tile_m)
+    pct = 100 * fill.pairs_per_woken_expert(1024, 6, 256) / tile_m
+    assert f"{pct:.1f}%" in q.qtip_moe_engaged_line(plan, 1024)
     q.qtip_moe_plan_destroy(plan)
 
 
@@ -69,7 +90,8 @@ def test_unsupported_arch_is_refused(arch):
 
 @pytest.mark.parametrize("bad", [dict(num_experts=0), dict(top_k=0), dict(top_k=300), dict(hidden=4000),
                                  dict(inter=64), dict(max_tokens=0), dict(arm_override=7), dict(out_dtype=3),
-                                 dict(tile_m=8), dict(num_experts=2048, top_k=6), dict(top_k=33)])
+                                 dict(tile_m=8), dict(num_experts=2048, top_k=6), dict(top_k=33),
+                                 dict(dispatch_tile_m=-1), dict(dispatch_tile_m=2000)])
 def test_invalid_desc_is_refused(bad):
     with pytest.raises(q.QtipError) as ei:
         q.qtip_moe_plan_for_arch(q.make_desc(**{**V4, **bad}), "gfx950")
@@ -125,3 +147,23 @@ def test_forward_argument_errors_return_before_any_launch():
 def test_status_strings():
     assert q.status_name(0) == "QTIP_OK"
     assert q.status_name(5) == "QTIP_ERR_CAPTURING"
+
+
+def test_schedule_reports_what_a_forward_launches():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    s4 = q.qtip_moe_plan_schedule(plan, 4)
+    s32 = q.qtip_moe_plan_schedule(plan, 32)
+    s1024 = q.qtip_moe_plan_schedule(plan, 1024)
+    assert s4["arm"] == q.QTIP_ARM_GEMV and s32["arm"] == q.QTIP_ARM_GROUPED and s1024["arm"] == q.QTIP_ARM_GROUPED
+    for s in (s32, s1024):
+        assert s["tile_m"] == 16
+        for st in (s["gate_up"], s["down"]):
+            assert 1 <= st["variant"] <= 5
+            assert st["rows_per_task"] in (16, 32, 64) and st["waves_per_workgroup"] in (8, 16)
+            assert st["pairs_per_decode"] >= 1
+    q.qtip_moe_plan_destroy(plan)
+    for v in range(1, 6):
+        plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, variant=v, arm_override=q.QTIP_ARM_GROUPED), "gfx950")
+        sch = q.qtip_moe_plan_schedule(plan, 64)
+        assert sch["gate_up"]["variant"] == v and sch["down"]["variant"] == v
+        q.qtip_moe_plan_destroy(plan)

@@ -31,7 +31,8 @@ QTIP_OUT_F32 = 1
 class qtip_moe_desc(ctypes.Structure):
     _fields_ = [("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("arm_override", ctypes.c_int32),
-                ("variant", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32)]
+                ("variant", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("dispatch_tile_m", ctypes.c_int32)]
 
 
 class qtip_moe_weights(ctypes.Structure):
@@ -45,6 +46,16 @@ class qtip_moe_stats(ctypes.Structure):
                 ("grouped_launches", ctypes.c_uint64), ("route_launches", ctypes.c_uint64),
                 ("combine_launches", ctypes.c_uint64), ("last_arm", ctypes.c_int32),
                 ("last_n_tokens", ctypes.c_int32)]
+
+
+class qtip_moe_kernel_shape(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("waves_per_workgroup", ctypes.c_int32),
+                ("rows_per_task", ctypes.c_int32), ("pairs_per_decode", ctypes.c_int32)]
+
+
+class qtip_moe_schedule(ctypes.Structure):
+    _fields_ = [("arm", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("gate_up", qtip_moe_kernel_shape),
+                ("down", qtip_moe_kernel_shape)]
 
 
 class QtipError(RuntimeError):
@@ -61,7 +72,7 @@ _SIGS = {
     "qtip_moe_plan_destroy": (_I32, [_P]),
     "qtip_moe_plan_info": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_I32)]),
     "qtip_moe_select_arm": (_I32, [_P, _I32]),
-    "qtip_moe_plan_schedule": (_I32, [_P] + [ctypes.POINTER(_I32)] * 4),
+    "qtip_moe_plan_schedule": (_I32, [_P, _I32, ctypes.POINTER(qtip_moe_schedule)]),
     "qtip_fill_woken_experts": (ctypes.c_double, [_I32, _I32, _I32]),
     "qtip_fill_pairs_per_woken_expert": (ctypes.c_double, [_I32, _I32, _I32]),
     "qtip_fill_select_grouped": (_I32, [_I32, _I32, _I32, _I32]),
@@ -134,8 +145,9 @@ def _check(fn: str, status: int):
 
 
 def make_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override=QTIP_ARM_AUTO, variant=0,
-              out_dtype=QTIP_OUT_F32, tile_m=0) -> qtip_moe_desc:
-    return qtip_moe_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override, variant, out_dtype, tile_m)
+              out_dtype=QTIP_OUT_F32, tile_m=0, dispatch_tile_m=0) -> qtip_moe_desc:
+    return qtip_moe_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override, variant, out_dtype, tile_m,
+                         dispatch_tile_m)
 
 
 def make_weights(codes_gate, codes_up, codes_down, scale_gate, scale_up, scale_down, lut) -> qtip_moe_weights:
@@ -166,13 +178,11 @@ def qtip_moe_plan_info(plan: int) -> dict:
     return {"tile_m": tm.value, "workspace_bytes": ws.value, "min_tokens_grouped": mt.value}
 
 
-def qtip_moe_plan_schedule(plan: int) -> dict:
-    variant, g, m = _I32(), _I32(), _I32()
-    waves = (_I32 * 2)()
-    _check("qtip_moe_plan_schedule", lib().qtip_moe_plan_schedule(plan, ctypes.byref(variant), waves,
-                                                                  ctypes.byref(g), ctypes.byref(m)))
-    return {"variant": variant.value, "waves_grouped": waves[0], "waves_gemv": waves[1],
-            "pairs_per_decode_grouped": g.value, "pairs_per_decode_gemv": m.value}
+def qtip_moe_plan_schedule(plan: int, n_tokens: int) -> dict:
+    out = qtip_moe_schedule()
+    _check("qtip_moe_plan_schedule", lib().qtip_moe_plan_schedule(plan, n_tokens, ctypes.byref(out)))
+    shape = lambda sh: {name: getattr(sh, name) for name, _ in qtip_moe_kernel_shape._fields_}
+    return {"arm": out.arm, "tile_m": out.tile_m, "gate_up": shape(out.gate_up), "down": shape(out.down)}
 
 
 def qtip_moe_select_arm(plan: int, n_tokens: int) -> int:

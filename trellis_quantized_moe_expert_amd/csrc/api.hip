@@ -23,9 +23,9 @@ using namespace qtip;
 struct qtip_moe_plan_s {
   qtip_moe_desc d;
   int32_t tile_m;
+  int32_t dispatch_tile_m;
   int32_t device;  // -1: created from an arch name; the current device is used at call time
-  int32_t kvariant_grouped;  // expert kernel configuration launched on each arm (kVariantW16 / kVariantW8)
-  int32_t kvariant_gemv;
+
   int32_t min_tokens_grouped;
   size_t ws_bytes;
   qtip_moe_stats stats;
@@ -55,10 +55,26 @@ inline hipError_t prof_mark(qtip_moe_plan_s* p, int b, hipStream_t st) {
 
 namespace {
 
-// The default variant takes, per arm, the configuration measured fastest on MI355X: 16 waves
-// with 32 pairs per decode on the grouped arm, 8 waves with 4 pairs per decode on the GEMV arm.
-constexpr int kDefaultGroupedVariant = kVariantW16;
-constexpr int kDefaultGemvVariant = kVariantW8;
+// Kernel configuration when the plan's variant is 0, measured on MI355X with V4-shaped layers
+// (bench.py --sweep over variants): per arm and pass, chosen by the closed-form pairs per woken
+// expert (host scalars only, so the choice is safe during graph capture).  Few pairs per expert:
+// 16 waves and short tasks keep every CU busy; many pairs: taller tasks (32 or 64 rows) feed
+// each activation fragment to more MFMAs and 8 waves leave room for the registers.
+int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_tokens) {
+  if (plan->d.variant != kVariantDefault) return plan->d.variant;
+  if (arm == kArmGemv) return 4;
+  const double ppe = n_tokens >= 1 ? fill_pairs_per_woken_expert(n_tokens, plan->d.top_k, plan->d.num_experts) : 1.0;
+  if (mode == kModeGateUp) return ppe < 4.0 ? 1 : 4;
+  return ppe < 8.0 ? 3 : 5;
+}
+
+// A variant whose task height does not divide `rows` falls back to the 16-row configuration
+// with the same number of waves.
+int fit_variant(int variant, int arm, int32_t rows) {
+  VariantInfo v{};
+  if (variant_info(variant, arm, v) && rows % v.rows_per_task == 0) return variant;
+  return (variant_info(variant, arm, v) && v.waves == 8) ? 2 : 1;
+}
 thread_local std::string g_detail;
 
 qtip_status fail(qtip_status s, const std::string& what) {
@@ -166,6 +182,13 @@ qtip_status ensure_device(qtip_moe_plan_t plan, hipStream_t stream, int* dev_out
   return QTIP_OK;
 }
 
+// MI355X dispatches workgroups round-robin over 8 XCDs of 32 CUs; other CU counts are
+// treated as one XCD (only the task order, not correctness, depends on this).
+int xcd_count(int dev) {
+  const int cus = g_cu_count[dev].load(std::memory_order_acquire);
+  return (cus >= 64 && cus % 32 == 0) ? cus / 32 : 1;
+}
+
 int persistent_grid(int dev, size_t max_tasks, int waves) {
   const size_t cus = (size_t)g_cu_count[dev].load(std::memory_order_acquire);
   size_t need = (max_tasks + waves - 1) / waves;
@@ -188,6 +211,8 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
   if (d->out_dtype != QTIP_OUT_BF16 && d->out_dtype != QTIP_OUT_F32) return fail(QTIP_ERR_INVALID_ARG, "unknown out_dtype");
   const int32_t tm = d->tile_m == 0 ? QTIP_DEFAULT_TILE_M : d->tile_m;
   if (tm != 16 && tm != 32 && tm != 64) return fail(QTIP_ERR_INVALID_ARG, "tile_m must be 0, 16, 32 or 64");
+  if (d->dispatch_tile_m < 0 || d->dispatch_tile_m > 1024)
+    return fail(QTIP_ERR_INVALID_ARG, "dispatch_tile_m must be in [0, 1024]");
   *tile_m = tm;
   return QTIP_OK;
 }
@@ -249,12 +274,12 @@ qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc, const char* gcn_ar
   if (!p) return fail(QTIP_ERR_INVALID_ARG, "out of host memory");
   p->d = *desc;
   p->d.variant = variant;
-  p->kvariant_grouped = variant == kVariantDefault ? kDefaultGroupedVariant : variant;
-  p->kvariant_gemv = variant == kVariantDefault ? kDefaultGemvVariant : variant;
   p->d.tile_m = tm;
   p->tile_m = tm;
+  p->dispatch_tile_m = desc->dispatch_tile_m == 0 ? QTIP_DEFAULT_DISPATCH_TILE_M : desc->dispatch_tile_m;
+  p->d.dispatch_tile_m = p->dispatch_tile_m;
   p->device = -1;
-  p->min_tokens_grouped = fill_min_tokens(desc->top_k, desc->num_experts, tm);
+  p->min_tokens_grouped = fill_min_tokens(desc->top_k, desc->num_experts, p->dispatch_tile_m);
   p->ws_bytes = ws_layout(p->d, tm, desc->max_tokens).total;
   *out = p;
   return QTIP_OK;
@@ -291,24 +316,35 @@ qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m, size_t* wo
   return QTIP_OK;
 }
 
-qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t* variant, int32_t* waves_per_workgroup,
-                                   int32_t* pairs_per_decode_grouped, int32_t* pairs_per_decode_gemv) {
-  if (!plan) return fail(QTIP_ERR_INVALID_ARG, "plan is NULL");
-  if (variant) *variant = plan->d.variant;
-  if (waves_per_workgroup) {
-    waves_per_workgroup[0] = expert_waves(plan->kvariant_grouped);
-    waves_per_workgroup[1] = expert_waves(plan->kvariant_gemv);
-  }
-  if (pairs_per_decode_grouped) *pairs_per_decode_grouped = expert_pairs_per_decode(plan->kvariant_grouped, kArmGrouped);
-  if (pairs_per_decode_gemv) *pairs_per_decode_gemv = expert_pairs_per_decode(plan->kvariant_gemv, kArmGemv);
+static void shape_of(const qtip_moe_plan_s* plan, int karm, int mode, int32_t n_tokens, int32_t rows,
+                     qtip_moe_kernel_shape* out) {
+  const int kv = fit_variant(resolve_variant(plan, karm, mode, n_tokens), karm, rows);
+  VariantInfo v{};
+  variant_info(kv, karm, v);
+  out->variant = kv;
+  out->waves_per_workgroup = v.waves;
+  out->rows_per_task = v.rows_per_task;
+  out->pairs_per_decode = v.pairs_per_decode;
+}
+
+qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_moe_schedule* out) {
+  if (!plan || !out) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (n_tokens < 1) return fail(QTIP_ERR_INVALID_CONFIG, "n_tokens must be >= 1");
+  const int32_t arm = qtip_moe_select_arm(plan, n_tokens);
+  const int karm = arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv;
+  out->arm = arm;
+  out->tile_m = plan->tile_m;
+  shape_of(plan, karm, kModeGateUp, n_tokens, plan->d.inter, &out->gate_up);
+  shape_of(plan, karm, kModeSingle, n_tokens, plan->d.hidden, &out->down);
   return QTIP_OK;
 }
 
 int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens) {
   if (!plan || n_tokens < 1) return -1;
   if (plan->d.arm_override != QTIP_ARM_AUTO) return plan->d.arm_override;
-  return fill_select_grouped(n_tokens, plan->d.top_k, plan->d.num_experts, plan->tile_m) ? QTIP_ARM_GROUPED
-                                                                                       : QTIP_ARM_GEMV;
+  return fill_select_grouped(n_tokens, plan->d.top_k, plan->d.num_experts, plan->dispatch_tile_m)
+             ? QTIP_ARM_GROUPED
+             : QTIP_ARM_GEMV;
 }
 
 qtip_status qtip_arch_witness(int device, void* stream) {
@@ -366,6 +402,10 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
   int dev = 0;
   qtip_status s = ensure_device(plan, st, &dev);
   if (s != QTIP_OK) return s;
+  const int karm = arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv;
+  const int kv = fit_variant(resolve_variant(plan, karm, kModeSingle, 0), karm, rows);
+  VariantInfo vi{};
+  variant_info(kv, karm, vi);
   ExpertParams p{};
   p.codes0 = codes;
   p.scale0 = scales;
@@ -381,9 +421,9 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
   p.n_act_rows = n_rows_a;
   p.out = y;
   p.n_out_rows = n_rows_a;
-  const int kv = arm == QTIP_ARM_GROUPED ? plan->kvariant_grouped : plan->kvariant_gemv;
-  const int grid = persistent_grid(dev, (size_t)n_units * (rows / kRowsPerTask), expert_waves(kv));
-  hipError_t e = launch_expert(kModeSingle, arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv, kv, p, grid, st);
+  p.n_xcd = xcd_count(dev);
+  const int grid = persistent_grid(dev, (size_t)n_units * (rows / vi.rows_per_task), vi.waves);
+  hipError_t e = launch_expert(kModeSingle, karm, kv, p, grid, st);
   if (e != hipSuccess) return hip_fail(e, "expert kernel launch");
   if (arm == QTIP_ARM_GROUPED) plan->stats.grouped_launches++; else plan->stats.gemv_launches++;
   return QTIP_OK;
@@ -456,9 +496,11 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
   gu.n_act_rows = n_tokens;
   gu.out = h;
   gu.n_out_rows = P;
-  const int kv = karm == kArmGrouped ? plan->kvariant_grouped : plan->kvariant_gemv;
-  const int waves = expert_waves(kv);
-  e = launch_expert(kModeGateUp, karm, kv, gu, persistent_grid(dev, max_units * (d.inter / kRowsPerTask), waves), st);
+  gu.n_xcd = xcd_count(dev);
+  const int kv_gu = fit_variant(resolve_variant(plan, karm, kModeGateUp, n_tokens), karm, d.inter);
+  VariantInfo vi{};
+  variant_info(kv_gu, karm, vi);
+  e = launch_expert(kModeGateUp, karm, kv_gu, gu, persistent_grid(dev, max_units * (d.inter / vi.rows_per_task), vi.waves), st);
   if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
   if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
 
@@ -478,7 +520,10 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
   dn.out = y;
   dn.out_row_map = sorted_pair;
   dn.n_out_rows = P;
-  e = launch_expert(kModeSingle, karm, kv, dn, persistent_grid(dev, max_units * (d.hidden / kRowsPerTask), waves), st);
+  dn.n_xcd = xcd_count(dev);
+  const int kv_dn = fit_variant(resolve_variant(plan, karm, kModeSingle, n_tokens), karm, d.hidden);
+  variant_info(kv_dn, karm, vi);
+  e = launch_expert(kModeSingle, karm, kv_dn, dn, persistent_grid(dev, max_units * (d.hidden / vi.rows_per_task), vi.waves), st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
   if (karm == kArmGrouped) plan->stats.grouped_launches += 2; else plan->stats.gemv_launches += 2;
@@ -555,9 +600,10 @@ qtip_status qtip_moe_engaged_line(qtip_moe_plan_t plan, int32_t n_tokens, char* 
   const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
   std::snprintf(buf, buf_len,
                 "qtip_moe: %s arm for %d tokens x top-%d of %d experts; mean m-tile fill %.1f%% "
-                "(%.2f pairs per woken expert, tile_m=%d); grouped from %d tokens%s",
+                "(%.2f pairs per woken expert, tile_m=%d); dispatch threshold %d pairs, grouped from %d "
+                "tokens%s",
                 arm == QTIP_ARM_GROUPED ? "grouped" : "GEMV", n_tokens, d.top_k, d.num_experts,
-                100.0 * ppe / plan->tile_m, ppe, plan->tile_m, plan->min_tokens_grouped,
+                100.0 * ppe / plan->tile_m, ppe, plan->tile_m, plan->dispatch_tile_m, plan->min_tokens_grouped,
                 d.arm_override != QTIP_ARM_AUTO ? " (arm pinned by the plan)" : "");
   return QTIP_OK;
 }

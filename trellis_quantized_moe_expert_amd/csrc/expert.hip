@@ -188,164 +188,223 @@ __device__ inline void act_rows(const ExpertParams& p, const Unit& un, int first
   }
 }
 
-// Grouped arm: NS row blocks of 16 pairs share one decode of 16 output rows.
-template <int MODE, int NS>
+// Codes of one 32-symbol run for each of NT row blocks (rows r0 + 16*nt + j).
+template <int NT>
+struct RunSet {
+  RunCodes c[NT];
+};
+
+template <int NT>
+__device__ inline RunSet<NT> load_runs(const uint8_t* const (&rows)[NT], int ob, int row_bytes) {
+  RunSet<NT> rs;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run(rows[nt], ob, row_bytes);
+  return rs;
+}
+
+// Grouped arm: NS row blocks of 16 pairs x NT row blocks of 16 outputs share one decode of
+// the 16*NT rows; each A fragment feeds NT MFMAs.
+template <int MODE, int NS, int NT>
 __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
-  const int r = r0 + j;
   const int row_bytes = p.cols >> 2;
   const int kblocks = p.cols / kKBlock;
-  const uint8_t* row0 = p.codes0 + ((size_t)un.e * p.rows + r) * row_bytes;
-  const uint8_t* row1 = (MODE == kModeGateUp) ? p.codes1 + ((size_t)un.e * p.rows + r) * row_bytes : row0;
+  const uint8_t* rows0[NT];
+  const uint8_t* rows1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const size_t row = (size_t)un.e * p.rows + r0 + 16 * nt + j;
+    rows0[nt] = p.codes0 + row * row_bytes;
+    rows1[nt] = (MODE == kModeGateUp) ? p.codes1 + row * row_bytes : rows0[nt];
+  }
 
   const uint16_t* abase[NS];  // A operand row i = lane%16 of each 16-pair block
   act_rows<NS>(p, un, j, 16, g, abase);
 
-  f32x4 acc0[NS], acc1[NS];
+  f32x4 acc0[NS][NT], acc1[NS][NT];
 #pragma unroll
   for (int m = 0; m < NS; ++m) {
-    acc0[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc0[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
 
   // Per block: the block's activations are requested first, then the next block's codes
   // (the block after the last wraps to block 0 and is not used), so waiting for the
   // activations never waits for those codes (memory counters retire in order) and the
   // codes have the whole block's decode to arrive.
-  RunCodes n0 = load_run(row0, g * 8, row_bytes);
-  RunCodes n1 = (MODE == kModeGateUp) ? load_run(row1, g * 8, row_bytes) : n0;
+  RunSet<NT> n0 = load_runs<NT>(rows0, g * 8, row_bytes);
+  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(rows1, g * 8, row_bytes) : n0;
   for (int kb = 0; kb < kblocks; ++kb) {
     u32x4 a[NS][4];
     load_a_block<NS>(a, abase, kb);
-    const RunCodes c0 = n0, c1 = n1;
+    const RunSet<NT> c0 = n0, c1 = n1;
     const int ob = (kb + 1 < kblocks ? kb + 1 : 0) * 32 + g * 8;
-    n0 = load_run(row0, ob, row_bytes);
-    if (MODE == kModeGateUp) n1 = load_run(row1, ob, row_bytes);
+    n0 = load_runs<NT>(rows0, ob, row_bytes);
+    if (MODE == kModeGateUp) n1 = load_runs<NT>(rows1, ob, row_bytes);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      u32x4 b0[2], b1[2];
-      decode16(lut, h ? c0.d1 : c0.d0, h ? c0.la : c0.d1, b0[0], b0[1]);
-      if (MODE == kModeGateUp) decode16(lut, h ? c1.d1 : c1.d0, h ? c1.la : c1.d1, b1[0], b1[1]);
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const int st = 2 * h + hs;
+      for (int nt = 0; nt < NT; ++nt) {
+        u32x4 b0[2], b1[2];
+        const RunCodes& x0 = c0.c[nt];
+        decode16(lut, h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
+        if (MODE == kModeGateUp) {
+          const RunCodes& x1 = c1.c[nt];
+          decode16(lut, h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+        }
 #pragma unroll
-        for (int m = 0; m < NS; ++m) {
-          acc0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
-                                                            __builtin_bit_cast(bf16x8, b0[hs]), acc0[m], 0, 0, 0);
-          if (MODE == kModeGateUp)
-            acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
-                                                              __builtin_bit_cast(bf16x8, b1[hs]), acc1[m], 0, 0, 0);
+        for (int hs = 0; hs < 2; ++hs) {
+          const int st = 2 * h + hs;
+#pragma unroll
+          for (int m = 0; m < NS; ++m) {
+            acc0[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
+                                                                  __builtin_bit_cast(bf16x8, b0[hs]), acc0[m][nt], 0, 0, 0);
+            if (MODE == kModeGateUp)
+              acc1[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
+                                                                    __builtin_bit_cast(bf16x8, b1[hs]), acc1[m][nt], 0, 0, 0);
+          }
         }
       }
     }
   }
 
-  // D layout: lane holds rows 4*(lane/16)+t (pairs) of column lane%16 (output row r)
-  const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
-  const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
+  // D layout: lane holds rows 4*(lane/16)+t (pairs) of column lane%16 (output row)
 #pragma unroll
-  for (int m = 0; m < NS; ++m) {
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = r0 + 16 * nt + j;
+    const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
+    const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int pi = m * 16 + 4 * g + t;
-      if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][t], acc1[m][t], s0, s1);
+    for (int m = 0; m < NS; ++m) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pi = m * 16 + 4 * g + t;
+        if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][nt][t], acc1[m][nt][t], s0, s1);
+      }
     }
   }
 }
 
-// GEMV arm: NQ pairs share one decode of 16 output rows; VALU bf16 dot products.
-template <int MODE, int NQ>
+// GEMV arm: NQ pairs x NT row blocks of 16 outputs share one decode; VALU bf16 dot products.
+template <int MODE, int NQ, int NT>
 __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
-  const int r = r0 + j;
   const int row_bytes = p.cols >> 2;
   const int kblocks = p.cols / kKBlock;
-  const uint8_t* row0 = p.codes0 + ((size_t)un.e * p.rows + r) * row_bytes;
-  const uint8_t* row1 = (MODE == kModeGateUp) ? p.codes1 + ((size_t)un.e * p.rows + r) * row_bytes : row0;
+  const uint8_t* rows0[NT];
+  const uint8_t* rows1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const size_t row = (size_t)un.e * p.rows + r0 + 16 * nt + j;
+    rows0[nt] = p.codes0 + row * row_bytes;
+    rows1[nt] = (MODE == kModeGateUp) ? p.codes1 + row * row_bytes : rows0[nt];
+  }
 
   const uint16_t* xb[NQ];  // every lane of group g reads the same 16 bytes of pair q
   act_rows<NQ>(p, un, 0, 1, g, xb);
-  float acc0[NQ], acc1[NQ];
+  float acc0[NQ][NT], acc1[NQ][NT];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) acc0[q] = acc1[q] = 0.f;
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc0[q][nt] = acc1[q][nt] = 0.f;
+  }
 
-  RunCodes n0 = load_run(row0, g * 8, row_bytes);
-  RunCodes n1 = (MODE == kModeGateUp) ? load_run(row1, g * 8, row_bytes) : n0;
+  RunSet<NT> n0 = load_runs<NT>(rows0, g * 8, row_bytes);
+  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(rows1, g * 8, row_bytes) : n0;
   for (int kb = 0; kb < kblocks; ++kb) {
     u32x4 x[NQ][4];
     load_a_block<NQ>(x, xb, kb);
-    const RunCodes c0 = n0, c1 = n1;
+    const RunSet<NT> c0 = n0, c1 = n1;
     const int ob = (kb + 1 < kblocks ? kb + 1 : 0) * 32 + g * 8;
-    n0 = load_run(row0, ob, row_bytes);
-    if (MODE == kModeGateUp) n1 = load_run(row1, ob, row_bytes);
+    n0 = load_runs<NT>(rows0, ob, row_bytes);
+    if (MODE == kModeGateUp) n1 = load_runs<NT>(rows1, ob, row_bytes);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      u32x4 b0[2], b1[2];
-      decode16(lut, h ? c0.d1 : c0.d0, h ? c0.la : c0.d1, b0[0], b0[1]);
-      if (MODE == kModeGateUp) decode16(lut, h ? c1.d1 : c1.d0, h ? c1.la : c1.d1, b1[0], b1[1]);
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
+      for (int nt = 0; nt < NT; ++nt) {
+        u32x4 b0[2], b1[2];
+        const RunCodes& x0 = c0.c[nt];
+        decode16(lut, h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
+        if (MODE == kModeGateUp) {
+          const RunCodes& x1 = c1.c[nt];
+          decode16(lut, h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+        }
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          acc0[q] = dot8(b0[hs], x[q][2 * h + hs], acc0[q]);
-          if (MODE == kModeGateUp) acc1[q] = dot8(b1[hs], x[q][2 * h + hs], acc1[q]);
+        for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            acc0[q][nt] = dot8(b0[hs], x[q][2 * h + hs], acc0[q][nt]);
+            if (MODE == kModeGateUp) acc1[q][nt] = dot8(b1[hs], x[q][2 * h + hs], acc1[q][nt]);
+          }
         }
       }
     }
   }
-  const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
-  const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
-  // sum the four lane groups (lanes j, j+16, j+32, j+48 hold one row's partial sums)
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    float a0 = acc0[q];
-    a0 += __shfl_xor(a0, 16, 64);
-    a0 += __shfl_xor(a0, 32, 64);
-    float a1 = 0.f;
-    if (MODE == kModeGateUp) {
-      a1 = acc1[q];
-      a1 += __shfl_xor(a1, 16, 64);
-      a1 += __shfl_xor(a1, 32, 64);
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = r0 + 16 * nt + j;
+    const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
+    const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
+    // sum the four lane groups (lanes j, j+16, j+32, j+48 hold one row's partial sums)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float a0 = acc0[q][nt];
+      a0 += __shfl_xor(a0, 16, 64);
+      a0 += __shfl_xor(a0, 32, 64);
+      float a1 = 0.f;
+      if (MODE == kModeGateUp) {
+        a1 = acc1[q][nt];
+        a1 += __shfl_xor(a1, 16, 64);
+        a1 += __shfl_xor(a1, 32, 64);
+      }
+      if (q < un.len && (q & 3) == g) epilogue_store<MODE>(p, un, r, q, a0, a1, s0, s1);
     }
-    if (q < un.len && (q & 3) == g) epilogue_store<MODE>(p, un, r, q, a0, a1, s0, s1);
   }
 }
 
-// Kernel configurations (the plan's `variant`): waves per workgroup, pairs per decode on the
-// grouped arm (in 16-pair MFMA row blocks) and on the GEMV arm.  Fewer waves leave each wave
-// more registers for activation and code prefetch; more pairs per decode mean fewer decodes.
-template <int WAVES, int NSUB, int GPAIRS>
+// Kernel configurations (the plan's `variant`): waves per workgroup, 16-row output blocks
+// per task (NT), pairs per decode on the grouped arm (in 16-pair MFMA row blocks, NSUB) and
+// on the GEMV arm.  Fewer waves leave each wave more registers; more rows per task feed each
+// activation fragment to more MFMAs; more pairs per decode mean fewer decodes.
+template <int WAVES, int NT, int NSUB, int GPAIRS>
 struct ExpertCfg {
-  static constexpr int kWaves = WAVES, kNSub = NSUB, kGPairs = GPAIRS;
+  static constexpr int kWaves = WAVES, kNT = NT, kNSub = NSUB, kGPairs = GPAIRS;
+  static constexpr int kRows = 16 * NT;
 };
-using CfgW16 = ExpertCfg<16, 2, 2>;
-using CfgW8 = ExpertCfg<8, 4, 4>;
+using Cfg1 = ExpertCfg<16, 1, 2, 2>;
+using Cfg2 = ExpertCfg<8, 1, 4, 4>;
+using Cfg3 = ExpertCfg<16, 2, 2, 2>;
+using Cfg4 = ExpertCfg<8, 2, 4, 4>;
+using Cfg5 = ExpertCfg<8, 4, 2, 2>;
 
 // A unit may hold more pairs than one decode serves; it is then processed in chunks, each
 // chunk decoding the rows again.  Each chunk runs the body specialised for its exact number
 // of 16-pair row blocks (grouped) or pairs (GEMV), chosen by a wave-uniform switch.
 template <int MODE, int ARM, class CFG>
 __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
+  constexpr int NT = CFG::kNT;
   constexpr int kChunk = (ARM == kArmGrouped) ? CFG::kNSub * 16 : CFG::kGPairs;
   static_assert(CFG::kNSub >= 1 && CFG::kNSub <= 4 && CFG::kGPairs >= 1 && CFG::kGPairs <= 4, "config");
   for (int c0 = 0; c0 < un.len; c0 += kChunk) {
     const Unit part{un.e, un.start + c0, min(kChunk, un.len - c0)};
     if (ARM == kArmGrouped) {
       switch ((part.len + 15) >> 4) {
-        case 1: task_grouped<MODE, 1>(p, lut, part, r0); break;
-        case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1)>(p, lut, part, r0); break;
-        case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1)>(p, lut, part, r0); break;
-        default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1)>(p, lut, part, r0); break;
+        case 1: task_grouped<MODE, 1, NT>(p, lut, part, r0); break;
+        case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT>(p, lut, part, r0); break;
+        case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT>(p, lut, part, r0); break;
+        default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT>(p, lut, part, r0); break;
       }
     } else {
       switch (part.len) {
-        case 1: task_gemv<MODE, 1>(p, lut, part, r0); break;
-        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1)>(p, lut, part, r0); break;
-        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1)>(p, lut, part, r0); break;
-        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1)>(p, lut, part, r0); break;
+        case 1: task_gemv<MODE, 1, NT>(p, lut, part, r0); break;
+        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT>(p, lut, part, r0); break;
+        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT>(p, lut, part, r0); break;
+        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT>(p, lut, part, r0); break;
       }
     }
   }
@@ -357,19 +416,27 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
   fill_lut(lut_s, p.lut);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = p.n_units_dev ? __builtin_amdgcn_readfirstlane(*p.n_units_dev) : p.n_units_host;
-  const int nblocks = p.rows / kRowsPerTask;
+  const int nblocks = p.rows / CFG::kRows;
   const long total = (long)n_units * nblocks;
-  // Each workgroup (one per CU) owns a contiguous, equal share of the tasks (+-1), so the
-  // CUs finish together; its waves take the share's tasks in turn, so neighbouring waves
-  // work on neighbouring row blocks of the same unit and share its activation rows in L1.
-  const long share_lo = total * blockIdx.x / gridDim.x;
-  const long share_hi = total * (blockIdx.x + 1) / gridDim.x;
-  for (long task = share_lo + wave; task < share_hi; task += CFG::kWaves) {
+  // Task order.  Workgroup b runs on XCD b % n_xcd (round-robin dispatch).  Each XCD owns a
+  // contiguous share of the tasks in proportion to its workgroups, and its waves take that
+  // share's tasks in turn across its CUs, so an XCD works on a few units at a time: their
+  // activation rows stay in its L2, and a CU's waves (row blocks of the same unit) share them
+  // in L1.  Shares differ by at most one task per CU, so the CUs finish together.
+  const int nx = p.n_xcd;
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % nx, cu = blockIdx.x / nx;
+  const int cus = G / nx + (xcd < G % nx ? 1 : 0);
+  const int before = xcd * (G / nx) + min(xcd, G % nx);
+  const long lo = total * before / G;
+  const long hi = total * (before + cus) / G;
+  const long nslots = (long)CFG::kWaves * cus;
+  for (long task = lo + (long)wave * cus + cu; task < hi; task += nslots) {
     const int u = (int)(task / nblocks);
     const int nb = (int)(task - (long)u * nblocks);
     Unit un;
     if (!read_unit(p, u, un)) continue;
-    run_task<MODE, ARM, CFG>(p, lut_s, un, nb * kRowsPerTask);
+    run_task<MODE, ARM, CFG>(p, lut_s, un, nb * CFG::kRows);
   }
 }
 
@@ -417,18 +484,35 @@ static void launch_cfg(int mode, int arm, const ExpertParams& p, int grid, hipSt
     hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGemv, CFG>), g, b, 0, stream, p);
 }
 
-int expert_waves(int variant) { return variant == kVariantW8 ? CfgW8::kWaves : CfgW16::kWaves; }
+template <class CFG>
+struct CfgInfo {
+  static void get(int arm, VariantInfo& v) {
+    v.waves = CFG::kWaves;
+    v.rows_per_task = CFG::kRows;
+    v.pairs_per_decode = arm == kArmGrouped ? CFG::kNSub * 16 : CFG::kGPairs;
+  }
+};
 
-int expert_pairs_per_decode(int variant, int arm) {
-  if (variant == kVariantW8) return arm == kArmGrouped ? CfgW8::kNSub * 16 : CfgW8::kGPairs;
-  return arm == kArmGrouped ? CfgW16::kNSub * 16 : CfgW16::kGPairs;
+bool variant_info(int variant, int arm, VariantInfo& v) {
+  switch (variant) {
+    case 1: CfgInfo<Cfg1>::get(arm, v); return true;
+    case 2: CfgInfo<Cfg2>::get(arm, v); return true;
+    case 3: CfgInfo<Cfg3>::get(arm, v); return true;
+    case 4: CfgInfo<Cfg4>::get(arm, v); return true;
+    case 5: CfgInfo<Cfg5>::get(arm, v); return true;
+    default: return false;
+  }
 }
 
 hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, hipStream_t stream) {
-  if (variant == kVariantW8)
-    launch_cfg<CfgW8>(mode, arm, p, grid, stream);
-  else
-    launch_cfg<CfgW16>(mode, arm, p, grid, stream);
+  switch (variant) {
+    case 1: launch_cfg<Cfg1>(mode, arm, p, grid, stream); break;
+    case 2: launch_cfg<Cfg2>(mode, arm, p, grid, stream); break;
+    case 3: launch_cfg<Cfg3>(mode, arm, p, grid, stream); break;
+    case 4: launch_cfg<Cfg4>(mode, arm, p, grid, stream); break;
+    case 5: launch_cfg<Cfg5>(mode, arm, p, grid, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -11,9 +11,9 @@ namespace qtip {
 constexpr int kLutEntries = 65536;     // 16-bit trellis state -> one LUT entry
 // The LUT fills 128 KiB of LDS, so one expert workgroup per CU is resident; the kernel
 // variant fixes its size (16 or 8 wave64).
-enum ExpertVariant { kVariantDefault = 0, kVariantW16 = 1, kVariantW8 = 2, kVariantCount = 3 };
+// Variants 1..5 are fixed kernel configurations (see variant_info); 0 lets the plan choose.
+enum ExpertVariant { kVariantDefault = 0, kVariantCount = 6 };
 constexpr int kExpertWaves = 16;       // waves of the binning workgroup
-constexpr int kRowsPerTask = 16;       // output rows per wave task (the MFMA N)
 constexpr int kKBlock = 128;           // inputs per K block: 4 lane groups x 32-symbol runs
 constexpr int kUnitMaxPairs = 64;      // pairs sharing one decode (4 MFMA row blocks of 16)
 constexpr int kRouteWaves = 4;         // tokens per route workgroup (one wave each)
@@ -42,15 +42,20 @@ struct ExpertParams {
   void* out;                    // fused: bf16 h [n_pos][rows]; single: fp32 y [n_out_rows][rows]
   const int32_t* out_row_map;   // single pass: output row of position s = map[s] (NULL: s)
   int32_t n_out_rows;
+  int32_t n_xcd;                // workgroups are dispatched round-robin over this many XCDs (>= 1)
 };
 
 enum ExpertMode { kModeGateUp = 0, kModeSingle = 1 };
 enum ExpertArm { kArmGemv = 0, kArmGrouped = 1 };
 
-// `variant` must be kVariantW16 or kVariantW8 (the plan resolves kVariantDefault).
+struct VariantInfo {
+  int waves;             // wave64 per workgroup
+  int rows_per_task;     // output rows per wave task (rows must be a multiple of it)
+  int pairs_per_decode;  // binned pairs sharing one decode of an expert's rows
+};
+// `variant` in 1..5 (the plan resolves 0).  variant_info returns false for other values.
+bool variant_info(int variant, int arm, VariantInfo& v);
 hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, hipStream_t stream);
-int expert_waves(int variant);
-int expert_pairs_per_decode(int variant, int arm);
 
 hipError_t launch_route_topk(const float* logits, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
                              float* topk_w, hipStream_t stream);
