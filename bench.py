@@ -31,6 +31,11 @@ METRIC = "MoE-layer tokens/s + packed-weight HBM GB/s (% peak) vs token count n"
 HBM_PEAK_GBS = 8000.0
 # VALU decode ceiling: 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-ops/s at 2 ops per symbol.
 DECODE_VALU_PEAK_SYMS = 256 * 64 * 2.4e9 / 2
+# LDS random-gather ceiling (the one that binds): 32 banks of 4 bytes, a wave64 read served as two
+# half-waves of 32 lanes; 32 uniformly random requests over 32 banks have an expected largest bank
+# load of 3.532, so a half-wave takes 3.532 cycles: 64 / (2 x 3.532) = 9.06 lookups/clk/CU, x 256
+# CUs x 2.4 GHz = 5.57 T lookups/s.
+LDS_GATHER_PEAK = 256 * 2.4e9 * 64 / (2 * 3.532)
 SWEEP_N = [8, 16, 32, 64, 128, 256, 512, 683, 1024]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["trellis_quantized_moe_expert_amd/csrc/expert.hip",
@@ -202,6 +207,14 @@ def summarize_traffic(fetch_csv, write_csv, workload, arm, command):
     log(json.dumps(ent))
 
 
+def measure_gather_ceiling(rounds=2000):
+    import torch
+    import trellis_quantized_moe_expert_amd as q
+    n = torch.cuda.get_device_properties(0).multi_processor_count * 1024
+    sink = torch.empty(n, dtype=torch.int32, device="cuda:0")
+    return q.qtip_measure_lut_gather(rounds, sink, n, torch.cuda.current_stream())
+
+
 def cpu_baseline(inp, n_sample):
     """The oracle as it stands, one BLAS thread, on the first n_sample tokens of the batch."""
     from threadpoolctl import threadpool_limits
@@ -332,6 +345,8 @@ def main():
         print(f"bench: launch counters do not show the {arm} arm: {counters}", file=sys.stderr)
         sys.exit(2)
 
+    gather_measured = measure_gather_ceiling()
+    gu_syms = fig["symbols_sched"]["gate_up"] / gu_s
     cpu = cpu_baseline(inp, args.cpu_sample) if args.cpu_sample > 0 else None
     line = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -352,8 +367,11 @@ def main():
             "gate_up_packed_bytes": fig["bytes"]["gate_up"], "down_packed_bytes": fig["bytes"]["down"],
             "woken_experts": fig["woken"], "max_pairs_per_expert": fig["max_count"], "m_tiles": n_tiles,
             "decode_units": fig["units"], "decodes": fig["decodes"],
-            "gate_up_symbols_per_s": fig["symbols_sched"]["gate_up"] / gu_s,
-            "gate_up_decode_valu_frac": fig["symbols_sched"]["gate_up"] / gu_s / DECODE_VALU_PEAK_SYMS,
+            "decode_roofline": {"bound": "lds_gather", "kernel": "gate+up", "achieved": gu_syms,
+                                "unit": "LUT lookups/s", "peak_model": LDS_GATHER_PEAK,
+                                "frac_model": gu_syms / LDS_GATHER_PEAK, "peak_measured": gather_measured,
+                                "frac_measured": gu_syms / gather_measured,
+                                "valu_peak": DECODE_VALU_PEAK_SYMS, "frac_valu": gu_syms / DECODE_VALU_PEAK_SYMS},
             "schedule": sched,
             "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "route_launches",
                                                          "combine_launches")},

@@ -242,6 +242,16 @@ qtip_status qtip_arch_witness(int device, void* stream);
 qtip_status qtip_moe_profile_enable(qtip_moe_plan_t plan, int32_t capacity);
 qtip_status qtip_moe_profile_read(qtip_moe_plan_t plan, double* stage_ms /*host [5]*/, int32_t* n_forwards /*host*/);
 
+/* Decode-ceiling calibration (a diagnostic, not part of the forward path).  The trellis decode
+ * is bound by uniformly random 2-byte gathers from the 65536-entry LUT held in LDS; this runs
+ * that gather alone on the current device (one 1024-thread workgroup per CU, 128 KiB LDS table,
+ * 16 gathers per lane per round at pseudo-random addresses, `rounds` rounds) and reports the
+ * measured lookups per second.  sink: device buffer of at least (CU count x 1024) uint32 that
+ * receives per-thread checksums (keeps the gathers live); its contents are meaningless.
+ * Synchronises the stream.  rounds in [1, 1 << 20]. */
+qtip_status qtip_measure_lut_gather(int32_t rounds, uint32_t* sink, size_t sink_elems, void* stream,
+                                    double* lookups_per_second /*host*/);
+
 const char* qtip_status_string(qtip_status s);
 /* Text of the last error raised on the calling thread ("" if none). */
 const char* qtip_last_error_detail(void);

@@ -72,3 +72,14 @@ def test_route_skewed_hot_expert():
     logits[:, 3] += 10.0          # every token picks expert 3: one bin of 1500 pairs
     say("route hot expert")
     compare(logits, 32, 4)
+
+
+def test_lut_gather_calibration_runs():
+    import torch
+    n = torch.cuda.get_device_properties(0).multi_processor_count * 1024
+    sink = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    rate = q.qtip_measure_lut_gather(200, sink, n)
+    say(f"LDS random gather: {rate / 1e12:.2f} T lookups/s")
+    assert 1e12 < rate < 2e13
+    with pytest.raises(q.QtipError):
+        q.qtip_measure_lut_gather(10, sink, 16)          # sink too small: refused, nothing launched

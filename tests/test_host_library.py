@@ -167,3 +167,17 @@ def test_schedule_reports_what_a_forward_launches():
         sch = q.qtip_moe_plan_schedule(plan, 64)
         assert sch["gate_up"]["variant"] == v and sch["down"]["variant"] == v
         q.qtip_moe_plan_destroy(plan)
+
+
+def test_gather_calibration_argument_errors():
+    lib = q.lib()
+    out = ctypes.c_double()
+    assert lib.qtip_measure_lut_gather(100, None, 0, None, ctypes.byref(out)) == q.QTIP_ERR_INVALID_ARG
+    assert lib.qtip_measure_lut_gather(0, 256, 1 << 20, None, ctypes.byref(out)) == q.QTIP_ERR_INVALID_CONFIG
+    assert lib.qtip_measure_lut_gather(1 << 21, 256, 1 << 20, None, ctypes.byref(out)) == q.QTIP_ERR_INVALID_CONFIG
+
+
+def test_offset_width_limits_are_enforced():
+    with pytest.raises(q.QtipError) as ei:
+        q.qtip_moe_plan_for_arch(q.make_desc(256, 8, 8192, 8192, 40000), "gfx950")
+    assert ei.value.status == q.QTIP_ERR_INVALID_ARG

@@ -86,6 +86,7 @@ _SIGS = {
     "qtip_arch_witness": (_I32, [ctypes.c_int, _P]),
     "qtip_moe_profile_enable": (_I32, [_P, _I32]),
     "qtip_moe_profile_read": (_I32, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)]),
+    "qtip_measure_lut_gather": (_I32, [_I32, _P, ctypes.c_size_t, _P, ctypes.POINTER(ctypes.c_double)]),
     "qtip_status_string": (ctypes.c_char_p, [_I32]),
     "qtip_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -258,6 +259,13 @@ def qtip_moe_profile_read(plan) -> dict:
     n = _I32()
     _check("qtip_moe_profile_read", lib().qtip_moe_profile_read(plan, ms, ctypes.byref(n)))
     return {"n_forwards": n.value, **{name: ms[i] for i, name in enumerate(PROFILE_STAGES)}}
+
+
+def qtip_measure_lut_gather(rounds: int, sink, sink_elems: int, stream=None) -> float:
+    out = ctypes.c_double()
+    _check("qtip_measure_lut_gather", lib().qtip_measure_lut_gather(rounds, _ptr(sink), sink_elems, _stream(stream),
+                                                                    ctypes.byref(out)))
+    return out.value
 
 
 def raw_status(fn_name: str, *args) -> int:

@@ -206,6 +206,11 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
   if (d->inter < kKBlock || d->inter % kKBlock) return fail(QTIP_ERR_INVALID_ARG, "inter must be a positive multiple of 128");
   if (d->max_tokens < 1) return fail(QTIP_ERR_INVALID_ARG, "max_tokens must be >= 1");
   if ((int64_t)d->max_tokens * d->top_k > (1 << 24)) return fail(QTIP_ERR_INVALID_ARG, "max_tokens * top_k exceeds 2^24");
+  // activation buffers (x: n x H, h: n k x I) are addressed with 32-bit element offsets
+  if ((int64_t)d->max_tokens * d->top_k * (d->hidden > d->inter ? d->hidden : d->inter) >= ((int64_t)1 << 31))
+    return fail(QTIP_ERR_INVALID_ARG, "max_tokens * top_k * max(hidden, inter) must be below 2^31");
+  if ((int64_t)d->hidden * d->inter / 4 >= ((int64_t)1 << 31))
+    return fail(QTIP_ERR_INVALID_ARG, "one expert matrix must be below 2^31 bytes");
   if (d->arm_override != QTIP_ARM_AUTO && d->arm_override != QTIP_ARM_GEMV && d->arm_override != QTIP_ARM_GROUPED)
     return fail(QTIP_ERR_INVALID_ARG, "unknown arm_override");
   if (d->out_dtype != QTIP_OUT_BF16 && d->out_dtype != QTIP_OUT_F32) return fail(QTIP_ERR_INVALID_ARG, "unknown out_dtype");
@@ -398,6 +403,8 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
       (reinterpret_cast<uintptr_t>(codes) & 7))
     return fail(QTIP_ERR_INVALID_ARG, "lut and a_bf16 must be 16-byte aligned, codes 8-byte aligned");
   if (n_units <= 0) return fail(QTIP_ERR_INVALID_CONFIG, "n_units must be >= 1 (an empty launch is an error)");
+  if ((int64_t)n_rows_a * cols >= ((int64_t)1 << 31) || (int64_t)rows * (cols / 4) >= ((int64_t)1 << 31))
+    return fail(QTIP_ERR_INVALID_ARG, "n_rows_a * cols and rows * cols / 4 must be below 2^31");
   const hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   qtip_status s = ensure_device(plan, st, &dev);
@@ -577,6 +584,34 @@ qtip_status qtip_moe_profile_read(qtip_moe_plan_t plan, double* stage_ms, int32_
   }
   *n_forwards = (int32_t)n;
   plan->prof_recorded = 0;
+  return QTIP_OK;
+}
+
+qtip_status qtip_measure_lut_gather(int32_t rounds, uint32_t* sink, size_t sink_elems, void* stream,
+                                    double* lookups_per_second) {
+  g_detail.clear();
+  if (!sink || !lookups_per_second) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (rounds < 1 || rounds > (1 << 20)) return fail(QTIP_ERR_INVALID_CONFIG, "rounds must be in [1, 2^20]");
+  const hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  qtip_status s = current_device(&dev);
+  if (s != QTIP_OK) return s;
+  if ((s = witness_on(dev, st)) != QTIP_OK) return s;
+  const int grid = g_cu_count[dev].load(std::memory_order_acquire);
+  if (sink_elems < (size_t)grid * 1024) return fail(QTIP_ERR_INVALID_ARG, "sink needs CU count x 1024 elements");
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = hipEventRecord(e0, st);
+  if (e == hipSuccess) e = launch_gather_probe(grid, rounds, sink, st);
+  if (e == hipSuccess) e = hipEventRecord(e1, st);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return hip_fail(e, "gather probe");
+  *lookups_per_second = (double)grid * 1024.0 * 16.0 * rounds / (ms * 1e-3);
   return QTIP_OK;
 }
 

@@ -92,14 +92,16 @@ struct RunCodes {
   uint32_t d0, d1, la;
 };
 
-__device__ inline RunCodes load_run(const uint8_t* __restrict__ row, int ob, int row_bytes) {
+// `base` is the (wave-uniform) start of the expert's matrix, `row_off` the lane's row offset in
+// bytes; 32-bit offsets keep the addresses in one VGPR each.
+__device__ inline RunCodes load_run(const uint8_t* __restrict__ base, uint32_t row_off, int ob, int row_bytes) {
   RunCodes rc;
-  const uint2 v = *reinterpret_cast<const uint2*>(row + ob);
+  const uint2 v = *reinterpret_cast<const uint2*>(base + (row_off + (uint32_t)ob));
   int nx = ob + 8;
   if (nx >= row_bytes) nx -= row_bytes;
   rc.d0 = v.x;
   rc.d1 = v.y;
-  rc.la = *reinterpret_cast<const uint32_t*>(row + nx);
+  rc.la = *reinterpret_cast<const uint32_t*>(base + (row_off + (uint32_t)nx));
   return rc;
 }
 
@@ -163,20 +165,23 @@ __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int
 // are unconditional (rows past the unit read a valid row and are discarded later), so the
 // compiler can count outstanding memory operations exactly.
 template <int NS>
-__device__ inline void load_a_block(u32x4 (&a)[NS][4], const uint16_t* const (&abase)[NS], int kb) {
+__device__ inline void load_a_block(u32x4 (&a)[NS][4], const uint16_t* __restrict__ act, const uint32_t (&aoff)[NS],
+                                    int kb) {
 #pragma unroll
   for (int m = 0; m < NS; ++m) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) a[m][st] = *reinterpret_cast<const u32x4*>(abase[m] + kb * kKBlock + st * 8);
+    for (int st = 0; st < 4; ++st)
+      a[m][st] = *reinterpret_cast<const u32x4*>(act + (aoff[m] + (uint32_t)(kb * kKBlock + st * 8)));
   }
 }
 
-// Activation row pointers of this lane for NS entries; entry m is the binned position
-// first + m*stride.  Positions past the unit, and rows out of range, read the unit's first
-// row (always valid); their results are never stored.
+// Activation row offsets (elements from p.act) of this lane for NS entries; entry m is the
+// binned position first + m*stride.  Positions past the unit, and rows out of range, read the
+// unit's first row (always valid); their results are never stored.  The plan keeps the
+// activation buffers below 2^31 elements, so 32-bit offsets suffice.
 template <int NS>
 __device__ inline void act_rows(const ExpertParams& p, const Unit& un, int first, int stride, int g,
-                                const uint16_t* (&base)[NS]) {
+                                uint32_t (&off)[NS]) {
   int r_first = act_row(p, un.start);
   if (r_first < 0) r_first = 0;
 #pragma unroll
@@ -184,7 +189,7 @@ __device__ inline void act_rows(const ExpertParams& p, const Unit& un, int first
     const int pi = first + m * stride;
     int ar = (pi < un.len) ? act_row(p, un.start + pi) : -1;
     if (ar < 0) ar = r_first;
-    base[m] = p.act + (size_t)ar * p.cols + g * 32;
+    off[m] = (uint32_t)ar * (uint32_t)p.cols + (uint32_t)(g * 32);
   }
 }
 
@@ -195,10 +200,11 @@ struct RunSet {
 };
 
 template <int NT>
-__device__ inline RunSet<NT> load_runs(const uint8_t* const (&rows)[NT], int ob, int row_bytes) {
+__device__ inline RunSet<NT> load_runs(const uint8_t* __restrict__ base, uint32_t row_off0, uint32_t nt_stride, int ob,
+                                       int row_bytes) {
   RunSet<NT> rs;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run(rows[nt], ob, row_bytes);
+  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run(base, row_off0 + nt * nt_stride, ob, row_bytes);
   return rs;
 }
 
@@ -210,17 +216,15 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
   const int j = lane & 15, g = lane >> 4;
   const int row_bytes = p.cols >> 2;
   const int kblocks = p.cols / kKBlock;
-  const uint8_t* rows0[NT];
-  const uint8_t* rows1[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const size_t row = (size_t)un.e * p.rows + r0 + 16 * nt + j;
-    rows0[nt] = p.codes0 + row * row_bytes;
-    rows1[nt] = (MODE == kModeGateUp) ? p.codes1 + row * row_bytes : rows0[nt];
-  }
+  // matrix bases are wave-uniform; each lane's row is a 32-bit byte offset from them
+  const size_t mat_bytes = (size_t)p.rows * row_bytes;
+  const uint8_t* base0 = p.codes0 + (size_t)un.e * mat_bytes;
+  const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
+  const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+  const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
 
-  const uint16_t* abase[NS];  // A operand row i = lane%16 of each 16-pair block
-  act_rows<NS>(p, un, j, 16, g, abase);
+  uint32_t aoff[NS];  // A operand row i = lane%16 of each 16-pair block
+  act_rows<NS>(p, un, j, 16, g, aoff);
 
   f32x4 acc0[NS][NT], acc1[NS][NT];
 #pragma unroll
@@ -236,15 +240,15 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
   // (the block after the last wraps to block 0 and is not used), so waiting for the
   // activations never waits for those codes (memory counters retire in order) and the
   // codes have the whole block's decode to arrive.
-  RunSet<NT> n0 = load_runs<NT>(rows0, g * 8, row_bytes);
-  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(rows1, g * 8, row_bytes) : n0;
+  RunSet<NT> n0 = load_runs<NT>(base0, roff, nt_stride, g * 8, row_bytes);
+  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(base1, roff, nt_stride, g * 8, row_bytes) : n0;
   for (int kb = 0; kb < kblocks; ++kb) {
     u32x4 a[NS][4];
-    load_a_block<NS>(a, abase, kb);
+    load_a_block<NS>(a, p.act, aoff, kb);
     const RunSet<NT> c0 = n0, c1 = n1;
     const int ob = (kb + 1 < kblocks ? kb + 1 : 0) * 32 + g * 8;
-    n0 = load_runs<NT>(rows0, ob, row_bytes);
-    if (MODE == kModeGateUp) n1 = load_runs<NT>(rows1, ob, row_bytes);
+    n0 = load_runs<NT>(base0, roff, nt_stride, ob, row_bytes);
+    if (MODE == kModeGateUp) n1 = load_runs<NT>(base1, roff, nt_stride, ob, row_bytes);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -296,17 +300,15 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
   const int j = lane & 15, g = lane >> 4;
   const int row_bytes = p.cols >> 2;
   const int kblocks = p.cols / kKBlock;
-  const uint8_t* rows0[NT];
-  const uint8_t* rows1[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const size_t row = (size_t)un.e * p.rows + r0 + 16 * nt + j;
-    rows0[nt] = p.codes0 + row * row_bytes;
-    rows1[nt] = (MODE == kModeGateUp) ? p.codes1 + row * row_bytes : rows0[nt];
-  }
+  // matrix bases are wave-uniform; each lane's row is a 32-bit byte offset from them
+  const size_t mat_bytes = (size_t)p.rows * row_bytes;
+  const uint8_t* base0 = p.codes0 + (size_t)un.e * mat_bytes;
+  const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
+  const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+  const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
 
-  const uint16_t* xb[NQ];  // every lane of group g reads the same 16 bytes of pair q
-  act_rows<NQ>(p, un, 0, 1, g, xb);
+  uint32_t xoff[NQ];  // every lane of group g reads the same 16 bytes of pair q
+  act_rows<NQ>(p, un, 0, 1, g, xoff);
   float acc0[NQ][NT], acc1[NQ][NT];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -314,15 +316,15 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
     for (int nt = 0; nt < NT; ++nt) acc0[q][nt] = acc1[q][nt] = 0.f;
   }
 
-  RunSet<NT> n0 = load_runs<NT>(rows0, g * 8, row_bytes);
-  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(rows1, g * 8, row_bytes) : n0;
+  RunSet<NT> n0 = load_runs<NT>(base0, roff, nt_stride, g * 8, row_bytes);
+  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(base1, roff, nt_stride, g * 8, row_bytes) : n0;
   for (int kb = 0; kb < kblocks; ++kb) {
     u32x4 x[NQ][4];
-    load_a_block<NQ>(x, xb, kb);
+    load_a_block<NQ>(x, p.act, xoff, kb);
     const RunSet<NT> c0 = n0, c1 = n1;
     const int ob = (kb + 1 < kblocks ? kb + 1 : 0) * 32 + g * 8;
-    n0 = load_runs<NT>(rows0, ob, row_bytes);
-    if (MODE == kModeGateUp) n1 = load_runs<NT>(rows1, ob, row_bytes);
+    n0 = load_runs<NT>(base0, roff, nt_stride, ob, row_bytes);
+    if (MODE == kModeGateUp) n1 = load_runs<NT>(base1, roff, nt_stride, ob, row_bytes);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -469,6 +471,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 __global__ void witness_kernel(int32_t* out) { out[0] = kWitnessValue; }
 
+// The decode's bottleneck in isolation: random 2-byte gathers from a 128 KiB LDS table.  Each
+// lane draws 16 even byte offsets below 2^17 (xorshift32) and, per round, gathers them all after
+// XOR-ing with a round-dependent even mask below 2^17, so every address stays inside the table.
+__global__ __launch_bounds__(1024, 1) void gather_probe_kernel(int32_t rounds, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint16_t table[kLutEntries];
+  for (int i = threadIdx.x; i < kLutEntries; i += blockDim.x) table[i] = (uint16_t)(i * 40503u);
+  __syncthreads();
+  uint32_t st = 0x9E3779B9u ^ ((blockIdx.x * 1024u + threadIdx.x) * 2654435761u);
+  uint32_t a[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    st ^= st << 13;
+    st ^= st >> 17;
+    st ^= st << 5;
+    a[q] = (st & 0xFFFFu) << 1;
+  }
+  uint32_t acc = 0;
+  const char* base = reinterpret_cast<const char*>(table);
+  for (int it = 0; it < rounds; ++it) {
+    const uint32_t m = ((uint32_t)it * 0x9E3779B9u) & 0x1FFFEu;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc += *reinterpret_cast<const uint16_t*>(base + (a[q] ^ m));
+  }
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 template <class CFG>
@@ -521,6 +549,11 @@ hipError_t launch_combine(const float* y, const float* topk_w, int32_t n, int32_
   const long total = (long)n * (H / 4);
   const int grid = (int)((total + 255) / 256);
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, stream, y, topk_w, n, k, H, out, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_probe(int grid, int32_t rounds, uint32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(gather_probe_kernel, dim3(grid), dim3(1024), 0, stream, rounds, sink);
   return hipGetLastError();
 }
 

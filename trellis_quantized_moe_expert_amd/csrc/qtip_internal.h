@@ -69,4 +69,6 @@ hipError_t launch_combine(const float* y, const float* topk_w, int32_t n, int32_
 
 hipError_t launch_witness(int32_t* out, hipStream_t stream);
 
+hipError_t launch_gather_probe(int grid, int32_t rounds, uint32_t* sink, hipStream_t stream);
+
 }  // namespace qtip
