@@ -158,15 +158,26 @@ def test_schedule_reports_what_a_forward_launches():
     for s in (s32, s1024):
         assert s["tile_m"] == 16
         for st in (s["gate_up"], s["down"]):
-            assert 1 <= st["variant"] <= 5
-            assert st["rows_per_task"] in (16, 32, 64) and st["waves_per_workgroup"] in (8, 16)
+            assert 1 <= st["variant"] <= 7
+            assert st["rows_per_task"] in (16, 32, 64) and st["waves_per_workgroup"] in (8, 12, 16)
             assert st["pairs_per_decode"] >= 1
     q.qtip_moe_plan_destroy(plan)
-    for v in range(1, 6):
+    for v in range(1, 8):
         plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, variant=v, arm_override=q.QTIP_ARM_GROUPED), "gfx950")
         sch = q.qtip_moe_plan_schedule(plan, 64)
         assert sch["gate_up"]["variant"] == v and sch["down"]["variant"] == v
         q.qtip_moe_plan_destroy(plan)
+
+
+def test_default_kernel_shapes_follow_the_measured_rules():
+    # V4 layer (E=256, k=6): GEMV switches to 32-row tasks once woken*rows/32 >= 2048 wave slots;
+    # grouped picks by pairs per woken expert (1.41 at n=32, 6.0 at 256, 12.0 at 512, 24.0 at 1024).
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    want = {1: (2, 2), 4: (2, 4), 8: (4, 4), 32: (1, 3), 256: (6, 3), 512: (6, 7), 1024: (4, 7)}
+    for n, (gu, dn) in want.items():
+        s = q.qtip_moe_plan_schedule(plan, n)
+        assert (s["gate_up"]["variant"], s["down"]["variant"]) == (gu, dn), n
+    q.qtip_moe_plan_destroy(plan)
 
 
 def test_gather_calibration_argument_errors():

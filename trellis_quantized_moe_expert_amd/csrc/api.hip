@@ -56,25 +56,38 @@ inline hipError_t prof_mark(qtip_moe_plan_s* p, int b, hipStream_t st) {
 namespace {
 
 // Kernel configuration when the plan's variant is 0, measured on MI355X with V4-shaped layers
-// (bench.py --sweep over variants): per arm and pass, chosen by the closed-form pairs per woken
-// expert (host scalars only, so the choice is safe during graph capture).  Few pairs per expert:
-// 16 waves and short tasks keep every CU busy; many pairs: taller tasks (32 or 64 rows) feed
-// each activation fragment to more MFMAs and 8 waves leave room for the registers.
+// (bench.py --sweep over variants) and chosen from host scalars only, so the choice is safe
+// during graph capture.
+//  * Grouped arm, by the closed-form pairs per woken expert: few pairs -> 16 waves of 16-row
+//    tasks keep every CU busy; a moderate number -> 12 waves of taller tasks (32 rows for the
+//    fused pass, 64 for down) feed each activation fragment to more MFMAs; many pairs (fused
+//    pass) -> 8 waves with four 16-pair blocks per decode.
+//  * GEMV arm, by the expected task count: 16-row tasks until there are enough 32-row tasks
+//    to give each of the 2048 wave slots of a 256-CU, 8-wave launch one.
 int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_tokens) {
   if (plan->d.variant != kVariantDefault) return plan->d.variant;
-  if (arm == kArmGemv) return 4;
-  const double ppe = n_tokens >= 1 ? fill_pairs_per_woken_expert(n_tokens, plan->d.top_k, plan->d.num_experts) : 1.0;
-  if (mode == kModeGateUp) return ppe < 4.0 ? 1 : 4;
-  return ppe < 8.0 ? 3 : 5;
+  const int32_t E = plan->d.num_experts, k = plan->d.top_k;
+  const int32_t n = n_tokens >= 1 ? n_tokens : 1;
+  if (arm == kArmGemv) {
+    const double rows = mode == kModeGateUp ? plan->d.inter : plan->d.hidden;
+    const double tall_tasks = fill_woken_experts(n, k, E) * rows / 32.0;
+    return tall_tasks >= 2048.0 ? 4 : 2;
+  }
+  const double ppe = fill_pairs_per_woken_expert(n, k, E);
+  if (mode == kModeGateUp) return ppe < 4.0 ? 1 : (ppe < 20.0 ? 6 : 4);
+  return ppe < 8.0 ? 3 : 7;
 }
 
-// A variant whose task height does not divide `rows` falls back to the 16-row configuration
-// with the same number of waves.
+// A variant whose task height does not divide `rows` falls back to the next shorter task of the
+// same family (64 -> 32 rows), then to the 16-row configuration with the same register budget.
 int fit_variant(int variant, int arm, int32_t rows) {
   VariantInfo v{};
-  if (variant_info(variant, arm, v) && rows % v.rows_per_task == 0) return variant;
-  return (variant_info(variant, arm, v) && v.waves == 8) ? 2 : 1;
+  if (!variant_info(variant, arm, v)) return 1;
+  if (rows % v.rows_per_task == 0) return variant;
+  if (rows % 32 == 0 && v.rows_per_task == 64) return v.waves == 12 ? 6 : 4;
+  return v.waves == 8 ? 2 : 1;
 }
+
 thread_local std::string g_detail;
 
 qtip_status fail(qtip_status s, const std::string& what) {

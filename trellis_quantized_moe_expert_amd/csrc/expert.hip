@@ -210,7 +210,7 @@ __device__ inline RunSet<NT> load_runs(const uint8_t* __restrict__ base, uint32_
 
 // Grouped arm: NS row blocks of 16 pairs x NT row blocks of 16 outputs share one decode of
 // the 16*NT rows; each A fragment feeds NT MFMAs.
-template <int MODE, int NS, int NT>
+template <int MODE, int NS, int NT, bool APRE>
 __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -240,13 +240,27 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
   // (the block after the last wraps to block 0 and is not used), so waiting for the
   // activations never waits for those codes (memory counters retire in order) and the
   // codes have the whole block's decode to arrive.
+  // With APRE the activations are double-buffered as well: block kb+1's are requested during
+  // block kb, so every wait in the loop is for loads issued a whole block earlier.
+  u32x4 an[NS][4];
+  if (APRE) load_a_block<NS>(an, p.act, aoff, 0);
   RunSet<NT> n0 = load_runs<NT>(base0, roff, nt_stride, g * 8, row_bytes);
   RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(base1, roff, nt_stride, g * 8, row_bytes) : n0;
   for (int kb = 0; kb < kblocks; ++kb) {
+    const int kn = kb + 1 < kblocks ? kb + 1 : 0;
     u32x4 a[NS][4];
-    load_a_block<NS>(a, p.act, aoff, kb);
+    if (APRE) {
+#pragma unroll
+      for (int m = 0; m < NS; ++m) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) a[m][st] = an[m][st];
+      }
+      load_a_block<NS>(an, p.act, aoff, kn);
+    } else {
+      load_a_block<NS>(a, p.act, aoff, kb);
+    }
     const RunSet<NT> c0 = n0, c1 = n1;
-    const int ob = (kb + 1 < kblocks ? kb + 1 : 0) * 32 + g * 8;
+    const int ob = kn * 32 + g * 8;
     n0 = load_runs<NT>(base0, roff, nt_stride, ob, row_bytes);
     if (MODE == kModeGateUp) n1 = load_runs<NT>(base1, roff, nt_stride, ob, row_bytes);
 #pragma unroll
@@ -294,7 +308,7 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
 }
 
 // GEMV arm: NQ pairs x NT row blocks of 16 outputs share one decode; VALU bf16 dot products.
-template <int MODE, int NQ, int NT>
+template <int MODE, int NQ, int NT, bool APRE>
 __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -316,13 +330,25 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
     for (int nt = 0; nt < NT; ++nt) acc0[q][nt] = acc1[q][nt] = 0.f;
   }
 
+  u32x4 xn[NQ][4];
+  if (APRE) load_a_block<NQ>(xn, p.act, xoff, 0);
   RunSet<NT> n0 = load_runs<NT>(base0, roff, nt_stride, g * 8, row_bytes);
   RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(base1, roff, nt_stride, g * 8, row_bytes) : n0;
   for (int kb = 0; kb < kblocks; ++kb) {
+    const int kn = kb + 1 < kblocks ? kb + 1 : 0;
     u32x4 x[NQ][4];
-    load_a_block<NQ>(x, p.act, xoff, kb);
+    if (APRE) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) x[q][st] = xn[q][st];
+      }
+      load_a_block<NQ>(xn, p.act, xoff, kn);
+    } else {
+      load_a_block<NQ>(x, p.act, xoff, kb);
+    }
     const RunSet<NT> c0 = n0, c1 = n1;
-    const int ob = (kb + 1 < kblocks ? kb + 1 : 0) * 32 + g * 8;
+    const int ob = kn * 32 + g * 8;
     n0 = load_runs<NT>(base0, roff, nt_stride, ob, row_bytes);
     if (MODE == kModeGateUp) n1 = load_runs<NT>(base1, roff, nt_stride, ob, row_bytes);
 #pragma unroll
@@ -377,12 +403,17 @@ template <int WAVES, int NT, int NSUB, int GPAIRS>
 struct ExpertCfg {
   static constexpr int kWaves = WAVES, kNT = NT, kNSub = NSUB, kGPairs = GPAIRS;
   static constexpr int kRows = 16 * NT;
+  // Activation double-buffering where the register budget allows it: 512 VGPRs per SIMD lane
+  // shared by WAVES/4 waves (168 at 12 waves, where the 4-block task would spill).
+  static constexpr bool kAPre = WAVES <= 8 || NT <= 2;
 };
 using Cfg1 = ExpertCfg<16, 1, 2, 2>;
 using Cfg2 = ExpertCfg<8, 1, 4, 4>;
 using Cfg3 = ExpertCfg<16, 2, 2, 2>;
 using Cfg4 = ExpertCfg<8, 2, 4, 4>;
 using Cfg5 = ExpertCfg<8, 4, 2, 2>;
+using Cfg6 = ExpertCfg<12, 2, 2, 2>;
+using Cfg7 = ExpertCfg<12, 4, 2, 2>;
 
 // A unit may hold more pairs than one decode serves; it is then processed in chunks, each
 // chunk decoding the rows again.  Each chunk runs the body specialised for its exact number
@@ -390,23 +421,24 @@ using Cfg5 = ExpertCfg<8, 4, 2, 2>;
 template <int MODE, int ARM, class CFG>
 __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   constexpr int NT = CFG::kNT;
+  constexpr bool AP = CFG::kAPre;
   constexpr int kChunk = (ARM == kArmGrouped) ? CFG::kNSub * 16 : CFG::kGPairs;
   static_assert(CFG::kNSub >= 1 && CFG::kNSub <= 4 && CFG::kGPairs >= 1 && CFG::kGPairs <= 4, "config");
   for (int c0 = 0; c0 < un.len; c0 += kChunk) {
     const Unit part{un.e, un.start + c0, min(kChunk, un.len - c0)};
     if (ARM == kArmGrouped) {
       switch ((part.len + 15) >> 4) {
-        case 1: task_grouped<MODE, 1, NT>(p, lut, part, r0); break;
-        case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT>(p, lut, part, r0); break;
-        case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT>(p, lut, part, r0); break;
-        default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT>(p, lut, part, r0); break;
+        case 1: task_grouped<MODE, 1, NT, AP>(p, lut, part, r0); break;
+        case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP>(p, lut, part, r0); break;
+        case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT, AP>(p, lut, part, r0); break;
+        default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT, AP>(p, lut, part, r0); break;
       }
     } else {
       switch (part.len) {
-        case 1: task_gemv<MODE, 1, NT>(p, lut, part, r0); break;
-        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT>(p, lut, part, r0); break;
-        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT>(p, lut, part, r0); break;
-        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT>(p, lut, part, r0); break;
+        case 1: task_gemv<MODE, 1, NT, AP>(p, lut, part, r0); break;
+        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP>(p, lut, part, r0); break;
+        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP>(p, lut, part, r0); break;
+        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP>(p, lut, part, r0); break;
       }
     }
   }
@@ -528,6 +560,8 @@ bool variant_info(int variant, int arm, VariantInfo& v) {
     case 3: CfgInfo<Cfg3>::get(arm, v); return true;
     case 4: CfgInfo<Cfg4>::get(arm, v); return true;
     case 5: CfgInfo<Cfg5>::get(arm, v); return true;
+    case 6: CfgInfo<Cfg6>::get(arm, v); return true;
+    case 7: CfgInfo<Cfg7>::get(arm, v); return true;
     default: return false;
   }
 }
@@ -539,6 +573,8 @@ hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, 
     case 3: launch_cfg<Cfg3>(mode, arm, p, grid, stream); break;
     case 4: launch_cfg<Cfg4>(mode, arm, p, grid, stream); break;
     case 5: launch_cfg<Cfg5>(mode, arm, p, grid, stream); break;
+    case 6: launch_cfg<Cfg6>(mode, arm, p, grid, stream); break;
+    case 7: launch_cfg<Cfg7>(mode, arm, p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
