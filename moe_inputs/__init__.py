@@ -18,6 +18,10 @@ Draw order from one numpy PCG64 generator is fixed: the LUT, then for each exper
 e = 0..E-1 the gate codes, gate scales, up codes, up scales, down codes, down
 scales, then the activations, then the logits.  The arrays are plain numpy arrays;
 bf16 values are carried as their uint16 bit patterns.
+
+For layers that start from hidden states, a router weight [E, H] of N(0, 1/H)
+samples rounded to bf16 comes from a second generator, PCG64([seed, 1]), so the
+draws above do not change; with N(0,1) activations its logits are close to N(0,1).
 """
 from __future__ import annotations
 
@@ -140,6 +144,13 @@ def make_inputs_multi(shape: MoEShape, n_list, seed: int = 0) -> dict:
         x = f32_to_bf16_bits(r.standard_normal((n, s.hidden)).astype(np.float32))
         out[n] = MoEInputs(s, seed, lut, *weights, x, _draw_logits(r, s))
     return out
+
+
+def make_router_weight(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    """Router weight [E, H] as bf16 bit patterns: N(0, 1/H) samples from PCG64([seed, 1])."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1]))
+    w = rng.standard_normal((shape.num_experts, shape.hidden)) / np.sqrt(shape.hidden)
+    return f32_to_bf16_bits(w.astype(np.float32))
 
 
 def make_workload(name: str, seed: int = 0, n_tokens: Optional[int] = None) -> MoEInputs:
