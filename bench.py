@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + packed-weight HBM GB/s (% peak) vs token count n"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
 # VALU decode ceiling: 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-ops/s at 2 ops per symbol.
 DECODE_VALU_PEAK_SYMS = 256 * 64 * 2.4e9 / 2
 # LDS random-gather ceiling (the one that binds): 32 banks of 4 bytes, a wave64 read served as two
@@ -125,6 +126,52 @@ def timed(runner, steps, warmup, profile=True):
     if profile:
         q.qtip_moe_profile_enable(runner.plan, 0)
     return {"wall_s": t1 - t0, "gpu_ms": ev0.elapsed_time(ev1), "stats": stats, "prof": prof}
+
+
+def measure_router(runner, inp, calls=200, layers=50):
+    """Router GEMM (qtip_moe_router_logits) per-call time from HIP events on the launch stream,
+    and the layer from hidden states (qtip_moe_forward_hidden) in tokens/s, on this batch."""
+    import numpy as np
+    import torch
+    import moe_inputs
+    q, s, n = runner.q, runner.shape, runner.n
+    w = moe_inputs.make_router_weight(s, seed=0)
+    w_dev = torch.from_numpy(w.view(np.int16)).to("cuda:0")
+    lg = torch.empty((n, s.num_experts), dtype=torch.float32, device="cuda:0")
+    call = lambda: q.qtip_moe_router_logits(runner.plan, runner.tok.x, w_dev, n, lg, runner.ws, runner.ws.numel(),
+                                            runner.stream)
+    layer = lambda: q.qtip_moe_forward_hidden(runner.plan, runner.w, w_dev, runner.tok.x, n, runner.out, runner.ws,
+                                              runner.ws.numel(), runner.stream)
+    for _ in range(10):
+        call()
+        layer()
+    torch.cuda.synchronize()
+    q.qtip_moe_stats_reset(runner.plan)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record(runner.stream)
+    for _ in range(calls):
+        call()
+    e[1].record(runner.stream)
+    e[2].record(runner.stream)
+    for _ in range(layers):
+        layer()
+    e[3].record(runner.stream)
+    torch.cuda.synchronize()
+    st = q.qtip_moe_stats_get(runner.plan)
+    if st["router_launches"] != calls + layers or st["forward_calls"] != layers:
+        print(f"bench: router counters do not match the calls made: {st}", file=sys.stderr)
+        sys.exit(2)
+    call_s = e[0].elapsed_time(e[1]) * 1e-3 / calls
+    layer_s = e[2].elapsed_time(e[3]) * 1e-3 / layers
+    S = q.qtip_moe_router_split(runner.plan, n)
+    flops = 2.0 * n * s.hidden * s.num_experts
+    nbytes = 2.0 * s.num_experts * s.hidden + 2.0 * n * s.hidden + 4.0 * n * s.num_experts
+    if S > 1:
+        nbytes += 2 * 4.0 * S * n * s.num_experts     # partial sums written, then read by the reduction
+    return {"split": S, "us_per_call": call_s * 1e6, "flops": flops, "tflops": flops / call_s / 1e12,
+            "mfma_bf16_frac": flops / call_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, "bytes": nbytes,
+            "gbs": nbytes / call_s / 1e9, "hbm_frac": nbytes / call_s / 1e9 / HBM_PEAK_GBS,
+            "forward_hidden_ms": layer_s * 1e3, "forward_hidden_tokens_per_s": n / layer_s}
 
 
 def schedule_figures(counts, shape, arm, sched):
@@ -325,6 +372,7 @@ def main():
     res = timed(runner, args.steps, args.warmup)
     counts, n_tiles = runner.routing_counts()
     sched = runner.q.qtip_moe_plan_schedule(runner.plan, s.n_tokens)
+    router = measure_router(runner, inp)
     runner.close()
 
     if res["wall_s"] <= 0 or res["prof"]["n_forwards"] <= 0:
@@ -373,6 +421,7 @@ def main():
                                 "frac_measured": gu_syms / gather_measured,
                                 "valu_peak": DECODE_VALU_PEAK_SYMS, "frac_valu": gu_syms / DECODE_VALU_PEAK_SYMS},
             "schedule": sched,
+            "router_gemm": router,
             "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "route_launches",
                                                          "combine_launches")},
             "kernel_source_sha": kernel_source_sha(),

@@ -119,6 +119,7 @@ typedef struct qtip_moe_stats {
   uint64_t grouped_launches;  /* expert-matrix kernel launches on the grouped arm */
   uint64_t route_launches;    /* routing / binning kernel launches */
   uint64_t combine_launches;  /* combine kernel launches */
+  uint64_t router_launches;   /* router GEMM launches (qtip_moe_forward_hidden, qtip_moe_router_logits) */
   int32_t last_arm;           /* arm taken by the last forward (QTIP_ARM_GEMV / _GROUPED) */
   int32_t last_n_tokens;      /* n of the last forward */
 } qtip_moe_stats;
@@ -190,6 +191,33 @@ int32_t qtip_fill_min_tokens(int32_t k, int32_t E, int32_t tile_m);             
 qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w /*host struct of device ptrs*/,
                              const void* x_bf16, const float* logits, int32_t n_tokens, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- router GEMM (794-ms-decode-step page, PR #202, closing list of remaining
+ * un-owned items, item (3): the router GEMM ahead of top-k, moved from FP32 scalar
+ * cores to the matrix units) ---------------------------------------------------------
+ * logits[t][e] = sum_h x[t][h] * w_router[e][h]: bf16 operands (both row-major, rows of
+ * H), fp32 accumulation on v_mfma_f32_16x16x32_bf16, no bias.  The sum over h is split
+ * into S = qtip_moe_router_split(plan, n) chunks of H/S inputs (a divisor of H/128 chosen
+ * from n, E and H only); each chunk is summed on the matrix cores and the chunks are added
+ * in ascending order, so for a given n both entry points below produce bit-identical
+ * logits.  Any order of fp32 additions errs by at most 2 H 2^-24 sum_h |x w| (per logit).
+ *
+ * qtip_moe_router_logits: writes logits [n][E] fp32 (device).  x [n][H] and w_router [E][H]
+ *   are device bf16, 16-byte aligned; the workspace is the forward's (same size rule).
+ *   Errors as qtip_moe_forward (NULL -> INVALID_ARG, n out of [1, max_tokens] ->
+ *   INVALID_CONFIG, small or misaligned workspace -> INVALID_ARG, launch -> HIP).
+ * qtip_moe_forward_hidden: the layer of qtip_moe_forward with its logits computed by the
+ *   router GEMM from x (the logits stay in the workspace); out equals
+ *   qtip_moe_forward(x, qtip_moe_router_logits(x)) bit for bit.  Errors as
+ *   qtip_moe_forward; w_router NULL or misaligned -> INVALID_ARG.
+ * qtip_moe_router_split: S for n tokens, or -1 for a bad plan/n (host only). */
+qtip_status qtip_moe_router_logits(qtip_moe_plan_t plan, const void* x_bf16, const void* w_router_bf16,
+                                   int32_t n_tokens, float* logits, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+qtip_status qtip_moe_forward_hidden(qtip_moe_plan_t plan, const qtip_moe_weights* w /*host struct of device ptrs*/,
+                                    const void* w_router_bf16, const void* x_bf16, int32_t n_tokens, void* out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+int32_t qtip_moe_router_split(qtip_moe_plan_t plan, int32_t n_tokens);
 
 /* ---- routing and binning alone (bit-exact testing of the routing launcher) ----------
  *   topk_idx [n][k] int32, topk_w [n][k] fp32, counts [E], offsets [E+1] (exclusive

@@ -180,6 +180,43 @@ def test_default_kernel_shapes_follow_the_measured_rules():
     q.qtip_moe_plan_destroy(plan)
 
 
+def test_router_argument_errors_return_before_any_launch():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    ws = q.qtip_moe_plan_info(plan)["workspace_bytes"]
+    lib = q.lib()
+    rl = lambda x, wr, n, lg, wsp, wsb: lib.qtip_moe_router_logits(plan, x, wr, n, lg, wsp, wsb, None)
+    assert rl(256, 256, 0, 256, 256, ws) == q.QTIP_ERR_INVALID_CONFIG
+    assert rl(256, 256, 1025, 256, 256, ws) == q.QTIP_ERR_INVALID_CONFIG
+    assert rl(None, 256, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG
+    assert rl(256, None, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG
+    assert rl(256, 264, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG              # misaligned router weight
+    assert rl(256, 256, 4, 256, 256, ws - 1) == q.QTIP_ERR_INVALID_ARG
+    w = q.qtip_moe_weights(256, 256, 256, 256, 256, 256, 256)
+    fh = lambda wr, x, n, out, wsp, wsb: lib.qtip_moe_forward_hidden(plan, ctypes.byref(w), wr, x, n, out, wsp, wsb,
+                                                                      None)
+    assert fh(None, 256, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG
+    assert fh(264, 256, 4, 256, 256, ws) == q.QTIP_ERR_INVALID_ARG
+    assert fh(256, 256, 0, 256, 256, ws) == q.QTIP_ERR_INVALID_CONFIG
+    assert fh(256, 256, 4, 256, 256, ws - 1) == q.QTIP_ERR_INVALID_ARG
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_router_split_divides_the_input_blocks():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    # 32-expert x 32-token tiles, about 256 workgroups, at most 4 chunks: n=32 -> 8 tiles -> 4
+    # chunks; n=1024 -> 256 tiles -> 1
+    assert q.qtip_moe_router_split(plan, 32) == 4
+    assert q.qtip_moe_router_split(plan, 1024) == 1
+    for n in (1, 7, 33, 100, 683):
+        S = q.qtip_moe_router_split(plan, n)
+        assert S >= 1 and (4096 // 128) % S == 0
+    assert q.qtip_moe_router_split(plan, 0) == -1
+    q.qtip_moe_plan_destroy(plan)
+    tiny = q.qtip_moe_plan_for_arch(q.make_desc(8, 2, 256, 128, 16), "gfx950")
+    assert q.qtip_moe_router_split(tiny, 16) == 2
+    q.qtip_moe_plan_destroy(tiny)
+
+
 def test_gather_calibration_argument_errors():
     lib = q.lib()
     out = ctypes.c_double()

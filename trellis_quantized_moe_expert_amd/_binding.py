@@ -44,7 +44,8 @@ class qtip_moe_weights(ctypes.Structure):
 class qtip_moe_stats(ctypes.Structure):
     _fields_ = [("forward_calls", ctypes.c_uint64), ("gemv_launches", ctypes.c_uint64),
                 ("grouped_launches", ctypes.c_uint64), ("route_launches", ctypes.c_uint64),
-                ("combine_launches", ctypes.c_uint64), ("last_arm", ctypes.c_int32),
+                ("combine_launches", ctypes.c_uint64), ("router_launches", ctypes.c_uint64),
+                ("last_arm", ctypes.c_int32),
                 ("last_n_tokens", ctypes.c_int32)]
 
 
@@ -78,6 +79,10 @@ _SIGS = {
     "qtip_fill_select_grouped": (_I32, [_I32, _I32, _I32, _I32]),
     "qtip_fill_min_tokens": (_I32, [_I32, _I32, _I32]),
     "qtip_moe_forward": (_I32, [_P, ctypes.POINTER(qtip_moe_weights), _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+    "qtip_moe_forward_hidden": (_I32, [_P, ctypes.POINTER(qtip_moe_weights), _P, _P, _I32, _P, _P, ctypes.c_size_t,
+                                       _P]),
+    "qtip_moe_router_logits": (_I32, [_P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+    "qtip_moe_router_split": (_I32, [_P, _I32]),
     "qtip_moe_route": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "qtip_expert_matmul": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _P]),
     "qtip_moe_stats_get": (_I32, [_P, ctypes.POINTER(qtip_moe_stats)]),
@@ -211,6 +216,25 @@ def qtip_moe_forward(plan, weights: qtip_moe_weights, x_bf16, logits, n_tokens, 
     _check("qtip_moe_forward", lib().qtip_moe_forward(plan, ctypes.byref(weights), _ptr(x_bf16), _ptr(logits),
                                                       n_tokens, _ptr(out), _ptr(workspace), workspace_bytes,
                                                       _stream(stream)))
+
+
+def qtip_moe_forward_hidden(plan, weights: qtip_moe_weights, w_router_bf16, x_bf16, n_tokens, out, workspace,
+                            workspace_bytes, stream=None) -> None:
+    _check("qtip_moe_forward_hidden", lib().qtip_moe_forward_hidden(plan, ctypes.byref(weights), _ptr(w_router_bf16),
+                                                                    _ptr(x_bf16), n_tokens, _ptr(out),
+                                                                    _ptr(workspace), workspace_bytes,
+                                                                    _stream(stream)))
+
+
+def qtip_moe_router_logits(plan, x_bf16, w_router_bf16, n_tokens, logits, workspace, workspace_bytes,
+                           stream=None) -> None:
+    _check("qtip_moe_router_logits", lib().qtip_moe_router_logits(plan, _ptr(x_bf16), _ptr(w_router_bf16), n_tokens,
+                                                                  _ptr(logits), _ptr(workspace), workspace_bytes,
+                                                                  _stream(stream)))
+
+
+def qtip_moe_router_split(plan, n_tokens) -> int:
+    return lib().qtip_moe_router_split(plan, n_tokens)
 
 
 def qtip_moe_route(plan, logits, n_tokens, topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles,

@@ -13,7 +13,7 @@ import subprocess
 import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/api.hip", "csrc/route.hip", "csrc/expert.hip"]
+SOURCES = ["csrc/api.hip", "csrc/route.hip", "csrc/expert.hip", "csrc/router.hip"]
 OUTPUT = os.path.join(_HERE, "libqtip_moe.so")
 ARCH = "gfx950"
 

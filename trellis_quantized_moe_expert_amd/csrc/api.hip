@@ -106,8 +106,22 @@ bool arch_is_supported(const char* name) { return name != nullptr && std::strncm
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, h, y, total;
+  size_t topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, h, y, router_part,
+      total;
 };
+
+// Largest router-GEMM partial buffer, S(n) * n * E floats, over the batch sizes a plan accepts.
+// From 32 * kRouterTargetGroups tokens on there are enough tiles for a split of 1, so n_max
+// bounds the rest.
+size_t router_part_elems(const qtip_moe_desc& d, int32_t n_max) {
+  size_t best = (size_t)n_max * (size_t)d.num_experts;
+  const int32_t scan = n_max < 32 * kRouterTargetGroups ? n_max : 32 * kRouterTargetGroups;
+  for (int32_t n = 1; n <= scan; ++n) {
+    const size_t e = (size_t)router_split(n, d.num_experts, d.hidden) * (size_t)n * (size_t)d.num_experts;
+    if (e > best) best = e;
+  }
+  return best;
+}
 
 WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens) {
   const size_t P = (size_t)n_tokens * d.top_k;
@@ -127,6 +141,7 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens) {
   L.n_units = o;      o = align256(o + 4);
   L.h = o;            o = align256(o + P * (size_t)d.inter * 2);
   L.y = o;            o = align256(o + P * (size_t)d.hidden * 4);
+  L.router_part = o;  o = align256(o + router_part_elems(d, n_tokens) * 4);
   L.total = o;
   return L;
 }
@@ -224,6 +239,8 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
     return fail(QTIP_ERR_INVALID_ARG, "max_tokens * top_k * max(hidden, inter) must be below 2^31");
   if ((int64_t)d->hidden * d->inter / 4 >= ((int64_t)1 << 31))
     return fail(QTIP_ERR_INVALID_ARG, "one expert matrix must be below 2^31 bytes");
+  if ((int64_t)d->num_experts * d->hidden >= ((int64_t)1 << 31))
+    return fail(QTIP_ERR_INVALID_ARG, "num_experts * hidden (the router weight) must be below 2^31 elements");
   if (d->arm_override != QTIP_ARM_AUTO && d->arm_override != QTIP_ARM_GEMV && d->arm_override != QTIP_ARM_GROUPED)
     return fail(QTIP_ERR_INVALID_ARG, "unknown arm_override");
   if (d->out_dtype != QTIP_OUT_BF16 && d->out_dtype != QTIP_OUT_F32) return fail(QTIP_ERR_INVALID_ARG, "unknown out_dtype");
@@ -393,7 +410,7 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
   qtip_status s = ensure_device(plan, st, &dev);
   if (s != QTIP_OK) return s;
   const qtip_moe_desc& d = plan->d;
-  hipError_t e = launch_route_topk(logits, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
+  hipError_t e = launch_route_topk(logits, 1, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
   if (e != hipSuccess) return hip_fail(e, "route_topk launch");
   plan->stats.route_launches++;
   e = launch_bin(topk_idx, n_tokens * d.top_k, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets,
@@ -449,10 +466,20 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
   return QTIP_OK;
 }
 
-qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, const void* x_bf16, const float* logits,
-                             int32_t n_tokens, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer from router logits (logits != NULL) or from hidden states through the router
+// GEMM (w_router != NULL; its K-chunk partial sums go to the workspace and the top-k kernel
+// adds them).
+qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const void* x_bf16, const float* logits,
+                         const void* w_router, int32_t n_tokens, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   g_detail.clear();
-  if (!plan || !w || !x_bf16 || !logits || !out || !workspace) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (!plan || !w || !x_bf16 || !(logits || w_router) || !out || !workspace)
+    return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (reinterpret_cast<uintptr_t>(w_router) & 15) return fail(QTIP_ERR_INVALID_ARG, "w_router must be 16-byte aligned");
   if (!w->codes_gate || !w->codes_up || !w->codes_down || !w->scale_gate || !w->scale_up || !w->scale_down || !w->lut)
     return fail(QTIP_ERR_INVALID_ARG, "NULL weight pointer");
   if ((reinterpret_cast<uintptr_t>(w->lut) & 15) || (reinterpret_cast<uintptr_t>(x_bf16) & 15) ||
@@ -488,7 +515,18 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
 
   hipError_t e = prof_mark(plan, 0, st);
   if (e != hipSuccess) return hip_fail(e, "profile event");
-  e = launch_route_topk(logits, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
+  const float* lg = logits;
+  int32_t n_part = 1;
+  if (w_router) {
+    n_part = router_split(n_tokens, d.num_experts, d.hidden);
+    float* part = reinterpret_cast<float*>(ws + L.router_part);
+    e = launch_router_gemm(reinterpret_cast<const uint16_t*>(x_bf16), reinterpret_cast<const uint16_t*>(w_router),
+                           n_tokens, d.num_experts, d.hidden, n_part, xcd_count(dev), part, st);
+    if (e != hipSuccess) return hip_fail(e, "router GEMM launch");
+    plan->stats.router_launches++;
+    lg = part;
+  }
+  e = launch_route_topk(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
   if (e != hipSuccess) return hip_fail(e, "route_topk launch");
   if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
   e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets, sorted_pair, tile_map,
@@ -557,6 +595,65 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, co
   plan->stats.last_arm = arm;
   plan->stats.last_n_tokens = n_tokens;
   return QTIP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w, const void* x_bf16, const float* logits,
+                             int32_t n_tokens, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits) {
+    g_detail.clear();
+    return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  }
+  return forward_impl(plan, w, x_bf16, logits, nullptr, n_tokens, out, workspace, workspace_bytes, stream);
+}
+
+qtip_status qtip_moe_forward_hidden(qtip_moe_plan_t plan, const qtip_moe_weights* w, const void* w_router_bf16,
+                                    const void* x_bf16, int32_t n_tokens, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!w_router_bf16) {
+    g_detail.clear();
+    return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  }
+  return forward_impl(plan, w, x_bf16, nullptr, w_router_bf16, n_tokens, out, workspace, workspace_bytes, stream);
+}
+
+qtip_status qtip_moe_router_logits(qtip_moe_plan_t plan, const void* x_bf16, const void* w_router_bf16,
+                                   int32_t n_tokens, float* logits, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  g_detail.clear();
+  if (!plan || !x_bf16 || !w_router_bf16 || !logits || !workspace) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if ((reinterpret_cast<uintptr_t>(x_bf16) & 15) || (reinterpret_cast<uintptr_t>(w_router_bf16) & 15))
+    return fail(QTIP_ERR_INVALID_ARG, "x and w_router must be 16-byte aligned");
+  if (n_tokens <= 0 || n_tokens > plan->d.max_tokens)
+    return fail(QTIP_ERR_INVALID_CONFIG, "n_tokens must be in [1, max_tokens] (an empty launch is an error)");
+  if (workspace_bytes < plan->ws_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(QTIP_ERR_INVALID_ARG, "workspace too small or not 256-byte aligned");
+  const hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  qtip_status s = ensure_device(plan, st, &dev);
+  if (s != QTIP_OK) return s;
+  const qtip_moe_desc& d = plan->d;
+  const int32_t S = router_split(n_tokens, d.num_experts, d.hidden);
+  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens);
+  float* part = S == 1 ? logits : reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.router_part);
+  hipError_t e = launch_router_gemm(reinterpret_cast<const uint16_t*>(x_bf16),
+                                    reinterpret_cast<const uint16_t*>(w_router_bf16), n_tokens, d.num_experts,
+                                    d.hidden, S, xcd_count(dev), part, st);
+  if (e != hipSuccess) return hip_fail(e, "router GEMM launch");
+  plan->stats.router_launches++;
+  if (S > 1) {
+    e = launch_router_reduce(part, S, (int64_t)n_tokens * d.num_experts, logits, st);
+    if (e != hipSuccess) return hip_fail(e, "router reduce launch");
+  }
+  return QTIP_OK;
+}
+
+int32_t qtip_moe_router_split(qtip_moe_plan_t plan, int32_t n_tokens) {
+  if (!plan || n_tokens < 1) return -1;
+  return router_split(n_tokens, plan->d.num_experts, plan->d.hidden);
 }
 
 qtip_status qtip_moe_profile_enable(qtip_moe_plan_t plan, int32_t capacity) {

@@ -21,6 +21,9 @@ constexpr int kBinThreads = 1024;      // binning runs in one workgroup (16 wave
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kWitnessValue = 0x950950;
+constexpr int kRouterMaxWaves = 8;        // waves of a router-GEMM workgroup (they split its input chunk)
+constexpr int kRouterTargetGroups = 256;  // router-GEMM workgroups wanted: one per CU
+constexpr int kRouterMaxSplit = 4;        // input chunks (partial sums) per logit at most
 
 // One pass of one (or two fused) trellis matrices over binned activation rows.
 struct ExpertParams {
@@ -57,8 +60,20 @@ struct VariantInfo {
 bool variant_info(int variant, int arm, VariantInfo& v);
 hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, hipStream_t stream);
 
-hipError_t launch_route_topk(const float* logits, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
-                             float* topk_w, hipStream_t stream);
+// Top-k over logits given as n_part partial sums part[s][t][e] (s-major, n*E apart), added in
+// ascending s; n_part = 1 reads plain logits.
+hipError_t launch_route_topk(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k,
+                             int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+// Router GEMM (hidden states -> logits).  router_split(n, E, H) is the number S of K chunks
+// (a divisor of H/128, at most kRouterMaxSplit) whose partial sums launch_router_gemm writes
+// to part[S][n][E]; launch_router_reduce adds them (ascending s) into logits[n][E].
+int32_t router_split(int32_t n, int32_t E, int32_t H);
+int32_t router_tiles(int32_t n, int32_t E);
+int32_t router_waves(int32_t H, int32_t S);
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w, int32_t n, int32_t E, int32_t H, int32_t S,
+                              int32_t n_xcd, float* part, hipStream_t stream);
+hipError_t launch_router_reduce(const float* part, int32_t S, int64_t count, float* logits, hipStream_t stream);
 
 hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
                       int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map,

@@ -23,8 +23,8 @@ __device__ inline bool beats(float v, int e, float bv, int be) {
 
 // One wave per token.  Each lane holds up to 16 logits (E <= 1024); k rounds of a wave-wide
 // argmax under the order (value descending, index ascending) pick the experts in order.
-__global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const float* __restrict__ logits, int32_t n,
-                                                                    int32_t E, int32_t k,
+__global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const float* __restrict__ logits,
+                                                                    int32_t n_part, int32_t n, int32_t E, int32_t k,
                                                                     int32_t* __restrict__ topk_idx,
                                                                     float* __restrict__ topk_w) {
   __shared__ float sel[kRouteWaves][kMaxTopK];
@@ -33,11 +33,31 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const floa
   const int t = blockIdx.x * kRouteWaves + wv;
   if (t >= n) return;  // whole wave leaves together; no barrier follows
   const float* row = logits + (size_t)t * E;
+  const size_t part_stride = (size_t)n * (size_t)E;
   float v[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int e = lane + 64 * q;
     v[q] = (e < E) ? row[e] : 0.0f;
+  }
+  // partial sums of the router GEMM's K chunks, added in ascending chunk order; the loads of
+  // up to 4 chunks are issued before their additions so their latencies overlap
+  if (n_part > 1) {
+    for (int s = 1; s < n_part; s += 4) {
+      float t[4][16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int e = lane + 64 * q;
+          t[i][q] = (s + i < n_part && e < E) ? row[(size_t)(s + i) * part_stride + e] : 0.0f;
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (s + i < n_part) v[q] += t[i][q];
+    }
   }
   uint32_t taken = 0;
   for (int jj = 0; jj < k; ++jj) {
@@ -190,11 +210,11 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
 
 }  // namespace
 
-hipError_t launch_route_topk(const float* logits, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
-                             float* topk_w, hipStream_t stream) {
+hipError_t launch_route_topk(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k,
+                             int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   const int grid = (n + kRouteWaves - 1) / kRouteWaves;
-  hipLaunchKernelGGL(route_topk_kernel, dim3(grid), dim3(kRouteWaves * 64), 0, stream, logits, n, E, k, topk_idx,
-                     topk_w);
+  hipLaunchKernelGGL(route_topk_kernel, dim3(grid), dim3(kRouteWaves * 64), 0, stream, logits, n_part, n, E, k,
+                     topk_idx, topk_w);
   return hipGetLastError();
 }
 
