@@ -100,3 +100,32 @@ def test_expected_tiles_v4_values():
     assert fill.expected_tiles(1024, 6, 256, 16) == pytest.approx(509.6, abs=0.1)
     # one tile per woken expert while no expert can reach a second tile
     assert fill.expected_tiles(10, 6, 256, 16) == pytest.approx(fill.woken_experts(10, 6, 256), rel=1e-9)
+
+
+@pytest.mark.parametrize("k,E", [(k, E) for (k, E, tm) in SHAPES if tm == 16])
+def test_equal_constants_leave_no_dequantize_window(k, E):
+    # the Tests section: both boundary constants at 16 leave no n for the third arm
+    n_max = fill.min_tokens_grouped(k, E, 16) + 200
+    assert fill.dequant_tokens(k, E, 16, 16, n_max) == []
+    # and a grouped threshold at or below the traffic ratio keeps it closed as well
+    assert fill.dequant_tokens(k, E, 1, 16, n_max) == []
+
+
+@pytest.mark.parametrize("k,E", [(6, 256), (2, 8), (8, 128)])
+def test_a_higher_grouped_threshold_opens_the_window_exactly_between_the_flips(k, E):
+    # grouped threshold 32 with traffic ratio 16: the dequantize arm takes exactly the n with
+    # 16 <= pairs per woken expert < 32 above the decode floor, i.e. [min_tokens(16), min_tokens(32))
+    lo, hi = fill.min_tokens_grouped(k, E, 16), fill.min_tokens_grouped(k, E, 32)
+    got = fill.dequant_tokens(k, E, 32, 16, hi + 50)
+    assert got == list(range(lo, hi))
+    assert fill.select_arm(lo - 1, k, E, 32, 16) == "gemv"
+    assert fill.select_arm(hi, k, E, 32, 16) == "grouped"
+
+
+def test_three_arm_dispatch_v4_values():
+    # V4 (top-6 of 256): the fused GEMV below 683 tokens, grouped from 683 with both at 16
+    assert fill.select_arm(682, 6, 256, 16) == "gemv"
+    assert fill.select_arm(683, 6, 256, 16) == "grouped"
+    assert fill.select_arm(8, 6, 256, 1) == "gemv"        # decode floor
+    assert fill.select_arm(9, 6, 256, 1) == "grouped"
+    assert fill.select_arm(1000, 6, 256, 64) == "dequant"  # 16 <= 23.4 < 64
