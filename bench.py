@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the trellis-quantized MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--arm auto|gemv|grouped]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--arm auto|gemv|grouped|dequant]
 
 A step is one qtip_moe_forward (route, bin, gate+up, down, combine) over one batch of the
 workload, with weights and inputs already resident in HBM.  The default workload is the
@@ -65,7 +65,8 @@ class Runner:
         self.q = q
         s = inp.shape
         self.shape = s
-        arm_code = {"auto": q.QTIP_ARM_AUTO, "gemv": q.QTIP_ARM_GEMV, "grouped": q.QTIP_ARM_GROUPED}[arm]
+        arm_code = {"auto": q.QTIP_ARM_AUTO, "gemv": q.QTIP_ARM_GEMV, "grouped": q.QTIP_ARM_GROUPED,
+                    "dequant": q.QTIP_ARM_DEQUANT}[arm]
         od = q.QTIP_OUT_BF16 if out_dtype == "bf16" else q.QTIP_OUT_F32
         self.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens, arm_code,
                                                 variant, od, 0), 0)
@@ -309,7 +310,8 @@ def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=N
                 ms = res["wall_s"] * 1e3 / steps
                 rec = {"arm": arm, "n": n, "variant_requested": variant, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
                        "stage_ms": {k: v / res["prof"]["n_forwards"] for k, v in res["prof"].items() if k != "n_forwards"},
-                       "launches": {k: res["stats"][k] for k in ("gemv_launches", "grouped_launches")},
+                       "launches": {k: res["stats"][k] for k in ("gemv_launches", "grouped_launches",
+                                                                 "dequant_launches")},
                        "woken": fig["woken"], "decodes": fig["decodes"], "schedule": sched,
                        "predicate_grouped": r.q.qtip_fill_select_grouped(n, 6, 256, 16)}
                 f.write(json.dumps(rec) + "\n")
@@ -324,7 +326,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v4_decode_n32")
-    ap.add_argument("--arm", choices=["auto", "gemv", "grouped"], default="auto")
+    ap.add_argument("--arm", choices=["auto", "gemv", "grouped", "dequant"], default="auto")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 = the plan's choice, 1..7 fixed; see qtip_moe_plan_schedule)")
     ap.add_argument("--cpu-sample", type=int, default=6, help="tokens the CPU oracle is timed on, about 10 s (0: skip)")
@@ -367,7 +369,7 @@ def main():
     runner = Runner(inp, args.arm, s.n_tokens, args.out_dtype, variant=args.variant)
     runner.bind(inp)
     arm_code = runner.q.qtip_moe_select_arm(runner.plan, s.n_tokens)
-    arm = "grouped" if arm_code == runner.q.QTIP_ARM_GROUPED else "gemv"
+    arm = {runner.q.QTIP_ARM_GROUPED: "grouped", runner.q.QTIP_ARM_DEQUANT: "dequant"}.get(arm_code, "gemv")
     log(runner.q.qtip_moe_engaged_line(runner.plan, s.n_tokens))
     res = timed(runner, args.steps, args.warmup)
     counts, n_tiles = runner.routing_counts()
@@ -389,7 +391,8 @@ def main():
     layer_gpu_s = res["gpu_ms"] * 1e-3 / args.steps
     counters = res["stats"]
     if (arm == "grouped" and counters["grouped_launches"] != 2 * args.steps) or \
-       (arm == "gemv" and counters["gemv_launches"] != 2 * args.steps):
+       (arm == "gemv" and counters["gemv_launches"] != 2 * args.steps) or \
+       (arm == "dequant" and counters["dequant_launches"] != 4 * args.steps):
         print(f"bench: launch counters do not show the {arm} arm: {counters}", file=sys.stderr)
         sys.exit(2)
 
@@ -422,8 +425,8 @@ def main():
                                 "valu_peak": DECODE_VALU_PEAK_SYMS, "frac_valu": gu_syms / DECODE_VALU_PEAK_SYMS},
             "schedule": sched,
             "router_gemm": router,
-            "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "route_launches",
-                                                         "combine_launches")},
+            "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "dequant_launches",
+                                                         "route_launches", "combine_launches", "router_launches")},
             "kernel_source_sha": kernel_source_sha(),
         },
     }

@@ -67,7 +67,10 @@ typedef enum qtip_status {
   QTIP_ERR_CAPTURING = 5       /* the arch witness cannot be taken on a capturing stream */
 } qtip_status;
 
-enum { QTIP_ARM_AUTO = 0, QTIP_ARM_GEMV = 1, QTIP_ARM_GROUPED = 2 };
+/* Arms: the fused GEMV (per-pair decode + VALU dot products), the grouped arm (one decode
+ * shared by up to 64 binned pairs, MFMA), and the dequantize arm (the woken experts' weights
+ * materialised as dense bf16 in the workspace, then an MFMA pass over them). */
+enum { QTIP_ARM_AUTO = 0, QTIP_ARM_GEMV = 1, QTIP_ARM_GROUPED = 2, QTIP_ARM_DEQUANT = 3 };
 enum { QTIP_OUT_BF16 = 0, QTIP_OUT_F32 = 1 };
 
 /* Decode-regime floor: n <= 8 tokens always take the GEMV arm (m-tile page, "The fix"). */
@@ -79,6 +82,11 @@ enum { QTIP_OUT_BF16 = 0, QTIP_OUT_F32 = 1 };
  * anything; the measured GEMV/grouped crossover lies between 4 and 8 tokens at V4 routing,
  * i.e. at the decode-regime floor, which a threshold of 1 pair per woken expert reproduces. */
 #define QTIP_DEFAULT_DISPATCH_TILE_M 1
+/* Fused GEMV vs dequantize arm: the GEMV streams an expert's packed bytes once per pair;
+ * materialising writes and re-reads dense bf16, 2 x 16/2 = 16 times the packed bytes (m-tile
+ * page, "Tests": the constant, and the rule that it must not leave a dequantize window below
+ * the grouped boundary). */
+#define QTIP_DEFAULT_DEQUANT_TRAFFIC_RATIO 16
 /* One decode of an expert's weights is shared by up to this many binned pairs. */
 #define QTIP_UNIT_MAX_PAIRS 64
 /* Inputs per K block: H and I must be multiples of this; rows a multiple of 16. */
@@ -90,7 +98,7 @@ typedef struct qtip_moe_desc {
   int32_t hidden;       /* H: gate/up inputs and down outputs; multiple of 128 */
   int32_t inter;        /* I: gate/up outputs and down inputs; multiple of 128 */
   int32_t max_tokens;   /* largest n a forward accepts (sizes the workspace), >= 1 */
-  int32_t arm_override; /* QTIP_ARM_AUTO (predicate), _GEMV or _GROUPED (pins the arm) */
+  int32_t arm_override; /* QTIP_ARM_AUTO (predicate), _GEMV, _GROUPED or _DEQUANT (pins the arm) */
   int32_t variant;      /* expert kernel configuration 1..7 for both passes, or 0 = chosen per arm,
                            pass and n by the plan (qtip_moe_plan_schedule reports it);
                            unknown: warning, 0 kept */
@@ -99,6 +107,12 @@ typedef struct qtip_moe_desc {
   int32_t dispatch_tile_m; /* the fill predicate's threshold in pairs per woken expert: 0 = the value
                               re-derived for these gfx950 kernels (QTIP_DEFAULT_DISPATCH_TILE_M);
                               16 reproduces the pages' sm80 gate; 1..1024 accepted */
+  int32_t dequant_traffic_ratio; /* AUTO dispatch keeps the fused GEMV while pairs per woken expert
+                              are below this, and sends fills in [ratio, dispatch_tile_m) past the
+                              decode floor to the dequantize arm: 0 = 16; 1..1024 accepted.  A plan
+                              that can take the dequantize arm (that window is not empty, or the
+                              override pins it) holds every expert's dense bf16 weights in its
+                              workspace: 3 x E x H x I x 2 bytes, and needs H x I < 2^31. */
 } qtip_moe_desc;
 
 typedef struct qtip_moe_plan_s* qtip_moe_plan_t;
@@ -120,7 +134,8 @@ typedef struct qtip_moe_stats {
   uint64_t route_launches;    /* routing / binning kernel launches */
   uint64_t combine_launches;  /* combine kernel launches */
   uint64_t router_launches;   /* router GEMM launches (qtip_moe_forward_hidden, qtip_moe_router_logits) */
-  int32_t last_arm;           /* arm taken by the last forward (QTIP_ARM_GEMV / _GROUPED) */
+  uint64_t dequant_launches;  /* dequantize arm: materialise launches and dense expert-pass launches */
+  int32_t last_arm;           /* arm taken by the last forward (QTIP_ARM_GEMV / _GROUPED / _DEQUANT) */
   int32_t last_n_tokens;      /* n of the last forward */
 } qtip_moe_stats;
 
@@ -156,17 +171,29 @@ typedef struct qtip_moe_kernel_shape {
   int32_t pairs_per_decode;    /* binned pairs of one expert that share one decode of its rows */
 } qtip_moe_kernel_shape;
 typedef struct qtip_moe_schedule {
-  int32_t arm;                  /* QTIP_ARM_GEMV or QTIP_ARM_GROUPED */
+  int32_t arm;                  /* QTIP_ARM_GEMV, QTIP_ARM_GROUPED or QTIP_ARM_DEQUANT */
   int32_t tile_m;               /* m-tile height of the tile map and the predicate */
   qtip_moe_kernel_shape gate_up; /* the fused gate+up pass */
   qtip_moe_kernel_shape down;    /* the down pass */
 } qtip_moe_schedule;
 qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_moe_schedule* out /*host*/);
 
-/* The arm a forward of n tokens takes: the override if one is set, else the closed-form
- * predicate with the plan's dispatch_tile_m.  Returns QTIP_ARM_GEMV or QTIP_ARM_GROUPED, or -1
- * for a bad plan/n. */
+/* The arm a forward of n tokens takes: the override if one is set, else the three-arm closed
+ * form (qtip_fill_select_arm) with the plan's dispatch_tile_m and dequant_traffic_ratio.
+ * Returns QTIP_ARM_GEMV, QTIP_ARM_GROUPED or QTIP_ARM_DEQUANT, or -1 for a bad plan/n. */
 int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens);
+
+/* The token counts [*n_lo, *n_hi) within [1, max_tokens] that the automatic dispatch sends to
+ * the dequantize arm (empty, 0 and 0, when dispatch_tile_m <= dequant_traffic_ratio: the m-tile
+ * page's "Tests" section requires the two boundaries to leave no such window). Host only. */
+qtip_status qtip_moe_dequant_range(qtip_moe_plan_t plan, int32_t* n_lo /*host*/, int32_t* n_hi /*host*/);
+
+/* The dequantize arm's first step alone (also a dense reference of the decode): writes
+ * bf16(LUT[state]) of every weight of one expert's matrix (0 = gate [I][H], 1 = up [I][H],
+ * 2 = down [H][I]; scales not applied) to dense_out (device, row-major, 16-byte aligned).
+ * Errors: NULL, matrix or expert out of range, misalignment -> INVALID_ARG; launch -> HIP. */
+qtip_status qtip_moe_dequantize(qtip_moe_plan_t plan, const qtip_moe_weights* w /*host struct of device ptrs*/,
+                                int32_t matrix, int32_t expert, void* dense_out, void* stream);
 
 /* ---- closed-form fill model (m-tile page, "The cause is a threshold" and "The fix") --
  * Uniform routing of n tokens to k of E experts wakes E(1-(1-k/E)^n) experts on average;
@@ -176,6 +203,9 @@ double qtip_fill_woken_experts(int32_t n, int32_t k, int32_t E);
 double qtip_fill_pairs_per_woken_expert(int32_t n, int32_t k, int32_t E);
 int32_t qtip_fill_select_grouped(int32_t n, int32_t k, int32_t E, int32_t tile_m); /* 1 / 0, -1 bad args */
 int32_t qtip_fill_min_tokens(int32_t k, int32_t E, int32_t tile_m);                /* smallest n selected */
+/* Three-arm dispatch: QTIP_ARM_GROUPED if qtip_fill_select_grouped; else QTIP_ARM_GEMV if n <= 8
+ * or pairs per woken expert < dequant_ratio; else QTIP_ARM_DEQUANT.  -1 for bad arguments. */
+int32_t qtip_fill_select_arm(int32_t n, int32_t k, int32_t E, int32_t tile_m, int32_t dequant_ratio);
 
 /* ---- forward ----------------------------------------------------------------------
  * One MoE layer for n tokens: route, bin, gate+up (SwiGLU), down, combine.

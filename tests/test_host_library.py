@@ -47,8 +47,72 @@ def test_plan_for_arch_accepts_gfx950_and_reports_schedule():
 def test_dispatch_threshold_drives_the_predicate(thr, expect):
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, dispatch_tile_m=thr), "gfx950")
     assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == expect == fill.min_tokens_grouped(6, 256, thr)
-    assert q.qtip_moe_select_arm(plan, expect - 1) == q.QTIP_ARM_GEMV
+    # below the grouped flip: the fused GEMV, or the dequantize arm once the fill reaches the
+    # traffic ratio (16) under a higher grouped threshold
+    below = {"gemv": q.QTIP_ARM_GEMV, "dequant": q.QTIP_ARM_DEQUANT}[fill.select_arm(expect - 1, 6, 256, thr)]
+    assert q.qtip_moe_select_arm(plan, expect - 1) == below
+    assert below == (q.QTIP_ARM_DEQUANT if thr > 16 else q.QTIP_ARM_GEMV)
     assert q.qtip_moe_select_arm(plan, expect) == q.QTIP_ARM_GROUPED
+    q.qtip_moe_plan_destroy(plan)
+
+
+ARM_CODE = {"gemv": q.QTIP_ARM_GEMV, "grouped": q.QTIP_ARM_GROUPED, "dequant": q.QTIP_ARM_DEQUANT}
+
+
+def test_three_arm_closed_form_matches_the_oracle():
+    for k, E in [(6, 256), (2, 8), (8, 128), (1, 4), (6, 64)]:
+        for tm in (1, 16, 32, 64):
+            for ratio in (8, 16, 32):
+                for n in (1, 8, 9, 20, 100, 300, 683, 1000, 1500, 3000):
+                    assert q.qtip_fill_select_arm(n, k, E, tm, ratio) == ARM_CODE[fill.select_arm(n, k, E, tm, ratio)]
+    assert q.qtip_fill_select_arm(0, 6, 256, 16, 16) == -1
+    assert q.qtip_fill_select_arm(9, 6, 256, 16, 0) == -1
+
+
+@pytest.mark.parametrize("k,E", [(6, 256), (2, 8), (8, 128), (1, 4), (6, 64), (8, 256)])
+def test_default_boundaries_leave_no_dequantize_window(k, E):
+    for thr in (0, 16):
+        plan = q.qtip_moe_plan_for_arch(q.make_desc(E, k, 256, 128, 4096, dispatch_tile_m=thr), "gfx950")
+        assert q.qtip_moe_dequant_range(plan) == (0, 0)
+        assert all(q.qtip_moe_select_arm(plan, n) != q.QTIP_ARM_DEQUANT for n in range(1, 4097, 7))
+        q.qtip_moe_plan_destroy(plan)
+
+
+def test_a_window_is_reported_and_sized():
+    base = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    ws0 = q.qtip_moe_plan_info(base)["workspace_bytes"]
+    q.qtip_moe_plan_destroy(base)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, dispatch_tile_m=32), "gfx950")
+    lo, hi = q.qtip_moe_dequant_range(plan)
+    assert (lo, hi) == (fill.min_tokens_grouped(6, 256, 16), 1025)      # grouped flip (1366) is past max_tokens
+    assert fill.dequant_tokens(6, 256, 32, 16, 1024) == list(range(lo, hi))
+    assert q.qtip_moe_select_arm(plan, lo) == q.QTIP_ARM_DEQUANT and q.qtip_moe_select_arm(plan, lo - 1) == q.QTIP_ARM_GEMV
+    dense = 3 * 256 * 4096 * 2048 * 2
+    assert q.qtip_moe_plan_info(plan)["workspace_bytes"] >= ws0 + dense
+    q.qtip_moe_plan_destroy(plan)
+    pinned = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_DEQUANT), "gfx950")
+    assert q.qtip_moe_select_arm(pinned, 32) == q.QTIP_ARM_DEQUANT
+    assert q.qtip_moe_plan_info(pinned)["workspace_bytes"] >= ws0 + dense
+    sch = q.qtip_moe_plan_schedule(pinned, 32)
+    assert sch["arm"] == q.QTIP_ARM_DEQUANT and sch["gate_up"]["waves_per_workgroup"] == 16
+    q.qtip_moe_plan_destroy(pinned)
+    with pytest.raises(q.QtipError):
+        q.qtip_moe_plan_for_arch(q.make_desc(**V4, dequant_traffic_ratio=-1), "gfx950")
+
+
+def test_dequantize_argument_errors_return_before_any_launch():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    w = q.qtip_moe_weights(256, 256, 256, 256, 256, 256, 256)
+    lib = q.lib()
+    dq = lambda m, e, out: lib.qtip_moe_dequantize(plan, ctypes.byref(w), m, e, out, None)
+    assert dq(3, 0, 256) == q.QTIP_ERR_INVALID_ARG
+    assert dq(-1, 0, 256) == q.QTIP_ERR_INVALID_ARG
+    assert dq(0, 256, 256) == q.QTIP_ERR_INVALID_ARG
+    assert dq(0, -1, 256) == q.QTIP_ERR_INVALID_ARG
+    assert dq(0, 0, None) == q.QTIP_ERR_INVALID_ARG
+    assert dq(0, 0, 264) == q.QTIP_ERR_INVALID_ARG                # misaligned output
+    w.codes_down = 260
+    assert dq(2, 0, 256) == q.QTIP_ERR_INVALID_ARG                # misaligned codes
     q.qtip_moe_plan_destroy(plan)
 
 

@@ -24,6 +24,7 @@ QTIP_ERR_CAPTURING = 5
 QTIP_ARM_AUTO = 0
 QTIP_ARM_GEMV = 1
 QTIP_ARM_GROUPED = 2
+QTIP_ARM_DEQUANT = 3
 QTIP_OUT_BF16 = 0
 QTIP_OUT_F32 = 1
 
@@ -32,7 +33,7 @@ class qtip_moe_desc(ctypes.Structure):
     _fields_ = [("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("arm_override", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("dispatch_tile_m", ctypes.c_int32)]
+                ("dispatch_tile_m", ctypes.c_int32), ("dequant_traffic_ratio", ctypes.c_int32)]
 
 
 class qtip_moe_weights(ctypes.Structure):
@@ -45,6 +46,7 @@ class qtip_moe_stats(ctypes.Structure):
     _fields_ = [("forward_calls", ctypes.c_uint64), ("gemv_launches", ctypes.c_uint64),
                 ("grouped_launches", ctypes.c_uint64), ("route_launches", ctypes.c_uint64),
                 ("combine_launches", ctypes.c_uint64), ("router_launches", ctypes.c_uint64),
+                ("dequant_launches", ctypes.c_uint64),
                 ("last_arm", ctypes.c_int32),
                 ("last_n_tokens", ctypes.c_int32)]
 
@@ -83,6 +85,9 @@ _SIGS = {
                                        _P]),
     "qtip_moe_router_logits": (_I32, [_P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     "qtip_moe_router_split": (_I32, [_P, _I32]),
+    "qtip_moe_dequant_range": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "qtip_moe_dequantize": (_I32, [_P, ctypes.POINTER(qtip_moe_weights), _I32, _I32, _P, _P]),
+    "qtip_fill_select_arm": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "qtip_moe_route": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "qtip_expert_matmul": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _P]),
     "qtip_moe_stats_get": (_I32, [_P, ctypes.POINTER(qtip_moe_stats)]),
@@ -151,9 +156,9 @@ def _check(fn: str, status: int):
 
 
 def make_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override=QTIP_ARM_AUTO, variant=0,
-              out_dtype=QTIP_OUT_F32, tile_m=0, dispatch_tile_m=0) -> qtip_moe_desc:
+              out_dtype=QTIP_OUT_F32, tile_m=0, dispatch_tile_m=0, dequant_traffic_ratio=0) -> qtip_moe_desc:
     return qtip_moe_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override, variant, out_dtype, tile_m,
-                         dispatch_tile_m)
+                         dispatch_tile_m, dequant_traffic_ratio)
 
 
 def make_weights(codes_gate, codes_up, codes_down, scale_gate, scale_up, scale_down, lut) -> qtip_moe_weights:
@@ -231,6 +236,21 @@ def qtip_moe_router_logits(plan, x_bf16, w_router_bf16, n_tokens, logits, worksp
     _check("qtip_moe_router_logits", lib().qtip_moe_router_logits(plan, _ptr(x_bf16), _ptr(w_router_bf16), n_tokens,
                                                                   _ptr(logits), _ptr(workspace), workspace_bytes,
                                                                   _stream(stream)))
+
+
+def qtip_moe_dequant_range(plan) -> tuple:
+    lo, hi = _I32(), _I32()
+    _check("qtip_moe_dequant_range", lib().qtip_moe_dequant_range(plan, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def qtip_moe_dequantize(plan, weights: qtip_moe_weights, matrix, expert, dense_out, stream=None) -> None:
+    _check("qtip_moe_dequantize", lib().qtip_moe_dequantize(plan, ctypes.byref(weights), matrix, expert,
+                                                            _ptr(dense_out), _stream(stream)))
+
+
+def qtip_fill_select_arm(n, k, E, tile_m, dequant_ratio) -> int:
+    return lib().qtip_fill_select_arm(n, k, E, tile_m, dequant_ratio)
 
 
 def qtip_moe_router_split(plan, n_tokens) -> int:

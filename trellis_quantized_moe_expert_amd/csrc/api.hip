@@ -24,6 +24,9 @@ struct qtip_moe_plan_s {
   qtip_moe_desc d;
   int32_t tile_m;
   int32_t dispatch_tile_m;
+  int32_t dequant_ratio;        // fused GEMV kept while pairs per woken expert are below this
+  int32_t dequant_lo, dequant_hi;  // token counts [lo, hi) the automatic dispatch sends to the dequantize arm
+  bool dense;                   // the dequantize arm may run: its dense weights are in the workspace
   int32_t device;  // -1: created from an arch name; the current device is used at call time
 
   int32_t min_tokens_grouped;
@@ -64,7 +67,12 @@ namespace {
 //    pass) -> 8 waves with four 16-pair blocks per decode.
 //  * GEMV arm, by the expected task count: 16-row tasks until there are enough 32-row tasks
 //    to give each of the 2048 wave slots of a 256-CU, 8-wave launch one.
+int kernel_arm(int32_t arm) {
+  return arm == QTIP_ARM_GROUPED ? kArmGrouped : (arm == QTIP_ARM_DEQUANT ? kArmDense : kArmGemv);
+}
+
 int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_tokens) {
+  if (arm == kArmDense) return 3;  // the dequantize arm has one configuration
   if (plan->d.variant != kVariantDefault) return plan->d.variant;
   const int32_t E = plan->d.num_experts, k = plan->d.top_k;
   const int32_t n = n_tokens >= 1 ? n_tokens : 1;
@@ -107,7 +115,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, h, y, router_part,
-      total;
+      dense_gate, dense_up, dense_down, total;
 };
 
 // Largest router-GEMM partial buffer, S(n) * n * E floats, over the batch sizes a plan accepts.
@@ -123,7 +131,7 @@ size_t router_part_elems(const qtip_moe_desc& d, int32_t n_max) {
   return best;
 }
 
-WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens) {
+WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, bool dense) {
   const size_t P = (size_t)n_tokens * d.top_k;
   const size_t woken_max = P < (size_t)d.num_experts ? P : (size_t)d.num_experts;
   const size_t max_tiles = P / tile_m + woken_max + 1;
@@ -142,6 +150,11 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens) {
   L.h = o;            o = align256(o + P * (size_t)d.inter * 2);
   L.y = o;            o = align256(o + P * (size_t)d.hidden * 4);
   L.router_part = o;  o = align256(o + router_part_elems(d, n_tokens) * 4);
+  // dequantize arm: every expert's dense bf16 weights (only when the plan can take that arm)
+  const size_t dense_mat = dense ? (size_t)d.num_experts * (size_t)d.hidden * (size_t)d.inter * 2 : 0;
+  L.dense_gate = o;   o = align256(o + dense_mat);
+  L.dense_up = o;     o = align256(o + dense_mat);
+  L.dense_down = o;   o = align256(o + dense_mat);
   L.total = o;
   return L;
 }
@@ -241,8 +254,11 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
     return fail(QTIP_ERR_INVALID_ARG, "one expert matrix must be below 2^31 bytes");
   if ((int64_t)d->num_experts * d->hidden >= ((int64_t)1 << 31))
     return fail(QTIP_ERR_INVALID_ARG, "num_experts * hidden (the router weight) must be below 2^31 elements");
-  if (d->arm_override != QTIP_ARM_AUTO && d->arm_override != QTIP_ARM_GEMV && d->arm_override != QTIP_ARM_GROUPED)
+  if (d->arm_override != QTIP_ARM_AUTO && d->arm_override != QTIP_ARM_GEMV && d->arm_override != QTIP_ARM_GROUPED &&
+      d->arm_override != QTIP_ARM_DEQUANT)
     return fail(QTIP_ERR_INVALID_ARG, "unknown arm_override");
+  if (d->dequant_traffic_ratio < 0 || d->dequant_traffic_ratio > 1024)
+    return fail(QTIP_ERR_INVALID_ARG, "dequant_traffic_ratio must be in [0, 1024]");
   if (d->out_dtype != QTIP_OUT_BF16 && d->out_dtype != QTIP_OUT_F32) return fail(QTIP_ERR_INVALID_ARG, "unknown out_dtype");
   const int32_t tm = d->tile_m == 0 ? QTIP_DEFAULT_TILE_M : d->tile_m;
   if (tm != 16 && tm != 32 && tm != 64) return fail(QTIP_ERR_INVALID_ARG, "tile_m must be 0, 16, 32 or 64");
@@ -315,7 +331,28 @@ qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc, const char* gcn_ar
   p->d.dispatch_tile_m = p->dispatch_tile_m;
   p->device = -1;
   p->min_tokens_grouped = fill_min_tokens(desc->top_k, desc->num_experts, p->dispatch_tile_m);
-  p->ws_bytes = ws_layout(p->d, tm, desc->max_tokens).total;
+  p->dequant_ratio = desc->dequant_traffic_ratio == 0 ? kDequantTrafficRatio : desc->dequant_traffic_ratio;
+  p->d.dequant_traffic_ratio = p->dequant_ratio;
+  // Pairs per woken expert never decrease with n, so the automatic dispatch's dequantize
+  // tokens form one interval: from the first n past the floor whose fill reaches the traffic
+  // ratio up to the grouped arm's first n.
+  p->dequant_lo = p->dequant_hi = 0;
+  if (p->dequant_ratio < p->dispatch_tile_m) {
+    const int32_t lo = fill_min_tokens(desc->top_k, desc->num_experts, p->dequant_ratio);
+    int32_t hi = p->min_tokens_grouped;
+    if (hi < 0 || hi > desc->max_tokens + 1) hi = desc->max_tokens + 1;
+    if (lo > 0 && lo < hi) {
+      p->dequant_lo = lo;
+      p->dequant_hi = hi;
+    }
+  }
+  p->dense = desc->arm_override == QTIP_ARM_DEQUANT ||
+             (desc->arm_override == QTIP_ARM_AUTO && p->dequant_lo < p->dequant_hi);
+  if (p->dense && (int64_t)desc->hidden * desc->inter >= ((int64_t)1 << 31)) {
+    delete p;
+    return fail(QTIP_ERR_INVALID_ARG, "the dequantize arm needs hidden * inter below 2^31 elements");
+  }
+  p->ws_bytes = ws_layout(p->d, tm, desc->max_tokens, p->dense).total;
   *out = p;
   return QTIP_OK;
 }
@@ -366,7 +403,7 @@ qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_
   if (!plan || !out) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
   if (n_tokens < 1) return fail(QTIP_ERR_INVALID_CONFIG, "n_tokens must be >= 1");
   const int32_t arm = qtip_moe_select_arm(plan, n_tokens);
-  const int karm = arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv;
+  const int karm = kernel_arm(arm);
   out->arm = arm;
   out->tile_m = plan->tile_m;
   shape_of(plan, karm, kModeGateUp, n_tokens, plan->d.inter, &out->gate_up);
@@ -377,9 +414,7 @@ qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_
 int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens) {
   if (!plan || n_tokens < 1) return -1;
   if (plan->d.arm_override != QTIP_ARM_AUTO) return plan->d.arm_override;
-  return fill_select_grouped(n_tokens, plan->d.top_k, plan->d.num_experts, plan->dispatch_tile_m)
-             ? QTIP_ARM_GROUPED
-             : QTIP_ARM_GEMV;
+  return fill_select_arm(n_tokens, plan->d.top_k, plan->d.num_experts, plan->dispatch_tile_m, plan->dequant_ratio);
 }
 
 qtip_status qtip_arch_witness(int device, void* stream) {
@@ -497,8 +532,9 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
 
   const qtip_moe_desc& d = plan->d;
   const int32_t arm = qtip_moe_select_arm(plan, n_tokens);
-  const int karm = arm == QTIP_ARM_GROUPED ? kArmGrouped : kArmGemv;
-  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens);
+  const int karm = kernel_arm(arm);
+  if (karm == kArmDense && !plan->dense) return fail(QTIP_ERR_INVALID_CONFIG, "the plan has no dequantize workspace");
+  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens, plan->dense);
   char* ws = reinterpret_cast<char*>(workspace);
   int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
   float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
@@ -535,8 +571,40 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   plan->stats.route_launches += 2;
   if ((e = prof_mark(plan, 2, st)) != hipSuccess) return hip_fail(e, "profile event");
 
+  uint16_t* dense_gate = reinterpret_cast<uint16_t*>(ws + L.dense_gate);
+  uint16_t* dense_up = reinterpret_cast<uint16_t*>(ws + L.dense_up);
+  uint16_t* dense_down = reinterpret_cast<uint16_t*>(ws + L.dense_down);
+  if (karm == kArmDense) {
+    // materialise the woken experts' three matrices (counts from the binning just launched)
+    DequantParams q{};
+    q.codes0 = w->codes_gate;
+    q.codes1 = w->codes_up;
+    q.lut = w->lut;
+    q.counts = counts;
+    q.num_experts = d.num_experts;
+    q.rows = d.inter;
+    q.cols = d.hidden;
+    q.expert = -1;
+    q.out0 = dense_gate;
+    q.out1 = dense_up;
+    q.out_expert_stride = (int64_t)d.inter * d.hidden;
+    e = launch_dequant(q, persistent_grid(dev, (size_t)d.num_experts * (d.inter / 16), kDequantWaves), st);
+    if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+    q.codes0 = w->codes_down;
+    q.codes1 = nullptr;
+    q.rows = d.hidden;
+    q.cols = d.inter;
+    q.out0 = dense_down;
+    q.out1 = nullptr;
+    e = launch_dequant(q, persistent_grid(dev, (size_t)d.num_experts * (d.hidden / 16), kDequantWaves), st);
+    if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+    plan->stats.dequant_launches += 2;
+  }
+
   const size_t max_units = max_units_for(d, n_tokens);
   ExpertParams gu{};
+  gu.dense0 = dense_gate;
+  gu.dense1 = dense_up;
   gu.codes0 = w->codes_gate;
   gu.codes1 = w->codes_up;
   gu.scale0 = w->scale_gate;
@@ -563,6 +631,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
 
   ExpertParams dn{};
+  dn.dense0 = dense_down;
   dn.codes0 = w->codes_down;
   dn.scale0 = w->scale_down;
   dn.lut = w->lut;
@@ -584,7 +653,9 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   e = launch_expert(kModeSingle, karm, kv_dn, dn, persistent_grid(dev, max_units * (d.hidden / vi.rows_per_task), vi.waves), st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
-  if (karm == kArmGrouped) plan->stats.grouped_launches += 2; else plan->stats.gemv_launches += 2;
+  if (karm == kArmGrouped) plan->stats.grouped_launches += 2;
+  else if (karm == kArmDense) plan->stats.dequant_launches += 2;
+  else plan->stats.gemv_launches += 2;
 
   e = launch_combine(y, topk_w, n_tokens, d.top_k, d.hidden, out, d.out_dtype == QTIP_OUT_BF16, st);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -637,7 +708,7 @@ qtip_status qtip_moe_router_logits(qtip_moe_plan_t plan, const void* x_bf16, con
   if (s != QTIP_OK) return s;
   const qtip_moe_desc& d = plan->d;
   const int32_t S = router_split(n_tokens, d.num_experts, d.hidden);
-  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens);
+  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens, plan->dense);
   float* part = S == 1 ? logits : reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.router_part);
   hipError_t e = launch_router_gemm(reinterpret_cast<const uint16_t*>(x_bf16),
                                     reinterpret_cast<const uint16_t*>(w_router_bf16), n_tokens, d.num_experts,
@@ -648,6 +719,50 @@ qtip_status qtip_moe_router_logits(qtip_moe_plan_t plan, const void* x_bf16, con
     e = launch_router_reduce(part, S, (int64_t)n_tokens * d.num_experts, logits, st);
     if (e != hipSuccess) return hip_fail(e, "router reduce launch");
   }
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_dequant_range(qtip_moe_plan_t plan, int32_t* n_lo, int32_t* n_hi) {
+  g_detail.clear();
+  if (!plan || !n_lo || !n_hi) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  *n_lo = plan->dequant_lo;
+  *n_hi = plan->dequant_hi;
+  return QTIP_OK;
+}
+
+int32_t qtip_fill_select_arm(int32_t n, int32_t k, int32_t E, int32_t tile_m, int32_t dequant_ratio) {
+  if (!fill_args_ok(n, k, E, tile_m) || dequant_ratio < 1) return -1;
+  return fill_select_arm(n, k, E, tile_m, dequant_ratio);
+}
+
+qtip_status qtip_moe_dequantize(qtip_moe_plan_t plan, const qtip_moe_weights* w, int32_t matrix, int32_t expert,
+                                void* dense_out, void* stream) {
+  g_detail.clear();
+  if (!plan || !w || !dense_out || !w->lut) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  const qtip_moe_desc& d = plan->d;
+  if (matrix < 0 || matrix > 2) return fail(QTIP_ERR_INVALID_ARG, "matrix must be 0 (gate), 1 (up) or 2 (down)");
+  if (expert < 0 || expert >= d.num_experts) return fail(QTIP_ERR_INVALID_ARG, "expert out of range");
+  const uint8_t* codes = matrix == 0 ? w->codes_gate : (matrix == 1 ? w->codes_up : w->codes_down);
+  if (!codes) return fail(QTIP_ERR_INVALID_ARG, "NULL codes");
+  if ((reinterpret_cast<uintptr_t>(codes) & 7) || (reinterpret_cast<uintptr_t>(w->lut) & 15) ||
+      (reinterpret_cast<uintptr_t>(dense_out) & 15))
+    return fail(QTIP_ERR_INVALID_ARG, "codes must be 8-byte aligned, lut and dense_out 16-byte aligned");
+  const hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  qtip_status s = ensure_device(plan, st, &dev);
+  if (s != QTIP_OK) return s;
+  DequantParams q{};
+  q.codes0 = codes;
+  q.lut = w->lut;
+  q.num_experts = d.num_experts;
+  q.rows = matrix == 2 ? d.hidden : d.inter;
+  q.cols = matrix == 2 ? d.inter : d.hidden;
+  q.expert = expert;
+  q.out0 = reinterpret_cast<uint16_t*>(dense_out);
+  q.out_expert_stride = 0;
+  hipError_t e = launch_dequant(q, persistent_grid(dev, (size_t)(q.rows / 16), kDequantWaves), st);
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  plan->stats.dequant_launches++;
   return QTIP_OK;
 }
 

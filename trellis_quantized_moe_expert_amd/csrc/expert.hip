@@ -208,6 +208,79 @@ __device__ inline RunSet<NT> load_runs(const uint8_t* __restrict__ base, uint32_
   return rs;
 }
 
+// Grouped and dequantize arms: scale and store one task's 16-pair x 16-row MFMA tiles.
+// D layout: lane holds rows 4*(lane/16)+t (pairs) of column lane%16 (output row).
+template <int MODE, int NS, int NT>
+__device__ inline void grouped_epilogue(const ExpertParams& p, const Unit& un, int r0, const f32x4 (&acc0)[NS][NT],
+                                        const f32x4 (&acc1)[NS][NT]) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = r0 + 16 * nt + j;
+    const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
+    const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pi = m * 16 + 4 * g + t;
+        if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][nt][t], acc1[m][nt][t], s0, s1);
+      }
+    }
+  }
+}
+
+// Dequantize arm: the grouped pass over weights materialised beforehand as dense bf16 rows
+// (no decode, no LUT).  The B fragment of MFMA step st of block kb is the 16 bytes of inputs
+// kb*128 + 32g + 8st .. +7 of row r0 + 16nt + j: the same K permutation as the decode.
+template <int MODE, int NS, int NT>
+__device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int kblocks = p.cols / kKBlock;
+  const size_t mat = (size_t)p.rows * (size_t)p.cols;
+  const uint16_t* w0 = p.dense0 + (size_t)un.e * mat;
+  const uint16_t* w1 = (MODE == kModeGateUp) ? p.dense1 + (size_t)un.e * mat : w0;
+  // the plan keeps rows * cols below 2^31, so element offsets within one matrix fit 32 bits
+  const uint32_t woff = (uint32_t)(r0 + j) * (uint32_t)p.cols + 32u * (uint32_t)g;
+  const uint32_t nt_stride = 16u * (uint32_t)p.cols;
+
+  uint32_t aoff[NS];
+  act_rows<NS>(p, un, j, 16, g, aoff);
+  f32x4 acc0[NS][NT], acc1[NS][NT];
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc0[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  for (int kb = 0; kb < kblocks; ++kb) {
+    u32x4 a[NS][4];
+    load_a_block<NS>(a, p.act, aoff, kb);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint32_t o = woff + (uint32_t)nt * nt_stride + (uint32_t)(kb * kKBlock + st * 8);
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(w0 + o);
+        const u32x4 b1 = (MODE == kModeGateUp) ? *reinterpret_cast<const u32x4*>(w1 + o) : b0;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+          acc0[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
+                                                                __builtin_bit_cast(bf16x8, b0), acc0[m][nt], 0, 0, 0);
+          if (MODE == kModeGateUp)
+            acc1[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
+                                                                  __builtin_bit_cast(bf16x8, b1), acc1[m][nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1);
+}
+
 // Grouped arm: NS row blocks of 16 pairs x NT row blocks of 16 outputs share one decode of
 // the 16*NT rows; each A fragment feeds NT MFMAs.
 template <int MODE, int NS, int NT, bool APRE>
@@ -290,21 +363,7 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
     }
   }
 
-  // D layout: lane holds rows 4*(lane/16)+t (pairs) of column lane%16 (output row)
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = r0 + 16 * nt + j;
-    const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
-    const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
-#pragma unroll
-    for (int m = 0; m < NS; ++m) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int pi = m * 16 + 4 * g + t;
-        if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][nt][t], acc1[m][nt][t], s0, s1);
-      }
-    }
-  }
+  grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1);
 }
 
 // GEMV arm: NQ pairs x NT row blocks of 16 outputs share one decode; VALU bf16 dot products.
@@ -422,11 +481,18 @@ template <int MODE, int ARM, class CFG>
 __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   constexpr int NT = CFG::kNT;
   constexpr bool AP = CFG::kAPre;
-  constexpr int kChunk = (ARM == kArmGrouped) ? CFG::kNSub * 16 : CFG::kGPairs;
+  constexpr int kChunk = (ARM == kArmGemv) ? CFG::kGPairs : CFG::kNSub * 16;
   static_assert(CFG::kNSub >= 1 && CFG::kNSub <= 4 && CFG::kGPairs >= 1 && CFG::kGPairs <= 4, "config");
   for (int c0 = 0; c0 < un.len; c0 += kChunk) {
     const Unit part{un.e, un.start + c0, min(kChunk, un.len - c0)};
-    if (ARM == kArmGrouped) {
+    if (ARM == kArmDense) {
+      switch ((part.len + 15) >> 4) {
+        case 1: task_dense<MODE, 1, NT>(p, part, r0); break;
+        case 2: if (CFG::kNSub >= 2) task_dense<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT>(p, part, r0); break;
+        case 3: if (CFG::kNSub >= 3) task_dense<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT>(p, part, r0); break;
+        default: if (CFG::kNSub >= 4) task_dense<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT>(p, part, r0); break;
+      }
+    } else if (ARM == kArmGrouped) {
       switch ((part.len + 15) >> 4) {
         case 1: task_grouped<MODE, 1, NT, AP>(p, lut, part, r0); break;
         case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP>(p, lut, part, r0); break;
@@ -445,9 +511,7 @@ __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, cons
 }
 
 template <int MODE, int ARM, class CFG>
-__global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
-  fill_lut(lut_s, p.lut);
+__device__ inline void expert_tasks(const ExpertParams& p, const uint16_t* lut_s) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = p.n_units_dev ? __builtin_amdgcn_readfirstlane(*p.n_units_dev) : p.n_units_host;
   const int nblocks = p.rows / CFG::kRows;
@@ -471,6 +535,52 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
     Unit un;
     if (!read_unit(p, u, un)) continue;
     run_task<MODE, ARM, CFG>(p, lut_s, un, nb * CFG::kRows);
+  }
+}
+
+template <int MODE, int ARM, class CFG>
+__global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParams p) {
+  if constexpr (ARM == kArmDense) {
+    expert_tasks<MODE, ARM, CFG>(p, nullptr);
+  } else {
+    __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
+    fill_lut(lut_s, p.lut);
+    expert_tasks<MODE, ARM, CFG>(p, lut_s);
+  }
+}
+
+// Dequantize-materialise: one wave task decodes 16 rows x all inputs of one matrix (two for
+// the fused gate/up pair) and stores bf16(LUT[state]) rows in natural input order.
+__global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantParams q) {
+  __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
+  fill_lut(lut_s, q.lut);
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row_bytes = q.cols >> 2;
+  const int kblocks = q.cols / kKBlock;
+  const int nblocks = q.rows / 16;
+  const int e_first = q.expert >= 0 ? q.expert : 0;
+  const long n_exp = q.expert >= 0 ? 1 : q.num_experts;
+  const long total = n_exp * nblocks;
+  const size_t mat_bytes = (size_t)q.rows * row_bytes;
+  for (long task = (long)blockIdx.x * kDequantWaves + wave; task < total; task += (long)gridDim.x * kDequantWaves) {
+    const int e = e_first + (int)(task / nblocks);
+    const int r0 = (int)(task % nblocks) * 16;
+    if (q.expert < 0 && q.counts && __builtin_amdgcn_readfirstlane(q.counts[e]) <= 0) continue;
+    for (int m = 0; m < (q.codes1 ? 2 : 1); ++m) {
+      const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
+      uint16_t* out = (m ? q.out1 : q.out0) + (size_t)e * (size_t)q.out_expert_stride + (size_t)(r0 + j) * q.cols;
+      const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+      for (int kb = 0; kb < kblocks; ++kb) {
+        const RunCodes rc = load_run(base, roff, kb * 32 + g * 8, row_bytes);
+        u32x4 w[4];
+        decode16(lut_s, rc.d0, rc.d1, w[0], w[1]);
+        decode16(lut_s, rc.d1, rc.la, w[2], w[3]);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(out + kb * kKBlock + 32 * g + 8 * st) = w[st];
+      }
+    }
   }
 }
 
@@ -531,10 +641,20 @@ __global__ __launch_bounds__(1024, 1) void gather_probe_kernel(int32_t rounds, u
 
 }  // namespace
 
+// The dequantize arm runs one configuration (variant 3's shape: 16 waves, 32-row tasks, up to
+// 32 pairs per pass over the weights).
+using CfgDense = ExpertCfg<16, 2, 2, 2>;
+
 template <class CFG>
 static void launch_cfg(int mode, int arm, const ExpertParams& p, int grid, hipStream_t stream) {
   const dim3 g(grid), b(CFG::kWaves * 64);
-  if (mode == kModeGateUp && arm == kArmGrouped)
+  if (arm == kArmDense) {
+    const dim3 bd(CfgDense::kWaves * 64);
+    if (mode == kModeGateUp)
+      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmDense, CfgDense>), g, bd, 0, stream, p);
+    else
+      hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmDense, CfgDense>), g, bd, 0, stream, p);
+  } else if (mode == kModeGateUp && arm == kArmGrouped)
     hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG>), g, b, 0, stream, p);
   else if (mode == kModeGateUp)
     hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG>), g, b, 0, stream, p);
@@ -547,6 +667,12 @@ static void launch_cfg(int mode, int arm, const ExpertParams& p, int grid, hipSt
 template <class CFG>
 struct CfgInfo {
   static void get(int arm, VariantInfo& v) {
+    if (arm == kArmDense) {
+      v.waves = CfgDense::kWaves;
+      v.rows_per_task = CfgDense::kRows;
+      v.pairs_per_decode = CfgDense::kNSub * 16;
+      return;
+    }
     v.waves = CFG::kWaves;
     v.rows_per_task = CFG::kRows;
     v.pairs_per_decode = arm == kArmGrouped ? CFG::kNSub * 16 : CFG::kGPairs;
@@ -577,6 +703,11 @@ hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, 
     case 7: launch_cfg<Cfg7>(mode, arm, p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantParams& q, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDequantWaves * 64), 0, stream, q);
   return hipGetLastError();
 }
 

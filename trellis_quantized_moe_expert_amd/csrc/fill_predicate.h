@@ -16,6 +16,11 @@
 namespace qtip {
 
 constexpr int32_t kDecodeRegimeMaxTokens = 8;
+// Fused GEMV vs dequantize-materialise: the GEMV streams an expert's packed bytes once per
+// pair; materialising writes the dense bf16 weights and reads them back, 2 x 16/2 = 16 times
+// the 2-bit packed bytes.  The m-tile page's "Tests" section names the constant (16) and
+// requires the grouped boundary not to leave a window for the dequantize arm between them.
+constexpr int32_t kDequantTrafficRatio = 16;
 
 inline double fill_woken_experts(int32_t n, int32_t k, int32_t E) {
   return (double)E * (1.0 - std::pow(1.0 - (double)k / (double)E, (double)n));
@@ -31,6 +36,14 @@ inline bool fill_args_ok(int32_t n, int32_t k, int32_t E, int32_t tile_m) {
 
 inline bool fill_select_grouped(int32_t n, int32_t k, int32_t E, int32_t tile_m) {
   return n > kDecodeRegimeMaxTokens && fill_pairs_per_woken_expert(n, k, E) >= (double)tile_m;
+}
+
+// Three-arm dispatch: 2 = grouped, 1 = fused GEMV, 3 = dequantize-materialise (the values of
+// QTIP_ARM_GROUPED / _GEMV / _DEQUANT).
+inline int32_t fill_select_arm(int32_t n, int32_t k, int32_t E, int32_t tile_m, int32_t dequant_ratio) {
+  if (fill_select_grouped(n, k, E, tile_m)) return 2;
+  if (n <= kDecodeRegimeMaxTokens || fill_pairs_per_woken_expert(n, k, E) < (double)dequant_ratio) return 1;
+  return 3;
 }
 
 // Smallest n that selects the grouped arm.  Pairs per woken expert never decreases with n

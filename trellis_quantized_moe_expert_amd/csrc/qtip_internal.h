@@ -46,10 +46,12 @@ struct ExpertParams {
   const int32_t* out_row_map;   // single pass: output row of position s = map[s] (NULL: s)
   int32_t n_out_rows;
   int32_t n_xcd;                // workgroups are dispatched round-robin over this many XCDs (>= 1)
+  const uint16_t* dense0;       // dequantize arm: [E][rows][cols] bf16 weights (gate, or the single matrix)
+  const uint16_t* dense1;       // dequantize arm: [E][rows][cols] bf16 up weights (fused pass only)
 };
 
 enum ExpertMode { kModeGateUp = 0, kModeSingle = 1 };
-enum ExpertArm { kArmGemv = 0, kArmGrouped = 1 };
+enum ExpertArm { kArmGemv = 0, kArmGrouped = 1, kArmDense = 2 };
 
 struct VariantInfo {
   int waves;             // wave64 per workgroup
@@ -62,6 +64,22 @@ hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, 
 
 // Top-k over logits given as n_part partial sums part[s][t][e] (s-major, n*E apart), added in
 // ascending s; n_part = 1 reads plain logits.
+// Dequantize-materialise: dense bf16(LUT[state]) (scales not applied) of every row of one or
+// two trellis matrices [E][rows][cols/4] into [E][rows][cols] bf16.  expert >= 0 does that
+// expert only; otherwise every expert e with counts[e] > 0 (every expert if counts is NULL).
+struct DequantParams {
+  const uint8_t* codes0;
+  const uint8_t* codes1;        // NULL: one matrix
+  const uint16_t* lut;
+  const int32_t* counts;
+  int32_t num_experts, rows, cols, expert;
+  uint16_t* out0;
+  uint16_t* out1;
+  int64_t out_expert_stride;    // elements between experts' matrices in out0/out1 (0: expert-less output)
+};
+hipError_t launch_dequant(const DequantParams& q, int grid, hipStream_t stream);
+constexpr int kDequantWaves = 16;
+
 hipError_t launch_route_topk(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k,
                              int32_t* topk_idx, float* topk_w, hipStream_t stream);
 
