@@ -588,6 +588,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     q.out0 = dense_gate;
     q.out1 = dense_up;
     q.out_expert_stride = (int64_t)d.inter * d.hidden;
+    q.fragment_order = 1;
     e = launch_dequant(q, persistent_grid(dev, (size_t)d.num_experts * (d.inter / 16), kDequantWaves), st);
     if (e != hipSuccess) return hip_fail(e, "dequantize launch");
     q.codes0 = w->codes_down;
@@ -760,6 +761,7 @@ qtip_status qtip_moe_dequantize(qtip_moe_plan_t plan, const qtip_moe_weights* w,
   q.expert = expert;
   q.out0 = reinterpret_cast<uint16_t*>(dense_out);
   q.out_expert_stride = 0;
+  q.fragment_order = 0;
   hipError_t e = launch_dequant(q, persistent_grid(dev, (size_t)(q.rows / 16), kDequantWaves), st);
   if (e != hipSuccess) return hip_fail(e, "dequantize launch");
   plan->stats.dequant_launches++;

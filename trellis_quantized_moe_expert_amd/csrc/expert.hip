@@ -231,9 +231,9 @@ __device__ inline void grouped_epilogue(const ExpertParams& p, const Unit& un, i
   }
 }
 
-// Dequantize arm: the grouped pass over weights materialised beforehand as dense bf16 rows
-// (no decode, no LUT).  The B fragment of MFMA step st of block kb is the 16 bytes of inputs
-// kb*128 + 32g + 8st .. +7 of row r0 + 16nt + j: the same K permutation as the decode.
+// Dequantize arm: the grouped pass over weights materialised beforehand as dense bf16 in
+// fragment order (no decode, no LUT): the B fragment of MFMA step st of block kb for row
+// block r0/16 + nt is one coalesced 16-byte load per lane.  Same K permutation as the decode.
 template <int MODE, int NS, int NT>
 __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
@@ -242,9 +242,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
   const size_t mat = (size_t)p.rows * (size_t)p.cols;
   const uint16_t* w0 = p.dense0 + (size_t)un.e * mat;
   const uint16_t* w1 = (MODE == kModeGateUp) ? p.dense1 + (size_t)un.e * mat : w0;
-  // the plan keeps rows * cols below 2^31, so element offsets within one matrix fit 32 bits
-  const uint32_t woff = (uint32_t)(r0 + j) * (uint32_t)p.cols + 32u * (uint32_t)g;
-  const uint32_t nt_stride = 16u * (uint32_t)p.cols;
+  const int rb0 = r0 / 16;
 
   uint32_t aoff[NS];
   act_rows<NS>(p, un, j, 16, g, aoff);
@@ -264,7 +262,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const uint32_t o = woff + (uint32_t)nt * nt_stride + (uint32_t)(kb * kKBlock + st * 8);
+        const size_t o = dense_fragment_offset(rb0 + nt, kb, st, lane, kblocks);
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(w0 + o);
         const u32x4 b1 = (MODE == kModeGateUp) ? *reinterpret_cast<const u32x4*>(w1 + o) : b0;
 #pragma unroll
@@ -550,7 +548,9 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
 }
 
 // Dequantize-materialise: one wave task decodes 16 rows x all inputs of one matrix (two for
-// the fused gate/up pair) and stores bf16(LUT[state]) rows in natural input order.
+// the fused gate/up pair) and stores bf16(LUT[state]), in row-major order or in the fragment
+// order of the dequantize arm's MFMA pass (there every store is 1 KiB contiguous per wave).
+// The next block's codes are requested before the current block is decoded.
 __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantParams q) {
   __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
   fill_lut(lut_s, q.lut);
@@ -566,19 +566,29 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
   const size_t mat_bytes = (size_t)q.rows * row_bytes;
   for (long task = (long)blockIdx.x * kDequantWaves + wave; task < total; task += (long)gridDim.x * kDequantWaves) {
     const int e = e_first + (int)(task / nblocks);
-    const int r0 = (int)(task % nblocks) * 16;
+    const int rb = (int)(task % nblocks);
+    const int r0 = rb * 16;
     if (q.expert < 0 && q.counts && __builtin_amdgcn_readfirstlane(q.counts[e]) <= 0) continue;
     for (int m = 0; m < (q.codes1 ? 2 : 1); ++m) {
       const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
-      uint16_t* out = (m ? q.out1 : q.out0) + (size_t)e * (size_t)q.out_expert_stride + (size_t)(r0 + j) * q.cols;
+      uint16_t* out = (m ? q.out1 : q.out0) + (size_t)e * (size_t)q.out_expert_stride;
       const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+      RunCodes nx = load_run(base, roff, g * 8, row_bytes);
       for (int kb = 0; kb < kblocks; ++kb) {
-        const RunCodes rc = load_run(base, roff, kb * 32 + g * 8, row_bytes);
+        const RunCodes rc = nx;
+        if (kb + 1 < kblocks) nx = load_run(base, roff, (kb + 1) * 32 + g * 8, row_bytes);
         u32x4 w[4];
         decode16(lut_s, rc.d0, rc.d1, w[0], w[1]);
         decode16(lut_s, rc.d1, rc.la, w[2], w[3]);
+        if (q.fragment_order) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(out + kb * kKBlock + 32 * g + 8 * st) = w[st];
+          for (int st = 0; st < 4; ++st)
+            *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
+        } else {
+          uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
+#pragma unroll
+          for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+        }
       }
     }
   }

@@ -46,8 +46,8 @@ struct ExpertParams {
   const int32_t* out_row_map;   // single pass: output row of position s = map[s] (NULL: s)
   int32_t n_out_rows;
   int32_t n_xcd;                // workgroups are dispatched round-robin over this many XCDs (>= 1)
-  const uint16_t* dense0;       // dequantize arm: [E][rows][cols] bf16 weights (gate, or the single matrix)
-  const uint16_t* dense1;       // dequantize arm: [E][rows][cols] bf16 up weights (fused pass only)
+  const uint16_t* dense0;       // dequantize arm: [E] x rows x cols bf16 weights in fragment order (gate, or the single matrix)
+  const uint16_t* dense1;       // dequantize arm: the same for the up weights (fused pass only)
 };
 
 enum ExpertMode { kModeGateUp = 0, kModeSingle = 1 };
@@ -76,7 +76,15 @@ struct DequantParams {
   uint16_t* out0;
   uint16_t* out1;
   int64_t out_expert_stride;    // elements between experts' matrices in out0/out1 (0: expert-less output)
+  int32_t fragment_order;       // 0: row-major [rows][cols]; 1: MFMA fragment order (dense_fragment_offset)
 };
+
+// Fragment order of a dense [rows][cols] bf16 matrix, as the dequantize arm's MFMA pass reads
+// it: for 16-row block rb, 128-input block kb and MFMA step st, the 64 lanes' 16-byte B
+// fragments are contiguous (lane j + 16g holds row 16rb + j, inputs kb*128 + 32g + 8st .. +7).
+__host__ __device__ inline size_t dense_fragment_offset(int rb, int kb, int st, int lane, int kblocks) {
+  return ((((size_t)rb * kblocks + kb) * 4 + st) * 64 + lane) * 8;
+}
 hipError_t launch_dequant(const DequantParams& q, int grid, hipStream_t stream);
 constexpr int kDequantWaves = 16;
 
