@@ -92,9 +92,33 @@ struct RunCodes {
   uint32_t d0, d1, la;
 };
 
-// `base` is the (wave-uniform) start of the expert's matrix, `row_off` the lane's row offset in
-// bytes; 32-bit offsets keep the addresses in one VGPR each.
-__device__ inline RunCodes load_run(const uint8_t* __restrict__ base, uint32_t row_off, int ob, int row_bytes) {
+// Codes of one 32-symbol run: the run's 8 bytes and the 4 after them (its look-ahead).  `base`
+// is the (wave-uniform) start of the expert's matrix, `row_off` the lane's row offset in bytes;
+// 32-bit offsets keep the addresses in one VGPR each.  `back` (0 or 4) moves the load 4 bytes
+// earlier, for a load whose data is never used and which must stay inside the row.  With X3 one
+// 12-byte load fetches all three dwords (half the vector-memory accesses of an 8-byte plus a
+// 4-byte load, at the cost of an aligned register triple: used where registers allow).
+template <bool X3>
+__device__ inline RunCodes load_run(const uint8_t* __restrict__ base, uint32_t row_off, int ob, uint32_t back = 0) {
+  const uint32_t o = row_off + (uint32_t)ob - back;
+  RunCodes rc;
+  if (X3) {
+    const uint3 v = *reinterpret_cast<const uint3*>(base + o);
+    rc.d0 = v.x;
+    rc.d1 = v.y;
+    rc.la = v.z;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(base + o);
+    rc.d0 = v.x;
+    rc.d1 = v.y;
+    rc.la = *reinterpret_cast<const uint32_t*>(base + (o + 8u));
+  }
+  return rc;
+}
+
+// The run of a row's last block: its look-ahead wraps to the row start (the window is circular).
+__device__ inline RunCodes load_run_wrapping(const uint8_t* __restrict__ base, uint32_t row_off, int ob,
+                                             int row_bytes) {
   RunCodes rc;
   const uint2 v = *reinterpret_cast<const uint2*>(base + (row_off + (uint32_t)ob));
   int nx = ob + 8;
@@ -199,14 +223,30 @@ struct RunSet {
   RunCodes c[NT];
 };
 
-template <int NT>
+template <int NT, bool X3>
 __device__ inline RunSet<NT> load_runs(const uint8_t* __restrict__ base, uint32_t row_off0, uint32_t nt_stride, int ob,
-                                       int row_bytes) {
+                                       uint32_t back = 0) {
   RunSet<NT> rs;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run(base, row_off0 + nt * nt_stride, ob, row_bytes);
+  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run<X3>(base, row_off0 + nt * nt_stride, ob, back);
   return rs;
 }
+
+template <int NT>
+__device__ inline RunSet<NT> load_runs_wrapping(const uint8_t* __restrict__ base, uint32_t row_off0,
+                                                uint32_t nt_stride, int ob, int row_bytes) {
+  RunSet<NT> rs;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run_wrapping(base, row_off0 + nt * nt_stride, ob, row_bytes);
+  return rs;
+}
+
+// Block order of a task: a row's last 128-input block first (the only one whose look-ahead
+// wraps, loaded before the loop), then blocks 0, 1, ..., kblocks-2, whose runs each come from
+// one 12-byte load that stays inside the row.  Iteration i works on block_at(i) and prefetches
+// block_at(i + 1) = i; the last iteration's prefetch is not used (block 0, moved 4 bytes back
+// for lane group 3 so that it stays inside a one-block row).
+__device__ inline int block_at(int i, int kblocks) { return i == 0 ? kblocks - 1 : i - 1; }
 
 // Grouped and dequantize arms: scale and store one task's 16-pair x 16-row MFMA tiles.
 // D layout: lane holds rows 4*(lane/16)+t (pairs) of column lane%16 (output row).
@@ -281,7 +321,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
 
 // Grouped arm: NS row blocks of 16 pairs x NT row blocks of 16 outputs share one decode of
 // the 16*NT rows; each A fragment feeds NT MFMAs.
-template <int MODE, int NS, int NT, bool APRE>
+template <int MODE, int NS, int NT, bool APRE, bool X3 = false>
 __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -314,11 +354,13 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
   // With APRE the activations are double-buffered as well: block kb+1's are requested during
   // block kb, so every wait in the loop is for loads issued a whole block earlier.
   u32x4 an[NS][4];
-  if (APRE) load_a_block<NS>(an, p.act, aoff, 0);
-  RunSet<NT> n0 = load_runs<NT>(base0, roff, nt_stride, g * 8, row_bytes);
-  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(base1, roff, nt_stride, g * 8, row_bytes) : n0;
-  for (int kb = 0; kb < kblocks; ++kb) {
-    const int kn = kb + 1 < kblocks ? kb + 1 : 0;
+  if (APRE) load_a_block<NS>(an, p.act, aoff, kblocks - 1);
+  const int ob_last = (kblocks - 1) * 32 + g * 8;
+  RunSet<NT> n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
+  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
+  for (int i = 0; i < kblocks; ++i) {
+    const int kb = block_at(i, kblocks);
+    const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
     u32x4 a[NS][4];
     if (APRE) {
 #pragma unroll
@@ -332,8 +374,9 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
     }
     const RunSet<NT> c0 = n0, c1 = n1;
     const int ob = kn * 32 + g * 8;
-    n0 = load_runs<NT>(base0, roff, nt_stride, ob, row_bytes);
-    if (MODE == kModeGateUp) n1 = load_runs<NT>(base1, roff, nt_stride, ob, row_bytes);
+    const uint32_t back = (i + 1 < kblocks || g != 3) ? 0u : 8u;
+    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
+    if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -365,7 +408,7 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
 }
 
 // GEMV arm: NQ pairs x NT row blocks of 16 outputs share one decode; VALU bf16 dot products.
-template <int MODE, int NQ, int NT, bool APRE>
+template <int MODE, int NQ, int NT, bool APRE, bool X3 = false>
 __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -388,11 +431,13 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
   }
 
   u32x4 xn[NQ][4];
-  if (APRE) load_a_block<NQ>(xn, p.act, xoff, 0);
-  RunSet<NT> n0 = load_runs<NT>(base0, roff, nt_stride, g * 8, row_bytes);
-  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs<NT>(base1, roff, nt_stride, g * 8, row_bytes) : n0;
-  for (int kb = 0; kb < kblocks; ++kb) {
-    const int kn = kb + 1 < kblocks ? kb + 1 : 0;
+  if (APRE) load_a_block<NQ>(xn, p.act, xoff, kblocks - 1);
+  const int ob_last = (kblocks - 1) * 32 + g * 8;
+  RunSet<NT> n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
+  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
+  for (int i = 0; i < kblocks; ++i) {
+    const int kb = block_at(i, kblocks);
+    const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
     u32x4 x[NQ][4];
     if (APRE) {
 #pragma unroll
@@ -406,8 +451,9 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
     }
     const RunSet<NT> c0 = n0, c1 = n1;
     const int ob = kn * 32 + g * 8;
-    n0 = load_runs<NT>(base0, roff, nt_stride, ob, row_bytes);
-    if (MODE == kModeGateUp) n1 = load_runs<NT>(base1, roff, nt_stride, ob, row_bytes);
+    const uint32_t back = (i + 1 < kblocks || g != 3) ? 0u : 8u;
+    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
+    if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -463,6 +509,9 @@ struct ExpertCfg {
   // Activation double-buffering where the register budget allows it: 512 VGPRs per SIMD lane
   // shared by WAVES/4 waves (168 at 12 waves, where the 4-block task would spill).
   static constexpr bool kAPre = WAVES <= 8 || NT <= 2;
+  // 12-byte code loads in the down pass: measured faster with 12 waves of 64-row tasks (fewer
+  // vector-memory accesses where they compete with the LUT gathers), slower with 16 waves.
+  static constexpr bool kX3Down = WAVES == 12 && NT == 4;
 };
 using Cfg1 = ExpertCfg<16, 1, 2, 2>;
 using Cfg2 = ExpertCfg<8, 1, 4, 4>;
@@ -479,6 +528,7 @@ template <int MODE, int ARM, class CFG>
 __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   constexpr int NT = CFG::kNT;
   constexpr bool AP = CFG::kAPre;
+  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
   constexpr int kChunk = (ARM == kArmGemv) ? CFG::kGPairs : CFG::kNSub * 16;
   static_assert(CFG::kNSub >= 1 && CFG::kNSub <= 4 && CFG::kGPairs >= 1 && CFG::kGPairs <= 4, "config");
   for (int c0 = 0; c0 < un.len; c0 += kChunk) {
@@ -492,17 +542,17 @@ __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, cons
       }
     } else if (ARM == kArmGrouped) {
       switch ((part.len + 15) >> 4) {
-        case 1: task_grouped<MODE, 1, NT, AP>(p, lut, part, r0); break;
-        case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP>(p, lut, part, r0); break;
-        case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT, AP>(p, lut, part, r0); break;
-        default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT, AP>(p, lut, part, r0); break;
+        case 1: task_grouped<MODE, 1, NT, AP, X3>(p, lut, part, r0); break;
+        case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP, X3>(p, lut, part, r0); break;
+        case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT, AP, X3>(p, lut, part, r0); break;
+        default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT, AP, X3>(p, lut, part, r0); break;
       }
     } else {
       switch (part.len) {
-        case 1: task_gemv<MODE, 1, NT, AP>(p, lut, part, r0); break;
-        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP>(p, lut, part, r0); break;
-        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP>(p, lut, part, r0); break;
-        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP>(p, lut, part, r0); break;
+        case 1: task_gemv<MODE, 1, NT, AP, X3>(p, lut, part, r0); break;
+        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP, X3>(p, lut, part, r0); break;
+        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP, X3>(p, lut, part, r0); break;
+        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP, X3>(p, lut, part, r0); break;
       }
     }
   }
@@ -573,10 +623,11 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
       const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
       uint16_t* out = (m ? q.out1 : q.out0) + (size_t)e * (size_t)q.out_expert_stride;
       const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
-      RunCodes nx = load_run(base, roff, g * 8, row_bytes);
-      for (int kb = 0; kb < kblocks; ++kb) {
+      RunCodes nx = load_run_wrapping(base, roff, (kblocks - 1) * 32 + g * 8, row_bytes);
+      for (int i = 0; i < kblocks; ++i) {
+        const int kb = block_at(i, kblocks);
         const RunCodes rc = nx;
-        if (kb + 1 < kblocks) nx = load_run(base, roff, (kb + 1) * 32 + g * 8, row_bytes);
+        if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + g * 8);
         u32x4 w[4];
         decode16(lut_s, rc.d0, rc.d1, w[0], w[1]);
         decode16(lut_s, rc.d1, rc.la, w[2], w[3]);
