@@ -58,7 +58,7 @@ def kernel_source_sha() -> str:
 class Runner:
     """Plan + device weights + workspace; forwards one batch through the C ABI."""
 
-    def __init__(self, inp, arm, max_tokens, out_dtype, weights=None, variant=0):
+    def __init__(self, inp, arm, max_tokens, out_dtype, weights=None, variant=0, act_layout=0):
         import torch
         import trellis_quantized_moe_expert_amd as q
         from moe_inputs.device import weights_to_device
@@ -69,7 +69,7 @@ class Runner:
                     "dequant": q.QTIP_ARM_DEQUANT}[arm]
         od = q.QTIP_OUT_BF16 if out_dtype == "bf16" else q.QTIP_OUT_F32
         self.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens, arm_code,
-                                                variant, od, 0), 0)
+                                                variant, od, 0, act_layout=act_layout), 0)
         self.info = q.qtip_moe_plan_info(self.plan)
         self.ws = torch.empty(self.info["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
         self.dw = weights if weights is not None else weights_to_device(inp)
@@ -290,7 +290,7 @@ def calibrate_copy():
     del a, b
 
 
-def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=None):
+def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=None, layouts=(0,)):
     import moe_inputs
     shape = moe_inputs.WORKLOADS["v4_decode_n32"]
     log("sweep: drawing V4-shaped weights once")
@@ -298,8 +298,8 @@ def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=N
     inps = moe_inputs.make_inputs_multi(shape, n_list, seed=0)
     base = None
     with open(path, "a") as f:
-        for arm in arms:
-            r = Runner(inps[n_list[0]], arm, max(n_list), "bf16", weights=base, variant=variant)
+        for arm, layout in [(a, l) for a in arms for l in layouts]:
+            r = Runner(inps[n_list[0]], arm, max(n_list), "bf16", weights=base, variant=variant, act_layout=layout)
             base = r.dw
             for n in n_list:
                 r.bind(inps[n])
@@ -308,7 +308,8 @@ def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=N
                 sched = r.q.qtip_moe_plan_schedule(r.plan, n)
                 fig = schedule_figures(counts, r.shape, arm, sched)
                 ms = res["wall_s"] * 1e3 / steps
-                rec = {"arm": arm, "n": n, "variant_requested": variant, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+                rec = {"arm": arm, "n": n, "variant_requested": variant, "act_layout": layout, "ms_per_step": ms,
+                       "tokens_per_s": n / (ms * 1e-3),
                        "stage_ms": {k: v / res["prof"]["n_forwards"] for k, v in res["prof"].items() if k != "n_forwards"},
                        "launches": {k: res["stats"][k] for k in ("gemv_launches", "grouped_launches",
                                                                  "dequant_launches")},
@@ -332,6 +333,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=6, help="tokens the CPU oracle is timed on, about 10 s (0: skip)")
     ap.add_argument("--sweep", metavar="PATH", default=None)
     ap.add_argument("--sweep-arms", default="gemv,grouped")
+    ap.add_argument("--sweep-layouts", default="0", help="grouped-arm activation layouts to sweep (0 auto, 1 rows, "
+                    "2 fragments)")
     ap.add_argument("--sweep-n", default=None, help="comma-separated token counts (default: the fixed list)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -360,7 +363,8 @@ def main():
         calibrate_copy()
     if args.sweep:
         n_list = [int(x) for x in args.sweep_n.split(",")] if args.sweep_n else None
-        run_sweep(args.sweep, args.steps, args.warmup, args.variant, tuple(args.sweep_arms.split(",")), n_list)
+        run_sweep(args.sweep, args.steps, args.warmup, args.variant, tuple(args.sweep_arms.split(",")), n_list,
+                  tuple(int(x) for x in args.sweep_layouts.split(",")))
         return
 
     log(f"bench: drawing workload {args.workload}")

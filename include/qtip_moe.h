@@ -72,6 +72,7 @@ typedef enum qtip_status {
  * materialised as dense bf16 in the workspace, then an MFMA pass over them). */
 enum { QTIP_ARM_AUTO = 0, QTIP_ARM_GEMV = 1, QTIP_ARM_GROUPED = 2, QTIP_ARM_DEQUANT = 3 };
 enum { QTIP_OUT_BF16 = 0, QTIP_OUT_F32 = 1 };
+enum { QTIP_ACT_AUTO = 0, QTIP_ACT_ROWS = 1, QTIP_ACT_FRAGMENTS = 2 };
 
 /* Decode-regime floor: n <= 8 tokens always take the GEMV arm (m-tile page, "The fix"). */
 #define QTIP_DECODE_REGIME_MAX_TOKENS 8
@@ -113,6 +114,10 @@ typedef struct qtip_moe_desc {
                               that can take the dequantize arm (that window is not empty, or the
                               override pins it) holds every expert's dense bf16 weights in its
                               workspace: 3 x E x H x I x 2 bytes, and needs H x I < 2^31. */
+  int32_t act_layout;   /* grouped arm's activation layout: QTIP_ACT_AUTO (by the closed-form pairs per
+                           woken expert), QTIP_ACT_ROWS (gathered rows) or QTIP_ACT_FRAGMENTS (every
+                           expert's bin padded to 16 pairs and stored in MFMA fragment order: h always,
+                           x packed by an extra pass) */
 } qtip_moe_desc;
 
 typedef struct qtip_moe_plan_s* qtip_moe_plan_t;

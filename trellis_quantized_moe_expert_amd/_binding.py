@@ -25,6 +25,9 @@ QTIP_ARM_AUTO = 0
 QTIP_ARM_GEMV = 1
 QTIP_ARM_GROUPED = 2
 QTIP_ARM_DEQUANT = 3
+QTIP_ACT_AUTO = 0
+QTIP_ACT_ROWS = 1
+QTIP_ACT_FRAGMENTS = 2
 QTIP_OUT_BF16 = 0
 QTIP_OUT_F32 = 1
 
@@ -33,7 +36,8 @@ class qtip_moe_desc(ctypes.Structure):
     _fields_ = [("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("arm_override", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("dispatch_tile_m", ctypes.c_int32), ("dequant_traffic_ratio", ctypes.c_int32)]
+                ("dispatch_tile_m", ctypes.c_int32), ("dequant_traffic_ratio", ctypes.c_int32),
+                ("act_layout", ctypes.c_int32)]
 
 
 class qtip_moe_weights(ctypes.Structure):
@@ -156,9 +160,10 @@ def _check(fn: str, status: int):
 
 
 def make_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override=QTIP_ARM_AUTO, variant=0,
-              out_dtype=QTIP_OUT_F32, tile_m=0, dispatch_tile_m=0, dequant_traffic_ratio=0) -> qtip_moe_desc:
+              out_dtype=QTIP_OUT_F32, tile_m=0, dispatch_tile_m=0, dequant_traffic_ratio=0,
+              act_layout=QTIP_ACT_AUTO) -> qtip_moe_desc:
     return qtip_moe_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override, variant, out_dtype, tile_m,
-                         dispatch_tile_m, dequant_traffic_ratio)
+                         dispatch_tile_m, dequant_traffic_ratio, act_layout)
 
 
 def make_weights(codes_gate, codes_up, codes_down, scale_gate, scale_up, scale_down, lut) -> qtip_moe_weights:

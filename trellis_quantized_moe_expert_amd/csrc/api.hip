@@ -115,8 +115,15 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, h, y, router_part,
-      dense_gate, dense_up, dense_down, total;
+      dense_gate, dense_up, dense_down, padded_pair, unit_pad, n_pad, xs, total;
 };
+
+// Padded positions (every woken expert's bin rounded up to 16 pairs) for n tokens, a multiple of 16.
+size_t pad_positions(const qtip_moe_desc& d, int32_t n_tokens) {
+  const size_t P = (size_t)n_tokens * d.top_k;
+  const size_t woken_max = P < (size_t)d.num_experts ? P : (size_t)d.num_experts;
+  return (P + 15 * woken_max + 15) & ~(size_t)15;
+}
 
 // Largest router-GEMM partial buffer, S(n) * n * E floats, over the batch sizes a plan accepts.
 // From 32 * kRouterTargetGroups tokens on there are enough tiles for a split of 1, so n_max
@@ -147,7 +154,8 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.n_tiles = o;      o = align256(o + 4);
   L.unit_map = o;     o = align256(o + max_units * 12);
   L.n_units = o;      o = align256(o + 4);
-  L.h = o;            o = align256(o + P * (size_t)d.inter * 2);
+  const size_t PP = pad_positions(d, n_tokens);
+  L.h = o;            o = align256(o + PP * (size_t)d.inter * 2);  // row-major (P rows) or fragment order (PP)
   L.y = o;            o = align256(o + P * (size_t)d.hidden * 4);
   L.router_part = o;  o = align256(o + router_part_elems(d, n_tokens) * 4);
   // dequantize arm: every expert's dense bf16 weights (only when the plan can take that arm)
@@ -155,6 +163,10 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.dense_gate = o;   o = align256(o + dense_mat);
   L.dense_up = o;     o = align256(o + dense_mat);
   L.dense_down = o;   o = align256(o + dense_mat);
+  L.padded_pair = o;  o = align256(o + PP * 4);
+  L.unit_pad = o;     o = align256(o + max_units * 4);
+  L.n_pad = o;        o = align256(o + 4);
+  L.xs = o;           o = align256(o + PP * (size_t)d.hidden * 2);
   L.total = o;
   return L;
 }
@@ -252,11 +264,19 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
     return fail(QTIP_ERR_INVALID_ARG, "max_tokens * top_k * max(hidden, inter) must be below 2^31");
   if ((int64_t)d->hidden * d->inter / 4 >= ((int64_t)1 << 31))
     return fail(QTIP_ERR_INVALID_ARG, "one expert matrix must be below 2^31 bytes");
+  {
+    const int64_t P = (int64_t)d->max_tokens * d->top_k;
+    const int64_t PP = P + 15 * (P < d->num_experts ? P : d->num_experts) + 15;
+    if (PP * (d->hidden > d->inter ? d->hidden : d->inter) >= ((int64_t)1 << 31))
+      return fail(QTIP_ERR_INVALID_ARG, "padded pairs * max(hidden, inter) must be below 2^31");
+  }
   if ((int64_t)d->num_experts * d->hidden >= ((int64_t)1 << 31))
     return fail(QTIP_ERR_INVALID_ARG, "num_experts * hidden (the router weight) must be below 2^31 elements");
   if (d->arm_override != QTIP_ARM_AUTO && d->arm_override != QTIP_ARM_GEMV && d->arm_override != QTIP_ARM_GROUPED &&
       d->arm_override != QTIP_ARM_DEQUANT)
     return fail(QTIP_ERR_INVALID_ARG, "unknown arm_override");
+  if (d->act_layout != QTIP_ACT_AUTO && d->act_layout != QTIP_ACT_ROWS && d->act_layout != QTIP_ACT_FRAGMENTS)
+    return fail(QTIP_ERR_INVALID_ARG, "unknown act_layout");
   if (d->dequant_traffic_ratio < 0 || d->dequant_traffic_ratio > 1024)
     return fail(QTIP_ERR_INVALID_ARG, "dequant_traffic_ratio must be in [0, 1024]");
   if (d->out_dtype != QTIP_OUT_BF16 && d->out_dtype != QTIP_OUT_F32) return fail(QTIP_ERR_INVALID_ARG, "unknown out_dtype");
@@ -449,7 +469,7 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
   if (e != hipSuccess) return hip_fail(e, "route_topk launch");
   plan->stats.route_launches++;
   e = launch_bin(topk_idx, n_tokens * d.top_k, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets,
-                 sorted_pair, tile_map, n_tiles, nullptr, nullptr, st);
+                 sorted_pair, tile_map, n_tiles, nullptr, nullptr, nullptr, nullptr, nullptr, st);
   if (e != hipSuccess) return hip_fail(e, "bin launch");
   plan->stats.route_launches++;
   return QTIP_OK;
@@ -565,10 +585,28 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   e = launch_route_topk(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
   if (e != hipSuccess) return hip_fail(e, "route_topk launch");
   if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
+  // The grouped arm's activation layout: fragment order over padded positions for h (and the
+  // down pass) from kFragMinPairs pairs per woken expert, for x too (an extra packing pass)
+  // from kPackMinPairs; gathered rows below.
+  const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
+  const bool frag = karm == kArmGrouped && d.act_layout != QTIP_ACT_ROWS &&
+                    (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kFragMinPairs);
+  int32_t* padded_pair = reinterpret_cast<int32_t*>(ws + L.padded_pair);
+  int32_t* unit_pad = reinterpret_cast<int32_t*>(ws + L.unit_pad);
+  int32_t* n_pad = reinterpret_cast<int32_t*>(ws + L.n_pad);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
+  const int32_t pp_max = (int32_t)pad_positions(d, n_tokens);
   e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets, sorted_pair, tile_map,
-                 n_tiles, unit_map, n_units, st);
+                 n_tiles, unit_map, n_units, frag ? padded_pair : nullptr, frag ? unit_pad : nullptr,
+                 frag ? n_pad : nullptr, st);
   if (e != hipSuccess) return hip_fail(e, "bin launch");
   plan->stats.route_launches += 2;
+  const bool pack = frag && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
+  if (pack) {
+    e = launch_pack_act(reinterpret_cast<const uint16_t*>(x_bf16), padded_pair, n_pad, d.top_k, d.hidden, pp_max, xs,
+                        st);
+    if (e != hipSuccess) return hip_fail(e, "activation pack launch");
+  }
   if ((e = prof_mark(plan, 2, st)) != hipSuccess) return hip_fail(e, "profile event");
 
   uint16_t* dense_gate = reinterpret_cast<uint16_t*>(ws + L.dense_gate);
@@ -624,6 +662,14 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   gu.out = h;
   gu.n_out_rows = P;
   gu.n_xcd = xcd_count(dev);
+  if (frag) {
+    gu.unit_pad = unit_pad;
+    gu.n_pad_max = pp_max;
+  }
+  if (pack) {
+    gu.act = xs;
+    gu.act_frag = 1;
+  }
   const int kv_gu = fit_variant(resolve_variant(plan, karm, kModeGateUp, n_tokens), karm, d.inter);
   VariantInfo vi{};
   variant_info(kv_gu, karm, vi);
@@ -649,6 +695,11 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   dn.out_row_map = sorted_pair;
   dn.n_out_rows = P;
   dn.n_xcd = xcd_count(dev);
+  if (frag) {
+    dn.unit_pad = unit_pad;
+    dn.act_frag = 1;
+    dn.n_pad_max = pp_max;
+  }
   const int kv_dn = fit_variant(resolve_variant(plan, karm, kModeSingle, n_tokens), karm, d.hidden);
   variant_info(kv_dn, karm, vi);
   e = launch_expert(kModeSingle, karm, kv_dn, dn, persistent_grid(dev, max_units * (d.hidden / vi.rows_per_task), vi.waves), st);

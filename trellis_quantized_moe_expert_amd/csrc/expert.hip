@@ -148,6 +148,7 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
 struct Unit {
   int e, start, len;
+  int pad;  // start in the padded position space (a multiple of 16), or -1 without one
 };
 
 // Reads and validates a unit; returns false for a unit that must be skipped.
@@ -155,8 +156,10 @@ __device__ inline bool read_unit(const ExpertParams& p, int u, Unit& un) {
   un.e = p.units[3 * u + 0];
   un.start = p.units[3 * u + 1];
   un.len = p.units[3 * u + 2];
+  un.pad = p.unit_pad ? p.unit_pad[u] : -1;
+  const bool pad_ok = !p.unit_pad || (un.pad >= 0 && (un.pad & 15) == 0 && un.pad <= p.n_pad_max - ((un.len + 15) & ~15));
   return un.e >= 0 && un.e < p.num_experts && un.len >= 1 && un.len <= kUnitMaxPairs && un.start >= 0 &&
-         un.start <= p.n_pos - un.len;
+         un.start <= p.n_pos - un.len && pad_ok;
 }
 
 // Activation row of binned position s, or -1 if it is out of range.
@@ -177,7 +180,16 @@ __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int
   if (MODE == kModeGateUp) {
     const float g = a0 * s0, u = a1 * s1;
     const float h = silu(g) * u;
-    reinterpret_cast<uint16_t*>(p.out)[(size_t)s * p.rows + r] = (uint16_t)f32_to_bf16_bits(h);
+    size_t o;
+    if (p.unit_pad) {
+      // h in fragment order over padded positions, as the down pass reads its A operand
+      // (its input index r = kb*128 + 32g + 8st + t)
+      const int pp = un.pad + pi;
+      o = dense_fragment_offset(pp >> 4, r >> 7, (r >> 3) & 3, (pp & 15) + 16 * ((r >> 5) & 3), p.rows >> 7) + (r & 7);
+    } else {
+      o = (size_t)s * p.rows + r;
+    }
+    reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_to_bf16_bits(h);
   } else {
     const int orow = out_row(p, s);
     if (orow >= 0) reinterpret_cast<float*>(p.out)[(size_t)orow * p.rows + r] = a0 * s0;
@@ -197,6 +209,26 @@ __device__ inline void load_a_block(u32x4 (&a)[NS][4], const uint16_t* __restric
     for (int st = 0; st < 4; ++st)
       a[m][st] = *reinterpret_cast<const u32x4*>(act + (aoff[m] + (uint32_t)(kb * kKBlock + st * 8)));
   }
+}
+
+// The same fragments from activations in fragment order: for 16-pair block m the wave's 64
+// lanes read 1 KiB contiguous per MFMA step (fo[m] = the block's offset for this lane at kb = 0,
+// st = 0; consecutive steps are 512 elements apart, blocks 2048).
+template <int NS>
+__device__ inline void load_a_block_frag(u32x4 (&a)[NS][4], const uint16_t* __restrict__ act, const uint32_t (&fo)[NS],
+                                         int kb) {
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      a[m][st] = *reinterpret_cast<const u32x4*>(act + (fo[m] + (uint32_t)(kb * 2048 + st * 512)));
+  }
+}
+
+template <int NS, bool FRAG>
+__device__ inline void load_a(u32x4 (&a)[NS][4], const uint16_t* __restrict__ act, const uint32_t (&off)[NS], int kb) {
+  if (FRAG) load_a_block_frag<NS>(a, act, off, kb);
+  else load_a_block<NS>(a, act, off, kb);
 }
 
 // Activation row offsets (elements from p.act) of this lane for NS entries; entry m is the
@@ -321,7 +353,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
 
 // Grouped arm: NS row blocks of 16 pairs x NT row blocks of 16 outputs share one decode of
 // the 16*NT rows; each A fragment feeds NT MFMAs.
-template <int MODE, int NS, int NT, bool APRE, bool X3 = false>
+template <int MODE, int NS, int NT, bool APRE, bool X3 = false, bool FRAG = false>
 __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -335,7 +367,12 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
 
   uint32_t aoff[NS];  // A operand row i = lane%16 of each 16-pair block
-  act_rows<NS>(p, un, j, 16, g, aoff);
+  if (FRAG) {
+#pragma unroll
+    for (int m = 0; m < NS; ++m) aoff[m] = (uint32_t)dense_fragment_offset((un.pad >> 4) + m, 0, 0, lane, kblocks);
+  } else {
+    act_rows<NS>(p, un, j, 16, g, aoff);
+  }
 
   f32x4 acc0[NS][NT], acc1[NS][NT];
 #pragma unroll
@@ -354,7 +391,7 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
   // With APRE the activations are double-buffered as well: block kb+1's are requested during
   // block kb, so every wait in the loop is for loads issued a whole block earlier.
   u32x4 an[NS][4];
-  if (APRE) load_a_block<NS>(an, p.act, aoff, kblocks - 1);
+  if (APRE) load_a<NS, FRAG>(an, p.act, aoff, kblocks - 1);
   const int ob_last = (kblocks - 1) * 32 + g * 8;
   RunSet<NT> n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
   RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
@@ -368,9 +405,9 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
 #pragma unroll
         for (int st = 0; st < 4; ++st) a[m][st] = an[m][st];
       }
-      load_a_block<NS>(an, p.act, aoff, kn);
+      load_a<NS, FRAG>(an, p.act, aoff, kn);
     } else {
-      load_a_block<NS>(a, p.act, aoff, kb);
+      load_a<NS, FRAG>(a, p.act, aoff, kb);
     }
     const RunSet<NT> c0 = n0, c1 = n1;
     const int ob = kn * 32 + g * 8;
@@ -521,10 +558,24 @@ using Cfg5 = ExpertCfg<8, 4, 2, 2>;
 using Cfg6 = ExpertCfg<12, 2, 2, 2>;
 using Cfg7 = ExpertCfg<12, 4, 2, 2>;
 
+// The grouped body specialised for the chunk's exact number of 16-pair row blocks.
+template <int MODE, class CFG, bool FRAG>
+__device__ inline void grouped_blocks(const ExpertParams& p, const uint16_t* lut, const Unit& part, int r0) {
+  constexpr int NT = CFG::kNT;
+  constexpr bool AP = CFG::kAPre;
+  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
+  switch ((part.len + 15) >> 4) {
+    case 1: task_grouped<MODE, 1, NT, AP, X3, FRAG>(p, lut, part, r0); break;
+    case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
+    case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
+    default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
+  }
+}
+
 // A unit may hold more pairs than one decode serves; it is then processed in chunks, each
 // chunk decoding the rows again.  Each chunk runs the body specialised for its exact number
 // of 16-pair row blocks (grouped) or pairs (GEMV), chosen by a wave-uniform switch.
-template <int MODE, int ARM, class CFG>
+template <int MODE, int ARM, class CFG, bool FRAG>
 __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
   constexpr int NT = CFG::kNT;
   constexpr bool AP = CFG::kAPre;
@@ -532,7 +583,7 @@ __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, cons
   constexpr int kChunk = (ARM == kArmGemv) ? CFG::kGPairs : CFG::kNSub * 16;
   static_assert(CFG::kNSub >= 1 && CFG::kNSub <= 4 && CFG::kGPairs >= 1 && CFG::kGPairs <= 4, "config");
   for (int c0 = 0; c0 < un.len; c0 += kChunk) {
-    const Unit part{un.e, un.start + c0, min(kChunk, un.len - c0)};
+    const Unit part{un.e, un.start + c0, min(kChunk, un.len - c0), un.pad >= 0 ? un.pad + c0 : -1};
     if (ARM == kArmDense) {
       switch ((part.len + 15) >> 4) {
         case 1: task_dense<MODE, 1, NT>(p, part, r0); break;
@@ -541,12 +592,7 @@ __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, cons
         default: if (CFG::kNSub >= 4) task_dense<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT>(p, part, r0); break;
       }
     } else if (ARM == kArmGrouped) {
-      switch ((part.len + 15) >> 4) {
-        case 1: task_grouped<MODE, 1, NT, AP, X3>(p, lut, part, r0); break;
-        case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP, X3>(p, lut, part, r0); break;
-        case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT, AP, X3>(p, lut, part, r0); break;
-        default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT, AP, X3>(p, lut, part, r0); break;
-      }
+      grouped_blocks<MODE, CFG, FRAG>(p, lut, part, r0);
     } else {
       switch (part.len) {
         case 1: task_gemv<MODE, 1, NT, AP, X3>(p, lut, part, r0); break;
@@ -558,7 +604,7 @@ __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, cons
   }
 }
 
-template <int MODE, int ARM, class CFG>
+template <int MODE, int ARM, class CFG, bool FRAG>
 __device__ inline void expert_tasks(const ExpertParams& p, const uint16_t* lut_s) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = p.n_units_dev ? __builtin_amdgcn_readfirstlane(*p.n_units_dev) : p.n_units_host;
@@ -582,18 +628,19 @@ __device__ inline void expert_tasks(const ExpertParams& p, const uint16_t* lut_s
     const int nb = (int)(task - (long)u * nblocks);
     Unit un;
     if (!read_unit(p, u, un)) continue;
-    run_task<MODE, ARM, CFG>(p, lut_s, un, nb * CFG::kRows);
+    run_task<MODE, ARM, CFG, FRAG>(p, lut_s, un, nb * CFG::kRows);
   }
 }
 
-template <int MODE, int ARM, class CFG>
+// FRAG: the grouped arm's activations are in fragment order (ExpertParams::act_frag).
+template <int MODE, int ARM, class CFG, bool FRAG = false>
 __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParams p) {
   if constexpr (ARM == kArmDense) {
-    expert_tasks<MODE, ARM, CFG>(p, nullptr);
+    expert_tasks<MODE, ARM, CFG, false>(p, nullptr);
   } else {
     __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
     fill_lut(lut_s, p.lut);
-    expert_tasks<MODE, ARM, CFG>(p, lut_s);
+    expert_tasks<MODE, ARM, CFG, FRAG>(p, lut_s);
   }
 }
 
@@ -642,6 +689,38 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
         }
       }
     }
+  }
+}
+
+// Activations of the grouped arm in fragment order: one thread per 16-byte fragment slot
+// (padded 16-row block, 128-input block kb, MFMA step st, lane j + 16g) copies inputs
+// kb*128 + 32g + 8st .. +7 of its padded position's token row, so consecutive threads write
+// consecutive 16-byte slots.  Padding slots are left as they are: only the MFMA rows of padded
+// positions read them, and those rows' results are never stored (each output row of an MFMA
+// depends on its own A row only).
+__global__ __launch_bounds__(256) void pack_act_kernel(const uint16_t* __restrict__ x,
+                                                       const int32_t* __restrict__ padded_pair,
+                                                       const int32_t* __restrict__ n_pad, int32_t k, int32_t H,
+                                                       int32_t n_pad_max, uint16_t* __restrict__ xs) {
+  // one thread per (padded 16-row block, 128-input block, lane): it reads the 64 contiguous
+  // bytes of its four MFMA steps and writes them to the four step slots, 1 KiB apart
+  const int kblocks = H / kKBlock;
+  const int npad = min(*n_pad, n_pad_max);
+  const long items = (long)(npad >> 4) * kblocks * 64;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < items; i += (long)gridDim.x * 256) {
+    const int lane = (int)(i & 63);
+    const long rest = i >> 6;
+    const int kb = (int)(rest % kblocks);
+    const int rb = (int)(rest / kblocks);
+    const int pair = padded_pair[rb * 16 + (lane & 15)];
+    if (pair < 0) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)(pair / k) * H + kb * kKBlock + 32 * (lane >> 4));
+    u32x4 v[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) v[st] = src[st];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      *reinterpret_cast<u32x4*>(xs + dense_fragment_offset(rb, kb, st, lane, kblocks)) = v[st];
   }
 }
 
@@ -715,13 +794,19 @@ static void launch_cfg(int mode, int arm, const ExpertParams& p, int grid, hipSt
       hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmDense, CfgDense>), g, bd, 0, stream, p);
     else
       hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmDense, CfgDense>), g, bd, 0, stream, p);
-  } else if (mode == kModeGateUp && arm == kArmGrouped)
-    hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG>), g, b, 0, stream, p);
-  else if (mode == kModeGateUp)
+  } else if (mode == kModeGateUp && arm == kArmGrouped) {
+    if (p.act_frag && p.unit_pad)
+      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, true>), g, b, 0, stream, p);
+    else
+      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, false>), g, b, 0, stream, p);
+  } else if (mode == kModeGateUp) {
     hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG>), g, b, 0, stream, p);
-  else if (arm == kArmGrouped)
-    hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped, CFG>), g, b, 0, stream, p);
-  else
+  } else if (arm == kArmGrouped) {
+    if (p.act_frag && p.unit_pad)
+      hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped, CFG, true>), g, b, 0, stream, p);
+    else
+      hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped, CFG, false>), g, b, 0, stream, p);
+  } else
     hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGemv, CFG>), g, b, 0, stream, p);
 }
 
@@ -764,6 +849,16 @@ hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, 
     case 7: launch_cfg<Cfg7>(mode, arm, p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_act(const uint16_t* x, const int32_t* padded_pair, const int32_t* n_pad, int32_t k,
+                           int32_t H, int32_t n_pad_max, uint16_t* xs, hipStream_t stream) {
+  const long items = (long)(n_pad_max >> 4) * (H / kKBlock) * 64;
+  const long blocks = (items + 255) / 256;
+  const int grid = (int)(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(pack_act_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, stream, x, padded_pair, n_pad, k, H,
+                     n_pad_max, xs);
   return hipGetLastError();
 }
 

@@ -24,6 +24,10 @@ constexpr int kWitnessValue = 0x950950;
 constexpr int kRouterMaxWaves = 8;        // waves of a router-GEMM workgroup (they split its input chunk)
 constexpr int kRouterTargetGroups = 256;  // router-GEMM workgroups wanted: one per CU
 constexpr int kRouterMaxSplit = 4;        // input chunks (partial sums) per logit at most
+// Automatic activation layout of the grouped arm (pairs per woken expert, closed form): h in
+// fragment order from kFragMinPairs on, x packed in fragment order from kPackMinPairs on.
+constexpr double kFragMinPairs = 8.0;
+constexpr double kPackMinPairs = 16.0;
 
 // One pass of one (or two fused) trellis matrices over binned activation rows.
 struct ExpertParams {
@@ -46,6 +50,12 @@ struct ExpertParams {
   const int32_t* out_row_map;   // single pass: output row of position s = map[s] (NULL: s)
   int32_t n_out_rows;
   int32_t n_xcd;                // workgroups are dispatched round-robin over this many XCDs (>= 1)
+  const int32_t* unit_pad;      // grouped arm: each unit's start in the padded position space (every expert's
+                                // bin rounded up to 16 pairs), or NULL.  When set, the fused pass writes h in
+                                // fragment order over padded positions (dense_fragment_offset, rows = padded
+                                // positions), the order the down pass reads it in.
+  int32_t act_frag;             // with unit_pad: the activations (act) are in that fragment order as well
+  int32_t n_pad_max;            // padded positions the fragment-order buffers hold (with unit_pad)
   const uint16_t* dense0;       // dequantize arm: [E] x rows x cols bf16 weights in fragment order (gate, or the single matrix)
   const uint16_t* dense1;       // dequantize arm: the same for the up weights (fused pass only)
 };
@@ -101,9 +111,19 @@ hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w, int32_t n, i
                               int32_t n_xcd, float* part, hipStream_t stream);
 hipError_t launch_router_reduce(const float* part, int32_t S, int64_t count, float* logits, hipStream_t stream);
 
+// Binning.  unit_map/n_units may be NULL (no units); padded_pair/unit_pad/n_pad may be NULL (no
+// padded position space).  The padded space rounds every expert's bin up to a multiple of 16
+// pairs: padded_pair[pp] is the pair at padded position pp or -1 in the padding, unit_pad[u]
+// the padded start of unit u (a multiple of 16), *n_pad the padded total.
 hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
                       int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map,
-                      int32_t* n_tiles, int32_t* unit_map, int32_t* n_units, hipStream_t stream);
+                      int32_t* n_tiles, int32_t* unit_map, int32_t* n_units, int32_t* padded_pair,
+                      int32_t* unit_pad, int32_t* n_pad, hipStream_t stream);
+
+// Gathers the activation row of every padded position (token = pair / k; padding untouched)
+// into fragment order: xs holds n_pad_max padded rows of H bf16 values.
+hipError_t launch_pack_act(const uint16_t* x, const int32_t* padded_pair, const int32_t* n_pad, int32_t k,
+                           int32_t H, int32_t n_pad_max, uint16_t* xs, hipStream_t stream);
 
 hipError_t launch_combine(const float* y, const float* topk_w, int32_t n, int32_t k, int32_t H, void* out,
                           int out_bf16, hipStream_t stream);

@@ -125,9 +125,13 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ sorted_pair,
                                                           int32_t* __restrict__ tile_map, int32_t* __restrict__ n_tiles,
                                                           int32_t* __restrict__ unit_map,
-                                                          int32_t* __restrict__ n_units) {
+                                                          int32_t* __restrict__ n_units,
+                                                          int32_t* __restrict__ padded_pair,
+                                                          int32_t* __restrict__ unit_pad,
+                                                          int32_t* __restrict__ n_pad) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int running[kMaxExperts];
+  __shared__ int pad_shift[kMaxExperts];  // padded position - binned position, per expert
   __shared__ int wave_cnt[kExpertWaves][kMaxExperts];
   __shared__ int wave_tot[kExpertWaves];
   const int tid = threadIdx.x;
@@ -145,14 +149,21 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
   const int c = (tid < E) ? cnt[tid] : 0;
   const int nt = (c + tile_m - 1) / tile_m;
   const int nu = (c + unit_pairs - 1) / unit_pairs;
+  const int pc = (c + 15) & ~15;  // the bin rounded up to whole 16-pair MFMA blocks
   const int c_incl = block_inclusive_scan(c, wave_tot);
   const int t_incl = block_inclusive_scan(nt, wave_tot);
   const int u_incl = block_inclusive_scan(nu, wave_tot);
+  const int p_incl = block_inclusive_scan(pc, wave_tot);
   if (tid < E) {
     const int off = c_incl - c;
+    const int poff = p_incl - pc;
     counts[tid] = c;
     offsets[tid] = off;
     running[tid] = off;
+    pad_shift[tid] = poff - off;
+    if (padded_pair)
+      for (int q = c; q < pc; ++q) padded_pair[poff + q] = -1;
+    for (int q = 0; unit_pad && q < nu; ++q) unit_pad[u_incl - nu + q] = poff + q * unit_pairs;
     int tb = t_incl - nt;
     for (int q = 0; q < nt; ++q) {
       tile_map[3 * (tb + q) + 0] = tid;
@@ -170,6 +181,7 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
     offsets[E] = c_incl;
     *n_tiles = t_incl;
     if (n_units) *n_units = u_incl;
+    if (n_pad) *n_pad = p_incl;
   }
   __syncthreads();
 
@@ -197,6 +209,7 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
       int pos = running[e] + rank;
       for (int w = 0; w < wv; ++w) pos += wave_cnt[w][e];
       sorted_pair[pos] = p;
+      if (padded_pair) padded_pair[pos + pad_shift[e]] = p;
     }
     __syncthreads();
     for (int ee = tid; ee < E; ee += kBinThreads) {
@@ -220,9 +233,11 @@ hipError_t launch_route_topk(const float* logits, int32_t n_part, int32_t n, int
 
 hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
                       int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
-                      int32_t* unit_map, int32_t* n_units, hipStream_t stream) {
+                      int32_t* unit_map, int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
+                      hipStream_t stream) {
   hipLaunchKernelGGL(bin_kernel, dim3(1), dim3(kBinThreads), 0, stream, topk_idx, n_pairs, E, tile_m, unit_pairs,
-                     counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units);
+                     counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, padded_pair, unit_pad,
+                     n_pad);
   return hipGetLastError();
 }
 
