@@ -154,3 +154,23 @@ def test_kernel_variants_full_parity(variant, arm):
     ref = moe.moe_forward(inp)
     assert ref["bins"]["counts"].max() > 64
     check(got, ref, "f32")
+
+
+@pytest.mark.parametrize("layout", [q.QTIP_ACT_ROWS, q.QTIP_ACT_FRAGMENTS])
+@pytest.mark.parametrize("variant", [1, 4, 7])
+@pytest.mark.parametrize("n", [1, 17, 260])
+def test_activation_layouts_full_parity(layout, variant, n):
+    """Both activation layouts of the grouped arm (gathered rows; fragment order over 16-padded
+    bins with the packing pass), forced on, with experts holding 1, a few and > 64 pairs."""
+    inp = moe_inputs.make_inputs(MID, seed=9, n_tokens=n)
+    say(f"forward layout={layout} variant={variant} n={n}")
+    s = inp.shape
+    layer = Layer(inp, arm=q.QTIP_ARM_GROUPED, max_tokens=260)
+    q.qtip_moe_plan_destroy(layer.plan)
+    layer.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, 260, q.QTIP_ARM_GROUPED,
+                                             variant, q.QTIP_OUT_F32, 0, act_layout=layout), 0)
+    import torch
+    layer.ws = torch.empty(q.qtip_moe_plan_info(layer.plan)["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
+    got = layer.forward(inp)
+    layer.close()
+    check(got, moe.moe_forward(inp), "f32")
