@@ -21,8 +21,42 @@ __device__ inline bool beats(float v, int e, float bv, int be) {
   return v > bv || (v == bv && e < be);
 }
 
+// Order-preserving integer key of a float under `>` (+0 and -0 map to the same key, as they
+// compare equal; NaN, never selected by `beats`, maps below every number).
+__device__ inline uint32_t order_key(float v) {
+  if (v != v) return 0u;
+  if (v == 0.0f) v = 0.0f;
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wave-wide max / min of one 32-bit value per lane without the LDS: an inclusive scan inside
+// each 16-lane row by DPP row shifts (lanes past the row start keep their own value), then the
+// four row results (lanes 15, 31, 47, 63) combined in scalar registers.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ inline int wave_min_i32(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x111, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x112, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xF, 0xF, false));
+  const int a = __builtin_amdgcn_readlane(v, 15), b = __builtin_amdgcn_readlane(v, 31);
+  const int c = __builtin_amdgcn_readlane(v, 47), d = __builtin_amdgcn_readlane(v, 63);
+  return min(min(a, b), min(c, d));
+}
+
 // One wave per token.  Each lane holds up to 16 logits (E <= 1024); k rounds of a wave-wide
-// argmax under the order (value descending, index ascending) pick the experts in order.
+// argmax under the order (value descending, index ascending) pick the experts in order: each
+// lane's best, then the largest value over the wave and the lowest index holding it, both by
+// DPP row scans and scalar reads (no LDS round trips).
 __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const float* __restrict__ logits,
                                                                     int32_t n_part, int32_t n, int32_t E, int32_t k,
                                                                     int32_t* __restrict__ topk_idx,
@@ -71,15 +105,14 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const floa
         be = e;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (beats(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    // the wave's winner under the same order: the largest value, then the lowest index
+    // among the lanes holding it (lanes without a candidate hold index INT_MAX)
+    const uint32_t kmax = wave_max_u32(be < E ? order_key(bv) : 0u);
+    const int cand = (be < E && order_key(bv) == kmax) ? be : 0x7fffffff;
+    const int win = wave_min_i32(cand);
+    // the winning lane's own best is the winner: take its value (the sign of a zero included)
+    if (win < E) bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), win & 63));
+    be = win;
     // non-finite logits can leave no winner (be stays out of range); the pair is then
     // recorded with an out-of-range expert id, which binning ignores
     if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
@@ -99,20 +132,41 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const floa
   if (lane < k) topk_w[(size_t)t * k + lane] = ex / z;
 }
 
-// Inclusive scan of one value per thread across a 1024-thread workgroup.
-__device__ inline int block_inclusive_scan(int x, int* wave_tot) {
+// Inclusive scan over a wave: DPP row shifts scan each 16-lane row, then the last lane of row 0
+// is added into rows 1 and 3 and the last lane of row 1 (now rows 0-1) into rows 2 and 3.
+__device__ inline int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+struct Scan4 {
+  int a, b, c, d;
+};
+
+// Inclusive scans of four values per thread across a 1024-thread workgroup, sharing one
+// exchange of the wave totals.
+__device__ inline Scan4 block_inclusive_scan4(Scan4 x, Scan4* wave_tot) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x.a = wave_inclusive_scan(x.a);
+  x.b = wave_inclusive_scan(x.b);
+  x.c = wave_inclusive_scan(x.c);
+  x.d = wave_inclusive_scan(x.d);
   if (lane == 63) wave_tot[wv] = x;
   __syncthreads();
-  int add = 0;
-  for (int w = 0; w < wv; ++w) add += wave_tot[w];
+  for (int w = 0; w < wv; ++w) {
+    const Scan4 t = wave_tot[w];
+    x.a += t.a;
+    x.b += t.b;
+    x.c += t.c;
+    x.d += t.d;
+  }
   __syncthreads();
-  return x + add;
+  return x;
 }
 
 // Stable counting sort of the n*k pairs by expert, plus the m-tile map and the unit map
@@ -133,7 +187,7 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
   __shared__ int running[kMaxExperts];
   __shared__ int pad_shift[kMaxExperts];  // padded position - binned position, per expert
   __shared__ int wave_cnt[kExpertWaves][kMaxExperts];
-  __shared__ int wave_tot[kExpertWaves];
+  __shared__ Scan4 wave_tot[kExpertWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
 
@@ -150,10 +204,8 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
   const int nt = (c + tile_m - 1) / tile_m;
   const int nu = (c + unit_pairs - 1) / unit_pairs;
   const int pc = (c + 15) & ~15;  // the bin rounded up to whole 16-pair MFMA blocks
-  const int c_incl = block_inclusive_scan(c, wave_tot);
-  const int t_incl = block_inclusive_scan(nt, wave_tot);
-  const int u_incl = block_inclusive_scan(nu, wave_tot);
-  const int p_incl = block_inclusive_scan(pc, wave_tot);
+  const Scan4 sc = block_inclusive_scan4(Scan4{c, nt, nu, pc}, wave_tot);
+  const int c_incl = sc.a, t_incl = sc.b, u_incl = sc.c, p_incl = sc.d;
   if (tid < E) {
     const int off = c_incl - c;
     const int poff = p_incl - pc;
