@@ -557,6 +557,9 @@ using Cfg4 = ExpertCfg<8, 2, 4, 4>;
 using Cfg5 = ExpertCfg<8, 4, 2, 2>;
 using Cfg6 = ExpertCfg<12, 2, 2, 2>;
 using Cfg7 = ExpertCfg<12, 4, 2, 2>;
+// One decode per 16-pair m-tile (no sharing across m-tiles): the pages' grouped-kernel
+// schedule, kept to measure what sharing a decode across m-tiles is worth.
+using Cfg8 = ExpertCfg<16, 1, 1, 1>;
 
 // The grouped body specialised for the chunk's exact number of 16-pair row blocks.
 template <int MODE, class CFG, bool FRAG>
@@ -834,6 +837,7 @@ bool variant_info(int variant, int arm, VariantInfo& v) {
     case 5: CfgInfo<Cfg5>::get(arm, v); return true;
     case 6: CfgInfo<Cfg6>::get(arm, v); return true;
     case 7: CfgInfo<Cfg7>::get(arm, v); return true;
+    case 8: CfgInfo<Cfg8>::get(arm, v); return true;
     default: return false;
   }
 }
@@ -847,6 +851,7 @@ hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, 
     case 5: launch_cfg<Cfg5>(mode, arm, p, grid, stream); break;
     case 6: launch_cfg<Cfg6>(mode, arm, p, grid, stream); break;
     case 7: launch_cfg<Cfg7>(mode, arm, p, grid, stream); break;
+    case 8: launch_cfg<Cfg8>(mode, arm, p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

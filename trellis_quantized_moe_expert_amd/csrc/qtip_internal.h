@@ -11,8 +11,8 @@ namespace qtip {
 constexpr int kLutEntries = 65536;     // 16-bit trellis state -> one LUT entry
 // The LUT fills 128 KiB of LDS, so one expert workgroup per CU is resident; the kernel
 // variant fixes its size (16 or 8 wave64).
-// Variants 1..7 are fixed kernel configurations (see variant_info); 0 lets the plan choose.
-enum ExpertVariant { kVariantDefault = 0, kVariantCount = 8 };
+// Variants 1..8 are fixed kernel configurations (see variant_info); 0 lets the plan choose.
+enum ExpertVariant { kVariantDefault = 0, kVariantCount = 9 };
 constexpr int kExpertWaves = 16;       // waves of the binning workgroup
 constexpr int kKBlock = 128;           // inputs per K block: 4 lane groups x 32-symbol runs
 constexpr int kUnitMaxPairs = 64;      // pairs sharing one decode (4 MFMA row blocks of 16)
@@ -68,7 +68,7 @@ struct VariantInfo {
   int rows_per_task;     // output rows per wave task (rows must be a multiple of it)
   int pairs_per_decode;  // binned pairs sharing one decode of an expert's rows
 };
-// `variant` in 1..7 (the plan resolves 0).  variant_info returns false for other values.
+// `variant` in 1..8 (the plan resolves 0).  variant_info returns false for other values.
 bool variant_info(int variant, int arm, VariantInfo& v);
 hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, hipStream_t stream);
 
