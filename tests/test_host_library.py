@@ -235,9 +235,10 @@ def test_schedule_reports_what_a_forward_launches():
 
 def test_default_kernel_shapes_follow_the_measured_rules():
     # V4 layer (E=256, k=6): GEMV switches to 32-row tasks once woken*rows/32 >= 2048 wave slots;
-    # grouped picks by pairs per woken expert (1.41 at n=32, 6.0 at 256, 12.0 at 512, 24.0 at 1024).
+    # grouped picks by pairs per woken expert (1.41 at n=32, 3.15 at 128, 6.0 at 256, 12.0 at 512,
+    # 24.0 at 1024).
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
-    want = {1: (2, 2), 4: (2, 4), 8: (4, 4), 32: (1, 3), 256: (6, 3), 512: (6, 7), 1024: (4, 7)}
+    want = {1: (2, 2), 4: (2, 4), 8: (4, 4), 32: (1, 3), 128: (1, 7), 256: (6, 7), 512: (6, 7), 1024: (4, 7)}
     for n, (gu, dn) in want.items():
         s = q.qtip_moe_plan_schedule(plan, n)
         assert (s["gate_up"]["variant"], s["down"]["variant"]) == (gu, dn), n

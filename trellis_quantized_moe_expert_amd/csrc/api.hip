@@ -83,7 +83,7 @@ int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_to
   }
   const double ppe = fill_pairs_per_woken_expert(n, k, E);
   if (mode == kModeGateUp) return ppe < 4.0 ? 1 : (ppe < 20.0 ? 6 : 4);
-  return ppe < 8.0 ? 3 : 7;
+  return ppe < 3.0 ? 3 : 7;
 }
 
 // A variant whose task height does not divide `rows` falls back to the next shorter task of the
