@@ -61,10 +61,11 @@ namespace {
 // Kernel configuration when the plan's variant is 0, measured on MI355X with V4-shaped layers
 // (bench.py --sweep over variants) and chosen from host scalars only, so the choice is safe
 // during graph capture.
-//  * Grouped arm, by the closed-form pairs per woken expert: few pairs -> 16 waves of 16-row
-//    tasks keep every CU busy; a moderate number -> 12 waves of taller tasks (32 rows for the
-//    fused pass, 64 for down) feed each activation fragment to more MFMAs; many pairs (fused
-//    pass) -> 8 waves with four 16-pair blocks per decode.
+//  * Grouped arm, by the closed-form pairs per woken expert (ppe).  Fused pass: 16 waves of
+//    16-row tasks below 4 (many short tasks keep every CU busy), 12 waves of 32-row tasks below
+//    20 (each activation fragment feeds more MFMAs), 8 waves of 32-row tasks sharing a decode
+//    across four 16-pair blocks from 20.  Down pass: 16 waves of 32-row tasks below 3, 12
+//    waves of 64-row tasks with 12-byte code loads from 3.
 //  * GEMV arm, by the expected task count: 16-row tasks until there are enough 32-row tasks
 //    to give each of the 2048 wave slots of a 256-CU, 8-wave launch one.
 int kernel_arm(int32_t arm) {
