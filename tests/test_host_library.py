@@ -92,7 +92,9 @@ def test_a_window_is_reported_and_sized():
     q.qtip_moe_plan_destroy(plan)
     pinned = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_DEQUANT), "gfx950")
     assert q.qtip_moe_select_arm(pinned, 32) == q.QTIP_ARM_DEQUANT
-    assert q.qtip_moe_plan_info(pinned)["workspace_bytes"] >= ws0 + dense
+    rows = q.qtip_moe_plan_for_arch(q.make_desc(**V4, act_layout=q.QTIP_ACT_ROWS), "gfx950")
+    assert q.qtip_moe_plan_info(pinned)["workspace_bytes"] >= q.qtip_moe_plan_info(rows)["workspace_bytes"] + dense
+    q.qtip_moe_plan_destroy(rows)
     sch = q.qtip_moe_plan_schedule(pinned, 32)
     assert sch["arm"] == q.QTIP_ARM_DEQUANT and sch["gate_up"]["waves_per_workgroup"] == 16
     q.qtip_moe_plan_destroy(pinned)
@@ -294,3 +296,16 @@ def test_offset_width_limits_are_enforced():
     with pytest.raises(q.QtipError) as ei:
         q.qtip_moe_plan_for_arch(q.make_desc(256, 8, 8192, 8192, 40000), "gfx950")
     assert ei.value.status == q.QTIP_ERR_INVALID_ARG
+
+
+def test_workspace_holds_only_the_layouts_the_plan_can_take():
+    ws = lambda mt, **kw: q.qtip_moe_plan_info(q.qtip_moe_plan_for_arch(q.make_desc(256, 6, 4096, 2048, mt, **kw),
+                                                                      "gfx950"))["workspace_bytes"]
+    # a decode-width plan (1.41 pairs per woken expert at n=32) never reaches the fragment layout
+    assert ws(32) == ws(32, act_layout=q.QTIP_ACT_ROWS) < ws(32, act_layout=q.QTIP_ACT_FRAGMENTS)
+    # at 1024 tokens (24 pairs) the automatic layout packs x: padded h and x buffers are added
+    rows, auto = ws(1024, act_layout=q.QTIP_ACT_ROWS), ws(1024)
+    P, PP = 1024 * 6, ((1024 * 6 + 15 * 256 + 15) // 16) * 16
+    assert auto - rows >= (PP - P) * 2048 * 2 + PP * 4096 * 2
+    # pinning the GEMV arm leaves the grouped layouts out
+    assert ws(1024, arm_override=q.QTIP_ARM_GEMV) == rows

@@ -27,6 +27,8 @@ struct qtip_moe_plan_s {
   int32_t dequant_ratio;        // fused GEMV kept while pairs per woken expert are below this
   int32_t dequant_lo, dequant_hi;  // token counts [lo, hi) the automatic dispatch sends to the dequantize arm
   bool dense;                   // the dequantize arm may run: its dense weights are in the workspace
+  bool frag;                    // the grouped arm may use the fragment-order layout (padded space, h)
+  bool pack;                    // ... and pack x into it (its buffer is in the workspace)
   int32_t device;  // -1: created from an arch name; the current device is used at call time
 
   int32_t min_tokens_grouped;
@@ -139,7 +141,9 @@ size_t router_part_elems(const qtip_moe_desc& d, int32_t n_max) {
   return best;
 }
 
-WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, bool dense) {
+// `dense`, `frag`, `pack`: whether the plan can take the dequantize arm, the fragment layout
+// and the packed x; the buffers of what it cannot take are left out.
+WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, bool dense, bool frag, bool pack) {
   const size_t P = (size_t)n_tokens * d.top_k;
   const size_t woken_max = P < (size_t)d.num_experts ? P : (size_t)d.num_experts;
   const size_t max_tiles = P / tile_m + woken_max + 1;
@@ -155,8 +159,8 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.n_tiles = o;      o = align256(o + 4);
   L.unit_map = o;     o = align256(o + max_units * 12);
   L.n_units = o;      o = align256(o + 4);
-  const size_t PP = pad_positions(d, n_tokens);
-  L.h = o;            o = align256(o + PP * (size_t)d.inter * 2);  // row-major (P rows) or fragment order (PP)
+  const size_t PP = frag ? pad_positions(d, n_tokens) : 0;
+  L.h = o;            o = align256(o + (frag ? PP : P) * (size_t)d.inter * 2);  // rows (P) or fragment order (PP)
   L.y = o;            o = align256(o + P * (size_t)d.hidden * 4);
   L.router_part = o;  o = align256(o + router_part_elems(d, n_tokens) * 4);
   // dequantize arm: every expert's dense bf16 weights (only when the plan can take that arm)
@@ -167,7 +171,7 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.padded_pair = o;  o = align256(o + PP * 4);
   L.unit_pad = o;     o = align256(o + max_units * 4);
   L.n_pad = o;        o = align256(o + 4);
-  L.xs = o;           o = align256(o + PP * (size_t)d.hidden * 2);
+  L.xs = o;           o = align256(o + (pack ? PP * (size_t)d.hidden * 2 : 0));
   L.total = o;
   return L;
 }
@@ -373,7 +377,14 @@ qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc, const char* gcn_ar
     delete p;
     return fail(QTIP_ERR_INVALID_ARG, "the dequantize arm needs hidden * inter below 2^31 elements");
   }
-  p->ws_bytes = ws_layout(p->d, tm, desc->max_tokens, p->dense).total;
+  // Pairs per woken expert never decrease with n, so the fragment layout and the packing are
+  // possible for some n <= max_tokens exactly when they are at max_tokens.
+  const bool grouped_ok = desc->arm_override == QTIP_ARM_AUTO || desc->arm_override == QTIP_ARM_GROUPED;
+  const double ppe_max = fill_pairs_per_woken_expert(desc->max_tokens, desc->top_k, desc->num_experts);
+  p->frag = grouped_ok && desc->act_layout != QTIP_ACT_ROWS &&
+            (desc->act_layout == QTIP_ACT_FRAGMENTS || ppe_max >= kFragMinPairs);
+  p->pack = p->frag && (desc->act_layout == QTIP_ACT_FRAGMENTS || ppe_max >= kPackMinPairs);
+  p->ws_bytes = ws_layout(p->d, tm, desc->max_tokens, p->dense, p->frag, p->pack).total;
   *out = p;
   return QTIP_OK;
 }
@@ -555,7 +566,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   const int32_t arm = qtip_moe_select_arm(plan, n_tokens);
   const int karm = kernel_arm(arm);
   if (karm == kArmDense && !plan->dense) return fail(QTIP_ERR_INVALID_CONFIG, "the plan has no dequantize workspace");
-  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens, plan->dense);
+  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens, plan->dense, plan->frag, plan->pack);
   char* ws = reinterpret_cast<char*>(workspace);
   int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
   float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
@@ -590,7 +601,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   // down pass) from kFragMinPairs pairs per woken expert, for x too (an extra packing pass)
   // from kPackMinPairs; gathered rows below.
   const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
-  const bool frag = karm == kArmGrouped && d.act_layout != QTIP_ACT_ROWS &&
+  const bool frag = plan->frag && karm == kArmGrouped &&
                     (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kFragMinPairs);
   int32_t* padded_pair = reinterpret_cast<int32_t*>(ws + L.padded_pair);
   int32_t* unit_pad = reinterpret_cast<int32_t*>(ws + L.unit_pad);
@@ -602,7 +613,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
                  frag ? n_pad : nullptr, st);
   if (e != hipSuccess) return hip_fail(e, "bin launch");
   plan->stats.route_launches += 2;
-  const bool pack = frag && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
+  const bool pack = frag && plan->pack && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
   if (pack) {
     e = launch_pack_act(reinterpret_cast<const uint16_t*>(x_bf16), padded_pair, n_pad, d.top_k, d.hidden, pp_max, xs,
                         st);
@@ -761,7 +772,7 @@ qtip_status qtip_moe_router_logits(qtip_moe_plan_t plan, const void* x_bf16, con
   if (s != QTIP_OK) return s;
   const qtip_moe_desc& d = plan->d;
   const int32_t S = router_split(n_tokens, d.num_experts, d.hidden);
-  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens, plan->dense);
+  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens, plan->dense, plan->frag, plan->pack);
   float* part = S == 1 ? logits : reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.router_part);
   hipError_t e = launch_router_gemm(reinterpret_cast<const uint16_t*>(x_bf16),
                                     reinterpret_cast<const uint16_t*>(w_router_bf16), n_tokens, d.num_experts,
