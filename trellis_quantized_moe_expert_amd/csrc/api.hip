@@ -8,6 +8,7 @@
 // witness declines under graph capture and caches only a successful answer.  The variant
 // knob follows the prefill page (PR #196): an unknown value warns and keeps the default.
 #include <atomic>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -118,7 +119,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, h, y, router_part,
-      dense_gate, dense_up, dense_down, padded_pair, unit_pad, n_pad, xs, total;
+      dense_gate, dense_up, dense_down, padded_pair, unit_pad, n_pad, xs, bounds_gu, bounds_dn, total;
 };
 
 // Padded positions (every woken expert's bin rounded up to 16 pairs) for n tokens, a multiple of 16.
@@ -172,6 +173,8 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.unit_pad = o;     o = align256(o + max_units * 4);
   L.n_pad = o;        o = align256(o + 4);
   L.xs = o;           o = align256(o + (pack ? PP * (size_t)d.hidden * 2 : 0));
+  L.bounds_gu = o;    o = align256(o + (kMaxXcds + 1) * 4);
+  L.bounds_dn = o;    o = align256(o + (kMaxXcds + 1) * 4);
   L.total = o;
   return L;
 }
@@ -244,7 +247,8 @@ qtip_status ensure_device(qtip_moe_plan_t plan, hipStream_t stream, int* dev_out
 // treated as one XCD (only the task order, not correctness, depends on this).
 int xcd_count(int dev) {
   const int cus = g_cu_count[dev].load(std::memory_order_acquire);
-  return (cus >= 64 && cus % 32 == 0) ? cus / 32 : 1;
+  const int nx = (cus >= 64 && cus % 32 == 0) ? cus / 32 : 1;
+  return nx <= kMaxXcds ? nx : 1;
 }
 
 int persistent_grid(int dev, size_t max_tasks, int waves) {
@@ -481,7 +485,7 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
   if (e != hipSuccess) return hip_fail(e, "route_topk launch");
   plan->stats.route_launches++;
   e = launch_bin(topk_idx, n_tokens * d.top_k, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets,
-                 sorted_pair, tile_map, n_tiles, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+                 sorted_pair, tile_map, n_tiles, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st);
   if (e != hipSuccess) return hip_fail(e, "bin launch");
   plan->stats.route_launches++;
   return QTIP_OK;
@@ -608,9 +612,24 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   int32_t* n_pad = reinterpret_cast<int32_t*>(ws + L.n_pad);
   uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
   const int32_t pp_max = (int32_t)pad_positions(d, n_tokens);
+  // kernel configurations of the two passes (the binning kernel splits their tasks over XCDs
+  // by the decodes their pairs per decode imply)
+  const int kv_gu = fit_variant(resolve_variant(plan, karm, kModeGateUp, n_tokens), karm, d.inter);
+  const int kv_dn = fit_variant(resolve_variant(plan, karm, kModeSingle, n_tokens), karm, d.hidden);
+  VariantInfo vi_gu{}, vi_dn{};
+  variant_info(kv_gu, karm, vi_gu);
+  variant_info(kv_dn, karm, vi_dn);
+  const size_t max_units = max_units_for(d, n_tokens);
+  const int grid_gu = persistent_grid(dev, max_units * (d.inter / vi_gu.rows_per_task), vi_gu.waves);
+  const int grid_dn = persistent_grid(dev, max_units * (d.hidden / vi_dn.rows_per_task), vi_dn.waves);
+  const int nx = xcd_count(dev);
+  int32_t* bounds_gu = reinterpret_cast<int32_t*>(ws + L.bounds_gu);
+  int32_t* bounds_dn = reinterpret_cast<int32_t*>(ws + L.bounds_dn);
+  const XcdSplit split_gu{grid_gu, nx, d.inter / vi_gu.rows_per_task, vi_gu.pairs_per_decode, bounds_gu};
+  const XcdSplit split_dn{grid_dn, nx, d.hidden / vi_dn.rows_per_task, vi_dn.pairs_per_decode, bounds_dn};
   e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets, sorted_pair, tile_map,
                  n_tiles, unit_map, n_units, frag ? padded_pair : nullptr, frag ? unit_pad : nullptr,
-                 frag ? n_pad : nullptr, st);
+                 frag ? n_pad : nullptr, &split_gu, &split_dn, st);
   if (e != hipSuccess) return hip_fail(e, "bin launch");
   plan->stats.route_launches += 2;
   const bool pack = frag && plan->pack && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
@@ -652,7 +671,6 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     plan->stats.dequant_launches += 2;
   }
 
-  const size_t max_units = max_units_for(d, n_tokens);
   ExpertParams gu{};
   gu.dense0 = dense_gate;
   gu.dense1 = dense_up;
@@ -682,10 +700,8 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     gu.act = xs;
     gu.act_frag = 1;
   }
-  const int kv_gu = fit_variant(resolve_variant(plan, karm, kModeGateUp, n_tokens), karm, d.inter);
-  VariantInfo vi{};
-  variant_info(kv_gu, karm, vi);
-  e = launch_expert(kModeGateUp, karm, kv_gu, gu, persistent_grid(dev, max_units * (d.inter / vi.rows_per_task), vi.waves), st);
+  gu.xcd_bounds = bounds_gu;
+  e = launch_expert(kModeGateUp, karm, kv_gu, gu, grid_gu, st);
   if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
   if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
 
@@ -712,9 +728,8 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     dn.act_frag = 1;
     dn.n_pad_max = pp_max;
   }
-  const int kv_dn = fit_variant(resolve_variant(plan, karm, kModeSingle, n_tokens), karm, d.hidden);
-  variant_info(kv_dn, karm, vi);
-  e = launch_expert(kModeSingle, karm, kv_dn, dn, persistent_grid(dev, max_units * (d.hidden / vi.rows_per_task), vi.waves), st);
+  dn.xcd_bounds = bounds_dn;
+  e = launch_expert(kModeSingle, karm, kv_dn, dn, grid_dn, st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
   if (karm == kArmGrouped) plan->stats.grouped_launches += 2;

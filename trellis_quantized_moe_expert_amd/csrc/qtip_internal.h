@@ -21,6 +21,7 @@ constexpr int kBinThreads = 1024;      // binning runs in one workgroup (16 wave
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kWitnessValue = 0x950950;
+constexpr int kMaxXcds = 64;           // XCDs a launch's task order may be split over
 constexpr int kRouterMaxWaves = 8;        // waves of a router-GEMM workgroup (they split its input chunk)
 constexpr int kRouterTargetGroups = 256;  // router-GEMM workgroups wanted: one per CU
 constexpr int kRouterMaxSplit = 4;        // input chunks (partial sums) per logit at most
@@ -55,6 +56,8 @@ struct ExpertParams {
                                 // fragment order over padded positions (dense_fragment_offset, rows = padded
                                 // positions), the order the down pass reads it in.
   int32_t act_frag;             // with unit_pad: the activations (act) are in that fragment order as well
+  const int32_t* xcd_bounds;    // task range of each XCD's share for this launch (n_xcd + 1 entries, split by
+                                // decodes; see XcdSplit), or NULL: shares then split tasks by count
   int32_t n_pad_max;            // padded positions the fragment-order buffers hold (with unit_pad)
   const uint16_t* dense0;       // dequantize arm: [E] x rows x cols bf16 weights in fragment order (gate, or the single matrix)
   const uint16_t* dense1;       // dequantize arm: the same for the up weights (fused pass only)
@@ -111,14 +114,29 @@ hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w, int32_t n, i
                               int32_t n_xcd, float* part, hipStream_t stream);
 hipError_t launch_router_reduce(const float* part, int32_t S, int64_t count, float* logits, hipStream_t stream);
 
+// How one expert pass's launch splits its tasks (unit x row block, unit-major) over XCDs:
+// workgroup b runs on XCD b % n_xcd, so XCD x holds `cus` = G/n_xcd (+1 for x < G % n_xcd)
+// workgroups, and its share holds that fraction of the pass's decodes (a unit of len pairs
+// decodes its rows ceil(len / pairs_per_decode) times), so XCDs holding the busiest experts'
+// units get fewer tasks.
+struct XcdSplit {
+  int32_t grid;            // G, the launch's workgroups
+  int32_t n_xcd;
+  int32_t row_blocks;      // tasks per unit (rows / rows per task)
+  int32_t pairs_per_decode;
+  int32_t* bounds;         // out: n_xcd + 1 task indices
+};
+
 // Binning.  unit_map/n_units may be NULL (no units); padded_pair/unit_pad/n_pad may be NULL (no
-// padded position space).  The padded space rounds every expert's bin up to a multiple of 16
-// pairs: padded_pair[pp] is the pair at padded position pp or -1 in the padding, unit_pad[u]
-// the padded start of unit u (a multiple of 16), *n_pad the padded total.
+// padded position space); split_gu/split_dn may be NULL (no XCD bounds; they need the units).
+// The padded space rounds every expert's bin up to a multiple of 16 pairs: padded_pair[pp] is the
+// pair at padded position pp or -1 in the padding, unit_pad[u] the padded start of unit u (a
+// multiple of 16), *n_pad the padded total.
 hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
                       int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map,
                       int32_t* n_tiles, int32_t* unit_map, int32_t* n_units, int32_t* padded_pair,
-                      int32_t* unit_pad, int32_t* n_pad, hipStream_t stream);
+                      int32_t* unit_pad, int32_t* n_pad, const XcdSplit* split_gu, const XcdSplit* split_dn,
+                      hipStream_t stream);
 
 // Gathers the activation row of every padded position (token = pair / k; padding untouched)
 // into fragment order: xs holds n_pad_max padded rows of H bf16 values.

@@ -144,29 +144,70 @@ __device__ inline int wave_inclusive_scan(int x) {
   return x;
 }
 
-struct Scan4 {
-  int a, b, c, d;
+// Values scanned together across the binning workgroup: a pair count, m-tiles, units and
+// padded pairs per expert, and the expert's decodes in the two expert passes.
+struct Scan6 {
+  int v[6];
 };
 
-// Inclusive scans of four values per thread across a 1024-thread workgroup, sharing one
-// exchange of the wave totals.
-__device__ inline Scan4 block_inclusive_scan4(Scan4 x, Scan4* wave_tot) {
+// Inclusive scans of six values per thread across a 1024-thread workgroup, sharing one
+// exchange of the wave totals (left in wave_tot: their sum is the workgroup total).
+__device__ inline Scan6 block_inclusive_scan6(Scan6 x, Scan6* wave_tot) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  x.a = wave_inclusive_scan(x.a);
-  x.b = wave_inclusive_scan(x.b);
-  x.c = wave_inclusive_scan(x.c);
-  x.d = wave_inclusive_scan(x.d);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) x.v[i] = wave_inclusive_scan(x.v[i]);
   if (lane == 63) wave_tot[wv] = x;
   __syncthreads();
   for (int w = 0; w < wv; ++w) {
-    const Scan4 t = wave_tot[w];
-    x.a += t.a;
-    x.b += t.b;
-    x.c += t.c;
-    x.d += t.d;
+    const Scan6 t = wave_tot[w];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) x.v[i] += t.v[i];
   }
   __syncthreads();
   return x;
+}
+
+// Decodes of one pass for an expert's c pairs: nu units (nu - 1 full ones of unit_pairs pairs
+// and a last one), each decoding its rows once per chunk of pairs_per_decode pairs.
+__device__ inline int expert_decodes(int c, int nu, int unit_pairs, int ppd) {
+  if (nu == 0) return 0;
+  const int last = c - (nu - 1) * unit_pairs;
+  return (nu - 1) * ((unit_pairs + ppd - 1) / ppd) + (last + ppd - 1) / ppd;
+}
+
+// Start task of XCD x's share in one expert pass (x = n_xcd: the end).  The share holds a
+// fraction of the pass's decodes in proportion to the XCD's workgroups.  Positions count
+// decodes times row blocks (each decode spread evenly over its unit's row-block tasks): the
+// boundary sits at pos = floor(D * nb * before_x / G) (D: the pass's decodes, cum: their
+// inclusive prefix over experts, cum_units: that of units), and a binary search finds the
+// expert holding it.  The task index is then rounded to a multiple of the XCD's workgroup
+// count Q = G / n_xcd when Q divides the row blocks per unit: the XCD's CUs take its tasks in
+// turn, so every CU then gets the same row blocks of the same units, the same work.  With
+// equal decodes per unit this is the split by task count.
+__device__ inline int share_bound(const XcdSplit& sp, int x, const int* cum, const int* cum_units, const int* cnt,
+                                  int E, int unit_pairs) {
+  const int G = sp.grid, nx = sp.n_xcd, nb = sp.row_blocks, ppd = sp.pairs_per_decode;
+  const int total = cum_units[E - 1] * nb;
+  const int before = x * (G / nx) + min(x, G % nx);
+  const int D = cum[E - 1];
+  if (x >= nx || before >= G || D == 0) return total;
+  const long pos = (long)D * nb * before / G;
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((long)cum[mid] * nb > pos) hi = mid;
+    else lo = mid + 1;
+  }
+  const int c = cnt[lo];
+  const int nu = (c + unit_pairs - 1) / unit_pairs;
+  const long off = pos - (long)(cum[lo] - expert_decodes(c, nu, unit_pairs, ppd)) * nb;
+  const int full = (unit_pairs + ppd - 1) / ppd;
+  const int q = (int)min(off / ((long)full * nb), (long)(nu - 1));
+  const int uc = q < nu - 1 ? full : (c - (nu - 1) * unit_pairs + ppd - 1) / ppd;
+  long t = (long)(cum_units[lo] - nu + q) * nb + (off - (long)q * full * nb) / uc;
+  const int Q = G / nx;
+  if (Q > 1 && nb % Q == 0) t = (t + Q / 2) / Q * Q;
+  return (int)min(t, (long)total);
 }
 
 // Stable counting sort of the n*k pairs by expert, plus the m-tile map and the unit map
@@ -182,12 +223,15 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ n_units,
                                                           int32_t* __restrict__ padded_pair,
                                                           int32_t* __restrict__ unit_pad,
-                                                          int32_t* __restrict__ n_pad) {
+                                                          int32_t* __restrict__ n_pad,
+                                                          XcdSplit split_gu, XcdSplit split_dn) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int running[kMaxExperts];
   __shared__ int pad_shift[kMaxExperts];  // padded position - binned position, per expert
   __shared__ int wave_cnt[kExpertWaves][kMaxExperts];
-  __shared__ Scan4 wave_tot[kExpertWaves];
+  __shared__ Scan6 wave_tot[kExpertWaves];
+  __shared__ int cum_dec[2][kMaxExperts];  // inclusive prefix of the passes' decodes over experts
+  __shared__ int cum_units[kMaxExperts];   // inclusive prefix of units over experts
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
 
@@ -204,14 +248,21 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
   const int nt = (c + tile_m - 1) / tile_m;
   const int nu = (c + unit_pairs - 1) / unit_pairs;
   const int pc = (c + 15) & ~15;  // the bin rounded up to whole 16-pair MFMA blocks
-  const Scan4 sc = block_inclusive_scan4(Scan4{c, nt, nu, pc}, wave_tot);
-  const int c_incl = sc.a, t_incl = sc.b, u_incl = sc.c, p_incl = sc.d;
+  // decodes of the two expert passes, scanned with the rest for the XCD shares
+  const bool split = unit_map && split_gu.bounds && split_dn.bounds;
+  const int dg = split ? expert_decodes(c, nu, unit_pairs, split_gu.pairs_per_decode) : 0;
+  const int dd = split ? expert_decodes(c, nu, unit_pairs, split_dn.pairs_per_decode) : 0;
+  const Scan6 sc = block_inclusive_scan6(Scan6{{c, nt, nu, pc, dg, dd}}, wave_tot);
+  const int c_incl = sc.v[0], t_incl = sc.v[1], u_incl = sc.v[2], p_incl = sc.v[3];
   if (tid < E) {
     const int off = c_incl - c;
     const int poff = p_incl - pc;
     counts[tid] = c;
     offsets[tid] = off;
     running[tid] = off;
+    cum_dec[0][tid] = sc.v[4];
+    cum_dec[1][tid] = sc.v[5];
+    cum_units[tid] = u_incl;
     pad_shift[tid] = poff - off;
     if (padded_pair)
       for (int q = c; q < pc; ++q) padded_pair[poff + q] = -1;
@@ -236,6 +287,11 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
     if (n_pad) *n_pad = p_incl;
   }
   __syncthreads();
+  if (split && tid < 2 * (kMaxXcds + 1)) {  // the XCD share boundaries of both passes
+    const int pass = tid / (kMaxXcds + 1), x = tid % (kMaxXcds + 1);
+    const XcdSplit& sp = pass ? split_dn : split_gu;
+    if (x <= sp.n_xcd) sp.bounds[x] = share_bound(sp, x, cum_dec[pass], cum_units, cnt, E, unit_pairs);
+  }
 
   // stable scatter, 1024 pairs per round: rank inside the wave from a bitwise match of
   // the expert id, then the counts of earlier waves and earlier rounds
@@ -286,10 +342,19 @@ hipError_t launch_route_topk(const float* logits, int32_t n_part, int32_t n, int
 hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
                       int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
                       int32_t* unit_map, int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
-                      hipStream_t stream) {
+                      const XcdSplit* split_gu, const XcdSplit* split_dn, hipStream_t stream) {
+  XcdSplit sg{}, sd{};
+  if (split_gu && split_dn) {
+    for (const XcdSplit* sp : {split_gu, split_dn})
+      if (!sp->bounds || sp->grid < 1 || sp->n_xcd < 1 || sp->n_xcd > kMaxXcds || sp->row_blocks < 1 ||
+          sp->pairs_per_decode < 1)
+        return hipErrorInvalidValue;
+    sg = *split_gu;
+    sd = *split_dn;
+  }
   hipLaunchKernelGGL(bin_kernel, dim3(1), dim3(kBinThreads), 0, stream, topk_idx, n_pairs, E, tile_m, unit_pairs,
                      counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, padded_pair, unit_pad,
-                     n_pad);
+                     n_pad, sg, sd);
   return hipGetLastError();
 }
 
