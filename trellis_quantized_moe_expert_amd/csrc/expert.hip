@@ -53,17 +53,31 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
 __device__ inline float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 // Stage the fp16 LUT into LDS as bf16 (8 entries per 16-byte load).
+template <int THREADS>
 __device__ inline void fill_lut(uint16_t* lut_s, const uint16_t* __restrict__ lut_g) {
+  // every 16-byte load of a thread is issued before the first conversion, so the fill waits for
+  // one memory round trip instead of one per load
+  constexpr int kVec = kLutEntries / 8;
+  constexpr int kIter = (kVec + THREADS - 1) / THREADS;
   const uint4* src = reinterpret_cast<const uint4*>(lut_g);
   uint4* dst = reinterpret_cast<uint4*>(lut_s);
-  for (int i = threadIdx.x; i < kLutEntries / 8; i += blockDim.x) {
-    const uint4 v = src[i];
-    uint4 o;
-    o.x = f16_to_bf16_bits(v.x & 0xFFFFu) | (f16_to_bf16_bits(v.x >> 16) << 16);
-    o.y = f16_to_bf16_bits(v.y & 0xFFFFu) | (f16_to_bf16_bits(v.y >> 16) << 16);
-    o.z = f16_to_bf16_bits(v.z & 0xFFFFu) | (f16_to_bf16_bits(v.z >> 16) << 16);
-    o.w = f16_to_bf16_bits(v.w & 0xFFFFu) | (f16_to_bf16_bits(v.w >> 16) << 16);
-    dst[i] = o;
+  uint4 v[kIter];
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int i = (int)threadIdx.x + it * THREADS;
+    if (kVec % THREADS == 0 || i < kVec) v[it] = src[i];
+  }
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int i = (int)threadIdx.x + it * THREADS;
+    if (kVec % THREADS == 0 || i < kVec) {
+      uint4 o;
+      o.x = f16_to_bf16_bits(v[it].x & 0xFFFFu) | (f16_to_bf16_bits(v[it].x >> 16) << 16);
+      o.y = f16_to_bf16_bits(v[it].y & 0xFFFFu) | (f16_to_bf16_bits(v[it].y >> 16) << 16);
+      o.z = f16_to_bf16_bits(v[it].z & 0xFFFFu) | (f16_to_bf16_bits(v[it].z >> 16) << 16);
+      o.w = f16_to_bf16_bits(v[it].w & 0xFFFFu) | (f16_to_bf16_bits(v[it].w >> 16) << 16);
+      dst[i] = o;
+    }
   }
   __syncthreads();
 }
@@ -652,7 +666,7 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
     expert_tasks<MODE, ARM, CFG, false>(p, nullptr);
   } else {
     __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
-    fill_lut(lut_s, p.lut);
+    fill_lut<CFG::kWaves * 64>(lut_s, p.lut);
     expert_tasks<MODE, ARM, CFG, FRAG>(p, lut_s);
   }
 }
@@ -663,7 +677,7 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
 // The next block's codes are requested before the current block is decoded.
 __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantParams q) {
   __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
-  fill_lut(lut_s, q.lut);
+  fill_lut<kDequantWaves * 64>(lut_s, q.lut);
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
