@@ -66,6 +66,20 @@ def test_route_bitexact_edge_shapes(n, E, k):
     compare(rng.standard_normal((n, E)).astype(np.float32), E, k)
 
 
+@pytest.mark.parametrize("n,E,k", [(16, 256, 6), (17, 256, 6), (16, 256, 20), (15, 200, 32), (16, 1, 1),
+                                   (14, 17, 16), (16, 1024, 8), (17, 1024, 8), (16, 300, 4), (12, 512, 3)])
+def test_route_bitexact_small_batches_with_ties(n, E, k):
+    # batches of up to 16 tokens are routed and binned by one workgroup (a token per wave),
+    # larger ones by the two launches; the shapes straddle that limit and each logits-per-lane
+    # instantiation (E up to 256, 512, 1024)
+    rng = np.random.default_rng(7 * n + E)
+    logits = np.round(rng.standard_normal((n, E)) * 1.5).astype(np.float32)   # heavy ties
+    logits[0] = 0.0
+    logits[-1, ::3] = -0.0
+    say(f"route small batch n={n} E={E} k={k}")
+    compare(logits, E, k)
+
+
 def test_route_skewed_hot_expert():
     rng = np.random.default_rng(9)
     logits = rng.standard_normal((1500, 32)).astype(np.float32)

@@ -481,7 +481,16 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
   qtip_status s = ensure_device(plan, st, &dev);
   if (s != QTIP_OK) return s;
   const qtip_moe_desc& d = plan->d;
-  hipError_t e = launch_route_topk(logits, 1, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
+  hipError_t e;
+  if (n_tokens <= kFusedRouteMaxTokens) {  // the same kernels as the forward's routing
+    e = launch_route_bin(logits, 1, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, plan->tile_m, kUnitMaxPairs,
+                         counts, offsets, sorted_pair, tile_map, n_tiles, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "route/bin launch");
+    plan->stats.route_launches++;
+    return QTIP_OK;
+  }
+  e = launch_route_topk(logits, 1, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
   if (e != hipSuccess) return hip_fail(e, "route_topk launch");
   plan->stats.route_launches++;
   e = launch_bin(topk_idx, n_tokens * d.top_k, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets,
@@ -598,9 +607,6 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     plan->stats.router_launches++;
     lg = part;
   }
-  e = launch_route_topk(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
-  if (e != hipSuccess) return hip_fail(e, "route_topk launch");
-  if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
   // The grouped arm's activation layout: fragment order over padded positions for h (and the
   // down pass) from kFragMinPairs pairs per woken expert, for x too (an extra packing pass)
   // from kPackMinPairs; gathered rows below.
@@ -627,11 +633,25 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   int32_t* bounds_dn = reinterpret_cast<int32_t*>(ws + L.bounds_dn);
   const XcdSplit split_gu{grid_gu, nx, d.inter / vi_gu.rows_per_task, vi_gu.pairs_per_decode, bounds_gu};
   const XcdSplit split_dn{grid_dn, nx, d.hidden / vi_dn.rows_per_task, vi_dn.pairs_per_decode, bounds_dn};
-  e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets, sorted_pair, tile_map,
-                 n_tiles, unit_map, n_units, frag ? padded_pair : nullptr, frag ? unit_pad : nullptr,
-                 frag ? n_pad : nullptr, &split_gu, &split_dn, st);
-  if (e != hipSuccess) return hip_fail(e, "bin launch");
-  plan->stats.route_launches += 2;
+  if (n_tokens <= kFusedRouteMaxTokens) {
+    // one workgroup routes and bins a small batch (the "route" stage then holds both)
+    e = launch_route_bin(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, plan->tile_m, kUnitMaxPairs,
+                         counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units,
+                         frag ? padded_pair : nullptr, frag ? unit_pad : nullptr, frag ? n_pad : nullptr, &split_gu,
+                         &split_dn, st);
+    if (e != hipSuccess) return hip_fail(e, "route/bin launch");
+    if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
+    plan->stats.route_launches += 1;
+  } else {
+    e = launch_route_topk(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
+    if (e != hipSuccess) return hip_fail(e, "route_topk launch");
+    if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
+    e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets, sorted_pair, tile_map,
+                   n_tiles, unit_map, n_units, frag ? padded_pair : nullptr, frag ? unit_pad : nullptr,
+                   frag ? n_pad : nullptr, &split_gu, &split_dn, st);
+    if (e != hipSuccess) return hip_fail(e, "bin launch");
+    plan->stats.route_launches += 2;
+  }
   const bool pack = frag && plan->pack && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
   if (pack) {
     e = launch_pack_act(reinterpret_cast<const uint16_t*>(x_bf16), padded_pair, n_pad, d.top_k, d.hidden, pp_max, xs,

@@ -138,6 +138,19 @@ hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32
                       int32_t* unit_pad, int32_t* n_pad, const XcdSplit* split_gu, const XcdSplit* split_dn,
                       hipStream_t stream);
 
+// Batches of at most this many tokens (one per wave of the binning workgroup) are routed and
+// binned by one workgroup (launch_route_bin); measured, a second token per wave already costs
+// more than the separate launches save.
+constexpr int kFusedRouteMaxTokens = kExpertWaves;
+
+// Routing (launch_route_topk) and binning (launch_bin) of n <= kFusedRouteMaxTokens tokens by
+// one workgroup, with the same outputs.
+hipError_t launch_route_bin(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
+                            float* topk_w, int32_t tile_m, int32_t unit_pairs, int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles, int32_t* unit_map,
+                            int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
+                            const XcdSplit* split_gu, const XcdSplit* split_dn, hipStream_t stream);
+
 // Gathers the activation row of every padded position (token = pair / k; padding untouched)
 // into fragment order: xs holds n_pad_max padded rows of H bf16 values.
 hipError_t launch_pack_act(const uint16_t* x, const int32_t* padded_pair, const int32_t* n_pad, int32_t k,

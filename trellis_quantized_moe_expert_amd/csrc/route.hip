@@ -53,52 +53,49 @@ __device__ inline int wave_min_i32(int v) {
   return min(min(a, b), min(c, d));
 }
 
-// One wave per token.  Each lane holds up to 16 logits (E <= 1024); k rounds of a wave-wide
-// argmax under the order (value descending, index ascending) pick the experts in order: each
-// lane's best, then the largest value over the wave and the lowest index holding it, both by
-// DPP row scans and scalar reads (no LDS round trips).
-__global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const float* __restrict__ logits,
-                                                                    int32_t n_part, int32_t n, int32_t E, int32_t k,
-                                                                    int32_t* __restrict__ topk_idx,
-                                                                    float* __restrict__ topk_w) {
-  __shared__ float sel[kRouteWaves][kMaxTopK];
+// Top-k and softmax of token t by one wave.  Each lane holds Q logits (E <= 64 Q); k rounds
+// of a wave-wide argmax under the order (value descending, index ascending) pick the experts
+// in order: each lane's best, then the largest value over the wave and the lowest index
+// holding it, both by DPP row scans and scalar reads (no LDS round trips).
+template <int Q>
+__device__ __attribute__((always_inline)) inline void route_token(const float* __restrict__ logits, int32_t n_part,
+                                                                  int32_t n, int32_t E, int32_t k, int t,
+                                                                  int32_t* __restrict__ topk_idx,
+                                                                  float* __restrict__ topk_w) {
+  __shared__ float sel_all[kExpertWaves][kMaxTopK];  // the k selected logits, per wave
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int t = blockIdx.x * kRouteWaves + wv;
-  if (t >= n) return;  // whole wave leaves together; no barrier follows
+  float* sel = sel_all[threadIdx.x >> 6];
   const float* row = logits + (size_t)t * E;
   const size_t part_stride = (size_t)n * (size_t)E;
-  float v[16];
+  float v[Q];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const int e = lane + 64 * q;
     v[q] = (e < E) ? row[e] : 0.0f;
   }
   // partial sums of the router GEMM's K chunks, added in ascending chunk order; the loads of
   // up to 4 chunks are issued before their additions so their latencies overlap
-  if (n_part > 1) {
-    for (int s = 1; s < n_part; s += 4) {
-      float t[4][16];
+  for (int s = 1; s < n_part; s += 4) {
+    float t4[4][Q];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int e = lane + 64 * q;
-          t[i][q] = (s + i < n_part && e < E) ? row[(size_t)(s + i) * part_stride + e] : 0.0f;
-        }
+      for (int q = 0; q < Q; ++q) {
+        const int e = lane + 64 * q;
+        t4[c][q] = (s + c < n_part && e < E) ? row[(size_t)(s + c) * part_stride + e] : 0.0f;
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (s + i < n_part) v[q] += t[i][q];
-    }
+      for (int q = 0; q < Q; ++q)
+        if (s + c < n_part) v[q] += t4[c][q];
   }
   uint32_t taken = 0;
   for (int jj = 0; jj < k; ++jj) {
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < Q; ++q) {
       const int e = lane + 64 * q;
       if (e < E && !((taken >> q) & 1u) && beats(v[q], e, bv, be)) {
         bv = v[q];
@@ -118,18 +115,29 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const floa
     if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
     if (lane == 0) {
       topk_idx[(size_t)t * k + jj] = be;
-      sel[wv][jj] = bv;
+      sel[jj] = bv;
     }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   // softmax over the k selected logits, max subtracted first (sel[0] is the largest)
   float ex = 0.0f;
-  if (lane < k) ex = expf(sel[wv][lane] - sel[wv][0]);
+  if (lane < k) ex = expf(sel[lane] - sel[0]);
   float z = ex;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
   if (lane < k) topk_w[(size_t)t * k + lane] = ex / z;
+}
+
+// One wave per token.
+template <int Q>
+__global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const float* __restrict__ logits,
+                                                                    int32_t n_part, int32_t n, int32_t E, int32_t k,
+                                                                    int32_t* __restrict__ topk_idx,
+                                                                    float* __restrict__ topk_w) {
+  const int t = blockIdx.x * kRouteWaves + (int)(threadIdx.x >> 6);
+  if (t >= n) return;  // whole wave leaves together; no barrier follows
+  route_token<Q>(logits, n_part, n, E, k, t, topk_idx, topk_w);
 }
 
 // Inclusive scan over a wave: DPP row shifts scan each 16-lane row, then the last lane of row 0
@@ -213,18 +221,14 @@ __device__ inline int share_bound(const XcdSplit& sp, int x, const int* cum, con
 // Stable counting sort of the n*k pairs by expert, plus the m-tile map and the unit map
 // (units = runs of up to unit_pairs pairs of one expert; each unit is one decode of the
 // expert's weights in the expert kernels; unit_map/n_units may be NULL to skip them).
-// One workgroup of 1024 threads.
-__global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restrict__ topk_idx, int32_t P, int32_t E,
-                                                          int32_t tile_m, int32_t unit_pairs,
-                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ sorted_pair,
-                                                          int32_t* __restrict__ tile_map, int32_t* __restrict__ n_tiles,
-                                                          int32_t* __restrict__ unit_map,
-                                                          int32_t* __restrict__ n_units,
-                                                          int32_t* __restrict__ padded_pair,
-                                                          int32_t* __restrict__ unit_pad,
-                                                          int32_t* __restrict__ n_pad,
-                                                          XcdSplit split_gu, XcdSplit split_dn) {
+// Run by one workgroup of 1024 threads.
+__device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* __restrict__ topk_idx, int32_t P, int32_t E, int32_t tile_m,
+                                 int32_t unit_pairs, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                 int32_t* __restrict__ sorted_pair, int32_t* __restrict__ tile_map,
+                                 int32_t* __restrict__ n_tiles, int32_t* __restrict__ unit_map,
+                                 int32_t* __restrict__ n_units, int32_t* __restrict__ padded_pair,
+                                 int32_t* __restrict__ unit_pad, int32_t* __restrict__ n_pad, const XcdSplit& split_gu,
+                                 const XcdSplit& split_dn) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int running[kMaxExperts];
   __shared__ int pad_shift[kMaxExperts];  // padded position - binned position, per expert
@@ -329,21 +333,58 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
   }
 }
 
+__global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restrict__ topk_idx, int32_t P, int32_t E,
+                                                          int32_t tile_m, int32_t unit_pairs, int32_t* counts,
+                                                          int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map,
+                                                          int32_t* n_tiles, int32_t* unit_map, int32_t* n_units,
+                                                          int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
+                                                          XcdSplit split_gu, XcdSplit split_dn) {
+  bin_pairs(topk_idx, P, E, tile_m, unit_pairs, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units,
+            padded_pair, unit_pad, n_pad, split_gu, split_dn);
+}
+
+// Routing and binning of a small batch (n <= kFusedRouteMaxTokens) in one workgroup: its waves
+// take a token each, then, once every pair is routed (the barrier makes the workgroup's stores
+// of topk_idx visible to all of it), the same workgroup bins them.  Saves a launch and its
+// latency where both steps are latency-bound.
+template <int Q>
+__global__ __launch_bounds__(kBinThreads) void route_bin_kernel(const float* __restrict__ logits, int32_t n_part,
+                                                                int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
+                                                                float* topk_w, int32_t tile_m, int32_t unit_pairs,
+                                                                int32_t* counts, int32_t* offsets,
+                                                                int32_t* sorted_pair, int32_t* tile_map,
+                                                                int32_t* n_tiles, int32_t* unit_map, int32_t* n_units,
+                                                                int32_t* padded_pair, int32_t* unit_pad,
+                                                                int32_t* n_pad, XcdSplit split_gu, XcdSplit split_dn) {
+  const int t = (int)(threadIdx.x >> 6);
+  if (t < n) route_token<Q>(logits, n_part, n, E, k, t, topk_idx, topk_w);
+  __syncthreads();
+  bin_pairs(topk_idx, n * k, E, tile_m, unit_pairs, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map,
+            n_units, padded_pair, unit_pad, n_pad, split_gu, split_dn);
+}
+
 }  // namespace
 
 hipError_t launch_route_topk(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k,
                              int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   const int grid = (n + kRouteWaves - 1) / kRouteWaves;
-  hipLaunchKernelGGL(route_topk_kernel, dim3(grid), dim3(kRouteWaves * 64), 0, stream, logits, n_part, n, E, k,
-                     topk_idx, topk_w);
+  if (E <= 256)
+    hipLaunchKernelGGL(route_topk_kernel<4>, dim3(grid), dim3(kRouteWaves * 64), 0, stream, logits, n_part, n, E, k,
+                       topk_idx, topk_w);
+  else if (E <= 512)
+    hipLaunchKernelGGL(route_topk_kernel<8>, dim3(grid), dim3(kRouteWaves * 64), 0, stream, logits, n_part, n, E, k,
+                       topk_idx, topk_w);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<16>, dim3(grid), dim3(kRouteWaves * 64), 0, stream, logits, n_part, n, E, k,
+                       topk_idx, topk_w);
   return hipGetLastError();
 }
 
-hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
-                      int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
-                      int32_t* unit_map, int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
-                      const XcdSplit* split_gu, const XcdSplit* split_dn, hipStream_t stream) {
-  XcdSplit sg{}, sd{};
+namespace {
+
+hipError_t check_splits(const XcdSplit* split_gu, const XcdSplit* split_dn, XcdSplit& sg, XcdSplit& sd) {
+  sg = XcdSplit{};
+  sd = XcdSplit{};
   if (split_gu && split_dn) {
     for (const XcdSplit* sp : {split_gu, split_dn})
       if (!sp->bounds || sp->grid < 1 || sp->n_xcd < 1 || sp->n_xcd > kMaxXcds || sp->row_blocks < 1 ||
@@ -352,9 +393,37 @@ hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32
     sg = *split_gu;
     sd = *split_dn;
   }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
+                      int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
+                      int32_t* unit_map, int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
+                      const XcdSplit* split_gu, const XcdSplit* split_dn, hipStream_t stream) {
+  XcdSplit sg, sd;
+  const hipError_t e = check_splits(split_gu, split_dn, sg, sd);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bin_kernel, dim3(1), dim3(kBinThreads), 0, stream, topk_idx, n_pairs, E, tile_m, unit_pairs,
                      counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, padded_pair, unit_pad,
                      n_pad, sg, sd);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_bin(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
+                            float* topk_w, int32_t tile_m, int32_t unit_pairs, int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles, int32_t* unit_map,
+                            int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
+                            const XcdSplit* split_gu, const XcdSplit* split_dn, hipStream_t stream) {
+  if (n < 1 || n > kFusedRouteMaxTokens) return hipErrorInvalidValue;
+  XcdSplit sg, sd;
+  const hipError_t e = check_splits(split_gu, split_dn, sg, sd);
+  if (e != hipSuccess) return e;
+  auto kernel = E <= 256 ? route_bin_kernel<4> : E <= 512 ? route_bin_kernel<8> : route_bin_kernel<16>;
+  hipLaunchKernelGGL(kernel, dim3(1), dim3(kBinThreads), 0, stream, logits, n_part, n, E, k, topk_idx, topk_w, tile_m,
+                     unit_pairs, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, padded_pair,
+                     unit_pad, n_pad, sg, sd);
   return hipGetLastError();
 }
 
