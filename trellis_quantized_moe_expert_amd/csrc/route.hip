@@ -230,25 +230,51 @@ __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* _
                                  int32_t* __restrict__ unit_pad, int32_t* __restrict__ n_pad, const XcdSplit& split_gu,
                                  const XcdSplit& split_dn) {
   __shared__ int cnt[kMaxExperts];
-  __shared__ int running[kMaxExperts];
   __shared__ int pad_shift[kMaxExperts];  // padded position - binned position, per expert
-  __shared__ int wave_cnt[kExpertWaves][kMaxExperts];
+  __shared__ int wave_cnt[kExpertWaves][kMaxExperts];  // per wave: its pairs of each expert, then their first slot
   __shared__ Scan6 wave_tot[kExpertWaves];
   __shared__ int cum_dec[2][kMaxExperts];  // inclusive prefix of the passes' decodes over experts
   __shared__ int cum_units[kMaxExperts];   // inclusive prefix of units over experts
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
 
-  for (int e = tid; e < E; e += kBinThreads) cnt[e] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += kBinThreads) {
-    const int e = topk_idx[p];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  // Wave w owns pairs [w C, (w + 1) C), C a multiple of 64, and walks them 64 at a time in
+  // ascending order, twice: first counting its pairs of each expert, then, once every wave's
+  // counts are turned into its first slot in each expert's bin, placing them.  A pair's rank
+  // among the lanes of its 64 holding the same expert comes from a bitwise match of the expert
+  // id over ballots; the lowest such lane advances the wave's count.  Bins keep ascending pair
+  // order (waves own ascending chunks), and no barrier falls inside the walks.
+  const int C = ((P + kExpertWaves - 1) / kExpertWaves + 63) & ~63;
+  const int p_lo = wv * C, p_hi = min(P, p_lo + C);
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  auto match = [&](int p, int& e, int& rank, int& group) {
+    const int ep = (p < p_hi) ? topk_idx[p] : E;
+    e = (ep >= 0 && ep < E) ? ep : E;  // E: one bucket for idle lanes and out-of-range ids
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot((e >> b) & 1);
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    rank = __popcll(peers & lt_mask);
+    group = __popcll(peers);
+  };
+  for (int e = lane; e < E; e += 64) wave_cnt[wv][e] = 0;
+  for (int base = p_lo; base < p_hi; base += 64) {
+    int e, rank, group;
+    match(base + lane, e, rank, group);
+    if (e < E && rank == 0) wave_cnt[wv][e] += group;
   }
   __syncthreads();
+  if (tid < E) {
+    int c = 0;
+    for (int w = 0; w < kExpertWaves; ++w) c += wave_cnt[w][tid];
+    cnt[tid] = c;
+  }
 
   // exclusive scans of counts, tiles per expert and units per expert (E <= 1024 = threads)
-  const int c = (tid < E) ? cnt[tid] : 0;
+  const int c = (tid < E) ? cnt[tid] : 0;  // written by this thread
   const int nt = (c + tile_m - 1) / tile_m;
   const int nu = (c + unit_pairs - 1) / unit_pairs;
   const int pc = (c + 15) & ~15;  // the bin rounded up to whole 16-pair MFMA blocks
@@ -263,7 +289,12 @@ __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* _
     const int poff = p_incl - pc;
     counts[tid] = c;
     offsets[tid] = off;
-    running[tid] = off;
+    int run = off;  // each wave's first slot in the bin: the pairs of earlier waves come first
+    for (int w = 0; w < kExpertWaves; ++w) {
+      const int nw = wave_cnt[w][tid];
+      wave_cnt[w][tid] = run;
+      run += nw;
+    }
     cum_dec[0][tid] = sc.v[4];
     cum_dec[1][tid] = sc.v[5];
     cum_units[tid] = u_incl;
@@ -297,39 +328,15 @@ __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* _
     if (x <= sp.n_xcd) sp.bounds[x] = share_bound(sp, x, cum_dec[pass], cum_units, cnt, E, unit_pairs);
   }
 
-  // stable scatter, 1024 pairs per round: rank inside the wave from a bitwise match of
-  // the expert id, then the counts of earlier waves and earlier rounds
-  int nbits = 1;
-  while ((1 << nbits) <= E) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < P; base += kBinThreads) {
-    for (int i = tid; i < kExpertWaves * E; i += kBinThreads) (&wave_cnt[0][0])[(i / E) * kMaxExperts + (i % E)] = 0;
-    const int p = base + tid;
-    const int ep = (p < P) ? topk_idx[p] : E;
-    const bool valid = ep >= 0 && ep < E;
-    const int e = valid ? ep : E;  // E: one bucket for idle lanes and out-of-range ids
-    uint64_t peers = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-      const uint64_t m = __ballot((e >> b) & 1);
-      peers &= ((e >> b) & 1) ? m : ~m;
+  for (int base = p_lo; base < p_hi; base += 64) {
+    int e, rank, group;
+    match(base + lane, e, rank, group);
+    if (e < E) {
+      const int pos = wave_cnt[wv][e] + rank;  // every lane reads before the lowest lane advances it
+      sorted_pair[pos] = base + lane;
+      if (padded_pair) padded_pair[pos + pad_shift[e]] = base + lane;
+      if (rank == 0) wave_cnt[wv][e] = pos + group;
     }
-    const int rank = __popcll(peers & lt_mask);
-    __syncthreads();
-    if (valid && rank == 0) wave_cnt[wv][e] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      int pos = running[e] + rank;
-      for (int w = 0; w < wv; ++w) pos += wave_cnt[w][e];
-      sorted_pair[pos] = p;
-      if (padded_pair) padded_pair[pos + pad_shift[e]] = p;
-    }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += kBinThreads) {
-      int add = 0;
-      for (int w = 0; w < kExpertWaves; ++w) add += wave_cnt[w][ee];
-      running[ee] += add;
-    }
-    __syncthreads();
   }
 }
 
