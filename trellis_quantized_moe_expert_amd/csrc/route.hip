@@ -218,6 +218,19 @@ __device__ inline int share_bound(const XcdSplit& sp, int x, const int* cum, con
   return (int)min(t, (long)total);
 }
 
+// A lane's expert id ep (E for none), its rank among the wave's lanes holding the same valid
+// expert (a bitwise match of the id over nbits ballots) and that group's size.
+__device__ inline void peer_rank(int ep, int E, int nbits, uint64_t lt_mask, int& e, int& rank, int& group) {
+  e = (ep >= 0 && ep < E) ? ep : E;  // E: one bucket for idle lanes and out-of-range ids
+  uint64_t peers = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const uint64_t m = __ballot((e >> b) & 1);
+    peers &= ((e >> b) & 1) ? m : ~m;
+  }
+  rank = __popcll(peers & lt_mask);
+  group = __popcll(peers);
+}
+
 // Stable counting sort of the n*k pairs by expert, plus the m-tile map and the unit map
 // (units = runs of up to unit_pairs pairs of one expert; each unit is one decode of the
 // expert's weights in the expert kernels; unit_map/n_units may be NULL to skip them).
@@ -249,22 +262,26 @@ __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* _
   int nbits = 1;
   while ((1 << nbits) <= E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  auto match = [&](int p, int& e, int& rank, int& group) {
-    const int ep = (p < p_hi) ? topk_idx[p] : E;
-    e = (ep >= 0 && ep < E) ? ep : E;  // E: one bucket for idle lanes and out-of-range ids
-    uint64_t peers = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-      const uint64_t m = __ballot((e >> b) & 1);
-      peers &= ((e >> b) & 1) ? m : ~m;
-    }
-    rank = __popcll(peers & lt_mask);
-    group = __popcll(peers);
-  };
+  // the first kBinCached groups of 64 of the wave's expert ids are loaded at once and kept for
+  // both walks (one memory round trip instead of one per group); later groups load as needed
+  int cached[kBinCached];
+#pragma unroll
+  for (int i = 0; i < kBinCached; ++i) {
+    const int p = p_lo + 64 * i + lane;
+    cached[i] = (p < p_hi) ? topk_idx[p] : E;
+  }
   for (int e = lane; e < E; e += 64) wave_cnt[wv][e] = 0;
-  for (int base = p_lo; base < p_hi; base += 64) {
+  auto count = [&](int ep) {
     int e, rank, group;
-    match(base + lane, e, rank, group);
+    peer_rank(ep, E, nbits, lt_mask, e, rank, group);
     if (e < E && rank == 0) wave_cnt[wv][e] += group;
+  };
+#pragma unroll
+  for (int i = 0; i < kBinCached; ++i)
+    if (p_lo + 64 * i < p_hi) count(cached[i]);
+  for (int i = kBinCached; p_lo + 64 * i < p_hi; ++i) {
+    const int p = p_lo + 64 * i + lane;
+    count(p < p_hi ? topk_idx[p] : E);
   }
   __syncthreads();
   if (tid < E) {
@@ -328,15 +345,22 @@ __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* _
     if (x <= sp.n_xcd) sp.bounds[x] = share_bound(sp, x, cum_dec[pass], cum_units, cnt, E, unit_pairs);
   }
 
-  for (int base = p_lo; base < p_hi; base += 64) {
+  auto place = [&](int ep, int p) {
     int e, rank, group;
-    match(base + lane, e, rank, group);
+    peer_rank(ep, E, nbits, lt_mask, e, rank, group);
     if (e < E) {
       const int pos = wave_cnt[wv][e] + rank;  // every lane reads before the lowest lane advances it
-      sorted_pair[pos] = base + lane;
-      if (padded_pair) padded_pair[pos + pad_shift[e]] = base + lane;
+      sorted_pair[pos] = p;
+      if (padded_pair) padded_pair[pos + pad_shift[e]] = p;
       if (rank == 0) wave_cnt[wv][e] = pos + group;
     }
+  };
+#pragma unroll
+  for (int i = 0; i < kBinCached; ++i)
+    if (p_lo + 64 * i < p_hi) place(cached[i], p_lo + 64 * i + lane);
+  for (int i = kBinCached; p_lo + 64 * i < p_hi; ++i) {
+    const int p = p_lo + 64 * i + lane;
+    place(p < p_hi ? topk_idx[p] : E, p);
   }
 }
 
