@@ -760,13 +760,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (idx >= (long)n * h4) return;
   const int t = (int)(idx / h4), c = (int)(idx - (long)t * h4) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int jj = 0; jj < k; ++jj) {
-    const float wt = w[(size_t)t * k + jj];
-    const float4 v = *reinterpret_cast<const float4*>(y + ((size_t)t * k + jj) * H + c);
-    acc.x = fmaf(wt, v.x, acc.x);
-    acc.y = fmaf(wt, v.y, acc.y);
-    acc.z = fmaf(wt, v.z, acc.z);
-    acc.w = fmaf(wt, v.w, acc.w);
+  // up to 8 rows' loads are issued before their (j-ascending) multiply-adds
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4 v[8];
+    float wt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (j0 + i < k) {
+        wt[i] = w[(size_t)t * k + j0 + i];
+        v[i] = *reinterpret_cast<const float4*>(y + ((size_t)t * k + j0 + i) * H + c);
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (j0 + i < k) {
+        acc.x = fmaf(wt[i], v[i].x, acc.x);
+        acc.y = fmaf(wt[i], v[i].y, acc.y);
+        acc.z = fmaf(wt[i], v[i].z, acc.z);
+        acc.w = fmaf(wt[i], v[i].w, acc.w);
+      }
   }
   if (out_bf16) {
     uint2 o;
