@@ -52,11 +52,15 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
 
 __device__ inline float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-// Stage the fp16 LUT into LDS as bf16 (8 entries per 16-byte load).
+__device__ inline uint32_t lut_bf16x2(uint32_t v) {
+  return f16_to_bf16_bits(v & 0xFFFFu) | (f16_to_bf16_bits(v >> 16) << 16);
+}
+
+// Stage the fp16 LUT into LDS as bf16 (8 entries per 16-byte load) with a workgroup of THREADS
+// threads: every load of a thread is issued before the first conversion, so the fill waits for
+// one memory round trip instead of one per load.
 template <int THREADS>
 __device__ inline void fill_lut(uint16_t* lut_s, const uint16_t* __restrict__ lut_g) {
-  // every 16-byte load of a thread is issued before the first conversion, so the fill waits for
-  // one memory round trip instead of one per load
   constexpr int kVec = kLutEntries / 8;
   constexpr int kIter = (kVec + THREADS - 1) / THREADS;
   const uint4* src = reinterpret_cast<const uint4*>(lut_g);
@@ -70,13 +74,28 @@ __device__ inline void fill_lut(uint16_t* lut_s, const uint16_t* __restrict__ lu
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     const int i = (int)threadIdx.x + it * THREADS;
-    if (kVec % THREADS == 0 || i < kVec) {
-      uint4 o;
-      o.x = f16_to_bf16_bits(v[it].x & 0xFFFFu) | (f16_to_bf16_bits(v[it].x >> 16) << 16);
-      o.y = f16_to_bf16_bits(v[it].y & 0xFFFFu) | (f16_to_bf16_bits(v[it].y >> 16) << 16);
-      o.z = f16_to_bf16_bits(v[it].z & 0xFFFFu) | (f16_to_bf16_bits(v[it].z >> 16) << 16);
-      o.w = f16_to_bf16_bits(v[it].w & 0xFFFFu) | (f16_to_bf16_bits(v[it].w >> 16) << 16);
-      dst[i] = o;
+    if (kVec % THREADS == 0 || i < kVec)
+      dst[i] = uint4{lut_bf16x2(v[it].x), lut_bf16x2(v[it].y), lut_bf16x2(v[it].z), lut_bf16x2(v[it].w)};
+  }
+  __syncthreads();
+}
+
+// The same with any workgroup size (a launch with fewer waves than its configuration's).
+__device__ inline void fill_lut_any(uint16_t* lut_s, const uint16_t* __restrict__ lut_g) {
+  constexpr int kVec = kLutEntries / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(lut_g);
+  uint4* dst = reinterpret_cast<uint4*>(lut_s);
+  for (int i0 = 0; i0 < kVec; i0 += 4 * (int)blockDim.x) {
+    uint4 v[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = i0 + (int)threadIdx.x + it * (int)blockDim.x;
+      if (i < kVec) v[it] = src[i];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = i0 + (int)threadIdx.x + it * (int)blockDim.x;
+      if (i < kVec) dst[i] = uint4{lut_bf16x2(v[it].x), lut_bf16x2(v[it].y), lut_bf16x2(v[it].z), lut_bf16x2(v[it].w)};
     }
   }
   __syncthreads();
@@ -621,7 +640,9 @@ __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, cons
   }
 }
 
-template <int MODE, int ARM, class CFG, bool FRAG>
+// SPREAD: the launch may run fewer waves per workgroup than the configuration's (a small
+// batch spread over more CUs).
+template <int MODE, int ARM, class CFG, bool FRAG, bool SPREAD>
 __device__ inline void expert_tasks(const ExpertParams& p, const uint16_t* lut_s) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = p.n_units_dev ? __builtin_amdgcn_readfirstlane(*p.n_units_dev) : p.n_units_host;
@@ -649,7 +670,7 @@ __device__ inline void expert_tasks(const ExpertParams& p, const uint16_t* lut_s
     lo = total * before / G;
     hi = total * (before + cus) / G;
   }
-  const long nslots = (long)CFG::kWaves * cus;
+  const long nslots = (long)(SPREAD ? (int)(blockDim.x >> 6) : CFG::kWaves) * cus;
   for (long task = lo + (long)wave * cus + cu; task < hi; task += nslots) {
     const int u = (int)(task / nblocks);
     const int nb = (int)(task - (long)u * nblocks);
@@ -660,14 +681,16 @@ __device__ inline void expert_tasks(const ExpertParams& p, const uint16_t* lut_s
 }
 
 // FRAG: the grouped arm's activations are in fragment order (ExpertParams::act_frag).
-template <int MODE, int ARM, class CFG, bool FRAG = false>
+// SPREAD (GEMV arm): the launch may run fewer waves per workgroup than CFG's.
+template <int MODE, int ARM, class CFG, bool FRAG = false, bool SPREAD = false>
 __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParams p) {
   if constexpr (ARM == kArmDense) {
-    expert_tasks<MODE, ARM, CFG, false>(p, nullptr);
+    expert_tasks<MODE, ARM, CFG, false, false>(p, nullptr);
   } else {
     __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
-    fill_lut<CFG::kWaves * 64>(lut_s, p.lut);
-    expert_tasks<MODE, ARM, CFG, FRAG>(p, lut_s);
+    if constexpr (SPREAD) fill_lut_any(lut_s, p.lut);
+    else fill_lut<CFG::kWaves * 64>(lut_s, p.lut);
+    expert_tasks<MODE, ARM, CFG, FRAG, SPREAD>(p, lut_s);
   }
 }
 
@@ -824,10 +847,14 @@ __global__ __launch_bounds__(1024, 1) void gather_probe_kernel(int32_t rounds, u
 using CfgDense = ExpertCfg<16, 2, 2, 2>;
 
 template <class CFG>
-static void launch_cfg(int mode, int arm, const ExpertParams& p, int grid, hipStream_t stream) {
-  const dim3 g(grid), b(CFG::kWaves * 64);
+static hipError_t launch_cfg(int mode, int arm, const ExpertParams& p, int grid, int waves, hipStream_t stream) {
+  // only the GEMV arm is built to run with fewer waves than its configuration's
+  const int full = arm == kArmDense ? CfgDense::kWaves : CFG::kWaves;
+  if (grid < 1 || waves < 1 || waves > full || (waves < full && arm != kArmGemv)) return hipErrorInvalidValue;
+  const dim3 g(grid), b(waves * 64);
+  const bool spread = waves < full;
   if (arm == kArmDense) {
-    const dim3 bd(CfgDense::kWaves * 64);
+    const dim3 bd(waves * 64);
     if (mode == kModeGateUp)
       hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmDense, CfgDense>), g, bd, 0, stream, p);
     else
@@ -838,14 +865,21 @@ static void launch_cfg(int mode, int arm, const ExpertParams& p, int grid, hipSt
     else
       hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, false>), g, b, 0, stream, p);
   } else if (mode == kModeGateUp) {
-    hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG>), g, b, 0, stream, p);
+    if (spread)
+      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG, false, true>), g, b, 0, stream, p);
+    else
+      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG>), g, b, 0, stream, p);
   } else if (arm == kArmGrouped) {
     if (p.act_frag && p.unit_pad)
       hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped, CFG, true>), g, b, 0, stream, p);
     else
       hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped, CFG, false>), g, b, 0, stream, p);
-  } else
+  } else if (spread) {
+    hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGemv, CFG, false, true>), g, b, 0, stream, p);
+  } else {
     hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGemv, CFG>), g, b, 0, stream, p);
+  }
+  return hipGetLastError();
 }
 
 template <class CFG>
@@ -877,19 +911,19 @@ bool variant_info(int variant, int arm, VariantInfo& v) {
   }
 }
 
-hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, hipStream_t stream) {
+hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, int waves,
+                         hipStream_t stream) {
   switch (variant) {
-    case 1: launch_cfg<Cfg1>(mode, arm, p, grid, stream); break;
-    case 2: launch_cfg<Cfg2>(mode, arm, p, grid, stream); break;
-    case 3: launch_cfg<Cfg3>(mode, arm, p, grid, stream); break;
-    case 4: launch_cfg<Cfg4>(mode, arm, p, grid, stream); break;
-    case 5: launch_cfg<Cfg5>(mode, arm, p, grid, stream); break;
-    case 6: launch_cfg<Cfg6>(mode, arm, p, grid, stream); break;
-    case 7: launch_cfg<Cfg7>(mode, arm, p, grid, stream); break;
-    case 8: launch_cfg<Cfg8>(mode, arm, p, grid, stream); break;
+    case 1: return launch_cfg<Cfg1>(mode, arm, p, grid, waves, stream);
+    case 2: return launch_cfg<Cfg2>(mode, arm, p, grid, waves, stream);
+    case 3: return launch_cfg<Cfg3>(mode, arm, p, grid, waves, stream);
+    case 4: return launch_cfg<Cfg4>(mode, arm, p, grid, waves, stream);
+    case 5: return launch_cfg<Cfg5>(mode, arm, p, grid, waves, stream);
+    case 6: return launch_cfg<Cfg6>(mode, arm, p, grid, waves, stream);
+    case 7: return launch_cfg<Cfg7>(mode, arm, p, grid, waves, stream);
+    case 8: return launch_cfg<Cfg8>(mode, arm, p, grid, waves, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_pack_act(const uint16_t* x, const int32_t* padded_pair, const int32_t* n_pad, int32_t k,

@@ -74,7 +74,10 @@ struct VariantInfo {
 };
 // `variant` in 1..8 (the plan resolves 0).  variant_info returns false for other values.
 bool variant_info(int variant, int arm, VariantInfo& v);
-hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, hipStream_t stream);
+// `waves` per workgroup: at most the variant's (VariantInfo::waves); fewer spread a small launch
+// over more CUs.
+hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, int waves,
+                         hipStream_t stream);
 
 // Top-k over logits given as n_part partial sums part[s][t][e] (s-major, n*E apart), added in
 // ascending s; n_part = 1 reads plain logits.
