@@ -125,6 +125,20 @@ def test_full_size_workloads_sampled_tokens(name):
     assert ok, st
 
 
+def test_v4_small_batches_full_parity():
+    """Decode-width batches of the V4 layer on the GEMV arm, whose launches have fewer tasks than
+    the GPU has wave slots and run with fewer waves per workgroup on every CU; every token is
+    compared."""
+    inps = moe_inputs.make_inputs_multi(moe_inputs.WORKLOADS["v4_decode_n32"], [1, 2, 5], seed=21)
+    layer = Layer(inps[1], out_dtype="f32", max_tokens=5)
+    for n in (1, 2, 5):
+        say(f"forward V4 small batch n={n}")
+        got = layer.forward(inps[n])
+        assert q.qtip_moe_stats_get(layer.plan)["last_arm"] == q.QTIP_ARM_GEMV
+        check(got, moe.moe_forward(inps[n]), "f32")
+    layer.close()
+
+
 def test_forward_rejects_empty_and_oversized_batches_on_device():
     import torch
     inp = moe_inputs.make_workload("tiny", seed=0)

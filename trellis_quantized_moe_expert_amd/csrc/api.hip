@@ -119,7 +119,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
   size_t topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, h, y, router_part,
-      dense_gate, dense_up, dense_down, padded_pair, unit_pad, n_pad, xs, bounds_gu, bounds_dn, total;
+      dense_gate, dense_up, dense_down, padded_pair, unit_pad, n_pad, xs, total;
+  size_t max_units;  // entries of each pass's unit map (and unit_pad)
 };
 
 // Padded positions (every woken expert's bin rounded up to 16 pairs) for n tokens, a multiple of 16.
@@ -148,8 +149,9 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   const size_t P = (size_t)n_tokens * d.top_k;
   const size_t woken_max = P < (size_t)d.num_experts ? P : (size_t)d.num_experts;
   const size_t max_tiles = P / tile_m + woken_max + 1;
-  const size_t max_units = P / kUnitMaxPairs + woken_max + 1;
+  const size_t max_units = P + woken_max + 1;  // units of one pair at the least (the GEMV arm's)
   WsLayout L{};
+  L.max_units = max_units;
   size_t o = 0;
   L.topk_idx = o;     o = align256(o + P * 4);
   L.topk_w = o;       o = align256(o + P * 4);
@@ -158,8 +160,8 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.sorted_pair = o;  o = align256(o + P * 4);
   L.tile_map = o;     o = align256(o + max_tiles * 12);
   L.n_tiles = o;      o = align256(o + 4);
-  L.unit_map = o;     o = align256(o + max_units * 12);
-  L.n_units = o;      o = align256(o + 4);
+  L.unit_map = o;     o = align256(o + 2 * max_units * 12);  // one unit map per expert pass
+  L.n_units = o;      o = align256(o + 2 * 4);
   const size_t PP = frag ? pad_positions(d, n_tokens) : 0;
   L.h = o;            o = align256(o + (frag ? PP : P) * (size_t)d.inter * 2);  // rows (P) or fragment order (PP)
   L.y = o;            o = align256(o + P * (size_t)d.hidden * 4);
@@ -170,19 +172,19 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.dense_up = o;     o = align256(o + dense_mat);
   L.dense_down = o;   o = align256(o + dense_mat);
   L.padded_pair = o;  o = align256(o + PP * 4);
-  L.unit_pad = o;     o = align256(o + max_units * 4);
+  L.unit_pad = o;     o = align256(o + (frag ? 2 * max_units * 4 : 0));
   L.n_pad = o;        o = align256(o + 4);
   L.xs = o;           o = align256(o + (pack ? PP * (size_t)d.hidden * 2 : 0));
-  L.bounds_gu = o;    o = align256(o + (kMaxXcds + 1) * 4);
-  L.bounds_dn = o;    o = align256(o + (kMaxXcds + 1) * 4);
   L.total = o;
   return L;
 }
 
-size_t max_units_for(const qtip_moe_desc& d, int32_t n_tokens) {
+// Units of at most unit_pairs pairs that n tokens can make: each woken expert's pairs / unit_pairs,
+// plus one partial unit.
+size_t max_units_for(const qtip_moe_desc& d, int32_t n_tokens, int32_t unit_pairs) {
   const size_t P = (size_t)n_tokens * d.top_k;
   const size_t woken_max = P < (size_t)d.num_experts ? P : (size_t)d.num_experts;
-  return P / kUnitMaxPairs + woken_max;
+  return P / (size_t)unit_pairs + woken_max;
 }
 
 // --- per-device state: CU count and the witness ---------------------------------------
@@ -503,9 +505,8 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
   const qtip_moe_desc& d = plan->d;
   hipError_t e;
   if (n_tokens <= kFusedRouteMaxTokens) {  // the same kernels as the forward's routing
-    e = launch_route_bin(logits, 1, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, plan->tile_m, kUnitMaxPairs,
-                         counts, offsets, sorted_pair, tile_map, n_tiles, nullptr, nullptr, nullptr, nullptr, nullptr,
-                         nullptr, nullptr, st);
+    e = launch_route_bin(logits, 1, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, plan->tile_m, counts, offsets,
+                         sorted_pair, tile_map, n_tiles, nullptr, nullptr, nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "route/bin launch");
     plan->stats.route_launches++;
     return QTIP_OK;
@@ -513,8 +514,8 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
   e = launch_route_topk(logits, 1, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
   if (e != hipSuccess) return hip_fail(e, "route_topk launch");
   plan->stats.route_launches++;
-  e = launch_bin(topk_idx, n_tokens * d.top_k, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets,
-                 sorted_pair, tile_map, n_tiles, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+  e = launch_bin(topk_idx, n_tokens * d.top_k, d.num_experts, plan->tile_m, counts, offsets, sorted_pair, tile_map,
+                 n_tiles, nullptr, nullptr, nullptr, st);
   if (e != hipSuccess) return hip_fail(e, "bin launch");
   plan->stats.route_launches++;
   return QTIP_OK;
@@ -635,33 +636,34 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   const bool frag = plan->frag && karm == kArmGrouped &&
                     (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kFragMinPairs);
   int32_t* padded_pair = reinterpret_cast<int32_t*>(ws + L.padded_pair);
-  int32_t* unit_pad = reinterpret_cast<int32_t*>(ws + L.unit_pad);
   int32_t* n_pad = reinterpret_cast<int32_t*>(ws + L.n_pad);
   uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
   const int32_t pp_max = (int32_t)pad_positions(d, n_tokens);
-  // kernel configurations of the two passes (the binning kernel splits their tasks over XCDs
-  // by the decodes their pairs per decode imply)
+  // kernel configurations of the two passes; each pass gets its own decode units (runs of its
+  // pairs per decode), so every task of a pass is one decode of its rows
   const int kv_gu = fit_variant(resolve_variant(plan, karm, kModeGateUp, n_tokens), karm, d.inter);
   const int kv_dn = fit_variant(resolve_variant(plan, karm, kModeSingle, n_tokens), karm, d.hidden);
   VariantInfo vi_gu{}, vi_dn{};
   variant_info(kv_gu, karm, vi_gu);
   variant_info(kv_dn, karm, vi_dn);
-  const size_t max_units = max_units_for(d, n_tokens);
+  UnitMaps um{};
+  um.unit_pairs[0] = vi_gu.pairs_per_decode;
+  um.unit_pairs[1] = vi_dn.pairs_per_decode;
+  um.map[0] = unit_map;
+  um.map[1] = unit_map + 3 * L.max_units;
+  um.count[0] = n_units;
+  um.count[1] = n_units + 1;
+  um.pad[0] = frag ? reinterpret_cast<int32_t*>(ws + L.unit_pad) : nullptr;
+  um.pad[1] = frag ? reinterpret_cast<int32_t*>(ws + L.unit_pad) + L.max_units : nullptr;
   const bool spread = karm == kArmGemv;
-  const LaunchShape shape_gu = persistent_shape(dev, max_units * (d.inter / vi_gu.rows_per_task), vi_gu.waves, spread);
-  const LaunchShape shape_dn = persistent_shape(dev, max_units * (d.hidden / vi_dn.rows_per_task), vi_dn.waves, spread);
-  const int grid_gu = shape_gu.grid, grid_dn = shape_dn.grid;
-  const int nx = xcd_count(dev);
-  int32_t* bounds_gu = reinterpret_cast<int32_t*>(ws + L.bounds_gu);
-  int32_t* bounds_dn = reinterpret_cast<int32_t*>(ws + L.bounds_dn);
-  const XcdSplit split_gu{grid_gu, nx, d.inter / vi_gu.rows_per_task, vi_gu.pairs_per_decode, bounds_gu};
-  const XcdSplit split_dn{grid_dn, nx, d.hidden / vi_dn.rows_per_task, vi_dn.pairs_per_decode, bounds_dn};
+  const LaunchShape shape_gu = persistent_shape(
+      dev, max_units_for(d, n_tokens, vi_gu.pairs_per_decode) * (d.inter / vi_gu.rows_per_task), vi_gu.waves, spread);
+  const LaunchShape shape_dn = persistent_shape(
+      dev, max_units_for(d, n_tokens, vi_dn.pairs_per_decode) * (d.hidden / vi_dn.rows_per_task), vi_dn.waves, spread);
   if (n_tokens <= kFusedRouteMaxTokens) {
     // one workgroup routes and bins a small batch (the "route" stage then holds both)
-    e = launch_route_bin(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, plan->tile_m, kUnitMaxPairs,
-                         counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units,
-                         frag ? padded_pair : nullptr, frag ? unit_pad : nullptr, frag ? n_pad : nullptr, &split_gu,
-                         &split_dn, st);
+    e = launch_route_bin(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, plan->tile_m, counts, offsets,
+                         sorted_pair, tile_map, n_tiles, frag ? padded_pair : nullptr, frag ? n_pad : nullptr, &um, st);
     if (e != hipSuccess) return hip_fail(e, "route/bin launch");
     if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
     plan->stats.route_launches += 1;
@@ -669,9 +671,8 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     e = launch_route_topk(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, st);
     if (e != hipSuccess) return hip_fail(e, "route_topk launch");
     if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
-    e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, kUnitMaxPairs, counts, offsets, sorted_pair, tile_map,
-                   n_tiles, unit_map, n_units, frag ? padded_pair : nullptr, frag ? unit_pad : nullptr,
-                   frag ? n_pad : nullptr, &split_gu, &split_dn, st);
+    e = launch_bin(topk_idx, P, d.num_experts, plan->tile_m, counts, offsets, sorted_pair, tile_map, n_tiles,
+                   frag ? padded_pair : nullptr, frag ? n_pad : nullptr, &um, st);
     if (e != hipSuccess) return hip_fail(e, "bin launch");
     plan->stats.route_launches += 2;
   }
@@ -725,8 +726,8 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   gu.act = reinterpret_cast<const uint16_t*>(x_bf16);
   gu.act_row_map = sorted_pair;
   gu.act_row_div = d.top_k;
-  gu.units = unit_map;
-  gu.n_units_dev = n_units;
+  gu.units = um.map[0];
+  gu.n_units_dev = um.count[0];
   gu.num_experts = d.num_experts;
   gu.rows = d.inter;
   gu.cols = d.hidden;
@@ -736,15 +737,14 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   gu.n_out_rows = P;
   gu.n_xcd = xcd_count(dev);
   if (frag) {
-    gu.unit_pad = unit_pad;
+    gu.unit_pad = um.pad[0];
     gu.n_pad_max = pp_max;
   }
   if (pack) {
     gu.act = xs;
     gu.act_frag = 1;
   }
-  gu.xcd_bounds = bounds_gu;
-  e = launch_expert(kModeGateUp, karm, kv_gu, gu, grid_gu, shape_gu.waves, st);
+  e = launch_expert(kModeGateUp, karm, kv_gu, gu, shape_gu.grid, shape_gu.waves, st);
   if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
   if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
 
@@ -755,8 +755,8 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   dn.lut = w->lut;
   dn.act = h;
   dn.act_row_div = 1;
-  dn.units = unit_map;
-  dn.n_units_dev = n_units;
+  dn.units = um.map[1];
+  dn.n_units_dev = um.count[1];
   dn.num_experts = d.num_experts;
   dn.rows = d.hidden;
   dn.cols = d.inter;
@@ -767,12 +767,11 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   dn.n_out_rows = P;
   dn.n_xcd = xcd_count(dev);
   if (frag) {
-    dn.unit_pad = unit_pad;
+    dn.unit_pad = um.pad[1];
     dn.act_frag = 1;
     dn.n_pad_max = pp_max;
   }
-  dn.xcd_bounds = bounds_dn;
-  e = launch_expert(kModeSingle, karm, kv_dn, dn, grid_dn, shape_dn.waves, st);
+  e = launch_expert(kModeSingle, karm, kv_dn, dn, shape_dn.grid, shape_dn.waves, st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
   if (karm == kArmGrouped) plan->stats.grouped_launches += 2;

@@ -649,26 +649,23 @@ __device__ inline void expert_tasks(const ExpertParams& p, const uint16_t* lut_s
   const int nblocks = p.rows / CFG::kRows;
   const long total = (long)n_units * nblocks;
   // Task order.  Workgroup b runs on XCD b % n_xcd (round-robin dispatch).  Each XCD owns a
-  // contiguous share of the tasks in proportion to its workgroups (weighted by decodes when
-  // the binning kernel sets the bounds), and its waves take that share's tasks in turn across
-  // its CUs, so an XCD works on a few units at a time: their activation rows stay in its L2,
-  // and a CU's waves (row blocks of the same unit) share them in L1.
+  // contiguous share of the tasks in proportion to its workgroups, and its waves take that
+  // share's tasks in turn across its CUs, so an XCD works on a few units at a time: their
+  // activation rows stay in its L2, and a CU's waves (row blocks of the same unit) share them
+  // in L1.  Every unit is one decode, so equal task counts are equal work; share boundaries are
+  // rounded to whole rounds of the XCD's CUs when those divide a unit's row blocks, so every CU
+  // then takes the same row blocks of the same units.
   const int nx = p.n_xcd;
   const int G = gridDim.x;
   const int xcd = blockIdx.x % nx, cu = blockIdx.x / nx;
   const int cus = G / nx + (xcd < G % nx ? 1 : 0);
   const int before = xcd * (G / nx) + min(xcd, G % nx);
-  long lo, hi;
-  if (p.xcd_bounds) {
-    // shares in proportion to the decodes they hold, set by the binning kernel, so XCDs
-    // holding the busiest experts' units get fewer tasks
-    lo = __builtin_amdgcn_readfirstlane(p.xcd_bounds[xcd]);
-    hi = __builtin_amdgcn_readfirstlane(p.xcd_bounds[xcd + 1]);
-    lo = lo < 0 ? 0 : (lo > total ? total : lo);
-    hi = hi < lo ? lo : (hi > total ? total : hi);
-  } else {
-    lo = total * before / G;
-    hi = total * (before + cus) / G;
+  long lo = total * before / G;
+  long hi = total * (before + cus) / G;
+  const long Q = G / nx;
+  if (Q > 1 && nblocks % Q == 0) {
+    lo = (lo + Q / 2) / Q * Q;
+    hi = (hi + Q / 2) / Q * Q;
   }
   const long nslots = (long)(SPREAD ? (int)(blockDim.x >> 6) : CFG::kWaves) * cus;
   for (long task = lo + (long)wave * cus + cu; task < hi; task += nslots) {

@@ -57,8 +57,6 @@ struct ExpertParams {
                                 // fragment order over padded positions (dense_fragment_offset, rows = padded
                                 // positions), the order the down pass reads it in.
   int32_t act_frag;             // with unit_pad: the activations (act) are in that fragment order as well
-  const int32_t* xcd_bounds;    // task range of each XCD's share for this launch (n_xcd + 1 entries, split by
-                                // decodes; see XcdSplit), or NULL: shares then split tasks by count
   int32_t n_pad_max;            // padded positions the fragment-order buffers hold (with unit_pad)
   const uint16_t* dense0;       // dequantize arm: [E] x rows x cols bf16 weights in fragment order (gate, or the single matrix)
   const uint16_t* dense1;       // dequantize arm: the same for the up weights (fused pass only)
@@ -118,29 +116,26 @@ hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w, int32_t n, i
                               int32_t n_xcd, float* part, hipStream_t stream);
 hipError_t launch_router_reduce(const float* part, int32_t S, int64_t count, float* logits, hipStream_t stream);
 
-// How one expert pass's launch splits its tasks (unit x row block, unit-major) over XCDs:
-// workgroup b runs on XCD b % n_xcd, so XCD x holds `cus` = G/n_xcd (+1 for x < G % n_xcd)
-// workgroups, and its share holds that fraction of the pass's decodes (a unit of len pairs
-// decodes its rows ceil(len / pairs_per_decode) times), so XCDs holding the busiest experts'
-// units get fewer tasks.
-struct XcdSplit {
-  int32_t grid;            // G, the launch's workgroups
-  int32_t n_xcd;
-  int32_t row_blocks;      // tasks per unit (rows / rows per task)
-  int32_t pairs_per_decode;
-  int32_t* bounds;         // out: n_xcd + 1 task indices
+// The decode units of the two expert passes (index 0: the fused gate/up pass, 1: the down
+// pass): runs of up to unit_pairs[i] pairs of one expert, unit_pairs[i] being that pass
+// kernel's pairs per decode (at most kUnitMaxPairs), so every unit is exactly one decode of its
+// expert's rows.  map[i]: (expert, first binned position, pairs) per unit, expert-ascending;
+// count[i]: the number of units; pad[i]: each unit's first padded position (a multiple of 16),
+// or NULL without the padded space.
+struct UnitMaps {
+  int32_t unit_pairs[2];
+  int32_t* map[2];
+  int32_t* pad[2];
+  int32_t* count[2];
 };
 
-// Binning.  unit_map/n_units may be NULL (no units); padded_pair/unit_pad/n_pad may be NULL (no
-// padded position space); split_gu/split_dn may be NULL (no XCD bounds; they need the units).
-// The padded space rounds every expert's bin up to a multiple of 16 pairs: padded_pair[pp] is the
-// pair at padded position pp or -1 in the padding, unit_pad[u] the padded start of unit u (a
-// multiple of 16), *n_pad the padded total.
-hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
-                      int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map,
-                      int32_t* n_tiles, int32_t* unit_map, int32_t* n_units, int32_t* padded_pair,
-                      int32_t* unit_pad, int32_t* n_pad, const XcdSplit* split_gu, const XcdSplit* split_dn,
-                      hipStream_t stream);
+// Binning.  units may be NULL (no units); padded_pair/n_pad may be NULL (no padded position
+// space).  The padded space rounds every expert's bin up to a multiple of 16 pairs:
+// padded_pair[pp] is the pair at padded position pp or -1 in the padding, *n_pad the padded
+// total.
+hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t* counts,
+                      int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
+                      int32_t* padded_pair, int32_t* n_pad, const UnitMaps* units, hipStream_t stream);
 
 // Batches of at most this many tokens (one per wave of the binning workgroup) are routed and
 // binned by one workgroup (launch_route_bin); measured, a second token per wave already costs
@@ -150,10 +145,9 @@ constexpr int kFusedRouteMaxTokens = kExpertWaves;
 // Routing (launch_route_topk) and binning (launch_bin) of n <= kFusedRouteMaxTokens tokens by
 // one workgroup, with the same outputs.
 hipError_t launch_route_bin(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
-                            float* topk_w, int32_t tile_m, int32_t unit_pairs, int32_t* counts, int32_t* offsets,
-                            int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles, int32_t* unit_map,
-                            int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
-                            const XcdSplit* split_gu, const XcdSplit* split_dn, hipStream_t stream);
+                            float* topk_w, int32_t tile_m, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                            int32_t* tile_map, int32_t* n_tiles, int32_t* padded_pair, int32_t* n_pad,
+                            const UnitMaps* units, hipStream_t stream);
 
 // Gathers the activation row of every padded position (token = pair / k; padding untouched)
 // into fragment order: xs holds n_pad_max padded rows of H bf16 values.

@@ -175,48 +175,16 @@ __device__ inline Scan6 block_inclusive_scan6(Scan6 x, Scan6* wave_tot) {
   return x;
 }
 
-// Decodes of one pass for an expert's c pairs: nu units (nu - 1 full ones of unit_pairs pairs
-// and a last one), each decoding its rows once per chunk of pairs_per_decode pairs.
-__device__ inline int expert_decodes(int c, int nu, int unit_pairs, int ppd) {
-  if (nu == 0) return 0;
-  const int last = c - (nu - 1) * unit_pairs;
-  return (nu - 1) * ((unit_pairs + ppd - 1) / ppd) + (last + ppd - 1) / ppd;
-}
-
-// Start task of XCD x's share in one expert pass (x = n_xcd: the end).  The share holds a
-// fraction of the pass's decodes in proportion to the XCD's workgroups.  Positions count
-// decodes times row blocks (each decode spread evenly over its unit's row-block tasks): the
-// boundary sits at pos = floor(D * nb * before_x / G) (D: the pass's decodes, cum: their
-// inclusive prefix over experts, cum_units: that of units), and a binary search finds the
-// expert holding it.  The task index is then rounded to a multiple of the XCD's workgroup
-// count Q = G / n_xcd when Q divides the row blocks per unit: the XCD's CUs take its tasks in
-// turn, so every CU then gets the same row blocks of the same units, the same work.  With
-// equal decodes per unit this is the split by task count.
-__device__ inline int share_bound(const XcdSplit& sp, int x, const int* cum, const int* cum_units, const int* cnt,
-                                  int E, int unit_pairs) {
-  const int G = sp.grid, nx = sp.n_xcd, nb = sp.row_blocks, ppd = sp.pairs_per_decode;
-  const int total = cum_units[E - 1] * nb;
-  const int before = x * (G / nx) + min(x, G % nx);
-  const int D = cum[E - 1];
-  if (x >= nx || before >= G || D == 0) return total;
-  const long pos = (long)D * nb * before / G;
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((long)cum[mid] * nb > pos) hi = mid;
-    else lo = mid + 1;
-  }
-  const int c = cnt[lo];
-  const int nu = (c + unit_pairs - 1) / unit_pairs;
-  const long off = pos - (long)(cum[lo] - expert_decodes(c, nu, unit_pairs, ppd)) * nb;
-  const int full = (unit_pairs + ppd - 1) / ppd;
-  const int q = (int)min(off / ((long)full * nb), (long)(nu - 1));
-  const int uc = q < nu - 1 ? full : (c - (nu - 1) * unit_pairs + ppd - 1) / ppd;
-  long t = (long)(cum_units[lo] - nu + q) * nb + (off - (long)q * full * nb) / uc;
-  const int Q = G / nx;
-  if (Q > 1 && nb % Q == 0) t = (t + Q / 2) / Q * Q;
-  return (int)min(t, (long)total);
-}
+// The decode units of one expert pass: runs of up to unit_pairs pairs of one expert, each one
+// decode of the expert's rows in that pass (unit_pairs = the pass kernel's pairs per decode).
+// map: (expert, first binned position, pairs) per unit; pad: each unit's first padded position
+// (NULL without the padded space); count: the number of units.  map NULL: no units.
+struct UnitOut {
+  int32_t unit_pairs;
+  int32_t* map;
+  int32_t* pad;
+  int32_t* count;
+};
 
 // A lane's expert id ep (E for none), its rank among the wave's lanes holding the same valid
 // expert (a bitwise match of the id over nbits ballots) and that group's size.
@@ -231,23 +199,18 @@ __device__ inline void peer_rank(int ep, int E, int nbits, uint64_t lt_mask, int
   group = __popcll(peers);
 }
 
-// Stable counting sort of the n*k pairs by expert, plus the m-tile map and the unit map
-// (units = runs of up to unit_pairs pairs of one expert; each unit is one decode of the
-// expert's weights in the expert kernels; unit_map/n_units may be NULL to skip them).
-// Run by one workgroup of 1024 threads.
+// Stable counting sort of the n*k pairs by expert, plus the m-tile map and the decode units of
+// the two expert passes (ug: the fused gate/up pass, ud: the down pass).  Run by one workgroup
+// of 1024 threads.
 __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* __restrict__ topk_idx, int32_t P, int32_t E, int32_t tile_m,
-                                 int32_t unit_pairs, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                 int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                  int32_t* __restrict__ sorted_pair, int32_t* __restrict__ tile_map,
-                                 int32_t* __restrict__ n_tiles, int32_t* __restrict__ unit_map,
-                                 int32_t* __restrict__ n_units, int32_t* __restrict__ padded_pair,
-                                 int32_t* __restrict__ unit_pad, int32_t* __restrict__ n_pad, const XcdSplit& split_gu,
-                                 const XcdSplit& split_dn) {
+                                 int32_t* __restrict__ n_tiles, int32_t* __restrict__ padded_pair,
+                                 int32_t* __restrict__ n_pad, const UnitOut& ug, const UnitOut& ud) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int pad_shift[kMaxExperts];  // padded position - binned position, per expert
   __shared__ int wave_cnt[kExpertWaves][kMaxExperts];  // per wave: its pairs of each expert, then their first slot
   __shared__ Scan6 wave_tot[kExpertWaves];
-  __shared__ int cum_dec[2][kMaxExperts];  // inclusive prefix of the passes' decodes over experts
-  __shared__ int cum_units[kMaxExperts];   // inclusive prefix of units over experts
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
 
@@ -290,17 +253,15 @@ __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* _
     cnt[tid] = c;
   }
 
-  // exclusive scans of counts, tiles per expert and units per expert (E <= 1024 = threads)
+  // exclusive scans of counts, m-tiles, padded pairs and both passes' units per expert
+  // (E <= 1024 = threads)
   const int c = (tid < E) ? cnt[tid] : 0;  // written by this thread
   const int nt = (c + tile_m - 1) / tile_m;
-  const int nu = (c + unit_pairs - 1) / unit_pairs;
   const int pc = (c + 15) & ~15;  // the bin rounded up to whole 16-pair MFMA blocks
-  // decodes of the two expert passes, scanned with the rest for the XCD shares
-  const bool split = unit_map && split_gu.bounds && split_dn.bounds;
-  const int dg = split ? expert_decodes(c, nu, unit_pairs, split_gu.pairs_per_decode) : 0;
-  const int dd = split ? expert_decodes(c, nu, unit_pairs, split_dn.pairs_per_decode) : 0;
-  const Scan6 sc = block_inclusive_scan6(Scan6{{c, nt, nu, pc, dg, dd}}, wave_tot);
-  const int c_incl = sc.v[0], t_incl = sc.v[1], u_incl = sc.v[2], p_incl = sc.v[3];
+  const int nug = ug.map ? (c + ug.unit_pairs - 1) / ug.unit_pairs : 0;
+  const int nud = ud.map ? (c + ud.unit_pairs - 1) / ud.unit_pairs : 0;
+  const Scan6 sc = block_inclusive_scan6(Scan6{{c, nt, pc, nug, nud, 0}}, wave_tot);
+  const int c_incl = sc.v[0], t_incl = sc.v[1], p_incl = sc.v[2];
   if (tid < E) {
     const int off = c_incl - c;
     const int poff = p_incl - pc;
@@ -312,38 +273,35 @@ __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* _
       wave_cnt[w][tid] = run;
       run += nw;
     }
-    cum_dec[0][tid] = sc.v[4];
-    cum_dec[1][tid] = sc.v[5];
-    cum_units[tid] = u_incl;
     pad_shift[tid] = poff - off;
     if (padded_pair)
       for (int q = c; q < pc; ++q) padded_pair[poff + q] = -1;
-    for (int q = 0; unit_pad && q < nu; ++q) unit_pad[u_incl - nu + q] = poff + q * unit_pairs;
     int tb = t_incl - nt;
     for (int q = 0; q < nt; ++q) {
       tile_map[3 * (tb + q) + 0] = tid;
       tile_map[3 * (tb + q) + 1] = off + q * tile_m;
       tile_map[3 * (tb + q) + 2] = min(tile_m, c - q * tile_m);
     }
-    int ub = u_incl - nu;
-    for (int q = 0; unit_map && q < nu; ++q) {
-      unit_map[3 * (ub + q) + 0] = tid;
-      unit_map[3 * (ub + q) + 1] = off + q * unit_pairs;
-      unit_map[3 * (ub + q) + 2] = min(unit_pairs, c - q * unit_pairs);
-    }
+    auto units = [&](const UnitOut& uo, int nu, int u_incl) {
+      const int ub = u_incl - nu;
+      for (int q = 0; q < nu; ++q) {
+        uo.map[3 * (ub + q) + 0] = tid;
+        uo.map[3 * (ub + q) + 1] = off + q * uo.unit_pairs;
+        uo.map[3 * (ub + q) + 2] = min(uo.unit_pairs, c - q * uo.unit_pairs);
+        if (uo.pad) uo.pad[ub + q] = poff + q * uo.unit_pairs;
+      }
+    };
+    if (ug.map) units(ug, nug, sc.v[3]);
+    if (ud.map) units(ud, nud, sc.v[4]);
   }
   if (tid == E - 1) {
     offsets[E] = c_incl;
     *n_tiles = t_incl;
-    if (n_units) *n_units = u_incl;
+    if (ug.map) *ug.count = sc.v[3];
+    if (ud.map) *ud.count = sc.v[4];
     if (n_pad) *n_pad = p_incl;
   }
   __syncthreads();
-  if (split && tid < 2 * (kMaxXcds + 1)) {  // the XCD share boundaries of both passes
-    const int pass = tid / (kMaxXcds + 1), x = tid % (kMaxXcds + 1);
-    const XcdSplit& sp = pass ? split_dn : split_gu;
-    if (x <= sp.n_xcd) sp.bounds[x] = share_bound(sp, x, cum_dec[pass], cum_units, cnt, E, unit_pairs);
-  }
 
   auto place = [&](int ep, int p) {
     int e, rank, group;
@@ -365,13 +323,10 @@ __device__ __attribute__((always_inline)) inline void bin_pairs(const int32_t* _
 }
 
 __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restrict__ topk_idx, int32_t P, int32_t E,
-                                                          int32_t tile_m, int32_t unit_pairs, int32_t* counts,
-                                                          int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map,
-                                                          int32_t* n_tiles, int32_t* unit_map, int32_t* n_units,
-                                                          int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
-                                                          XcdSplit split_gu, XcdSplit split_dn) {
-  bin_pairs(topk_idx, P, E, tile_m, unit_pairs, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units,
-            padded_pair, unit_pad, n_pad, split_gu, split_dn);
+                                                          int32_t tile_m, int32_t* counts, int32_t* offsets,
+                                                          int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
+                                                          int32_t* padded_pair, int32_t* n_pad, UnitOut ug, UnitOut ud) {
+  bin_pairs(topk_idx, P, E, tile_m, counts, offsets, sorted_pair, tile_map, n_tiles, padded_pair, n_pad, ug, ud);
 }
 
 // Routing and binning of a small batch (n <= kFusedRouteMaxTokens) in one workgroup: its waves
@@ -381,17 +336,15 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const int32_t* __restr
 template <int Q>
 __global__ __launch_bounds__(kBinThreads) void route_bin_kernel(const float* __restrict__ logits, int32_t n_part,
                                                                 int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
-                                                                float* topk_w, int32_t tile_m, int32_t unit_pairs,
-                                                                int32_t* counts, int32_t* offsets,
-                                                                int32_t* sorted_pair, int32_t* tile_map,
-                                                                int32_t* n_tiles, int32_t* unit_map, int32_t* n_units,
-                                                                int32_t* padded_pair, int32_t* unit_pad,
-                                                                int32_t* n_pad, XcdSplit split_gu, XcdSplit split_dn) {
+                                                                float* topk_w, int32_t tile_m, int32_t* counts,
+                                                                int32_t* offsets, int32_t* sorted_pair,
+                                                                int32_t* tile_map, int32_t* n_tiles,
+                                                                int32_t* padded_pair, int32_t* n_pad, UnitOut ug,
+                                                                UnitOut ud) {
   const int t = (int)(threadIdx.x >> 6);
   if (t < n) route_token<Q>(logits, n_part, n, E, k, t, topk_idx, topk_w);
   __syncthreads();
-  bin_pairs(topk_idx, n * k, E, tile_m, unit_pairs, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map,
-            n_units, padded_pair, unit_pad, n_pad, split_gu, split_dn);
+  bin_pairs(topk_idx, n * k, E, tile_m, counts, offsets, sorted_pair, tile_map, n_tiles, padded_pair, n_pad, ug, ud);
 }
 
 }  // namespace
@@ -413,48 +366,38 @@ hipError_t launch_route_topk(const float* logits, int32_t n_part, int32_t n, int
 
 namespace {
 
-hipError_t check_splits(const XcdSplit* split_gu, const XcdSplit* split_dn, XcdSplit& sg, XcdSplit& sd) {
-  sg = XcdSplit{};
-  sd = XcdSplit{};
-  if (split_gu && split_dn) {
-    for (const XcdSplit* sp : {split_gu, split_dn})
-      if (!sp->bounds || sp->grid < 1 || sp->n_xcd < 1 || sp->n_xcd > kMaxXcds || sp->row_blocks < 1 ||
-          sp->pairs_per_decode < 1)
-        return hipErrorInvalidValue;
-    sg = *split_gu;
-    sd = *split_dn;
-  }
-  return hipSuccess;
+UnitOut unit_out(const UnitMaps* um, int pass) {
+  if (!um) return UnitOut{1, nullptr, nullptr, nullptr};
+  return UnitOut{um->unit_pairs[pass], um->map[pass], um->pad[pass], um->count[pass]};
+}
+
+bool units_ok(const UnitMaps* um) {
+  if (!um) return true;
+  for (int i = 0; i < 2; ++i)
+    if (!um->map[i] || !um->count[i] || um->unit_pairs[i] < 1 || um->unit_pairs[i] > kUnitMaxPairs) return false;
+  return true;
 }
 
 }  // namespace
 
-hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t unit_pairs,
-                      int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
-                      int32_t* unit_map, int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
-                      const XcdSplit* split_gu, const XcdSplit* split_dn, hipStream_t stream) {
-  XcdSplit sg, sd;
-  const hipError_t e = check_splits(split_gu, split_dn, sg, sd);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bin_kernel, dim3(1), dim3(kBinThreads), 0, stream, topk_idx, n_pairs, E, tile_m, unit_pairs,
-                     counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, padded_pair, unit_pad,
-                     n_pad, sg, sd);
+hipError_t launch_bin(const int32_t* topk_idx, int32_t n_pairs, int32_t E, int32_t tile_m, int32_t* counts,
+                      int32_t* offsets, int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles,
+                      int32_t* padded_pair, int32_t* n_pad, const UnitMaps* units, hipStream_t stream) {
+  if (!units_ok(units)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bin_kernel, dim3(1), dim3(kBinThreads), 0, stream, topk_idx, n_pairs, E, tile_m, counts, offsets,
+                     sorted_pair, tile_map, n_tiles, padded_pair, n_pad, unit_out(units, 0), unit_out(units, 1));
   return hipGetLastError();
 }
 
 hipError_t launch_route_bin(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k, int32_t* topk_idx,
-                            float* topk_w, int32_t tile_m, int32_t unit_pairs, int32_t* counts, int32_t* offsets,
-                            int32_t* sorted_pair, int32_t* tile_map, int32_t* n_tiles, int32_t* unit_map,
-                            int32_t* n_units, int32_t* padded_pair, int32_t* unit_pad, int32_t* n_pad,
-                            const XcdSplit* split_gu, const XcdSplit* split_dn, hipStream_t stream) {
-  if (n < 1 || n > kFusedRouteMaxTokens) return hipErrorInvalidValue;
-  XcdSplit sg, sd;
-  const hipError_t e = check_splits(split_gu, split_dn, sg, sd);
-  if (e != hipSuccess) return e;
+                            float* topk_w, int32_t tile_m, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                            int32_t* tile_map, int32_t* n_tiles, int32_t* padded_pair, int32_t* n_pad,
+                            const UnitMaps* units, hipStream_t stream) {
+  if (n < 1 || n > kFusedRouteMaxTokens || !units_ok(units)) return hipErrorInvalidValue;
   auto kernel = E <= 256 ? route_bin_kernel<4> : E <= 512 ? route_bin_kernel<8> : route_bin_kernel<16>;
   hipLaunchKernelGGL(kernel, dim3(1), dim3(kBinThreads), 0, stream, logits, n_part, n, E, k, topk_idx, topk_w, tile_m,
-                     unit_pairs, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, padded_pair,
-                     unit_pad, n_pad, sg, sd);
+                     counts, offsets, sorted_pair, tile_map, n_tiles, padded_pair, n_pad, unit_out(units, 0),
+                     unit_out(units, 1));
   return hipGetLastError();
 }
 
