@@ -182,20 +182,13 @@ def schedule_figures(counts, shape, arm, sched):
     E, H, I = shape.num_experts, shape.hidden, shape.inter
     woken = int((counts > 0).sum())
     per_expert_bytes = {"gate_up": 2 * I * H // 4 + 2 * I * 2, "down": H * I // 4 + H * 2}
-    units = [(c + 63) // 64 for c in counts.tolist()]      # the router's units hold <= 64 pairs
 
-    def decodes_for(per):
-        d = 0
-        for c in counts.tolist():
-            while c > 0:
-                L = min(64, c)
-                d += (L + per - 1) // per
-                c -= L
-        return d
+    def decodes_for(per):  # each pass's units hold up to `per` pairs: one decode each
+        return int(sum((c + per - 1) // per for c in counts.tolist()))
 
     dec = {"gate_up": decodes_for(sched["gate_up"]["pairs_per_decode"]),
            "down": decodes_for(sched["down"]["pairs_per_decode"])}
-    return {"woken": woken, "units": int(sum(units)), "decodes": dec,
+    return {"woken": woken, "units": dict(dec), "decodes": dec,
             "bytes": {k: woken * v for k, v in per_expert_bytes.items()},
             "symbols_min": {"gate_up": woken * 2 * I * H, "down": woken * H * I},
             "symbols_sched": {"gate_up": dec["gate_up"] * 2 * I * H, "down": dec["down"] * H * I},
