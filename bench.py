@@ -424,6 +424,14 @@ def main():
                                 "frac_model": gu_syms / LDS_GATHER_PEAK, "peak_measured": gather_measured,
                                 "frac_measured": gu_syms / gather_measured,
                                 "valu_peak": DECODE_VALU_PEAK_SYMS, "frac_valu": gu_syms / DECODE_VALU_PEAK_SYMS},
+            # MFMA work of the layer (g, u and y: 2 n k H I flops each) against
+            # the dense bf16 peak: the contraction is thin, so this stays a few percent at most
+            "mfma": {"flops": 6.0 * s.n_tokens * s.top_k * s.hidden * s.inter,
+                     "layer_tflops": 6.0 * s.n_tokens * s.top_k * s.hidden * s.inter / layer_gpu_s / 1e12,
+                     "layer_frac": 6.0 * s.n_tokens * s.top_k * s.hidden * s.inter / layer_gpu_s / 1e12
+                     / MFMA_BF16_PEAK_TFLOPS,
+                     "gate_up_frac": 4.0 * s.n_tokens * s.top_k * s.hidden * s.inter / gu_s / 1e12
+                     / MFMA_BF16_PEAK_TFLOPS},
             "schedule": sched,
             "router_gemm": router,
             "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "dequant_launches",
