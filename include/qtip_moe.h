@@ -297,7 +297,9 @@ qtip_status qtip_arch_witness(int device, void* stream);
 /* Per-stage timing.  qtip_moe_profile_enable(plan, capacity) creates capacity x 6 HIP events
  * (capacity <= 4096; 0 disables and frees them); every later forward on the plan records an
  * event before its first kernel and after each of its five kernels (route, bin, gate+up,
- * down, combine) on the forward's stream, cycling through `capacity` slots.
+ * down, combine) on the forward's stream, cycling through `capacity` slots.  Batches of up to
+ * 16 tokens are routed and binned by one kernel: their "route" stage holds both and their
+ * "bin" stage only the activation packing, if any (the "bin" stage always includes it).
  * qtip_moe_profile_read waits for the recorded events, writes the summed milliseconds per
  * stage over the last min(forwards, capacity) forwards into stage_ms[5] (host), their count
  * into n_forwards, and clears the record.  Enabling creates events, so do it outside capture. */

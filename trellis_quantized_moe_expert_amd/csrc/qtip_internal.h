@@ -16,7 +16,7 @@ enum ExpertVariant { kVariantDefault = 0, kVariantCount = 9 };
 constexpr int kExpertWaves = 16;       // waves of the binning workgroup
 constexpr int kBinCached = 8;          // groups of 64 expert ids a binning wave keeps in registers
 constexpr int kKBlock = 128;           // inputs per K block: 4 lane groups x 32-symbol runs
-constexpr int kUnitMaxPairs = 64;      // pairs sharing one decode (4 MFMA row blocks of 16)
+constexpr int kUnitMaxPairs = 64;      // most pairs one decode serves (4 MFMA row blocks of 16)
 constexpr int kRouteWaves = 4;         // tokens per route workgroup (one wave each)
 constexpr int kBinThreads = 1024;      // binning runs in one workgroup (16 waves)
 constexpr int kMaxExperts = 1024;
