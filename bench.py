@@ -129,6 +129,34 @@ def timed(runner, steps, warmup, profile=True):
     return {"wall_s": t1 - t0, "gpu_ms": ev0.elapsed_time(ev1), "stats": stats, "prof": prof}
 
 
+def measure_graph(runner, steps, warmup=5):
+    """The same forward captured once in a HIP graph and replayed `steps` times (HIP events on
+    the replay stream): what a serving loop that captures the layer sees, without per-kernel
+    launch costs.  Reported beside the eager figure, not as it."""
+    import torch
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            runner.q.qtip_moe_forward(runner.plan, runner.w, runner.tok.x, runner.tok.logits, runner.n, runner.out,
+                                      runner.ws, runner.ws.numel(), cap)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    del g
+    return {"ms_per_step": ms, "tokens_per_s": runner.n / (ms * 1e-3), "steps": steps}
+
+
 def measure_router(runner, inp, calls=200, layers=50):
     """Router GEMM (qtip_moe_router_logits) per-call time from HIP events on the launch stream,
     and the layer from hidden states (qtip_moe_forward_hidden) in tokens/s, on this batch."""
@@ -376,6 +404,7 @@ def main():
     counts, n_tiles = runner.routing_counts()
     sched = runner.q.qtip_moe_plan_schedule(runner.plan, s.n_tokens)
     router = measure_router(runner, inp)
+    graph = measure_graph(runner, args.steps)
     runner.close()
 
     if res["wall_s"] <= 0 or res["prof"]["n_forwards"] <= 0:
@@ -433,6 +462,7 @@ def main():
                      "gate_up_frac": 4.0 * s.n_tokens * s.top_k * s.hidden * s.inter / gu_s / 1e12
                      / MFMA_BF16_PEAK_TFLOPS},
             "schedule": sched,
+            "graph_replay": graph,
             "router_gemm": router,
             "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "dequant_launches",
                                                          "route_launches", "combine_launches", "router_launches")},
