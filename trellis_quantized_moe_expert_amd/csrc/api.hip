@@ -264,20 +264,27 @@ int persistent_grid(int dev, size_t max_tasks, int waves) {
 // tasks: one workgroup per CU with the configuration's waves when the tasks fill them.  With
 // fewer tasks, the GEMV arm (spread) still takes a workgroup on as many CUs as there are tasks,
 // each with fewer waves (a CU's LUT gathers are its own: measured +35 % per layer at one token,
-// +7 % at two); the other arms keep full workgroups on fewer CUs.
+// +7 % at two); the other arms keep full workgroups on fewer CUs.  Where a workgroup would then
+// hold few waves, the GEMV arm can also split each task's kblocks input blocks over ksplit waves
+// (a power of 2, at least 2 blocks each) to fill its configuration's waves.
 struct LaunchShape {
-  int grid, waves;
+  int grid, waves, ksplit;
 };
 
-LaunchShape persistent_shape(int dev, size_t max_tasks, int max_waves, bool spread) {
+LaunchShape persistent_shape(int dev, size_t max_tasks, int max_waves, bool spread, bool input_split = false,
+                             int kblocks = 1) {
   const size_t cus = (size_t)g_cu_count[dev].load(std::memory_order_acquire);
-  if (!spread || max_tasks >= cus * (size_t)max_waves) return {persistent_grid(dev, max_tasks, max_waves), max_waves};
-  size_t waves = (max_tasks + cus - 1) / cus;
-  if (waves < 1) waves = 1;
-  size_t grid = (max_tasks + waves - 1) / waves;
+  if (!spread || max_tasks >= cus * (size_t)max_waves) return {persistent_grid(dev, max_tasks, max_waves), max_waves, 1};
+  size_t tpw = (max_tasks + cus - 1) / cus;  // tasks per workgroup
+  if (tpw < 1) tpw = 1;
+  size_t grid = (max_tasks + tpw - 1) / tpw;
   if (grid < 1) grid = 1;
   if (grid > cus) grid = cus;
-  return {(int)grid, (int)waves};
+  int split = 1;
+  while (input_split && tpw * (size_t)(2 * split) <= (size_t)max_waves && kblocks % (2 * split) == 0 &&
+         kblocks / (2 * split) >= 2)
+    split *= 2;
+  return {(int)grid, (int)tpw * split, split};
 }
 
 qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
@@ -656,10 +663,12 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   um.pad[0] = frag ? reinterpret_cast<int32_t*>(ws + L.unit_pad) : nullptr;
   um.pad[1] = frag ? reinterpret_cast<int32_t*>(ws + L.unit_pad) + L.max_units : nullptr;
   const bool spread = karm == kArmGemv;
-  const LaunchShape shape_gu = persistent_shape(
-      dev, max_units_for(d, n_tokens, vi_gu.pairs_per_decode) * (d.inter / vi_gu.rows_per_task), vi_gu.waves, spread);
-  const LaunchShape shape_dn = persistent_shape(
-      dev, max_units_for(d, n_tokens, vi_dn.pairs_per_decode) * (d.hidden / vi_dn.rows_per_task), vi_dn.waves, spread);
+  const LaunchShape shape_gu =
+      persistent_shape(dev, max_units_for(d, n_tokens, vi_gu.pairs_per_decode) * (d.inter / vi_gu.rows_per_task),
+                       vi_gu.waves, spread, vi_gu.input_split, d.hidden / kKBlock);
+  const LaunchShape shape_dn =
+      persistent_shape(dev, max_units_for(d, n_tokens, vi_dn.pairs_per_decode) * (d.hidden / vi_dn.rows_per_task),
+                       vi_dn.waves, spread, vi_dn.input_split, d.inter / kKBlock);
   if (n_tokens <= kFusedRouteMaxTokens) {
     // one workgroup routes and bins a small batch (the "route" stage then holds both)
     e = launch_route_bin(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, plan->tile_m, counts, offsets,
@@ -744,6 +753,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     gu.act = xs;
     gu.act_frag = 1;
   }
+  gu.ksplit = shape_gu.ksplit;
   e = launch_expert(kModeGateUp, karm, kv_gu, gu, shape_gu.grid, shape_gu.waves, st);
   if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
   if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
@@ -771,6 +781,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     dn.act_frag = 1;
     dn.n_pad_max = pp_max;
   }
+  dn.ksplit = shape_dn.ksplit;
   e = launch_expert(kModeSingle, karm, kv_dn, dn, shape_dn.grid, shape_dn.waves, st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");

@@ -80,20 +80,22 @@ __device__ inline void fill_lut(uint16_t* lut_s, const uint16_t* __restrict__ lu
   __syncthreads();
 }
 
-// The same with any workgroup size (a launch with fewer waves than its configuration's).
+// The same with any workgroup size (a launch with fewer waves than its configuration's), four
+// loads of a thread in flight at a time (measured: sixteen made the one-token down pass slower).
 __device__ inline void fill_lut_any(uint16_t* lut_s, const uint16_t* __restrict__ lut_g) {
   constexpr int kVec = kLutEntries / 8;
+  constexpr int kBatch = 4;
   const uint4* src = reinterpret_cast<const uint4*>(lut_g);
   uint4* dst = reinterpret_cast<uint4*>(lut_s);
-  for (int i0 = 0; i0 < kVec; i0 += 4 * (int)blockDim.x) {
-    uint4 v[4];
+  for (int i0 = 0; i0 < kVec; i0 += kBatch * (int)blockDim.x) {
+    uint4 v[kBatch];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kBatch; ++it) {
       const int i = i0 + (int)threadIdx.x + it * (int)blockDim.x;
       if (i < kVec) v[it] = src[i];
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kBatch; ++it) {
       const int i = i0 + (int)threadIdx.x + it * (int)blockDim.x;
       if (i < kVec) dst[i] = uint4{lut_bf16x2(v[it].x), lut_bf16x2(v[it].y), lut_bf16x2(v[it].z), lut_bf16x2(v[it].w)};
     }
@@ -478,8 +480,14 @@ __device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const U
 }
 
 // GEMV arm: NQ pairs x NT row blocks of 16 outputs share one decode; VALU bf16 dot products.
-template <int MODE, int NQ, int NT, bool APRE, bool X3 = false>
-__device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
+// GEMV arm body over the 128-input blocks [kb_lo, kb_hi) of a task (unit un, rows r0..): each
+// lane accumulates its row's dot products with the NQ pairs over its quarter of each block
+// into acc0 (gate or the single matrix) and acc1 (up).  A range holding the row's last block
+// takes it first (its look-ahead wraps to the row start), then blocks kb_lo.. in order; every
+// other block's run is one in-row load.
+template <int MODE, int NQ, int NT, bool APRE, bool X3>
+__device__ inline void gemv_range(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0, int kb_lo,
+                                  int kb_hi, float (&acc0)[NQ][NT], float (&acc1)[NQ][NT]) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int row_bytes = p.cols >> 2;
@@ -490,10 +498,13 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
   const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
   const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
+  const bool wraps = kb_hi == kblocks;
+  const int len = kb_hi - kb_lo;
+  // the i-th block of the range's order
+  auto block_of = [&](int i) { return wraps ? (i == 0 ? kblocks - 1 : kb_lo + i - 1) : kb_lo + i; };
 
   uint32_t xoff[NQ];  // every lane of group g reads the same 16 bytes of pair q
   act_rows<NQ>(p, un, 0, 1, g, xoff);
-  float acc0[NQ][NT], acc1[NQ][NT];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
 #pragma unroll
@@ -501,13 +512,22 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
   }
 
   u32x4 xn[NQ][4];
-  if (APRE) load_a_block<NQ>(xn, p.act, xoff, kblocks - 1);
-  const int ob_last = (kblocks - 1) * 32 + g * 8;
-  RunSet<NT> n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
-  for (int i = 0; i < kblocks; ++i) {
-    const int kb = block_at(i, kblocks);
-    const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
+  if (APRE) load_a_block<NQ>(xn, p.act, xoff, block_of(0));
+  RunSet<NT> n0, n1;
+  if (wraps) {
+    const int ob_last = (kblocks - 1) * 32 + g * 8;
+    n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
+    n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
+  } else {
+    const int ob = kb_lo * 32 + g * 8;
+    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob);
+    n1 = (MODE == kModeGateUp) ? load_runs<NT, false>(base1, roff, nt_stride, ob) : n0;
+  }
+  for (int i = 0; i < len; ++i) {
+    const int kb = block_of(i);
+    // the next block; after the last, the range's first in-row block again (unused; 8 bytes
+    // back for lane group 3 where a one-block row would otherwise be left)
+    const int kn = i + 1 < len ? block_of(i + 1) : kb_lo;
     u32x4 x[NQ][4];
     if (APRE) {
 #pragma unroll
@@ -521,7 +541,7 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
     }
     const RunSet<NT> c0 = n0, c1 = n1;
     const int ob = kn * 32 + g * 8;
-    const uint32_t back = (i + 1 < kblocks || g != 3) ? 0u : 8u;
+    const uint32_t back = (i + 1 < len || g != 3 || kn + 1 < kblocks) ? 0u : 8u;
     n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
     if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
 #pragma unroll
@@ -546,12 +566,20 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
       }
     }
   }
+}
+
+// GEMV arm: sum the four lane groups' partial dot products of each row (lanes j, j+16, j+32,
+// j+48) and store the NQ pairs' outputs.
+template <int MODE, int NQ, int NT>
+__device__ inline void gemv_epilogue(const ExpertParams& p, const Unit& un, int r0, const float (&acc0)[NQ][NT],
+                                     const float (&acc1)[NQ][NT]) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = r0 + 16 * nt + j;
     const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
     const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
-    // sum the four lane groups (lanes j, j+16, j+32, j+48 hold one row's partial sums)
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       float a0 = acc0[q][nt];
@@ -567,6 +595,64 @@ __device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit
     }
   }
 }
+
+// GEMV arm: the NQ pairs of a unit chunk against 16*NT rows of its expert (the per-pair dot
+// products on the VALU, the decode in registers from the LDS LUT).
+template <int MODE, int NQ, int NT, bool APRE, bool X3 = false>
+__device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
+  float acc0[NQ][NT], acc1[NQ][NT];
+  gemv_range<MODE, NQ, NT, APRE, X3>(p, lut, un, r0, 0, p.cols / kKBlock, acc0, acc1);
+  gemv_epilogue<MODE, NQ, NT>(p, un, r0, acc0, acc1);
+}
+
+// GEMV arm with each task's inputs split over S waves of a workgroup (ExpertParams::ksplit),
+// for launches with fewer tasks than the GPU has wave slots: wave s of a task's group decodes
+// blocks [s K/S, (s+1) K/S) and leaves its partial sums in LDS; after a barrier the group's first
+// wave adds the S partials in ascending s and stores the outputs.
+template <int MODE, int NQ, int NT, bool APRE, bool X3>
+__device__ inline void gemv_part(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0, int kb_lo,
+                                 int kb_hi, float* slot) {
+  float acc0[NQ][NT], acc1[NQ][NT];
+  gemv_range<MODE, NQ, NT, APRE, X3>(p, lut, un, r0, kb_lo, kb_hi, acc0, acc1);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      slot[((q * NT + nt) * 2 + 0) * 64 + lane] = acc0[q][nt];
+      if (MODE == kModeGateUp) slot[((q * NT + nt) * 2 + 1) * 64 + lane] = acc1[q][nt];
+    }
+  }
+}
+
+template <int MODE, int NQ, int NT>
+__device__ inline void gemv_finish(const ExpertParams& p, const Unit& un, int r0, const float* slots, int slot_floats,
+                                   int S) {
+  const int lane = threadIdx.x & 63;
+  float acc0[NQ][NT], acc1[NQ][NT];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float a0 = 0.f, a1 = 0.f;
+      for (int w = 0; w < S; ++w) {
+        a0 += slots[w * slot_floats + ((q * NT + nt) * 2 + 0) * 64 + lane];
+        if (MODE == kModeGateUp) a1 += slots[w * slot_floats + ((q * NT + nt) * 2 + 1) * 64 + lane];
+      }
+      acc0[q][nt] = a0;
+      acc1[q][nt] = a1;
+    }
+  }
+  gemv_epilogue<MODE, NQ, NT>(p, un, r0, acc0, acc1);
+}
+
+// LDS the split-input GEMV path needs beside the LUT: every wave's partial sums.
+template <class CFG>
+struct GemvSplit {
+  static constexpr int kSlotFloats = CFG::kGPairs * CFG::kNT * 2 * 64;
+  static constexpr int kFloats = CFG::kWaves * kSlotFloats;
+  static constexpr bool kFits = kFloats * 4 <= 160 * 1024 - kLutEntries * 2;
+};
 
 // Kernel configurations (the plan's `variant`): waves per workgroup, 16-row output blocks
 // per task (NT), pairs per decode on the grouped arm (in 16-pair MFMA row blocks, NSUB) and
@@ -640,6 +726,55 @@ __device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, cons
   }
 }
 
+// The GEMV arm's task loop with split inputs: a workgroup of tpw x S waves takes tpw tasks per
+// round, S waves each (every wave runs the same rounds, so the barriers line up).
+template <int MODE, class CFG>
+__device__ inline void gemv_split_tasks(const ExpertParams& p, const uint16_t* lut, float* part) {
+  constexpr int NT = CFG::kNT;
+  constexpr bool AP = CFG::kAPre;
+  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
+  constexpr int kSlot = GemvSplit<CFG>::kSlotFloats;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = p.ksplit, tpw = (int)(blockDim.x >> 6) / S;
+  const int q = wave / S, sidx = wave % S;
+  const int kper = p.cols / kKBlock / S;
+  const int n_units = p.n_units_dev ? __builtin_amdgcn_readfirstlane(*p.n_units_dev) : p.n_units_host;
+  const int nblocks = p.rows / CFG::kRows;
+  const long total = (long)n_units * nblocks;
+  float* mine = part + wave * kSlot;
+  for (long base = (long)blockIdx.x * tpw; base < total; base += (long)gridDim.x * tpw) {
+    const long t = base + q;
+    Unit un{};
+    const bool ok = t < total && read_unit(p, (int)(t / nblocks), un);
+    const int r0 = (int)(t % nblocks) * CFG::kRows;
+    const bool one = ok && un.len <= CFG::kGPairs;  // a single chunk (the layer's own units)
+    const int lo = sidx * kper, hi = lo + kper;
+    if (one) {
+      switch (un.len) {
+        case 1: gemv_part<MODE, 1, NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
+        case 2: if (CFG::kGPairs >= 2) gemv_part<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
+        case 3: if (CFG::kGPairs >= 3) gemv_part<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
+        default: if (CFG::kGPairs >= 4) gemv_part<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
+      }
+    }
+    __syncthreads();
+    if (ok && sidx == 0) {
+      const float* slots = part + (q * S) * kSlot;
+      if (one) {
+        switch (un.len) {
+          case 1: gemv_finish<MODE, 1, NT>(p, un, r0, slots, kSlot, S); break;
+          case 2: if (CFG::kGPairs >= 2) gemv_finish<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT>(p, un, r0, slots, kSlot, S); break;
+          case 3: if (CFG::kGPairs >= 3) gemv_finish<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT>(p, un, r0, slots, kSlot, S); break;
+          default: if (CFG::kGPairs >= 4) gemv_finish<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT>(p, un, r0, slots, kSlot, S); break;
+        }
+      } else {
+        run_task<MODE, kArmGemv, CFG, false>(p, lut, un, r0);  // a longer unit: its group's first wave alone
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // SPREAD: the launch may run fewer waves per workgroup than the configuration's (a small
 // batch spread over more CUs).
 template <int MODE, int ARM, class CFG, bool FRAG, bool SPREAD>
@@ -687,6 +822,13 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
     __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
     if constexpr (SPREAD) fill_lut_any(lut_s, p.lut);
     else fill_lut<CFG::kWaves * 64>(lut_s, p.lut);
+    if constexpr (SPREAD && ARM == kArmGemv && GemvSplit<CFG>::kFits) {
+      if (p.ksplit > 1) {
+        __shared__ float part[GemvSplit<CFG>::kFloats];
+        gemv_split_tasks<MODE, CFG>(p, lut_s, part);
+        return;
+      }
+    }
     expert_tasks<MODE, ARM, CFG, FRAG, SPREAD>(p, lut_s);
   }
 }
@@ -886,11 +1028,13 @@ struct CfgInfo {
       v.waves = CfgDense::kWaves;
       v.rows_per_task = CfgDense::kRows;
       v.pairs_per_decode = CfgDense::kNSub * 16;
+      v.input_split = false;
       return;
     }
     v.waves = CFG::kWaves;
     v.rows_per_task = CFG::kRows;
     v.pairs_per_decode = arm == kArmGrouped ? CFG::kNSub * 16 : CFG::kGPairs;
+    v.input_split = arm == kArmGemv && GemvSplit<CFG>::kFits;
   }
 };
 

@@ -60,6 +60,8 @@ struct ExpertParams {
   int32_t n_pad_max;            // padded positions the fragment-order buffers hold (with unit_pad)
   const uint16_t* dense0;       // dequantize arm: [E] x rows x cols bf16 weights in fragment order (gate, or the single matrix)
   const uint16_t* dense1;       // dequantize arm: the same for the up weights (fused pass only)
+  int32_t ksplit;               // GEMV arm launched with fewer waves than its configuration's: waves
+                                // sharing one task's inputs (a power of 2 dividing cols/128), or <= 1
 };
 
 enum ExpertMode { kModeGateUp = 0, kModeSingle = 1 };
@@ -69,6 +71,7 @@ struct VariantInfo {
   int waves;             // wave64 per workgroup
   int rows_per_task;     // output rows per wave task (rows must be a multiple of it)
   int pairs_per_decode;  // binned pairs sharing one decode of an expert's rows
+  bool input_split;      // GEMV arm: can split a task's inputs over waves (ExpertParams::ksplit)
 };
 // `variant` in 1..8 (the plan resolves 0).  variant_info returns false for other values.
 bool variant_info(int variant, int arm, VariantInfo& v);
