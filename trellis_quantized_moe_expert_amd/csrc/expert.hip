@@ -12,19 +12,21 @@
 //
 // gfx950 design (what differs from the pages' CUDA kernels):
 //  - The 65536-entry LUT, narrowed to bf16, lives in LDS (128 KiB of the 160 KiB); one
-//    1024-thread workgroup per CU, persistent over wave-sized tasks.  Random 2-byte LUT
-//    gathers are the decode's bottleneck, so LDS carries nothing else: decoded weights go
-//    straight into MFMA B-operand registers instead of through an LDS weight tile, and
-//    activations are read from global memory (L2-resident) into A-operand registers.
-//  - A wave task is one unit (up to 64 binned pairs of one expert, i.e. several m-tiles
-//    sharing one decode) x 16 output rows x all inputs.  Lane (j = lane%16, g = lane/16)
-//    decodes row j; within each 128-input block lane group g owns the contiguous 32-symbol
-//    run [32g, 32g+32), loaded as 8 bytes plus one look-ahead dword (the next 7 symbols,
-//    wrapping to the row start at the row end: the window is circular).  The contraction
-//    index is permuted accordingly: MFMA step s of a block pairs K slot 8g+t with input
-//    32g + 8s + t, for both operands, which leaves the dot products unchanged.
+//    workgroup of 8, 12 or 16 waves per CU, persistent over wave-sized tasks.  Random 2-byte LUT
+//    gathers are the decode's bottleneck, so decoded weights go straight into MFMA B-operand
+//    registers instead of through an LDS weight tile, and activations are read from global
+//    memory (L2-resident) into A-operand registers.  (Small GEMV launches also keep partial
+//    sums in the rest of LDS; see gemv_split_tasks.)
+//  - A wave task is one decode unit (the binned pairs of one expert that one decode serves:
+//    up to 16, 32 or 64 on the grouped arm, 1 to 4 on the GEMV arm) x 16 NT output rows x all
+//    inputs.  Lane (j = lane%16, g = lane/16) decodes row j of each 16-row block; within each
+//    128-input block lane group g owns the contiguous 32-symbol run [32g, 32g+32), loaded as
+//    8 bytes plus one look-ahead dword (the next 7 symbols, wrapping to the row start at the
+//    row end: the window is circular).  The contraction index is permuted accordingly: MFMA
+//    step s of a block pairs K slot 8g+t with input 32g + 8s + t, for both operands, which
+//    leaves the dot products unchanged.
 //  - Grouped arm: v_mfma_f32_16x16x32_bf16 per 16-pair row block.  GEMV arm: the same
-//    decoded registers feed VALU bf16 dot products per pair (8 pairs per decode).
+//    decoded registers feed VALU bf16 dot products per pair.
 #include "qtip_internal.h"
 
 namespace qtip {

@@ -10,7 +10,7 @@ namespace qtip {
 
 constexpr int kLutEntries = 65536;     // 16-bit trellis state -> one LUT entry
 // The LUT fills 128 KiB of LDS, so one expert workgroup per CU is resident; the kernel
-// variant fixes its size (16 or 8 wave64).
+// variant fixes its size (8, 12 or 16 wave64; a small GEMV launch may run fewer).
 // Variants 1..8 are fixed kernel configurations (see variant_info); 0 lets the plan choose.
 enum ExpertVariant { kVariantDefault = 0, kVariantCount = 9 };
 constexpr int kExpertWaves = 16;       // waves of the binning workgroup
