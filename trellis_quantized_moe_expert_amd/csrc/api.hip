@@ -65,10 +65,10 @@ namespace {
 // (bench.py --sweep over variants) and chosen from host scalars only, so the choice is safe
 // during graph capture.
 //  * Grouped arm, by the closed-form pairs per woken expert (ppe).  Fused pass: 16 waves of
-//    16-row tasks below 4 (many short tasks keep every CU busy), 12 waves of 32-row tasks below
-//    20 (each activation fragment feeds more MFMAs), 8 waves of 32-row tasks sharing a decode
-//    across four 16-pair blocks from 20.  Down pass: 16 waves of 32-row tasks below 3, 12
-//    waves of 64-row tasks with 12-byte code loads from 3.
+//    16-row tasks below 4 (many short tasks keep every CU busy), then 12 waves of 32-row tasks
+//    sharing a decode across three 16-pair blocks (each activation fragment feeds more MFMAs,
+//    and an expert with up to 48 pairs is decoded once).  Down pass: 16 waves of 32-row tasks
+//    below 3, 12 waves of 64-row tasks with 12-byte code loads from 3.
 //  * GEMV arm, by the expected task count: 16-row tasks until there are enough 32-row tasks
 //    to give each of the 2048 wave slots of a 256-CU, 8-wave launch one.
 int kernel_arm(int32_t arm) {
@@ -86,7 +86,7 @@ int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_to
     return tall_tasks >= 2048.0 ? 4 : 2;
   }
   const double ppe = fill_pairs_per_woken_expert(n, k, E);
-  if (mode == kModeGateUp) return ppe < 4.0 ? 1 : (ppe < 20.0 ? 6 : 4);
+  if (mode == kModeGateUp) return ppe < 4.0 ? 1 : 9;
   return ppe < 3.0 ? 3 : 7;
 }
 

@@ -18,7 +18,7 @@
 //    memory (L2-resident) into A-operand registers.  (Small GEMV launches also keep partial
 //    sums in the rest of LDS; see gemv_split_tasks.)
 //  - A wave task is one decode unit (the binned pairs of one expert that one decode serves:
-//    up to 16, 32 or 64 on the grouped arm, 1 to 4 on the GEMV arm) x 16 NT output rows x all
+//    up to 16, 32, 48 or 64 on the grouped arm, 1 to 4 on the GEMV arm) x 16 NT output rows x all
 //    inputs.  Lane (j = lane%16, g = lane/16) decodes row j of each 16-row block; within each
 //    128-input block lane group g owns the contiguous 32-symbol run [32g, 32g+32), loaded as
 //    8 bytes plus one look-ahead dword (the next 7 symbols, wrapping to the row start at the
@@ -665,8 +665,9 @@ struct ExpertCfg {
   static constexpr int kWaves = WAVES, kNT = NT, kNSub = NSUB, kGPairs = GPAIRS;
   static constexpr int kRows = 16 * NT;
   // Activation double-buffering where the register budget allows it: 512 VGPRs per SIMD lane
-  // shared by WAVES/4 waves (168 at 12 waves, where the 4-block task would spill).
-  static constexpr bool kAPre = WAVES <= 8 || NT <= 2;
+  // shared by WAVES/4 waves (168 at 12 waves, where the 4-block task, or three 16-pair blocks
+  // per decode, would spill).
+  static constexpr bool kAPre = WAVES <= 8 || (NT <= 2 && NSUB <= 2);
   // 12-byte code loads in the down pass: measured faster with 12 waves of 64-row tasks (fewer
   // vector-memory accesses where they compete with the LUT gathers), slower with 16 waves.
   static constexpr bool kX3Down = WAVES == 12 && NT == 4;
@@ -681,6 +682,8 @@ using Cfg7 = ExpertCfg<12, 4, 2, 2>;
 // One decode per 16-pair m-tile (no sharing across m-tiles): the pages' grouped-kernel
 // schedule, kept to measure what sharing a decode across m-tiles is worth.
 using Cfg8 = ExpertCfg<16, 1, 1, 1>;
+// 12 waves of 32-row tasks sharing a decode across three 16-pair blocks (48 pairs).
+using Cfg9 = ExpertCfg<12, 2, 3, 3>;
 
 // The grouped body specialised for the chunk's exact number of 16-pair row blocks.
 template <int MODE, class CFG, bool FRAG>
@@ -1050,6 +1053,7 @@ bool variant_info(int variant, int arm, VariantInfo& v) {
     case 6: CfgInfo<Cfg6>::get(arm, v); return true;
     case 7: CfgInfo<Cfg7>::get(arm, v); return true;
     case 8: CfgInfo<Cfg8>::get(arm, v); return true;
+    case 9: CfgInfo<Cfg9>::get(arm, v); return true;
     default: return false;
   }
 }
@@ -1065,6 +1069,7 @@ hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, 
     case 6: return launch_cfg<Cfg6>(mode, arm, p, grid, waves, stream);
     case 7: return launch_cfg<Cfg7>(mode, arm, p, grid, waves, stream);
     case 8: return launch_cfg<Cfg8>(mode, arm, p, grid, waves, stream);
+    case 9: return launch_cfg<Cfg9>(mode, arm, p, grid, waves, stream);
     default: return hipErrorInvalidValue;
   }
 }
