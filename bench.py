@@ -351,7 +351,7 @@ def main():
     ap.add_argument("--workload", default="v4_decode_n32")
     ap.add_argument("--arm", choices=["auto", "gemv", "grouped", "dequant"], default="auto")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
-    ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 = the plan's choice, 1..9 fixed; see qtip_moe_plan_schedule)")
+    ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 = the plan's choice, 1..10 fixed; see qtip_moe_plan_schedule)")
     ap.add_argument("--cpu-sample", type=int, default=6, help="tokens the CPU oracle is timed on, about 10 s (0: skip)")
     ap.add_argument("--sweep", metavar="PATH", default=None)
     ap.add_argument("--sweep-arms", default="gemv,grouped")

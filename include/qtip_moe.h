@@ -100,8 +100,9 @@ typedef struct qtip_moe_desc {
   int32_t inter;        /* I: gate/up outputs and down inputs; multiple of 128 */
   int32_t max_tokens;   /* largest n a forward accepts (sizes the workspace), >= 1 */
   int32_t arm_override; /* QTIP_ARM_AUTO (predicate), _GEMV, _GROUPED or _DEQUANT (pins the arm) */
-  int32_t variant;      /* expert kernel configuration 1..9 for both passes, or 0 = chosen per arm,
-                           pass and n by the plan (qtip_moe_plan_schedule reports it);
+  int32_t variant;      /* expert kernel configuration 1..10 for both passes (10 is a down-pass
+                           shape: with it the grouped arm's fused pass runs 9), or 0 = chosen per
+                           arm, pass and n by the plan (qtip_moe_plan_schedule reports it);
                            unknown: warning, 0 kept */
   int32_t out_dtype;    /* QTIP_OUT_BF16 or QTIP_OUT_F32 */
   int32_t tile_m;       /* m-tile height of the tile map: 0 = default (16, the MFMA M); else 16, 32, 64 */
@@ -170,7 +171,7 @@ qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m /*host*/, s
  * expert passes, the kernel configuration and its shape): the pages' schedule query, so
  * callers and benchmarks read what runs. */
 typedef struct qtip_moe_kernel_shape {
-  int32_t variant;             /* kernel configuration 1..9 actually launched */
+  int32_t variant;             /* kernel configuration 1..10 actually launched */
   int32_t waves_per_workgroup; /* wave64 per (persistent, one-per-CU) workgroup */
   int32_t rows_per_task;       /* output rows each wave decodes per task (16, 32 or 64) */
   int32_t pairs_per_decode;    /* binned pairs of one expert that share one decode of its rows */

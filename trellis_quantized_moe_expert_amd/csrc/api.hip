@@ -68,7 +68,8 @@ namespace {
 //    16-row tasks below 4 (many short tasks keep every CU busy), then 12 waves of 32-row tasks
 //    sharing a decode across three 16-pair blocks (each activation fragment feeds more MFMAs,
 //    and an expert with up to 48 pairs is decoded once).  Down pass: 16 waves of 32-row tasks
-//    below 3, 12 waves of 64-row tasks with 12-byte code loads from 3.
+//    below 3, 12 waves of 64-row tasks with 12-byte code loads from 3, sharing a decode across
+//    three 16-pair blocks from 4.
 //  * GEMV arm, by the expected task count: 16-row tasks until there are enough 32-row tasks
 //    to give each of the 2048 wave slots of a 256-CU, 8-wave launch one.
 int kernel_arm(int32_t arm) {
@@ -77,7 +78,11 @@ int kernel_arm(int32_t arm) {
 
 int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_tokens) {
   if (arm == kArmDense) return 3;  // the dequantize arm has one configuration
-  if (plan->d.variant != kVariantDefault) return plan->d.variant;
+  if (plan->d.variant != kVariantDefault) {
+    // variant 10 is a down-pass shape; its fused grouped task would spill, so that pass runs 9
+    if (plan->d.variant == 10 && mode == kModeGateUp && arm == kArmGrouped) return 9;
+    return plan->d.variant;
+  }
   const int32_t E = plan->d.num_experts, k = plan->d.top_k;
   const int32_t n = n_tokens >= 1 ? n_tokens : 1;
   if (arm == kArmGemv) {
@@ -87,7 +92,7 @@ int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_to
   }
   const double ppe = fill_pairs_per_woken_expert(n, k, E);
   if (mode == kModeGateUp) return ppe < 4.0 ? 1 : 9;
-  return ppe < 3.0 ? 3 : 7;
+  return ppe < 3.0 ? 3 : (ppe < 4.0 ? 7 : 10);
 }
 
 // A variant whose task height does not divide `rows` falls back to the next shorter task of the

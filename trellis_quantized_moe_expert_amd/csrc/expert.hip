@@ -671,6 +671,9 @@ struct ExpertCfg {
   // 12-byte code loads in the down pass: measured faster with 12 waves of 64-row tasks (fewer
   // vector-memory accesses where they compete with the LUT gathers), slower with 16 waves.
   static constexpr bool kX3Down = WAVES == 12 && NT == 4;
+  // The fused grouped task of 64 rows x three 16-pair blocks would spill heavily at 12 waves;
+  // that configuration serves the down pass only (the plan runs the fused pass as 32-row tasks).
+  static constexpr bool kGroupedFused = !(NT == 4 && NSUB >= 3);
 };
 using Cfg1 = ExpertCfg<16, 1, 2, 2>;
 using Cfg2 = ExpertCfg<8, 1, 4, 4>;
@@ -684,6 +687,9 @@ using Cfg7 = ExpertCfg<12, 4, 2, 2>;
 using Cfg8 = ExpertCfg<16, 1, 1, 1>;
 // 12 waves of 32-row tasks sharing a decode across three 16-pair blocks (48 pairs).
 using Cfg9 = ExpertCfg<12, 2, 3, 3>;
+// 12 waves of 64-row tasks sharing a decode across three 16-pair blocks (48 pairs): a down-pass
+// shape (see kGroupedFused).
+using Cfg10 = ExpertCfg<12, 4, 3, 3>;
 
 // The grouped body specialised for the chunk's exact number of 16-pair row blocks.
 template <int MODE, class CFG, bool FRAG>
@@ -1004,10 +1010,14 @@ static hipError_t launch_cfg(int mode, int arm, const ExpertParams& p, int grid,
     else
       hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmDense, CfgDense>), g, bd, 0, stream, p);
   } else if (mode == kModeGateUp && arm == kArmGrouped) {
-    if (p.act_frag && p.unit_pad)
-      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, true>), g, b, 0, stream, p);
-    else
-      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, false>), g, b, 0, stream, p);
+    if constexpr (CFG::kGroupedFused) {
+      if (p.act_frag && p.unit_pad)
+        hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, true>), g, b, 0, stream, p);
+      else
+        hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, false>), g, b, 0, stream, p);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else if (mode == kModeGateUp) {
     if (spread)
       hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG, false, true>), g, b, 0, stream, p);
@@ -1054,6 +1064,7 @@ bool variant_info(int variant, int arm, VariantInfo& v) {
     case 7: CfgInfo<Cfg7>::get(arm, v); return true;
     case 8: CfgInfo<Cfg8>::get(arm, v); return true;
     case 9: CfgInfo<Cfg9>::get(arm, v); return true;
+    case 10: CfgInfo<Cfg10>::get(arm, v); return true;
     default: return false;
   }
 }
@@ -1070,6 +1081,7 @@ hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, 
     case 7: return launch_cfg<Cfg7>(mode, arm, p, grid, waves, stream);
     case 8: return launch_cfg<Cfg8>(mode, arm, p, grid, waves, stream);
     case 9: return launch_cfg<Cfg9>(mode, arm, p, grid, waves, stream);
+    case 10: return launch_cfg<Cfg10>(mode, arm, p, grid, waves, stream);
     default: return hipErrorInvalidValue;
   }
 }
