@@ -236,11 +236,13 @@ def test_schedule_reports_what_a_forward_launches():
 
 
 def test_default_kernel_shapes_follow_the_measured_rules():
-    # V4 layer (E=256, k=6): GEMV switches to 32-row tasks once woken*rows/32 >= 2048 wave slots;
-    # grouped picks by pairs per woken expert (1.41 at n=32, 3.15 at 128, 6.0 at 256, 12.0 at 512,
-    # 24.0 at 1024).
+    # V4 layer (E=256, k=6; 6, 11.9, 23.2 and 44.3 woken experts at n = 1, 2, 4, 8).  GEMV fused
+    # pass: 8 waves below 5 16-row tasks per CU, 16 waves from there, 32-row tasks once
+    # woken*rows/32 >= 2048 wave slots; GEMV down pass: 16 waves up to 6144 32-row tasks.  Grouped
+    # picks by pairs per woken expert (1.41 at n=32, 3.15 at 128, 6.0 at 256, 12.0 at 512, 24.0 at
+    # 1024).
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
-    want = {1: (2, 2), 4: (2, 4), 8: (4, 4), 32: (1, 3), 128: (1, 7), 256: (9, 10), 512: (9, 10), 1024: (9, 10)}
+    want = {1: (2, 1), 2: (1, 1), 4: (1, 1), 8: (4, 1), 32: (1, 3), 128: (1, 7), 256: (9, 10), 512: (9, 10), 1024: (9, 10)}
     for n, (gu, dn) in want.items():
         s = q.qtip_moe_plan_schedule(plan, n)
         assert (s["gate_up"]["variant"], s["down"]["variant"]) == (gu, dn), n

@@ -70,8 +70,12 @@ namespace {
 //    and an expert with up to 48 pairs is decoded once).  Down pass: 16 waves of 32-row tasks
 //    below 3, 12 waves of 64-row tasks with 12-byte code loads from 3, sharing a decode across
 //    three 16-pair blocks from 4.
-//  * GEMV arm, by the expected task count: 16-row tasks until there are enough 32-row tasks
-//    to give each of the 2048 wave slots of a 256-CU, 8-wave launch one.
+//  * GEMV arm, by the expected task count.  Fused pass: 8-wave workgroups of 16-row tasks
+//    while a 256-CU launch has fewer than 5 of them per CU (each task's inputs then split over
+//    two waves), 16-wave workgroups of 16-row tasks from there (their inputs split over two
+//    waves where the tasks are few), and 8 waves of 32-row tasks once those give each of the
+//    2048 wave slots of a 256-CU, 8-wave launch one.  Down pass: 16-wave workgroups of 16-row
+//    tasks up to 6144 32-row tasks (every measured batch of 1 to 8 tokens), 32-row tasks beyond.
 int kernel_arm(int32_t arm) {
   return arm == QTIP_ARM_GROUPED ? kArmGrouped : (arm == QTIP_ARM_DEQUANT ? kArmDense : kArmGemv);
 }
@@ -87,8 +91,11 @@ int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_to
   const int32_t n = n_tokens >= 1 ? n_tokens : 1;
   if (arm == kArmGemv) {
     const double rows = mode == kModeGateUp ? plan->d.inter : plan->d.hidden;
-    const double tall_tasks = fill_woken_experts(n, k, E) * rows / 32.0;
-    return tall_tasks >= 2048.0 ? 4 : 2;
+    const double woken = fill_woken_experts(n, k, E);
+    const double tall_tasks = woken * rows / 32.0;
+    if (mode == kModeSingle) return tall_tasks < 6144.0 ? 1 : 4;
+    if (tall_tasks >= 2048.0) return 4;
+    return woken * rows / 16.0 >= 5.0 * 256.0 ? 1 : 2;
   }
   const double ppe = fill_pairs_per_woken_expert(n, k, E);
   if (mode == kModeGateUp) return ppe < 4.0 ? 1 : 9;
