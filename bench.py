@@ -122,7 +122,7 @@ def timed(runner, steps, warmup, profile=True):
     ev1.record(runner.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    stats = q.qtip_moe_stats_get(runner.plan)
+    stats = q.qtip_moe_stats(runner.plan)
     prof = q.qtip_moe_profile_read(runner.plan) if profile else None
     if profile:
         q.qtip_moe_profile_enable(runner.plan, 0)
@@ -186,7 +186,7 @@ def measure_router(runner, inp, calls=200, layers=50):
         layer()
     e[3].record(runner.stream)
     torch.cuda.synchronize()
-    st = q.qtip_moe_stats_get(runner.plan)
+    st = q.qtip_moe_stats(runner.plan)
     if st["router_launches"] != calls + layers or st["forward_calls"] != layers:
         print(f"bench: router counters do not match the calls made: {st}", file=sys.stderr)
         sys.exit(2)

@@ -133,7 +133,11 @@ typedef struct qtip_moe_weights {
   const uint16_t* lut;        /* [65536] fp16, finite values */
 } qtip_moe_weights;
 
-typedef struct qtip_moe_stats {
+/* Launch counters of a plan (prefill page, PR #196, "Two things that were built, correct, and
+ * switched off": a harness that reports a per-variant timing must show the counter of the
+ * variant it claims advancing and the others not; the counters are read by qtip_moe_stats). */
+#define QTIP_VARIANT_SLOTS 11 /* index = kernel configuration 1..10 (0 unused) */
+typedef struct qtip_moe_stats_s {
   uint64_t forward_calls;     /* successful qtip_moe_forward calls */
   uint64_t gemv_launches;     /* expert-matrix kernel launches on the GEMV arm */
   uint64_t grouped_launches;  /* expert-matrix kernel launches on the grouped arm */
@@ -143,7 +147,9 @@ typedef struct qtip_moe_stats {
   uint64_t dequant_launches;  /* dequantize arm: materialise launches and dense expert-pass launches */
   int32_t last_arm;           /* arm taken by the last forward (QTIP_ARM_GEMV / _GROUPED / _DEQUANT) */
   int32_t last_n_tokens;      /* n of the last forward */
-} qtip_moe_stats;
+  uint64_t gemv_variant_launches[QTIP_VARIANT_SLOTS];    /* GEMV-arm expert launches per configuration */
+  uint64_t grouped_variant_launches[QTIP_VARIANT_SLOTS]; /* grouped-arm expert launches per configuration */
+} qtip_moe_stats_t;
 
 /* ---- plan -------------------------------------------------------------------------
  * qtip_moe_plan: validate `desc` (host) for `device`, fix the m-tile height and the
@@ -151,25 +157,36 @@ typedef struct qtip_moe_stats {
  * inside graph capture).  Checks: 1 <= k <= E <= 1024, k <= 32, H and I multiples of
  * 128, max_tokens >= 1, a known arm/out_dtype, tile_m in {0,16,32,64}, and the device
  * arch reported by HIP is gfx950 (else QTIP_ERR_NOT_SUPPORTED).  Free with
- * qtip_moe_plan_destroy.  Not thread-safe per plan object (counters). */
+ * qtip_moe_plan_destroy.  Not thread-safe per plan object (counters).
+ * Source: arch-specialise page, PR #99, "D18": an unsupported device is refused instead of
+ * running compiled-out code, and the m-tile height has one source of truth that the router,
+ * the kernels and the predicate all read (here: the plan); m-tile page, PR #167, "The fix":
+ * the dispatch inputs are host scalars, so planning is capture-safe. */
 qtip_status qtip_moe_plan(const qtip_moe_desc* desc /*host*/, int device, qtip_moe_plan_t* out /*host*/);
 
 /* Same as qtip_moe_plan for an explicit arch name (e.g. "gfx950:sramecc+:xnack-"),
- * without querying a device: lets host-only callers validate a configuration. */
+ * without querying a device: lets host-only callers validate a configuration.  Any other
+ * arch is QTIP_ERR_NOT_SUPPORTED (arch-specialise page, PR #99, "D18"). */
 qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc /*host*/, const char* gcn_arch_name /*host*/,
                                    qtip_moe_plan_t* out /*host*/);
 
+/* Frees a plan (host memory and any profiling events).  NULL is accepted. */
 qtip_status qtip_moe_plan_destroy(qtip_moe_plan_t plan);
 
 /* What the kernels will use: the m-tile height, the workspace bytes a forward needs at
  * max_tokens, and the smallest n for which the predicate (with the plan's dispatch_tile_m)
- * selects the grouped arm.  Any output pointer may be NULL. */
+ * selects the grouped arm.  Any output pointer may be NULL.
+ * Source: m-tile page, PR #167, "Tests" (the reported boundary is the exact flip point of the
+ * predicate) and arch-specialise page, "D18" (callers read the m-tile height the kernels use
+ * from the same place the kernels do). */
 qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m /*host*/, size_t* workspace_bytes /*host*/,
                                int32_t* min_tokens_grouped /*host*/);
 
 /* The expert-kernel schedule a forward of n tokens launches (the arm and, for each of the two
- * expert passes, the kernel configuration and its shape): the pages' schedule query, so
- * callers and benchmarks read what runs. */
+ * expert passes, the kernel configuration and its shape), so callers and benchmarks read what
+ * runs.  Source: prefill page, PR #196, "Two things that were built, correct, and switched off"
+ * (the selected variant is printed next to every result; a variant that cannot be reached is a
+ * defect) and arch-specialise page, "D18" (one source of truth for the tile height). */
 typedef struct qtip_moe_kernel_shape {
   int32_t variant;             /* kernel configuration 1..10 actually launched */
   int32_t waves_per_workgroup; /* wave64 per (persistent, one-per-CU) workgroup */
@@ -186,18 +203,30 @@ qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_
 
 /* The arm a forward of n tokens takes: the override if one is set, else the three-arm closed
  * form (qtip_fill_select_arm) with the plan's dispatch_tile_m and dequant_traffic_ratio.
- * Returns QTIP_ARM_GEMV, QTIP_ARM_GROUPED or QTIP_ARM_DEQUANT, or -1 for a bad plan/n. */
+ * Returns QTIP_ARM_GEMV, QTIP_ARM_GROUPED or QTIP_ARM_DEQUANT, or -1 for a bad plan/n.
+ * Source: m-tile page, PR #167, "The fix" (the predicate and the floor) and its post-merge
+ * note (an explicit arm pin overrides the predicate, so a harness can A/B the kernels). */
 int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens);
+
+/* The pure closed-form predicate for the plan's routing shape: 1 if n > 8 and the expected
+ * pairs per woken expert, n k / (E (1 - (1 - k/E)^n)), reach the plan's dispatch_tile_m,
+ * else 0; -1 for a bad plan or n < 1.  The plan's arm override is NOT applied here (the arm a
+ * forward takes is qtip_moe_select_arm).  Host only; the same header-only code as the plan.
+ * Source: m-tile page, PR #167, "The fix" (grouped_gemm_tiles_amortize: an average m-tile is
+ * full; the decode-regime floor stays) and "Tests" (the predicate unit-tested at n and n-1). */
+int32_t qtip_moe_select_grouped(qtip_moe_plan_t plan, int32_t n_tokens);
 
 /* The token counts [*n_lo, *n_hi) within [1, max_tokens] that the automatic dispatch sends to
  * the dequantize arm (empty, 0 and 0, when dispatch_tile_m <= dequant_traffic_ratio: the m-tile
- * page's "Tests" section requires the two boundaries to leave no such window). Host only. */
+ * page's "Tests" section requires the two boundaries to leave no such window). Host only;
+ * NULL -> INVALID_ARG. */
 qtip_status qtip_moe_dequant_range(qtip_moe_plan_t plan, int32_t* n_lo /*host*/, int32_t* n_hi /*host*/);
 
 /* The dequantize arm's first step alone (also a dense reference of the decode): writes
  * bf16(LUT[state]) of every weight of one expert's matrix (0 = gate [I][H], 1 = up [I][H],
  * 2 = down [H][I]; scales not applied) to dense_out (device, row-major, 16-byte aligned).
- * Errors: NULL, matrix or expert out of range, misalignment -> INVALID_ARG; launch -> HIP. */
+ * Errors: NULL, matrix or expert out of range, misalignment -> INVALID_ARG; launch -> HIP.
+ * Source: m-tile page, PR #167, "Tests" (the dequantize-materialize path, the third arm). */
 qtip_status qtip_moe_dequantize(qtip_moe_plan_t plan, const qtip_moe_weights* w /*host struct of device ptrs*/,
                                 int32_t matrix, int32_t expert, void* dense_out, void* stream);
 
@@ -215,6 +244,12 @@ int32_t qtip_fill_select_arm(int32_t n, int32_t k, int32_t E, int32_t tile_m, in
 
 /* ---- forward ----------------------------------------------------------------------
  * One MoE layer for n tokens: route, bin, gate+up (SwiGLU), down, combine.
+ * Source: m-tile page, PR #167, "The cause is a threshold" (pairs sorted by expert and walked
+ * as sum_e ceil(count_e / tile_m) m-tiles; the per-pair GEMV for low fill); arch-specialise
+ * page, PR #99, "The two levers" (packed 2-bit bytes decoded inside the multiply, runs of 32
+ * symbols seeded from their window; fewer decodes per expert) and "D18" (status of every
+ * launch; an empty launch is an error; no success with an unwritten output); step page, PR
+ * #202, "Ruled out by reading" (the weighted per-token combine of the expert outputs).
  *   x        [n][H] bf16 activations;   logits [n][E] fp32 router logits
  *   out      [n][H] bf16 or fp32 (plan's out_dtype); every element is written
  *   workspace >= qtip_moe_plan_info(...).workspace_bytes bytes, 256-byte aligned,
@@ -256,6 +291,9 @@ qtip_status qtip_moe_forward_hidden(qtip_moe_plan_t plan, const qtip_moe_weights
 int32_t qtip_moe_router_split(qtip_moe_plan_t plan, int32_t n_tokens);
 
 /* ---- routing and binning alone (bit-exact testing of the routing launcher) ----------
+ * Source: m-tile page, PR #167, "The cause is a threshold": (token, expert) pairs sorted by
+ * expert and cut into m-tiles of at most tile_m pairs, sum_e ceil(count_e / tile_m) of them;
+ * the workload definition's router (softmax over the top-k logits).
  *   topk_idx [n][k] int32, topk_w [n][k] fp32, counts [E], offsets [E+1] (exclusive
  *   scan, offsets[E] = n k), sorted_pair [n k] (pair ids p = t k + j grouped by expert,
  *   ascending p inside each expert), tile_map [n k][3] int32 (expert, start, len) tiles
@@ -266,6 +304,12 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
                            int32_t* tile_map, int32_t* n_tiles, void* stream);
 
 /* ---- one trellis matrix times binned activation rows ------------------------------
+ * The expert matmul by itself (arch-specialise page, PR #99, "The two levers": packed codes
+ * decoded in-kernel and multiplied; used for per-matrix timing and the bit-exact decode test).
+ * It walks a unit map rather than a tile map: a unit is (expert, first binned row, pairs) with
+ * up to 64 pairs, which one decode of the expert's rows serves.  Any m-tile map of
+ * qtip_moe_route (tiles of at most tile_m <= 64 pairs) is a valid unit map, so a tile map can
+ * be passed as it is; num_experts and n_rows_a bound the map's entries on the device.
  * For each unit u < n_units of unit_map [n_units][3] = (expert e, start s, len L):
  *   y[s+i][r] = scale[e][r] * sum_c a[s+i][c] * bf16(lut[state_e(r, c)])   (i < L, r < rows)
  *   codes [E][rows][cols/4], scales [E][rows] fp16, lut [65536] fp16,
@@ -280,22 +324,41 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
                                const void* a_bf16, int32_t n_rows_a, const int32_t* unit_map, int32_t n_units,
                                float* y, void* stream);
 
-/* ---- observability ----------------------------------------------------------------- */
-qtip_status qtip_moe_stats_get(qtip_moe_plan_t plan, qtip_moe_stats* out /*host*/);
+/* ---- observability -----------------------------------------------------------------
+ * qtip_moe_stats: copies the plan's launch counters (per arm, and per kernel configuration
+ * on the GEMV and grouped arms) into *out; qtip_moe_stats_reset zeroes them.  Host only.
+ * Source: prefill page, PR #196, "Two things that were built, correct, and switched off" (a
+ * per-variant timing must come with the launch counter of that variant advancing, and only
+ * that one). */
+qtip_status qtip_moe_stats(qtip_moe_plan_t plan, qtip_moe_stats_t* out /*host*/);
 qtip_status qtip_moe_stats_reset(qtip_moe_plan_t plan);
 
-/* One line naming the arm the plan takes for n tokens, the mean m-tile fill, pairs per
- * woken expert and the boundary n (the engagement line of the m-tile page,
- * "Re-measurement on this branch").  Writes at most buf_len bytes including the NUL. */
+/* One line naming the arm the plan takes for n tokens (GEMV, grouped or dequantize), the mean
+ * m-tile fill, pairs per woken expert and the boundary n, so a results artifact can be read
+ * back to the dispatch that produced it.  Writes at most buf_len bytes including the NUL.
+ * Source: m-tile page, PR #167, "Tests" (the engagement log) and "Re-measurement on this
+ * branch" (the line: tokens x top-k of E, m-tile fill %, pairs per woken expert against the
+ * m-tile height, the boundary n of the routing shape). */
 qtip_status qtip_moe_engaged_line(qtip_moe_plan_t plan, int32_t n_tokens, char* buf /*host*/, size_t buf_len);
+
+/* Writes the engagement line (qtip_moe_engaged_line) for n tokens to stderr once per plan and
+ * arm: the first call for the arm that n selects prints it and sets *printed = 1 (if printed is
+ * not NULL); later calls for the same arm print nothing and set *printed = 0.  Host only;
+ * errors as qtip_moe_engaged_line.  Source: m-tile page, PR #167, "Tests" (runs log which MoE
+ * kernel was selected and at what tile fill, once) and "Re-measurement on this branch". */
+qtip_status qtip_moe_log_engaged(qtip_moe_plan_t plan, int32_t n_tokens, int32_t* printed /*host*/);
 
 /* Take (once per device, cached only on success) the arch witness: a one-thread kernel
  * from this library's gfx950 code object writes a known value that is read back.  Fails
  * with CAPTURING if `stream` is capturing, NOT_SUPPORTED if the value is wrong or the
- * kernel cannot run.  qtip_moe_forward / _route / qtip_expert_matmul call it on first use. */
+ * kernel cannot run.  qtip_moe_forward / _route / qtip_expert_matmul call it on first use.
+ * Source: arch-specialise page, PR #99, "The arch witness" (never cache a non-answer; decline
+ * under graph capture rather than launch a probe into the capture). */
 qtip_status qtip_arch_witness(int device, void* stream);
 
-/* Per-stage timing.  qtip_moe_profile_enable(plan, capacity) creates capacity x 6 HIP events
+/* Per-stage timing (prefill page, PR #196: a measurement is only believed when a second
+ * instrument agrees; these events are checked against the profiler's kernel times).
+ * qtip_moe_profile_enable(plan, capacity) creates capacity x 6 HIP events
  * (capacity <= 4096; 0 disables and frees them); every later forward on the plan records an
  * event before its first kernel and after each of its five kernels (route, bin, gate+up,
  * down, combine) on the forward's stream, cycling through `capacity` slots.  Batches of up to
@@ -308,7 +371,8 @@ qtip_status qtip_arch_witness(int device, void* stream);
 qtip_status qtip_moe_profile_enable(qtip_moe_plan_t plan, int32_t capacity);
 qtip_status qtip_moe_profile_read(qtip_moe_plan_t plan, double* stage_ms /*host [5]*/, int32_t* n_forwards /*host*/);
 
-/* Decode-ceiling calibration (a diagnostic, not part of the forward path).  The trellis decode
+/* Decode-ceiling calibration (a diagnostic of this implementation, not part of the forward path
+ * and not taken from the pages).  The trellis decode
  * is bound by uniformly random 2-byte gathers from the 65536-entry LUT held in LDS; this runs
  * that gather alone on the current device (one 1024-thread workgroup per CU, 128 KiB LDS table,
  * 16 gathers per lane per round at pseudo-random addresses, `rounds` rounds) and reports the
@@ -318,8 +382,11 @@ qtip_status qtip_moe_profile_read(qtip_moe_plan_t plan, double* stage_ms /*host 
 qtip_status qtip_measure_lut_gather(int32_t rounds, uint32_t* sink, size_t sink_elems, void* stream,
                                     double* lookups_per_second /*host*/);
 
+/* Status names and error text (arch-specialise page, PR #99, "D18": every launch status is read
+ * back and surfaced, never swallowed).  qtip_status_string returns a static name
+ * ("QTIP_ERR_UNKNOWN" for a value outside the enum); qtip_last_error_detail returns the text of
+ * the last error raised on the calling thread ("" if none), valid until that thread's next call. */
 const char* qtip_status_string(qtip_status s);
-/* Text of the last error raised on the calling thread ("" if none). */
 const char* qtip_last_error_detail(void);
 
 #ifdef __cplusplus

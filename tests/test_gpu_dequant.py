@@ -45,7 +45,7 @@ def test_dequantize_is_bit_exact(name, shape, experts):
             want = f64_to_bf16_bits(trellis.decode_declared(codes[e], inp.lut))
             ok, st = parity.check_exact(got, want)
             assert ok, st
-    st = q.qtip_moe_stats_get(layer.plan)
+    st = q.qtip_moe_stats(layer.plan)
     layer.close()
     assert st["dequant_launches"] == 3 * len(experts)
 
@@ -70,7 +70,7 @@ def test_tiny_layer_on_the_dequantize_arm(seed, out_dtype):
     say(f"dequantize arm tiny seed={seed} out={out_dtype}")
     layer = dequant_layer(inp, out_dtype)
     got = layer.forward(inp)
-    st = q.qtip_moe_stats_get(layer.plan)
+    st = q.qtip_moe_stats(layer.plan)
     layer.close()
     assert st["last_arm"] == q.QTIP_ARM_DEQUANT
     assert st["dequant_launches"] == 4 and st["grouped_launches"] == 0 and st["gemv_launches"] == 0
@@ -106,7 +106,7 @@ def test_automatic_dispatch_inside_a_dequantize_window():
     assert q.qtip_moe_dequant_range(layer.plan) == (lo, hi)
     say(f"automatic dispatch n={n} in window [{lo}, {hi})")
     got = layer.forward(inp)
-    st = q.qtip_moe_stats_get(layer.plan)
+    st = q.qtip_moe_stats(layer.plan)
     layer.close()
     assert st["last_arm"] == q.QTIP_ARM_DEQUANT and st["dequant_launches"] == 4
     check(got, moe.moe_forward(inp), "f32")

@@ -43,7 +43,7 @@ def test_degenerate_and_extreme_shapes(name, arm, layout):
                                              act_layout=layout), 0)
     layer.ws = torch.empty(q.qtip_moe_plan_info(layer.plan)["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
     got = layer.forward(inp)
-    st = q.qtip_moe_stats_get(layer.plan)
+    st = q.qtip_moe_stats(layer.plan)
     layer.close()
     assert st["last_arm"] == arm
     ref = moe.moe_forward(inp)

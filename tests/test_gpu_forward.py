@@ -38,7 +38,7 @@ def test_tiny_workload_full_parity(seed, arm, out_dtype):
     say(f"forward tiny seed={seed} arm={arm} out={out_dtype}")
     layer = Layer(inp, arm=arm, out_dtype=out_dtype)
     got = layer.forward(inp)
-    st = q.qtip_moe_stats_get(layer.plan)
+    st = q.qtip_moe_stats(layer.plan)
     expect_arm = q.qtip_moe_select_arm(layer.plan, 16)
     assert st["last_arm"] == expect_arm
     if expect_arm == q.QTIP_ARM_GROUPED:
@@ -115,7 +115,7 @@ def test_full_size_workloads_sampled_tokens(name):
     say(f"forward full-size {name} n={n}")
     layer = Layer(inp, out_dtype="f32", max_tokens=1024)
     got = layer.forward(inp)
-    arm = q.qtip_moe_stats_get(layer.plan)["last_arm"]
+    arm = q.qtip_moe_stats(layer.plan)["last_arm"]
     layer.close()
     assert np.all(np.isfinite(got))
     toks = V4_SAMPLES[name]
@@ -134,7 +134,7 @@ def test_v4_small_batches_full_parity():
     for n in (1, 2, 5):
         say(f"forward V4 small batch n={n}")
         got = layer.forward(inps[n])
-        assert q.qtip_moe_stats_get(layer.plan)["last_arm"] == q.QTIP_ARM_GEMV
+        assert q.qtip_moe_stats(layer.plan)["last_arm"] == q.QTIP_ARM_GEMV
         check(got, moe.moe_forward(inps[n]), "f32")
     layer.close()
 

@@ -82,7 +82,7 @@ def test_forward_hidden_equals_forward_of_router_logits(name, shape, n):
     out_b = torch.empty_like(out_a)
     q.qtip_moe_forward_hidden(layer.plan, layer.w, w_dev, x, n, out_b, layer.ws, layer.ws.numel())
     torch.cuda.synchronize()
-    st = q.qtip_moe_stats_get(layer.plan)
+    st = q.qtip_moe_stats(layer.plan)
     layer.close()
     assert st["router_launches"] == 1 and st["forward_calls"] == 1
     assert np.array_equal(out_a.cpu().numpy().view(np.uint32), out_b.cpu().numpy().view(np.uint32))

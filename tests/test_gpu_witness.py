@@ -44,7 +44,7 @@ with torch.cuda.stream(stream):
     g.capture_end()
 torch.cuda.synchronize()
 assert status == q.QTIP_ERR_CAPTURING, status
-assert q.qtip_moe_stats_get(plan)["forward_calls"] == 0
+assert q.qtip_moe_stats(plan)["forward_calls"] == 0
 q.qtip_moe_forward(plan, w, t.x, t.logits, s.n_tokens, out, ws, ws.numel())
 torch.cuda.synchronize()
 assert torch.isfinite(out).all().item()

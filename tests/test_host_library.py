@@ -311,3 +311,81 @@ def test_workspace_holds_only_the_layouts_the_plan_can_take():
     assert auto - rows >= (PP - P) * 2048 * 2 + PP * 4096 * 2
     # pinning the GEMV arm leaves the grouped layouts out
     assert ws(1024, arm_override=q.QTIP_ARM_GEMV) == rows
+
+
+# ---- the boundary's closed-form predicate, counters and engagement log -------------------
+SHAPES = [(6, 256, 16), (6, 256, 1), (2, 8, 16), (6, 8, 16), (8, 128, 16), (4, 64, 32), (1, 16, 4), (8, 256, 64)]
+
+
+@pytest.mark.parametrize("k,E,thr", SHAPES)
+def test_select_grouped_is_the_oracle_predicate(k, E, thr):
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(E, k, 256, 128, 4096, dispatch_tile_m=thr), "gfx950")
+    for n in list(range(1, 40)) + [64, 127, 128, 512, 682, 683, 684, 1024, 1572, 2000, 4096]:
+        assert q.qtip_moe_select_grouped(plan, n) == int(fill.select_grouped(n, k, E, thr)), (k, E, thr, n)
+    n0 = fill.min_tokens_grouped(k, E, thr)
+    if n0 <= 4096:
+        assert q.qtip_moe_select_grouped(plan, n0) == 1 and q.qtip_moe_select_grouped(plan, n0 - 1) == 0
+    assert q.qtip_moe_select_grouped(plan, 0) == -1
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_select_grouped_ignores_the_arm_pin():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_GEMV, dispatch_tile_m=16), "gfx950")
+    assert q.qtip_moe_select_grouped(plan, 1024) == 1          # the closed form
+    assert q.qtip_moe_select_arm(plan, 1024) == q.QTIP_ARM_GEMV  # the arm a forward takes
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_stats_start_at_zero_with_per_variant_slots():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    st = q.qtip_moe_stats(plan)
+    assert st["forward_calls"] == 0 and st["last_arm"] == 0
+    assert st["gemv_variant_launches"] == [0] * 11 and st["grouped_variant_launches"] == [0] * 11
+    q.qtip_moe_stats_reset(plan)
+    assert ctypes.sizeof(q.qtip_moe_stats_t) == 7 * 8 + 2 * 4 + 2 * 11 * 8
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_log_engaged_prints_once_per_arm(capfd):
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, dispatch_tile_m=16), "gfx950")
+    assert q.qtip_moe_log_engaged(plan, 1572) is True
+    assert q.qtip_moe_log_engaged(plan, 2000) is False        # grouped again: already logged
+    assert q.qtip_moe_log_engaged(plan, 32) is True           # first GEMV engagement
+    err = capfd.readouterr().err.strip().splitlines()
+    assert len(err) == 2
+    pct = 100 * fill.pairs_per_woken_expert(1572, 6, 256) / 16
+    assert "grouped arm for 1572 tokens" in err[0] and f"{pct:.1f}%" in err[0] and "grouped from 683" in err[0]
+    assert "GEMV arm for 32 tokens" in err[1]
+    with pytest.raises(q.QtipError):
+        q.qtip_moe_log_engaged(plan, 0)
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_engaged_line_names_the_dequantize_arm():
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**{**V4, "max_tokens": 64}, arm_override=q.QTIP_ARM_DEQUANT), "gfx950")
+    line = q.qtip_moe_engaged_line(plan, 32)
+    assert line.startswith("qtip_moe: dequantize arm for 32 tokens") and "pinned" in line
+    q.qtip_moe_plan_destroy(plan)
+    # a window between the traffic ratio and a raised grouped threshold, reached by AUTO
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**{**V4, "max_tokens": 2048}, dispatch_tile_m=32), "gfx950")
+    lo, hi = q.qtip_moe_dequant_range(plan)
+    assert lo < hi and fill.select_arm(lo, 6, 256, 32) == "dequant"
+    assert q.qtip_moe_engaged_line(plan, lo).startswith(f"qtip_moe: dequantize arm for {lo} tokens")
+    q.qtip_moe_plan_destroy(plan)
+
+
+def test_build_rejects_packed_fp32_in_device_assembly():
+    from trellis_quantized_moe_expert_amd import build
+    asm = "\tv_fmac_f32_e32 v1, v5, v7\n\tv_pk_fma_f32 v[0:1], v[4:5], v[6:7], s[0:1]\n; v_pk_add_f32 in a comment\n"
+    assert build.packed_fp32_lines(asm) == ["v_pk_fma_f32 v[0:1], v[4:5], v[6:7], s[0:1]"]
+    assert build.packed_fp32_lines("\tv_pk_mul_f16 v0, v1, v2\n\tv_add_f32 v0, v1, v2\n") == []
+    cmd = build.compile_command("csrc/expert.hip", "/tmp/x.o")
+    i = cmd.index("-target-feature")
+    assert cmd[i - 1:i + 3] == ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    # the build kept the device assembly of the library it produced: none of it is packed FP32
+    asm_dir = os.path.join(ROOT, "_build", "expert")
+    if os.path.isdir(asm_dir):
+        files = build.device_asm_files(asm_dir)
+        assert files
+        for f in files:
+            assert build.packed_fp32_lines(open(f).read()) == [], f

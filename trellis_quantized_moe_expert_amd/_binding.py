@@ -46,13 +46,18 @@ class qtip_moe_weights(ctypes.Structure):
                 ("lut", ctypes.c_void_p)]
 
 
-class qtip_moe_stats(ctypes.Structure):
+QTIP_VARIANT_SLOTS = 11
+
+
+class qtip_moe_stats_t(ctypes.Structure):
     _fields_ = [("forward_calls", ctypes.c_uint64), ("gemv_launches", ctypes.c_uint64),
                 ("grouped_launches", ctypes.c_uint64), ("route_launches", ctypes.c_uint64),
                 ("combine_launches", ctypes.c_uint64), ("router_launches", ctypes.c_uint64),
                 ("dequant_launches", ctypes.c_uint64),
                 ("last_arm", ctypes.c_int32),
-                ("last_n_tokens", ctypes.c_int32)]
+                ("last_n_tokens", ctypes.c_int32),
+                ("gemv_variant_launches", ctypes.c_uint64 * QTIP_VARIANT_SLOTS),
+                ("grouped_variant_launches", ctypes.c_uint64 * QTIP_VARIANT_SLOTS)]
 
 
 class qtip_moe_kernel_shape(ctypes.Structure):
@@ -79,6 +84,7 @@ _SIGS = {
     "qtip_moe_plan_destroy": (_I32, [_P]),
     "qtip_moe_plan_info": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_I32)]),
     "qtip_moe_select_arm": (_I32, [_P, _I32]),
+    "qtip_moe_select_grouped": (_I32, [_P, _I32]),
     "qtip_moe_plan_schedule": (_I32, [_P, _I32, ctypes.POINTER(qtip_moe_schedule)]),
     "qtip_fill_woken_experts": (ctypes.c_double, [_I32, _I32, _I32]),
     "qtip_fill_pairs_per_woken_expert": (ctypes.c_double, [_I32, _I32, _I32]),
@@ -94,9 +100,10 @@ _SIGS = {
     "qtip_fill_select_arm": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "qtip_moe_route": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "qtip_expert_matmul": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _P, _P]),
-    "qtip_moe_stats_get": (_I32, [_P, ctypes.POINTER(qtip_moe_stats)]),
+    "qtip_moe_stats": (_I32, [_P, ctypes.POINTER(qtip_moe_stats_t)]),
     "qtip_moe_stats_reset": (_I32, [_P]),
     "qtip_moe_engaged_line": (_I32, [_P, _I32, ctypes.c_char_p, ctypes.c_size_t]),
+    "qtip_moe_log_engaged": (_I32, [_P, _I32, ctypes.POINTER(_I32)]),
     "qtip_arch_witness": (_I32, [ctypes.c_int, _P]),
     "qtip_moe_profile_enable": (_I32, [_P, _I32]),
     "qtip_moe_profile_read": (_I32, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)]),
@@ -205,6 +212,10 @@ def qtip_moe_select_arm(plan: int, n_tokens: int) -> int:
     return lib().qtip_moe_select_arm(plan, n_tokens)
 
 
+def qtip_moe_select_grouped(plan: int, n_tokens: int) -> int:
+    return lib().qtip_moe_select_grouped(plan, n_tokens)
+
+
 def qtip_fill_woken_experts(n, k, E) -> float:
     return lib().qtip_fill_woken_experts(n, k, E)
 
@@ -276,10 +287,14 @@ def qtip_expert_matmul(plan, arm, codes, scales, lut, num_experts, rows, cols, a
                                                           _ptr(unit_map), n_units, _ptr(y), _stream(stream)))
 
 
-def qtip_moe_stats_get(plan) -> dict:
-    s = qtip_moe_stats()
-    _check("qtip_moe_stats_get", lib().qtip_moe_stats_get(plan, ctypes.byref(s)))
-    return {name: getattr(s, name) for name, _ in qtip_moe_stats._fields_}
+def qtip_moe_stats(plan) -> dict:
+    s = qtip_moe_stats_t()
+    _check("qtip_moe_stats", lib().qtip_moe_stats(plan, ctypes.byref(s)))
+    out = {}
+    for name, _ in qtip_moe_stats_t._fields_:
+        v = getattr(s, name)
+        out[name] = list(v) if isinstance(v, ctypes.Array) else v
+    return out
 
 
 def qtip_moe_stats_reset(plan) -> None:
@@ -290,6 +305,12 @@ def qtip_moe_engaged_line(plan, n_tokens) -> str:
     buf = ctypes.create_string_buffer(512)
     _check("qtip_moe_engaged_line", lib().qtip_moe_engaged_line(plan, n_tokens, buf, len(buf)))
     return buf.value.decode()
+
+
+def qtip_moe_log_engaged(plan, n_tokens) -> bool:
+    printed = _I32()
+    _check("qtip_moe_log_engaged", lib().qtip_moe_log_engaged(plan, n_tokens, ctypes.byref(printed)))
+    return bool(printed.value)
 
 
 def qtip_arch_witness(device: int = 0, stream=None) -> None:

@@ -34,7 +34,8 @@ struct qtip_moe_plan_s {
 
   int32_t min_tokens_grouped;
   size_t ws_bytes;
-  qtip_moe_stats stats;
+  qtip_moe_stats_t stats;
+  bool engaged_logged[4] = {false, false, false, false};  // qtip_moe_log_engaged: printed per arm
   // per-stage timing ring (qtip_moe_profile_enable)
   std::vector<hipEvent_t> prof_events;  // capacity x (kStages + 1)
   int32_t prof_capacity = 0;
@@ -488,6 +489,11 @@ qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_
   return QTIP_OK;
 }
 
+int32_t qtip_moe_select_grouped(qtip_moe_plan_t plan, int32_t n_tokens) {
+  if (!plan || n_tokens < 1) return -1;
+  return fill_select_grouped(n_tokens, plan->d.top_k, plan->d.num_experts, plan->dispatch_tile_m) ? 1 : 0;
+}
+
 int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens) {
   if (!plan || n_tokens < 1) return -1;
   if (plan->d.arm_override != QTIP_ARM_AUTO) return plan->d.arm_override;
@@ -583,7 +589,13 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
       persistent_shape(dev, (size_t)n_units * (rows / vi.rows_per_task), vi.waves, karm == kArmGemv);
   hipError_t e = launch_expert(kModeSingle, karm, kv, p, shape.grid, shape.waves, st);
   if (e != hipSuccess) return hip_fail(e, "expert kernel launch");
-  if (arm == QTIP_ARM_GROUPED) plan->stats.grouped_launches++; else plan->stats.gemv_launches++;
+  if (arm == QTIP_ARM_GROUPED) {
+    plan->stats.grouped_launches++;
+    plan->stats.grouped_variant_launches[kv]++;
+  } else {
+    plan->stats.gemv_launches++;
+    plan->stats.gemv_variant_launches[kv]++;
+  }
   return QTIP_OK;
 }
 
@@ -797,9 +809,17 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   e = launch_expert(kModeSingle, karm, kv_dn, dn, shape_dn.grid, shape_dn.waves, st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
-  if (karm == kArmGrouped) plan->stats.grouped_launches += 2;
-  else if (karm == kArmDense) plan->stats.dequant_launches += 2;
-  else plan->stats.gemv_launches += 2;
+  if (karm == kArmGrouped) {
+    plan->stats.grouped_launches += 2;
+    plan->stats.grouped_variant_launches[kv_gu]++;
+    plan->stats.grouped_variant_launches[kv_dn]++;
+  } else if (karm == kArmDense) {
+    plan->stats.dequant_launches += 2;
+  } else {
+    plan->stats.gemv_launches += 2;
+    plan->stats.gemv_variant_launches[kv_gu]++;
+    plan->stats.gemv_variant_launches[kv_dn]++;
+  }
 
   e = launch_combine(y, topk_w, n_tokens, d.top_k, d.hidden, out, d.out_dtype == QTIP_OUT_BF16, st);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -985,7 +1005,7 @@ qtip_status qtip_measure_lut_gather(int32_t rounds, uint32_t* sink, size_t sink_
   return QTIP_OK;
 }
 
-qtip_status qtip_moe_stats_get(qtip_moe_plan_t plan, qtip_moe_stats* out) {
+qtip_status qtip_moe_stats(qtip_moe_plan_t plan, qtip_moe_stats_t* out) {
   if (!plan || !out) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
   *out = plan->stats;
   return QTIP_OK;
@@ -993,7 +1013,7 @@ qtip_status qtip_moe_stats_get(qtip_moe_plan_t plan, qtip_moe_stats* out) {
 
 qtip_status qtip_moe_stats_reset(qtip_moe_plan_t plan) {
   if (!plan) return fail(QTIP_ERR_INVALID_ARG, "plan is NULL");
-  plan->stats = qtip_moe_stats{};
+  plan->stats = qtip_moe_stats_t{};
   return QTIP_OK;
 }
 
@@ -1007,9 +1027,24 @@ qtip_status qtip_moe_engaged_line(qtip_moe_plan_t plan, int32_t n_tokens, char* 
                 "qtip_moe: %s arm for %d tokens x top-%d of %d experts; mean m-tile fill %.1f%% "
                 "(%.2f pairs per woken expert, tile_m=%d); dispatch threshold %d pairs, grouped from %d "
                 "tokens%s",
-                arm == QTIP_ARM_GROUPED ? "grouped" : "GEMV", n_tokens, d.top_k, d.num_experts,
+                arm == QTIP_ARM_GROUPED ? "grouped" : (arm == QTIP_ARM_DEQUANT ? "dequantize" : "GEMV"), n_tokens,
+                d.top_k, d.num_experts,
                 100.0 * ppe / plan->tile_m, ppe, plan->tile_m, plan->dispatch_tile_m, plan->min_tokens_grouped,
                 d.arm_override != QTIP_ARM_AUTO ? " (arm pinned by the plan)" : "");
+  return QTIP_OK;
+}
+
+qtip_status qtip_moe_log_engaged(qtip_moe_plan_t plan, int32_t n_tokens, int32_t* printed) {
+  if (printed) *printed = 0;
+  char line[512];
+  const qtip_status s = qtip_moe_engaged_line(plan, n_tokens, line, sizeof(line));
+  if (s != QTIP_OK) return s;
+  const int32_t arm = qtip_moe_select_arm(plan, n_tokens);
+  if (arm < 0 || arm > 3 || plan->engaged_logged[arm]) return QTIP_OK;
+  plan->engaged_logged[arm] = true;
+  std::fprintf(stderr, "%s\n", line);
+  std::fflush(stderr);
+  if (printed) *printed = 1;
   return QTIP_OK;
 }
 
