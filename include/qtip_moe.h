@@ -263,6 +263,29 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w /*h
                              const void* x_bf16, const float* logits, int32_t n_tokens, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- the forward without allocation -----------------------------------------------------
+ * For callers that cannot allocate: code under HIP graph capture that may not call hipMalloc,
+ * tight serving loops, and harnesses that forbid allocation.  The same layer as
+ * qtip_moe_forward (same kernels, same results bit for bit), with its scratch in a device
+ * array that the library holds for the life of the process, QTIP_NOALLOC_SCRATCH_BYTES per
+ * GPU it runs on, instead of a caller workspace.  The caller still passes inputs and outputs.
+ *   The scratch is laid out for this call's n_tokens, so a call fits when the layer needs at
+ *   most QTIP_NOALLOC_SCRATCH_BYTES for n tokens: the V4 layer (E=256, top-6, H=4096,
+ *   I=2048) up to 405 tokens (534 with the GEMV arm pinned), the tiny layer at any n.  A call
+ *   that takes the dequantize arm (every expert's dense weights) does not fit at V4 sizes.
+ *   Makes no allocation, no free and no synchronisation on any call; the first call on a
+ *   device looks up that device's scratch address (and takes the arch witness, as
+ *   qtip_moe_forward does), so make it once outside capture.  The scratch needs no
+ *   initialisation: every call writes what it reads.
+ *   All calls on one GPU share that GPU's scratch: calls that overlap on one GPU (two
+ *   streams, two threads, two plans) race and must be serialised by the caller.
+ * Errors: as qtip_moe_forward; a layer that needs more scratch than the maximum for n tokens
+ * -> QTIP_ERR_INVALID_CONFIG (checked on the host before any device work). */
+#define QTIP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+qtip_status qtip_moe_forward_noalloc(qtip_moe_plan_t plan, const qtip_moe_weights* w /*host struct of device ptrs*/,
+                                     const void* x_bf16, const float* logits, int32_t n_tokens, void* out,
+                                     void* stream);
+
 /* ---- router GEMM (794-ms-decode-step page, PR #202, closing list of remaining
  * un-owned items, item (3): the router GEMM ahead of top-k, moved from FP32 scalar
  * cores to the matrix units) ---------------------------------------------------------

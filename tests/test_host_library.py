@@ -389,3 +389,22 @@ def test_build_rejects_packed_fp32_in_device_assembly():
         assert files
         for f in files:
             assert build.packed_fp32_lines(open(f).read()) == [], f
+
+
+def test_noalloc_refuses_layers_beyond_its_scratch_on_the_host():
+    w = q.make_weights(*[256] * 7)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    with pytest.raises(q.QtipError) as ei:
+        q.qtip_moe_forward_noalloc(plan, w, 256, 256, 406, 256)     # first V4 size past 64 MiB
+    assert ei.value.status == q.QTIP_ERR_INVALID_CONFIG and "scratch" in str(ei.value)
+    for n in (0, 1025):
+        with pytest.raises(q.QtipError) as ei:
+            q.qtip_moe_forward_noalloc(plan, w, 256, 256, n, 256)
+        assert ei.value.status == q.QTIP_ERR_INVALID_CONFIG
+    q.qtip_moe_plan_destroy(plan)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_DEQUANT), "gfx950")
+    with pytest.raises(q.QtipError) as ei:
+        q.qtip_moe_forward_noalloc(plan, w, 256, 256, 1, 256)       # dense weights never fit
+    assert "scratch" in str(ei.value)
+    q.qtip_moe_plan_destroy(plan)
+    assert q.QTIP_NOALLOC_SCRATCH_BYTES == 64 << 20

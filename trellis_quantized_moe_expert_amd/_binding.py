@@ -91,6 +91,7 @@ _SIGS = {
     "qtip_fill_select_grouped": (_I32, [_I32, _I32, _I32, _I32]),
     "qtip_fill_min_tokens": (_I32, [_I32, _I32, _I32]),
     "qtip_moe_forward": (_I32, [_P, ctypes.POINTER(qtip_moe_weights), _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
+    "qtip_moe_forward_noalloc": (_I32, [_P, ctypes.POINTER(qtip_moe_weights), _P, _P, _I32, _P, _P]),
     "qtip_moe_forward_hidden": (_I32, [_P, ctypes.POINTER(qtip_moe_weights), _P, _P, _I32, _P, _P, ctypes.c_size_t,
                                        _P]),
     "qtip_moe_router_logits": (_I32, [_P, _P, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
@@ -237,6 +238,15 @@ def qtip_moe_forward(plan, weights: qtip_moe_weights, x_bf16, logits, n_tokens, 
     _check("qtip_moe_forward", lib().qtip_moe_forward(plan, ctypes.byref(weights), _ptr(x_bf16), _ptr(logits),
                                                       n_tokens, _ptr(out), _ptr(workspace), workspace_bytes,
                                                       _stream(stream)))
+
+
+QTIP_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def qtip_moe_forward_noalloc(plan, weights: qtip_moe_weights, x_bf16, logits, n_tokens, out, stream=None) -> None:
+    _check("qtip_moe_forward_noalloc", lib().qtip_moe_forward_noalloc(plan, ctypes.byref(weights), _ptr(x_bf16),
+                                                                      _ptr(logits), n_tokens, _ptr(out),
+                                                                      _stream(stream)))
 
 
 def qtip_moe_forward_hidden(plan, weights: qtip_moe_weights, w_router_bf16, x_bf16, n_tokens, out, workspace,

@@ -339,6 +339,62 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
   return QTIP_OK;
 }
 
+// What a forward of n tokens uses: its kernel arm, and whether the grouped arm runs on the
+// fragment-order activations (h, and x packed by an extra pass).
+struct CallChoice {
+  int32_t arm;
+  int karm;
+  bool frag, pack;
+};
+
+CallChoice call_choice(const qtip_moe_plan_s* plan, int32_t n_tokens) {
+  const qtip_moe_desc& d = plan->d;
+  CallChoice c{};
+  c.arm = d.arm_override != QTIP_ARM_AUTO
+              ? d.arm_override
+              : fill_select_arm(n_tokens, d.top_k, d.num_experts, plan->dispatch_tile_m, plan->dequant_ratio);
+  c.karm = kernel_arm(c.arm);
+  const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
+  c.frag = plan->frag && c.karm == kArmGrouped && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kFragMinPairs);
+  c.pack = c.frag && plan->pack && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
+  return c;
+}
+
+// Scratch of a forward laid out for its own n tokens: only the buffers that call uses.
+WsLayout call_layout(const qtip_moe_plan_s* plan, int32_t n_tokens) {
+  const CallChoice c = call_choice(plan, n_tokens);
+  return ws_layout(plan->d, plan->tile_m, n_tokens, c.karm == kArmDense, c.frag, c.pack);
+}
+
+// --- the allocation-free entry point's scratch ---------------------------------------------
+// One array per GPU, held until the process ends.  Host code never uses the array's name as a
+// device address (on the host it names a stand-in): the address of each device's copy comes
+// from hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is passed to kernels.
+constexpr size_t kScratchBytes = QTIP_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<char*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+qtip_status scratch_on(int dev, char** out) {
+  char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      void* addr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!addr || (reinterpret_cast<uintptr_t>(addr) & 255))
+        return fail(QTIP_ERR_HIP, "scratch symbol address is NULL or not 256-byte aligned");
+      p = static_cast<char*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return QTIP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -605,10 +661,11 @@ namespace {
 
 // The layer from router logits (logits != NULL) or from hidden states through the router
 // GEMM (w_router != NULL; its K-chunk partial sums go to the workspace and the top-k kernel
-// adds them).
+// adds them).  The workspace regions are laid out for the plan's max_tokens, or, with
+// layout_for_n (the allocation-free entry point), for this call's n_tokens only.
 qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const void* x_bf16, const float* logits,
                          const void* w_router, int32_t n_tokens, void* out, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         void* stream, bool layout_for_n = false) {
   g_detail.clear();
   if (!plan || !w || !x_bf16 || !(logits || w_router) || !out || !workspace)
     return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
@@ -621,7 +678,8 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     return fail(QTIP_ERR_INVALID_ARG, "lut, x and out must be 16-byte aligned, codes 8-byte aligned");
   if (n_tokens <= 0 || n_tokens > plan->d.max_tokens)
     return fail(QTIP_ERR_INVALID_CONFIG, "n_tokens must be in [1, max_tokens] (an empty launch is an error)");
-  if (workspace_bytes < plan->ws_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
+  const size_t ws_need = layout_for_n ? call_layout(plan, n_tokens).total : plan->ws_bytes;
+  if (workspace_bytes < ws_need || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return fail(QTIP_ERR_INVALID_ARG, "workspace too small or not 256-byte aligned");
   const hipStream_t st = (hipStream_t)stream;
   int dev = 0;
@@ -629,10 +687,12 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   if (s != QTIP_OK) return s;
 
   const qtip_moe_desc& d = plan->d;
-  const int32_t arm = qtip_moe_select_arm(plan, n_tokens);
-  const int karm = kernel_arm(arm);
+  const CallChoice choice = call_choice(plan, n_tokens);
+  const int32_t arm = choice.arm;
+  const int karm = choice.karm;
   if (karm == kArmDense && !plan->dense) return fail(QTIP_ERR_INVALID_CONFIG, "the plan has no dequantize workspace");
-  const WsLayout L = ws_layout(d, plan->tile_m, d.max_tokens, plan->dense, plan->frag, plan->pack);
+  const WsLayout L = layout_for_n ? call_layout(plan, n_tokens)
+                                  : ws_layout(d, plan->tile_m, d.max_tokens, plan->dense, plan->frag, plan->pack);
   char* ws = reinterpret_cast<char*>(workspace);
   int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
   float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
@@ -663,9 +723,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   // The grouped arm's activation layout: fragment order over padded positions for h (and the
   // down pass) from kFragMinPairs pairs per woken expert, for x too (an extra packing pass)
   // from kPackMinPairs; gathered rows below.
-  const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
-  const bool frag = plan->frag && karm == kArmGrouped &&
-                    (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kFragMinPairs);
+  const bool frag = choice.frag;
   int32_t* padded_pair = reinterpret_cast<int32_t*>(ws + L.padded_pair);
   int32_t* n_pad = reinterpret_cast<int32_t*>(ws + L.n_pad);
   uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
@@ -709,7 +767,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     if (e != hipSuccess) return hip_fail(e, "bin launch");
     plan->stats.route_launches += 2;
   }
-  const bool pack = frag && plan->pack && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
+  const bool pack = choice.pack;
   if (pack) {
     e = launch_pack_act(reinterpret_cast<const uint16_t*>(x_bf16), padded_pair, n_pad, d.top_k, d.hidden, pp_max, xs,
                         st);
@@ -853,6 +911,27 @@ qtip_status qtip_moe_forward_hidden(qtip_moe_plan_t plan, const qtip_moe_weights
     return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
   }
   return forward_impl(plan, w, x_bf16, nullptr, w_router_bf16, n_tokens, out, workspace, workspace_bytes, stream);
+}
+
+qtip_status qtip_moe_forward_noalloc(qtip_moe_plan_t plan, const qtip_moe_weights* w, const void* x_bf16,
+                                     const float* logits, int32_t n_tokens, void* out, void* stream) {
+  g_detail.clear();
+  if (!plan || !logits) return fail(QTIP_ERR_INVALID_ARG, "NULL argument");
+  if (n_tokens <= 0 || n_tokens > plan->d.max_tokens)
+    return fail(QTIP_ERR_INVALID_CONFIG, "n_tokens must be in [1, max_tokens] (an empty launch is an error)");
+  // the size check needs host scalars only, so an oversized call touches no device state
+  const size_t need = call_layout(plan, n_tokens).total;
+  if (need > kScratchBytes)
+    return fail(QTIP_ERR_INVALID_CONFIG, "this layer needs " + std::to_string(need) +
+                                             " bytes of scratch for " + std::to_string(n_tokens) +
+                                             " tokens; the allocation-free entry point holds " +
+                                             std::to_string(kScratchBytes) + " (QTIP_NOALLOC_SCRATCH_BYTES)");
+  int dev = 0;
+  qtip_status s = current_device(&dev);
+  if (s != QTIP_OK) return s;
+  char* ptr = nullptr;
+  if ((s = scratch_on(dev, &ptr)) != QTIP_OK) return s;
+  return forward_impl(plan, w, x_bf16, logits, nullptr, n_tokens, out, ptr, kScratchBytes, stream, true);
 }
 
 qtip_status qtip_moe_router_logits(qtip_moe_plan_t plan, const void* x_bf16, const void* w_router_bf16,
