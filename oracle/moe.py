@@ -62,6 +62,47 @@ def _finish(acc: np.ndarray, out_dtype: str) -> np.ndarray:
     raise ValueError(out_dtype)
 
 
+def decode_expert(inp, e: int, mode: str = "declared"):
+    """Expert e's gate, up and down weights: unscaled bf16(LUT[state]) in declared mode (the
+    scales are applied after each dot product), float32(LUT) * float32(scale) in exact mode."""
+    if mode == "declared":
+        return tuple(trellis.decode_declared(c[e], inp.lut) for c in (inp.codes_gate, inp.codes_up, inp.codes_down))
+    if mode == "exact":
+        return tuple(trellis.decode_exact(c[e], inp.lut, sc[e])
+                     for c, sc in ((inp.codes_gate, inp.scale_gate), (inp.codes_up, inp.scale_up),
+                                   (inp.codes_down, inp.scale_down)))
+    raise ValueError(mode)
+
+
+def expert_pairs(inp, e: int, pids, mode: str = "declared", weights=None):
+    """Outputs y [len(pids), H] and intermediates h of expert e for the binned pairs `pids`
+    (pair id p = t*k + j reads token t = p // k).  `weights`, if given, is
+    decode_expert(inp, e, mode), so one decode can serve several calls."""
+    k = inp.shape.top_k
+    pids = np.asarray(pids, np.int64)
+    xr = bf16_bits_to_f64(inp.x_bf16[pids // k])
+    wg, wu, wd = weights if weights is not None else decode_expert(inp, e, mode)
+    if mode == "declared":
+        return expert_declared(xr, wg, wu, wd, inp.scale_gate[e], inp.scale_up[e], inp.scale_down[e])
+    if mode == "exact":
+        return expert_exact(xr, wg, wu, wd)
+    raise ValueError(mode)
+
+
+def combine(y: dict, topk_w: np.ndarray, tokens, k: int, hidden: int) -> np.ndarray:
+    """out[t] = sum_{j=0..k-1} w[t, j] * y[t*k + j], j ascending (float64), for each token listed."""
+    acc = np.zeros((len(tokens), hidden), np.float64)
+    for r, t in enumerate(tokens):
+        for j in range(k):
+            acc[r] += np.float64(topk_w[t, j]) * y[t * k + j]
+    return acc
+
+
+def finish(acc: np.ndarray, out_dtype: str) -> np.ndarray:
+    """The single final cast: fp32 values, or bf16 bit patterns (via fp32, nearest-even)."""
+    return _finish(acc, out_dtype)
+
+
 def moe_forward(inp, tile_m: int = 16, mode: str = "declared", out_dtype: str = "f32",
                 tokens=None) -> dict:
     """Route, bin, run each woken expert over its binned pairs, combine.
@@ -72,7 +113,7 @@ def moe_forward(inp, tile_m: int = 16, mode: str = "declared", out_dtype: str = 
     are still computed for the whole batch).
     """
     s = inp.shape
-    E, k, H, I = s.num_experts, s.top_k, s.hidden, s.inter
+    E, k, H = s.num_experts, s.top_k, s.hidden
     n = inp.logits.shape[0]
     idx, w = routing.route_topk(inp.logits, k)
     bins = routing.bin_pairs(idx, E, tile_m)
@@ -86,27 +127,12 @@ def moe_forward(inp, tile_m: int = 16, mode: str = "declared", out_dtype: str = 
             pids = np.array([p for p in pids if int(p) // k in want], np.int32)
         if len(pids) == 0:
             continue
-        xr = bf16_bits_to_f64(inp.x_bf16[pids // k])
-        if mode == "declared":
-            wg = trellis.decode_declared(inp.codes_gate[e], inp.lut)
-            wu = trellis.decode_declared(inp.codes_up[e], inp.lut)
-            wd = trellis.decode_declared(inp.codes_down[e], inp.lut)
-            ye, he = expert_declared(xr, wg, wu, wd, inp.scale_gate[e], inp.scale_up[e], inp.scale_down[e])
-        elif mode == "exact":
-            wg = trellis.decode_exact(inp.codes_gate[e], inp.lut, inp.scale_gate[e])
-            wu = trellis.decode_exact(inp.codes_up[e], inp.lut, inp.scale_up[e])
-            wd = trellis.decode_exact(inp.codes_down[e], inp.lut, inp.scale_down[e])
-            ye, he = expert_exact(xr, wg, wu, wd)
-        else:
-            raise ValueError(mode)
+        ye, he = expert_pairs(inp, e, pids, mode)
         for q, p in enumerate(pids):
             y[int(p)] = ye[q]
             h_sorted[int(p)] = he[q]
     toks = list(range(n)) if tokens is None else [int(t) for t in tokens]
-    acc = np.zeros((len(toks), H), np.float64)
-    for r, t in enumerate(toks):
-        for j in range(k):
-            acc[r] += np.float64(w[t, j]) * y[t * k + j]
+    acc = combine(y, w, toks, k, H)
     return {"out": _finish(acc, out_dtype), "out_f64": acc, "topk_idx": idx, "topk_w": w,
             "bins": bins, "y": y, "h": h_sorted}
 
