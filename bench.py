@@ -1,14 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the trellis-quantized MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--arm auto|gemv|grouped|dequant]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--curve NAMES]
 
 A step is one qtip_moe_forward (route, bin, gate+up, down, combine) over one batch of the
-workload, with weights and inputs already resident in HBM.  The default workload is the
-V4-shaped decode layer (E=256, top-6, hidden 4096, expert intermediate 2048, n=32 tokens,
-uniform routing, seed 0).  Prints ONE JSON line: tokens/s over the timed steps, the
-roofline of the dominant kernel (gate+up, packed-weight bytes per launch over its
-HIP-event-measured duration, against 8 TB/s), and the CPU oracle timed on a bounded sample.
+workload, with weights and inputs already resident in HBM.  The headline workload is the
+largest V4-shaped layer (E=256, top-6, hidden 4096, expert intermediate 2048, n=1024 tokens,
+uniform routing, seed 0), in the plan a caller of that size uses (max_tokens = n, automatic arm
+and kernel configuration, bf16 output).  Prints ONE JSON line: tokens/s over the timed steps,
+the roofline of the dominant kernel (gate+up: packed-weight bytes per launch over its
+HIP-event-measured duration, against 8 TB/s), the CPU oracle timed on a bounded sample over
+the host's cores, and in "detail.curve" the same measurements for the other workloads (the
+metric against token count n: V4 n = 1, 32, 128, 512, 683, Zipf(1.1) n = 256, and the tiny
+layer).
 
 Other modes (not used by the driver):
   --sweep PATH        both arms forced at n in {8,16,32,64,128,256,512,683,1024}; JSON lines to PATH
@@ -284,19 +288,46 @@ def measure_gather_ceiling(rounds=2000):
     return q.qtip_measure_lut_gather(rounds, sink, n, torch.cuda.current_stream())
 
 
-def cpu_baseline(inp, n_sample):
-    """The oracle as it stands, one BLAS thread, on the first n_sample tokens of the batch."""
-    from threadpoolctl import threadpool_limits
-    from oracle import moe
-    toks = list(range(n_sample))
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        moe.moe_forward(inp, tokens=toks)
-        dt = time.perf_counter() - t0
-    return {"value": n_sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_sample} of the {inp.shape.n_tokens} tokens of this batch: routing and binning of the "
-                      f"whole batch, then the declared-mode layer for those tokens (decode of every expert they "
-                      f"use), numpy float64, 1 thread, {dt:.1f} s"}
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, n_experts=-1):
+    """The oracle as it stands (declared mode, numpy float64) over a process pool on the host's
+    cores, one BLAS thread per worker: routing and binning of the batch, each woken expert
+    decoded once and evaluated on all its pairs, and the combine.  n_experts < 0 times the whole
+    layer; otherwise only the first n_experts woken experts are evaluated (no combine) and the
+    time is scaled to every woken expert.  Must run before this process touches the GPU (the
+    pool forks)."""
+    import numpy as np
+    from oracle import pool, routing
+    s = inp.shape
+    idx, _ = routing.route_topk(inp.logits, s.top_k)
+    woken = [int(e) for e in np.nonzero(np.bincount(idx.reshape(-1), minlength=s.num_experts))[0]]
+    whole = n_experts < 0 or n_experts >= len(woken)
+    sample = woken if whole else woken[:max(1, n_experts)]
+    workers = pool.default_workers()
+    t0 = time.perf_counter()
+    pool.layer_outputs({"layer": inp}, workers, experts=None if whole else sample)
+    dt = time.perf_counter() - t0
+    full_s = dt * len(woken) / len(sample)
+    what = (f"the whole {s.n_tokens}-token layer (routing and binning, all {len(woken)} woken experts each "
+            f"decoded once and evaluated on all its pairs, the combine)" if whole else
+            f"{len(sample)} of the {len(woken)} woken experts of this {s.n_tokens}-token batch (routing and "
+            f"binning of the whole batch, then each sampled expert decoded once and evaluated on all its "
+            f"pairs), scaled by {len(woken)}/{len(sample)} to the whole layer")
+    return {"value": s.n_tokens / full_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{what}; {dt:.1f} s wall on {workers} worker processes with one BLAS thread each",
+            "host": {"os_cpu_count": os.cpu_count(), "workers": workers, "blas_threads_per_worker": 1,
+                     "cpu_model": cpu_model()},
+            "seconds_measured": dt, "seconds_layer": full_s}
 
 
 def calibrate_copy():
@@ -343,16 +374,114 @@ def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=N
             r.close()
 
 
+HEADLINE = "v4_full_n1024"
+CURVE = ["v4_decode_n1", "v4_decode_n32", "v4_mid_n128", "v4_mid_n512", "v4_full_n683", "v4_zipf_n256", "tiny"]
+
+
+def draw_layers(names):
+    """Seeded inputs for each workload; V4 layers with uniform routing share one weight draw (the
+    draw make_workload makes for each of them), so the device holds one copy of the weights."""
+    import moe_inputs
+    W = moe_inputs.WORKLOADS
+    shared = [n for n in names if W[n].num_experts == 256 and W[n].routing == "uniform"]
+    out = {}
+    if shared:
+        multi = moe_inputs.make_inputs_multi(W[shared[0]], sorted({W[n].n_tokens for n in shared}), seed=0)
+        out.update({n: multi[W[n].n_tokens] for n in shared})
+    for n in names:
+        if n not in out:
+            out[n] = moe_inputs.make_workload(n, seed=0)
+    return out
+
+
+def measure_workload(name, inp, weights, args, gather_measured, full=False):
+    """Times one workload in the plan a caller of that size uses (max_tokens = n, automatic arm
+    unless --arm, bf16 output unless --out-dtype) and returns its record."""
+    s = inp.shape
+    runner = Runner(inp, args.arm, s.n_tokens, args.out_dtype, weights=weights, variant=args.variant)
+    runner.bind(inp)
+    q = runner.q
+    arm_code = q.qtip_moe_select_arm(runner.plan, s.n_tokens)
+    arm = {q.QTIP_ARM_GROUPED: "grouped", q.QTIP_ARM_DEQUANT: "dequant"}.get(arm_code, "gemv")
+    q.qtip_moe_log_engaged(runner.plan, s.n_tokens)
+    # the timed loop records no stage events (they would add gaps between the kernels); the stage
+    # breakdown comes from a second, profiled loop of the same forward
+    res = timed(runner, args.steps, args.warmup, profile=False)
+    res["prof"] = timed(runner, min(args.steps, 100), 2, profile=True)["prof"]
+    counts, n_tiles = runner.routing_counts()
+    sched = q.qtip_moe_plan_schedule(runner.plan, s.n_tokens)
+    extra = {}
+    if full:
+        extra["router_gemm"] = measure_router(runner, inp)
+        extra["graph_replay"] = measure_graph(runner, args.steps)
+    runner.close()
+    if res["wall_s"] <= 0 or res["prof"]["n_forwards"] <= 0:
+        print(f"bench: no time or no profiled forwards recorded for {name}", file=sys.stderr)
+        sys.exit(2)
+    counters = res["stats"]
+    want = {"grouped": ("grouped_launches", 2), "gemv": ("gemv_launches", 2), "dequant": ("dequant_launches", 4)}[arm]
+    vkey = {"grouped": "grouped_variant_launches", "gemv": "gemv_variant_launches"}.get(arm)
+    variants_ok = vkey is None or all(counters[vkey][sched[p]["variant"]] >= args.steps for p in ("gate_up", "down"))
+    if counters[want[0]] != want[1] * args.steps or not variants_ok:
+        print(f"bench: launch counters do not show the {arm} arm and its configurations for {name}: {counters}",
+              file=sys.stderr)
+        sys.exit(2)
+    fig = schedule_figures(counts, s, arm, sched)
+    nf = res["prof"]["n_forwards"]
+    stage_ms = {k: v / nf for k, v in res["prof"].items() if k != "n_forwards"}
+    ms_per_step = res["wall_s"] * 1e3 / args.steps
+    layer_gpu_s = res["gpu_ms"] * 1e-3 / args.steps
+    gu_s, dn_s = stage_ms["gate_up"] * 1e-3, stage_ms["down"] * 1e-3
+    gu_gbs = fig["bytes"]["gate_up"] / gu_s / 1e9
+    layer_bytes = fig["bytes"]["gate_up"] + fig["bytes"]["down"]
+    gu_syms = fig["symbols_sched"]["gate_up"] / gu_s
+    layer_syms = (fig["symbols_sched"]["gate_up"] + fig["symbols_sched"]["down"]) / (gu_s + dn_s)
+    flops = 6.0 * s.n_tokens * s.top_k * s.hidden * s.inter
+    rec = {
+        "workload": name, "n_tokens": s.n_tokens, "routing": s.routing,
+        "shape": {"experts": s.num_experts, "top_k": s.top_k, "hidden": s.hidden, "inter": s.inter},
+        "arm": arm, "variant": {"gate_up": sched["gate_up"]["variant"], "down": sched["down"]["variant"]},
+        "tokens_per_s": s.n_tokens * args.steps / res["wall_s"], "ms_per_step": ms_per_step,
+        "gpu_event_ms_per_step": layer_gpu_s * 1e3, "stage_ms": stage_ms,
+        "gate_up_packed_bytes": fig["bytes"]["gate_up"], "down_packed_bytes": fig["bytes"]["down"],
+        "gate_up_packed_gbs": gu_gbs, "gate_up_hbm_frac": gu_gbs / HBM_PEAK_GBS,
+        "layer_packed_gbs": layer_bytes / layer_gpu_s / 1e9,
+        "layer_hbm_frac": layer_bytes / layer_gpu_s / 1e9 / HBM_PEAK_GBS,
+        "woken_experts": fig["woken"], "max_pairs_per_expert": fig["max_count"], "m_tiles": n_tiles,
+        "decodes": fig["decodes"],
+        "decode_roofline": {"bound": "lds_gather", "unit": "LUT lookups/s",
+                            "gate_up_achieved": gu_syms, "expert_passes_achieved": layer_syms,
+                            "peak_measured": gather_measured, "gate_up_frac_measured": gu_syms / gather_measured,
+                            "expert_passes_frac_measured": layer_syms / gather_measured,
+                            "peak_model": LDS_GATHER_PEAK, "gate_up_frac_model": gu_syms / LDS_GATHER_PEAK,
+                            "valu_peak": DECODE_VALU_PEAK_SYMS, "gate_up_frac_valu": gu_syms / DECODE_VALU_PEAK_SYMS,
+                            "expert_passes_frac_valu": layer_syms / DECODE_VALU_PEAK_SYMS},
+        # MFMA work of the layer (g, u and y: 2 n k H I flops each) against the dense bf16 peak: the
+        # contraction is thin, so this stays a few percent at most
+        "mfma": {"flops": flops, "layer_tflops": flops / layer_gpu_s / 1e12,
+                 "layer_frac": flops / layer_gpu_s / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "schedule": sched,
+        "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "dequant_launches",
+                                                     "route_launches", "combine_launches", "router_launches",
+                                                     "gemv_variant_launches", "grouped_variant_launches")},
+    }
+    rec.update(extra)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="v4_decode_n32")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--curve", default=",".join(CURVE), help="comma-separated workloads measured beside the "
+                    "headline and reported in detail.curve ('' for none)")
     ap.add_argument("--arm", choices=["auto", "gemv", "grouped", "dequant"], default="auto")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 = the plan's choice, 1..10 fixed; see qtip_moe_plan_schedule)")
-    ap.add_argument("--cpu-sample", type=int, default=6, help="tokens the CPU oracle is timed on, about 10 s (0: skip)")
+    ap.add_argument("--cpu-experts", type=int, default=-1, help="woken experts the CPU oracle is timed on (-1: the "
+                    "whole layer, about 13 s on 16 cores at n=1024; 0: skip)")
     ap.add_argument("--sweep", metavar="PATH", default=None)
     ap.add_argument("--sweep-arms", default="gemv,grouped")
     ap.add_argument("--sweep-layouts", default="0", help="grouped-arm activation layouts to sweep (0 auto, 1 rows, "
@@ -369,105 +498,80 @@ def main():
                           "grouped" if args.arm == "grouped" else args.arm, args.traffic_command)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (the path has no multi-GPU mode); got --gpus {args.gpus}",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU only: the path is measured on one GPU's share and has no multi-GPU "
+              f"mode; got --gpus {args.gpus}", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1:
         print("--steps must be >= 1", file=sys.stderr)
         sys.exit(2)
-
-    import torch
     import moe_inputs
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        calibrate_copy()
     if args.sweep:
+        import torch
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(2)
+        if args.calibrate_copy:
+            calibrate_copy()
         n_list = [int(x) for x in args.sweep_n.split(",")] if args.sweep_n else None
         run_sweep(args.sweep, args.steps, args.warmup, args.variant, tuple(args.sweep_arms.split(",")), n_list,
                   tuple(int(x) for x in args.sweep_layouts.split(",")))
         return
 
-    log(f"bench: drawing workload {args.workload}")
-    inp = moe_inputs.make_workload(args.workload, seed=0)
-    s = inp.shape
-    runner = Runner(inp, args.arm, s.n_tokens, args.out_dtype, variant=args.variant)
-    runner.bind(inp)
-    arm_code = runner.q.qtip_moe_select_arm(runner.plan, s.n_tokens)
-    arm = {runner.q.QTIP_ARM_GROUPED: "grouped", runner.q.QTIP_ARM_DEQUANT: "dequant"}.get(arm_code, "gemv")
-    log(runner.q.qtip_moe_engaged_line(runner.plan, s.n_tokens))
-    # the timed loop records no stage events (they would add gaps between the kernels); the stage
-    # breakdown comes from a second, profiled loop of the same forward
-    res = timed(runner, args.steps, args.warmup, profile=False)
-    res["prof"] = timed(runner, min(args.steps, 100), 2, profile=True)["prof"]
-    counts, n_tiles = runner.routing_counts()
-    sched = runner.q.qtip_moe_plan_schedule(runner.plan, s.n_tokens)
-    router = measure_router(runner, inp)
-    graph = measure_graph(runner, args.steps)
-    runner.close()
+    curve = [c for c in args.curve.split(",") if c and c != args.workload]
+    for name in [args.workload] + curve:
+        if name not in moe_inputs.WORKLOADS:
+            print(f"unknown workload {name!r}", file=sys.stderr)
+            sys.exit(2)
+    log(f"bench: drawing workloads {[args.workload] + curve}")
+    layers = draw_layers([args.workload] + curve)
+    # the CPU oracle runs first: its worker pool forks, and this process has not touched the GPU yet
+    cpu = cpu_baseline(layers[args.workload], args.cpu_experts) if args.cpu_experts != 0 else None
+    if cpu:
+        log(f"bench: cpu baseline {cpu['value']:.3f} tokens/s ({cpu['sample']})")
 
-    if res["wall_s"] <= 0 or res["prof"]["n_forwards"] <= 0:
-        print("bench: no time or no profiled forwards recorded", file=sys.stderr)
+    import torch
+    from moe_inputs.device import weights_to_device
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
         sys.exit(2)
-    fig = schedule_figures(counts, s, arm, sched)
-    nf = res["prof"]["n_forwards"]
-    stage_ms = {k: v / nf for k, v in res["prof"].items() if k != "n_forwards"}
-    ms_per_step = res["wall_s"] * 1e3 / args.steps
-    tokens_per_s = s.n_tokens * args.steps / res["wall_s"]
-    gu_s = stage_ms["gate_up"] * 1e-3
-    achieved = fig["bytes"]["gate_up"] / gu_s / 1e9
-    layer_bytes = fig["bytes"]["gate_up"] + fig["bytes"]["down"]
-    layer_gpu_s = res["gpu_ms"] * 1e-3 / args.steps
-    counters = res["stats"]
-    if (arm == "grouped" and counters["grouped_launches"] != 2 * args.steps) or \
-       (arm == "gemv" and counters["gemv_launches"] != 2 * args.steps) or \
-       (arm == "dequant" and counters["dequant_launches"] != 4 * args.steps):
-        print(f"bench: launch counters do not show the {arm} arm: {counters}", file=sys.stderr)
-        sys.exit(2)
-
+    if args.calibrate_copy:
+        calibrate_copy()
     gather_measured = measure_gather_ceiling()
-    gu_syms = fig["symbols_sched"]["gate_up"] / gu_s
-    cpu = cpu_baseline(inp, args.cpu_sample) if args.cpu_sample > 0 else None
+    import numpy as np
+    dev_weights = []   # (host inputs, device weights): one device copy per distinct weight draw
+    fields = ("lut", "codes_gate", "codes_up", "codes_down", "scale_gate", "scale_up", "scale_down")
+
+    def weights_for(name):
+        inp = layers[name]
+        for host, dw in dev_weights:
+            if all(getattr(host, f).shape == getattr(inp, f).shape and np.array_equal(getattr(host, f), getattr(inp, f))
+                   for f in fields):
+                return dw
+        dw = weights_to_device(inp)
+        dev_weights.append((inp, dw))
+        return dw
+
+    head = measure_workload(args.workload, layers[args.workload], weights_for(args.workload), args, gather_measured,
+                            full=True)
+    points = []
+    for name in curve:
+        log(f"bench: curve point {name}")
+        points.append(measure_workload(name, layers[name], weights_for(name), args, gather_measured))
+    s = layers[args.workload].shape
     line = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "experts": s.num_experts, "top_k": s.top_k, "hidden": s.hidden,
-                   "inter": s.inter, "n_tokens": s.n_tokens, "routing": s.routing, "seed": 0, "arm": arm,
-                   "out_dtype": args.out_dtype,
-                   "variant": {"gate_up": sched["gate_up"]["variant"], "down": sched["down"]["variant"]}},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(args.workload, arm)},
+                   "inter": s.inter, "n_tokens": s.n_tokens, "routing": s.routing, "seed": 0, "arm": head["arm"],
+                   "out_dtype": args.out_dtype, "max_tokens": s.n_tokens, "variant": head["variant"]},
+        "roofline": {"bound": "hbm", "achieved": head["gate_up_packed_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["gate_up_packed_gbs"] / HBM_PEAK_GBS,
+                     "traffic": read_traffic(args.workload, head["arm"])},
         "cpu_baseline": cpu,
-        "detail": {
-            "dominant_kernel": f"expert_kernel gate+up ({arm} arm)",
-            "stage_ms": stage_ms,
-            "layer_packed_gbs": layer_bytes / layer_gpu_s / 1e9,
-            "layer_packed_frac": layer_bytes / layer_gpu_s / 1e9 / HBM_PEAK_GBS,
-            "gate_up_packed_bytes": fig["bytes"]["gate_up"], "down_packed_bytes": fig["bytes"]["down"],
-            "woken_experts": fig["woken"], "max_pairs_per_expert": fig["max_count"], "m_tiles": n_tiles,
-            "decode_units": fig["units"], "decodes": fig["decodes"],
-            "decode_roofline": {"bound": "lds_gather", "kernel": "gate+up", "achieved": gu_syms,
-                                "unit": "LUT lookups/s", "peak_model": LDS_GATHER_PEAK,
-                                "frac_model": gu_syms / LDS_GATHER_PEAK, "peak_measured": gather_measured,
-                                "frac_measured": gu_syms / gather_measured,
-                                "valu_peak": DECODE_VALU_PEAK_SYMS, "frac_valu": gu_syms / DECODE_VALU_PEAK_SYMS},
-            # MFMA work of the layer (g, u and y: 2 n k H I flops each) against
-            # the dense bf16 peak: the contraction is thin, so this stays a few percent at most
-            "mfma": {"flops": 6.0 * s.n_tokens * s.top_k * s.hidden * s.inter,
-                     "layer_tflops": 6.0 * s.n_tokens * s.top_k * s.hidden * s.inter / layer_gpu_s / 1e12,
-                     "layer_frac": 6.0 * s.n_tokens * s.top_k * s.hidden * s.inter / layer_gpu_s / 1e12
-                     / MFMA_BF16_PEAK_TFLOPS,
-                     "gate_up_frac": 4.0 * s.n_tokens * s.top_k * s.hidden * s.inter / gu_s / 1e12
-                     / MFMA_BF16_PEAK_TFLOPS},
-            "schedule": sched,
-            "graph_replay": graph,
-            "router_gemm": router,
-            "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "dequant_launches",
-                                                         "route_launches", "combine_launches", "router_launches")},
-            "kernel_source_sha": kernel_source_sha(),
-        },
+        "detail": {"dominant_kernel": f"expert_kernel gate+up ({head['arm']} arm)", "headline": head,
+                   "curve": points, "gather_ceiling_measured": gather_measured,
+                   "kernel_source_sha": kernel_source_sha()},
     }
     print(json.dumps(line), flush=True)
 

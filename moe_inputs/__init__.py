@@ -68,6 +68,8 @@ WORKLOADS = {
     "v4_full_n683": MoEShape(256, 6, 4096, 2048, 683),
     "v4_full_n1024": MoEShape(256, 6, 4096, 2048, 1024),
     "v4_zipf_n256": MoEShape(256, 6, 4096, 2048, 256, routing="zipf", zipf_s=1.1),
+    # a one-token decode step of the same layer: the low-fill extreme, reported beside the others
+    "v4_decode_n1": MoEShape(256, 6, 4096, 2048, 1),
 }
 
 
