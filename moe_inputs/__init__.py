@@ -22,6 +22,10 @@ bf16 values are carried as their uint16 bit patterns.
 For layers that start from hidden states, a router weight [E, H] of N(0, 1/H)
 samples rounded to bf16 comes from a second generator, PCG64([seed, 1]), so the
 draws above do not change; with N(0,1) activations its logits are close to N(0,1).
+
+Layers of the LUT rung (shape.rung == "lut") draw, in the LUT's place, a codebook of
+2**9 two-dimensional fp16 N(0,1) samples ([512, 2], carried in the `lut` field); the
+codes, scales, activations and logits are drawn exactly as for the bitshift rung.
 """
 from __future__ import annotations
 
@@ -42,13 +46,14 @@ class MoEShape:
     n_tokens: int
     routing: str = "uniform"      # "uniform" (logits N(0,1)) or "zipf"
     zipf_s: float = 1.1
+    rung: str = "bitshift"        # "bitshift" (65536-entry LUT) or "lut" (512 x 2 codebook)
 
 
 @dataclasses.dataclass
 class MoEInputs:
     shape: MoEShape
     seed: int
-    lut: np.ndarray          # [65536] float16
+    lut: np.ndarray          # [65536] float16 (bitshift rung) or [512, 2] float16 codebook (LUT rung)
     codes_gate: np.ndarray   # [E, I, H/4] uint8
     codes_up: np.ndarray     # [E, I, H/4] uint8
     codes_down: np.ndarray   # [E, H, I/4] uint8
@@ -70,7 +75,17 @@ WORKLOADS = {
     "v4_zipf_n256": MoEShape(256, 6, 4096, 2048, 256, routing="zipf", zipf_s=1.1),
     # a one-token decode step of the same layer: the low-fill extreme, reported beside the others
     "v4_decode_n1": MoEShape(256, 6, 4096, 2048, 1),
+    # the same layers with LUT-rung experts (a 512 x 2 codebook instead of the 65536-entry LUT)
+    "lut_tiny": MoEShape(8, 2, 256, 128, 16, rung="lut"),
+    "lut_v4_decode_n1": MoEShape(256, 6, 4096, 2048, 1, rung="lut"),
+    "lut_v4_decode_n32": MoEShape(256, 6, 4096, 2048, 32, rung="lut"),
+    "lut_v4_mid_n128": MoEShape(256, 6, 4096, 2048, 128, rung="lut"),
+    "lut_v4_mid_n512": MoEShape(256, 6, 4096, 2048, 512, rung="lut"),
+    "lut_v4_full_n1024": MoEShape(256, 6, 4096, 2048, 1024, rung="lut"),
+    "lut_v4_zipf_n256": MoEShape(256, 6, 4096, 2048, 256, routing="zipf", zipf_s=1.1, rung="lut"),
 }
+
+LUT_RUNG_BITS = 9   # codebook index bits of the LUT rung (2**9 entries of two fp16 values)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -101,6 +116,14 @@ def _draw_experts(rng: np.random.Generator, s: MoEShape):
     return cg, cu, cd, sg, su, sd
 
 
+def _draw_table(rng: np.random.Generator, s: MoEShape) -> np.ndarray:
+    if s.rung == "bitshift":
+        return rng.standard_normal(LUT_SIZE).astype(np.float16)
+    if s.rung == "lut":
+        return rng.standard_normal((1 << LUT_RUNG_BITS, 2)).astype(np.float16)
+    raise ValueError(f"unknown rung {s.rung!r}")
+
+
 def _draw_logits(rng: np.random.Generator, s: MoEShape) -> np.ndarray:
     n, E = s.n_tokens, s.num_experts
     if s.routing == "uniform":
@@ -123,7 +146,7 @@ def make_inputs(shape: MoEShape, seed: int = 0, n_tokens: Optional[int] = None) 
     if s.hidden % 4 or s.inter % 4:
         raise ValueError("hidden and inter must be multiples of 4 (4 symbols per byte)")
     rng = np.random.Generator(np.random.PCG64(seed))
-    lut = rng.standard_normal(LUT_SIZE).astype(np.float16)
+    lut = _draw_table(rng, s)
     cg, cu, cd, sg, su, sd = _draw_experts(rng, s)
     x = f32_to_bf16_bits(rng.standard_normal((s.n_tokens, s.hidden)).astype(np.float32))
     logits = _draw_logits(rng, s)
@@ -135,7 +158,7 @@ def make_inputs_multi(shape: MoEShape, n_list, seed: int = 0) -> dict:
     make_inputs(shape, seed, n) would draw (the generator state after the weights is
     replayed for each n).  Returns {n: MoEInputs}, all sharing the weight arrays."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    lut = rng.standard_normal(LUT_SIZE).astype(np.float16)
+    lut = _draw_table(rng, shape)
     weights = _draw_experts(rng, shape)
     state = rng.bit_generator.state
     out = {}

@@ -9,7 +9,9 @@ float64 except at the rounding points the path declares (bf16 LUT values, bf16
 intermediate activation, final output cast), which are modelled explicitly.
 
 Modules
-  trellis  -- bitstream -> symbols -> 16-bit window state -> LUT value (decode)
+  trellis  -- bitstream -> symbols -> 16-bit window state -> LUT value (decode, bitshift rung)
+  lut_rung -- bitstream -> 9-bit pair state -> 2-D codebook vector (decode, LUT rung)
+  pool     -- the layer over a process pool for large layers (scheduling only)
   routing  -- top-k routing, softmax over the selected logits, expert binning, m-tile map
   fill     -- the closed-form m-tile fill model and the grouped-arm dispatch predicate
   moe      -- one MoE layer: gated experts, weighted combine, and a separately written
@@ -17,6 +19,6 @@ Modules
   numerics -- the oracle's own bf16 rounding
 
 Parity pins: every function is pinned by tests/test_oracle_*.py; the one item
-left "parity unpinned" is compatibility of the bit layout with real QTIP
-checkpoints (no checkpoint or encoder exists in these inputs).
+left "parity unpinned" is compatibility of the bit layouts (both rungs) with real
+QTIP checkpoints (no checkpoint or encoder exists in these inputs).
 """

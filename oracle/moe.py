@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import routing, trellis
+from . import lut_rung, routing, trellis
 from .numerics import bf16_bits_to_f64, bf16_round, f64_to_bf16_bits
 
 
@@ -62,13 +62,25 @@ def _finish(acc: np.ndarray, out_dtype: str) -> np.ndarray:
     raise ValueError(out_dtype)
 
 
+def _decoder(inp):
+    """The decode of the layer's rung: the bitshift rung's 16-bit-window LUT (oracle.trellis) or
+    the LUT rung's 2-D codebook (oracle.lut_rung)."""
+    rung = getattr(inp.shape, "rung", "bitshift")
+    if rung == "bitshift":
+        return trellis
+    if rung == "lut":
+        return lut_rung
+    raise ValueError(rung)
+
+
 def decode_expert(inp, e: int, mode: str = "declared"):
-    """Expert e's gate, up and down weights: unscaled bf16(LUT[state]) in declared mode (the
-    scales are applied after each dot product), float32(LUT) * float32(scale) in exact mode."""
+    """Expert e's gate, up and down weights: unscaled bf16 table values in declared mode (the
+    scales are applied after each dot product), float32(table) * float32(scale) in exact mode."""
+    dec = _decoder(inp)
     if mode == "declared":
-        return tuple(trellis.decode_declared(c[e], inp.lut) for c in (inp.codes_gate, inp.codes_up, inp.codes_down))
+        return tuple(dec.decode_declared(c[e], inp.lut) for c in (inp.codes_gate, inp.codes_up, inp.codes_down))
     if mode == "exact":
-        return tuple(trellis.decode_exact(c[e], inp.lut, sc[e])
+        return tuple(dec.decode_exact(c[e], inp.lut, sc[e])
                      for c, sc in ((inp.codes_gate, inp.scale_gate), (inp.codes_up, inp.scale_up),
                                    (inp.codes_down, inp.scale_down)))
     raise ValueError(mode)
@@ -155,7 +167,7 @@ def dense_reference(inp, mode: str = "declared", out_dtype: str = "f32") -> np.n
         for j in range(k):
             e = int(idx[t, j])
             if e not in dense:
-                dense[e] = [trellis.dense_weights_bruteforce(c[e], inp.lut, sc[e], declared)
+                dense[e] = [_decoder(inp).dense_weights_bruteforce(c[e], inp.lut, sc[e], declared)
                             for c, sc in ((inp.codes_gate, inp.scale_gate), (inp.codes_up, inp.scale_up),
                                           (inp.codes_down, inp.scale_down))]
             wg, wu, wd = dense[e]
