@@ -44,6 +44,8 @@ LDS_GATHER_PEAK = 256 * 2.4e9 * 64 / (2 * 3.532)
 SWEEP_N = [8, 16, 32, 64, 128, 256, 512, 683, 1024]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["trellis_quantized_moe_expert_amd/csrc/expert.hip",
+                  "trellis_quantized_moe_expert_amd/csrc/expert_body.h",
+                  "trellis_quantized_moe_expert_amd/csrc/expert_lut.hip",
                   "trellis_quantized_moe_expert_amd/csrc/qtip_internal.h"]
 
 
@@ -72,8 +74,9 @@ class Runner:
         arm_code = {"auto": q.QTIP_ARM_AUTO, "gemv": q.QTIP_ARM_GEMV, "grouped": q.QTIP_ARM_GROUPED,
                     "dequant": q.QTIP_ARM_DEQUANT}[arm]
         od = q.QTIP_OUT_BF16 if out_dtype == "bf16" else q.QTIP_OUT_F32
+        rung = q.QTIP_RUNG_LUT if s.rung == "lut" else q.QTIP_RUNG_BITSHIFT
         self.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens, arm_code,
-                                                variant, od, 0, act_layout=act_layout), 0)
+                                                variant, od, 0, act_layout=act_layout, rung=rung), 0)
         self.info = q.qtip_moe_plan_info(self.plan)
         self.ws = torch.empty(self.info["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
         self.dw = weights if weights is not None else weights_to_device(inp)

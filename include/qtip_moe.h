@@ -34,14 +34,19 @@
  *    error text is available from qtip_last_error_detail()).
  *  - bf16 and fp16 values are passed as their 16-bit patterns.
  *
- * Weight format (reading of the pages, which give only "packed 2-bit bytes"):
+ * Weight formats (readings of the pages, which give only "packed 2-bit bytes" and name two
+ * rungs, the bitshift rung "qtip2b" and the LUT rung "qtip2"):
  *  - A matrix with `rows` outputs and `cols` inputs is `rows` independent rows
- *    of cols/4 bytes.  Symbol c of a row = bits [2(c%4), 2(c%4)+2) of byte c/4.
- *  - The 16-bit state of weight (r, c) is the 8-symbol window starting at c,
- *    read circularly within the row: state = sum_j sym((c+j) mod cols) * 4^j.
- *  - weight(r, c) = bf16(lut[state]) * scale[r]: the fp16 LUT value is rounded
- *    to bf16 (nearest-even), the dot product accumulates in fp32, and the fp16
- *    per-output-row scale multiplies the fp32 sum.
+ *    of cols/4 bytes.  Symbol c of a row = bits [2(c%4), 2(c%4)+2) of byte c/4; the row's
+ *    stream bits are its bytes' bits, little-endian, read circularly.
+ *  - Bitshift rung: the 16-bit state of weight (r, c) is the 8-symbol window starting at c:
+ *    state = sum_j sym((c+j) mod cols) * 4^j; weight(r, c) = bf16(lut[state]) * scale[r], with
+ *    lut the 65536-entry fp16 table.
+ *  - LUT rung: weights come in pairs (2i, 2i+1); the pair's state is the 9 stream bits from bit
+ *    4i on (the low 9 bits of the bitshift state of weight 2i), and the pair's two weights are
+ *    bf16(cb[state][0]), bf16(cb[state][1]) times scale[r], with cb the 512 x 2 fp16 codebook.
+ *  - Either way the fp16 table value is rounded to bf16 (nearest-even), the dot product
+ *    accumulates in fp32, and the fp16 per-output-row scale multiplies the fp32 sum.
  *  - Layer: h = silu(x Wg^T) * (x Wu^T) rounded to bf16; y = h Wd^T;
  *    out[t] = sum_{j<k} w[t,j] * y(t, j) in fp32 (j ascending), then cast.
  *  - Routing: the k largest logits of a token in descending order (ties go to
@@ -73,6 +78,9 @@ typedef enum qtip_status {
 enum { QTIP_ARM_AUTO = 0, QTIP_ARM_GEMV = 1, QTIP_ARM_GROUPED = 2, QTIP_ARM_DEQUANT = 3 };
 enum { QTIP_OUT_BF16 = 0, QTIP_OUT_F32 = 1 };
 enum { QTIP_ACT_AUTO = 0, QTIP_ACT_ROWS = 1, QTIP_ACT_FRAGMENTS = 2 };
+/* The two 2-bit rungs (weight formats) of the expert matrices; see "Weight formats" above. */
+enum { QTIP_RUNG_BITSHIFT = 0, QTIP_RUNG_LUT = 1 };
+#define QTIP_LUT_RUNG_BITS 9 /* pair-state bits of the LUT rung: a 2^9 x 2 codebook */
 
 /* Decode-regime floor: n <= 8 tokens always take the GEMV arm (m-tile page, "The fix"). */
 #define QTIP_DECODE_REGIME_MAX_TOKENS 8
@@ -119,6 +127,9 @@ typedef struct qtip_moe_desc {
                            woken expert), QTIP_ACT_ROWS (gathered rows) or QTIP_ACT_FRAGMENTS (every
                            expert's bin padded to 16 pairs and stored in MFMA fragment order: h always,
                            x packed by an extra pass) */
+  int32_t rung;         /* weight format of the experts: QTIP_RUNG_BITSHIFT (a 16-bit window per weight into
+                           the 65536-entry LUT) or QTIP_RUNG_LUT (a 9-bit state per weight pair into the
+                           512 x 2 codebook); see the weight formats above */
 } qtip_moe_desc;
 
 typedef struct qtip_moe_plan_s* qtip_moe_plan_t;
@@ -130,7 +141,7 @@ typedef struct qtip_moe_weights {
   const uint16_t* scale_gate; /* [E][I] fp16, one per output row */
   const uint16_t* scale_up;   /* [E][I] fp16 */
   const uint16_t* scale_down; /* [E][H] fp16 */
-  const uint16_t* lut;        /* [65536] fp16, finite values */
+  const uint16_t* lut;        /* bitshift rung: [65536] fp16 LUT; LUT rung: [512][2] fp16 codebook; finite */
 } qtip_moe_weights;
 
 /* Launch counters of a plan (prefill page, PR #196, "Two things that were built, correct, and

@@ -43,12 +43,12 @@ def pair_state_bruteforce(row_bytes, i: int, q: int = LUT_RUNG_BITS) -> int:
 def pair_states(codes: np.ndarray, q: int = LUT_RUNG_BITS) -> np.ndarray:
     """codes [..., cols/4] uint8 -> pair states [..., cols/2] (int64), vectorised from the definition."""
     c = np.asarray(codes, dtype=np.uint8)
-    bits = np.unpackbits(c, axis=-1, bitorder="little").astype(np.int64)   # [..., 2*cols], bit j of the stream
+    bits = np.unpackbits(c, axis=-1, bitorder="little")        # [..., 2*cols], bit j of the stream
     nbits = bits.shape[-1]
     starts = np.arange(0, nbits, STEP_BITS)
     state = np.zeros(bits.shape[:-1] + (starts.size,), np.int64)
     for b in range(q):
-        state += bits[..., (starts + b) % nbits] << b
+        state += bits[..., (starts + b) % nbits].astype(np.int64) << b
     return state
 
 

@@ -9,6 +9,10 @@ def say(*a):
     print(*a, flush=True)
 
 
+def rung_code(shape):
+    return q.QTIP_RUNG_LUT if getattr(shape, "rung", "bitshift") == "lut" else q.QTIP_RUNG_BITSHIFT
+
+
 class Layer:
     """A plan + device weights + workspace for one MoE layer."""
 
@@ -18,7 +22,8 @@ class Layer:
         self.shape = s
         self.out_dtype = out_dtype
         od = q.QTIP_OUT_F32 if out_dtype == "f32" else q.QTIP_OUT_BF16
-        self.desc = q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens or s.n_tokens, arm, 0, od, tile_m)
+        self.desc = q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens or s.n_tokens, arm, 0, od, tile_m,
+                                rung=rung_code(s))
         self.plan = q.qtip_moe_plan(self.desc, 0)
         self.info = q.qtip_moe_plan_info(self.plan)
         self.ws = torch.empty(self.info["workspace_bytes"], dtype=torch.uint8, device="cuda:0")

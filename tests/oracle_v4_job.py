@@ -4,7 +4,7 @@ All V4 workloads draw the same seed-0 expert weights, so the oracle decodes each
 all of them (oracle.pool).  Run as its own process (the full-size parity tests start it with
 subprocess), so that its worker pool forks from a process that has not touched a GPU:
 
-    python tests/oracle_v4_job.py --out PATH [--workers N]
+    python tests/oracle_v4_job.py --out PATH [--workers N] [--rung bitshift|lut]
 """
 import argparse
 import os
@@ -22,14 +22,20 @@ from oracle import pool  # noqa: E402
 
 UNIFORM = ["v4_decode_n32", "v4_mid_n128", "v4_mid_n512", "v4_full_n683", "v4_full_n1024"]
 SKEWED = ["v4_zipf_n256"]
+# the same layers with LUT-rung experts
+LUT_UNIFORM = ["lut_v4_decode_n32", "lut_v4_mid_n128", "lut_v4_mid_n512", "lut_v4_full_n1024"]
+LUT_SKEWED = ["lut_v4_zipf_n256"]
+RUNGS = {"bitshift": (UNIFORM, SKEWED), "lut": (LUT_UNIFORM, LUT_SKEWED)}
 
 
-def v4_layers() -> dict:
-    """Every V4 workload, the uniform ones sharing one weight draw (moe_inputs.make_inputs_multi)."""
+def v4_layers(rung: str = "bitshift") -> dict:
+    """Every V4 workload of the rung, the uniform ones sharing one weight draw
+    (moe_inputs.make_inputs_multi)."""
+    uniform, skewed = RUNGS[rung]
     W = moe_inputs.WORKLOADS
-    uni = moe_inputs.make_inputs_multi(W[UNIFORM[0]], [W[n].n_tokens for n in UNIFORM], seed=0)
-    layers = {name: uni[W[name].n_tokens] for name in UNIFORM}
-    for name in SKEWED:
+    uni = moe_inputs.make_inputs_multi(W[uniform[0]], [W[n].n_tokens for n in uniform], seed=0)
+    layers = {name: uni[W[name].n_tokens] for name in uniform}
+    for name in skewed:
         layers[name] = moe_inputs.make_inputs_multi(W[name], [W[name].n_tokens], seed=0)[W[name].n_tokens]
     return layers
 
@@ -38,10 +44,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", required=True)
     ap.add_argument("--workers", type=int, default=pool.default_workers())
+    ap.add_argument("--rung", choices=sorted(RUNGS), default="bitshift")
     args = ap.parse_args()
     t0 = time.perf_counter()
     say = lambda *a: print(*a, flush=True)
-    layers = v4_layers()
+    layers = v4_layers(args.rung)
     say(f"oracle job: {len(layers)} V4 layers drawn in {time.perf_counter() - t0:.1f} s; {args.workers} workers")
     res = pool.layer_outputs(layers, args.workers, log=say)
     np.savez(args.out, **{name: res[name]["out_f64"] for name in layers})

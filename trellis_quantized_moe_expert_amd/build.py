@@ -24,7 +24,7 @@ import subprocess
 import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/api.hip", "csrc/route.hip", "csrc/expert.hip", "csrc/router.hip"]
+SOURCES = ["csrc/api.hip", "csrc/route.hip", "csrc/expert.hip", "csrc/expert_lut.hip", "csrc/router.hip"]
 OUTPUT = os.path.join(_HERE, "libqtip_moe.so")
 BUILD_DIR = os.path.join(os.path.dirname(_HERE), "_build")
 ARCH = "gfx950"

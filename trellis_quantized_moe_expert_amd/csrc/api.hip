@@ -335,6 +335,8 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
   if (tm != 16 && tm != 32 && tm != 64) return fail(QTIP_ERR_INVALID_ARG, "tile_m must be 0, 16, 32 or 64");
   if (d->dispatch_tile_m < 0 || d->dispatch_tile_m > 1024)
     return fail(QTIP_ERR_INVALID_ARG, "dispatch_tile_m must be in [0, 1024]");
+  if (d->rung != QTIP_RUNG_BITSHIFT && d->rung != QTIP_RUNG_LUT)
+    return fail(QTIP_ERR_INVALID_ARG, "rung must be QTIP_RUNG_BITSHIFT or QTIP_RUNG_LUT");
   *tile_m = tm;
   return QTIP_OK;
 }
@@ -643,7 +645,7 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
   p.n_xcd = xcd_count(dev);
   const LaunchShape shape =
       persistent_shape(dev, (size_t)n_units * (rows / vi.rows_per_task), vi.waves, karm == kArmGemv);
-  hipError_t e = launch_expert(kModeSingle, karm, kv, p, shape.grid, shape.waves, st);
+  hipError_t e = launch_expert(kModeSingle, karm, kv, plan->d.rung, p, shape.grid, shape.waves, st);
   if (e != hipSuccess) return hip_fail(e, "expert kernel launch");
   if (arm == QTIP_ARM_GROUPED) {
     plan->stats.grouped_launches++;
@@ -793,7 +795,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     q.out1 = dense_up;
     q.out_expert_stride = (int64_t)d.inter * d.hidden;
     q.fragment_order = 1;
-    e = launch_dequant(q, persistent_grid(dev, (size_t)d.num_experts * (d.inter / 16), kDequantWaves), st);
+    e = launch_dequant(q, plan->d.rung, persistent_grid(dev, (size_t)d.num_experts * (d.inter / 16), kDequantWaves), st);
     if (e != hipSuccess) return hip_fail(e, "dequantize launch");
     q.codes0 = w->codes_down;
     q.codes1 = nullptr;
@@ -801,7 +803,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     q.cols = d.inter;
     q.out0 = dense_down;
     q.out1 = nullptr;
-    e = launch_dequant(q, persistent_grid(dev, (size_t)d.num_experts * (d.hidden / 16), kDequantWaves), st);
+    e = launch_dequant(q, plan->d.rung, persistent_grid(dev, (size_t)d.num_experts * (d.hidden / 16), kDequantWaves), st);
     if (e != hipSuccess) return hip_fail(e, "dequantize launch");
     plan->stats.dequant_launches += 2;
   }
@@ -836,7 +838,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     gu.act_frag = 1;
   }
   gu.ksplit = shape_gu.ksplit;
-  e = launch_expert(kModeGateUp, karm, kv_gu, gu, shape_gu.grid, shape_gu.waves, st);
+  e = launch_expert(kModeGateUp, karm, kv_gu, plan->d.rung, gu, shape_gu.grid, shape_gu.waves, st);
   if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
   if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
 
@@ -864,7 +866,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     dn.n_pad_max = pp_max;
   }
   dn.ksplit = shape_dn.ksplit;
-  e = launch_expert(kModeSingle, karm, kv_dn, dn, shape_dn.grid, shape_dn.waves, st);
+  e = launch_expert(kModeSingle, karm, kv_dn, plan->d.rung, dn, shape_dn.grid, shape_dn.waves, st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
   if (karm == kArmGrouped) {
@@ -1004,7 +1006,7 @@ qtip_status qtip_moe_dequantize(qtip_moe_plan_t plan, const qtip_moe_weights* w,
   q.out0 = reinterpret_cast<uint16_t*>(dense_out);
   q.out_expert_stride = 0;
   q.fragment_order = 0;
-  hipError_t e = launch_dequant(q, persistent_grid(dev, (size_t)(q.rows / 16), kDequantWaves), st);
+  hipError_t e = launch_dequant(q, plan->d.rung, persistent_grid(dev, (size_t)(q.rows / 16), kDequantWaves), st);
   if (e != hipSuccess) return hip_fail(e, "dequantize launch");
   plan->stats.dequant_launches++;
   return QTIP_OK;

@@ -27,870 +27,11 @@
 //    leaves the dot products unchanged.
 //  - Grouped arm: v_mfma_f32_16x16x32_bf16 per 16-pair row block.  GEMV arm: the same
 //    decoded registers feed VALU bf16 dot products per pair.
-#include "qtip_internal.h"
+#include "expert_body.h"
 
 namespace qtip {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// fp16 -> bf16 bits: exact widening to fp32, then round to nearest even on the top 16 bits.
-__device__ inline uint32_t f16_to_bf16_bits(uint32_t h) {
-  const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ inline float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
-
-__device__ inline uint32_t lut_bf16x2(uint32_t v) {
-  return f16_to_bf16_bits(v & 0xFFFFu) | (f16_to_bf16_bits(v >> 16) << 16);
-}
-
-// Stage the fp16 LUT into LDS as bf16 (8 entries per 16-byte load) with a workgroup of THREADS
-// threads: every load of a thread is issued before the first conversion, so the fill waits for
-// one memory round trip instead of one per load.
-template <int THREADS>
-__device__ inline void fill_lut(uint16_t* lut_s, const uint16_t* __restrict__ lut_g) {
-  constexpr int kVec = kLutEntries / 8;
-  constexpr int kIter = (kVec + THREADS - 1) / THREADS;
-  const uint4* src = reinterpret_cast<const uint4*>(lut_g);
-  uint4* dst = reinterpret_cast<uint4*>(lut_s);
-  uint4 v[kIter];
-#pragma unroll
-  for (int it = 0; it < kIter; ++it) {
-    const int i = (int)threadIdx.x + it * THREADS;
-    if (kVec % THREADS == 0 || i < kVec) v[it] = src[i];
-  }
-#pragma unroll
-  for (int it = 0; it < kIter; ++it) {
-    const int i = (int)threadIdx.x + it * THREADS;
-    if (kVec % THREADS == 0 || i < kVec)
-      dst[i] = uint4{lut_bf16x2(v[it].x), lut_bf16x2(v[it].y), lut_bf16x2(v[it].z), lut_bf16x2(v[it].w)};
-  }
-  __syncthreads();
-}
-
-// The same with any workgroup size (a launch with fewer waves than its configuration's), four
-// loads of a thread in flight at a time (measured: sixteen made the one-token down pass slower).
-__device__ inline void fill_lut_any(uint16_t* lut_s, const uint16_t* __restrict__ lut_g) {
-  constexpr int kVec = kLutEntries / 8;
-  constexpr int kBatch = 4;
-  const uint4* src = reinterpret_cast<const uint4*>(lut_g);
-  uint4* dst = reinterpret_cast<uint4*>(lut_s);
-  for (int i0 = 0; i0 < kVec; i0 += kBatch * (int)blockDim.x) {
-    uint4 v[kBatch];
-#pragma unroll
-    for (int it = 0; it < kBatch; ++it) {
-      const int i = i0 + (int)threadIdx.x + it * (int)blockDim.x;
-      if (i < kVec) v[it] = src[i];
-    }
-#pragma unroll
-    for (int it = 0; it < kBatch; ++it) {
-      const int i = i0 + (int)threadIdx.x + it * (int)blockDim.x;
-      if (i < kVec) dst[i] = uint4{lut_bf16x2(v[it].x), lut_bf16x2(v[it].y), lut_bf16x2(v[it].z), lut_bf16x2(v[it].w)};
-    }
-  }
-  __syncthreads();
-}
-
-__device__ inline uint32_t lut_pair(const uint16_t* lut, uint32_t s0, uint32_t s1) {
-  return (uint32_t)lut[s0] | ((uint32_t)lut[s1] << 16);
-}
-
-// Decode 16 consecutive symbols of a run.  `lo` holds the stream bits of the 16 symbols,
-// `hi` the 16 symbols after them (the look-ahead).  The 32-bit window alignbit(hi, lo, 2t)
-// holds the state of symbol t in its low half and of symbol t+8 in its high half, so one
-// funnel shift serves two symbols.  Returns the 8 bf16 weights of symbols 0..7 in `first`
-// and of symbols 8..15 in `second`, packed two per dword (lower symbol in the low half).
-__device__ inline void decode16(const uint16_t* lut, uint32_t lo, uint32_t hi, u32x4& first, u32x4& second) {
-  uint32_t x[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) x[t] = (t == 0) ? lo : __builtin_amdgcn_alignbit(hi, lo, 2 * t);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    first[q] = lut_pair(lut, x[2 * q] & 0xFFFFu, x[2 * q + 1] & 0xFFFFu);
-    second[q] = lut_pair(lut, x[2 * q] >> 16, x[2 * q + 1] >> 16);
-  }
-}
-
-struct RunCodes {
-  uint32_t d0, d1, la;
-};
-
-// Codes of one 32-symbol run: the run's 8 bytes and the 4 after them (its look-ahead).  `base`
-// is the (wave-uniform) start of the expert's matrix, `row_off` the lane's row offset in bytes;
-// 32-bit offsets keep the addresses in one VGPR each.  `back` (0 or 4) moves the load 4 bytes
-// earlier, for a load whose data is never used and which must stay inside the row.  With X3 one
-// 12-byte load fetches all three dwords (half the vector-memory accesses of an 8-byte plus a
-// 4-byte load, at the cost of an aligned register triple: used where registers allow).
-template <bool X3>
-__device__ inline RunCodes load_run(const uint8_t* __restrict__ base, uint32_t row_off, int ob, uint32_t back = 0) {
-  const uint32_t o = row_off + (uint32_t)ob - back;
-  RunCodes rc;
-  if (X3) {
-    const uint3 v = *reinterpret_cast<const uint3*>(base + o);
-    rc.d0 = v.x;
-    rc.d1 = v.y;
-    rc.la = v.z;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(base + o);
-    rc.d0 = v.x;
-    rc.d1 = v.y;
-    rc.la = *reinterpret_cast<const uint32_t*>(base + (o + 8u));
-  }
-  return rc;
-}
-
-// The run of a row's last block: its look-ahead wraps to the row start (the window is circular).
-__device__ inline RunCodes load_run_wrapping(const uint8_t* __restrict__ base, uint32_t row_off, int ob,
-                                             int row_bytes) {
-  RunCodes rc;
-  const uint2 v = *reinterpret_cast<const uint2*>(base + (row_off + (uint32_t)ob));
-  int nx = ob + 8;
-  if (nx >= row_bytes) nx -= row_bytes;
-  rc.d0 = v.x;
-  rc.d1 = v.y;
-  rc.la = *reinterpret_cast<const uint32_t*>(base + (row_off + (uint32_t)nx));
-  return rc;
-}
-
-// Takes the dword by value: __builtin_bit_cast applied directly to an ext-vector element
-// (w[i]) compiles to a read of element 0 for every i with this clang, so each element is
-// first copied into a plain uint32_t.
-__device__ inline bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
-
-__device__ inline float dot8(u32x4 w, u32x4 x, float acc) {
-  const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
-  const uint32_t x0 = x.x, x1 = x.y, x2 = x.z, x3 = x.w;
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(x0), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(x1), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(x2), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(x3), acc, false);
-  return acc;
-}
-
-__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
-
-struct Unit {
-  int e, start, len;
-  int pad;  // start in the padded position space (a multiple of 16), or -1 without one
-};
-
-// Reads and validates a unit; returns false for a unit that must be skipped.
-__device__ inline bool read_unit(const ExpertParams& p, int u, Unit& un) {
-  un.e = p.units[3 * u + 0];
-  un.start = p.units[3 * u + 1];
-  un.len = p.units[3 * u + 2];
-  un.pad = p.unit_pad ? p.unit_pad[u] : -1;
-  const bool pad_ok = !p.unit_pad || (un.pad >= 0 && (un.pad & 15) == 0 && un.pad <= p.n_pad_max - ((un.len + 15) & ~15));
-  return un.e >= 0 && un.e < p.num_experts && un.len >= 1 && un.len <= kUnitMaxPairs && un.start >= 0 &&
-         un.start <= p.n_pos - un.len && pad_ok;
-}
-
-// Activation row of binned position s, or -1 if it is out of range.
-__device__ inline int act_row(const ExpertParams& p, int s) {
-  int r = p.act_row_map ? p.act_row_map[s] / p.act_row_div : s;
-  return (r >= 0 && r < p.n_act_rows) ? r : -1;
-}
-
-__device__ inline int out_row(const ExpertParams& p, int s) {
-  int r = p.out_row_map ? p.out_row_map[s] : s;
-  return (r >= 0 && r < p.n_out_rows) ? r : -1;
-}
-
-template <int MODE>
-__device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int r, int pi, float a0, float a1,
-                                      float s0, float s1) {
-  const int s = un.start + pi;
-  if (MODE == kModeGateUp) {
-    const float g = a0 * s0, u = a1 * s1;
-    const float h = silu(g) * u;
-    size_t o;
-    if (p.unit_pad) {
-      // h in fragment order over padded positions, as the down pass reads its A operand
-      // (its input index r = kb*128 + 32g + 8st + t)
-      const int pp = un.pad + pi;
-      o = dense_fragment_offset(pp >> 4, r >> 7, (r >> 3) & 3, (pp & 15) + 16 * ((r >> 5) & 3), p.rows >> 7) + (r & 7);
-    } else {
-      o = (size_t)s * p.rows + r;
-    }
-    reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_to_bf16_bits(h);
-  } else {
-    const int orow = out_row(p, s);
-    if (orow >= 0) reinterpret_cast<float*>(p.out)[(size_t)orow * p.rows + r] = a0 * s0;
-  }
-}
-
-// Loads the A fragments of one K block: for each 16-pair row block m < NS, the 16 bytes of
-// each of the 4 MFMA steps (K slots 8g..8g+7 <-> inputs kb*128 + 32g + 8s + 0..7).  Loads
-// are unconditional (rows past the unit read a valid row and are discarded later), so the
-// compiler can count outstanding memory operations exactly.
-template <int NS>
-__device__ inline void load_a_block(u32x4 (&a)[NS][4], const uint16_t* __restrict__ act, const uint32_t (&aoff)[NS],
-                                    int kb) {
-#pragma unroll
-  for (int m = 0; m < NS; ++m) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-      a[m][st] = *reinterpret_cast<const u32x4*>(act + (aoff[m] + (uint32_t)(kb * kKBlock + st * 8)));
-  }
-}
-
-// The same fragments from activations in fragment order: for 16-pair block m the wave's 64
-// lanes read 1 KiB contiguous per MFMA step (fo[m] = the block's offset for this lane at kb = 0,
-// st = 0; consecutive steps are 512 elements apart, blocks 2048).
-template <int NS>
-__device__ inline void load_a_block_frag(u32x4 (&a)[NS][4], const uint16_t* __restrict__ act, const uint32_t (&fo)[NS],
-                                         int kb) {
-#pragma unroll
-  for (int m = 0; m < NS; ++m) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-      a[m][st] = *reinterpret_cast<const u32x4*>(act + (fo[m] + (uint32_t)(kb * 2048 + st * 512)));
-  }
-}
-
-template <int NS, bool FRAG>
-__device__ inline void load_a(u32x4 (&a)[NS][4], const uint16_t* __restrict__ act, const uint32_t (&off)[NS], int kb) {
-  if (FRAG) load_a_block_frag<NS>(a, act, off, kb);
-  else load_a_block<NS>(a, act, off, kb);
-}
-
-// Activation row offsets (elements from p.act) of this lane for NS entries; entry m is the
-// binned position first + m*stride.  Positions past the unit, and rows out of range, read the
-// unit's first row (always valid); their results are never stored.  The plan keeps the
-// activation buffers below 2^31 elements, so 32-bit offsets suffice.
-template <int NS>
-__device__ inline void act_rows(const ExpertParams& p, const Unit& un, int first, int stride, int g,
-                                uint32_t (&off)[NS]) {
-  int r_first = act_row(p, un.start);
-  if (r_first < 0) r_first = 0;
-#pragma unroll
-  for (int m = 0; m < NS; ++m) {
-    const int pi = first + m * stride;
-    int ar = (pi < un.len) ? act_row(p, un.start + pi) : -1;
-    if (ar < 0) ar = r_first;
-    off[m] = (uint32_t)ar * (uint32_t)p.cols + (uint32_t)(g * 32);
-  }
-}
-
-// Codes of one 32-symbol run for each of NT row blocks (rows r0 + 16*nt + j).
-template <int NT>
-struct RunSet {
-  RunCodes c[NT];
-};
-
-template <int NT, bool X3>
-__device__ inline RunSet<NT> load_runs(const uint8_t* __restrict__ base, uint32_t row_off0, uint32_t nt_stride, int ob,
-                                       uint32_t back = 0) {
-  RunSet<NT> rs;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run<X3>(base, row_off0 + nt * nt_stride, ob, back);
-  return rs;
-}
-
-template <int NT>
-__device__ inline RunSet<NT> load_runs_wrapping(const uint8_t* __restrict__ base, uint32_t row_off0,
-                                                uint32_t nt_stride, int ob, int row_bytes) {
-  RunSet<NT> rs;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run_wrapping(base, row_off0 + nt * nt_stride, ob, row_bytes);
-  return rs;
-}
-
-// Block order of a task: a row's last 128-input block first (the only one whose look-ahead
-// wraps, loaded before the loop), then blocks 0, 1, ..., kblocks-2, whose runs each come from
-// one 12-byte load that stays inside the row.  Iteration i works on block_at(i) and prefetches
-// block_at(i + 1) = i; the last iteration's prefetch is not used (block 0, moved 4 bytes back
-// for lane group 3 so that it stays inside a one-block row).
-__device__ inline int block_at(int i, int kblocks) { return i == 0 ? kblocks - 1 : i - 1; }
-
-// Grouped and dequantize arms: scale and store one task's 16-pair x 16-row MFMA tiles.
-// D layout: lane holds rows 4*(lane/16)+t (pairs) of column lane%16 (output row).
-template <int MODE, int NS, int NT>
-__device__ inline void grouped_epilogue(const ExpertParams& p, const Unit& un, int r0, const f32x4 (&acc0)[NS][NT],
-                                        const f32x4 (&acc1)[NS][NT]) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = r0 + 16 * nt + j;
-    const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
-    const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
-#pragma unroll
-    for (int m = 0; m < NS; ++m) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int pi = m * 16 + 4 * g + t;
-        if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][nt][t], acc1[m][nt][t], s0, s1);
-      }
-    }
-  }
-}
-
-// Dequantize arm: the grouped pass over weights materialised beforehand as dense bf16 in
-// fragment order (no decode, no LUT): the B fragment of MFMA step st of block kb for row
-// block r0/16 + nt is one coalesced 16-byte load per lane.  Same K permutation as the decode.
-template <int MODE, int NS, int NT>
-__device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, g = lane >> 4;
-  const int kblocks = p.cols / kKBlock;
-  const size_t mat = (size_t)p.rows * (size_t)p.cols;
-  const uint16_t* w0 = p.dense0 + (size_t)un.e * mat;
-  const uint16_t* w1 = (MODE == kModeGateUp) ? p.dense1 + (size_t)un.e * mat : w0;
-  const int rb0 = r0 / 16;
-
-  uint32_t aoff[NS];
-  act_rows<NS>(p, un, j, 16, g, aoff);
-  f32x4 acc0[NS][NT], acc1[NS][NT];
-#pragma unroll
-  for (int m = 0; m < NS; ++m) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      acc0[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc1[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  for (int kb = 0; kb < kblocks; ++kb) {
-    u32x4 a[NS][4];
-    load_a_block<NS>(a, p.act, aoff, kb);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const size_t o = dense_fragment_offset(rb0 + nt, kb, st, lane, kblocks);
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(w0 + o);
-        const u32x4 b1 = (MODE == kModeGateUp) ? *reinterpret_cast<const u32x4*>(w1 + o) : b0;
-#pragma unroll
-        for (int m = 0; m < NS; ++m) {
-          acc0[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
-                                                                __builtin_bit_cast(bf16x8, b0), acc0[m][nt], 0, 0, 0);
-          if (MODE == kModeGateUp)
-            acc1[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
-                                                                  __builtin_bit_cast(bf16x8, b1), acc1[m][nt], 0, 0, 0);
-        }
-      }
-    }
-  }
-  grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1);
-}
-
-// Grouped arm: NS row blocks of 16 pairs x NT row blocks of 16 outputs share one decode of
-// the 16*NT rows; each A fragment feeds NT MFMAs.
-template <int MODE, int NS, int NT, bool APRE, bool X3 = false, bool FRAG = false>
-__device__ void task_grouped(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, g = lane >> 4;
-  const int row_bytes = p.cols >> 2;
-  const int kblocks = p.cols / kKBlock;
-  // matrix bases are wave-uniform; each lane's row is a 32-bit byte offset from them
-  const size_t mat_bytes = (size_t)p.rows * row_bytes;
-  const uint8_t* base0 = p.codes0 + (size_t)un.e * mat_bytes;
-  const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
-  const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
-  const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
-
-  uint32_t aoff[NS];  // A operand row i = lane%16 of each 16-pair block
-  if (FRAG) {
-#pragma unroll
-    for (int m = 0; m < NS; ++m) aoff[m] = (uint32_t)dense_fragment_offset((un.pad >> 4) + m, 0, 0, lane, kblocks);
-  } else {
-    act_rows<NS>(p, un, j, 16, g, aoff);
-  }
-
-  f32x4 acc0[NS][NT], acc1[NS][NT];
-#pragma unroll
-  for (int m = 0; m < NS; ++m) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      acc0[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc1[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-
-  // Per block: the block's activations are requested first, then the next block's codes
-  // (the block after the last wraps to block 0 and is not used), so waiting for the
-  // activations never waits for those codes (memory counters retire in order) and the
-  // codes have the whole block's decode to arrive.
-  // With APRE the activations are double-buffered as well: block kb+1's are requested during
-  // block kb, so every wait in the loop is for loads issued a whole block earlier.
-  u32x4 an[NS][4];
-  if (APRE) load_a<NS, FRAG>(an, p.act, aoff, kblocks - 1);
-  const int ob_last = (kblocks - 1) * 32 + g * 8;
-  RunSet<NT> n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
-  for (int i = 0; i < kblocks; ++i) {
-    const int kb = block_at(i, kblocks);
-    const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
-    u32x4 a[NS][4];
-    if (APRE) {
-#pragma unroll
-      for (int m = 0; m < NS; ++m) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) a[m][st] = an[m][st];
-      }
-      load_a<NS, FRAG>(an, p.act, aoff, kn);
-    } else {
-      load_a<NS, FRAG>(a, p.act, aoff, kb);
-    }
-    const RunSet<NT> c0 = n0, c1 = n1;
-    const int ob = kn * 32 + g * 8;
-    const uint32_t back = (i + 1 < kblocks || g != 3) ? 0u : 8u;
-    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
-    if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        u32x4 b0[2], b1[2];
-        const RunCodes& x0 = c0.c[nt];
-        decode16(lut, h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
-        if (MODE == kModeGateUp) {
-          const RunCodes& x1 = c1.c[nt];
-          decode16(lut, h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
-        }
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const int st = 2 * h + hs;
-#pragma unroll
-          for (int m = 0; m < NS; ++m) {
-            acc0[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
-                                                                  __builtin_bit_cast(bf16x8, b0[hs]), acc0[m][nt], 0, 0, 0);
-            if (MODE == kModeGateUp)
-              acc1[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
-                                                                    __builtin_bit_cast(bf16x8, b1[hs]), acc1[m][nt], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
-
-  grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1);
-}
-
-// GEMV arm: NQ pairs x NT row blocks of 16 outputs share one decode; VALU bf16 dot products.
-// GEMV arm body over the 128-input blocks [kb_lo, kb_hi) of a task (unit un, rows r0..): each
-// lane accumulates its row's dot products with the NQ pairs over its quarter of each block
-// into acc0 (gate or the single matrix) and acc1 (up).  A range holding the row's last block
-// takes it first (its look-ahead wraps to the row start), then blocks kb_lo.. in order; every
-// other block's run is one in-row load.
-template <int MODE, int NQ, int NT, bool APRE, bool X3>
-__device__ inline void gemv_range(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0, int kb_lo,
-                                  int kb_hi, float (&acc0)[NQ][NT], float (&acc1)[NQ][NT]) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, g = lane >> 4;
-  const int row_bytes = p.cols >> 2;
-  const int kblocks = p.cols / kKBlock;
-  // matrix bases are wave-uniform; each lane's row is a 32-bit byte offset from them
-  const size_t mat_bytes = (size_t)p.rows * row_bytes;
-  const uint8_t* base0 = p.codes0 + (size_t)un.e * mat_bytes;
-  const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
-  const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
-  const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
-  const bool wraps = kb_hi == kblocks;
-  const int len = kb_hi - kb_lo;
-  // the i-th block of the range's order
-  auto block_of = [&](int i) { return wraps ? (i == 0 ? kblocks - 1 : kb_lo + i - 1) : kb_lo + i; };
-
-  uint32_t xoff[NQ];  // every lane of group g reads the same 16 bytes of pair q
-  act_rows<NQ>(p, un, 0, 1, g, xoff);
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc0[q][nt] = acc1[q][nt] = 0.f;
-  }
-
-  u32x4 xn[NQ][4];
-  if (APRE) load_a_block<NQ>(xn, p.act, xoff, block_of(0));
-  RunSet<NT> n0, n1;
-  if (wraps) {
-    const int ob_last = (kblocks - 1) * 32 + g * 8;
-    n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-    n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
-  } else {
-    const int ob = kb_lo * 32 + g * 8;
-    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob);
-    n1 = (MODE == kModeGateUp) ? load_runs<NT, false>(base1, roff, nt_stride, ob) : n0;
-  }
-  for (int i = 0; i < len; ++i) {
-    const int kb = block_of(i);
-    // the next block; after the last, the range's first in-row block again (unused; 8 bytes
-    // back for lane group 3 where a one-block row would otherwise be left)
-    const int kn = i + 1 < len ? block_of(i + 1) : kb_lo;
-    u32x4 x[NQ][4];
-    if (APRE) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) x[q][st] = xn[q][st];
-      }
-      load_a_block<NQ>(xn, p.act, xoff, kn);
-    } else {
-      load_a_block<NQ>(x, p.act, xoff, kb);
-    }
-    const RunSet<NT> c0 = n0, c1 = n1;
-    const int ob = kn * 32 + g * 8;
-    const uint32_t back = (i + 1 < len || g != 3 || kn + 1 < kblocks) ? 0u : 8u;
-    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
-    if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        u32x4 b0[2], b1[2];
-        const RunCodes& x0 = c0.c[nt];
-        decode16(lut, h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
-        if (MODE == kModeGateUp) {
-          const RunCodes& x1 = c1.c[nt];
-          decode16(lut, h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
-        }
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-#pragma unroll
-          for (int q = 0; q < NQ; ++q) {
-            acc0[q][nt] = dot8(b0[hs], x[q][2 * h + hs], acc0[q][nt]);
-            if (MODE == kModeGateUp) acc1[q][nt] = dot8(b1[hs], x[q][2 * h + hs], acc1[q][nt]);
-          }
-        }
-      }
-    }
-  }
-}
-
-// GEMV arm: sum the four lane groups' partial dot products of each row (lanes j, j+16, j+32,
-// j+48) and store the NQ pairs' outputs.
-template <int MODE, int NQ, int NT>
-__device__ inline void gemv_epilogue(const ExpertParams& p, const Unit& un, int r0, const float (&acc0)[NQ][NT],
-                                     const float (&acc1)[NQ][NT]) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = r0 + 16 * nt + j;
-    const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
-    const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      float a0 = acc0[q][nt];
-      a0 += __shfl_xor(a0, 16, 64);
-      a0 += __shfl_xor(a0, 32, 64);
-      float a1 = 0.f;
-      if (MODE == kModeGateUp) {
-        a1 = acc1[q][nt];
-        a1 += __shfl_xor(a1, 16, 64);
-        a1 += __shfl_xor(a1, 32, 64);
-      }
-      if (q < un.len && (q & 3) == g) epilogue_store<MODE>(p, un, r, q, a0, a1, s0, s1);
-    }
-  }
-}
-
-// GEMV arm: the NQ pairs of a unit chunk against 16*NT rows of its expert (the per-pair dot
-// products on the VALU, the decode in registers from the LDS LUT).
-template <int MODE, int NQ, int NT, bool APRE, bool X3 = false>
-__device__ void task_gemv(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
-  float acc0[NQ][NT], acc1[NQ][NT];
-  gemv_range<MODE, NQ, NT, APRE, X3>(p, lut, un, r0, 0, p.cols / kKBlock, acc0, acc1);
-  gemv_epilogue<MODE, NQ, NT>(p, un, r0, acc0, acc1);
-}
-
-// GEMV arm with each task's inputs split over S waves of a workgroup (ExpertParams::ksplit),
-// for launches with fewer tasks than the GPU has wave slots: wave s of a task's group decodes
-// blocks [s K/S, (s+1) K/S) and leaves its partial sums in LDS; after a barrier the group's first
-// wave adds the S partials in ascending s and stores the outputs.
-template <int MODE, int NQ, int NT, bool APRE, bool X3>
-__device__ inline void gemv_part(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0, int kb_lo,
-                                 int kb_hi, float* slot) {
-  float acc0[NQ][NT], acc1[NQ][NT];
-  gemv_range<MODE, NQ, NT, APRE, X3>(p, lut, un, r0, kb_lo, kb_hi, acc0, acc1);
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      slot[((q * NT + nt) * 2 + 0) * 64 + lane] = acc0[q][nt];
-      if (MODE == kModeGateUp) slot[((q * NT + nt) * 2 + 1) * 64 + lane] = acc1[q][nt];
-    }
-  }
-}
-
-template <int MODE, int NQ, int NT>
-__device__ inline void gemv_finish(const ExpertParams& p, const Unit& un, int r0, const float* slots, int slot_floats,
-                                   int S) {
-  const int lane = threadIdx.x & 63;
-  float acc0[NQ][NT], acc1[NQ][NT];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float a0 = 0.f, a1 = 0.f;
-      for (int w = 0; w < S; ++w) {
-        a0 += slots[w * slot_floats + ((q * NT + nt) * 2 + 0) * 64 + lane];
-        if (MODE == kModeGateUp) a1 += slots[w * slot_floats + ((q * NT + nt) * 2 + 1) * 64 + lane];
-      }
-      acc0[q][nt] = a0;
-      acc1[q][nt] = a1;
-    }
-  }
-  gemv_epilogue<MODE, NQ, NT>(p, un, r0, acc0, acc1);
-}
-
-// LDS the split-input GEMV path needs beside the LUT: every wave's partial sums.
-template <class CFG>
-struct GemvSplit {
-  static constexpr int kSlotFloats = CFG::kGPairs * CFG::kNT * 2 * 64;
-  static constexpr int kFloats = CFG::kWaves * kSlotFloats;
-  static constexpr bool kFits = kFloats * 4 <= 160 * 1024 - kLutEntries * 2;
-};
-
-// Kernel configurations (the plan's `variant`): waves per workgroup, 16-row output blocks
-// per task (NT), pairs per decode on the grouped arm (in 16-pair MFMA row blocks, NSUB) and
-// on the GEMV arm.  Fewer waves leave each wave more registers; more rows per task feed each
-// activation fragment to more MFMAs; more pairs per decode mean fewer decodes.
-template <int WAVES, int NT, int NSUB, int GPAIRS>
-struct ExpertCfg {
-  static constexpr int kWaves = WAVES, kNT = NT, kNSub = NSUB, kGPairs = GPAIRS;
-  static constexpr int kRows = 16 * NT;
-  // Activation double-buffering where the register budget allows it: 512 VGPRs per SIMD lane
-  // shared by WAVES/4 waves (168 at 12 waves, where the 4-block task, or three 16-pair blocks
-  // per decode, would spill).
-  static constexpr bool kAPre = WAVES <= 8 || (NT <= 2 && NSUB <= 2);
-  // 12-byte code loads in the down pass: measured faster with 12 waves of 64-row tasks (fewer
-  // vector-memory accesses where they compete with the LUT gathers), slower with 16 waves.
-  static constexpr bool kX3Down = WAVES == 12 && NT == 4;
-  // The fused grouped task of 64 rows x three 16-pair blocks would spill heavily at 12 waves;
-  // that configuration serves the down pass only (the plan runs the fused pass as 32-row tasks).
-  static constexpr bool kGroupedFused = !(NT == 4 && NSUB >= 3);
-};
-using Cfg1 = ExpertCfg<16, 1, 2, 2>;
-using Cfg2 = ExpertCfg<8, 1, 4, 4>;
-using Cfg3 = ExpertCfg<16, 2, 2, 2>;
-using Cfg4 = ExpertCfg<8, 2, 4, 4>;
-using Cfg5 = ExpertCfg<8, 4, 2, 2>;
-using Cfg6 = ExpertCfg<12, 2, 2, 2>;
-using Cfg7 = ExpertCfg<12, 4, 2, 2>;
-// One decode per 16-pair m-tile (no sharing across m-tiles): the pages' grouped-kernel
-// schedule, kept to measure what sharing a decode across m-tiles is worth.
-using Cfg8 = ExpertCfg<16, 1, 1, 1>;
-// 12 waves of 32-row tasks sharing a decode across three 16-pair blocks (48 pairs).
-using Cfg9 = ExpertCfg<12, 2, 3, 3>;
-// 12 waves of 64-row tasks sharing a decode across three 16-pair blocks (48 pairs): a down-pass
-// shape (see kGroupedFused).
-using Cfg10 = ExpertCfg<12, 4, 3, 3>;
-
-// The grouped body specialised for the chunk's exact number of 16-pair row blocks.
-template <int MODE, class CFG, bool FRAG>
-__device__ inline void grouped_blocks(const ExpertParams& p, const uint16_t* lut, const Unit& part, int r0) {
-  constexpr int NT = CFG::kNT;
-  constexpr bool AP = CFG::kAPre;
-  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
-  switch ((part.len + 15) >> 4) {
-    case 1: task_grouped<MODE, 1, NT, AP, X3, FRAG>(p, lut, part, r0); break;
-    case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
-    case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
-    default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
-  }
-}
-
-// A unit may hold more pairs than one decode serves; it is then processed in chunks, each
-// chunk decoding the rows again.  Each chunk runs the body specialised for its exact number
-// of 16-pair row blocks (grouped) or pairs (GEMV), chosen by a wave-uniform switch.
-template <int MODE, int ARM, class CFG, bool FRAG>
-__device__ inline void run_task(const ExpertParams& p, const uint16_t* lut, const Unit& un, int r0) {
-  constexpr int NT = CFG::kNT;
-  constexpr bool AP = CFG::kAPre;
-  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
-  constexpr int kChunk = (ARM == kArmGemv) ? CFG::kGPairs : CFG::kNSub * 16;
-  static_assert(CFG::kNSub >= 1 && CFG::kNSub <= 4 && CFG::kGPairs >= 1 && CFG::kGPairs <= 4, "config");
-  for (int c0 = 0; c0 < un.len; c0 += kChunk) {
-    const Unit part{un.e, un.start + c0, min(kChunk, un.len - c0), un.pad >= 0 ? un.pad + c0 : -1};
-    if (ARM == kArmDense) {
-      switch ((part.len + 15) >> 4) {
-        case 1: task_dense<MODE, 1, NT>(p, part, r0); break;
-        case 2: if (CFG::kNSub >= 2) task_dense<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT>(p, part, r0); break;
-        case 3: if (CFG::kNSub >= 3) task_dense<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT>(p, part, r0); break;
-        default: if (CFG::kNSub >= 4) task_dense<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT>(p, part, r0); break;
-      }
-    } else if (ARM == kArmGrouped) {
-      grouped_blocks<MODE, CFG, FRAG>(p, lut, part, r0);
-    } else {
-      switch (part.len) {
-        case 1: task_gemv<MODE, 1, NT, AP, X3>(p, lut, part, r0); break;
-        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP, X3>(p, lut, part, r0); break;
-        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP, X3>(p, lut, part, r0); break;
-        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP, X3>(p, lut, part, r0); break;
-      }
-    }
-  }
-}
-
-// The GEMV arm's task loop with split inputs: a workgroup of tpw x S waves takes tpw tasks per
-// round, S waves each (every wave runs the same rounds, so the barriers line up).
-template <int MODE, class CFG>
-__device__ inline void gemv_split_tasks(const ExpertParams& p, const uint16_t* lut, float* part) {
-  constexpr int NT = CFG::kNT;
-  constexpr bool AP = CFG::kAPre;
-  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
-  constexpr int kSlot = GemvSplit<CFG>::kSlotFloats;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int S = p.ksplit, tpw = (int)(blockDim.x >> 6) / S;
-  const int q = wave / S, sidx = wave % S;
-  const int kper = p.cols / kKBlock / S;
-  const int n_units = p.n_units_dev ? __builtin_amdgcn_readfirstlane(*p.n_units_dev) : p.n_units_host;
-  const int nblocks = p.rows / CFG::kRows;
-  const long total = (long)n_units * nblocks;
-  float* mine = part + wave * kSlot;
-  for (long base = (long)blockIdx.x * tpw; base < total; base += (long)gridDim.x * tpw) {
-    const long t = base + q;
-    Unit un{};
-    const bool ok = t < total && read_unit(p, (int)(t / nblocks), un);
-    const int r0 = (int)(t % nblocks) * CFG::kRows;
-    const bool one = ok && un.len <= CFG::kGPairs;  // a single chunk (the layer's own units)
-    const int lo = sidx * kper, hi = lo + kper;
-    if (one) {
-      switch (un.len) {
-        case 1: gemv_part<MODE, 1, NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
-        case 2: if (CFG::kGPairs >= 2) gemv_part<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
-        case 3: if (CFG::kGPairs >= 3) gemv_part<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
-        default: if (CFG::kGPairs >= 4) gemv_part<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
-      }
-    }
-    __syncthreads();
-    if (ok && sidx == 0) {
-      const float* slots = part + (q * S) * kSlot;
-      if (one) {
-        switch (un.len) {
-          case 1: gemv_finish<MODE, 1, NT>(p, un, r0, slots, kSlot, S); break;
-          case 2: if (CFG::kGPairs >= 2) gemv_finish<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT>(p, un, r0, slots, kSlot, S); break;
-          case 3: if (CFG::kGPairs >= 3) gemv_finish<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT>(p, un, r0, slots, kSlot, S); break;
-          default: if (CFG::kGPairs >= 4) gemv_finish<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT>(p, un, r0, slots, kSlot, S); break;
-        }
-      } else {
-        run_task<MODE, kArmGemv, CFG, false>(p, lut, un, r0);  // a longer unit: its group's first wave alone
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// SPREAD: the launch may run fewer waves per workgroup than the configuration's (a small
-// batch spread over more CUs).
-template <int MODE, int ARM, class CFG, bool FRAG, bool SPREAD>
-__device__ inline void expert_tasks(const ExpertParams& p, const uint16_t* lut_s) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_units = p.n_units_dev ? __builtin_amdgcn_readfirstlane(*p.n_units_dev) : p.n_units_host;
-  const int nblocks = p.rows / CFG::kRows;
-  const long total = (long)n_units * nblocks;
-  // Task order.  Workgroup b runs on XCD b % n_xcd (round-robin dispatch).  Each XCD owns a
-  // contiguous share of the tasks in proportion to its workgroups, and its waves take that
-  // share's tasks in turn across its CUs, so an XCD works on a few units at a time: their
-  // activation rows stay in its L2, and a CU's waves (row blocks of the same unit) share them
-  // in L1.  Every unit is one decode, so equal task counts are equal work; share boundaries are
-  // rounded to whole rounds of the XCD's CUs when those divide a unit's row blocks, so every CU
-  // then takes the same row blocks of the same units.
-  const int nx = p.n_xcd;
-  const int G = gridDim.x;
-  const int xcd = blockIdx.x % nx, cu = blockIdx.x / nx;
-  const int cus = G / nx + (xcd < G % nx ? 1 : 0);
-  const int before = xcd * (G / nx) + min(xcd, G % nx);
-  long lo = total * before / G;
-  long hi = total * (before + cus) / G;
-  const long Q = G / nx;
-  if (Q > 1 && nblocks % Q == 0) {
-    lo = (lo + Q / 2) / Q * Q;
-    hi = (hi + Q / 2) / Q * Q;
-  }
-  const long nslots = (long)(SPREAD ? (int)(blockDim.x >> 6) : CFG::kWaves) * cus;
-  for (long task = lo + (long)wave * cus + cu; task < hi; task += nslots) {
-    const int u = (int)(task / nblocks);
-    const int nb = (int)(task - (long)u * nblocks);
-    Unit un;
-    if (!read_unit(p, u, un)) continue;
-    run_task<MODE, ARM, CFG, FRAG>(p, lut_s, un, nb * CFG::kRows);
-  }
-}
-
-// FRAG: the grouped arm's activations are in fragment order (ExpertParams::act_frag).
-// SPREAD (GEMV arm): the launch may run fewer waves per workgroup than CFG's.
-template <int MODE, int ARM, class CFG, bool FRAG = false, bool SPREAD = false>
-__global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParams p) {
-  if constexpr (ARM == kArmDense) {
-    expert_tasks<MODE, ARM, CFG, false, false>(p, nullptr);
-  } else {
-    __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
-    if constexpr (SPREAD) fill_lut_any(lut_s, p.lut);
-    else fill_lut<CFG::kWaves * 64>(lut_s, p.lut);
-    if constexpr (SPREAD && ARM == kArmGemv && GemvSplit<CFG>::kFits) {
-      if (p.ksplit > 1) {
-        __shared__ float part[GemvSplit<CFG>::kFloats];
-        gemv_split_tasks<MODE, CFG>(p, lut_s, part);
-        return;
-      }
-    }
-    expert_tasks<MODE, ARM, CFG, FRAG, SPREAD>(p, lut_s);
-  }
-}
-
-// Dequantize-materialise: one wave task decodes 16 rows x all inputs of one matrix (two for
-// the fused gate/up pair) and stores bf16(LUT[state]), in row-major order or in the fragment
-// order of the dequantize arm's MFMA pass (there every store is 1 KiB contiguous per wave).
-// The next block's codes are requested before the current block is decoded.
-__global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantParams q) {
-  __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
-  fill_lut<kDequantWaves * 64>(lut_s, q.lut);
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15, g = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row_bytes = q.cols >> 2;
-  const int kblocks = q.cols / kKBlock;
-  const int nblocks = q.rows / 16;
-  const int e_first = q.expert >= 0 ? q.expert : 0;
-  const long n_exp = q.expert >= 0 ? 1 : q.num_experts;
-  const long total = n_exp * nblocks;
-  const size_t mat_bytes = (size_t)q.rows * row_bytes;
-  for (long task = (long)blockIdx.x * kDequantWaves + wave; task < total; task += (long)gridDim.x * kDequantWaves) {
-    const int e = e_first + (int)(task / nblocks);
-    const int rb = (int)(task % nblocks);
-    const int r0 = rb * 16;
-    if (q.expert < 0 && q.counts && __builtin_amdgcn_readfirstlane(q.counts[e]) <= 0) continue;
-    for (int m = 0; m < (q.codes1 ? 2 : 1); ++m) {
-      const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
-      uint16_t* out = (m ? q.out1 : q.out0) + (size_t)e * (size_t)q.out_expert_stride;
-      const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
-      RunCodes nx = load_run_wrapping(base, roff, (kblocks - 1) * 32 + g * 8, row_bytes);
-      for (int i = 0; i < kblocks; ++i) {
-        const int kb = block_at(i, kblocks);
-        const RunCodes rc = nx;
-        if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + g * 8);
-        u32x4 w[4];
-        decode16(lut_s, rc.d0, rc.d1, w[0], w[1]);
-        decode16(lut_s, rc.d1, rc.la, w[2], w[3]);
-        if (q.fragment_order) {
-#pragma unroll
-          for (int st = 0; st < 4; ++st)
-            *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
-        } else {
-          uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
-#pragma unroll
-          for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
-        }
-      }
-    }
-  }
-}
 
 // Activations of the grouped arm in fragment order: one thread per 16-byte fragment slot
 // (padded 16-row block, 128-input block kb, MFMA step st, lane j + 16g) copies inputs
@@ -992,50 +133,6 @@ __global__ __launch_bounds__(1024, 1) void gather_probe_kernel(int32_t rounds, u
 
 }  // namespace
 
-// The dequantize arm runs one configuration (variant 3's shape: 16 waves, 32-row tasks, up to
-// 32 pairs per pass over the weights).
-using CfgDense = ExpertCfg<16, 2, 2, 2>;
-
-template <class CFG>
-static hipError_t launch_cfg(int mode, int arm, const ExpertParams& p, int grid, int waves, hipStream_t stream) {
-  // only the GEMV arm is built to run with fewer waves than its configuration's
-  const int full = arm == kArmDense ? CfgDense::kWaves : CFG::kWaves;
-  if (grid < 1 || waves < 1 || waves > full || (waves < full && arm != kArmGemv)) return hipErrorInvalidValue;
-  const dim3 g(grid), b(waves * 64);
-  const bool spread = waves < full;
-  if (arm == kArmDense) {
-    const dim3 bd(waves * 64);
-    if (mode == kModeGateUp)
-      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmDense, CfgDense>), g, bd, 0, stream, p);
-    else
-      hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmDense, CfgDense>), g, bd, 0, stream, p);
-  } else if (mode == kModeGateUp && arm == kArmGrouped) {
-    if constexpr (CFG::kGroupedFused) {
-      if (p.act_frag && p.unit_pad)
-        hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, true>), g, b, 0, stream, p);
-      else
-        hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGrouped, CFG, false>), g, b, 0, stream, p);
-    } else {
-      return hipErrorInvalidValue;
-    }
-  } else if (mode == kModeGateUp) {
-    if (spread)
-      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG, false, true>), g, b, 0, stream, p);
-    else
-      hipLaunchKernelGGL((expert_kernel<kModeGateUp, kArmGemv, CFG>), g, b, 0, stream, p);
-  } else if (arm == kArmGrouped) {
-    if (p.act_frag && p.unit_pad)
-      hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped, CFG, true>), g, b, 0, stream, p);
-    else
-      hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGrouped, CFG, false>), g, b, 0, stream, p);
-  } else if (spread) {
-    hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGemv, CFG, false, true>), g, b, 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((expert_kernel<kModeSingle, kArmGemv, CFG>), g, b, 0, stream, p);
-  }
-  return hipGetLastError();
-}
-
 template <class CFG>
 struct CfgInfo {
   static void get(int arm, VariantInfo& v) {
@@ -1069,21 +166,12 @@ bool variant_info(int variant, int arm, VariantInfo& v) {
   }
 }
 
-hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, int waves,
+hipError_t launch_expert(int mode, int arm, int variant, int rung, const ExpertParams& p, int grid, int waves,
                          hipStream_t stream) {
-  switch (variant) {
-    case 1: return launch_cfg<Cfg1>(mode, arm, p, grid, waves, stream);
-    case 2: return launch_cfg<Cfg2>(mode, arm, p, grid, waves, stream);
-    case 3: return launch_cfg<Cfg3>(mode, arm, p, grid, waves, stream);
-    case 4: return launch_cfg<Cfg4>(mode, arm, p, grid, waves, stream);
-    case 5: return launch_cfg<Cfg5>(mode, arm, p, grid, waves, stream);
-    case 6: return launch_cfg<Cfg6>(mode, arm, p, grid, waves, stream);
-    case 7: return launch_cfg<Cfg7>(mode, arm, p, grid, waves, stream);
-    case 8: return launch_cfg<Cfg8>(mode, arm, p, grid, waves, stream);
-    case 9: return launch_cfg<Cfg9>(mode, arm, p, grid, waves, stream);
-    case 10: return launch_cfg<Cfg10>(mode, arm, p, grid, waves, stream);
-    default: return hipErrorInvalidValue;
-  }
+  // the dequantize arm's MFMA pass reads dense weights and does not depend on the rung
+  if (rung == kRungLut && arm != kArmDense) return launch_expert_lut(mode, arm, variant, p, grid, waves, stream);
+  if (rung != kRungBitshift && rung != kRungLut) return hipErrorInvalidValue;
+  return launch_expert_rung<kRungBitshift>(mode, arm, variant, p, grid, waves, stream);
 }
 
 hipError_t launch_pack_act(const uint16_t* x, const int32_t* padded_pair, const int32_t* n_pad, int32_t k,
@@ -1096,9 +184,10 @@ hipError_t launch_pack_act(const uint16_t* x, const int32_t* padded_pair, const 
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(const DequantParams& q, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(kDequantWaves * 64), 0, stream, q);
-  return hipGetLastError();
+hipError_t launch_dequant(const DequantParams& q, int rung, int grid, hipStream_t stream) {
+  if (rung == kRungLut) return launch_dequant_lut(q, grid, stream);
+  if (rung != kRungBitshift) return hipErrorInvalidValue;
+  return launch_dequant_rung<kRungBitshift>(q, grid, stream);
 }
 
 hipError_t launch_combine(const float* y, const float* topk_w, int32_t n, int32_t k, int32_t H, void* out,

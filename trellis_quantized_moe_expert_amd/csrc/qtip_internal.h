@@ -8,7 +8,13 @@
 
 namespace qtip {
 
-constexpr int kLutEntries = 65536;     // 16-bit trellis state -> one LUT entry
+constexpr int kLutEntries = 65536;     // 16-bit trellis state -> one LUT entry (bitshift rung)
+// The two 2-bit rungs: the bitshift rung (one weight per 16-bit window, a 65536-entry LUT) and the
+// LUT rung (one 2-D codebook vector per 9-bit pair state, a 512 x 2 codebook).
+enum Rung { kRungBitshift = 0, kRungLut = 1 };
+constexpr int kLutRungBits = 9;                      // pair-state bits of the LUT rung
+constexpr int kCodebookEntries = 1 << kLutRungBits;  // 512 two-dimensional entries
+constexpr int kCodebookCopies = 32;                  // one copy per LDS bank (see DecoderLut)
 // The LUT fills 128 KiB of LDS, so one expert workgroup per CU is resident; the kernel
 // variant fixes its size (8, 12 or 16 wave64; a small GEMV launch may run fewer).
 // Variants 1..10 are fixed kernel configurations (see variant_info); 0 lets the plan choose.
@@ -37,7 +43,7 @@ struct ExpertParams {
   const uint8_t* codes1;        // [E][rows][cols/4]  up (fused pass only)
   const uint16_t* scale0;       // [E][rows] fp16
   const uint16_t* scale1;       // [E][rows] fp16 (fused pass only)
-  const uint16_t* lut;          // [65536] fp16
+  const uint16_t* lut;          // bitshift rung: [65536] fp16 LUT; LUT rung: [512][2] fp16 codebook
   const uint16_t* act;          // [n_act_rows][cols] bf16
   const int32_t* act_row_map;   // activation row of binned position s = map[s] / act_row_div (NULL: s)
   int32_t act_row_div;
@@ -77,8 +83,11 @@ struct VariantInfo {
 bool variant_info(int variant, int arm, VariantInfo& v);
 // `waves` per workgroup: at most the variant's (VariantInfo::waves); fewer spread a small launch
 // over more CUs.
-hipError_t launch_expert(int mode, int arm, int variant, const ExpertParams& p, int grid, int waves,
+hipError_t launch_expert(int mode, int arm, int variant, int rung, const ExpertParams& p, int grid, int waves,
                          hipStream_t stream);
+// The LUT rung's instantiations (their own translation unit, so the two rungs compile in parallel).
+hipError_t launch_expert_lut(int mode, int arm, int variant, const ExpertParams& p, int grid, int waves,
+                             hipStream_t stream);
 
 // Top-k over logits given as n_part partial sums part[s][t][e] (s-major, n*E apart), added in
 // ascending s; n_part = 1 reads plain logits.
@@ -103,7 +112,8 @@ struct DequantParams {
 __host__ __device__ inline size_t dense_fragment_offset(int rb, int kb, int st, int lane, int kblocks) {
   return ((((size_t)rb * kblocks + kb) * 4 + st) * 64 + lane) * 8;
 }
-hipError_t launch_dequant(const DequantParams& q, int grid, hipStream_t stream);
+hipError_t launch_dequant(const DequantParams& q, int rung, int grid, hipStream_t stream);
+hipError_t launch_dequant_lut(const DequantParams& q, int grid, hipStream_t stream);
 constexpr int kDequantWaves = 16;
 
 hipError_t launch_route_topk(const float* logits, int32_t n_part, int32_t n, int32_t E, int32_t k,
