@@ -132,7 +132,13 @@ __device__ inline void decode16(const uint16_t* lut, uint32_t lo, uint32_t hi, u
 
 // Decoders of one 16-symbol piece of a run, one per rung; `decode16` has the same contract for
 // both: 8 bf16 weights of symbols 0..7 in `first`, of symbols 8..15 in `second`, two per dword.
+// kPipelined selects the block loop.  The bitshift rung is bound by its LDS gathers, which hide
+// memory latency and leave no LDS time for cross-lane moves: its loops load codes directly in the
+// MFMA layout, one block ahead.  The LUT rung's gathers are cheap, and its loops are bound by the
+// vector-memory path instead: they load codes transposed (to_mfma_layout) and run over ping-pong
+// buffers so that the one-block prefetch survives compilation.
 struct DecoderBitshift {
+  static constexpr bool kPipelined = false;
   const uint16_t* lut;  // the bf16 LUT in LDS (65536 entries)
   __device__ inline void decode16(uint32_t lo, uint32_t hi, u32x4& first, u32x4& second) const {
     ::qtip::decode16(lut, lo, hi, first, second);
@@ -145,6 +151,7 @@ struct DecoderBitshift {
 // Pair states sit at even symbols: the window alignbit(hi, lo, 4q) holds the state of the pair at
 // symbol 2q in its low 9 bits and of the pair at symbol 2q + 8 in bits 16..24.
 struct DecoderLut {
+  static constexpr bool kPipelined = true;
   const char* cb;     // LDS codebook, 32 x 4 bytes per entry
   uint32_t bank_off;  // (lane % 32) * 4
   __device__ inline uint32_t entry(uint32_t byte_off) const {
@@ -178,6 +185,21 @@ __device__ inline void fill_codebook(uint32_t* cb_s, const uint16_t* __restrict_
 struct RunCodes {
   uint32_t d0, d1, la;
 };
+
+// Codes are loaded transposed: lane 4r + c loads chunk c (8 bytes, plus its 4-byte look-ahead) of
+// row r of the task's 16-row block, so the four lanes of each quad read one row's consecutive
+// bytes (one or two cache lines per quad instead of four).  The MFMA operand layout wants chunk g
+// of row j in lane j + 16g; one cross-lane pull per dword (ds_bpermute: lane L reads lane
+// 4 (L % 16) + L / 16) moves the loaded dwords there before the decode.
+__device__ inline int code_row(int lane) { return lane >> 2; }
+__device__ inline int code_chunk(int lane) { return lane & 3; }
+__device__ inline RunCodes to_mfma_layout(const RunCodes& t) {
+  const int lane = threadIdx.x & 63;
+  const int addr = (((lane & 15) << 2) | (lane >> 4)) << 2;
+  return RunCodes{(uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)t.d0),
+                  (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)t.d1),
+                  (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)t.la)};
+}
 
 // Codes of one 32-symbol run: the run's 8 bytes and the 4 after them (its look-ahead).  `base`
 // is the (wave-uniform) start of the expert's matrix, `row_off` the lane's row offset in bytes;
@@ -342,6 +364,41 @@ struct RunSet {
   RunCodes c[NT];
 };
 
+// The prefetch loops below carry a value loaded before the loop (the first block's codes or
+// activations) that each iteration replaces by a load for the next block.  Left alone, the
+// compiler merges those two loads into one load of a merged address at the top of the loop body,
+// which then waits for its own data: the one-block prefetch disappears and every block waits a
+// full memory round trip.  Passing the values loaded before the loop through an empty asm (no
+// instruction, registers only) makes them opaque, so the loads stay where the loop puts them.
+__device__ inline void keep_apart(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ inline void keep_apart(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ inline void keep_apart(RunCodes& c) {
+  keep_apart(c.d0);
+  keep_apart(c.d1);
+  keep_apart(c.la);
+}
+template <int NT>
+__device__ inline void keep_apart(RunSet<NT>& r) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) keep_apart(r.c[nt]);
+}
+template <int NS>
+__device__ inline void keep_apart(u32x4 (&a)[NS][4]) {
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) keep_apart(a[m][st]);
+  }
+}
+
+template <int NT>
+__device__ inline RunSet<NT> to_mfma_layout(const RunSet<NT>& t) {
+  RunSet<NT> r;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) r.c[nt] = to_mfma_layout(t.c[nt]);
+  return r;
+}
+
 template <int NT, bool X3>
 __device__ inline RunSet<NT> load_runs(const uint8_t* __restrict__ base, uint32_t row_off0, uint32_t nt_stride, int ob,
                                        uint32_t back = 0) {
@@ -450,7 +507,9 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
   const size_t mat_bytes = (size_t)p.rows * row_bytes;
   const uint8_t* base0 = p.codes0 + (size_t)un.e * mat_bytes;
   const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
-  const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+  // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
+  const int tc = DEC::kPipelined ? code_chunk(lane) : g;
+  const uint32_t roff = (uint32_t)(r0 + (DEC::kPipelined ? code_row(lane) : j)) * (uint32_t)row_bytes;
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
 
   uint32_t aoff[NS];  // A operand row i = lane%16 of each 16-pair block
@@ -471,61 +530,130 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
     }
   }
 
-  // Per block: the block's activations are requested first, then the next block's codes
-  // (the block after the last wraps to block 0 and is not used), so waiting for the
-  // activations never waits for those codes (memory counters retire in order) and the
-  // codes have the whole block's decode to arrive.
-  // With APRE the activations are double-buffered as well: block kb+1's are requested during
-  // block kb, so every wait in the loop is for loads issued a whole block earlier.
-  u32x4 an[NS][4];
-  if (APRE) load_a<NS, FRAG>(an, p.act, aoff, kblocks - 1);
-  const int ob_last = (kblocks - 1) * 32 + g * 8;
-  RunSet<NT> n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-  RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
-  for (int i = 0; i < kblocks; ++i) {
-    const int kb = block_at(i, kblocks);
-    const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
-    u32x4 a[NS][4];
-    if (APRE) {
+  if constexpr (!DEC::kPipelined) {
+    // Per block: the block's activations are requested first, then the next block's codes
+    // (the block after the last wraps to block 0 and is not used), so waiting for the
+    // activations never waits for those codes (memory counters retire in order) and the
+    // codes have the whole block's decode to arrive.
+    // With APRE the activations are double-buffered as well: block kb+1's are requested during
+    // block kb, so every wait in the loop is for loads issued a whole block earlier.
+    u32x4 an[NS][4];
+    if (APRE) load_a<NS, FRAG>(an, p.act, aoff, kblocks - 1);
+    const int ob_last = (kblocks - 1) * 32 + tc * 8;
+    RunSet<NT> n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
+    RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
+    for (int i = 0; i < kblocks; ++i) {
+      const int kb = block_at(i, kblocks);
+      const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
+      u32x4 a[NS][4];
+      if (APRE) {
 #pragma unroll
-      for (int m = 0; m < NS; ++m) {
+        for (int m = 0; m < NS; ++m) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) a[m][st] = an[m][st];
-      }
-      load_a<NS, FRAG>(an, p.act, aoff, kn);
-    } else {
-      load_a<NS, FRAG>(a, p.act, aoff, kb);
-    }
-    const RunSet<NT> c0 = n0, c1 = n1;
-    const int ob = kn * 32 + g * 8;
-    const uint32_t back = (i + 1 < kblocks || g != 3) ? 0u : 8u;
-    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
-    if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        u32x4 b0[2], b1[2];
-        const RunCodes& x0 = c0.c[nt];
-        lut.decode16(h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
-        if (MODE == kModeGateUp) {
-          const RunCodes& x1 = c1.c[nt];
-          lut.decode16(h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+          for (int st = 0; st < 4; ++st) a[m][st] = an[m][st];
         }
+        load_a<NS, FRAG>(an, p.act, aoff, kn);
+      } else {
+        load_a<NS, FRAG>(a, p.act, aoff, kb);
+      }
+      const RunSet<NT> c0 = n0, c1 = n1;
+      const int ob = kn * 32 + tc * 8;
+      const uint32_t back = (i + 1 < kblocks || tc != 3) ? 0u : 8u;
+      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
+      if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const int st = 2 * h + hs;
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int m = 0; m < NS; ++m) {
-            acc0[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
-                                                                  __builtin_bit_cast(bf16x8, b0[hs]), acc0[m][nt], 0, 0, 0);
-            if (MODE == kModeGateUp)
-              acc1[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
-                                                                    __builtin_bit_cast(bf16x8, b1[hs]), acc1[m][nt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          u32x4 b0[2], b1[2];
+          const RunCodes& x0 = c0.c[nt];
+          lut.decode16(h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
+          if (MODE == kModeGateUp) {
+            const RunCodes& x1 = c1.c[nt];
+            lut.decode16(h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+          }
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            const int st = 2 * h + hs;
+#pragma unroll
+            for (int m = 0; m < NS; ++m) {
+              acc0[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
+                                                                    __builtin_bit_cast(bf16x8, b0[hs]), acc0[m][nt], 0, 0, 0);
+              if (MODE == kModeGateUp)
+                acc1[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][st]),
+                                                                      __builtin_bit_cast(bf16x8, b1[hs]), acc1[m][nt], 0, 0, 0);
+            }
           }
         }
       }
     }
+  } else {
+    // Per block: the block's activations are requested first, then the next block's codes
+    // (the block after the last wraps to block 0 and is not used), so waiting for the
+    // activations never waits for those codes (memory counters retire in order) and the
+    // codes have the whole block's decode to arrive.
+    // With APRE the activations are double-buffered as well: block kb+1's are requested during
+    // block kb, so every wait in the loop is for loads issued a whole block earlier.
+    // The loop is unrolled by two over ping-pong buffers (A, B): the buffer being decoded and the
+    // one being loaded are live together, and with one buffer per role in every step no register
+    // copy (which would wait for the load it copies) is needed between blocks.
+    u32x4 aA[NS][4], aB[NS][4];
+    if (APRE) load_a<NS, FRAG>(aA, p.act, aoff, kblocks - 1);
+    const int ob_last = (kblocks - 1) * 32 + tc * 8;
+    RunSet<NT> A0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
+    RunSet<NT> A1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : A0;
+    RunSet<NT> B0, B1;
+    keep_apart(A0);
+    if (MODE == kModeGateUp) keep_apart(A1);
+    if (APRE) keep_apart<NS>(aA);
+    // one block: decode c0/c1 (block_at(i)) against its activations `acur`, while block_at(i+1)'s
+    // codes go to n0/n1 and (APRE) its activations to `anext`
+    auto step = [&](int i, const RunSet<NT>& c0, const RunSet<NT>& c1, u32x4 (&acur)[NS][4], RunSet<NT>& n0,
+                    RunSet<NT>& n1, u32x4 (&anext)[NS][4]) {
+      const int kb = block_at(i, kblocks);
+      const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
+      if (APRE) load_a<NS, FRAG>(anext, p.act, aoff, kn);
+      else load_a<NS, FRAG>(acur, p.act, aoff, kb);
+      const int ob = kn * 32 + tc * 8;
+      const uint32_t back = (i + 1 < kblocks || tc != 3) ? 0u : 8u;
+      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
+      if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
+      const RunSet<NT> m0 = to_mfma_layout(c0);
+      const RunSet<NT> m1 = (MODE == kModeGateUp) ? to_mfma_layout(c1) : m0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          u32x4 b0[2], b1[2];
+          const RunCodes& x0 = m0.c[nt];
+          lut.decode16(h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
+          if (MODE == kModeGateUp) {
+            const RunCodes& x1 = m1.c[nt];
+            lut.decode16(h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+          }
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            const int st = 2 * h + hs;
+#pragma unroll
+            for (int m = 0; m < NS; ++m) {
+              acc0[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, acur[m][st]),
+                                                                    __builtin_bit_cast(bf16x8, b0[hs]), acc0[m][nt], 0, 0, 0);
+              if (MODE == kModeGateUp)
+                acc1[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, acur[m][st]),
+                                                                      __builtin_bit_cast(bf16x8, b1[hs]), acc1[m][nt], 0, 0, 0);
+            }
+          }
+        }
+      }
+      // keep the next block's decode (which reads the codes just requested) after this block's work
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int i = 0;
+    for (; i + 1 < kblocks; i += 2) {
+      step(i, A0, A1, aA, B0, B1, aB);
+      step(i + 1, B0, B1, aB, A0, A1, aA);
+    }
+    if (i < kblocks) step(i, A0, A1, aA, B0, B1, aB);
   }
 
   grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1);
@@ -548,7 +676,9 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
   const size_t mat_bytes = (size_t)p.rows * row_bytes;
   const uint8_t* base0 = p.codes0 + (size_t)un.e * mat_bytes;
   const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
-  const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+  // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
+  const int tc = DEC::kPipelined ? code_chunk(lane) : g;
+  const uint32_t roff = (uint32_t)(r0 + (DEC::kPipelined ? code_row(lane) : j)) * (uint32_t)row_bytes;
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
   const bool wraps = kb_hi == kblocks;
   const int len = kb_hi - kb_lo;
@@ -563,60 +693,122 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
     for (int nt = 0; nt < NT; ++nt) acc0[q][nt] = acc1[q][nt] = 0.f;
   }
 
-  u32x4 xn[NQ][4];
-  if (APRE) load_a_block<NQ>(xn, p.act, xoff, block_of(0));
-  RunSet<NT> n0, n1;
-  if (wraps) {
-    const int ob_last = (kblocks - 1) * 32 + g * 8;
-    n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-    n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
-  } else {
-    const int ob = kb_lo * 32 + g * 8;
-    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob);
-    n1 = (MODE == kModeGateUp) ? load_runs<NT, false>(base1, roff, nt_stride, ob) : n0;
-  }
-  for (int i = 0; i < len; ++i) {
-    const int kb = block_of(i);
-    // the next block; after the last, the range's first in-row block again (unused; 8 bytes
-    // back for lane group 3 where a one-block row would otherwise be left)
-    const int kn = i + 1 < len ? block_of(i + 1) : kb_lo;
-    u32x4 x[NQ][4];
-    if (APRE) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) x[q][st] = xn[q][st];
-      }
-      load_a_block<NQ>(xn, p.act, xoff, kn);
+  if constexpr (!DEC::kPipelined) {
+    u32x4 xn[NQ][4];
+    if (APRE) load_a_block<NQ>(xn, p.act, xoff, block_of(0));
+    RunSet<NT> n0, n1;
+    if (wraps) {
+      const int ob_last = (kblocks - 1) * 32 + tc * 8;
+      n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
+      n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
     } else {
-      load_a_block<NQ>(x, p.act, xoff, kb);
+      const int ob = kb_lo * 32 + tc * 8;
+      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob);
+      n1 = (MODE == kModeGateUp) ? load_runs<NT, false>(base1, roff, nt_stride, ob) : n0;
     }
-    const RunSet<NT> c0 = n0, c1 = n1;
-    const int ob = kn * 32 + g * 8;
-    const uint32_t back = (i + 1 < len || g != 3 || kn + 1 < kblocks) ? 0u : 8u;
-    n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
-    if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
+    for (int i = 0; i < len; ++i) {
+      const int kb = block_of(i);
+      // the next block; after the last, the range's first in-row block again (unused; 8 bytes
+      // back for lane group 3 where a one-block row would otherwise be left)
+      const int kn = i + 1 < len ? block_of(i + 1) : kb_lo;
+      u32x4 x[NQ][4];
+      if (APRE) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+        for (int q = 0; q < NQ; ++q) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        u32x4 b0[2], b1[2];
-        const RunCodes& x0 = c0.c[nt];
-        lut.decode16(h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
-        if (MODE == kModeGateUp) {
-          const RunCodes& x1 = c1.c[nt];
-          lut.decode16(h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+          for (int st = 0; st < 4; ++st) x[q][st] = xn[q][st];
         }
+        load_a_block<NQ>(xn, p.act, xoff, kn);
+      } else {
+        load_a_block<NQ>(x, p.act, xoff, kb);
+      }
+      const RunSet<NT> c0 = n0, c1 = n1;
+      const int ob = kn * 32 + tc * 8;
+      const uint32_t back = (i + 1 < len || tc != 3 || kn + 1 < kblocks) ? 0u : 8u;
+      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
+      if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
-            acc0[q][nt] = dot8(b0[hs], x[q][2 * h + hs], acc0[q][nt]);
-            if (MODE == kModeGateUp) acc1[q][nt] = dot8(b1[hs], x[q][2 * h + hs], acc1[q][nt]);
+        for (int nt = 0; nt < NT; ++nt) {
+          u32x4 b0[2], b1[2];
+          const RunCodes& x0 = c0.c[nt];
+          lut.decode16(h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
+          if (MODE == kModeGateUp) {
+            const RunCodes& x1 = c1.c[nt];
+            lut.decode16(h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+          }
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+              acc0[q][nt] = dot8(b0[hs], x[q][2 * h + hs], acc0[q][nt]);
+              if (MODE == kModeGateUp) acc1[q][nt] = dot8(b1[hs], x[q][2 * h + hs], acc1[q][nt]);
+            }
           }
         }
       }
     }
+  } else {
+    // ping-pong buffers, as in task_grouped: no register copy between blocks
+    u32x4 xA[NQ][4], xB[NQ][4];
+    if (APRE) load_a_block<NQ>(xA, p.act, xoff, block_of(0));
+    RunSet<NT> A0, A1, B0, B1;
+    if (wraps) {
+      const int ob_last = (kblocks - 1) * 32 + tc * 8;
+      A0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
+      A1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : A0;
+    } else {
+      const int ob = kb_lo * 32 + tc * 8;
+      A0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob);
+      A1 = (MODE == kModeGateUp) ? load_runs<NT, false>(base1, roff, nt_stride, ob) : A0;
+    }
+    keep_apart(A0);
+    if (MODE == kModeGateUp) keep_apart(A1);
+    if (APRE) keep_apart<NQ>(xA);
+    auto step = [&](int i, const RunSet<NT>& c0, const RunSet<NT>& c1, u32x4 (&x)[NQ][4], RunSet<NT>& n0,
+                    RunSet<NT>& n1, u32x4 (&xnext)[NQ][4]) {
+      const int kb = block_of(i);
+      // the next block; after the last, the range's first in-row block again (unused; 8 bytes
+      // back for lane group 3 where a one-block row would otherwise be left)
+      const int kn = i + 1 < len ? block_of(i + 1) : kb_lo;
+      if (APRE) load_a_block<NQ>(xnext, p.act, xoff, kn);
+      else load_a_block<NQ>(x, p.act, xoff, kb);
+      const int ob = kn * 32 + tc * 8;
+      const uint32_t back = (i + 1 < len || tc != 3 || kn + 1 < kblocks) ? 0u : 8u;
+      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
+      if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
+      const RunSet<NT> m0 = to_mfma_layout(c0);
+      const RunSet<NT> m1 = (MODE == kModeGateUp) ? to_mfma_layout(c1) : m0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          u32x4 b0[2], b1[2];
+          const RunCodes& x0 = m0.c[nt];
+          lut.decode16(h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
+          if (MODE == kModeGateUp) {
+            const RunCodes& x1 = m1.c[nt];
+            lut.decode16(h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+          }
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+              acc0[q][nt] = dot8(b0[hs], x[q][2 * h + hs], acc0[q][nt]);
+              if (MODE == kModeGateUp) acc1[q][nt] = dot8(b1[hs], x[q][2 * h + hs], acc1[q][nt]);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // as in task_grouped
+    };
+    int i = 0;
+    for (; i + 1 < len; i += 2) {
+      step(i, A0, A1, xA, B0, B1, xB);
+      step(i + 1, B0, B1, xB, A0, A1, xA);
+    }
+    if (i < len) step(i, A0, A1, xA, B0, B1, xB);
   }
 }
 
@@ -940,24 +1132,58 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
     for (int m = 0; m < (q.codes1 ? 2 : 1); ++m) {
       const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
       uint16_t* out = (m ? q.out1 : q.out0) + (size_t)e * (size_t)q.out_expert_stride;
-      const uint32_t roff = (uint32_t)(r0 + j) * (uint32_t)row_bytes;
-      RunCodes nx = load_run_wrapping(base, roff, (kblocks - 1) * 32 + g * 8, row_bytes);
-      for (int i = 0; i < kblocks; ++i) {
-        const int kb = block_at(i, kblocks);
-        const RunCodes rc = nx;
-        if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + g * 8);
-        u32x4 w[4];
-        dec.decode16(rc.d0, rc.d1, w[0], w[1]);
-        dec.decode16(rc.d1, rc.la, w[2], w[3]);
-        if (q.fragment_order) {
+      // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
+      const int tc = Dec::kPipelined ? code_chunk(lane) : g;
+      const uint32_t roff = (uint32_t)(r0 + (Dec::kPipelined ? code_row(lane) : j)) * (uint32_t)row_bytes;
+      if constexpr (!Dec::kPipelined) {
+        RunCodes nx = load_run_wrapping(base, roff, (kblocks - 1) * 32 + tc * 8, row_bytes);
+        for (int i = 0; i < kblocks; ++i) {
+          const int kb = block_at(i, kblocks);
+          const RunCodes rc = nx;
+          if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + tc * 8);
+          u32x4 w[4];
+          dec.decode16(rc.d0, rc.d1, w[0], w[1]);
+          dec.decode16(rc.d1, rc.la, w[2], w[3]);
+          if (q.fragment_order) {
 #pragma unroll
-          for (int st = 0; st < 4; ++st)
-            *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
-        } else {
-          uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
+            for (int st = 0; st < 4; ++st)
+              *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
+          } else {
+            uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
 #pragma unroll
-          for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+            for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+          }
         }
+
+      } else {
+        // ping-pong code buffers (no register copy between blocks; see task_grouped)
+        RunCodes cA = load_run_wrapping(base, roff, (kblocks - 1) * 32 + tc * 8, row_bytes), cB{};
+        keep_apart(cA);
+        auto step = [&](int i, const RunCodes& rc, RunCodes& nx) {
+          const int kb = block_at(i, kblocks);
+          if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + tc * 8);
+          const RunCodes m = to_mfma_layout(rc);
+          u32x4 w[4];
+          dec.decode16(m.d0, m.d1, w[0], w[1]);
+          dec.decode16(m.d1, m.la, w[2], w[3]);
+          if (q.fragment_order) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
+          } else {
+            uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+          }
+          __builtin_amdgcn_sched_barrier(0);  // as in task_grouped
+        };
+        int i = 0;
+        for (; i + 1 < kblocks; i += 2) {
+          step(i, cA, cB);
+          step(i + 1, cB, cA);
+        }
+        if (i < kblocks) step(i, cA, cB);
+
       }
     }
   }
