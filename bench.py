@@ -345,9 +345,9 @@ def calibrate_copy():
     del a, b
 
 
-def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=None, layouts=(0,)):
+def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=None, layouts=(0,), rung="bitshift"):
     import moe_inputs
-    shape = moe_inputs.WORKLOADS["v4_decode_n32"]
+    shape = moe_inputs.WORKLOADS["v4_decode_n32" if rung == "bitshift" else "lut_v4_decode_n32"]
     log("sweep: drawing V4-shaped weights once")
     n_list = n_list or SWEEP_N
     inps = moe_inputs.make_inputs_multi(shape, n_list, seed=0)
@@ -364,7 +364,8 @@ def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=N
                 sched = r.q.qtip_moe_plan_schedule(r.plan, n)
                 fig = schedule_figures(counts, r.shape, arm, sched)
                 ms = res["wall_s"] * 1e3 / steps
-                rec = {"arm": arm, "n": n, "variant_requested": variant, "act_layout": layout, "ms_per_step": ms,
+                rec = {"rung": rung, "arm": arm, "n": n, "variant_requested": variant, "act_layout": layout,
+                       "ms_per_step": ms,
                        "tokens_per_s": n / (ms * 1e-3),
                        "stage_ms": {k: v / prof["n_forwards"] for k, v in prof.items() if k != "n_forwards"},
                        "launches": {k: res["stats"][k] for k in ("gemv_launches", "grouped_launches",
@@ -490,6 +491,7 @@ def main():
     ap.add_argument("--sweep-layouts", default="0", help="grouped-arm activation layouts to sweep (0 auto, 1 rows, "
                     "2 fragments)")
     ap.add_argument("--sweep-n", default=None, help="comma-separated token counts (default: the fixed list)")
+    ap.add_argument("--sweep-rung", choices=["bitshift", "lut"], default="bitshift")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection files")
@@ -517,7 +519,7 @@ def main():
             calibrate_copy()
         n_list = [int(x) for x in args.sweep_n.split(",")] if args.sweep_n else None
         run_sweep(args.sweep, args.steps, args.warmup, args.variant, tuple(args.sweep_arms.split(",")), n_list,
-                  tuple(int(x) for x in args.sweep_layouts.split(",")))
+                  tuple(int(x) for x in args.sweep_layouts.split(",")), args.sweep_rung)
         return
 
     curve = [c for c in args.curve.split(",") if c and c != args.workload]

@@ -82,14 +82,22 @@ enum { QTIP_ACT_AUTO = 0, QTIP_ACT_ROWS = 1, QTIP_ACT_FRAGMENTS = 2 };
 enum { QTIP_RUNG_BITSHIFT = 0, QTIP_RUNG_LUT = 1 };
 #define QTIP_LUT_RUNG_BITS 9 /* pair-state bits of the LUT rung: a 2^9 x 2 codebook */
 
-/* Decode-regime floor: n <= 8 tokens always take the GEMV arm (m-tile page, "The fix"). */
+/* Decode-regime floor of the pages: n <= 8 tokens always take the GEMV arm (m-tile page, "The
+ * fix": kept there as a graph-capture safety rule, not a performance claim).  The plan-free
+ * qtip_fill_* functions below use it. */
 #define QTIP_DECODE_REGIME_MAX_TOKENS 8
+/* The floor a plan uses by default (qtip_moe_desc.decode_floor = 0): re-derived for these
+ * kernels on MI355X, where both arms are safe under graph capture and the measured crossover of
+ * the V4 layer lies between 4 and 5 tokens on both rungs (the grouped arm is faster from 5). */
+#define QTIP_DEFAULT_DECODE_FLOOR 4
 /* Default m-tile height: the M of one bf16 MFMA (v_mfma_f32_16x16x32_bf16). */
 #define QTIP_DEFAULT_TILE_M 16
 /* The fill threshold re-derived for these kernels on MI355X.  The grouped arm decodes each
- * expert once per up to 64 binned pairs (not once per m-tile), so tile fill does not amortise
- * anything; the measured GEMV/grouped crossover lies between 4 and 8 tokens at V4 routing,
- * i.e. at the decode-regime floor, which a threshold of 1 pair per woken expert reproduces. */
+ * expert once per up to 48-64 binned pairs (not once per m-tile), so tile fill amortises
+ * nothing; the measured GEMV/grouped crossover lies between 4 and 5 tokens at V4 routing, where
+ * pairs per woken expert are about 1.  At this threshold (1 pair) the fill predicate holds for
+ * every n, so the plan's decode floor alone places the switch; the predicate decides with a
+ * higher threshold (16 reproduces the pages' gate at 683 tokens). */
 #define QTIP_DEFAULT_DISPATCH_TILE_M 1
 /* Fused GEMV vs dequantize arm: the GEMV streams an expert's packed bytes once per pair;
  * materialising writes and re-reads dense bf16, 2 x 16/2 = 16 times the packed bytes (m-tile
@@ -130,6 +138,9 @@ typedef struct qtip_moe_desc {
   int32_t rung;         /* weight format of the experts: QTIP_RUNG_BITSHIFT (a 16-bit window per weight into
                            the 65536-entry LUT) or QTIP_RUNG_LUT (a 9-bit state per weight pair into the
                            512 x 2 codebook); see the weight formats above */
+  int32_t decode_floor; /* AUTO dispatch sends n <= decode_floor to the GEMV arm whatever the fill: 0 = the
+                           value measured for these kernels (QTIP_DEFAULT_DECODE_FLOOR); 8 reproduces the
+                           pages' floor; 1..1024 accepted */
 } qtip_moe_desc;
 
 typedef struct qtip_moe_plan_s* qtip_moe_plan_t;
@@ -213,13 +224,14 @@ typedef struct qtip_moe_schedule {
 qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_moe_schedule* out /*host*/);
 
 /* The arm a forward of n tokens takes: the override if one is set, else the three-arm closed
- * form (qtip_fill_select_arm) with the plan's dispatch_tile_m and dequant_traffic_ratio.
+ * form (qtip_fill_select_arm) with the plan's dispatch_tile_m, dequant_traffic_ratio and decode_floor.
  * Returns QTIP_ARM_GEMV, QTIP_ARM_GROUPED or QTIP_ARM_DEQUANT, or -1 for a bad plan/n.
  * Source: m-tile page, PR #167, "The fix" (the predicate and the floor) and its post-merge
  * note (an explicit arm pin overrides the predicate, so a harness can A/B the kernels). */
 int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens);
 
-/* The pure closed-form predicate for the plan's routing shape: 1 if n > 8 and the expected
+/* The pure closed-form predicate for the plan's routing shape: 1 if n > the plan's decode_floor
+ * and the expected
  * pairs per woken expert, n k / (E (1 - (1 - k/E)^n)), reach the plan's dispatch_tile_m,
  * else 0; -1 for a bad plan or n < 1.  The plan's arm override is NOT applied here (the arm a
  * forward takes is qtip_moe_select_arm).  Host only; the same header-only code as the plan.
@@ -243,8 +255,9 @@ qtip_status qtip_moe_dequantize(qtip_moe_plan_t plan, const qtip_moe_weights* w 
 
 /* ---- closed-form fill model (m-tile page, "The cause is a threshold" and "The fix") --
  * Uniform routing of n tokens to k of E experts wakes E(1-(1-k/E)^n) experts on average;
- * pairs per woken expert = n k / that.  The grouped arm is selected iff n > 8 and pairs
- * per woken expert >= tile_m (the threshold).  Pure host functions of their arguments. */
+ * pairs per woken expert = n k / that.  The grouped arm is selected iff n > 8 (the pages'
+ * floor, QTIP_DECODE_REGIME_MAX_TOKENS; a plan uses its own decode_floor) and pairs per woken
+ * expert >= tile_m (the threshold).  Pure host functions of their arguments. */
 double qtip_fill_woken_experts(int32_t n, int32_t k, int32_t E);
 double qtip_fill_pairs_per_woken_expert(int32_t n, int32_t k, int32_t E);
 int32_t qtip_fill_select_grouped(int32_t n, int32_t k, int32_t E, int32_t tile_m); /* 1 / 0, -1 bad args */

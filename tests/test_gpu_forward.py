@@ -129,12 +129,25 @@ def test_v4_small_batches_full_parity():
     """Decode-width batches of the V4 layer on the GEMV arm, whose launches have fewer tasks than
     the GPU has wave slots and run with fewer waves per workgroup on every CU; every token is
     compared."""
-    inps = moe_inputs.make_inputs_multi(moe_inputs.WORKLOADS["v4_decode_n32"], [1, 2, 5], seed=21)
-    layer = Layer(inps[1], out_dtype="f32", max_tokens=5)
-    for n in (1, 2, 5):
+    inps = moe_inputs.make_inputs_multi(moe_inputs.WORKLOADS["v4_decode_n32"], [1, 2, 5, 8], seed=21)
+    layer = Layer(inps[1], arm=q.QTIP_ARM_GEMV, out_dtype="f32", max_tokens=8)
+    for n in (1, 2, 5, 8):
         say(f"forward V4 small batch n={n}")
         got = layer.forward(inps[n])
         assert q.qtip_moe_stats(layer.plan)["last_arm"] == q.QTIP_ARM_GEMV
+        check(got, moe.moe_forward(inps[n]), "f32")
+    layer.close()
+
+
+def test_v4_decode_floor_sends_five_tokens_to_the_grouped_arm():
+    """The plan's decode floor (4 by default): 4 tokens take the GEMV arm, 5 the grouped arm; both
+    match the oracle token by token."""
+    inps = moe_inputs.make_inputs_multi(moe_inputs.WORKLOADS["v4_decode_n32"], [4, 5], seed=22)
+    layer = Layer(inps[4], out_dtype="f32", max_tokens=5)
+    for n, arm in ((4, q.QTIP_ARM_GEMV), (5, q.QTIP_ARM_GROUPED)):
+        say(f"forward V4 floor n={n}")
+        got = layer.forward(inps[n])
+        assert q.qtip_moe_stats(layer.plan)["last_arm"] == arm
         check(got, moe.moe_forward(inps[n]), "f32")
     layer.close()
 

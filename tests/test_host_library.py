@@ -119,13 +119,32 @@ def test_dequantize_argument_errors_return_before_any_launch():
 
 
 def test_default_dispatch_threshold_is_the_rederived_value():
-    # one pair per woken expert: the grouped arm from the decode-regime floor on
+    # one pair per woken expert, floor 4: the grouped arm from 5 tokens (the measured crossover)
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
-    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == 9 == fill.min_tokens_grouped(6, 256, 1)
-    assert q.qtip_moe_select_arm(plan, 8) == q.QTIP_ARM_GEMV
-    assert q.qtip_moe_select_arm(plan, 9) == q.QTIP_ARM_GROUPED
-    assert "threshold 1 pairs" in q.qtip_moe_engaged_line(plan, 32)
+    assert q.QTIP_DEFAULT_DECODE_FLOOR == 4
+    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == 5 == fill.min_tokens_grouped(6, 256, 1, floor=4)
+    assert q.qtip_moe_select_arm(plan, 4) == q.QTIP_ARM_GEMV
+    assert q.qtip_moe_select_arm(plan, 5) == q.QTIP_ARM_GROUPED
+    line = q.qtip_moe_engaged_line(plan, 32)
+    assert "threshold 1 pairs" in line and "GEMV up to 4 tokens" in line
     q.qtip_moe_plan_destroy(plan)
+    # the pages' floor, 8, as a plan field
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, decode_floor=8), "gfx950")
+    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == 9 == fill.min_tokens_grouped(6, 256, 1)
+    assert q.qtip_moe_select_arm(plan, 8) == q.QTIP_ARM_GEMV and q.qtip_moe_select_arm(plan, 9) == q.QTIP_ARM_GROUPED
+    q.qtip_moe_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("floor", [1, 2, 4, 8, 16, 100])
+def test_decode_floor_field_moves_the_switch(floor):
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, decode_floor=floor), "gfx950")
+    for n in range(1, 130):
+        want = {"gemv": q.QTIP_ARM_GEMV, "grouped": q.QTIP_ARM_GROUPED}[fill.select_arm(n, 6, 256, 1, floor=floor)]
+        assert q.qtip_moe_select_arm(plan, n) == want, (floor, n)
+    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == floor + 1
+    q.qtip_moe_plan_destroy(plan)
+    with pytest.raises(q.QtipError):
+        q.qtip_moe_plan_for_arch(q.make_desc(**V4, decode_floor=-1), "gfx950")
 
 
 @pytest.mark.parametrize("tile_m", [16, 32, 64])
@@ -236,13 +255,13 @@ def test_schedule_reports_what_a_forward_launches():
 
 
 def test_default_kernel_shapes_follow_the_measured_rules():
-    # V4 layer (E=256, k=6; 6, 11.9, 23.2 and 44.3 woken experts at n = 1, 2, 4, 8).  GEMV fused
+    # V4 layer (E=256, k=6; 6, 11.9 and 23.2 woken experts at n = 1, 2, 4; grouped from 5).  GEMV fused
     # pass: 8 waves below 5 16-row tasks per CU, 16 waves from there, 32-row tasks once
     # woken*rows/32 >= 2048 wave slots; GEMV down pass: 16 waves up to 6144 32-row tasks.  Grouped
     # picks by pairs per woken expert (1.41 at n=32, 3.15 at 128, 6.0 at 256, 12.0 at 512, 24.0 at
     # 1024).
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
-    want = {1: (2, 1), 2: (1, 1), 4: (1, 1), 8: (4, 1), 32: (1, 3), 128: (1, 7), 256: (9, 10), 512: (9, 10), 1024: (9, 10)}
+    want = {1: (2, 1), 2: (1, 1), 4: (1, 1), 8: (1, 3), 32: (1, 3), 128: (1, 7), 256: (9, 10), 512: (9, 10), 1024: (9, 10)}
     for n, (gu, dn) in want.items():
         s = q.qtip_moe_plan_schedule(plan, n)
         assert (s["gate_up"]["variant"], s["down"]["variant"]) == (gu, dn), n
@@ -319,7 +338,8 @@ SHAPES = [(6, 256, 16), (6, 256, 1), (2, 8, 16), (6, 8, 16), (8, 128, 16), (4, 6
 
 @pytest.mark.parametrize("k,E,thr", SHAPES)
 def test_select_grouped_is_the_oracle_predicate(k, E, thr):
-    plan = q.qtip_moe_plan_for_arch(q.make_desc(E, k, 256, 128, 4096, dispatch_tile_m=thr), "gfx950")
+    # the pages' floor (8) set on the plan, so the closed form is the pages' predicate exactly
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(E, k, 256, 128, 4096, dispatch_tile_m=thr, decode_floor=8), "gfx950")
     for n in list(range(1, 40)) + [64, 127, 128, 512, 682, 683, 684, 1024, 1572, 2000, 4096]:
         assert q.qtip_moe_select_grouped(plan, n) == int(fill.select_grouped(n, k, E, thr)), (k, E, thr, n)
     n0 = fill.min_tokens_grouped(k, E, thr)

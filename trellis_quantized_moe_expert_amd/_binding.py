@@ -30,6 +30,8 @@ QTIP_ACT_ROWS = 1
 QTIP_ACT_FRAGMENTS = 2
 QTIP_OUT_BF16 = 0
 QTIP_OUT_F32 = 1
+QTIP_DEFAULT_DECODE_FLOOR = 4
+QTIP_DECODE_REGIME_MAX_TOKENS = 8
 QTIP_RUNG_BITSHIFT = 0
 QTIP_RUNG_LUT = 1
 QTIP_LUT_RUNG_BITS = 9
@@ -40,7 +42,7 @@ class qtip_moe_desc(ctypes.Structure):
                 ("inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("arm_override", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("dispatch_tile_m", ctypes.c_int32), ("dequant_traffic_ratio", ctypes.c_int32),
-                ("act_layout", ctypes.c_int32), ("rung", ctypes.c_int32)]
+                ("act_layout", ctypes.c_int32), ("rung", ctypes.c_int32), ("decode_floor", ctypes.c_int32)]
 
 
 class qtip_moe_weights(ctypes.Structure):
@@ -172,9 +174,9 @@ def _check(fn: str, status: int):
 
 def make_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override=QTIP_ARM_AUTO, variant=0,
               out_dtype=QTIP_OUT_F32, tile_m=0, dispatch_tile_m=0, dequant_traffic_ratio=0,
-              act_layout=QTIP_ACT_AUTO, rung=QTIP_RUNG_BITSHIFT) -> qtip_moe_desc:
+              act_layout=QTIP_ACT_AUTO, rung=QTIP_RUNG_BITSHIFT, decode_floor=0) -> qtip_moe_desc:
     return qtip_moe_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override, variant, out_dtype, tile_m,
-                         dispatch_tile_m, dequant_traffic_ratio, act_layout, rung)
+                         dispatch_tile_m, dequant_traffic_ratio, act_layout, rung, decode_floor)
 
 
 def make_weights(codes_gate, codes_up, codes_down, scale_gate, scale_up, scale_down, lut) -> qtip_moe_weights:

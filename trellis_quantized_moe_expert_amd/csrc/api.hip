@@ -25,6 +25,7 @@ struct qtip_moe_plan_s {
   qtip_moe_desc d;
   int32_t tile_m;
   int32_t dispatch_tile_m;
+  int32_t decode_floor;         // n <= decode_floor always takes the GEMV arm
   int32_t dequant_ratio;        // fused GEMV kept while pairs per woken expert are below this
   int32_t dequant_lo, dequant_hi;  // token counts [lo, hi) the automatic dispatch sends to the dequantize arm
   bool dense;                   // the dequantize arm may run: its dense weights are in the workspace
@@ -335,6 +336,8 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
   if (tm != 16 && tm != 32 && tm != 64) return fail(QTIP_ERR_INVALID_ARG, "tile_m must be 0, 16, 32 or 64");
   if (d->dispatch_tile_m < 0 || d->dispatch_tile_m > 1024)
     return fail(QTIP_ERR_INVALID_ARG, "dispatch_tile_m must be in [0, 1024]");
+  if (d->decode_floor < 0 || d->decode_floor > 1024)
+    return fail(QTIP_ERR_INVALID_ARG, "decode_floor must be in [0, 1024]");
   if (d->rung != QTIP_RUNG_BITSHIFT && d->rung != QTIP_RUNG_LUT)
     return fail(QTIP_ERR_INVALID_ARG, "rung must be QTIP_RUNG_BITSHIFT or QTIP_RUNG_LUT");
   *tile_m = tm;
@@ -354,7 +357,8 @@ CallChoice call_choice(const qtip_moe_plan_s* plan, int32_t n_tokens) {
   CallChoice c{};
   c.arm = d.arm_override != QTIP_ARM_AUTO
               ? d.arm_override
-              : fill_select_arm(n_tokens, d.top_k, d.num_experts, plan->dispatch_tile_m, plan->dequant_ratio);
+              : fill_select_arm(n_tokens, d.top_k, d.num_experts, plan->dispatch_tile_m, plan->dequant_ratio,
+                                plan->decode_floor);
   c.karm = kernel_arm(c.arm);
   const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
   c.frag = plan->frag && c.karm == kArmGrouped && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kFragMinPairs);
@@ -459,7 +463,9 @@ qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc, const char* gcn_ar
   p->dispatch_tile_m = desc->dispatch_tile_m == 0 ? QTIP_DEFAULT_DISPATCH_TILE_M : desc->dispatch_tile_m;
   p->d.dispatch_tile_m = p->dispatch_tile_m;
   p->device = -1;
-  p->min_tokens_grouped = fill_min_tokens(desc->top_k, desc->num_experts, p->dispatch_tile_m);
+  p->decode_floor = desc->decode_floor == 0 ? QTIP_DEFAULT_DECODE_FLOOR : desc->decode_floor;
+  p->d.decode_floor = p->decode_floor;
+  p->min_tokens_grouped = fill_min_tokens(desc->top_k, desc->num_experts, p->dispatch_tile_m, p->decode_floor);
   p->dequant_ratio = desc->dequant_traffic_ratio == 0 ? kDequantTrafficRatio : desc->dequant_traffic_ratio;
   p->d.dequant_traffic_ratio = p->dequant_ratio;
   // Pairs per woken expert never decrease with n, so the automatic dispatch's dequantize
@@ -467,7 +473,7 @@ qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc, const char* gcn_ar
   // ratio up to the grouped arm's first n.
   p->dequant_lo = p->dequant_hi = 0;
   if (p->dequant_ratio < p->dispatch_tile_m) {
-    const int32_t lo = fill_min_tokens(desc->top_k, desc->num_experts, p->dequant_ratio);
+    const int32_t lo = fill_min_tokens(desc->top_k, desc->num_experts, p->dequant_ratio, p->decode_floor);
     int32_t hi = p->min_tokens_grouped;
     if (hi < 0 || hi > desc->max_tokens + 1) hi = desc->max_tokens + 1;
     if (lo > 0 && lo < hi) {
@@ -549,13 +555,15 @@ qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_
 
 int32_t qtip_moe_select_grouped(qtip_moe_plan_t plan, int32_t n_tokens) {
   if (!plan || n_tokens < 1) return -1;
-  return fill_select_grouped(n_tokens, plan->d.top_k, plan->d.num_experts, plan->dispatch_tile_m) ? 1 : 0;
+  return fill_select_grouped(n_tokens, plan->d.top_k, plan->d.num_experts, plan->dispatch_tile_m, plan->decode_floor)
+             ? 1 : 0;
 }
 
 int32_t qtip_moe_select_arm(qtip_moe_plan_t plan, int32_t n_tokens) {
   if (!plan || n_tokens < 1) return -1;
   if (plan->d.arm_override != QTIP_ARM_AUTO) return plan->d.arm_override;
-  return fill_select_arm(n_tokens, plan->d.top_k, plan->d.num_experts, plan->dispatch_tile_m, plan->dequant_ratio);
+  return fill_select_arm(n_tokens, plan->d.top_k, plan->d.num_experts, plan->dispatch_tile_m, plan->dequant_ratio,
+                         plan->decode_floor);
 }
 
 qtip_status qtip_arch_witness(int device, void* stream) {
@@ -1106,11 +1114,12 @@ qtip_status qtip_moe_engaged_line(qtip_moe_plan_t plan, int32_t n_tokens, char* 
   const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
   std::snprintf(buf, buf_len,
                 "qtip_moe: %s arm for %d tokens x top-%d of %d experts; mean m-tile fill %.1f%% "
-                "(%.2f pairs per woken expert, tile_m=%d); dispatch threshold %d pairs, grouped from %d "
-                "tokens%s",
+                "(%.2f pairs per woken expert, tile_m=%d); dispatch threshold %d pairs, GEMV up to %d tokens, "
+                "grouped from %d tokens%s",
                 arm == QTIP_ARM_GROUPED ? "grouped" : (arm == QTIP_ARM_DEQUANT ? "dequantize" : "GEMV"), n_tokens,
                 d.top_k, d.num_experts,
-                100.0 * ppe / plan->tile_m, ppe, plan->tile_m, plan->dispatch_tile_m, plan->min_tokens_grouped,
+                100.0 * ppe / plan->tile_m, ppe, plan->tile_m, plan->dispatch_tile_m, plan->decode_floor,
+                plan->min_tokens_grouped,
                 d.arm_override != QTIP_ARM_AUTO ? " (arm pinned by the plan)" : "");
   return QTIP_OK;
 }
