@@ -86,15 +86,17 @@ enum { QTIP_RUNG_BITSHIFT = 0, QTIP_RUNG_LUT = 1 };
  * fix": kept there as a graph-capture safety rule, not a performance claim).  The plan-free
  * qtip_fill_* functions below use it. */
 #define QTIP_DECODE_REGIME_MAX_TOKENS 8
-/* The floor a plan uses by default (qtip_moe_desc.decode_floor = 0): re-derived for these
- * kernels on MI355X, where both arms are safe under graph capture and the measured crossover of
- * the V4 layer lies between 4 and 5 tokens on both rungs (the grouped arm is faster from 5). */
-#define QTIP_DEFAULT_DECODE_FLOOR 4
+/* The floor a plan uses by default (qtip_moe_desc.decode_floor = 0), per rung: re-derived for
+ * these kernels on MI355X, where both arms are safe under graph capture.  The measured crossover
+ * of the V4 layer lies between 6 and 7 tokens on the bitshift rung and between 4 and 5 on the LUT
+ * rung (the grouped arm is faster from 7 and from 5). */
+#define QTIP_DEFAULT_DECODE_FLOOR_BITSHIFT 6
+#define QTIP_DEFAULT_DECODE_FLOOR_LUT 4
 /* Default m-tile height: the M of one bf16 MFMA (v_mfma_f32_16x16x32_bf16). */
 #define QTIP_DEFAULT_TILE_M 16
 /* The fill threshold re-derived for these kernels on MI355X.  The grouped arm decodes each
  * expert once per up to 48-64 binned pairs (not once per m-tile), so tile fill amortises
- * nothing; the measured GEMV/grouped crossover lies between 4 and 5 tokens at V4 routing, where
+ * nothing; the measured GEMV/grouped crossover lies between 4 and 7 tokens at V4 routing, where
  * pairs per woken expert are about 1.  At this threshold (1 pair) the fill predicate holds for
  * every n, so the plan's decode floor alone places the switch; the predicate decides with a
  * higher threshold (16 reproduces the pages' gate at 683 tokens). */
@@ -139,8 +141,8 @@ typedef struct qtip_moe_desc {
                            the 65536-entry LUT) or QTIP_RUNG_LUT (a 9-bit state per weight pair into the
                            512 x 2 codebook); see the weight formats above */
   int32_t decode_floor; /* AUTO dispatch sends n <= decode_floor to the GEMV arm whatever the fill: 0 = the
-                           value measured for these kernels (QTIP_DEFAULT_DECODE_FLOOR); 8 reproduces the
-                           pages' floor; 1..1024 accepted */
+                           value measured for these kernels and the rung (QTIP_DEFAULT_DECODE_FLOOR_*); 8
+                           reproduces the pages' floor; 1..1024 accepted */
 } qtip_moe_desc;
 
 typedef struct qtip_moe_plan_s* qtip_moe_plan_t;

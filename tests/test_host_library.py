@@ -119,15 +119,18 @@ def test_dequantize_argument_errors_return_before_any_launch():
 
 
 def test_default_dispatch_threshold_is_the_rederived_value():
-    # one pair per woken expert, floor 4: the grouped arm from 5 tokens (the measured crossover)
-    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
-    assert q.QTIP_DEFAULT_DECODE_FLOOR == 4
-    assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == 5 == fill.min_tokens_grouped(6, 256, 1, floor=4)
-    assert q.qtip_moe_select_arm(plan, 4) == q.QTIP_ARM_GEMV
-    assert q.qtip_moe_select_arm(plan, 5) == q.QTIP_ARM_GROUPED
-    line = q.qtip_moe_engaged_line(plan, 32)
-    assert "threshold 1 pairs" in line and "GEMV up to 4 tokens" in line
-    q.qtip_moe_plan_destroy(plan)
+    # one pair per woken expert and the measured floor of each rung: the grouped arm from 7 tokens
+    # (bitshift) and from 5 (LUT rung), the measured crossovers
+    for rung, floor in ((q.QTIP_RUNG_BITSHIFT, 6), (q.QTIP_RUNG_LUT, 4)):
+        plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, rung=rung), "gfx950")
+        assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == floor + 1 == \
+            fill.min_tokens_grouped(6, 256, 1, floor=floor)
+        assert q.qtip_moe_select_arm(plan, floor) == q.QTIP_ARM_GEMV
+        assert q.qtip_moe_select_arm(plan, floor + 1) == q.QTIP_ARM_GROUPED
+        line = q.qtip_moe_engaged_line(plan, 32)
+        assert "threshold 1 pairs" in line and f"GEMV up to {floor} tokens" in line
+        q.qtip_moe_plan_destroy(plan)
+    assert (q.QTIP_DEFAULT_DECODE_FLOOR_BITSHIFT, q.QTIP_DEFAULT_DECODE_FLOOR_LUT) == (6, 4)
     # the pages' floor, 8, as a plan field
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, decode_floor=8), "gfx950")
     assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == 9 == fill.min_tokens_grouped(6, 256, 1)

@@ -463,7 +463,8 @@ qtip_status qtip_moe_plan_for_arch(const qtip_moe_desc* desc, const char* gcn_ar
   p->dispatch_tile_m = desc->dispatch_tile_m == 0 ? QTIP_DEFAULT_DISPATCH_TILE_M : desc->dispatch_tile_m;
   p->d.dispatch_tile_m = p->dispatch_tile_m;
   p->device = -1;
-  p->decode_floor = desc->decode_floor == 0 ? QTIP_DEFAULT_DECODE_FLOOR : desc->decode_floor;
+  p->decode_floor = desc->decode_floor != 0 ? desc->decode_floor
+                    : (desc->rung == QTIP_RUNG_LUT ? QTIP_DEFAULT_DECODE_FLOOR_LUT : QTIP_DEFAULT_DECODE_FLOOR_BITSHIFT);
   p->d.decode_floor = p->decode_floor;
   p->min_tokens_grouped = fill_min_tokens(desc->top_k, desc->num_experts, p->dispatch_tile_m, p->decode_floor);
   p->dequant_ratio = desc->dequant_traffic_ratio == 0 ? kDequantTrafficRatio : desc->dequant_traffic_ratio;
