@@ -379,19 +379,23 @@ def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=N
 
 
 HEADLINE = "v4_full_n1024"
-CURVE = ["v4_decode_n1", "v4_decode_n32", "v4_mid_n128", "v4_mid_n512", "v4_full_n683", "v4_zipf_n256", "tiny"]
+CURVE = ["v4_decode_n1", "v4_decode_n32", "v4_mid_n128", "v4_mid_n512", "v4_full_n683", "v4_zipf_n256", "tiny",
+         # the LUT rung (a 512 x 2 codebook per layer) on the same layer shapes
+         "lut_v4_decode_n1", "lut_v4_decode_n32", "lut_v4_mid_n128", "lut_v4_full_n1024"]
 
 
 def draw_layers(names):
-    """Seeded inputs for each workload; V4 layers with uniform routing share one weight draw (the
-    draw make_workload makes for each of them), so the device holds one copy of the weights."""
+    """Seeded inputs for each workload; the V4 layers of one rung with uniform routing share one
+    weight draw (the draw make_workload makes for each of them), so the device holds one copy of
+    each rung's weights."""
     import moe_inputs
     W = moe_inputs.WORKLOADS
-    shared = [n for n in names if W[n].num_experts == 256 and W[n].routing == "uniform"]
     out = {}
-    if shared:
-        multi = moe_inputs.make_inputs_multi(W[shared[0]], sorted({W[n].n_tokens for n in shared}), seed=0)
-        out.update({n: multi[W[n].n_tokens] for n in shared})
+    for rung in ("bitshift", "lut"):
+        shared = [n for n in names if W[n].num_experts == 256 and W[n].routing == "uniform" and W[n].rung == rung]
+        if shared:
+            multi = moe_inputs.make_inputs_multi(W[shared[0]], sorted({W[n].n_tokens for n in shared}), seed=0)
+            out.update({n: multi[W[n].n_tokens] for n in shared})
     for n in names:
         if n not in out:
             out[n] = moe_inputs.make_workload(n, seed=0)
@@ -442,7 +446,7 @@ def measure_workload(name, inp, weights, args, gather_measured, full=False):
     layer_syms = (fig["symbols_sched"]["gate_up"] + fig["symbols_sched"]["down"]) / (gu_s + dn_s)
     flops = 6.0 * s.n_tokens * s.top_k * s.hidden * s.inter
     rec = {
-        "workload": name, "n_tokens": s.n_tokens, "routing": s.routing,
+        "workload": name, "n_tokens": s.n_tokens, "routing": s.routing, "rung": s.rung,
         "shape": {"experts": s.num_experts, "top_k": s.top_k, "hidden": s.hidden, "inter": s.inter},
         "arm": arm, "variant": {"gate_up": sched["gate_up"]["variant"], "down": sched["down"]["variant"]},
         "tokens_per_s": s.n_tokens * args.steps / res["wall_s"], "ms_per_step": ms_per_step,

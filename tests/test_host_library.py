@@ -431,3 +431,17 @@ def test_noalloc_refuses_layers_beyond_its_scratch_on_the_host():
     assert "scratch" in str(ei.value)
     q.qtip_moe_plan_destroy(plan)
     assert q.QTIP_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_dequantize_workspace_holds_only_the_woken_experts():
+    # at most min(E, max_tokens * k) experts are woken, one dense slot each (3 matrices of H x I bf16)
+    per_expert = 3 * 4096 * 2048 * 2
+    for max_tokens, woken in ((1, 6), (32, 192), (43, 256), (1024, 256)):
+        plan = q.qtip_moe_plan_for_arch(q.make_desc(**{**V4, "max_tokens": max_tokens},
+                                                    arm_override=q.QTIP_ARM_DEQUANT), "gfx950")
+        base = q.qtip_moe_plan_for_arch(q.make_desc(**{**V4, "max_tokens": max_tokens},
+                                                    arm_override=q.QTIP_ARM_GEMV), "gfx950")
+        extra = q.qtip_moe_plan_info(plan)["workspace_bytes"] - q.qtip_moe_plan_info(base)["workspace_bytes"]
+        assert woken * per_expert <= extra < woken * per_expert + 4096, (max_tokens, extra)
+        q.qtip_moe_plan_destroy(plan)
+        q.qtip_moe_plan_destroy(base)

@@ -181,7 +181,8 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.y = o;            o = align256(o + P * (size_t)d.hidden * 4);
   L.router_part = o;  o = align256(o + router_part_elems(d, n_tokens) * 4);
   // dequantize arm: every expert's dense bf16 weights (only when the plan can take that arm)
-  const size_t dense_mat = dense ? (size_t)d.num_experts * (size_t)d.hidden * (size_t)d.inter * 2 : 0;
+  // dequantize arm: the dense weights of at most min(E, n k) woken experts, one slot each
+  const size_t dense_mat = dense ? woken_max * (size_t)d.hidden * (size_t)d.inter * 2 : 0;
   L.dense_gate = o;   o = align256(o + dense_mat);
   L.dense_up = o;     o = align256(o + dense_mat);
   L.dense_down = o;   o = align256(o + dense_mat);
@@ -820,6 +821,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   ExpertParams gu{};
   gu.dense0 = dense_gate;
   gu.dense1 = dense_up;
+  gu.dense_counts = counts;
   gu.codes0 = w->codes_gate;
   gu.codes1 = w->codes_up;
   gu.scale0 = w->scale_gate;
@@ -853,6 +855,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
 
   ExpertParams dn{};
   dn.dense0 = dense_down;
+  dn.dense_counts = counts;
   dn.codes0 = w->codes_down;
   dn.scale0 = w->scale_down;
   dn.lut = w->lut;

@@ -447,6 +447,18 @@ __device__ inline void grouped_epilogue(const ExpertParams& p, const Unit& un, i
   }
 }
 
+// The dense-weight slot of woken expert e: the number of experts below e with binned pairs (the
+// woken experts are materialised compactly, so the workspace holds min(E, n k) of them).  Every
+// lane of the wave gets the same value.
+__device__ inline int dense_slot(const int32_t* __restrict__ counts, int e) {
+  const int lane = threadIdx.x & 63;
+  int c = 0;
+  for (int i = lane; i < e; i += 64) c += counts[i] > 0 ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  return __builtin_amdgcn_readfirstlane(c);
+}
+
 // Dequantize arm: the grouped pass over weights materialised beforehand as dense bf16 in
 // fragment order (no decode, no LUT): the B fragment of MFMA step st of block kb for row
 // block r0/16 + nt is one coalesced 16-byte load per lane.  Same K permutation as the decode.
@@ -456,8 +468,9 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
   const int j = lane & 15, g = lane >> 4;
   const int kblocks = p.cols / kKBlock;
   const size_t mat = (size_t)p.rows * (size_t)p.cols;
-  const uint16_t* w0 = p.dense0 + (size_t)un.e * mat;
-  const uint16_t* w1 = (MODE == kModeGateUp) ? p.dense1 + (size_t)un.e * mat : w0;
+  const size_t slot = (size_t)dense_slot(p.dense_counts, un.e);
+  const uint16_t* w0 = p.dense0 + slot * mat;
+  const uint16_t* w1 = (MODE == kModeGateUp) ? p.dense1 + slot * mat : w0;
   const int rb0 = r0 / 16;
 
   uint32_t aoff[NS];
@@ -1129,9 +1142,10 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
     const int rb = (int)(task % nblocks);
     const int r0 = rb * 16;
     if (q.expert < 0 && q.counts && __builtin_amdgcn_readfirstlane(q.counts[e]) <= 0) continue;
+    const size_t slot = q.counts ? (size_t)dense_slot(q.counts, e) : (size_t)e;
     for (int m = 0; m < (q.codes1 ? 2 : 1); ++m) {
       const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
-      uint16_t* out = (m ? q.out1 : q.out0) + (size_t)e * (size_t)q.out_expert_stride;
+      uint16_t* out = (m ? q.out1 : q.out0) + slot * (size_t)q.out_expert_stride;
       // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
       const int tc = Dec::kPipelined ? code_chunk(lane) : g;
       const uint32_t roff = (uint32_t)(r0 + (Dec::kPipelined ? code_row(lane) : j)) * (uint32_t)row_bytes;
@@ -1154,37 +1168,34 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
             for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
           }
         }
-
-      } else {
-        // ping-pong code buffers (no register copy between blocks; see task_grouped)
-        RunCodes cA = load_run_wrapping(base, roff, (kblocks - 1) * 32 + tc * 8, row_bytes), cB{};
-        keep_apart(cA);
-        auto step = [&](int i, const RunCodes& rc, RunCodes& nx) {
-          const int kb = block_at(i, kblocks);
-          if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + tc * 8);
-          const RunCodes m = to_mfma_layout(rc);
-          u32x4 w[4];
-          dec.decode16(m.d0, m.d1, w[0], w[1]);
-          dec.decode16(m.d1, m.la, w[2], w[3]);
-          if (q.fragment_order) {
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-              *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
-          } else {
-            uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
-          }
-          __builtin_amdgcn_sched_barrier(0);  // as in task_grouped
-        };
-        int i = 0;
-        for (; i + 1 < kblocks; i += 2) {
-          step(i, cA, cB);
-          step(i + 1, cB, cA);
-        }
-        if (i < kblocks) step(i, cA, cB);
-
+        continue;
       }
+      RunCodes cA = load_run_wrapping(base, roff, (kblocks - 1) * 32 + tc * 8, row_bytes), cB{};
+      keep_apart(cA);
+      auto step = [&](int i, const RunCodes& rc, RunCodes& nx) {
+        const int kb = block_at(i, kblocks);
+        if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + tc * 8);
+        const RunCodes mc = to_mfma_layout(rc);
+        u32x4 w[4];
+        dec.decode16(mc.d0, mc.d1, w[0], w[1]);
+        dec.decode16(mc.d1, mc.la, w[2], w[3]);
+        if (q.fragment_order) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
+        } else {
+          uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
+#pragma unroll
+          for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // as in task_grouped
+      };
+      int i = 0;
+      for (; i + 1 < kblocks; i += 2) {
+        step(i, cA, cB);
+        step(i + 1, cB, cA);
+      }
+      if (i < kblocks) step(i, cA, cB);
     }
   }
 }

@@ -64,8 +64,10 @@ struct ExpertParams {
                                 // positions), the order the down pass reads it in.
   int32_t act_frag;             // with unit_pad: the activations (act) are in that fragment order as well
   int32_t n_pad_max;            // padded positions the fragment-order buffers hold (with unit_pad)
-  const uint16_t* dense0;       // dequantize arm: [E] x rows x cols bf16 weights in fragment order (gate, or the single matrix)
+  const uint16_t* dense0;       // dequantize arm: one rows x cols bf16 matrix in fragment order per woken expert, at
+                                // its slot (dense_slot) (gate, or the single matrix)
   const uint16_t* dense1;       // dequantize arm: the same for the up weights (fused pass only)
+  const int32_t* dense_counts;  // dequantize arm: the per-expert pair counts that define the slots
   int32_t ksplit;               // GEMV arm launched with fewer waves than its configuration's: waves
                                 // sharing one task's inputs (a power of 2 dividing cols/128), or <= 1
 };
@@ -102,7 +104,8 @@ struct DequantParams {
   int32_t num_experts, rows, cols, expert;
   uint16_t* out0;
   uint16_t* out1;
-  int64_t out_expert_stride;    // elements between experts' matrices in out0/out1 (0: expert-less output)
+  int64_t out_expert_stride;    // elements between slots' matrices in out0/out1 (0: expert-less output); with counts
+                                // the woken experts are stored compactly, expert e at slot dense_slot(counts, e)
   int32_t fragment_order;       // 0: row-major [rows][cols]; 1: MFMA fragment order (dense_fragment_offset)
 };
 
