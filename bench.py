@@ -487,7 +487,7 @@ def main():
                     "headline and reported in detail.curve ('' for none)")
     ap.add_argument("--arm", choices=["auto", "gemv", "grouped", "dequant"], default="auto")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
-    ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 = the plan's choice, 1..10 fixed; see qtip_moe_plan_schedule)")
+    ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 = the plan's choice, 1..11 fixed; see qtip_moe_plan_schedule)")
     ap.add_argument("--cpu-experts", type=int, default=-1, help="woken experts the CPU oracle is timed on (-1: the "
                     "whole layer, about 13 s on 16 cores at n=1024; 0: skip)")
     ap.add_argument("--sweep", metavar="PATH", default=None)

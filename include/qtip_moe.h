@@ -118,7 +118,7 @@ typedef struct qtip_moe_desc {
   int32_t inter;        /* I: gate/up outputs and down inputs; multiple of 128 */
   int32_t max_tokens;   /* largest n a forward accepts (sizes the workspace), >= 1 */
   int32_t arm_override; /* QTIP_ARM_AUTO (predicate), _GEMV, _GROUPED or _DEQUANT (pins the arm) */
-  int32_t variant;      /* expert kernel configuration 1..10 for both passes (10 is a down-pass
+  int32_t variant;      /* expert kernel configuration 1..11 for both passes (10 is a down-pass
                            shape: with it the grouped arm's fused pass runs 9), or 0 = chosen per
                            arm, pass and n by the plan (qtip_moe_plan_schedule reports it);
                            unknown: warning, 0 kept */
@@ -160,7 +160,7 @@ typedef struct qtip_moe_weights {
 /* Launch counters of a plan (prefill page, PR #196, "Two things that were built, correct, and
  * switched off": a harness that reports a per-variant timing must show the counter of the
  * variant it claims advancing and the others not; the counters are read by qtip_moe_stats). */
-#define QTIP_VARIANT_SLOTS 11 /* index = kernel configuration 1..10 (0 unused) */
+#define QTIP_VARIANT_SLOTS 12 /* index = kernel configuration 1..11 (0 unused) */
 typedef struct qtip_moe_stats_s {
   uint64_t forward_calls;     /* successful qtip_moe_forward calls */
   uint64_t gemv_launches;     /* expert-matrix kernel launches on the GEMV arm */
@@ -212,7 +212,7 @@ qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m /*host*/, s
  * (the selected variant is printed next to every result; a variant that cannot be reached is a
  * defect) and arch-specialise page, "D18" (one source of truth for the tile height). */
 typedef struct qtip_moe_kernel_shape {
-  int32_t variant;             /* kernel configuration 1..10 actually launched */
+  int32_t variant;             /* kernel configuration 1..11 actually launched */
   int32_t waves_per_workgroup; /* wave64 per (persistent, one-per-CU) workgroup */
   int32_t rows_per_task;       /* output rows each wave decodes per task (16, 32 or 64) */
   int32_t pairs_per_decode;    /* binned pairs of one expert that share one decode of its rows */

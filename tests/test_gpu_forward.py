@@ -164,7 +164,7 @@ def test_forward_rejects_empty_and_oversized_batches_on_device():
     layer.close()
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
 @pytest.mark.parametrize("arm", [q.QTIP_ARM_GEMV, q.QTIP_ARM_GROUPED])
 def test_kernel_variants_full_parity(variant, arm):
     """Both kernel configurations (16 waves / 32-pair decodes, 8 waves / 64-pair decodes) on a

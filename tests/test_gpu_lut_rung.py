@@ -118,7 +118,7 @@ def test_mid_lut_layer_ragged_tiles(arm, n):
     check(got, moe.moe_forward(inp), "f32")
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
 @pytest.mark.parametrize("arm", [q.QTIP_ARM_GEMV, q.QTIP_ARM_GROUPED])
 def test_lut_kernel_variants(variant, arm):
     inp = moe_inputs.make_inputs(MID, seed=8, n_tokens=260)

@@ -363,9 +363,9 @@ def test_stats_start_at_zero_with_per_variant_slots():
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
     st = q.qtip_moe_stats(plan)
     assert st["forward_calls"] == 0 and st["last_arm"] == 0
-    assert st["gemv_variant_launches"] == [0] * 11 and st["grouped_variant_launches"] == [0] * 11
+    assert st["gemv_variant_launches"] == [0] * 12 and st["grouped_variant_launches"] == [0] * 12
     q.qtip_moe_stats_reset(plan)
-    assert ctypes.sizeof(q.qtip_moe_stats_t) == 7 * 8 + 2 * 4 + 2 * 11 * 8
+    assert ctypes.sizeof(q.qtip_moe_stats_t) == 7 * 8 + 2 * 4 + 2 * 12 * 8
     q.qtip_moe_plan_destroy(plan)
 
 

@@ -52,7 +52,7 @@ class qtip_moe_weights(ctypes.Structure):
                 ("lut", ctypes.c_void_p)]
 
 
-QTIP_VARIANT_SLOTS = 11
+QTIP_VARIANT_SLOTS = 12
 
 
 class qtip_moe_stats_t(ctypes.Structure):

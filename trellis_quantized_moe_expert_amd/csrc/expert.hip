@@ -162,6 +162,7 @@ bool variant_info(int variant, int arm, VariantInfo& v) {
     case 8: CfgInfo<Cfg8>::get(arm, v); return true;
     case 9: CfgInfo<Cfg9>::get(arm, v); return true;
     case 10: CfgInfo<Cfg10>::get(arm, v); return true;
+    case 11: CfgInfo<Cfg11>::get(arm, v); return true;
     default: return false;
   }
 }

@@ -945,6 +945,11 @@ using Cfg9 = ExpertCfg<12, 2, 3, 3>;
 // 12 waves of 64-row tasks sharing a decode across three 16-pair blocks (48 pairs): a down-pass
 // shape (see kGroupedFused).
 using Cfg10 = ExpertCfg<12, 4, 3, 3>;
+// 12 waves of 16-row tasks sharing a decode across three 16-pair blocks (48 pairs): the decode
+// sharing of variant 9 with half the code rows in flight per task, so that the code lines a task
+// reads over four consecutive blocks (each 128-byte line holds four blocks of a row) stay in the
+// XCD's L2 between their uses.
+using Cfg11 = ExpertCfg<12, 1, 3, 3>;
 
 // The grouped body specialised for the chunk's exact number of 16-pair row blocks.
 template <int MODE, class CFG, bool FRAG, class DEC>
@@ -1263,6 +1268,7 @@ static hipError_t launch_expert_rung(int mode, int arm, int variant, const Exper
     case 8: return launch_cfg<Cfg8, RUNG>(mode, arm, p, grid, waves, stream);
     case 9: return launch_cfg<Cfg9, RUNG>(mode, arm, p, grid, waves, stream);
     case 10: return launch_cfg<Cfg10, RUNG>(mode, arm, p, grid, waves, stream);
+    case 11: return launch_cfg<Cfg11, RUNG>(mode, arm, p, grid, waves, stream);
     default: return hipErrorInvalidValue;
   }
 }

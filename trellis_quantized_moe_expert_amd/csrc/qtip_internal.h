@@ -17,8 +17,8 @@ constexpr int kCodebookEntries = 1 << kLutRungBits;  // 512 two-dimensional entr
 constexpr int kCodebookCopies = 32;                  // one copy per LDS bank (see DecoderLut)
 // The LUT fills 128 KiB of LDS, so one expert workgroup per CU is resident; the kernel
 // variant fixes its size (8, 12 or 16 wave64; a small GEMV launch may run fewer).
-// Variants 1..10 are fixed kernel configurations (see variant_info); 0 lets the plan choose.
-enum ExpertVariant { kVariantDefault = 0, kVariantCount = 11 };
+// Variants 1..11 are fixed kernel configurations (see variant_info); 0 lets the plan choose.
+enum ExpertVariant { kVariantDefault = 0, kVariantCount = 12 };
 constexpr int kExpertWaves = 16;       // waves of the binning workgroup
 constexpr int kBinCached = 8;          // groups of 64 expert ids a binning wave keeps in registers
 constexpr int kKBlock = 128;           // inputs per K block: 4 lane groups x 32-symbol runs
@@ -81,7 +81,7 @@ struct VariantInfo {
   int pairs_per_decode;  // binned pairs sharing one decode of an expert's rows
   bool input_split;      // GEMV arm: can split a task's inputs over waves (ExpertParams::ksplit)
 };
-// `variant` in 1..10 (the plan resolves 0).  variant_info returns false for other values.
+// `variant` in 1..11 (the plan resolves 0).  variant_info returns false for other values.
 bool variant_info(int variant, int arm, VariantInfo& v);
 // `waves` per workgroup: at most the variant's (VariantInfo::waves); fewer spread a small launch
 // over more CUs.
