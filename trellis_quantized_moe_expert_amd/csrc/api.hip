@@ -78,6 +78,16 @@ namespace {
 //    waves where the tasks are few), and 8 waves of 32-row tasks once those give each of the
 //    2048 wave slots of a 256-CU, 8-wave launch one.  Down pass: 16-wave workgroups of 16-row
 //    tasks up to 6144 32-row tasks (every measured batch of 1 to 8 tokens), 32-row tasks beyond.
+// The LUT rung's decode reads one 4-byte codebook entry per two weights, so its passes are
+// bound by the vector-memory path (activation fragments above all) rather than by LDS gathers;
+// taller tasks, which feed each fragment to more MFMAs, pay there (bench.py --sweep-rung lut
+// over variants, n = 1 to 1024):
+//  * Grouped arm.  Fused pass: 16 waves of 16-row tasks below 1.15 pairs per woken expert, 8
+//    waves of 32-row tasks sharing a decode across up to four 16-pair blocks below 6, 8 waves of
+//    64-row tasks from 6.  Down pass: 12 waves of 64-row tasks (two 16-pair blocks per decode)
+//    below 16, three blocks per decode from 16.
+//  * GEMV arm.  Fused pass as on the bitshift rung; down pass: 16-wave workgroups of 16-row
+//    tasks below 1536 32-row tasks (batches of one and two tokens), of 32-row tasks from there.
 int kernel_arm(int32_t arm) {
   return arm == QTIP_ARM_GROUPED ? kArmGrouped : (arm == QTIP_ARM_DEQUANT ? kArmDense : kArmGemv);
 }
@@ -91,15 +101,23 @@ int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_to
   }
   const int32_t E = plan->d.num_experts, k = plan->d.top_k;
   const int32_t n = n_tokens >= 1 ? n_tokens : 1;
+  const bool lut = plan->d.rung == QTIP_RUNG_LUT;
   if (arm == kArmGemv) {
     const double rows = mode == kModeGateUp ? plan->d.inter : plan->d.hidden;
     const double woken = fill_woken_experts(n, k, E);
     const double tall_tasks = woken * rows / 32.0;
-    if (mode == kModeSingle) return tall_tasks < 6144.0 ? 1 : 4;
+    if (mode == kModeSingle) {
+      if (lut) return tall_tasks < 1536.0 ? 1 : 3;
+      return tall_tasks < 6144.0 ? 1 : 4;
+    }
     if (tall_tasks >= 2048.0) return 4;
     return woken * rows / 16.0 >= 5.0 * 256.0 ? 1 : 2;
   }
   const double ppe = fill_pairs_per_woken_expert(n, k, E);
+  if (lut) {
+    if (mode == kModeGateUp) return ppe < 1.15 ? 1 : (ppe < 6.0 ? 4 : 5);
+    return ppe < 16.0 ? 7 : 10;
+  }
   if (mode == kModeGateUp) return ppe < 4.0 ? 1 : 9;
   return ppe < 3.0 ? 3 : (ppe < 4.0 ? 7 : 10);
 }
