@@ -179,8 +179,9 @@ typedef struct qtip_moe_stats_s {
  * qtip_moe_plan: validate `desc` (host) for `device`, fix the m-tile height and the
  * workspace size, and return a plan (host memory only; launches nothing, so it is safe
  * inside graph capture).  Checks: 1 <= k <= E <= 1024, k <= 32, H and I multiples of
- * 128, max_tokens >= 1, a known arm/out_dtype, tile_m in {0,16,32,64}, and the device
- * arch reported by HIP is gfx950 (else QTIP_ERR_NOT_SUPPORTED).  Free with
+ * 128, max_tokens >= 1, a known arm/out_dtype, tile_m in {0,16,32,64}, max_tokens x k x
+ * max(H, I) and the 16-padded pairs x max(H, I) below 2^30 (activation buffers), and the
+ * device arch reported by HIP is gfx950 (else QTIP_ERR_NOT_SUPPORTED).  Free with
  * qtip_moe_plan_destroy.  Not thread-safe per plan object (counters).
  * Source: arch-specialise page, PR #99, "D18": an unsupported device is refused instead of
  * running compiled-out code, and the m-tile height has one source of truth that the router,
@@ -364,7 +365,7 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
  *   codes [E][rows][cols/4], scales [E][rows] fp16, lut [65536] fp16,
  *   a [n_rows_a][cols] bf16, y [n_rows_a][rows] fp32.
  * `arm` is QTIP_ARM_GEMV or QTIP_ARM_GROUPED.  Constraints: rows % 16 == 0, cols % 128
- * == 0, 1 <= L <= 64, 0 <= e < num_experts, 0 <= s, s + L <= n_rows_a.  A unit that
+ * == 0, n_rows_a x cols < 2^30, 1 <= L <= 64, 0 <= e < num_experts, 0 <= s, s + L <= n_rows_a.  A unit that
  * violates them on the device is skipped (its rows of y are not written), so device-side
  * garbage cannot cause out-of-bounds access.  Rows of y no unit covers are not written.
  * n_units == 0 is INVALID_CONFIG. */

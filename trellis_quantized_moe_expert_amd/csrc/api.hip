@@ -330,16 +330,17 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
   if (d->inter < kKBlock || d->inter % kKBlock) return fail(QTIP_ERR_INVALID_ARG, "inter must be a positive multiple of 128");
   if (d->max_tokens < 1) return fail(QTIP_ERR_INVALID_ARG, "max_tokens must be >= 1");
   if ((int64_t)d->max_tokens * d->top_k > (1 << 24)) return fail(QTIP_ERR_INVALID_ARG, "max_tokens * top_k exceeds 2^24");
-  // activation buffers (x: n x H, h: n k x I) are addressed with 32-bit element offsets
-  if ((int64_t)d->max_tokens * d->top_k * (d->hidden > d->inter ? d->hidden : d->inter) >= ((int64_t)1 << 31))
-    return fail(QTIP_ERR_INVALID_ARG, "max_tokens * top_k * max(hidden, inter) must be below 2^31");
+  // activation buffers (x: n x H, h: n k x I) are read through buffer resources with 32-bit byte
+  // offsets below 2^31 (the offset 2^31 marks a skipped load)
+  if ((int64_t)d->max_tokens * d->top_k * (d->hidden > d->inter ? d->hidden : d->inter) >= ((int64_t)1 << 30))
+    return fail(QTIP_ERR_INVALID_ARG, "max_tokens * top_k * max(hidden, inter) must be below 2^30");
   if ((int64_t)d->hidden * d->inter / 4 >= ((int64_t)1 << 31))
     return fail(QTIP_ERR_INVALID_ARG, "one expert matrix must be below 2^31 bytes");
   {
     const int64_t P = (int64_t)d->max_tokens * d->top_k;
     const int64_t PP = P + 15 * (P < d->num_experts ? P : d->num_experts) + 15;
-    if (PP * (d->hidden > d->inter ? d->hidden : d->inter) >= ((int64_t)1 << 31))
-      return fail(QTIP_ERR_INVALID_ARG, "padded pairs * max(hidden, inter) must be below 2^31");
+    if (PP * (d->hidden > d->inter ? d->hidden : d->inter) >= ((int64_t)1 << 30))
+      return fail(QTIP_ERR_INVALID_ARG, "padded pairs * max(hidden, inter) must be below 2^30");
   }
   if ((int64_t)d->num_experts * d->hidden >= ((int64_t)1 << 31))
     return fail(QTIP_ERR_INVALID_ARG, "num_experts * hidden (the router weight) must be below 2^31 elements");
@@ -645,8 +646,8 @@ qtip_status qtip_expert_matmul(qtip_moe_plan_t plan, int32_t arm, const uint8_t*
       (reinterpret_cast<uintptr_t>(codes) & 7))
     return fail(QTIP_ERR_INVALID_ARG, "lut and a_bf16 must be 16-byte aligned, codes 8-byte aligned");
   if (n_units <= 0) return fail(QTIP_ERR_INVALID_CONFIG, "n_units must be >= 1 (an empty launch is an error)");
-  if ((int64_t)n_rows_a * cols >= ((int64_t)1 << 31) || (int64_t)rows * (cols / 4) >= ((int64_t)1 << 31))
-    return fail(QTIP_ERR_INVALID_ARG, "n_rows_a * cols and rows * cols / 4 must be below 2^31");
+  if ((int64_t)n_rows_a * cols >= ((int64_t)1 << 30) || (int64_t)rows * (cols / 4) >= ((int64_t)1 << 31))
+    return fail(QTIP_ERR_INVALID_ARG, "n_rows_a * cols must be below 2^30 and rows * cols / 4 below 2^31");
   const hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   qtip_status s = ensure_device(plan, st, &dev);

@@ -305,18 +305,37 @@ __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int
   }
 }
 
+// Activation loads go through a buffer resource whose range ends at 2^31 bytes.  The plan keeps
+// every activation buffer below 2^30 elements, so each real fragment lies inside the range; a
+// lane whose row is past its unit gets the element offset kNoActRow (byte offset 2^31), and its
+// load returns zeros without a memory access.  The instruction still counts as one load for the
+// whole wave (no branch, so the compiler counts outstanding memory operations exactly), while
+// the lanes it skips cost no cache access.  Only the MFMA output row of such a lane reads the
+// zeros (each output row depends on its own A row alone), and that row is never stored.
+constexpr uint32_t kNoActRow = 1u << 30;
+constexpr uint32_t kActRangeBytes = 1u << 31;
+
+__device__ inline __amdgpu_buffer_rsrc_t act_rsrc(const uint16_t* act) {
+  // raw buffer (stride 0), range in bytes; the last word is the gfx9 data format for untyped loads
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(act), (short)0, (int)kActRangeBytes, 0x00020000);
+}
+
+// 16 bytes at byte offset voff + soff (soff wave-uniform, the position within a row); a voff at
+// or past kActRangeBytes reads zeros.  voff + soff stays below 2^32: soff is below a row's bytes.
+__device__ inline u32x4 act_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, 0));
+}
+
 // Loads the A fragments of one K block: for each 16-pair row block m < NS, the 16 bytes of
-// each of the 4 MFMA steps (K slots 8g..8g+7 <-> inputs kb*128 + 32g + 8s + 0..7).  Loads
-// are unconditional (rows past the unit read a valid row and are discarded later), so the
-// compiler can count outstanding memory operations exactly.
+// each of the 4 MFMA steps (K slots 8g..8g+7 <-> inputs kb*128 + 32g + 8s + 0..7).
 template <int NS>
 __device__ inline void load_a_block(u32x4 (&a)[NS][4], const uint16_t* __restrict__ act, const uint32_t (&aoff)[NS],
                                     int kb) {
+  const __amdgpu_buffer_rsrc_t rs = act_rsrc(act);
 #pragma unroll
   for (int m = 0; m < NS; ++m) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-      a[m][st] = *reinterpret_cast<const u32x4*>(act + (aoff[m] + (uint32_t)(kb * kKBlock + st * 8)));
+    for (int st = 0; st < 4; ++st) a[m][st] = act_load16(rs, aoff[m] * 2u, (uint32_t)(kb * kKBlock * 2 + st * 16));
   }
 }
 
@@ -326,11 +345,11 @@ __device__ inline void load_a_block(u32x4 (&a)[NS][4], const uint16_t* __restric
 template <int NS>
 __device__ inline void load_a_block_frag(u32x4 (&a)[NS][4], const uint16_t* __restrict__ act, const uint32_t (&fo)[NS],
                                          int kb) {
+  const __amdgpu_buffer_rsrc_t rs = act_rsrc(act);
 #pragma unroll
   for (int m = 0; m < NS; ++m) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-      a[m][st] = *reinterpret_cast<const u32x4*>(act + (fo[m] + (uint32_t)(kb * 2048 + st * 512)));
+    for (int st = 0; st < 4; ++st) a[m][st] = act_load16(rs, fo[m] * 2u, (uint32_t)(kb * 4096 + st * 1024));
   }
 }
 
@@ -341,20 +360,16 @@ __device__ inline void load_a(u32x4 (&a)[NS][4], const uint16_t* __restrict__ ac
 }
 
 // Activation row offsets (elements from p.act) of this lane for NS entries; entry m is the
-// binned position first + m*stride.  Positions past the unit, and rows out of range, read the
-// unit's first row (always valid); their results are never stored.  The plan keeps the
-// activation buffers below 2^31 elements, so 32-bit offsets suffice.
+// binned position first + m*stride.  Positions past the unit, and rows out of range, get
+// kNoActRow: their loads read zeros, and their results are never stored.
 template <int NS>
 __device__ inline void act_rows(const ExpertParams& p, const Unit& un, int first, int stride, int g,
                                 uint32_t (&off)[NS]) {
-  int r_first = act_row(p, un.start);
-  if (r_first < 0) r_first = 0;
 #pragma unroll
   for (int m = 0; m < NS; ++m) {
     const int pi = first + m * stride;
-    int ar = (pi < un.len) ? act_row(p, un.start + pi) : -1;
-    if (ar < 0) ar = r_first;
-    off[m] = (uint32_t)ar * (uint32_t)p.cols + (uint32_t)(g * 32);
+    const int ar = (pi < un.len) ? act_row(p, un.start + pi) : -1;
+    off[m] = ar >= 0 ? (uint32_t)ar * (uint32_t)p.cols + (uint32_t)(g * 32) : kNoActRow;
   }
 }
 
@@ -528,7 +543,8 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
   uint32_t aoff[NS];  // A operand row i = lane%16 of each 16-pair block
   if (FRAG) {
 #pragma unroll
-    for (int m = 0; m < NS; ++m) aoff[m] = (uint32_t)dense_fragment_offset((un.pad >> 4) + m, 0, 0, lane, kblocks);
+    for (int m = 0; m < NS; ++m)
+      aoff[m] = 16 * m + j < un.len ? (uint32_t)dense_fragment_offset((un.pad >> 4) + m, 0, 0, lane, kblocks) : kNoActRow;
   } else {
     act_rows<NS>(p, un, j, 16, g, aoff);
   }
