@@ -41,6 +41,12 @@ DECODE_VALU_PEAK_SYMS = 256 * 64 * 2.4e9 / 2
 # load of 3.532, so a half-wave takes 3.532 cycles: 64 / (2 x 3.532) = 9.06 lookups/clk/CU, x 256
 # CUs x 2.4 GHz = 5.57 T lookups/s.
 LDS_GATHER_PEAK = 256 * 2.4e9 * 64 / (2 * 3.532)
+# LUT rung: one conflict-free 4-byte codebook read per two weights (the codebook is replicated
+# across the banks); the LDS serves 128 bytes per clock per CU, i.e. 32 such reads: 256 CUs x
+# 2.4 GHz x 32 = 19.7 T reads/s (39.3 T weights/s).  It is not what binds that rung: its passes
+# wait on the vector-memory path (texture addresser and data return), whose counters are kept
+# with the LUT-rung kernel profiles.
+LDS_CODEBOOK_PEAK = 256 * 2.4e9 * 32
 SWEEP_N = [8, 16, 32, 64, 128, 256, 512, 683, 1024]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["trellis_quantized_moe_expert_amd/csrc/expert.hip",
@@ -402,6 +408,25 @@ def draw_layers(names):
     return out
 
 
+def decode_roofline(rung, gu_syms, layer_syms, gather_measured):
+    """The decode's own ceiling for decoded weights per second of the gate+up pass and of both
+    expert passes: bitshift rung, one random LDS gather per weight (model and measured ceilings);
+    LUT rung, one conflict-free codebook read per two weights."""
+    if rung == "lut":
+        return {"bound": "lds_codebook", "unit": "codebook reads/s (two weights each)",
+                "gate_up_achieved": gu_syms / 2, "expert_passes_achieved": layer_syms / 2,
+                "peak_model": LDS_CODEBOOK_PEAK, "gate_up_frac_model": gu_syms / 2 / LDS_CODEBOOK_PEAK,
+                "expert_passes_frac_model": layer_syms / 2 / LDS_CODEBOOK_PEAK,
+                "binding": "vector-memory path (texture addresser and data return), not the LDS"}
+    return {"bound": "lds_gather", "unit": "LUT lookups/s",
+            "gate_up_achieved": gu_syms, "expert_passes_achieved": layer_syms,
+            "peak_measured": gather_measured, "gate_up_frac_measured": gu_syms / gather_measured,
+            "expert_passes_frac_measured": layer_syms / gather_measured,
+            "peak_model": LDS_GATHER_PEAK, "gate_up_frac_model": gu_syms / LDS_GATHER_PEAK,
+            "valu_peak": DECODE_VALU_PEAK_SYMS, "gate_up_frac_valu": gu_syms / DECODE_VALU_PEAK_SYMS,
+            "expert_passes_frac_valu": layer_syms / DECODE_VALU_PEAK_SYMS}
+
+
 def measure_workload(name, inp, weights, args, gather_measured, full=False):
     """Times one workload in the plan a caller of that size uses (max_tokens = n, automatic arm
     unless --arm, bf16 output unless --out-dtype) and returns its record."""
@@ -457,13 +482,7 @@ def measure_workload(name, inp, weights, args, gather_measured, full=False):
         "layer_hbm_frac": layer_bytes / layer_gpu_s / 1e9 / HBM_PEAK_GBS,
         "woken_experts": fig["woken"], "max_pairs_per_expert": fig["max_count"], "m_tiles": n_tiles,
         "decodes": fig["decodes"],
-        "decode_roofline": {"bound": "lds_gather", "unit": "LUT lookups/s",
-                            "gate_up_achieved": gu_syms, "expert_passes_achieved": layer_syms,
-                            "peak_measured": gather_measured, "gate_up_frac_measured": gu_syms / gather_measured,
-                            "expert_passes_frac_measured": layer_syms / gather_measured,
-                            "peak_model": LDS_GATHER_PEAK, "gate_up_frac_model": gu_syms / LDS_GATHER_PEAK,
-                            "valu_peak": DECODE_VALU_PEAK_SYMS, "gate_up_frac_valu": gu_syms / DECODE_VALU_PEAK_SYMS,
-                            "expert_passes_frac_valu": layer_syms / DECODE_VALU_PEAK_SYMS},
+        "decode_roofline": decode_roofline(s.rung, gu_syms, layer_syms, gather_measured),
         # MFMA work of the layer (g, u and y: 2 n k H I flops each) against the dense bf16 peak: the
         # contraction is thin, so this stays a few percent at most
         "mfma": {"flops": flops, "layer_tflops": flops / layer_gpu_s / 1e12,

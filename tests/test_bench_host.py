@@ -52,6 +52,22 @@ GEMV_GATE_UP = "void qtip::(anonymous namespace)::expert_kernel<0, 0, qtip::(ano
 COPY = "__amd_rocclr_copyBuffer"
 
 
+def test_decode_roofline_counts_one_read_per_weight_pair_on_the_lut_rung():
+    # 2 T decoded weights/s: the bitshift rung gathers once per weight, the LUT rung reads its
+    # codebook once per pair of weights
+    bs = bench.decode_roofline("bitshift", 2e12, 1e12, 5e12)
+    assert bs["bound"] == "lds_gather" and bs["gate_up_achieved"] == 2e12
+    assert bs["gate_up_frac_measured"] == pytest.approx(0.4)
+    assert bs["gate_up_frac_model"] == pytest.approx(2e12 / bench.LDS_GATHER_PEAK)
+    lut = bench.decode_roofline("lut", 2e12, 1e12, 5e12)
+    assert lut["bound"] == "lds_codebook" and lut["gate_up_achieved"] == 1e12
+    assert lut["expert_passes_achieved"] == 0.5e12
+    # 32 four-byte reads per clock per CU (128 bytes), 256 CUs at 2.4 GHz
+    assert bench.LDS_CODEBOOK_PEAK == pytest.approx(19.6608e12)
+    assert lut["gate_up_frac_model"] == pytest.approx(1e12 / 19.6608e12)
+    assert "peak_measured" not in lut       # the random-gather probe does not apply to this rung
+
+
 def test_traffic_is_scaled_by_what_the_counter_reads_for_a_known_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
