@@ -131,8 +131,9 @@ typedef struct qtip_moe_desc {
                               are below this, and sends fills in [ratio, dispatch_tile_m) past the
                               decode floor to the dequantize arm: 0 = 16; 1..1024 accepted.  A plan
                               that can take the dequantize arm (that window is not empty, or the
-                              override pins it) holds every expert's dense bf16 weights in its
-                              workspace: 3 x E x H x I x 2 bytes, and needs H x I < 2^31. */
+                              override pins it) holds the dense bf16 weights of every expert a
+                              forward can wake in its workspace: 3 x min(E, max_tokens x k) x H x I x
+                              2 bytes, and needs H x I < 2^31. */
   int32_t act_layout;   /* grouped arm's activation layout: QTIP_ACT_AUTO (by the closed-form pairs per
                            woken expert), QTIP_ACT_ROWS (gathered rows) or QTIP_ACT_FRAGMENTS (every
                            expert's bin padded to 16 pairs and stored in MFMA fragment order: h always,
@@ -299,7 +300,7 @@ qtip_status qtip_moe_forward(qtip_moe_plan_t plan, const qtip_moe_weights* w /*h
  *   The scratch is laid out for this call's n_tokens, so a call fits when the layer needs at
  *   most QTIP_NOALLOC_SCRATCH_BYTES for n tokens: the V4 layer (E=256, top-6, H=4096,
  *   I=2048) up to 405 tokens (534 with the GEMV arm pinned), the tiny layer at any n.  A call
- *   that takes the dequantize arm (every expert's dense weights) does not fit at V4 sizes.
+ *   that takes the dequantize arm (the woken experts' dense weights) does not fit at V4 sizes.
  *   Makes no allocation, no free and no synchronisation on any call; the first call on a
  *   device looks up that device's scratch address (and takes the arch witness, as
  *   qtip_moe_forward does), so make it once outside capture.  The scratch needs no

@@ -198,8 +198,8 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.h = o;            o = align256(o + (frag ? PP : P) * (size_t)d.inter * 2);  // rows (P) or fragment order (PP)
   L.y = o;            o = align256(o + P * (size_t)d.hidden * 4);
   L.router_part = o;  o = align256(o + router_part_elems(d, n_tokens) * 4);
-  // dequantize arm: every expert's dense bf16 weights (only when the plan can take that arm)
-  // dequantize arm: the dense weights of at most min(E, n k) woken experts, one slot each
+  // dequantize arm (only when the plan can take it): the dense bf16 weights of at most
+  // min(E, n k) woken experts, one slot each
   const size_t dense_mat = dense ? woken_max * (size_t)d.hidden * (size_t)d.inter * 2 : 0;
   L.dense_gate = o;   o = align256(o + dense_mat);
   L.dense_up = o;     o = align256(o + dense_mat);
