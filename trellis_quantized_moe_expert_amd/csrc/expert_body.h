@@ -645,8 +645,9 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
       else load_a<NS, FRAG>(acur, p.act, aoff, kb);
       const int ob = kn * 32 + tc * 8;
       const uint32_t back = (i + 1 < kblocks || tc != 3) ? 0u : 8u;
-      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
-      if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
+      // one 12-byte load per run (chunk and look-ahead together): half the vector-memory instructions
+      n0 = load_runs<NT, true>(base0, roff, nt_stride, ob, back);
+      if (MODE == kModeGateUp) n1 = load_runs<NT, true>(base1, roff, nt_stride, ob, back);
       const RunSet<NT> m0 = to_mfma_layout(c0);
       const RunSet<NT> m1 = (MODE == kModeGateUp) ? to_mfma_layout(c1) : m0;
 #pragma unroll
@@ -805,8 +806,9 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
       else load_a_block<NQ>(x, p.act, xoff, kb);
       const int ob = kn * 32 + tc * 8;
       const uint32_t back = (i + 1 < len || tc != 3 || kn + 1 < kblocks) ? 0u : 8u;
-      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
-      if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
+      // one 12-byte load per run (chunk and look-ahead together): half the vector-memory instructions
+      n0 = load_runs<NT, true>(base0, roff, nt_stride, ob, back);
+      if (MODE == kModeGateUp) n1 = load_runs<NT, true>(base1, roff, nt_stride, ob, back);
       const RunSet<NT> m0 = to_mfma_layout(c0);
       const RunSet<NT> m1 = (MODE == kModeGateUp) ? to_mfma_layout(c1) : m0;
 #pragma unroll
