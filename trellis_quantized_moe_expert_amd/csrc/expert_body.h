@@ -201,6 +201,37 @@ __device__ inline RunCodes to_mfma_layout(const RunCodes& t) {
                   (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)t.la)};
 }
 
+// A run's 8 bytes without the look-ahead (the grouped arm's descending loop takes the look-ahead
+// from the neighbouring run instead), transposed like RunCodes.
+struct RunChunk {
+  uint32_t d0, d1;
+};
+template <int NT>
+struct ChunkSet {
+  RunChunk c[NT];
+};
+template <int NT>
+__device__ inline ChunkSet<NT> load_chunks(const uint8_t* __restrict__ base, uint32_t row_off0, uint32_t nt_stride,
+                                           int ob) {
+  ChunkSet<NT> cs;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint2 v = *reinterpret_cast<const uint2*>(base + (row_off0 + nt * nt_stride + (uint32_t)ob));
+    cs.c[nt] = RunChunk{v.x, v.y};
+  }
+  return cs;
+}
+// Lane j+16g gets chunk g of row j: d0, d1 pulled from the transposed lanes, and the look-ahead
+// from lane j+16(g+1), the next chunk's d0; lane group 3 reads lane group 0, whose `prev` (the
+// first dword of the row's next block, already in MFMA layout) it gets instead.
+__device__ inline RunCodes chunk_to_mfma_layout(const RunChunk& t, uint32_t prev, int cv_addr, int la_addr, int g) {
+  RunCodes r;
+  r.d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(cv_addr, (int)t.d0);
+  r.d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(cv_addr, (int)t.d1);
+  r.la = (uint32_t)__builtin_amdgcn_ds_bpermute(la_addr, (int)(g == 0 ? prev : r.d0));
+  return r;
+}
+
 // Codes of one 32-symbol run: the run's 8 bytes and the 4 after them (its look-ahead).  `base`
 // is the (wave-uniform) start of the expert's matrix, `row_off` the lane's row offset in bytes;
 // 32-bit offsets keep the addresses in one VGPR each.  `back` (0 or 4) moves the load 4 bytes
@@ -396,6 +427,14 @@ template <int NT>
 __device__ inline void keep_apart(RunSet<NT>& r) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) keep_apart(r.c[nt]);
+}
+template <int NT>
+__device__ inline void keep_apart(ChunkSet<NT>& r) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    keep_apart(r.c[nt].d0);
+    keep_apart(r.c[nt].d1);
+  }
 }
 template <int NS>
 __device__ inline void keep_apart(u32x4 (&a)[NS][4]) {
@@ -617,48 +656,68 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
       }
     }
   } else {
-    // Per block: the block's activations are requested first, then the next block's codes
-    // (the block after the last wraps to block 0 and is not used), so waiting for the
-    // activations never waits for those codes (memory counters retire in order) and the
-    // codes have the whole block's decode to arrive.
-    // With APRE the activations are double-buffered as well: block kb+1's are requested during
-    // block kb, so every wait in the loop is for loads issued a whole block earlier.
-    // The loop is unrolled by two over ping-pong buffers (A, B): the buffer being decoded and the
-    // one being loaded are live together, and with one buffer per role in every step no register
-    // copy (which would wait for the load it copies) is needed between blocks.
+    // Blocks in descending order, kblocks-1 down to 0, over ping-pong buffers (A, B) unrolled by
+    // two: per block the activations are requested first, then the next block's codes (8 bytes
+    // per lane, one 32-byte sector per row; the load after block 0 repeats block 0 and is not
+    // used), so every wait is for loads issued a whole block earlier and no register copy
+    // (which would wait for the load it copies) is needed between blocks.
+    // A run's look-ahead is the first dword of the next run of its row: for chunks 0-2 the
+    // next chunk's first dword in the same block, for chunk 3 the first dword of block kb+1,
+    // which descending order has just decoded (its MFMA-layout d0 is carried from the previous
+    // block); the first block's (kblocks-1) wraps to the row's first dword, loaded once.
+    const int cv_addr = (((lane & 15) << 2) | (lane >> 4)) << 2;  // transposed -> MFMA layout
+    const int la_addr = ((lane + 16) & 63) << 2;                   // lane j+16g reads lane j+16(g+1)
     u32x4 aA[NS][4], aB[NS][4];
     if (APRE) load_a<NS, FRAG>(aA, p.act, aoff, kblocks - 1);
     const int ob_last = (kblocks - 1) * 32 + tc * 8;
-    RunSet<NT> A0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-    RunSet<NT> A1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : A0;
-    RunSet<NT> B0, B1;
+    ChunkSet<NT> A0 = load_chunks<NT>(base0, roff, nt_stride, ob_last);
+    ChunkSet<NT> A1 = (MODE == kModeGateUp) ? load_chunks<NT>(base1, roff, nt_stride, ob_last) : A0;
+    uint32_t w0[NT], w1[NT];  // each row's first dword (every lane of its quad loads it)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      w0[nt] = *reinterpret_cast<const uint32_t*>(base0 + (roff + nt * nt_stride));
+      w1[nt] = (MODE == kModeGateUp) ? *reinterpret_cast<const uint32_t*>(base1 + (roff + nt * nt_stride)) : w0[nt];
+    }
+    ChunkSet<NT> B0, B1;
     keep_apart(A0);
     if (MODE == kModeGateUp) keep_apart(A1);
     if (APRE) keep_apart<NS>(aA);
-    // one block: decode c0/c1 (block_at(i)) against its activations `acur`, while block_at(i+1)'s
-    // codes go to n0/n1 and (APRE) its activations to `anext`
-    auto step = [&](int i, const RunSet<NT>& c0, const RunSet<NT>& c1, u32x4 (&acur)[NS][4], RunSet<NT>& n0,
-                    RunSet<NT>& n1, u32x4 (&anext)[NS][4]) {
-      const int kb = block_at(i, kblocks);
-      const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
+    uint32_t pA0[NT], pA1[NT], pB0[NT], pB1[NT];  // MFMA-layout d0 of the block decoded last
+    // one block: decode c0/c1 (block kb = kblocks-1-s) against `acur`, with p0/p1 the previous
+    // block's MFMA-layout d0 (FIRST: the row's first dword, still in transposed layout, in w0/w1);
+    // block kb-1's codes go to n0/n1 and (APRE) its activations to `anext`; this block's d0 to q0/q1
+    auto step = [&](auto first, int s, const ChunkSet<NT>& c0, const ChunkSet<NT>& c1, u32x4 (&acur)[NS][4],
+                    const uint32_t (&p0)[NT], const uint32_t (&p1)[NT], ChunkSet<NT>& n0, ChunkSet<NT>& n1,
+                    u32x4 (&anext)[NS][4], uint32_t (&q0)[NT], uint32_t (&q1)[NT]) {
+      constexpr bool FIRST = decltype(first)::value;
+      const int kb = kblocks - 1 - s;
+      const int kn = kb > 0 ? kb - 1 : 0;
       if (APRE) load_a<NS, FRAG>(anext, p.act, aoff, kn);
       else load_a<NS, FRAG>(acur, p.act, aoff, kb);
       const int ob = kn * 32 + tc * 8;
-      const uint32_t back = (i + 1 < kblocks || tc != 3) ? 0u : 8u;
-      // one 12-byte load per run (chunk and look-ahead together): half the vector-memory instructions
-      n0 = load_runs<NT, true>(base0, roff, nt_stride, ob, back);
-      if (MODE == kModeGateUp) n1 = load_runs<NT, true>(base1, roff, nt_stride, ob, back);
-      const RunSet<NT> m0 = to_mfma_layout(c0);
-      const RunSet<NT> m1 = (MODE == kModeGateUp) ? to_mfma_layout(c1) : m0;
+      n0 = load_chunks<NT>(base0, roff, nt_stride, ob);
+      if (MODE == kModeGateUp) n1 = load_chunks<NT>(base1, roff, nt_stride, ob);
+      RunCodes m0[NT], m1[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t prev0 = FIRST ? (uint32_t)__builtin_amdgcn_ds_bpermute(cv_addr, (int)w0[nt]) : p0[nt];
+        m0[nt] = chunk_to_mfma_layout(c0.c[nt], prev0, cv_addr, la_addr, g);
+        q0[nt] = m0[nt].d0;
+        if (MODE == kModeGateUp) {
+          const uint32_t prev1 = FIRST ? (uint32_t)__builtin_amdgcn_ds_bpermute(cv_addr, (int)w1[nt]) : p1[nt];
+          m1[nt] = chunk_to_mfma_layout(c1.c[nt], prev1, cv_addr, la_addr, g);
+          q1[nt] = m1[nt].d0;
+        }
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           u32x4 b0[2], b1[2];
-          const RunCodes& x0 = m0.c[nt];
+          const RunCodes& x0 = m0[nt];
           lut.decode16(h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
           if (MODE == kModeGateUp) {
-            const RunCodes& x1 = m1.c[nt];
+            const RunCodes& x1 = m1[nt];
             lut.decode16(h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
           }
 #pragma unroll
@@ -678,12 +737,15 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
       // keep the next block's decode (which reads the codes just requested) after this block's work
       __builtin_amdgcn_sched_barrier(0);
     };
-    int i = 0;
-    for (; i + 1 < kblocks; i += 2) {
-      step(i, A0, A1, aA, B0, B1, aB);
-      step(i + 1, B0, B1, aB, A0, A1, aA);
+    using First = std::integral_constant<bool, true>;
+    using Later = std::integral_constant<bool, false>;
+    step(First{}, 0, A0, A1, aA, pA0, pA1, B0, B1, aB, pB0, pB1);
+    int s = 1;
+    for (; s + 1 < kblocks; s += 2) {
+      step(Later{}, s, B0, B1, aB, pB0, pB1, A0, A1, aA, pA0, pA1);
+      step(Later{}, s + 1, A0, A1, aA, pA0, pA1, B0, B1, aB, pB0, pB1);
     }
-    if (i < kblocks) step(i, A0, A1, aA, B0, B1, aB);
+    if (s < kblocks) step(Later{}, s, B0, B1, aB, pB0, pB1, A0, A1, aA, pA0, pA1);
   }
 
   grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1);
