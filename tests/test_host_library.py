@@ -274,12 +274,11 @@ def test_default_kernel_shapes_follow_the_measured_rules():
 def test_lut_rung_default_kernel_shapes_follow_its_own_sweep():
     # The LUT rung on the same V4 layer (GEMV up to 4 tokens, grouped from 5).  GEMV fused pass as on
     # the bitshift rung; GEMV down pass: 32-row tasks from 1536 of them (n >= 3).  Grouped fused
-    # pass: 4 (8 waves, 32-row tasks, up to four 16-pair blocks per decode) from 1.15 pairs per
-    # woken expert, 5 (8 waves, 64-row tasks) from 6; grouped down pass: 7 (12 waves, 64-row
-    # tasks) below 16, 10 from there.
+    # pass: 6 (12 waves, 32-row tasks) from 1.15 pairs per woken expert, 5 (8 waves, 64-row
+    # tasks) from 8; grouped down pass: 7 (12 waves, 64-row tasks) throughout.
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, rung=q.QTIP_RUNG_LUT), "gfx950")
-    want = {1: (2, 1), 2: (1, 1), 4: (1, 3), 8: (1, 7), 16: (4, 7), 32: (4, 7), 128: (4, 7), 256: (5, 7),
-            512: (5, 7), 1024: (5, 10)}
+    want = {1: (2, 1), 2: (1, 1), 4: (1, 3), 8: (1, 7), 16: (6, 7), 32: (6, 7), 128: (6, 7), 256: (6, 7),
+            512: (5, 7), 1024: (5, 7)}
     for n, (gu, dn) in want.items():
         s = q.qtip_moe_plan_schedule(plan, n)
         assert (s["gate_up"]["variant"], s["down"]["variant"]) == (gu, dn), n

@@ -82,10 +82,10 @@ namespace {
 // bound by the vector-memory path (activation fragments above all) rather than by LDS gathers;
 // taller tasks, which feed each fragment to more MFMAs, pay there (bench.py --sweep-rung lut
 // over variants, n = 1 to 1024):
-//  * Grouped arm.  Fused pass: 16 waves of 16-row tasks below 1.15 pairs per woken expert, 8
-//    waves of 32-row tasks sharing a decode across up to four 16-pair blocks below 6, 8 waves of
-//    64-row tasks from 6.  Down pass: 12 waves of 64-row tasks (two 16-pair blocks per decode)
-//    below 16, three blocks per decode from 16.
+//  * Grouped arm.  Fused pass: 16 waves of 16-row tasks below 1.15 pairs per woken expert, 12
+//    waves of 32-row tasks below 8, 8 waves of 64-row tasks from 8.  Down pass: 12 waves of
+//    64-row tasks (two 16-pair blocks per decode) throughout (level with three blocks per
+//    decode at n = 1024, ahead below).
 //  * GEMV arm.  Fused pass as on the bitshift rung; down pass: 16-wave workgroups of 16-row
 //    tasks below 1536 32-row tasks (batches of one and two tokens), of 32-row tasks from there.
 int kernel_arm(int32_t arm) {
@@ -115,8 +115,8 @@ int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_to
   }
   const double ppe = fill_pairs_per_woken_expert(n, k, E);
   if (lut) {
-    if (mode == kModeGateUp) return ppe < 1.15 ? 1 : (ppe < 6.0 ? 4 : 5);
-    return ppe < 16.0 ? 7 : 10;
+    if (mode == kModeGateUp) return ppe < 1.15 ? 1 : (ppe < 8.0 ? 6 : 5);
+    return 7;
   }
   if (mode == kModeGateUp) return ppe < 4.0 ? 1 : 9;
   return ppe < 3.0 ? 3 : (ppe < 4.0 ? 7 : 10);
