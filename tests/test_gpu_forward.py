@@ -139,12 +139,12 @@ def test_v4_small_batches_full_parity():
     layer.close()
 
 
-def test_v4_decode_floor_switches_arms_at_seven_tokens():
-    """The plan's decode floor (6 by default on the bitshift rung): 6 tokens take the GEMV arm, 7
+def test_v4_decode_floor_switches_arms_at_eight_tokens():
+    """The plan's decode floor (7 by default on the bitshift rung): 7 tokens take the GEMV arm, 8
     the grouped arm; both match the oracle token by token."""
-    inps = moe_inputs.make_inputs_multi(moe_inputs.WORKLOADS["v4_decode_n32"], [6, 7], seed=22)
-    layer = Layer(inps[6], out_dtype="f32", max_tokens=7)
-    for n, arm in ((6, q.QTIP_ARM_GEMV), (7, q.QTIP_ARM_GROUPED)):
+    inps = moe_inputs.make_inputs_multi(moe_inputs.WORKLOADS["v4_decode_n32"], [7, 8], seed=22)
+    layer = Layer(inps[7], out_dtype="f32", max_tokens=8)
+    for n, arm in ((7, q.QTIP_ARM_GEMV), (8, q.QTIP_ARM_GROUPED)):
         say(f"forward V4 floor n={n}")
         got = layer.forward(inps[n])
         assert q.qtip_moe_stats(layer.plan)["last_arm"] == arm
