@@ -697,6 +697,10 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
       const int ob = kn * 32 + tc * 8;
       n0 = load_chunks<NT>(base0, roff, nt_stride, ob);
       if (MODE == kModeGateUp) n1 = load_chunks<NT>(base1, roff, nt_stride, ob);
+      // single-matrix pass: the next block's loads go out before this block's first wait (left to
+      // itself the scheduler sinks them below the waits for this block's data, leaving them a
+      // fraction of a block); the fused pass's registers do not allow it (pinned there, it spills)
+      if (MODE == kModeSingle) __builtin_amdgcn_sched_barrier(0);
       RunCodes m0[NT], m1[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
