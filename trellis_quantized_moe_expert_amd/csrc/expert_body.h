@@ -692,15 +692,23 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
       constexpr bool FIRST = decltype(first)::value;
       const int kb = kblocks - 1 - s;
       const int kn = kb > 0 ? kb - 1 : 0;
-      if (APRE) load_a<NS, FRAG>(anext, p.act, aoff, kn);
-      else load_a<NS, FRAG>(acur, p.act, aoff, kb);
       const int ob = kn * 32 + tc * 8;
-      n0 = load_chunks<NT>(base0, roff, nt_stride, ob);
-      if (MODE == kModeGateUp) n1 = load_chunks<NT>(base1, roff, nt_stride, ob);
-      // single-matrix pass: the next block's loads go out before this block's first wait (left to
-      // itself the scheduler sinks them below the waits for this block's data, leaving them a
-      // fraction of a block); the fused pass's registers do not allow it (pinned there, it spills)
-      if (MODE == kModeSingle) __builtin_amdgcn_sched_barrier(0);
+      if (MODE == kModeGateUp) {
+        // fused pass: the next block's codes go out first, pinned before this block's first wait
+        // (left to itself the scheduler sinks them below the waits for this block's data); its
+        // activations may float, since pinning them too spills the fused kernels
+        n0 = load_chunks<NT>(base0, roff, nt_stride, ob);
+        n1 = load_chunks<NT>(base1, roff, nt_stride, ob);
+        __builtin_amdgcn_sched_barrier(0);
+        if (APRE) load_a<NS, FRAG>(anext, p.act, aoff, kn);
+        else load_a<NS, FRAG>(acur, p.act, aoff, kb);
+      } else {
+        // single-matrix pass: activations, then codes, all pinned before this block's first wait
+        if (APRE) load_a<NS, FRAG>(anext, p.act, aoff, kn);
+        else load_a<NS, FRAG>(acur, p.act, aoff, kb);
+        n0 = load_chunks<NT>(base0, roff, nt_stride, ob);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       RunCodes m0[NT], m1[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
