@@ -883,6 +883,8 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
       // one 12-byte load per run (chunk and look-ahead together): half the vector-memory instructions
       n0 = load_runs<NT, true>(base0, roff, nt_stride, ob, back);
       if (MODE == kModeGateUp) n1 = load_runs<NT, true>(base1, roff, nt_stride, ob, back);
+      // the next block's loads stay ahead of this block's first wait (see task_grouped)
+      __builtin_amdgcn_sched_barrier(0);
       const RunSet<NT> m0 = to_mfma_layout(c0);
       const RunSet<NT> m1 = (MODE == kModeGateUp) ? to_mfma_layout(c1) : m0;
 #pragma unroll
