@@ -44,7 +44,7 @@ def int_codebook():
 
 
 @pytest.mark.parametrize("arm", [q.QTIP_ARM_GEMV, q.QTIP_ARM_GROUPED])
-@pytest.mark.parametrize("rows,cols", [(64, 128), (32, 512), (2048, 4096), (4096, 2048)])
+@pytest.mark.parametrize("rows,cols", [(64, 128), (32, 384), (32, 512), (48, 640), (2048, 4096), (4096, 2048)])
 def test_matmul_decodes_an_integer_codebook_exactly(arm, rows, cols):
     """y = a W^T with one-hot rows of a picks columns of W; with integer weights, scale 1 and
     exact fp32 sums the GPU must return the decoded weights bit for bit (the wrap region of each
@@ -105,6 +105,23 @@ def test_tiny_lut_layer_full_parity(seed, arm, out_dtype):
     assert st["last_arm"] == q.qtip_moe_select_arm(layer.plan, 16)
     layer.close()
     check(got, moe.moe_forward(inp, out_dtype=out_dtype), out_dtype)
+
+
+# an odd number of 128-input blocks in both passes (3 in gate+up, 5 in down): the grouped arm walks
+# the blocks of a row in descending order over two alternating buffers, so odd counts end on the
+# other buffer
+ODD = moe_inputs.MoEShape(num_experts=12, top_k=3, hidden=384, inter=640, n_tokens=60, rung="lut")
+
+
+@pytest.mark.parametrize("arm", [q.QTIP_ARM_GEMV, q.QTIP_ARM_GROUPED])
+@pytest.mark.parametrize("n", [1, 7, 60, 90])
+def test_lut_layer_with_odd_block_counts(arm, n):
+    inp = moe_inputs.make_inputs(ODD, seed=5, n_tokens=n)
+    say(f"LUT-rung forward odd blocks n={n} arm={arm}")
+    layer = Layer(inp, arm=arm, out_dtype="f32", max_tokens=90)
+    got = layer.forward(inp)
+    layer.close()
+    check(got, moe.moe_forward(inp), "f32")
 
 
 @pytest.mark.parametrize("arm", [q.QTIP_ARM_GEMV, q.QTIP_ARM_GROUPED])
