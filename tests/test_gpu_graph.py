@@ -27,7 +27,9 @@ def bits(t):
 @pytest.mark.parametrize("name,shape,n,arm", [("mid", MID, 100, q.QTIP_ARM_GROUPED), ("mid", MID, 6, q.QTIP_ARM_GEMV),
                                               ("mid", MID, 40, q.QTIP_ARM_DEQUANT),
                                               ("v4", moe_inputs.WORKLOADS["v4_decode_n32"], 32, q.QTIP_ARM_AUTO),
-                                              ("v4", moe_inputs.WORKLOADS["v4_full_n1024"], 1024, q.QTIP_ARM_AUTO)])
+                                              ("v4", moe_inputs.WORKLOADS["v4_full_n1024"], 1024, q.QTIP_ARM_AUTO),
+                                              ("lut_v4", moe_inputs.WORKLOADS["lut_v4_decode_n32"], 32, q.QTIP_ARM_AUTO),
+                                              ("lut_v4", moe_inputs.WORKLOADS["lut_v4_decode_n32"], 3, q.QTIP_ARM_AUTO)])
 def test_captured_forward_replays_match_eager(name, shape, n, arm):
     import torch
     inp = moe_inputs.make_inputs(shape, seed=12, n_tokens=n)
