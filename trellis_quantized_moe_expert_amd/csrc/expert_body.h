@@ -12,12 +12,15 @@
 //    the expert-binned m-tiles; the per-pair GEMV is the arm for low fill.
 //
 // gfx950 design (what differs from the pages' CUDA kernels):
-//  - The 65536-entry LUT, narrowed to bf16, lives in LDS (128 KiB of the 160 KiB); one
-//    workgroup of 8, 12 or 16 waves per CU, persistent over wave-sized tasks.  Random 2-byte LUT
-//    gathers are the decode's bottleneck, so decoded weights go straight into MFMA B-operand
-//    registers instead of through an LDS weight tile, and activations are read from global
-//    memory (L2-resident) into A-operand registers.  (Small GEMV launches also keep partial
-//    sums in the rest of LDS; see gemv_split_tasks.)
+//  - The decoder's table lives in LDS; one workgroup of 8, 12 or 16 waves per CU, persistent over
+//    wave-sized tasks.  Bitshift rung: the 65536-entry LUT narrowed to bf16 (128 KiB of the
+//    160 KiB); its random 2-byte gathers are the decode's bottleneck, so decoded weights go
+//    straight into MFMA B-operand registers instead of through an LDS weight tile, and
+//    activations are read from global memory (L2-resident) into A-operand registers.  LUT rung:
+//    the 512 x 2 codebook as 32 bank-replicated copies (64 KiB), one conflict-free read per two
+//    weights; that rung waits on its vector-memory loads instead, so its loops load codes
+//    transposed and pipeline them (DecoderLut::kPipelined).  (Small GEMV launches also keep
+//    partial sums in the rest of LDS; see gemv_split_tasks.)
 //  - A wave task is one decode unit (the binned pairs of one expert that one decode serves:
 //    up to 16, 32, 48 or 64 on the grouped arm, 1 to 4 on the GEMV arm) x 16 NT output rows x all
 //    inputs.  Lane (j = lane%16, g = lane/16) decodes row j of each 16-row block; within each
@@ -234,8 +237,8 @@ __device__ inline RunCodes chunk_to_mfma_layout(const RunChunk& t, uint32_t prev
 
 // Codes of one 32-symbol run: the run's 8 bytes and the 4 after them (its look-ahead).  `base`
 // is the (wave-uniform) start of the expert's matrix, `row_off` the lane's row offset in bytes;
-// 32-bit offsets keep the addresses in one VGPR each.  `back` (0 or 4) moves the load 4 bytes
-// earlier, for a load whose data is never used and which must stay inside the row.  With X3 one
+// 32-bit offsets keep the addresses in one VGPR each.  `back` (0 or 8) moves the load that many
+// bytes earlier, for a load whose data is never used and which must stay inside the row.  With X3 one
 // 12-byte load fetches all three dwords (half the vector-memory accesses of an 8-byte plus a
 // 4-byte load, at the cost of an aligned register triple: used where registers allow).
 template <bool X3>
@@ -471,11 +474,11 @@ __device__ inline RunSet<NT> load_runs_wrapping(const uint8_t* __restrict__ base
   return rs;
 }
 
-// Block order of a task: a row's last 128-input block first (the only one whose look-ahead
-// wraps, loaded before the loop), then blocks 0, 1, ..., kblocks-2, whose runs each come from
-// one 12-byte load that stays inside the row.  Iteration i works on block_at(i) and prefetches
-// block_at(i + 1) = i; the last iteration's prefetch is not used (block 0, moved 4 bytes back
-// for lane group 3 so that it stays inside a one-block row).
+// Block order of a task (the bitshift rung's loops and the GEMV arm): a row's last 128-input
+// block first (the only one whose look-ahead wraps, loaded before the loop), then blocks 0, 1,
+// ..., kblocks-2, whose runs (8 + 4 or 12 bytes) stay inside the row.  Iteration i works on
+// block_at(i) and prefetches block_at(i + 1) = i; the last iteration's prefetch is not used
+// (block 0, moved 8 bytes back for lane group 3 so that it stays inside a one-block row).
 __device__ inline int block_at(int i, int kblocks) { return i == 0 ? kblocks - 1 : i - 1; }
 
 // Grouped and dequantize arms: scale and store one task's 16-pair x 16-row MFMA tiles.
