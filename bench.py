@@ -323,8 +323,9 @@ def cpu_baseline(inp, n_experts=-1):
     whole = n_experts < 0 or n_experts >= len(woken)
     sample = woken if whole else woken[:max(1, n_experts)]
     workers = pool.default_workers()
+    split = {}
     t0 = time.perf_counter()
-    pool.layer_outputs({"layer": inp}, workers, experts=None if whole else sample)
+    pool.layer_outputs({"layer": inp}, workers, experts=None if whole else sample, timing=split)
     dt = time.perf_counter() - t0
     full_s = dt * len(woken) / len(sample)
     what = (f"the whole {s.n_tokens}-token layer (routing and binning, all {len(woken)} woken experts each "
@@ -336,7 +337,11 @@ def cpu_baseline(inp, n_experts=-1):
             "sample": f"{what}; {dt:.1f} s wall on {workers} worker processes with one BLAS thread each",
             "host": {"os_cpu_count": os.cpu_count(), "workers": workers, "blas_threads_per_worker": 1,
                      "cpu_model": cpu_model()},
-            "seconds_measured": dt, "seconds_layer": full_s}
+            "seconds_measured": dt, "seconds_layer": full_s,
+            # worker seconds (summed over the pool) spent decoding the experts' weights and in the
+            # matmuls of their pairs; the rest of the wall time is routing, binning, the combine and
+            # the pool itself
+            "worker_seconds": {"decode": split.get("decode_s"), "matmul": split.get("pairs_s")}}
 
 
 def calibrate_copy():

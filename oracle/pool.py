@@ -33,6 +33,7 @@ def _expert_task(e: int):
     first = next(iter(layers.values()))
     weights = None
     out = {}
+    t_decode = t_pairs = 0.0
     for name, inp in layers.items():
         b = bins[name]
         start, cnt = int(b["offsets"][e]), int(b["counts"][e])
@@ -40,10 +41,14 @@ def _expert_task(e: int):
             continue
         pids = b["sorted_pair"][start:start + cnt]
         if weights is None:
+            t0 = time.perf_counter()
             weights = moe.decode_expert(first, e)
+            t_decode += time.perf_counter() - t0
+        t0 = time.perf_counter()
         ye, _ = moe.expert_pairs(inp, e, pids, weights=weights)
+        t_pairs += time.perf_counter() - t0
         out[name] = (np.asarray(pids), ye)
-    return e, out
+    return e, out, (t_decode, t_pairs)
 
 
 def same_weights(a, b) -> bool:
@@ -51,13 +56,15 @@ def same_weights(a, b) -> bool:
                ("lut", "codes_gate", "codes_up", "codes_down", "scale_gate", "scale_up", "scale_down"))
 
 
-def layer_outputs(layers: dict, workers: int, experts=None, tile_m: int = 16, log=None) -> dict:
+def layer_outputs(layers: dict, workers: int, experts=None, tile_m: int = 16, log=None, timing=None) -> dict:
     """Declared-mode outputs of several layers that share expert weights.
 
     layers: {name: MoEInputs}; every entry must hold the same weights.  experts: expert ids to
     evaluate (default: every expert some layer wakes); with a subset, only the pairs of those
     experts are computed and no combine is done.  Returns {name: {"out_f64", "topk_idx",
-    "topk_w", "bins", "y"}} ("out_f64" only when every woken expert was evaluated)."""
+    "topk_w", "bins", "y"}} ("out_f64" only when every woken expert was evaluated).  If `timing`
+    is a dict it receives the worker seconds spent decoding experts ("decode_s") and evaluating
+    their pairs ("pairs_s", the matmuls), summed over workers."""
     global _JOB
     names = list(layers)
     first = layers[names[0]]
@@ -79,13 +86,19 @@ def layer_outputs(layers: dict, workers: int, experts=None, tile_m: int = 16, lo
     ctx = mp.get_context("fork")
     workers = max(1, min(workers, len(todo)))
     with ctx.Pool(workers, initializer=_init_worker) as pool:
-        for i, (e, res) in enumerate(pool.imap_unordered(_expert_task, todo, chunksize=1)):
+        t_decode = t_pairs = 0.0
+        for i, (e, res, (td, tp)) in enumerate(pool.imap_unordered(_expert_task, todo, chunksize=1)):
+            t_decode += td
+            t_pairs += tp
             for name, (pids, ye) in res.items():
                 for q, p in enumerate(pids):
                     y[name][int(p)] = ye[q]
             if log and (i + 1) % 32 == 0:
                 log(f"oracle pool: {i + 1}/{len(todo)} experts in {time.perf_counter() - t0:.1f} s")
     _JOB = None
+    if timing is not None:
+        timing["decode_s"] = t_decode
+        timing["pairs_s"] = t_pairs
     out = {}
     for name in names:
         idx, w = routed[name]

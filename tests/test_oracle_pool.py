@@ -35,3 +35,14 @@ def test_pool_expert_subset_returns_only_those_pairs():
     assert set(res["x"]["y"]) == want and "out_f64" not in res["x"]
     for p in want:
         assert np.allclose(res["x"]["y"][p], ref["y"][p], rtol=1e-12, atol=1e-15)
+
+
+def test_timing_split_is_reported_when_asked():
+    inp = moe_inputs.make_workload("tiny", seed=0)
+    timing = {}
+    res = pool.layer_outputs({"t": inp}, 2, timing=timing)
+    assert set(timing) == {"decode_s", "pairs_s"}
+    assert timing["decode_s"] > 0.0 and timing["pairs_s"] > 0.0
+    # the same outputs with or without the timing dict
+    again = pool.layer_outputs({"t": inp}, 2)
+    assert np.array_equal(res["t"]["out_f64"], again["t"]["out_f64"])
