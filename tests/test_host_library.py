@@ -376,10 +376,10 @@ def test_select_grouped_ignores_the_arm_pin():
 def test_stats_start_at_zero_with_per_variant_slots():
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
     st = q.qtip_moe_stats(plan)
-    assert st["forward_calls"] == 0 and st["last_arm"] == 0
+    assert st["forward_calls"] == 0 and st["last_arm"] == 0 and st["routed_in_gate_up"] == 0
     assert st["gemv_variant_launches"] == [0] * 12 and st["grouped_variant_launches"] == [0] * 12
     q.qtip_moe_stats_reset(plan)
-    assert ctypes.sizeof(q.qtip_moe_stats_t) == 7 * 8 + 2 * 4 + 2 * 12 * 8
+    assert ctypes.sizeof(q.qtip_moe_stats_t) == 7 * 8 + 2 * 4 + 2 * 12 * 8 + 8
     q.qtip_moe_plan_destroy(plan)
 
 
@@ -459,3 +459,27 @@ def test_dequantize_workspace_holds_only_the_woken_experts():
         assert woken * per_expert <= extra < woken * per_expert + 4096, (max_tokens, extra)
         q.qtip_moe_plan_destroy(plan)
         q.qtip_moe_plan_destroy(base)
+
+
+def test_small_gemv_batches_are_routed_inside_the_gate_up_launch():
+    # V4 (k = 6): the GEMV arm serves n <= 7 by default; the fused routing takes batches of at most
+    # 16 tokens and 64 pairs on that arm, unless the plan asks for the routing kernels.
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
+    for n in range(1, 8):
+        assert q.qtip_moe_plan_schedule(plan, n)["route_in_gate_up"] == 1, n
+    for n in (8, 16, 1024):
+        assert q.qtip_moe_plan_schedule(plan, n)["route_in_gate_up"] == 0, n
+    q.qtip_moe_plan_destroy(plan)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_GEMV), "gfx950")
+    assert [q.qtip_moe_plan_schedule(plan, n)["route_in_gate_up"] for n in (10, 11, 16, 17)] == [1, 0, 0, 0]
+    q.qtip_moe_plan_destroy(plan)
+    small = dict(num_experts=16, top_k=4, hidden=256, inter=128, max_tokens=32, arm_override=q.QTIP_ARM_GEMV)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**small), "gfx950")
+    assert [q.qtip_moe_plan_schedule(plan, n)["route_in_gate_up"] for n in (1, 16, 17)] == [1, 1, 0]
+    q.qtip_moe_plan_destroy(plan)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, route_launch=q.QTIP_ROUTE_SEPARATE), "gfx950")
+    assert q.qtip_moe_plan_schedule(plan, 1)["route_in_gate_up"] == 0
+    q.qtip_moe_plan_destroy(plan)
+    with pytest.raises(q.QtipError) as ei:
+        q.qtip_moe_plan_for_arch(q.make_desc(**V4, route_launch=2), "gfx950")
+    assert ei.value.status == q.QTIP_ERR_INVALID_ARG

@@ -360,6 +360,8 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
     return fail(QTIP_ERR_INVALID_ARG, "decode_floor must be in [0, 1024]");
   if (d->rung != QTIP_RUNG_BITSHIFT && d->rung != QTIP_RUNG_LUT)
     return fail(QTIP_ERR_INVALID_ARG, "rung must be QTIP_RUNG_BITSHIFT or QTIP_RUNG_LUT");
+  if (d->route_launch != QTIP_ROUTE_AUTO && d->route_launch != QTIP_ROUTE_SEPARATE)
+    return fail(QTIP_ERR_INVALID_ARG, "route_launch must be QTIP_ROUTE_AUTO or QTIP_ROUTE_SEPARATE");
   *tile_m = tm;
   return QTIP_OK;
 }
@@ -370,6 +372,7 @@ struct CallChoice {
   int32_t arm;
   int karm;
   bool frag, pack;
+  bool route_in_gate_up;  // the batch is routed and binned inside the gate/up launch (SmallRoute)
 };
 
 CallChoice call_choice(const qtip_moe_plan_s* plan, int32_t n_tokens) {
@@ -383,6 +386,8 @@ CallChoice call_choice(const qtip_moe_plan_s* plan, int32_t n_tokens) {
   const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
   c.frag = plan->frag && c.karm == kArmGrouped && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kFragMinPairs);
   c.pack = c.frag && plan->pack && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
+  c.route_in_gate_up = d.route_launch == QTIP_ROUTE_AUTO && c.karm == kArmGemv && !c.frag &&
+                       n_tokens <= kFusedRouteMaxTokens && (int64_t)n_tokens * d.top_k <= kSmallRouteMaxPairs;
   return c;
 }
 
@@ -569,6 +574,7 @@ qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_
   const int karm = kernel_arm(arm);
   out->arm = arm;
   out->tile_m = plan->tile_m;
+  out->route_in_gate_up = call_choice(plan, n_tokens).route_in_gate_up ? 1 : 0;
   shape_of(plan, karm, kModeGateUp, n_tokens, plan->d.inter, &out->gate_up);
   shape_of(plan, karm, kModeSingle, n_tokens, plan->d.hidden, &out->down);
   return QTIP_OK;
@@ -782,7 +788,10 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   const LaunchShape shape_dn =
       persistent_shape(dev, max_units_for(d, n_tokens, vi_dn.pairs_per_decode) * (d.hidden / vi_dn.rows_per_task),
                        vi_dn.waves, spread, vi_dn.input_split, d.inter / kKBlock);
-  if (n_tokens <= kFusedRouteMaxTokens) {
+  if (choice.route_in_gate_up) {
+    // routed and binned inside the gate/up launch below (the "route" stage is empty)
+    if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
+  } else if (n_tokens <= kFusedRouteMaxTokens) {
     // one workgroup routes and bins a small batch (the "route" stage then holds both)
     e = launch_route_bin(lg, n_part, n_tokens, d.num_experts, d.top_k, topk_idx, topk_w, plan->tile_m, counts, offsets,
                          sorted_pair, tile_map, n_tiles, frag ? padded_pair : nullptr, frag ? n_pad : nullptr, &um, st);
@@ -868,6 +877,21 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     gu.act_frag = 1;
   }
   gu.ksplit = shape_gu.ksplit;
+  if (choice.route_in_gate_up) {
+    SmallRoute& r = gu.route;
+    r.logits = lg;
+    r.n_part = n_part;
+    r.n = n_tokens;
+    r.top_k = d.top_k;
+    r.topk_idx = topk_idx;
+    r.topk_w = topk_w;
+    r.sorted_pair = sorted_pair;
+    for (int i = 0; i < 2; ++i) {
+      r.unit_pairs[i] = um.unit_pairs[i];
+      r.units[i] = um.map[i];
+      r.n_units[i] = um.count[i];
+    }
+  }
   e = launch_expert(kModeGateUp, karm, kv_gu, plan->d.rung, gu, shape_gu.grid, shape_gu.waves, st);
   if (e != hipSuccess) return hip_fail(e, "gate/up expert kernel launch");
   if ((e = prof_mark(plan, 3, st)) != hipSuccess) return hip_fail(e, "profile event");
@@ -917,6 +941,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   if ((e = prof_mark(plan, 5, st)) != hipSuccess) return hip_fail(e, "profile event");
   if (plan->prof_capacity) plan->prof_recorded++;
   plan->stats.combine_launches++;
+  if (choice.route_in_gate_up) plan->stats.routed_in_gate_up++;
   plan->stats.forward_calls++;
   plan->stats.last_arm = arm;
   plan->stats.last_n_tokens = n_tokens;

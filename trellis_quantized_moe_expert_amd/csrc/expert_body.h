@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "qtip_internal.h"
+#include "route_device.h"
 
 namespace qtip {
 
@@ -1000,13 +1001,82 @@ __device__ inline void gemv_finish(const ExpertParams& p, const Unit& un, int r0
   gemv_epilogue<MODE, NQ, NT>(p, un, r0, acc0, acc1);
 }
 
-// LDS the split-input GEMV path needs beside the LUT: every wave's partial sums.
+// A small batch's expert ids in workgroup memory (SmallRoute).
+struct SmallRouteLds {
+  int32_t idx[kSmallRouteMaxPairs];
+};
+
+// LDS the split-input GEMV path needs beside the LUT (and a small batch's routing): every wave's
+// partial sums.
 template <class CFG>
 struct GemvSplit {
   static constexpr int kSlotFloats = CFG::kGPairs * CFG::kNT * 2 * 64;
   static constexpr int kFloats = CFG::kWaves * kSlotFloats;
-  static constexpr bool kFits = kFloats * 4 <= 160 * 1024 - kLutEntries * 2;
+  static constexpr bool kFits = kFloats * 4 <= 160 * 1024 - kLutEntries * 2 - (int)sizeof(SmallRouteLds);
 };
+
+// SmallRoute, step 1: the workgroup's waves route the batch's tokens (token t by wave t modulo
+// the waves) into workgroup memory; workgroup 0 also stores the expert ids and router weights.
+__device__ inline void small_route_tokens(const ExpertParams& p, SmallRouteLds& rs) {
+  const SmallRoute& r = p.route;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = (int)(blockDim.x >> 6);
+  const bool first = blockIdx.x == 0;
+  for (int t = wave; t < r.n; t += nw) {
+    int32_t* idx2 = first ? r.topk_idx : nullptr;
+    float* w = first ? r.topk_w : nullptr;
+    if (p.num_experts <= 256) route_token<4>(r.logits, r.n_part, r.n, p.num_experts, r.top_k, t, rs.idx, idx2, w);
+    else route_token<16>(r.logits, r.n_part, r.n, p.num_experts, r.top_k, t, rs.idx, idx2, w);
+  }
+}
+
+// SmallRoute, step 2, by one wave once the ids are in workgroup memory: the stable counting sort
+// of the P <= 64 pairs by expert (lane p holds pair p) and the runs that cut each expert's bin
+// into the two passes' units, stored as the binning kernel stores them (out-of-range ids are left
+// out).  A pair's binned position is the number of valid pairs of lower experts plus the number
+// of its expert's pairs before it; a unit starts at every unit_pairs-th pair of a bin, and a
+// unit's index is the number of unit starts at lower positions.  Every workgroup stores what its
+// own tasks read back after a workgroup barrier (the binned order and the gate/up units: the same
+// values from every workgroup); workgroup 0 also stores the down pass's units.
+__device__ inline void small_bin(const ExpertParams& p, const SmallRouteLds& rs) {
+  const SmallRoute& r = p.route;
+  const int lane = threadIdx.x & 63;
+  const int E = p.num_experts, P = r.n * r.top_k;
+  int e = lane < P ? rs.idx[lane] : E;
+  const bool valid = lane < P && e >= 0 && e < E;
+  if (!valid) e = E;
+  int below = 0, same = 0, rank = 0;
+  for (int q = 0; q < P; ++q) {
+    const int eq = __builtin_amdgcn_readlane(e, q);
+    below += eq < e;
+    same += eq == e;
+    rank += (eq == e) & (q < lane);
+  }
+  const int pos = below + rank;
+  const int U0 = r.unit_pairs[0], U1 = r.unit_pairs[1];
+  const bool s0 = valid && rank % U0 == 0, s1 = valid && rank % U1 == 0;
+  const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
+  int u0 = 0, u1 = 0;
+  for (int q = 0; q < P; ++q) {
+    const bool lower = __builtin_amdgcn_readlane(pos, q) < pos;
+    u0 += (int)((m0 >> q) & 1u) & lower;
+    u1 += (int)((m1 >> q) & 1u) & lower;
+  }
+  if (valid) r.sorted_pair[pos] = lane;
+  if (s0) {
+    r.units[0][3 * u0 + 0] = e;
+    r.units[0][3 * u0 + 1] = pos;
+    r.units[0][3 * u0 + 2] = min(U0, same - rank);
+  }
+  if (lane == 0) *r.n_units[0] = __popcll(m0);
+  if (blockIdx.x != 0) return;
+  if (s1) {
+    r.units[1][3 * u1 + 0] = e;
+    r.units[1][3 * u1 + 1] = pos;
+    r.units[1][3 * u1 + 2] = min(U1, same - rank);
+  }
+  if (lane == 0) *r.n_units[1] = __popcll(m1);
+}
 
 // Kernel configurations (the plan's `variant`): waves per workgroup, 16-row output blocks
 // per task (NT), pairs per decode on the grouped arm (in 16-pair MFMA row blocks, NSUB) and
@@ -1180,6 +1250,40 @@ __device__ inline void expert_tasks(const ExpertParams& p, const DEC& lut_s) {
   }
 }
 
+// A pass's tasks once the decoder's table is in LDS.
+template <int MODE, int ARM, class CFG, bool FRAG, bool SPREAD, class DEC>
+__device__ inline void expert_pass(const ExpertParams& p, const DEC& dec) {
+  if constexpr (SPREAD && ARM == kArmGemv && GemvSplit<CFG>::kFits) {
+    if (p.ksplit > 1) {
+      __shared__ float part[GemvSplit<CFG>::kFloats];
+      gemv_split_tasks<MODE, CFG>(p, dec, part);
+      return;
+    }
+  }
+  expert_tasks<MODE, ARM, CFG, FRAG, SPREAD>(p, dec);
+}
+
+// The fill of the decoder's table (ending in a workgroup barrier), then the pass.  The GEMV
+// arm's fused pass may first route and bin a small batch itself (SmallRoute): the routing is
+// issued before the fill and the binning follows it.
+template <int MODE, int ARM, class CFG, bool FRAG, bool SPREAD, class FILL, class DEC>
+__device__ inline void fill_and_run(const ExpertParams& p, const FILL& fill, const DEC& dec) {
+  if constexpr (MODE == kModeGateUp && ARM == kArmGemv) {
+    __shared__ SmallRouteLds rs;
+    const bool route = p.route.logits != nullptr;
+    if (route) small_route_tokens(p, rs);
+    fill();
+    if (route) {
+      if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) small_bin(p, rs);
+      __syncthreads();
+    }
+    expert_pass<MODE, ARM, CFG, FRAG, SPREAD>(p, dec);
+  } else {
+    fill();
+    expert_pass<MODE, ARM, CFG, FRAG, SPREAD>(p, dec);
+  }
+}
+
 // FRAG: the grouped arm's activations are in fragment order (ExpertParams::act_frag).
 // SPREAD (GEMV arm): the launch may run fewer waves per workgroup than CFG's.
 // RUNG: the decode (kRungBitshift: the 128 KiB LUT in LDS; kRungLut: the 64 KiB replicated codebook).
@@ -1189,29 +1293,15 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
     expert_tasks<MODE, ARM, CFG, false, false>(p, DecoderBitshift{nullptr});
   } else if constexpr (RUNG == kRungLut) {
     __shared__ __attribute__((aligned(16))) uint32_t cb_s[kCodebookEntries * kCodebookCopies];
-    fill_codebook(cb_s, p.lut);
     const DecoderLut dec{reinterpret_cast<const char*>(cb_s), (uint32_t)(threadIdx.x & 31) * 4u};
-    if constexpr (SPREAD && ARM == kArmGemv && GemvSplit<CFG>::kFits) {
-      if (p.ksplit > 1) {
-        __shared__ float part[GemvSplit<CFG>::kFloats];
-        gemv_split_tasks<MODE, CFG>(p, dec, part);
-        return;
-      }
-    }
-    expert_tasks<MODE, ARM, CFG, FRAG, SPREAD>(p, dec);
+    fill_and_run<MODE, ARM, CFG, FRAG, SPREAD>(p, [&] { fill_codebook(cb_s, p.lut); }, dec);
   } else {
     __shared__ __attribute__((aligned(16))) uint16_t lut_s[kLutEntries];
-    if constexpr (SPREAD) fill_lut_any(lut_s, p.lut);
-    else fill_lut<CFG::kWaves * 64>(lut_s, p.lut);
     const DecoderBitshift dec{lut_s};
-    if constexpr (SPREAD && ARM == kArmGemv && GemvSplit<CFG>::kFits) {
-      if (p.ksplit > 1) {
-        __shared__ float part[GemvSplit<CFG>::kFloats];
-        gemv_split_tasks<MODE, CFG>(p, dec, part);
-        return;
-      }
-    }
-    expert_tasks<MODE, ARM, CFG, FRAG, SPREAD>(p, dec);
+    fill_and_run<MODE, ARM, CFG, FRAG, SPREAD>(p, [&] {
+      if constexpr (SPREAD) fill_lut_any(lut_s, p.lut);
+      else fill_lut<CFG::kWaves * 64>(lut_s, p.lut);
+    }, dec);
   }
 }
 

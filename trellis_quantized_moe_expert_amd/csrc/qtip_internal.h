@@ -37,6 +37,26 @@ constexpr int kRouterMaxSplit = 4;        // input chunks (partial sums) per log
 constexpr double kFragMinPairs = 8.0;
 constexpr double kPackMinPairs = 16.0;
 
+// Routing and binning of a small GEMV-arm batch inside the fused gate/up launch (logits NULL: the
+// batch was routed and binned by the routing kernels).  Every workgroup of that launch routes the
+// batch while its table fill is in flight, bins the pairs, and stores the binned order and the
+// gate/up units it reads back (every workgroup stores the same values); workgroup 0 also stores
+// the expert ids, the router weights and the down pass's units, which the down pass and the
+// combine read.  (The per-expert counts, offsets and tile map, which no later launch of this arm
+// reads, are not stored.)  At most kSmallRouteMaxPairs pairs and kFusedRouteMaxTokens tokens; no
+// padded position space.
+constexpr int kSmallRouteMaxPairs = 64;
+struct SmallRoute {
+  const float* logits;  // [n_part][n][E] partial sums added in ascending order, or NULL
+  int32_t n_part, n, top_k;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* sorted_pair;
+  int32_t unit_pairs[2];  // pairs per decode of the gate/up (0) and down (1) passes
+  int32_t* units[2];      // their unit maps (expert, first binned position, pairs)
+  int32_t* n_units[2];
+};
+
 // One pass of one (or two fused) trellis matrices over binned activation rows.
 struct ExpertParams {
   const uint8_t* codes0;        // [E][rows][cols/4]  gate (fused pass) or the single matrix
@@ -70,6 +90,7 @@ struct ExpertParams {
   const int32_t* dense_counts;  // dequantize arm: the per-expert pair counts that define the slots
   int32_t ksplit;               // GEMV arm launched with fewer waves than its configuration's: waves
                                 // sharing one task's inputs (a power of 2 dividing cols/128), or <= 1
+  SmallRoute route;             // GEMV arm, fused pass: the batch's routing, when logits is set
 };
 
 enum ExpertMode { kModeGateUp = 0, kModeSingle = 1 };

@@ -10,124 +10,13 @@
 // bin pairs keep ascending pair id p = t*k + j (a stable counting sort), so the binning
 // is unique and can be compared bit for bit.
 #include "qtip_internal.h"
+#include "route_device.h"
 
 #include <cmath>
 
 namespace qtip {
 
 namespace {
-
-__device__ inline bool beats(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
-}
-
-// Order-preserving integer key of a float under `>` (+0 and -0 map to the same key, as they
-// compare equal; NaN, never selected by `beats`, maps below every number).
-__device__ inline uint32_t order_key(float v) {
-  if (v != v) return 0u;
-  if (v == 0.0f) v = 0.0f;
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Wave-wide max / min of one 32-bit value per lane without the LDS: an inclusive scan inside
-// each 16-lane row by DPP row shifts (lanes past the row start keep their own value), then the
-// four row results (lanes 15, 31, 47, 63) combined in scalar registers.
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
-  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-  return max(max(a, b), max(c, d));
-}
-
-__device__ inline int wave_min_i32(int v) {
-  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x111, 0xF, 0xF, false));
-  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x112, 0xF, 0xF, false));
-  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false));
-  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xF, 0xF, false));
-  const int a = __builtin_amdgcn_readlane(v, 15), b = __builtin_amdgcn_readlane(v, 31);
-  const int c = __builtin_amdgcn_readlane(v, 47), d = __builtin_amdgcn_readlane(v, 63);
-  return min(min(a, b), min(c, d));
-}
-
-// Top-k and softmax of token t by one wave.  Each lane holds Q logits (E <= 64 Q); k rounds
-// of a wave-wide argmax under the order (value descending, index ascending) pick the experts
-// in order: each lane's best, then the largest value over the wave and the lowest index
-// holding it, both by DPP row scans and scalar reads (no LDS round trips).
-template <int Q>
-__device__ __attribute__((always_inline)) inline void route_token(const float* __restrict__ logits, int32_t n_part,
-                                                                  int32_t n, int32_t E, int32_t k, int t,
-                                                                  int32_t* __restrict__ topk_idx,
-                                                                  float* __restrict__ topk_w) {
-  __shared__ float sel_all[kExpertWaves][kMaxTopK];  // the k selected logits, per wave
-  const int lane = threadIdx.x & 63;
-  float* sel = sel_all[threadIdx.x >> 6];
-  const float* row = logits + (size_t)t * E;
-  const size_t part_stride = (size_t)n * (size_t)E;
-  float v[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int e = lane + 64 * q;
-    v[q] = (e < E) ? row[e] : 0.0f;
-  }
-  // partial sums of the router GEMM's K chunks, added in ascending chunk order; the loads of
-  // up to 4 chunks are issued before their additions so their latencies overlap
-  for (int s = 1; s < n_part; s += 4) {
-    float t4[4][Q];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
-        t4[c][q] = (s + c < n_part && e < E) ? row[(size_t)(s + c) * part_stride + e] : 0.0f;
-      }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int q = 0; q < Q; ++q)
-        if (s + c < n_part) v[q] += t4[c][q];
-  }
-  uint32_t taken = 0;
-  for (int jj = 0; jj < k; ++jj) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int e = lane + 64 * q;
-      if (e < E && !((taken >> q) & 1u) && beats(v[q], e, bv, be)) {
-        bv = v[q];
-        be = e;
-      }
-    }
-    // the wave's winner under the same order: the largest value, then the lowest index
-    // among the lanes holding it (lanes without a candidate hold index INT_MAX)
-    const uint32_t kmax = wave_max_u32(be < E ? order_key(bv) : 0u);
-    const int cand = (be < E && order_key(bv) == kmax) ? be : 0x7fffffff;
-    const int win = wave_min_i32(cand);
-    // the winning lane's own best is the winner: take its value (the sign of a zero included)
-    if (win < E) bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), win & 63));
-    be = win;
-    // non-finite logits can leave no winner (be stays out of range); the pair is then
-    // recorded with an out-of-range expert id, which binning ignores
-    if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == 0) {
-      topk_idx[(size_t)t * k + jj] = be;
-      sel[jj] = bv;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  // softmax over the k selected logits, max subtracted first (sel[0] is the largest)
-  float ex = 0.0f;
-  if (lane < k) ex = expf(sel[lane] - sel[0]);
-  float z = ex;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-  if (lane < k) topk_w[(size_t)t * k + lane] = ex / z;
-}
 
 // One wave per token.
 template <int Q>
@@ -137,7 +26,7 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_kernel(const floa
                                                                     float* __restrict__ topk_w) {
   const int t = blockIdx.x * kRouteWaves + (int)(threadIdx.x >> 6);
   if (t >= n) return;  // whole wave leaves together; no barrier follows
-  route_token<Q>(logits, n_part, n, E, k, t, topk_idx, topk_w);
+  route_token<Q>(logits, n_part, n, E, k, t, topk_idx, nullptr, topk_w);
 }
 
 // Inclusive scan over a wave: DPP row shifts scan each 16-lane row, then the last lane of row 0
@@ -342,7 +231,7 @@ __global__ __launch_bounds__(kBinThreads) void route_bin_kernel(const float* __r
                                                                 int32_t* padded_pair, int32_t* n_pad, UnitOut ug,
                                                                 UnitOut ud) {
   const int t = (int)(threadIdx.x >> 6);
-  if (t < n) route_token<Q>(logits, n_part, n, E, k, t, topk_idx, topk_w);
+  if (t < n) route_token<Q>(logits, n_part, n, E, k, t, topk_idx, nullptr, topk_w);
   __syncthreads();
   bin_pairs(topk_idx, n * k, E, tile_m, counts, offsets, sorted_pair, tile_map, n_tiles, padded_pair, n_pad, ug, ud);
 }
