@@ -70,7 +70,7 @@ def kernel_source_sha() -> str:
 class Runner:
     """Plan + device weights + workspace; forwards one batch through the C ABI."""
 
-    def __init__(self, inp, arm, max_tokens, out_dtype, weights=None, variant=0, act_layout=0, route_launch="auto"):
+    def __init__(self, inp, arm, max_tokens, out_dtype, weights=None, variant=0, act_layout=0, small_batch="fused"):
         import torch
         import trellis_quantized_moe_expert_amd as q
         from moe_inputs.device import weights_to_device
@@ -81,10 +81,10 @@ class Runner:
                     "dequant": q.QTIP_ARM_DEQUANT}[arm]
         od = q.QTIP_OUT_BF16 if out_dtype == "bf16" else q.QTIP_OUT_F32
         rung = q.QTIP_RUNG_LUT if s.rung == "lut" else q.QTIP_RUNG_BITSHIFT
-        rl = q.QTIP_ROUTE_SEPARATE if route_launch == "separate" else q.QTIP_ROUTE_AUTO
+        sb = q.QTIP_SMALL_BATCH_SEPARATE if small_batch == "separate" else q.QTIP_SMALL_BATCH_FUSED
         self.plan = q.qtip_moe_plan(q.make_desc(s.num_experts, s.top_k, s.hidden, s.inter, max_tokens, arm_code,
                                                 variant, od, 0, act_layout=act_layout, rung=rung,
-                                                route_launch=rl), 0)
+                                                small_batch=sb), 0)
         self.info = q.qtip_moe_plan_info(self.plan)
         self.ws = torch.empty(self.info["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
         self.dw = weights if weights is not None else weights_to_device(inp)
@@ -359,7 +359,7 @@ def calibrate_copy():
 
 
 def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=None, layouts=(0,), rung="bitshift",
-              route_launch="auto"):
+              small_batch="fused"):
     import moe_inputs
     shape = moe_inputs.WORKLOADS["v4_decode_n32" if rung == "bitshift" else "lut_v4_decode_n32"]
     log("sweep: drawing V4-shaped weights once")
@@ -369,7 +369,7 @@ def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=N
     with open(path, "a") as f:
         for arm, layout in [(a, l) for a in arms for l in layouts]:
             r = Runner(inps[n_list[0]], arm, max(n_list), "bf16", weights=base, variant=variant, act_layout=layout,
-                       route_launch=route_launch)
+                       small_batch=small_batch)
             base = r.dw
             for n in n_list:
                 r.bind(inps[n])
@@ -380,7 +380,7 @@ def run_sweep(path, steps, warmup, variant=0, arms=("gemv", "grouped"), n_list=N
                 fig = schedule_figures(counts, r.shape, arm, sched)
                 ms = res["wall_s"] * 1e3 / steps
                 rec = {"rung": rung, "arm": arm, "n": n, "variant_requested": variant, "act_layout": layout,
-                       "route_launch": route_launch,
+                       "small_batch": small_batch,
                        "ms_per_step": ms,
                        "tokens_per_s": n / (ms * 1e-3),
                        "stage_ms": {k: v / prof["n_forwards"] for k, v in prof.items() if k != "n_forwards"},
@@ -442,7 +442,7 @@ def measure_workload(name, inp, weights, args, gather_measured, full=False):
     unless --arm, bf16 output unless --out-dtype) and returns its record."""
     s = inp.shape
     runner = Runner(inp, args.arm, s.n_tokens, args.out_dtype, weights=weights, variant=args.variant,
-                    route_launch=args.route_launch)
+                    small_batch=args.small_batch)
     runner.bind(inp)
     q = runner.q
     arm_code = q.qtip_moe_select_arm(runner.plan, s.n_tokens)
@@ -501,6 +501,7 @@ def measure_workload(name, inp, weights, args, gather_measured, full=False):
         "schedule": sched,
         "launch_counters": {k: counters[k] for k in ("gemv_launches", "grouped_launches", "dequant_launches",
                                                      "route_launches", "combine_launches", "router_launches",
+                                                     "routed_in_gate_up", "combined_in_down",
                                                      "gemv_variant_launches", "grouped_variant_launches")},
     }
     rec.update(extra)
@@ -516,8 +517,9 @@ def main():
     ap.add_argument("--curve", default=",".join(CURVE), help="comma-separated workloads measured beside the "
                     "headline and reported in detail.curve ('' for none)")
     ap.add_argument("--arm", choices=["auto", "gemv", "grouped", "dequant"], default="auto")
-    ap.add_argument("--route-launch", choices=["auto", "separate"], default="auto",
-                    help="small GEMV batches routed inside the gate+up launch (auto) or by the routing kernels")
+    ap.add_argument("--small-batch", choices=["fused", "separate"], default="fused",
+                    help="small GEMV batches in two launches (routing in the gate+up launch, combine in the down "
+                    "launch) or in four")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--variant", type=int, default=0, help="expert kernel variant (0 = the plan's choice, 1..11 fixed; see qtip_moe_plan_schedule)")
     ap.add_argument("--cpu-experts", type=int, default=-1, help="woken experts the CPU oracle is timed on (-1: the "
@@ -555,7 +557,7 @@ def main():
             calibrate_copy()
         n_list = [int(x) for x in args.sweep_n.split(",")] if args.sweep_n else None
         run_sweep(args.sweep, args.steps, args.warmup, args.variant, tuple(args.sweep_arms.split(",")), n_list,
-                  tuple(int(x) for x in args.sweep_layouts.split(",")), args.sweep_rung, args.route_launch)
+                  tuple(int(x) for x in args.sweep_layouts.split(",")), args.sweep_rung, args.small_batch)
         return
 
     curve = [c for c in args.curve.split(",") if c and c != args.workload]

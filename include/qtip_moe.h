@@ -80,8 +80,8 @@ enum { QTIP_OUT_BF16 = 0, QTIP_OUT_F32 = 1 };
 enum { QTIP_ACT_AUTO = 0, QTIP_ACT_ROWS = 1, QTIP_ACT_FRAGMENTS = 2 };
 /* The two 2-bit rungs (weight formats) of the expert matrices; see "Weight formats" above. */
 enum { QTIP_RUNG_BITSHIFT = 0, QTIP_RUNG_LUT = 1 };
-/* Where a small GEMV-arm batch is routed and binned (qtip_moe_desc.route_launch). */
-enum { QTIP_ROUTE_AUTO = 0, QTIP_ROUTE_SEPARATE = 1 };
+/* How a small GEMV-arm batch is launched (qtip_moe_desc.small_batch). */
+enum { QTIP_SMALL_BATCH_FUSED = 0, QTIP_SMALL_BATCH_SEPARATE = 1 };
 #define QTIP_LUT_RUNG_BITS 9 /* pair-state bits of the LUT rung: a 2^9 x 2 codebook */
 
 /* Decode-regime floor of the pages: n <= 8 tokens always take the GEMV arm (m-tile page, "The
@@ -146,11 +146,16 @@ typedef struct qtip_moe_desc {
   int32_t decode_floor; /* AUTO dispatch sends n <= decode_floor to the GEMV arm whatever the fill: 0 = the
                            value measured for these kernels and the rung (QTIP_DEFAULT_DECODE_FLOOR_*); 8
                            reproduces the pages' floor; 1..1024 accepted */
-  int32_t route_launch; /* QTIP_ROUTE_AUTO: a GEMV-arm batch of at most 16 tokens and 64 pairs is routed and
-                           binned inside the fused gate+up launch (every workgroup routes it while its table
-                           fill is in flight; one of them stores the routing for the later launches), which
-                           saves the routing launch; QTIP_ROUTE_SEPARATE: always by the routing kernels.
-                           The outputs are the same either way. */
+  int32_t small_batch;  /* QTIP_SMALL_BATCH_FUSED: a GEMV-arm batch of at most 16 tokens and 64 pairs is routed
+                           and binned inside the fused gate+up launch (every workgroup routes it before its
+                           table fill; one of them stores the routing for the later launches), which saves
+                           the routing launch; and where its down pass fits one round of workgroup tasks on
+                           the GPU (one task per token and 16-row block: a single token at H = 4096) and k x
+                           the pass's input split fits a workgroup, the combine runs inside the down launch
+                           (the token's k pairs summed in ascending j), which saves the combine launch too.
+                           QTIP_SMALL_BATCH_SEPARATE: the routing and the combine kernels.  Same arithmetic
+                           in the same order either way; the down pass may split its inputs over a different
+                           number of waves, which changes the order of its fp32 additions. */
 } qtip_moe_desc;
 
 typedef struct qtip_moe_plan_s* qtip_moe_plan_t;
@@ -182,6 +187,7 @@ typedef struct qtip_moe_stats_s {
   uint64_t gemv_variant_launches[QTIP_VARIANT_SLOTS];    /* GEMV-arm expert launches per configuration */
   uint64_t grouped_variant_launches[QTIP_VARIANT_SLOTS]; /* grouped-arm expert launches per configuration */
   uint64_t routed_in_gate_up; /* forwards whose batch was routed and binned inside the gate+up launch */
+  uint64_t combined_in_down;  /* forwards whose combine ran inside the down launch */
 } qtip_moe_stats_t;
 
 /* ---- plan -------------------------------------------------------------------------
@@ -233,7 +239,8 @@ typedef struct qtip_moe_schedule {
   qtip_moe_kernel_shape gate_up; /* the fused gate+up pass */
   qtip_moe_kernel_shape down;    /* the down pass */
   int32_t route_in_gate_up;      /* 1: the batch is routed and binned inside the gate+up launch
-                                    (qtip_moe_desc.route_launch), 0: by the routing kernels */
+                                    (qtip_moe_desc.small_batch), 0: by the routing kernels */
+  int32_t combine_in_down;       /* 1: the combine runs inside the down launch, 0: its own kernel */
 } qtip_moe_schedule;
 qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_moe_schedule* out /*host*/);
 

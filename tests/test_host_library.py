@@ -376,10 +376,11 @@ def test_select_grouped_ignores_the_arm_pin():
 def test_stats_start_at_zero_with_per_variant_slots():
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
     st = q.qtip_moe_stats(plan)
-    assert st["forward_calls"] == 0 and st["last_arm"] == 0 and st["routed_in_gate_up"] == 0
+    assert st["forward_calls"] == 0 and st["last_arm"] == 0
+    assert st["routed_in_gate_up"] == 0 and st["combined_in_down"] == 0
     assert st["gemv_variant_launches"] == [0] * 12 and st["grouped_variant_launches"] == [0] * 12
     q.qtip_moe_stats_reset(plan)
-    assert ctypes.sizeof(q.qtip_moe_stats_t) == 7 * 8 + 2 * 4 + 2 * 12 * 8 + 8
+    assert ctypes.sizeof(q.qtip_moe_stats_t) == 7 * 8 + 2 * 4 + 2 * 12 * 8 + 2 * 8
     q.qtip_moe_plan_destroy(plan)
 
 
@@ -461,14 +462,34 @@ def test_dequantize_workspace_holds_only_the_woken_experts():
         q.qtip_moe_plan_destroy(base)
 
 
-def test_small_gemv_batches_are_routed_inside_the_gate_up_launch():
-    # V4 (k = 6): the GEMV arm serves n <= 7 by default; the fused routing takes batches of at most
-    # 16 tokens and 64 pairs on that arm, unless the plan asks for the routing kernels.
+def test_small_gemv_batches_run_in_fewer_launches():
+    # V4 (k = 6): the GEMV arm serves n <= 7 by default; a batch of at most 16 tokens and 64 pairs on
+    # that arm is routed inside the gate+up launch, and a single token (256 token tasks of 16 rows:
+    # one round on the CUs) is also combined inside the down launch (6 pairs x 2 input halves = 12
+    # waves of the 16-wave down configuration), unless the plan asks for the separate kernels.
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
-    for n in range(1, 8):
-        assert q.qtip_moe_plan_schedule(plan, n)["route_in_gate_up"] == 1, n
+    s = q.qtip_moe_plan_schedule(plan, 1)
+    assert (s["route_in_gate_up"], s["combine_in_down"]) == (1, 1)
+    assert s["down"]["waves_per_workgroup"] == 16 and s["down"]["rows_per_task"] == 16
+    for n in range(2, 8):
+        s = q.qtip_moe_plan_schedule(plan, n)
+        assert (s["route_in_gate_up"], s["combine_in_down"]) == (1, 0), n
     for n in (8, 16, 1024):
-        assert q.qtip_moe_plan_schedule(plan, n)["route_in_gate_up"] == 0, n
+        s = q.qtip_moe_plan_schedule(plan, n)
+        assert (s["route_in_gate_up"], s["combine_in_down"]) == (0, 0), n
+    q.qtip_moe_plan_destroy(plan)
+    # smaller rows: more tokens fit one round (H = 512: 32 tasks per token, 8 tokens)
+    small = dict(num_experts=16, top_k=4, hidden=512, inter=256, max_tokens=32, arm_override=q.QTIP_ARM_GEMV)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**small), "gfx950")
+    assert [q.qtip_moe_plan_schedule(plan, n)["combine_in_down"] for n in (1, 8, 9)] == [1, 1, 0]
+    q.qtip_moe_plan_destroy(plan)
+    # the LUT rung's default GEMV down configuration at n >= 3 (32-row tasks) cannot split its
+    # inputs; at one token (16-row configuration) it can
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, rung=q.QTIP_RUNG_LUT), "gfx950")
+    s = q.qtip_moe_plan_schedule(plan, 1)
+    assert (s["route_in_gate_up"], s["combine_in_down"], s["down"]["variant"]) == (1, 1, 1)
+    s = q.qtip_moe_plan_schedule(plan, 3)
+    assert (s["route_in_gate_up"], s["combine_in_down"], s["down"]["variant"]) == (1, 0, 3)
     q.qtip_moe_plan_destroy(plan)
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_GEMV), "gfx950")
     assert [q.qtip_moe_plan_schedule(plan, n)["route_in_gate_up"] for n in (10, 11, 16, 17)] == [1, 0, 0, 0]
@@ -477,9 +498,21 @@ def test_small_gemv_batches_are_routed_inside_the_gate_up_launch():
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**small), "gfx950")
     assert [q.qtip_moe_plan_schedule(plan, n)["route_in_gate_up"] for n in (1, 16, 17)] == [1, 1, 0]
     q.qtip_moe_plan_destroy(plan)
-    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, route_launch=q.QTIP_ROUTE_SEPARATE), "gfx950")
-    assert q.qtip_moe_plan_schedule(plan, 1)["route_in_gate_up"] == 0
+    # a forced kernel configuration that cannot split its inputs keeps the combine kernel
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, variant=4), "gfx950")
+    s = q.qtip_moe_plan_schedule(plan, 1)
+    assert (s["route_in_gate_up"], s["combine_in_down"], s["down"]["variant"]) == (1, 0, 4)
+    q.qtip_moe_plan_destroy(plan)
+    # top-k above the down configuration's waves keeps the combine kernel
+    wide = dict(num_experts=64, top_k=20, hidden=256, inter=256, max_tokens=8)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**wide, arm_override=q.QTIP_ARM_GEMV), "gfx950")
+    s = q.qtip_moe_plan_schedule(plan, 2)
+    assert (s["route_in_gate_up"], s["combine_in_down"]) == (1, 0)
+    q.qtip_moe_plan_destroy(plan)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, small_batch=q.QTIP_SMALL_BATCH_SEPARATE), "gfx950")
+    s = q.qtip_moe_plan_schedule(plan, 1)
+    assert (s["route_in_gate_up"], s["combine_in_down"]) == (0, 0)
     q.qtip_moe_plan_destroy(plan)
     with pytest.raises(q.QtipError) as ei:
-        q.qtip_moe_plan_for_arch(q.make_desc(**V4, route_launch=2), "gfx950")
+        q.qtip_moe_plan_for_arch(q.make_desc(**V4, small_batch=2), "gfx950")
     assert ei.value.status == q.QTIP_ERR_INVALID_ARG

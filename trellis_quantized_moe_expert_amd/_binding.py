@@ -35,8 +35,8 @@ QTIP_DEFAULT_DECODE_FLOOR_LUT = 5
 QTIP_DECODE_REGIME_MAX_TOKENS = 8
 QTIP_RUNG_BITSHIFT = 0
 QTIP_RUNG_LUT = 1
-QTIP_ROUTE_AUTO = 0
-QTIP_ROUTE_SEPARATE = 1
+QTIP_SMALL_BATCH_FUSED = 0
+QTIP_SMALL_BATCH_SEPARATE = 1
 QTIP_LUT_RUNG_BITS = 9
 
 
@@ -46,7 +46,7 @@ class qtip_moe_desc(ctypes.Structure):
                 ("variant", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("dispatch_tile_m", ctypes.c_int32), ("dequant_traffic_ratio", ctypes.c_int32),
                 ("act_layout", ctypes.c_int32), ("rung", ctypes.c_int32), ("decode_floor", ctypes.c_int32),
-                ("route_launch", ctypes.c_int32)]
+                ("small_batch", ctypes.c_int32)]
 
 
 class qtip_moe_weights(ctypes.Structure):
@@ -67,7 +67,7 @@ class qtip_moe_stats_t(ctypes.Structure):
                 ("last_n_tokens", ctypes.c_int32),
                 ("gemv_variant_launches", ctypes.c_uint64 * QTIP_VARIANT_SLOTS),
                 ("grouped_variant_launches", ctypes.c_uint64 * QTIP_VARIANT_SLOTS),
-                ("routed_in_gate_up", ctypes.c_uint64)]
+                ("routed_in_gate_up", ctypes.c_uint64), ("combined_in_down", ctypes.c_uint64)]
 
 
 class qtip_moe_kernel_shape(ctypes.Structure):
@@ -77,7 +77,8 @@ class qtip_moe_kernel_shape(ctypes.Structure):
 
 class qtip_moe_schedule(ctypes.Structure):
     _fields_ = [("arm", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("gate_up", qtip_moe_kernel_shape),
-                ("down", qtip_moe_kernel_shape), ("route_in_gate_up", ctypes.c_int32)]
+                ("down", qtip_moe_kernel_shape), ("route_in_gate_up", ctypes.c_int32),
+                ("combine_in_down", ctypes.c_int32)]
 
 
 class QtipError(RuntimeError):
@@ -180,9 +181,9 @@ def _check(fn: str, status: int):
 def make_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override=QTIP_ARM_AUTO, variant=0,
               out_dtype=QTIP_OUT_F32, tile_m=0, dispatch_tile_m=0, dequant_traffic_ratio=0,
               act_layout=QTIP_ACT_AUTO, rung=QTIP_RUNG_BITSHIFT, decode_floor=0,
-              route_launch=QTIP_ROUTE_AUTO) -> qtip_moe_desc:
+              small_batch=QTIP_SMALL_BATCH_FUSED) -> qtip_moe_desc:
     return qtip_moe_desc(num_experts, top_k, hidden, inter, max_tokens, arm_override, variant, out_dtype, tile_m,
-                         dispatch_tile_m, dequant_traffic_ratio, act_layout, rung, decode_floor, route_launch)
+                         dispatch_tile_m, dequant_traffic_ratio, act_layout, rung, decode_floor, small_batch)
 
 
 def make_weights(codes_gate, codes_up, codes_down, scale_gate, scale_up, scale_down, lut) -> qtip_moe_weights:
@@ -218,7 +219,7 @@ def qtip_moe_plan_schedule(plan: int, n_tokens: int) -> dict:
     _check("qtip_moe_plan_schedule", lib().qtip_moe_plan_schedule(plan, n_tokens, ctypes.byref(out)))
     shape = lambda sh: {name: getattr(sh, name) for name, _ in qtip_moe_kernel_shape._fields_}
     return {"arm": out.arm, "tile_m": out.tile_m, "gate_up": shape(out.gate_up), "down": shape(out.down),
-            "route_in_gate_up": out.route_in_gate_up}
+            "route_in_gate_up": out.route_in_gate_up, "combine_in_down": out.combine_in_down}
 
 
 def qtip_moe_select_arm(plan: int, n_tokens: int) -> int:

@@ -360,8 +360,8 @@ qtip_status validate_desc(const qtip_moe_desc* d, int32_t* tile_m) {
     return fail(QTIP_ERR_INVALID_ARG, "decode_floor must be in [0, 1024]");
   if (d->rung != QTIP_RUNG_BITSHIFT && d->rung != QTIP_RUNG_LUT)
     return fail(QTIP_ERR_INVALID_ARG, "rung must be QTIP_RUNG_BITSHIFT or QTIP_RUNG_LUT");
-  if (d->route_launch != QTIP_ROUTE_AUTO && d->route_launch != QTIP_ROUTE_SEPARATE)
-    return fail(QTIP_ERR_INVALID_ARG, "route_launch must be QTIP_ROUTE_AUTO or QTIP_ROUTE_SEPARATE");
+  if (d->small_batch != QTIP_SMALL_BATCH_FUSED && d->small_batch != QTIP_SMALL_BATCH_SEPARATE)
+    return fail(QTIP_ERR_INVALID_ARG, "small_batch must be QTIP_SMALL_BATCH_FUSED or QTIP_SMALL_BATCH_SEPARATE");
   *tile_m = tm;
   return QTIP_OK;
 }
@@ -386,9 +386,45 @@ CallChoice call_choice(const qtip_moe_plan_s* plan, int32_t n_tokens) {
   const double ppe = fill_pairs_per_woken_expert(n_tokens, d.top_k, d.num_experts);
   c.frag = plan->frag && c.karm == kArmGrouped && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kFragMinPairs);
   c.pack = c.frag && plan->pack && (d.act_layout == QTIP_ACT_FRAGMENTS || ppe >= kPackMinPairs);
-  c.route_in_gate_up = d.route_launch == QTIP_ROUTE_AUTO && c.karm == kArmGemv && !c.frag &&
+  c.route_in_gate_up = d.small_batch == QTIP_SMALL_BATCH_FUSED && c.karm == kArmGemv && !c.frag &&
                        n_tokens <= kFusedRouteMaxTokens && (int64_t)n_tokens * d.top_k <= kSmallRouteMaxPairs;
   return c;
+}
+
+// The kernel configurations of a forward's two passes, and the down pass's token tasks
+// (TokenCombine) where they apply: small batches routed inside the gate/up launch whose token
+// tasks fit in one round on the CUs (measured on the V4 layer: one token; every further round
+// adds a barrier and the first wave's serial sum, and with two tokens the launch of the combine
+// kernel is already cheaper), a down configuration that can split a task's inputs over waves (by
+// default one that can: 16 waves of 16-row tasks), and k x S waves within its workgroup, S the
+// largest power of two that cuts the inputs into runs of at least two blocks.
+constexpr long kTokenTaskRound = 256;  // CUs of an MI355X (gfx950)
+
+struct PassPlan {
+  int kv_gu, kv_dn;
+  int tok_split;  // the token tasks' waves per pair, or 0: no token tasks (the combine kernel runs)
+};
+
+PassPlan pass_plan(const qtip_moe_plan_s* plan, const CallChoice& c, int32_t n_tokens) {
+  const qtip_moe_desc& d = plan->d;
+  PassPlan pp{};
+  pp.kv_gu = fit_variant(resolve_variant(plan, c.karm, kModeGateUp, n_tokens), c.karm, d.inter);
+  pp.kv_dn = fit_variant(resolve_variant(plan, c.karm, kModeSingle, n_tokens), c.karm, d.hidden);
+  if (!c.route_in_gate_up) return pp;
+  int kv = pp.kv_dn;
+  VariantInfo v{};
+  variant_info(kv, kArmGemv, v);
+  if (!v.input_split && d.variant == kVariantDefault) {
+    kv = fit_variant(1, kArmGemv, d.hidden);
+    variant_info(kv, kArmGemv, v);
+  }
+  const int k = d.top_k, kblocks = d.inter / kKBlock;
+  if (!v.input_split || k > v.waves || (long)n_tokens * (d.hidden / v.rows_per_task) > kTokenTaskRound) return pp;
+  int S = 1;
+  while (k * 2 * S <= v.waves && kblocks % (2 * S) == 0 && kblocks / (2 * S) >= 2) S *= 2;
+  pp.kv_dn = kv;
+  pp.tok_split = S;
+  return pp;
 }
 
 // Scratch of a forward laid out for its own n tokens: only the buffers that call uses.
@@ -556,9 +592,7 @@ qtip_status qtip_moe_plan_info(qtip_moe_plan_t plan, int32_t* tile_m, size_t* wo
   return QTIP_OK;
 }
 
-static void shape_of(const qtip_moe_plan_s* plan, int karm, int mode, int32_t n_tokens, int32_t rows,
-                     qtip_moe_kernel_shape* out) {
-  const int kv = fit_variant(resolve_variant(plan, karm, mode, n_tokens), karm, rows);
+static void shape_of(int kv, int karm, qtip_moe_kernel_shape* out) {
   VariantInfo v{};
   variant_info(kv, karm, v);
   out->variant = kv;
@@ -574,9 +608,12 @@ qtip_status qtip_moe_plan_schedule(qtip_moe_plan_t plan, int32_t n_tokens, qtip_
   const int karm = kernel_arm(arm);
   out->arm = arm;
   out->tile_m = plan->tile_m;
-  out->route_in_gate_up = call_choice(plan, n_tokens).route_in_gate_up ? 1 : 0;
-  shape_of(plan, karm, kModeGateUp, n_tokens, plan->d.inter, &out->gate_up);
-  shape_of(plan, karm, kModeSingle, n_tokens, plan->d.hidden, &out->down);
+  const CallChoice c = call_choice(plan, n_tokens);
+  const PassPlan pp = pass_plan(plan, c, n_tokens);
+  out->route_in_gate_up = c.route_in_gate_up ? 1 : 0;
+  out->combine_in_down = pp.tok_split > 0 ? 1 : 0;
+  shape_of(pp.kv_gu, karm, &out->gate_up);
+  shape_of(pp.kv_dn, karm, &out->down);
   return QTIP_OK;
 }
 
@@ -767,8 +804,8 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   const int32_t pp_max = (int32_t)pad_positions(d, n_tokens);
   // kernel configurations of the two passes; each pass gets its own decode units (runs of its
   // pairs per decode), so every task of a pass is one decode of its rows
-  const int kv_gu = fit_variant(resolve_variant(plan, karm, kModeGateUp, n_tokens), karm, d.inter);
-  const int kv_dn = fit_variant(resolve_variant(plan, karm, kModeSingle, n_tokens), karm, d.hidden);
+  const PassPlan pp = pass_plan(plan, choice, n_tokens);
+  const int kv_gu = pp.kv_gu, kv_dn = pp.kv_dn;
   VariantInfo vi_gu{}, vi_dn{};
   variant_info(kv_gu, karm, vi_gu);
   variant_info(kv_dn, karm, vi_dn);
@@ -785,9 +822,15 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   const LaunchShape shape_gu =
       persistent_shape(dev, max_units_for(d, n_tokens, vi_gu.pairs_per_decode) * (d.inter / vi_gu.rows_per_task),
                        vi_gu.waves, spread, vi_gu.input_split, d.hidden / kKBlock);
-  const LaunchShape shape_dn =
+  LaunchShape shape_dn =
       persistent_shape(dev, max_units_for(d, n_tokens, vi_dn.pairs_per_decode) * (d.hidden / vi_dn.rows_per_task),
                        vi_dn.waves, spread, vi_dn.input_split, d.inter / kKBlock);
+  if (pp.tok_split) {
+    // token tasks: one workgroup of k x S waves per token and row block, persistent over the CUs
+    const long tok_tasks = (long)n_tokens * (d.hidden / vi_dn.rows_per_task);
+    const long cus = g_cu_count[dev].load(std::memory_order_acquire);
+    shape_dn = LaunchShape{(int)(tok_tasks < cus ? tok_tasks : cus), d.top_k * pp.tok_split, pp.tok_split};
+  }
   if (choice.route_in_gate_up) {
     // routed and binned inside the gate/up launch below (the "route" stage is empty)
     if ((e = prof_mark(plan, 1, st)) != hipSuccess) return hip_fail(e, "profile event");
@@ -877,6 +920,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     gu.act_frag = 1;
   }
   gu.ksplit = shape_gu.ksplit;
+  if (pp.tok_split) gu.out_row_map = sorted_pair;  // h by pair, as the token tasks read it
   if (choice.route_in_gate_up) {
     SmallRoute& r = gu.route;
     r.logits = lg;
@@ -921,6 +965,11 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     dn.n_pad_max = pp_max;
   }
   dn.ksplit = shape_dn.ksplit;
+  if (pp.tok_split) {
+    // h was stored by pair (gu.out_row_map); the down pass adds each token's pairs into out
+    dn.act_row_map = nullptr;
+    dn.tok = TokenCombine{topk_idx, topk_w, out, n_tokens, d.top_k, d.out_dtype == QTIP_OUT_BF16 ? 1 : 0};
+  }
   e = launch_expert(kModeSingle, karm, kv_dn, plan->d.rung, dn, shape_dn.grid, shape_dn.waves, st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");
   if ((e = prof_mark(plan, 4, st)) != hipSuccess) return hip_fail(e, "profile event");
@@ -936,11 +985,15 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     plan->stats.gemv_variant_launches[kv_dn]++;
   }
 
-  e = launch_combine(y, topk_w, n_tokens, d.top_k, d.hidden, out, d.out_dtype == QTIP_OUT_BF16, st);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (pp.tok_split) {
+    plan->stats.combined_in_down++;  // the "combine" stage is empty
+  } else {
+    e = launch_combine(y, topk_w, n_tokens, d.top_k, d.hidden, out, d.out_dtype == QTIP_OUT_BF16, st);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    plan->stats.combine_launches++;
+  }
   if ((e = prof_mark(plan, 5, st)) != hipSuccess) return hip_fail(e, "profile event");
   if (plan->prof_capacity) plan->prof_recorded++;
-  plan->stats.combine_launches++;
   if (choice.route_in_gate_up) plan->stats.routed_in_gate_up++;
   plan->stats.forward_calls++;
   plan->stats.last_arm = arm;

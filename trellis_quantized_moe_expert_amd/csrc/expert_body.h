@@ -317,7 +317,9 @@ __device__ inline int out_row(const ExpertParams& p, int s) {
   return (r >= 0 && r < p.n_out_rows) ? r : -1;
 }
 
-template <int MODE>
+// BYPAIR (GEMV arm): the fused pass may store h by pair (out_row_map set) instead of by binned
+// position.
+template <int MODE, bool BYPAIR = false>
 __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int r, int pi, float a0, float a1,
                                       float s0, float s1) {
   const int s = un.start + pi;
@@ -325,7 +327,11 @@ __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int
     const float g = a0 * s0, u = a1 * s1;
     const float h = silu(g) * u;
     size_t o;
-    if (p.unit_pad) {
+    if (BYPAIR && p.out_row_map) {
+      const int orow = out_row(p, s);
+      if (orow < 0) return;
+      o = (size_t)orow * p.rows + r;
+    } else if (p.unit_pad) {
       // h in fragment order over padded positions, as the down pass reads its A operand
       // (its input index r = kb*128 + 32g + 8st + t)
       const int pp = un.pad + pi;
@@ -946,7 +952,7 @@ __device__ inline void gemv_epilogue(const ExpertParams& p, const Unit& un, int 
         a1 += __shfl_xor(a1, 16, 64);
         a1 += __shfl_xor(a1, 32, 64);
       }
-      if (q < un.len && (q & 3) == g) epilogue_store<MODE>(p, un, r, q, a0, a1, s0, s1);
+      if (q < un.len && (q & 3) == g) epilogue_store<MODE, true>(p, un, r, q, a0, a1, s0, s1);
     }
   }
 }
@@ -1014,6 +1020,70 @@ struct GemvSplit {
   static constexpr int kFloats = CFG::kWaves * kSlotFloats;
   static constexpr bool kFits = kFloats * 4 <= 160 * 1024 - kLutEntries * 2 - (int)sizeof(SmallRouteLds);
 };
+
+// TokenCombine: the first wave adds the k x S partial sums of one token's 16 NT rows into the
+// layer output (the sums as the split GEMV path and the combine kernel form them: ascending s, the
+// lane groups' reduction, the row scale, then ascending j weighted by the router weights).
+template <int NT>
+__device__ inline void token_finish(const ExpertParams& p, int t, int r0, const float* part, int slot_floats,
+                                    int S) {
+  const TokenCombine& tc = p.tok;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = r0 + 16 * nt + (lane & 15);
+    float acc = 0.f;
+    for (int jj = 0; jj < tc.k; ++jj) {
+      const int pair = t * tc.k + jj;
+      const int e = __builtin_amdgcn_readfirstlane(tc.topk_idx[pair]);
+      if (e < 0 || e >= p.num_experts) continue;
+      float a0 = 0.f;
+      for (int w = 0; w < S; ++w) a0 += part[(jj * S + w) * slot_floats + nt * 2 * 64 + lane];
+      a0 += __shfl_xor(a0, 16, 64);
+      a0 += __shfl_xor(a0, 32, 64);
+      const float y = a0 * f16_to_f32(p.scale0[(size_t)e * p.rows + r]);
+      acc = fmaf(tc.topk_w[pair], y, acc);
+    }
+    if (lane < 16) {
+      const size_t o = (size_t)t * p.rows + r;
+      if (tc.out_bf16) reinterpret_cast<uint16_t*>(tc.out)[o] = (uint16_t)f32_to_bf16_bits(acc);
+      else reinterpret_cast<float*>(tc.out)[o] = acc;
+    }
+  }
+}
+
+// TokenCombine's task loop: a workgroup of k x S waves per token task (waves past k S idle).
+template <class CFG, class DEC>
+__device__ inline void gemv_token_tasks(const ExpertParams& p, const DEC& lut, float* part) {
+  constexpr int NT = CFG::kNT;
+  constexpr bool AP = CFG::kAPre;
+  constexpr bool X3 = CFG::kX3Down;
+  constexpr int kSlot = GemvSplit<CFG>::kSlotFloats;
+  const TokenCombine& tc = p.tok;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = p.ksplit > 1 ? p.ksplit : 1;
+  const int j = wave / S, sidx = wave % S;
+  const int kper = p.cols / kKBlock / S;
+  const int lo = sidx * kper, hi = lo + kper;
+  const int nblocks = p.rows / CFG::kRows;
+  const long total = (long)tc.n * nblocks;
+  float* mine = part + wave * kSlot;
+  for (long task = blockIdx.x; task < total; task += gridDim.x) {
+    const int t = (int)(task / nblocks);
+    const int r0 = (int)(task - (long)t * nblocks) * CFG::kRows;
+    if (j < tc.k) {
+      const int pair = t * tc.k + j;
+      const int e = __builtin_amdgcn_readfirstlane(tc.topk_idx[pair]);
+      if (e >= 0 && e < p.num_experts) {
+        const Unit un{e, pair, 1, -1};
+        gemv_part<kModeSingle, 1, NT, AP, X3>(p, lut, un, r0, lo, hi, mine);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) token_finish<NT>(p, t, r0, part, kSlot, S);
+    __syncthreads();
+  }
+}
 
 // SmallRoute, step 1: the workgroup's waves route the batch's tokens (token t by wave t modulo
 // the waves) into workgroup memory; workgroup 0 also stores the expert ids and router weights.
@@ -1253,9 +1323,15 @@ __device__ inline void expert_tasks(const ExpertParams& p, const DEC& lut_s) {
 // A pass's tasks once the decoder's table is in LDS.
 template <int MODE, int ARM, class CFG, bool FRAG, bool SPREAD, class DEC>
 __device__ inline void expert_pass(const ExpertParams& p, const DEC& dec) {
-  if constexpr (SPREAD && ARM == kArmGemv && GemvSplit<CFG>::kFits) {
-    if (p.ksplit > 1) {
-      __shared__ float part[GemvSplit<CFG>::kFloats];
+  if constexpr (ARM == kArmGemv && GemvSplit<CFG>::kFits && (SPREAD || MODE == kModeSingle)) {
+    __shared__ float part[GemvSplit<CFG>::kFloats];
+    if constexpr (MODE == kModeSingle) {
+      if (p.tok.out) {
+        gemv_token_tasks<CFG>(p, dec, part);
+        return;
+      }
+    }
+    if (SPREAD && p.ksplit > 1) {
       gemv_split_tasks<MODE, CFG>(p, dec, part);
       return;
     }

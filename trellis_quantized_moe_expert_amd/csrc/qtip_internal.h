@@ -57,6 +57,20 @@ struct SmallRoute {
   int32_t* n_units[2];
 };
 
+// The combine folded into the GEMV arm's down pass for a small batch (out NULL: the combine
+// kernel runs).  A workgroup task is one token's 16 NT output rows: wave j S + s takes the
+// token's pair j over input blocks [s K/S, (s+1) K/S) (S = ksplit), leaving its partial sums in
+// LDS; after a barrier the first wave adds them in ascending s, scales each pair's rows, and adds
+// the pairs weighted by their router weights in ascending j (the combine's order) into out.  The
+// fused pass then stores h by pair (ExpertParams::out_row_map = the binned order) rather than by
+// binned position.
+struct TokenCombine {
+  const int32_t* topk_idx;  // [n][k] expert of each pair (out of range: the pair is left out)
+  const float* topk_w;      // [n][k] router weights
+  void* out;                // [n][rows] bf16 or fp32
+  int32_t n, k, out_bf16;
+};
+
 // One pass of one (or two fused) trellis matrices over binned activation rows.
 struct ExpertParams {
   const uint8_t* codes0;        // [E][rows][cols/4]  gate (fused pass) or the single matrix
@@ -75,7 +89,8 @@ struct ExpertParams {
   int32_t n_pos;                // binned positions are [0, n_pos)
   int32_t n_act_rows;
   void* out;                    // fused: bf16 h [n_pos][rows]; single: fp32 y [n_out_rows][rows]
-  const int32_t* out_row_map;   // single pass: output row of position s = map[s] (NULL: s)
+  const int32_t* out_row_map;   // single pass, and the GEMV arm's fused pass: output row of position s = map[s]
+                                // (NULL: s)
   int32_t n_out_rows;
   int32_t n_xcd;                // workgroups are dispatched round-robin over this many XCDs (>= 1)
   const int32_t* unit_pad;      // grouped arm: each unit's start in the padded position space (every expert's
@@ -91,6 +106,7 @@ struct ExpertParams {
   int32_t ksplit;               // GEMV arm launched with fewer waves than its configuration's: waves
                                 // sharing one task's inputs (a power of 2 dividing cols/128), or <= 1
   SmallRoute route;             // GEMV arm, fused pass: the batch's routing, when logits is set
+  TokenCombine tok;             // GEMV arm, down pass: token tasks with the combine, when out is set
 };
 
 enum ExpertMode { kModeGateUp = 0, kModeSingle = 1 };
