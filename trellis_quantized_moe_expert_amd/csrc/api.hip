@@ -150,7 +150,7 @@ bool arch_is_supported(const char* name) { return name != nullptr && std::strncm
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t topk_idx, topk_w, counts, offsets, sorted_pair, tile_map, n_tiles, unit_map, n_units, h, y, router_part,
+  size_t topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos, tile_map, n_tiles, unit_map, n_units, h, y, router_part,
       dense_gate, dense_up, dense_down, padded_pair, unit_pad, n_pad, xs, total;
   size_t max_units;  // entries of each pass's unit map (and unit_pad)
 };
@@ -190,6 +190,7 @@ WsLayout ws_layout(const qtip_moe_desc& d, int32_t tile_m, int32_t n_tokens, boo
   L.counts = o;       o = align256(o + (size_t)d.num_experts * 4);
   L.offsets = o;      o = align256(o + ((size_t)d.num_experts + 1) * 4);
   L.sorted_pair = o;  o = align256(o + P * 4);
+  L.pair_pos = o;     o = align256(o + P * 4);  // token tasks: each pair's binned position
   L.tile_map = o;     o = align256(o + max_tiles * 12);
   L.n_tiles = o;      o = align256(o + 4);
   L.unit_map = o;     o = align256(o + 2 * max_units * 12);  // one unit map per expert pass
@@ -774,6 +775,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   int32_t* sorted_pair = reinterpret_cast<int32_t*>(ws + L.sorted_pair);
   int32_t* tile_map = reinterpret_cast<int32_t*>(ws + L.tile_map);
+  int32_t* pair_pos = reinterpret_cast<int32_t*>(ws + L.pair_pos);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + L.n_tiles);
   int32_t* unit_map = reinterpret_cast<int32_t*>(ws + L.unit_map);
   int32_t* n_units = reinterpret_cast<int32_t*>(ws + L.n_units);
@@ -920,7 +922,6 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     gu.act_frag = 1;
   }
   gu.ksplit = shape_gu.ksplit;
-  if (pp.tok_split) gu.out_row_map = sorted_pair;  // h by pair, as the token tasks read it
   if (choice.route_in_gate_up) {
     SmallRoute& r = gu.route;
     r.logits = lg;
@@ -930,6 +931,7 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
     r.topk_idx = topk_idx;
     r.topk_w = topk_w;
     r.sorted_pair = sorted_pair;
+    r.pair_pos = pp.tok_split ? pair_pos : nullptr;
     for (int i = 0; i < 2; ++i) {
       r.unit_pairs[i] = um.unit_pairs[i];
       r.units[i] = um.map[i];
@@ -966,9 +968,8 @@ qtip_status forward_impl(qtip_moe_plan_t plan, const qtip_moe_weights* w, const 
   }
   dn.ksplit = shape_dn.ksplit;
   if (pp.tok_split) {
-    // h was stored by pair (gu.out_row_map); the down pass adds each token's pairs into out
-    dn.act_row_map = nullptr;
-    dn.tok = TokenCombine{topk_idx, topk_w, out, n_tokens, d.top_k, d.out_dtype == QTIP_OUT_BF16 ? 1 : 0};
+    // the down pass adds each token's pairs into out; pair p's h row is its binned position
+    dn.tok = TokenCombine{topk_idx, topk_w, pair_pos, out, n_tokens, d.top_k, d.out_dtype == QTIP_OUT_BF16 ? 1 : 0};
   }
   e = launch_expert(kModeSingle, karm, kv_dn, plan->d.rung, dn, shape_dn.grid, shape_dn.waves, st);
   if (e != hipSuccess) return hip_fail(e, "down expert kernel launch");

@@ -317,9 +317,7 @@ __device__ inline int out_row(const ExpertParams& p, int s) {
   return (r >= 0 && r < p.n_out_rows) ? r : -1;
 }
 
-// BYPAIR (GEMV arm): the fused pass may store h by pair (out_row_map set) instead of by binned
-// position.
-template <int MODE, bool BYPAIR = false>
+template <int MODE>
 __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int r, int pi, float a0, float a1,
                                       float s0, float s1) {
   const int s = un.start + pi;
@@ -327,11 +325,7 @@ __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int
     const float g = a0 * s0, u = a1 * s1;
     const float h = silu(g) * u;
     size_t o;
-    if (BYPAIR && p.out_row_map) {
-      const int orow = out_row(p, s);
-      if (orow < 0) return;
-      o = (size_t)orow * p.rows + r;
-    } else if (p.unit_pad) {
+    if (p.unit_pad) {
       // h in fragment order over padded positions, as the down pass reads its A operand
       // (its input index r = kb*128 + 32g + 8st + t)
       const int pp = un.pad + pi;
@@ -952,7 +946,7 @@ __device__ inline void gemv_epilogue(const ExpertParams& p, const Unit& un, int 
         a1 += __shfl_xor(a1, 16, 64);
         a1 += __shfl_xor(a1, 32, 64);
       }
-      if (q < un.len && (q & 3) == g) epilogue_store<MODE, true>(p, un, r, q, a0, a1, s0, s1);
+      if (q < un.len && (q & 3) == g) epilogue_store<MODE>(p, un, r, q, a0, a1, s0, s1);
     }
   }
 }
@@ -1075,7 +1069,7 @@ __device__ inline void gemv_token_tasks(const ExpertParams& p, const DEC& lut, f
       const int pair = t * tc.k + j;
       const int e = __builtin_amdgcn_readfirstlane(tc.topk_idx[pair]);
       if (e >= 0 && e < p.num_experts) {
-        const Unit un{e, pair, 1, -1};
+        const Unit un{e, __builtin_amdgcn_readfirstlane(tc.pair_pos[pair]), 1, -1};
         gemv_part<kModeSingle, 1, NT, AP, X3>(p, lut, un, r0, lo, hi, mine);
       }
     }
@@ -1140,6 +1134,7 @@ __device__ inline void small_bin(const ExpertParams& p, const SmallRouteLds& rs)
   }
   if (lane == 0) *r.n_units[0] = __popcll(m0);
   if (blockIdx.x != 0) return;
+  if (r.pair_pos && lane < P) r.pair_pos[lane] = valid ? pos : -1;
   if (s1) {
     r.units[1][3 * u1 + 0] = e;
     r.units[1][3 * u1 + 1] = pos;

@@ -39,12 +39,12 @@ constexpr double kPackMinPairs = 16.0;
 
 // Routing and binning of a small GEMV-arm batch inside the fused gate/up launch (logits NULL: the
 // batch was routed and binned by the routing kernels).  Every workgroup of that launch routes the
-// batch while its table fill is in flight, bins the pairs, and stores the binned order and the
-// gate/up units it reads back (every workgroup stores the same values); workgroup 0 also stores
-// the expert ids, the router weights and the down pass's units, which the down pass and the
-// combine read.  (The per-expert counts, offsets and tile map, which no later launch of this arm
-// reads, are not stored.)  At most kSmallRouteMaxPairs pairs and kFusedRouteMaxTokens tokens; no
-// padded position space.
+// batch before its table fill, bins the pairs, and stores the binned order and the gate/up units
+// it reads back (every workgroup stores the same values); workgroup 0 also stores the expert ids,
+// the router weights, the down pass's units and, when asked, each pair's binned position, which
+// the down pass and the combine read.  (The per-expert counts, offsets and tile map, which no
+// later launch of this arm reads, are not stored.)  At most kSmallRouteMaxPairs pairs and
+// kFusedRouteMaxTokens tokens; no padded position space.
 constexpr int kSmallRouteMaxPairs = 64;
 struct SmallRoute {
   const float* logits;  // [n_part][n][E] partial sums added in ascending order, or NULL
@@ -52,6 +52,7 @@ struct SmallRoute {
   int32_t* topk_idx;
   float* topk_w;
   int32_t* sorted_pair;
+  int32_t* pair_pos;      // NULL, or [n][k]: the binned position of each pair (-1: left out), for TokenCombine
   int32_t unit_pairs[2];  // pairs per decode of the gate/up (0) and down (1) passes
   int32_t* units[2];      // their unit maps (expert, first binned position, pairs)
   int32_t* n_units[2];
@@ -59,14 +60,14 @@ struct SmallRoute {
 
 // The combine folded into the GEMV arm's down pass for a small batch (out NULL: the combine
 // kernel runs).  A workgroup task is one token's 16 NT output rows: wave j S + s takes the
-// token's pair j over input blocks [s K/S, (s+1) K/S) (S = ksplit), leaving its partial sums in
-// LDS; after a barrier the first wave adds them in ascending s, scales each pair's rows, and adds
-// the pairs weighted by their router weights in ascending j (the combine's order) into out.  The
-// fused pass then stores h by pair (ExpertParams::out_row_map = the binned order) rather than by
-// binned position.
+// token's pair j (its h row at the pair's binned position) over input blocks [s K/S, (s+1) K/S)
+// (S = ksplit), leaving its partial sums in LDS; after a barrier the first wave adds them in
+// ascending s, scales each pair's rows, and adds the pairs weighted by their router weights in
+// ascending j (the combine's order) into out.
 struct TokenCombine {
   const int32_t* topk_idx;  // [n][k] expert of each pair (out of range: the pair is left out)
   const float* topk_w;      // [n][k] router weights
+  const int32_t* pair_pos;  // [n][k] binned position of each pair (SmallRoute::pair_pos)
   void* out;                // [n][rows] bf16 or fp32
   int32_t n, k, out_bf16;
 };
@@ -89,8 +90,7 @@ struct ExpertParams {
   int32_t n_pos;                // binned positions are [0, n_pos)
   int32_t n_act_rows;
   void* out;                    // fused: bf16 h [n_pos][rows]; single: fp32 y [n_out_rows][rows]
-  const int32_t* out_row_map;   // single pass, and the GEMV arm's fused pass: output row of position s = map[s]
-                                // (NULL: s)
+  const int32_t* out_row_map;   // single pass: output row of position s = map[s] (NULL: s)
   int32_t n_out_rows;
   int32_t n_xcd;                // workgroups are dispatched round-robin over this many XCDs (>= 1)
   const int32_t* unit_pad;      // grouped arm: each unit's start in the padded position space (every expert's
