@@ -78,9 +78,10 @@ def decode_expert(inp, e: int, mode: str = "declared"):
     scales are applied after each dot product), float32(table) * float32(scale) in exact mode."""
     dec = _decoder(inp)
     if mode == "declared":
-        return tuple(dec.decode_declared(c[e], inp.lut) for c in (inp.codes_gate, inp.codes_up, inp.codes_down))
+        return tuple(dec.decode_declared(dec.stored_rows(c[e]), inp.lut)
+                     for c in (inp.codes_gate, inp.codes_up, inp.codes_down))
     if mode == "exact":
-        return tuple(dec.decode_exact(c[e], inp.lut, sc[e])
+        return tuple(dec.decode_exact(dec.stored_rows(c[e]), inp.lut, sc[e])
                      for c, sc in ((inp.codes_gate, inp.scale_gate), (inp.codes_up, inp.scale_up),
                                    (inp.codes_down, inp.scale_down)))
     raise ValueError(mode)
@@ -167,7 +168,8 @@ def dense_reference(inp, mode: str = "declared", out_dtype: str = "f32") -> np.n
         for j in range(k):
             e = int(idx[t, j])
             if e not in dense:
-                dense[e] = [_decoder(inp).dense_weights_bruteforce(c[e], inp.lut, sc[e], declared)
+                dec = _decoder(inp)
+                dense[e] = [dec.dense_weights_bruteforce(dec.stored_rows(c[e]), inp.lut, sc[e], declared)
                             for c, sc in ((inp.codes_gate, inp.scale_gate), (inp.codes_up, inp.scale_up),
                                           (inp.codes_down, inp.scale_down))]
             wg, wu, wd = dense[e]

@@ -110,6 +110,11 @@ def window_states(codes: np.ndarray) -> np.ndarray:
     return state
 
 
+def stored_rows(stored: np.ndarray) -> np.ndarray:
+    """The bitshift rung stores a matrix's rows one after another: the stored bytes are the rows."""
+    return np.asarray(stored, np.uint8)
+
+
 def lut_bf16(lut_f16: np.ndarray) -> np.ndarray:
     """The LUT narrowed to bf16 (fp16 -> exact fp32 -> bf16 nearest-even), as float64."""
     from .numerics import bf16_round

@@ -68,7 +68,7 @@ def test_matmul_decodes_an_integer_codebook_exactly(arm, rows, cols):
         q.qtip_expert_matmul(plan, arm, dev(codes), dev(scales.view(np.int16)), dev(cb.view(np.int16)), E, rows, cols,
                              dev(a_bits.view(np.int16)), len(picks), dev(units), 1, y)
         torch.cuda.synchronize()
-        w = lut_rung.decode_declared(codes[e], cb)
+        w = lut_rung.decode_declared(lut_rung.stored_rows(codes[e]), cb)
         assert np.array_equal(y.cpu().numpy(), w[:, picks].T.astype(np.float32)), e
     q.qtip_moe_plan_destroy(plan)
 
@@ -88,7 +88,7 @@ def test_dequantize_is_bit_exact(name, shape, experts):
             q.qtip_moe_dequantize(layer.plan, layer.w, m, e, out)
             torch.cuda.synchronize()
             got = out.cpu().numpy().view(np.uint16)
-            want = numerics.f64_to_bf16_bits(lut_rung.decode_declared(codes[e], inp.lut))
+            want = numerics.f64_to_bf16_bits(lut_rung.decode_declared(lut_rung.stored_rows(codes[e]), inp.lut))
             assert np.array_equal(got, want), (name, e, m)
     layer.close()
 

@@ -152,3 +152,22 @@ def test_planted_mutations_are_caught(name):
 
 def test_unmutated_model_passes_the_mutation_harness():
     assert _pins_hold(*_mut_states())
+
+
+def test_stored_rows_undoes_the_block_interleaved_storage():
+    """Brute force on small matrices: each row byte is placed by the stated formula, one at a time,
+    and stored_rows must give the rows back (a transposed axis or a wrong block size fails)."""
+    rng = np.random.default_rng(5)
+    for rows, cols in ((16, 128), (32, 256), (48, 384)):
+        nb = cols // 4
+        r_bytes = rng.integers(0, 256, size=(rows, nb), dtype=np.uint8)
+        flat = np.zeros(rows * nb, np.uint8)
+        for r in range(rows):
+            for c in range(nb):
+                k, cc = divmod(c, 32)
+                flat[((r // 16) * (cols // 128) + k) * 512 + (r % 16) * 32 + cc] = r_bytes[r, c]
+        assert np.array_equal(lut_rung.stored_rows(flat.reshape(rows, nb)), r_bytes), (rows, cols)
+    experts = rng.integers(0, 256, size=(3, 32, 64), dtype=np.uint8)
+    assert np.array_equal(lut_rung.stored_rows(experts)[1], lut_rung.stored_rows(experts[1]))
+    with pytest.raises(ValueError):
+        lut_rung.stored_rows(np.zeros((8, 32), np.uint8))

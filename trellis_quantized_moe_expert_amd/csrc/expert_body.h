@@ -192,7 +192,9 @@ struct RunCodes {
 
 // Codes are loaded transposed: lane 4r + c loads chunk c (8 bytes, plus its 4-byte look-ahead) of
 // row r of the task's 16-row block, so the four lanes of each quad read one row's consecutive
-// bytes (one or two cache lines per quad instead of four).  The MFMA operand layout wants chunk g
+// bytes, and with the LUT rung's block-interleaved layout a wave's 16 rows x 32 bytes of a block
+// are 512 contiguous bytes (four lines, instead of sixteen in a row-major layout).  The MFMA operand
+// layout wants chunk g
 // of row j in lane j + 16g; one cross-lane pull per dword (ds_bpermute: lane L reads lane
 // 4 (L % 16) + L / 16) moves the loaded dwords there before the decode.
 __device__ inline int code_row(int lane) { return lane >> 2; }
@@ -270,6 +272,31 @@ __device__ inline RunCodes load_run_wrapping(const uint8_t* __restrict__ base, u
   rc.d0 = v.x;
   rc.d1 = v.y;
   rc.la = *reinterpret_cast<const uint32_t*>(base + (row_off + (uint32_t)nx));
+  return rc;
+}
+
+// The LUT rung's codes are stored block-interleaved: the 16 rows x 32 bytes of one 16-row block
+// and one 128-input block lie together (512 bytes, blocks of a 16-row block consecutive), so a
+// wave's loads of a block touch four whole 128-byte lines.  Row r's bytes [32 kb, 32 kb + 32) sit
+// at byte ((r / 16) kblocks + kb) 512 + (r % 16) 32 of its matrix: row r's offset is
+// code_blk_row(r), block kb's kCodeBlk * kb.
+constexpr int kCodeBlk = 512;
+__device__ inline uint32_t code_blk_row(int r, int row_bytes) {
+  return (uint32_t)(r >> 4) * (16u * (uint32_t)row_bytes) + (uint32_t)(r & 15) * 32u;
+}
+
+// A run (chunk tc of block kb) in the block-interleaved layout: 8 bytes, and the look-ahead
+// dword, which is the next chunk's first dword, or for chunk 3 the first dword of block kb + 1
+// (of block 0 after the row's last block: the window is circular).
+__device__ inline RunCodes load_run_blk(const uint8_t* __restrict__ base, uint32_t row_off, int kb, int tc,
+                                        int kblocks) {
+  const uint32_t o = row_off + (uint32_t)(kb * kCodeBlk + tc * 8);
+  const uint32_t la = tc < 3 ? o + 8u : row_off + (uint32_t)((kb + 1 < kblocks ? kb + 1 : 0) * kCodeBlk);
+  const uint2 v = *reinterpret_cast<const uint2*>(base + o);
+  RunCodes rc;
+  rc.d0 = v.x;
+  rc.d1 = v.y;
+  rc.la = *reinterpret_cast<const uint32_t*>(base + la);
   return rc;
 }
 
@@ -467,6 +494,15 @@ __device__ inline RunSet<NT> load_runs(const uint8_t* __restrict__ base, uint32_
 }
 
 template <int NT>
+__device__ inline RunSet<NT> load_runs_blk(const uint8_t* __restrict__ base, uint32_t row_off0, uint32_t nt_stride,
+                                           int kb, int tc, int kblocks) {
+  RunSet<NT> rs;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run_blk(base, row_off0 + nt * nt_stride, kb, tc, kblocks);
+  return rs;
+}
+
+template <int NT>
 __device__ inline RunSet<NT> load_runs_wrapping(const uint8_t* __restrict__ base, uint32_t row_off0,
                                                 uint32_t nt_stride, int ob, int row_bytes) {
   RunSet<NT> rs;
@@ -578,9 +614,11 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
   const size_t mat_bytes = (size_t)p.rows * row_bytes;
   const uint8_t* base0 = p.codes0 + (size_t)un.e * mat_bytes;
   const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
-  // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
+  // this lane's code chunk and row: transposed for a pipelined decoder (LUT rung, block-interleaved
+  // codes), the MFMA layout otherwise
   const int tc = DEC::kPipelined ? code_chunk(lane) : g;
-  const uint32_t roff = (uint32_t)(r0 + (DEC::kPipelined ? code_row(lane) : j)) * (uint32_t)row_bytes;
+  const uint32_t roff = DEC::kPipelined ? code_blk_row(r0 + code_row(lane), row_bytes)
+                                        : (uint32_t)(r0 + j) * (uint32_t)row_bytes;
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
 
   uint32_t aoff[NS];  // A operand row i = lane%16 of each 16-pair block
@@ -673,7 +711,7 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
     const int la_addr = ((lane + 16) & 63) << 2;                   // lane j+16g reads lane j+16(g+1)
     u32x4 aA[NS][4], aB[NS][4];
     if (APRE) load_a<NS, FRAG>(aA, p.act, aoff, kblocks - 1);
-    const int ob_last = (kblocks - 1) * 32 + tc * 8;
+    const int ob_last = (kblocks - 1) * kCodeBlk + tc * 8;
     ChunkSet<NT> A0 = load_chunks<NT>(base0, roff, nt_stride, ob_last);
     ChunkSet<NT> A1 = (MODE == kModeGateUp) ? load_chunks<NT>(base1, roff, nt_stride, ob_last) : A0;
     uint32_t w0[NT], w1[NT];  // each row's first dword (every lane of its quad loads it)
@@ -696,7 +734,7 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
       constexpr bool FIRST = decltype(first)::value;
       const int kb = kblocks - 1 - s;
       const int kn = kb > 0 ? kb - 1 : 0;
-      const int ob = kn * 32 + tc * 8;
+      const int ob = kn * kCodeBlk + tc * 8;
       if (MODE == kModeGateUp) {
         // fused pass: the next block's codes go out first, pinned before this block's first wait
         // (left to itself the scheduler sinks them below the waits for this block's data); its
@@ -784,9 +822,11 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
   const size_t mat_bytes = (size_t)p.rows * row_bytes;
   const uint8_t* base0 = p.codes0 + (size_t)un.e * mat_bytes;
   const uint8_t* base1 = (MODE == kModeGateUp) ? p.codes1 + (size_t)un.e * mat_bytes : base0;
-  // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
+  // this lane's code chunk and row: transposed for a pipelined decoder (LUT rung, block-interleaved
+  // codes), the MFMA layout otherwise
   const int tc = DEC::kPipelined ? code_chunk(lane) : g;
-  const uint32_t roff = (uint32_t)(r0 + (DEC::kPipelined ? code_row(lane) : j)) * (uint32_t)row_bytes;
+  const uint32_t roff = DEC::kPipelined ? code_blk_row(r0 + code_row(lane), row_bytes)
+                                        : (uint32_t)(r0 + j) * (uint32_t)row_bytes;
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
   const bool wraps = kb_hi == kblocks;
   const int len = kb_hi - kb_lo;
@@ -862,31 +902,20 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
     u32x4 xA[NQ][4], xB[NQ][4];
     if (APRE) load_a_block<NQ>(xA, p.act, xoff, block_of(0));
     RunSet<NT> A0, A1, B0, B1;
-    if (wraps) {
-      const int ob_last = (kblocks - 1) * 32 + tc * 8;
-      A0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-      A1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : A0;
-    } else {
-      const int ob = kb_lo * 32 + tc * 8;
-      A0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob);
-      A1 = (MODE == kModeGateUp) ? load_runs<NT, false>(base1, roff, nt_stride, ob) : A0;
-    }
+    A0 = load_runs_blk<NT>(base0, roff, nt_stride, block_of(0), tc, kblocks);
+    A1 = (MODE == kModeGateUp) ? load_runs_blk<NT>(base1, roff, nt_stride, block_of(0), tc, kblocks) : A0;
     keep_apart(A0);
     if (MODE == kModeGateUp) keep_apart(A1);
     if (APRE) keep_apart<NQ>(xA);
     auto step = [&](int i, const RunSet<NT>& c0, const RunSet<NT>& c1, u32x4 (&x)[NQ][4], RunSet<NT>& n0,
                     RunSet<NT>& n1, u32x4 (&xnext)[NQ][4]) {
       const int kb = block_of(i);
-      // the next block; after the last, the range's first in-row block again (unused; 8 bytes
-      // back for lane group 3 where a one-block row would otherwise be left)
+      // the next block; after the last, the range's first in-row block again (unused)
       const int kn = i + 1 < len ? block_of(i + 1) : kb_lo;
       if (APRE) load_a_block<NQ>(xnext, p.act, xoff, kn);
       else load_a_block<NQ>(x, p.act, xoff, kb);
-      const int ob = kn * 32 + tc * 8;
-      const uint32_t back = (i + 1 < len || tc != 3 || kn + 1 < kblocks) ? 0u : 8u;
-      // one 12-byte load per run (chunk and look-ahead together): half the vector-memory instructions
-      n0 = load_runs<NT, true>(base0, roff, nt_stride, ob, back);
-      if (MODE == kModeGateUp) n1 = load_runs<NT, true>(base1, roff, nt_stride, ob, back);
+      n0 = load_runs_blk<NT>(base0, roff, nt_stride, kn, tc, kblocks);
+      if (MODE == kModeGateUp) n1 = load_runs_blk<NT>(base1, roff, nt_stride, kn, tc, kblocks);
       // the next block's loads stay ahead of this block's first wait (see task_grouped)
       __builtin_amdgcn_sched_barrier(0);
       const RunSet<NT> m0 = to_mfma_layout(c0);
@@ -1411,7 +1440,8 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
       uint16_t* out = (m ? q.out1 : q.out0) + slot * (size_t)q.out_expert_stride;
       // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
       const int tc = Dec::kPipelined ? code_chunk(lane) : g;
-      const uint32_t roff = (uint32_t)(r0 + (Dec::kPipelined ? code_row(lane) : j)) * (uint32_t)row_bytes;
+      const uint32_t roff = Dec::kPipelined ? code_blk_row(r0 + code_row(lane), row_bytes)
+                                            : (uint32_t)(r0 + j) * (uint32_t)row_bytes;
       if constexpr (!Dec::kPipelined) {
         RunCodes nx = load_run_wrapping(base, roff, (kblocks - 1) * 32 + tc * 8, row_bytes);
         for (int i = 0; i < kblocks; ++i) {
@@ -1433,11 +1463,11 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
         }
         continue;
       }
-      RunCodes cA = load_run_wrapping(base, roff, (kblocks - 1) * 32 + tc * 8, row_bytes), cB{};
+      RunCodes cA = load_run_blk(base, roff, kblocks - 1, tc, kblocks), cB{};
       keep_apart(cA);
       auto step = [&](int i, const RunCodes& rc, RunCodes& nx) {
         const int kb = block_at(i, kblocks);
-        if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + tc * 8);
+        if (i + 1 < kblocks) nx = load_run_blk(base, roff, i, tc, kblocks);
         const RunCodes mc = to_mfma_layout(rc);
         u32x4 w[4];
         dec.decode16(mc.d0, mc.d1, w[0], w[1]);
