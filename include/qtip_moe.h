@@ -94,10 +94,10 @@ enum { QTIP_SMALL_BATCH_FUSED = 0, QTIP_SMALL_BATCH_SEPARATE = 1 };
 #define QTIP_DECODE_REGIME_MAX_TOKENS 8
 /* The floor a plan uses by default (qtip_moe_desc.decode_floor = 0), per rung: re-derived for
  * these kernels on MI355X, where both arms are safe under graph capture.  The measured crossover
- * of the V4 layer lies between 7 and 8 tokens on the bitshift rung and between 5 and 6 on the LUT
- * rung (the grouped arm is faster from 8 and from 6). */
+ * of the V4 layer lies between 7 and 8 tokens on the bitshift rung and between 4 and 5 on the LUT
+ * rung (the grouped arm is faster from 8 and from 5). */
 #define QTIP_DEFAULT_DECODE_FLOOR_BITSHIFT 7
-#define QTIP_DEFAULT_DECODE_FLOOR_LUT 5
+#define QTIP_DEFAULT_DECODE_FLOOR_LUT 4
 /* Default m-tile height: the M of one bf16 MFMA (v_mfma_f32_16x16x32_bf16). */
 #define QTIP_DEFAULT_TILE_M 16
 /* The fill threshold re-derived for these kernels on MI355X.  The grouped arm decodes each

@@ -135,12 +135,12 @@ def test_mid_lut_layer_ragged_tiles(arm, n):
     check(got, moe.moe_forward(inp), "f32")
 
 
-def test_lut_decode_floor_switches_arms_at_six_tokens():
-    """The plan's default decode floor on this rung (5, a token count whatever the shape): 5 tokens
-    take the GEMV arm, 6 the grouped arm; both match the oracle token by token."""
-    inps = moe_inputs.make_inputs_multi(MID, [5, 6], seed=22)
-    layer = Layer(inps[5], out_dtype="f32", max_tokens=6)
-    for n, arm in ((5, q.QTIP_ARM_GEMV), (6, q.QTIP_ARM_GROUPED)):
+def test_lut_decode_floor_switches_arms_at_five_tokens():
+    """The plan's default decode floor on this rung (4, a token count whatever the shape): 4 tokens
+    take the GEMV arm, 5 the grouped arm; both match the oracle token by token."""
+    inps = moe_inputs.make_inputs_multi(MID, [4, 5], seed=22)
+    layer = Layer(inps[4], out_dtype="f32", max_tokens=5)
+    for n, arm in ((4, q.QTIP_ARM_GEMV), (5, q.QTIP_ARM_GROUPED)):
         say(f"LUT-rung forward V4 floor n={n}")
         got = layer.forward(inps[n])
         assert q.qtip_moe_stats(layer.plan)["last_arm"] == arm

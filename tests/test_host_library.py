@@ -120,8 +120,8 @@ def test_dequantize_argument_errors_return_before_any_launch():
 
 def test_default_dispatch_threshold_is_the_rederived_value():
     # one pair per woken expert and the measured floor of each rung: the grouped arm from 8 tokens
-    # (bitshift) and from 6 (LUT rung), the measured crossovers
-    for rung, floor in ((q.QTIP_RUNG_BITSHIFT, 7), (q.QTIP_RUNG_LUT, 5)):
+    # (bitshift) and from 5 (LUT rung), the measured crossovers
+    for rung, floor in ((q.QTIP_RUNG_BITSHIFT, 7), (q.QTIP_RUNG_LUT, 4)):
         plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, rung=rung), "gfx950")
         assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == floor + 1 == \
             fill.min_tokens_grouped(6, 256, 1, floor=floor)
@@ -130,7 +130,7 @@ def test_default_dispatch_threshold_is_the_rederived_value():
         line = q.qtip_moe_engaged_line(plan, 32)
         assert "threshold 1 pairs" in line and f"GEMV up to {floor} tokens" in line
         q.qtip_moe_plan_destroy(plan)
-    assert (q.QTIP_DEFAULT_DECODE_FLOOR_BITSHIFT, q.QTIP_DEFAULT_DECODE_FLOOR_LUT) == (7, 5)
+    assert (q.QTIP_DEFAULT_DECODE_FLOOR_BITSHIFT, q.QTIP_DEFAULT_DECODE_FLOOR_LUT) == (7, 4)
     # the pages' floor, 8, as a plan field
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, decode_floor=8), "gfx950")
     assert q.qtip_moe_plan_info(plan)["min_tokens_grouped"] == 9 == fill.min_tokens_grouped(6, 256, 1)
@@ -272,7 +272,7 @@ def test_default_kernel_shapes_follow_the_measured_rules():
 
 
 def test_lut_rung_default_kernel_shapes_follow_its_own_sweep():
-    # The LUT rung on the same V4 layer (GEMV up to 5 tokens, grouped from 6).  GEMV fused pass as on
+    # The LUT rung on the same V4 layer (GEMV up to 4 tokens, grouped from 5).  GEMV fused pass as on
     # the bitshift rung; GEMV down pass: 32-row tasks from 1536 of them (n >= 3).  Grouped fused
     # pass: 6 (12 waves, 32-row tasks) from 1.15 pairs per woken expert, 5 (8 waves, 64-row
     # tasks) from 8; grouped down pass: 7 (12 waves, 64-row tasks) throughout.

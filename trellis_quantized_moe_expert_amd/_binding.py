@@ -31,7 +31,7 @@ QTIP_ACT_FRAGMENTS = 2
 QTIP_OUT_BF16 = 0
 QTIP_OUT_F32 = 1
 QTIP_DEFAULT_DECODE_FLOOR_BITSHIFT = 7
-QTIP_DEFAULT_DECODE_FLOOR_LUT = 5
+QTIP_DEFAULT_DECODE_FLOOR_LUT = 4
 QTIP_DECODE_REGIME_MAX_TOKENS = 8
 QTIP_RUNG_BITSHIFT = 0
 QTIP_RUNG_LUT = 1
