@@ -39,16 +39,16 @@
  *  - A matrix with `rows` outputs and `cols` inputs is `rows` independent rows
  *    of cols/4 bytes.  Symbol c of a row = bits [2(c%4), 2(c%4)+2) of byte c/4; the row's
  *    stream bits are its bytes' bits, little-endian, read circularly.
+ *  - Storage: a matrix's rows x cols/4 bytes are stored block-interleaved, the 32 bytes of rows
+ *    16b..16b+15 for inputs [128k, 128k+128) together: byte 32k + c of row r (c < 32) is at
+ *    byte ((r/16) (cols/128) + k) 512 + (r%16) 32 + c of the matrix ([rows/16][cols/128][16][32];
+ *    a wave's loads of one block then cover four whole 128-byte lines).
  *  - Bitshift rung: the 16-bit state of weight (r, c) is the 8-symbol window starting at c:
  *    state = sum_j sym((c+j) mod cols) * 4^j; weight(r, c) = bf16(lut[state]) * scale[r], with
  *    lut the 65536-entry fp16 table.
  *  - LUT rung: weights come in pairs (2i, 2i+1); the pair's state is the 9 stream bits from bit
  *    4i on (the low 9 bits of the bitshift state of weight 2i), and the pair's two weights are
  *    bf16(cb[state][0]), bf16(cb[state][1]) times scale[r], with cb the 512 x 2 fp16 codebook.
- *    Its matrices are stored block-interleaved: the 32 bytes of rows 16b..16b+15 for inputs
- *    [128k, 128k+128) lie together, so byte 32k + c of row r (c < 32) is at byte
- *    ((r/16) (cols/128) + k) 512 + (r%16) 32 + c of the matrix (the same rows x cols/4 bytes;
- *    the bitshift rung stores rows one after another).
  *  - Either way the fp16 table value is rounded to bf16 (nearest-even), the dot product
  *    accumulates in fp32, and the fp16 per-output-row scale multiplies the fp32 sum.
  *  - Layer: h = silu(x Wg^T) * (x Wu^T) rounded to bf16; y = h Wd^T;
@@ -165,9 +165,9 @@ typedef struct qtip_moe_desc {
 typedef struct qtip_moe_plan_s* qtip_moe_plan_t;
 
 typedef struct qtip_moe_weights {
-  const uint8_t* codes_gate;  /* [E][I][H/4] packed 2-bit codes (LUT rung: [E][I/16][H/128][16][32]) */
-  const uint8_t* codes_up;    /* [E][I][H/4] (LUT rung: [E][I/16][H/128][16][32]) */
-  const uint8_t* codes_down;  /* [E][H][I/4] (LUT rung: [E][H/16][I/128][16][32]) */
+  const uint8_t* codes_gate;  /* [E][I][H/4] packed 2-bit codes, block-interleaved: [E][I/16][H/128][16][32] */
+  const uint8_t* codes_up;    /* [E][I][H/4], block-interleaved */
+  const uint8_t* codes_down;  /* [E][H][I/4], block-interleaved: [E][H/16][I/128][16][32] */
   const uint16_t* scale_gate; /* [E][I] fp16, one per output row */
   const uint16_t* scale_up;   /* [E][I] fp16 */
   const uint16_t* scale_down; /* [E][H] fp16 */
@@ -384,8 +384,8 @@ qtip_status qtip_moe_route(qtip_moe_plan_t plan, const float* logits, int32_t n_
  * be passed as it is; num_experts and n_rows_a bound the map's entries on the device.
  * For each unit u < n_units of unit_map [n_units][3] = (expert e, start s, len L):
  *   y[s+i][r] = scale[e][r] * sum_c a[s+i][c] * bf16(lut[state_e(r, c)])   (i < L, r < rows)
- *   codes [E][rows][cols/4] (the plan's rung: block-interleaved on the LUT rung, see the
- *   weight formats above), scales [E][rows] fp16, lut [65536] fp16 (LUT rung: [512][2] codebook),
+ *   codes [E][rows][cols/4] (block-interleaved, see the weight formats above; the plan's rung),
+ *   scales [E][rows] fp16, lut [65536] fp16 (LUT rung: [512][2] codebook),
  *   a [n_rows_a][cols] bf16, y [n_rows_a][rows] fp32.
  * `arm` is QTIP_ARM_GEMV or QTIP_ARM_GROUPED.  Constraints: rows % 16 == 0, cols % 128
  * == 0, n_rows_a x cols < 2^30, 1 <= L <= 64, 0 <= e < num_experts, 0 <= s, s + L <= n_rows_a.  A unit that

@@ -25,9 +25,9 @@ draws above do not change; with N(0,1) activations its logits are close to N(0,1
 
 Layers of the LUT rung (shape.rung == "lut") draw, in the LUT's place, a codebook of
 2**9 two-dimensional fp16 N(0,1) samples ([512, 2], carried in the `lut` field); the
-codes, scales, activations and logits are drawn exactly as for the bitshift rung (the code
-bytes are uniform random either way; that rung's kernels and oracle read them in its
-block-interleaved storage).
+codes, scales, activations and logits are drawn exactly as for the bitshift rung.  Code bytes
+are uniform random, so their storage order (block-interleaved, as the kernels and the oracle
+read them) does not change what is drawn.
 """
 from __future__ import annotations
 

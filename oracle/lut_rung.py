@@ -20,28 +20,20 @@ once, also documented with the C ABI):
   table, which is what sets the rung apart from the bitshift rung's 2**16-entry one).
 * Rounding as declared for the path: the fp16 codebook value is narrowed to bf16 (nearest-even),
   the dot product accumulates wide and the fp16 per-output-row scale multiplies it afterwards.
-* Storage (a layout, not part of the arithmetic): a matrix's rows x cols/4 bytes are stored
-  block-interleaved, the 32 bytes of 16 consecutive rows for 128 consecutive weights together:
-  byte 32k + c of row r sits at ((r // 16) * (cols // 128) + k) * 512 + (r % 16) * 32 + c.
-  stored_rows() turns stored bytes back into the rows above; every decode below takes rows.
+* Storage: the bitshift rung's block-interleaved layout (oracle.trellis.stored_rows, here
+  stored_rows too, turns stored bytes back into the rows above); every decode below takes rows.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from . import trellis
+
 LUT_RUNG_BITS = 9            # Q: codebook index bits
 STEP_BITS = 4                # bits a step consumes: 2 weights x 2 bits
 
 
-def stored_rows(stored: np.ndarray) -> np.ndarray:
-    """The rows [..., rows, cols/4] of matrices held in the block-interleaved storage (the same
-    number of bytes, in the same array shape): blocks [rows/16][cols/128][16 rows][32 bytes]."""
-    s = np.asarray(stored, np.uint8)
-    *lead, rows, nb = s.shape
-    if rows % 16 or nb % 32:
-        raise ValueError("LUT-rung matrices have rows % 16 == 0 and cols % 128 == 0")
-    b = s.reshape(*lead, rows // 16, nb // 32, 16, 32)
-    return np.ascontiguousarray(np.swapaxes(b, -3, -2)).reshape(*lead, rows, nb)
+stored_rows = trellis.stored_rows  # both rungs store their matrices the same way
 
 
 def pair_state_bruteforce(row_bytes, i: int, q: int = LUT_RUNG_BITS) -> int:

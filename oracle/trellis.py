@@ -18,6 +18,11 @@ C ABI) is:
 * The weight value is LUT[state] (a 65536-entry fp16 table) times a per-row
   fp16 scale.  In the path's declared rounding the LUT value is narrowed to bf16
   and the scale multiplies the fp32 dot product afterwards.
+* Storage (a layout, not part of the arithmetic; the pages give only "packed
+  2-bit bytes"): a matrix's rows x cols/4 bytes are stored block-interleaved, the
+  32 bytes of 16 consecutive rows for 128 consecutive inputs together (byte
+  32k + c of row r at ((r // 16) * (cols // 128) + k) * 512 + (r % 16) * 32 + c).
+  stored_rows() turns stored bytes back into rows; every decode below takes rows.
 """
 from __future__ import annotations
 
@@ -111,8 +116,17 @@ def window_states(codes: np.ndarray) -> np.ndarray:
 
 
 def stored_rows(stored: np.ndarray) -> np.ndarray:
-    """The bitshift rung stores a matrix's rows one after another: the stored bytes are the rows."""
-    return np.asarray(stored, np.uint8)
+    """The rows [..., rows, cols/4] of matrices held in the block-interleaved storage (the same
+    number of bytes, in the same array shape): blocks [rows/16][cols/128][16 rows][32 bytes], i.e.
+    byte 32k + c of row r sits at ((r // 16) * (cols // 128) + k) * 512 + (r % 16) * 32 + c.
+    The layout needs whole blocks; smaller test matrices whose sides are not multiples of 16 rows
+    and 128 inputs (shapes the library does not accept) are taken as stored row by row."""
+    s = np.asarray(stored, np.uint8)
+    *lead, rows, nb = s.shape
+    if rows % 16 or nb % 32:
+        return s
+    b = s.reshape(*lead, rows // 16, nb // 32, 16, 32)
+    return np.ascontiguousarray(np.swapaxes(b, -3, -2)).reshape(*lead, rows, nb)
 
 
 def lut_bf16(lut_f16: np.ndarray) -> np.ndarray:

@@ -47,7 +47,7 @@ def test_decode_bitexact_one_hot(arm, rows, cols):
     q.qtip_moe_plan_destroy(plan)
     got = y.cpu().numpy()
     for (ex, st, L) in units:
-        w = trellis.decode_declared(codes[ex], lut)            # [rows, cols]
+        w = trellis.decode_declared(trellis.stored_rows(codes[ex]), lut)  # [rows, cols]
         for i in range(L):
             expect = w[:, cols_hot[st + i]]
             assert np.array_equal(got[st + i], expect.astype(np.float32)), (ex, st + i, cols_hot[st + i])

@@ -30,7 +30,7 @@ def oracle_y(codes, scales, lut, a_bits, units, rows):
     y = np.full((P, rows), np.nan)
     a = numerics.bf16_bits_to_f64(a_bits)
     for (e, s, L) in units:
-        w = trellis.decode_declared(codes[e], lut)
+        w = trellis.decode_declared(trellis.stored_rows(codes[e]), lut)
         y[s:s + L] = (a[s:s + L] @ w.T) * scales[e].astype(np.float64)[None, :]
     return y
 

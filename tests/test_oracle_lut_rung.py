@@ -156,7 +156,9 @@ def test_unmutated_model_passes_the_mutation_harness():
 
 def test_stored_rows_undoes_the_block_interleaved_storage():
     """Brute force on small matrices: each row byte is placed by the stated formula, one at a time,
-    and stored_rows must give the rows back (a transposed axis or a wrong block size fails)."""
+    and stored_rows must give the rows back (a transposed axis or a wrong block size fails).  Both
+    rungs store their matrices this way."""
+    assert lut_rung.stored_rows is trellis.stored_rows
     rng = np.random.default_rng(5)
     for rows, cols in ((16, 128), (32, 256), (48, 384)):
         nb = cols // 4
@@ -169,5 +171,5 @@ def test_stored_rows_undoes_the_block_interleaved_storage():
         assert np.array_equal(lut_rung.stored_rows(flat.reshape(rows, nb)), r_bytes), (rows, cols)
     experts = rng.integers(0, 256, size=(3, 32, 64), dtype=np.uint8)
     assert np.array_equal(lut_rung.stored_rows(experts)[1], lut_rung.stored_rows(experts[1]))
-    with pytest.raises(ValueError):
-        lut_rung.stored_rows(np.zeros((8, 32), np.uint8))
+    odd = rng.integers(0, 256, size=(8, 32), dtype=np.uint8)  # not whole blocks: taken row by row
+    assert np.array_equal(lut_rung.stored_rows(odd), odd)

@@ -238,49 +238,15 @@ __device__ inline RunCodes chunk_to_mfma_layout(const RunChunk& t, uint32_t prev
   return r;
 }
 
-// Codes of one 32-symbol run: the run's 8 bytes and the 4 after them (its look-ahead).  `base`
-// is the (wave-uniform) start of the expert's matrix, `row_off` the lane's row offset in bytes;
-// 32-bit offsets keep the addresses in one VGPR each.  `back` (0 or 8) moves the load that many
-// bytes earlier, for a load whose data is never used and which must stay inside the row.  With X3 one
-// 12-byte load fetches all three dwords (half the vector-memory accesses of an 8-byte plus a
-// 4-byte load, at the cost of an aligned register triple: used where registers allow).
-template <bool X3>
-__device__ inline RunCodes load_run(const uint8_t* __restrict__ base, uint32_t row_off, int ob, uint32_t back = 0) {
-  const uint32_t o = row_off + (uint32_t)ob - back;
-  RunCodes rc;
-  if (X3) {
-    const uint3 v = *reinterpret_cast<const uint3*>(base + o);
-    rc.d0 = v.x;
-    rc.d1 = v.y;
-    rc.la = v.z;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(base + o);
-    rc.d0 = v.x;
-    rc.d1 = v.y;
-    rc.la = *reinterpret_cast<const uint32_t*>(base + (o + 8u));
-  }
-  return rc;
-}
-
-// The run of a row's last block: its look-ahead wraps to the row start (the window is circular).
-__device__ inline RunCodes load_run_wrapping(const uint8_t* __restrict__ base, uint32_t row_off, int ob,
-                                             int row_bytes) {
-  RunCodes rc;
-  const uint2 v = *reinterpret_cast<const uint2*>(base + (row_off + (uint32_t)ob));
-  int nx = ob + 8;
-  if (nx >= row_bytes) nx -= row_bytes;
-  rc.d0 = v.x;
-  rc.d1 = v.y;
-  rc.la = *reinterpret_cast<const uint32_t*>(base + (row_off + (uint32_t)nx));
-  return rc;
-}
-
-// The LUT rung's codes are stored block-interleaved: the 16 rows x 32 bytes of one 16-row block
-// and one 128-input block lie together (512 bytes, blocks of a 16-row block consecutive), so a
-// wave's loads of a block touch four whole 128-byte lines.  Row r's bytes [32 kb, 32 kb + 32) sit
-// at byte ((r / 16) kblocks + kb) 512 + (r % 16) 32 of its matrix: row r's offset is
-// code_blk_row(r), block kb's kCodeBlk * kb.
+// Codes are stored block-interleaved: the 16 rows x 32 bytes of one 16-row block and one
+// 128-input block lie together (512 bytes, the blocks of a 16-row block consecutive), so a wave's
+// loads of a block touch four whole 128-byte lines, each used once.  Row r's bytes [32 kb, 32 kb +
+// 32) sit at byte ((r / 16) kblocks + kb) 512 + (r % 16) 32 of its matrix: row r's offset is
+// code_blk_row(r), block kb's kCodeBlk * kb.  `base` is the (wave-uniform) start of the expert's
+// matrix; 32-bit offsets keep the addresses in one VGPR each.
 constexpr int kCodeBlk = 512;
+// Dequantize arm: blocks whose codes are requested together, ahead of the previous ones' stores.
+constexpr int kDqBatch = 4;
 __device__ inline uint32_t code_blk_row(int r, int row_bytes) {
   return (uint32_t)(r >> 4) * (16u * (uint32_t)row_bytes) + (uint32_t)(r & 15) * 32u;
 }
@@ -484,13 +450,13 @@ __device__ inline RunSet<NT> to_mfma_layout(const RunSet<NT>& t) {
   return r;
 }
 
-template <int NT, bool X3>
-__device__ inline RunSet<NT> load_runs(const uint8_t* __restrict__ base, uint32_t row_off0, uint32_t nt_stride, int ob,
-                                       uint32_t back = 0) {
-  RunSet<NT> rs;
+// The look-ahead dwords alone (see load_run_blk), for NT row blocks.
+template <int NT>
+__device__ inline void load_las_blk(uint32_t (&la)[NT], const uint8_t* __restrict__ base, uint32_t row_off0,
+                                    uint32_t nt_stride, int kb, int tc, int kblocks) {
+  const uint32_t o = tc < 3 ? (uint32_t)(kb * kCodeBlk + tc * 8 + 8) : (uint32_t)((kb + 1 < kblocks ? kb + 1 : 0) * kCodeBlk);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run<X3>(base, row_off0 + nt * nt_stride, ob, back);
-  return rs;
+  for (int nt = 0; nt < NT; ++nt) la[nt] = *reinterpret_cast<const uint32_t*>(base + (row_off0 + nt * nt_stride + o));
 }
 
 template <int NT>
@@ -502,20 +468,10 @@ __device__ inline RunSet<NT> load_runs_blk(const uint8_t* __restrict__ base, uin
   return rs;
 }
 
-template <int NT>
-__device__ inline RunSet<NT> load_runs_wrapping(const uint8_t* __restrict__ base, uint32_t row_off0,
-                                                uint32_t nt_stride, int ob, int row_bytes) {
-  RunSet<NT> rs;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) rs.c[nt] = load_run_wrapping(base, row_off0 + nt * nt_stride, ob, row_bytes);
-  return rs;
-}
-
-// Block order of a task (the bitshift rung's loops and the GEMV arm): a row's last 128-input
-// block first (the only one whose look-ahead wraps, loaded before the loop), then blocks 0, 1,
-// ..., kblocks-2, whose runs (8 + 4 or 12 bytes) stay inside the row.  Iteration i works on
-// block_at(i) and prefetches block_at(i + 1) = i; the last iteration's prefetch is not used
-// (block 0, moved 8 bytes back for lane group 3 so that it stays inside a one-block row).
+// Block order of a task (the bitshift rung's loops and the dequantize arm): a row's last 128-input
+// block first (the one whose look-ahead wraps to the row's first block, loaded before the loop),
+// then blocks 0, 1, ..., kblocks-2.  Iteration i works on block_at(i) and prefetches block_at(i +
+// 1) = i; the last iteration's prefetch (block 0) is not used.
 __device__ inline int block_at(int i, int kblocks) { return i == 0 ? kblocks - 1 : i - 1; }
 
 // Grouped and dequantize arms: scale and store one task's 16-pair x 16-row MFMA tiles.
@@ -553,6 +509,32 @@ __device__ inline int dense_slot(const int32_t* __restrict__ counts, int e) {
   return __builtin_amdgcn_readfirstlane(c);
 }
 
+// Number of experts with pairs (wave-uniform).
+__device__ inline int woken_count(const int32_t* __restrict__ counts, int E) {
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  for (int b = 0; b < E; b += 64) n += __popcll(__ballot(b + lane < E && counts[b + lane] > 0));
+  return __builtin_amdgcn_readfirstlane(n);
+}
+
+// The expert with pairs at slot s (the s-th in ascending expert order), or -1 past the last.
+__device__ inline int nth_woken(const int32_t* __restrict__ counts, int E, int s) {
+  const int lane = threadIdx.x & 63;
+  int below = 0;
+  for (int b = 0; b < E; b += 64) {
+    const bool v = b + lane < E && counts[b + lane] > 0;
+    const uint64_t m = __ballot(v);
+    const int pc = __popcll(m);
+    if (s < below + pc) {
+      const int before = __popcll(m & ((1ull << lane) - 1ull));  // woken lanes below this one
+      const uint64_t hit = __ballot(v && before == s - below);
+      return b + (int)__builtin_ctzll(hit);
+    }
+    below += pc;
+  }
+  return -1;
+}
+
 // Dequantize arm: the grouped pass over weights materialised beforehand as dense bf16 in
 // fragment order (no decode, no LUT): the B fragment of MFMA step st of block kb for row
 // block r0/16 + nt is one coalesced 16-byte load per lane.  Same K permutation as the decode.
@@ -585,7 +567,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const size_t o = dense_fragment_offset(rb0 + nt, kb, st, lane, kblocks);
+        const size_t o = dense_weight_offset(rb0 + nt, kb, st, lane, p.rows / 16);
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(w0 + o);
         const u32x4 b1 = (MODE == kModeGateUp) ? *reinterpret_cast<const u32x4*>(w1 + o) : b0;
 #pragma unroll
@@ -604,7 +586,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
 
 // Grouped arm: NS row blocks of 16 pairs x NT row blocks of 16 outputs share one decode of
 // the 16*NT rows; each A fragment feeds NT MFMAs.
-template <int MODE, int NS, int NT, bool APRE, bool X3 = false, bool FRAG = false, class DEC = DecoderBitshift>
+template <int MODE, int NS, int NT, bool APRE, bool FRAG = false, class DEC = DecoderBitshift>
 __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -617,8 +599,7 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
   // this lane's code chunk and row: transposed for a pipelined decoder (LUT rung, block-interleaved
   // codes), the MFMA layout otherwise
   const int tc = DEC::kPipelined ? code_chunk(lane) : g;
-  const uint32_t roff = DEC::kPipelined ? code_blk_row(r0 + code_row(lane), row_bytes)
-                                        : (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+  const uint32_t roff = code_blk_row(r0 + (DEC::kPipelined ? code_row(lane) : j), row_bytes);
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
 
   uint32_t aoff[NS];  // A operand row i = lane%16 of each 16-pair block
@@ -649,9 +630,8 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
     // block kb, so every wait in the loop is for loads issued a whole block earlier.
     u32x4 an[NS][4];
     if (APRE) load_a<NS, FRAG>(an, p.act, aoff, kblocks - 1);
-    const int ob_last = (kblocks - 1) * 32 + tc * 8;
-    RunSet<NT> n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-    RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
+    RunSet<NT> n0 = load_runs_blk<NT>(base0, roff, nt_stride, kblocks - 1, tc, kblocks);
+    RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_blk<NT>(base1, roff, nt_stride, kblocks - 1, tc, kblocks) : n0;
     for (int i = 0; i < kblocks; ++i) {
       const int kb = block_at(i, kblocks);
       const int kn = i + 1 < kblocks ? i : 0;  // block_at(i + 1); unused after the last block
@@ -667,10 +647,8 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
         load_a<NS, FRAG>(a, p.act, aoff, kb);
       }
       const RunSet<NT> c0 = n0, c1 = n1;
-      const int ob = kn * 32 + tc * 8;
-      const uint32_t back = (i + 1 < kblocks || tc != 3) ? 0u : 8u;
-      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
-      if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
+      n0 = load_runs_blk<NT>(base0, roff, nt_stride, kn, tc, kblocks);
+      if (MODE == kModeGateUp) n1 = load_runs_blk<NT>(base1, roff, nt_stride, kn, tc, kblocks);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -809,9 +787,8 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
 // GEMV arm body over the 128-input blocks [kb_lo, kb_hi) of a task (unit un, rows r0..): each
 // lane accumulates its row's dot products with the NQ pairs over its quarter of each block
 // into acc0 (gate or the single matrix) and acc1 (up).  A range holding the row's last block
-// takes it first (its look-ahead wraps to the row start), then blocks kb_lo.. in order; every
-// other block's run is one in-row load.
-template <int MODE, int NQ, int NT, bool APRE, bool X3, class DEC>
+// takes it first (its look-ahead wraps to the row start), then blocks kb_lo.. in order.
+template <int MODE, int NQ, int NT, bool APRE, bool DEEP, class DEC>
 __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const Unit& un, int r0, int kb_lo,
                                   int kb_hi, float (&acc0)[NQ][NT], float (&acc1)[NQ][NT]) {
   const int lane = threadIdx.x & 63;
@@ -825,8 +802,7 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
   // this lane's code chunk and row: transposed for a pipelined decoder (LUT rung, block-interleaved
   // codes), the MFMA layout otherwise
   const int tc = DEC::kPipelined ? code_chunk(lane) : g;
-  const uint32_t roff = DEC::kPipelined ? code_blk_row(r0 + code_row(lane), row_bytes)
-                                        : (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+  const uint32_t roff = code_blk_row(r0 + (DEC::kPipelined ? code_row(lane) : j), row_bytes);
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
   const bool wraps = kb_hi == kblocks;
   const int len = kb_hi - kb_lo;
@@ -841,23 +817,85 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
     for (int nt = 0; nt < NT; ++nt) acc0[q][nt] = acc1[q][nt] = 0.f;
   }
 
-  if constexpr (!DEC::kPipelined) {
+  if constexpr (!DEC::kPipelined && DEEP) {
+    // DEEP (where the registers allow): with the block-interleaved storage each block's codes lie
+    // in lines no earlier block read, and where a small launch leaves little work per block one
+    // block does not cover the memory round trip.  So the look-ahead dwords (the chunk-3 lanes'
+    // lie in the next block's lines) are loaded two blocks ahead, in two register sets (A for
+    // even iterations, B for odd), and bring in the lines the next block's chunks, loaded one
+    // block ahead, then read.  Past the range's end the loads re-read its first block (unused).
     u32x4 xn[NQ][4];
     if (APRE) load_a_block<NQ>(xn, p.act, xoff, block_of(0));
-    RunSet<NT> n0, n1;
-    if (wraps) {
-      const int ob_last = (kblocks - 1) * 32 + tc * 8;
-      n0 = load_runs_wrapping<NT>(base0, roff, nt_stride, ob_last, row_bytes);
-      n1 = (MODE == kModeGateUp) ? load_runs_wrapping<NT>(base1, roff, nt_stride, ob_last, row_bytes) : n0;
-    } else {
-      const int ob = kb_lo * 32 + tc * 8;
-      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob);
-      n1 = (MODE == kModeGateUp) ? load_runs<NT, false>(base1, roff, nt_stride, ob) : n0;
+    auto blk = [&](int i) { return i < len ? block_of(i) : kb_lo; };
+    ChunkSet<NT> n0 = load_chunks<NT>(base0, roff, nt_stride, blk(0) * kCodeBlk + tc * 8);
+    ChunkSet<NT> n1 = (MODE == kModeGateUp) ? load_chunks<NT>(base1, roff, nt_stride, blk(0) * kCodeBlk + tc * 8) : n0;
+    uint32_t lA0[NT], lA1[NT], lB0[NT], lB1[NT];
+    load_las_blk<NT>(lA0, base0, roff, nt_stride, blk(0), tc, kblocks);
+    load_las_blk<NT>(lB0, base0, roff, nt_stride, blk(1), tc, kblocks);
+    if (MODE == kModeGateUp) {
+      load_las_blk<NT>(lA1, base1, roff, nt_stride, blk(0), tc, kblocks);
+      load_las_blk<NT>(lB1, base1, roff, nt_stride, blk(1), tc, kblocks);
     }
+    auto step = [&](int i, uint32_t (&l0)[NT], uint32_t (&l1)[NT]) {
+      const int kb = block_of(i);
+      const int kn = blk(i + 1);
+      u32x4 x[NQ][4];
+      if (APRE) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) x[q][st] = xn[q][st];
+        }
+        load_a_block<NQ>(xn, p.act, xoff, kn);
+      } else {
+        load_a_block<NQ>(x, p.act, xoff, kb);
+      }
+      RunSet<NT> c0, c1;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        c0.c[nt] = RunCodes{n0.c[nt].d0, n0.c[nt].d1, l0[nt]};
+        if (MODE == kModeGateUp) c1.c[nt] = RunCodes{n1.c[nt].d0, n1.c[nt].d1, l1[nt]};
+      }
+      n0 = load_chunks<NT>(base0, roff, nt_stride, kn * kCodeBlk + tc * 8);
+      load_las_blk<NT>(l0, base0, roff, nt_stride, blk(i + 2), tc, kblocks);
+      if (MODE == kModeGateUp) {
+        n1 = load_chunks<NT>(base1, roff, nt_stride, kn * kCodeBlk + tc * 8);
+        load_las_blk<NT>(l1, base1, roff, nt_stride, blk(i + 2), tc, kblocks);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          u32x4 b0[2], b1[2];
+          const RunCodes& x0 = c0.c[nt];
+          lut.decode16(h ? x0.d1 : x0.d0, h ? x0.la : x0.d1, b0[0], b0[1]);
+          if (MODE == kModeGateUp) {
+            const RunCodes& x1 = c1.c[nt];
+            lut.decode16(h ? x1.d1 : x1.d0, h ? x1.la : x1.d1, b1[0], b1[1]);
+          }
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+              acc0[q][nt] = dot8(b0[hs], x[q][2 * h + hs], acc0[q][nt]);
+              if (MODE == kModeGateUp) acc1[q][nt] = dot8(b1[hs], x[q][2 * h + hs], acc1[q][nt]);
+            }
+          }
+        }
+      }
+    };
+    for (int i = 0; i < len; i += 2) {
+      step(i, lA0, lA1);
+      if (i + 1 < len) step(i + 1, lB0, lB1);
+    }
+  } else if constexpr (!DEC::kPipelined) {
+    u32x4 xn[NQ][4];
+    if (APRE) load_a_block<NQ>(xn, p.act, xoff, block_of(0));
+    RunSet<NT> n0 = load_runs_blk<NT>(base0, roff, nt_stride, block_of(0), tc, kblocks);
+    RunSet<NT> n1 = (MODE == kModeGateUp) ? load_runs_blk<NT>(base1, roff, nt_stride, block_of(0), tc, kblocks) : n0;
     for (int i = 0; i < len; ++i) {
       const int kb = block_of(i);
-      // the next block; after the last, the range's first in-row block again (unused; 8 bytes
-      // back for lane group 3 where a one-block row would otherwise be left)
+      // the next block; after the last, the range's first in-row block again (unused)
       const int kn = i + 1 < len ? block_of(i + 1) : kb_lo;
       u32x4 x[NQ][4];
       if (APRE) {
@@ -871,10 +909,8 @@ __device__ inline void gemv_range(const ExpertParams& p, const DEC& lut, const U
         load_a_block<NQ>(x, p.act, xoff, kb);
       }
       const RunSet<NT> c0 = n0, c1 = n1;
-      const int ob = kn * 32 + tc * 8;
-      const uint32_t back = (i + 1 < len || tc != 3 || kn + 1 < kblocks) ? 0u : 8u;
-      n0 = load_runs<NT, X3 && MODE == kModeSingle>(base0, roff, nt_stride, ob, back);
-      if (MODE == kModeGateUp) n1 = load_runs<NT, false>(base1, roff, nt_stride, ob, back);
+      n0 = load_runs_blk<NT>(base0, roff, nt_stride, kn, tc, kblocks);
+      if (MODE == kModeGateUp) n1 = load_runs_blk<NT>(base1, roff, nt_stride, kn, tc, kblocks);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -982,10 +1018,10 @@ __device__ inline void gemv_epilogue(const ExpertParams& p, const Unit& un, int 
 
 // GEMV arm: the NQ pairs of a unit chunk against 16*NT rows of its expert (the per-pair dot
 // products on the VALU, the decode in registers from the LDS LUT).
-template <int MODE, int NQ, int NT, bool APRE, bool X3 = false, class DEC = DecoderBitshift>
+template <int MODE, int NQ, int NT, bool APRE, bool DEEP = false, class DEC = DecoderBitshift>
 __device__ void task_gemv(const ExpertParams& p, const DEC& lut, const Unit& un, int r0) {
   float acc0[NQ][NT], acc1[NQ][NT];
-  gemv_range<MODE, NQ, NT, APRE, X3>(p, lut, un, r0, 0, p.cols / kKBlock, acc0, acc1);
+  gemv_range<MODE, NQ, NT, APRE, DEEP>(p, lut, un, r0, 0, p.cols / kKBlock, acc0, acc1);
   gemv_epilogue<MODE, NQ, NT>(p, un, r0, acc0, acc1);
 }
 
@@ -993,11 +1029,11 @@ __device__ void task_gemv(const ExpertParams& p, const DEC& lut, const Unit& un,
 // for launches with fewer tasks than the GPU has wave slots: wave s of a task's group decodes
 // blocks [s K/S, (s+1) K/S) and leaves its partial sums in LDS; after a barrier the group's first
 // wave adds the S partials in ascending s and stores the outputs.
-template <int MODE, int NQ, int NT, bool APRE, bool X3, class DEC>
+template <int MODE, int NQ, int NT, bool APRE, bool DEEP, class DEC>
 __device__ inline void gemv_part(const ExpertParams& p, const DEC& lut, const Unit& un, int r0, int kb_lo,
                                  int kb_hi, float* slot) {
   float acc0[NQ][NT], acc1[NQ][NT];
-  gemv_range<MODE, NQ, NT, APRE, X3>(p, lut, un, r0, kb_lo, kb_hi, acc0, acc1);
+  gemv_range<MODE, NQ, NT, APRE, DEEP>(p, lut, un, r0, kb_lo, kb_hi, acc0, acc1);
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -1080,7 +1116,6 @@ template <class CFG, class DEC>
 __device__ inline void gemv_token_tasks(const ExpertParams& p, const DEC& lut, float* part) {
   constexpr int NT = CFG::kNT;
   constexpr bool AP = CFG::kAPre;
-  constexpr bool X3 = CFG::kX3Down;
   constexpr int kSlot = GemvSplit<CFG>::kSlotFloats;
   const TokenCombine& tc = p.tok;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1099,7 +1134,7 @@ __device__ inline void gemv_token_tasks(const ExpertParams& p, const DEC& lut, f
       const int e = __builtin_amdgcn_readfirstlane(tc.topk_idx[pair]);
       if (e >= 0 && e < p.num_experts) {
         const Unit un{e, __builtin_amdgcn_readfirstlane(tc.pair_pos[pair]), 1, -1};
-        gemv_part<kModeSingle, 1, NT, AP, X3>(p, lut, un, r0, lo, hi, mine);
+        gemv_part<kModeSingle, 1, NT, AP, CFG::kDeepGemvDown>(p, lut, un, r0, lo, hi, mine);
       }
     }
     __syncthreads();
@@ -1184,9 +1219,11 @@ struct ExpertCfg {
   // shared by WAVES/4 waves (168 at 12 waves, where the 4-block task, or three 16-pair blocks
   // per decode, would spill).
   static constexpr bool kAPre = WAVES <= 8 || (NT <= 2 && NSUB <= 2);
-  // 12-byte code loads in the down pass: measured faster with 12 waves of 64-row tasks (fewer
-  // vector-memory accesses where they compete with the LUT gathers), slower with 16 waves.
-  static constexpr bool kX3Down = WAVES == 12 && NT == 4;
+  // GEMV arm: look-ahead dwords loaded two blocks ahead (gemv_range) where the registers allow it:
+  // the fused pass at 8 waves and 16 rows, the single-matrix pass up to 12 waves and 8 row-pair
+  // products per lane (larger tasks spill).
+  static constexpr bool kDeepGemvGateUp = WAVES <= 8 && NT == 1;
+  static constexpr bool kDeepGemvDown = NT == 1 || (WAVES <= 12 && NT * GPAIRS <= 8);
   // The fused grouped task of 64 rows x three 16-pair blocks would spill heavily at 12 waves;
   // that configuration serves the down pass only (the plan runs the fused pass as 32-row tasks).
   static constexpr bool kGroupedFused = !(NT == 4 && NSUB >= 3);
@@ -1217,12 +1254,11 @@ template <int MODE, class CFG, bool FRAG, class DEC>
 __device__ inline void grouped_blocks(const ExpertParams& p, const DEC& lut, const Unit& part, int r0) {
   constexpr int NT = CFG::kNT;
   constexpr bool AP = CFG::kAPre;
-  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
   switch ((part.len + 15) >> 4) {
-    case 1: task_grouped<MODE, 1, NT, AP, X3, FRAG>(p, lut, part, r0); break;
-    case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
-    case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
-    default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT, AP, X3, FRAG>(p, lut, part, r0); break;
+    case 1: task_grouped<MODE, 1, NT, AP, FRAG>(p, lut, part, r0); break;
+    case 2: if (CFG::kNSub >= 2) task_grouped<MODE, (CFG::kNSub >= 2 ? 2 : 1), NT, AP, FRAG>(p, lut, part, r0); break;
+    case 3: if (CFG::kNSub >= 3) task_grouped<MODE, (CFG::kNSub >= 3 ? 3 : 1), NT, AP, FRAG>(p, lut, part, r0); break;
+    default: if (CFG::kNSub >= 4) task_grouped<MODE, (CFG::kNSub >= 4 ? 4 : 1), NT, AP, FRAG>(p, lut, part, r0); break;
   }
 }
 
@@ -1233,8 +1269,8 @@ template <int MODE, int ARM, class CFG, bool FRAG, class DEC>
 __device__ inline void run_task(const ExpertParams& p, const DEC& lut, const Unit& un, int r0) {
   constexpr int NT = CFG::kNT;
   constexpr bool AP = CFG::kAPre;
-  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
   constexpr int kChunk = (ARM == kArmGemv) ? CFG::kGPairs : CFG::kNSub * 16;
+  constexpr bool DEEP = MODE == kModeSingle ? CFG::kDeepGemvDown : CFG::kDeepGemvGateUp;
   static_assert(CFG::kNSub >= 1 && CFG::kNSub <= 4 && CFG::kGPairs >= 1 && CFG::kGPairs <= 4, "config");
   for (int c0 = 0; c0 < un.len; c0 += kChunk) {
     const Unit part{un.e, un.start + c0, min(kChunk, un.len - c0), un.pad >= 0 ? un.pad + c0 : -1};
@@ -1249,10 +1285,10 @@ __device__ inline void run_task(const ExpertParams& p, const DEC& lut, const Uni
       grouped_blocks<MODE, CFG, FRAG>(p, lut, part, r0);
     } else {
       switch (part.len) {
-        case 1: task_gemv<MODE, 1, NT, AP, X3>(p, lut, part, r0); break;
-        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP, X3>(p, lut, part, r0); break;
-        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP, X3>(p, lut, part, r0); break;
-        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP, X3>(p, lut, part, r0); break;
+        case 1: task_gemv<MODE, 1, NT, AP, DEEP>(p, lut, part, r0); break;
+        case 2: if (CFG::kGPairs >= 2) task_gemv<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP, DEEP>(p, lut, part, r0); break;
+        case 3: if (CFG::kGPairs >= 3) task_gemv<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP, DEEP>(p, lut, part, r0); break;
+        default: if (CFG::kGPairs >= 4) task_gemv<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP, DEEP>(p, lut, part, r0); break;
       }
     }
   }
@@ -1264,8 +1300,8 @@ template <int MODE, class CFG, class DEC>
 __device__ inline void gemv_split_tasks(const ExpertParams& p, const DEC& lut, float* part) {
   constexpr int NT = CFG::kNT;
   constexpr bool AP = CFG::kAPre;
-  constexpr bool X3 = CFG::kX3Down && MODE == kModeSingle;
   constexpr int kSlot = GemvSplit<CFG>::kSlotFloats;
+  constexpr bool DEEP = MODE == kModeSingle ? CFG::kDeepGemvDown : CFG::kDeepGemvGateUp;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int S = p.ksplit, tpw = (int)(blockDim.x >> 6) / S;
   const int q = wave / S, sidx = wave % S;
@@ -1283,10 +1319,10 @@ __device__ inline void gemv_split_tasks(const ExpertParams& p, const DEC& lut, f
     const int lo = sidx * kper, hi = lo + kper;
     if (one) {
       switch (un.len) {
-        case 1: gemv_part<MODE, 1, NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
-        case 2: if (CFG::kGPairs >= 2) gemv_part<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
-        case 3: if (CFG::kGPairs >= 3) gemv_part<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
-        default: if (CFG::kGPairs >= 4) gemv_part<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP, X3>(p, lut, un, r0, lo, hi, mine); break;
+        case 1: gemv_part<MODE, 1, NT, AP, DEEP>(p, lut, un, r0, lo, hi, mine); break;
+        case 2: if (CFG::kGPairs >= 2) gemv_part<MODE, (CFG::kGPairs >= 2 ? 2 : 1), NT, AP, DEEP>(p, lut, un, r0, lo, hi, mine); break;
+        case 3: if (CFG::kGPairs >= 3) gemv_part<MODE, (CFG::kGPairs >= 3 ? 3 : 1), NT, AP, DEEP>(p, lut, un, r0, lo, hi, mine); break;
+        default: if (CFG::kGPairs >= 4) gemv_part<MODE, (CFG::kGPairs >= 4 ? 4 : 1), NT, AP, DEEP>(p, lut, un, r0, lo, hi, mine); break;
       }
     }
     __syncthreads();
@@ -1405,10 +1441,10 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
   }
 }
 
-// Dequantize-materialise: one wave task decodes 16 rows x all inputs of one matrix (two for
-// the fused gate/up pair) and stores bf16(LUT[state]), in row-major order or in the fragment
-// order of the dequantize arm's MFMA pass (there every store is 1 KiB contiguous per wave).
-// The next block's codes are requested before the current block is decoded.
+// Dequantize-materialise: one wave task decodes 16 rows x all inputs of one matrix and stores
+// bf16(LUT[state]), in row-major order or in the dense weight order of the dequantize arm's MFMA
+// pass (dense_weight_offset: every store 1 KiB contiguous per wave, neighbouring waves' stores
+// side by side), there as non-temporal stores (written once, read once by a later launch).
 template <int RUNG>
 __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantParams q) {
   __shared__ __attribute__((aligned(16))) uint16_t lut_s[RUNG == kRungLut ? 2 * kCodebookEntries * kCodebookCopies
@@ -1426,41 +1462,82 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
   const int kblocks = q.cols / kKBlock;
   const int nblocks = q.rows / 16;
   const int e_first = q.expert >= 0 ? q.expert : 0;
-  const long n_exp = q.expert >= 0 ? 1 : q.num_experts;
-  const long total = n_exp * nblocks;
+  // with counts, the tasks cover the woken experts only (slot s = the s-th woken expert), so that
+  // every wave gets the same share of them
+  const bool by_slot = q.expert < 0 && q.counts;
+  const long n_exp = q.expert >= 0 ? 1 : (by_slot ? woken_count(q.counts, q.num_experts) : q.num_experts);
+  // a task: one matrix's 16-row block (gate and up are separate tasks)
+  const int nmat = q.codes1 ? 2 : 1;
+  const long total = n_exp * nmat * nblocks;
   const size_t mat_bytes = (size_t)q.rows * row_bytes;
   for (long task = (long)blockIdx.x * kDequantWaves + wave; task < total; task += (long)gridDim.x * kDequantWaves) {
-    const int e = e_first + (int)(task / nblocks);
+    const int s = (int)(task / ((long)nmat * nblocks));
+    const int m = (int)((task / nblocks) % nmat);
+    const int e = by_slot ? nth_woken(q.counts, q.num_experts, s) : e_first + s;
     const int rb = (int)(task % nblocks);
     const int r0 = rb * 16;
-    if (q.expert < 0 && q.counts && __builtin_amdgcn_readfirstlane(q.counts[e]) <= 0) continue;
-    const size_t slot = q.counts ? (size_t)dense_slot(q.counts, e) : (size_t)e;
-    for (int m = 0; m < (q.codes1 ? 2 : 1); ++m) {
+    if (e < 0) continue;  // counts changed under the launch: not reached
+    const size_t slot = by_slot ? (size_t)s : (q.counts ? (size_t)dense_slot(q.counts, e) : (size_t)e);
+    {
       const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
       uint16_t* out = (m ? q.out1 : q.out0) + slot * (size_t)q.out_expert_stride;
       // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
       const int tc = Dec::kPipelined ? code_chunk(lane) : g;
-      const uint32_t roff = Dec::kPipelined ? code_blk_row(r0 + code_row(lane), row_bytes)
-                                            : (uint32_t)(r0 + j) * (uint32_t)row_bytes;
+      const uint32_t roff = code_blk_row(r0 + (Dec::kPipelined ? code_row(lane) : j), row_bytes);
       if constexpr (!Dec::kPipelined) {
-        RunCodes nx = load_run_wrapping(base, roff, (kblocks - 1) * 32 + tc * 8, row_bytes);
-        for (int i = 0; i < kblocks; ++i) {
-          const int kb = block_at(i, kblocks);
-          const RunCodes rc = nx;
-          if (i + 1 < kblocks) nx = load_run<true>(base, roff, i * 32 + tc * 8);
-          u32x4 w[4];
-          dec.decode16(rc.d0, rc.d1, w[0], w[1]);
-          dec.decode16(rc.d1, rc.la, w[2], w[3]);
-          if (q.fragment_order) {
+        auto rows = [&](auto frag) {
+          constexpr bool FRAG = decltype(frag)::value;
+          auto store_block = [&](const RunCodes& c, int kb) {
+            u32x4 w[4];
+            dec.decode16(c.d0, c.d1, w[0], w[1]);
+            dec.decode16(c.d1, c.la, w[2], w[3]);
+            if constexpr (FRAG) {
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-              *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
-          } else {
-            uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
+              for (int st = 0; st < 4; ++st)
+                __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_weight_offset(rb, kb, st, lane, nblocks)));
+            } else {
+              uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
 #pragma unroll
-            for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+              for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+            }
+          };
+          constexpr int B = kDqBatch;
+          if (kblocks % (4 * B) != 0) {
+            RunCodes nx = load_run_blk(base, roff, kblocks - 1, tc, kblocks);
+            for (int i = 0; i < kblocks; ++i) {
+              const RunCodes rc = nx;
+              if (i + 1 < kblocks) nx = load_run_blk(base, roff, i, tc, kblocks);
+              store_block(rc, block_at(i, kblocks));
+            }
+            return;
           }
-        }
+          // One counter covers loads and stores, so a wait for codes also waits for every store
+          // issued before their load.  Batches of B blocks in two register sets: the next
+          // batch's codes are requested before this batch's stores, so a store is waited for a
+          // batch later, not on the next block.  Four batches per iteration: at the loop head
+          // the compiler's wait covers the previous batch's stores too.  (The last batch's loads
+          // re-read the row's first blocks, unused.)
+          auto load_batch = [&](RunCodes (&c)[B], int i0) {
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+              c[b] = load_run_blk(base, roff, block_at(i0 + b < kblocks ? i0 + b : 0, kblocks), tc, kblocks);
+          };
+          RunCodes cA[B], cB[B];
+          load_batch(cA, 0);
+          for (int i = 0; i < kblocks; i += 4 * B) {
+#pragma unroll
+            for (int h = 0; h < 4; h += 2) {
+              load_batch(cB, i + (h + 1) * B);
+#pragma unroll
+              for (int b = 0; b < B; ++b) store_block(cA[b], block_at(i + h * B + b, kblocks));
+              load_batch(cA, i + (h + 2) * B);
+#pragma unroll
+              for (int b = 0; b < B; ++b) store_block(cB[b], block_at(i + (h + 1) * B + b, kblocks));
+            }
+          }
+        };
+        if (q.fragment_order) rows(std::true_type{});
+        else rows(std::false_type{});
         continue;
       }
       RunCodes cA = load_run_blk(base, roff, kblocks - 1, tc, kblocks), cB{};
@@ -1475,7 +1552,7 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
         if (q.fragment_order) {
 #pragma unroll
           for (int st = 0; st < 4; ++st)
-            *reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)) = w[st];
+            __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_weight_offset(rb, kb, st, lane, nblocks)));
         } else {
           uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
 #pragma unroll
