@@ -567,7 +567,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const size_t o = dense_weight_offset(rb0 + nt, kb, st, lane, p.rows / 16);
+        const size_t o = dense_fragment_offset(rb0 + nt, kb, st, lane, kblocks);
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(w0 + o);
         const u32x4 b1 = (MODE == kModeGateUp) ? *reinterpret_cast<const u32x4*>(w1 + o) : b0;
 #pragma unroll
@@ -1442,9 +1442,9 @@ __global__ __launch_bounds__(CFG::kWaves * 64, 1) void expert_kernel(ExpertParam
 }
 
 // Dequantize-materialise: one wave task decodes 16 rows x all inputs of one matrix and stores
-// bf16(LUT[state]), in row-major order or in the dense weight order of the dequantize arm's MFMA
-// pass (dense_weight_offset: every store 1 KiB contiguous per wave, neighbouring waves' stores
-// side by side), there as non-temporal stores (written once, read once by a later launch).
+// bf16(LUT[state]), in row-major order or in the fragment order of the dequantize arm's MFMA
+// pass (every store 1 KiB contiguous per wave), there as non-temporal stores (written once, read
+// once by a later launch).
 template <int RUNG>
 __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantParams q) {
   __shared__ __attribute__((aligned(16))) uint16_t lut_s[RUNG == kRungLut ? 2 * kCodebookEntries * kCodebookCopies
@@ -1494,7 +1494,7 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
             if constexpr (FRAG) {
 #pragma unroll
               for (int st = 0; st < 4; ++st)
-                __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_weight_offset(rb, kb, st, lane, nblocks)));
+                __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)));
             } else {
               uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
 #pragma unroll
@@ -1552,7 +1552,7 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
         if (q.fragment_order) {
 #pragma unroll
           for (int st = 0; st < 4; ++st)
-            __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_weight_offset(rb, kb, st, lane, nblocks)));
+            __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)));
         } else {
           uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
 #pragma unroll

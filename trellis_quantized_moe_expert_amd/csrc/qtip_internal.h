@@ -152,12 +152,6 @@ struct DequantParams {
 __host__ __device__ inline size_t dense_fragment_offset(int rb, int kb, int st, int lane, int kblocks) {
   return ((((size_t)rb * kblocks + kb) * 4 + st) * 64 + lane) * 8;
 }
-// The dequantize arm's dense weights: the same 1 KiB fragments with the 128-input block outermost,
-// so that the row blocks which neighbouring waves write (and later read) at one time lie side by
-// side in memory.
-__host__ __device__ inline size_t dense_weight_offset(int rb, int kb, int st, int lane, int rblocks) {
-  return ((((size_t)kb * rblocks + rb) * 4 + st) * 64 + lane) * 8;
-}
 hipError_t launch_dequant(const DequantParams& q, int rung, int grid, hipStream_t stream);
 hipError_t launch_dequant_lut(const DequantParams& q, int grid, hipStream_t stream);
 constexpr int kDequantWaves = 16;
