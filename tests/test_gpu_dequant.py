@@ -88,6 +88,27 @@ def test_mid_layer_on_the_dequantize_arm_ragged(n):
     say(f"  {st}")
 
 
+WIDE = moe_inputs.MoEShape(num_experts=150, top_k=4, hidden=256, inter=128, n_tokens=40)
+
+
+@pytest.mark.parametrize("n", [3, 40])
+def test_dequantize_arm_over_a_wide_router(n):
+    """150 experts: the woken ones spread over three 64-expert chunks, the last one partly past E.
+    The materialise tasks cover the woken experts only (slot s is the s-th woken expert), so a wrong
+    slot-to-expert walk would put another expert's weights under a pair."""
+    inp = moe_inputs.make_inputs(WIDE, seed=5, n_tokens=n)
+    ref = moe.moe_forward(inp)
+    woken = np.flatnonzero(ref["bins"]["counts"] > 0)
+    say(f"dequantize arm E=150 n={n}: {woken.size} woken, first {woken[0]}, last {woken[-1]}")
+    layer = dequant_layer(inp, max_tokens=n)
+    got = layer.forward(inp)
+    st = q.qtip_moe_stats(layer.plan)
+    layer.close()
+    # two materialise launches and the two dense expert passes
+    assert st["last_arm"] == q.QTIP_ARM_DEQUANT and st["dequant_launches"] == 4
+    check(got, ref, "f32")
+
+
 def test_automatic_dispatch_inside_a_dequantize_window():
     # grouped threshold 8 with traffic ratio 4 on the mid shape (top-4 of 16) opens a window
     shape = MID
