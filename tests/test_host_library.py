@@ -259,15 +259,21 @@ def test_schedule_reports_what_a_forward_launches():
 
 def test_default_kernel_shapes_follow_the_measured_rules():
     # V4 layer (E=256, k=6; 6, 11.9 and 23.2 woken experts at n = 1, 2, 4; grouped from 8).  GEMV fused
-    # pass: 8 waves below 5 16-row tasks per CU, 16 waves from there, 32-row tasks once
-    # woken*rows/32 >= 2048 wave slots; GEMV down pass: 16 waves up to 6144 32-row tasks.  Grouped
+    # pass: 12 waves of 16-row tasks below 14000 32-row tasks (n <= 64), 8 waves of 32-row tasks
+    # from there; GEMV down pass: 16 waves up to 6144 32-row tasks.  Grouped
     # picks by pairs per woken expert (1.41 at n=32, 3.15 at 128, 6.0 at 256, 12.0 at 512, 24.0 at
     # 1024).
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4), "gfx950")
-    want = {1: (2, 1), 2: (1, 1), 4: (1, 1), 8: (1, 3), 32: (1, 3), 128: (1, 7), 256: (9, 10), 512: (9, 10), 1024: (9, 10)}
+    want = {1: (11, 1), 2: (11, 1), 4: (11, 1), 8: (1, 3), 32: (1, 3), 128: (1, 7), 256: (9, 10), 512: (9, 10), 1024: (9, 10)}
     for n, (gu, dn) in want.items():
         s = q.qtip_moe_plan_schedule(plan, n)
         assert (s["gate_up"]["variant"], s["down"]["variant"]) == (gu, dn), n
+    q.qtip_moe_plan_destroy(plan)
+    # the GEMV arm forced past the floor: 12-wave 16-row tasks through n=64 (199.8 woken experts,
+    # 12787 32-row tasks), 8-wave 32-row tasks from n=128 (243.8 woken, 15603)
+    plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, arm_override=q.QTIP_ARM_GEMV), "gfx950")
+    for n, gu in {16: 11, 64: 11, 128: 4, 1024: 4}.items():
+        assert q.qtip_moe_plan_schedule(plan, n)["gate_up"]["variant"] == gu, n
     q.qtip_moe_plan_destroy(plan)
 
 

@@ -72,12 +72,11 @@ namespace {
 //    and an expert with up to 48 pairs is decoded once).  Down pass: 16 waves of 32-row tasks
 //    below 3, 12 waves of 64-row tasks with 12-byte code loads from 3, sharing a decode across
 //    three 16-pair blocks from 4.
-//  * GEMV arm, by the expected task count.  Fused pass: 8-wave workgroups of 16-row tasks
-//    while a 256-CU launch has fewer than 5 of them per CU (each task's inputs then split over
-//    two waves), 16-wave workgroups of 16-row tasks from there (their inputs split over two
-//    waves where the tasks are few), and 8 waves of 32-row tasks once those give each of the
-//    2048 wave slots of a 256-CU, 8-wave launch one.  Down pass: 16-wave workgroups of 16-row
-//    tasks up to 6144 32-row tasks (every measured batch of 1 to 8 tokens), 32-row tasks beyond.
+//  * GEMV arm, by the expected task count.  Fused pass: 12-wave workgroups of 16-row tasks
+//    (inputs split over several waves where the tasks are few) below 14000 32-row tasks
+//    (n <= 64 on the V4 layer: 1-11 % ahead of the 8- and 16-wave shapes), 8 waves of 32-row
+//    tasks from there.  Down pass: 16-wave workgroups of 16-row tasks up to 6144 32-row tasks
+//    (every measured batch of 1 to 8 tokens), 32-row tasks beyond.
 // The LUT rung's decode reads one 4-byte codebook entry per two weights, so its passes are
 // bound by the vector-memory path (activation fragments above all) rather than by LDS gathers;
 // taller tasks, which feed each fragment to more MFMAs, pay there (bench.py --sweep-rung lut
@@ -86,8 +85,11 @@ namespace {
 //    waves of 32-row tasks below 8, 8 waves of 64-row tasks from 8.  Down pass: 12 waves of
 //    64-row tasks (two 16-pair blocks per decode) throughout (level with three blocks per
 //    decode at n = 1024, ahead below).
-//  * GEMV arm.  Fused pass as on the bitshift rung; down pass: 16-wave workgroups of 16-row
-//    tasks below 1536 32-row tasks (batches of one and two tokens), of 32-row tasks from there.
+//  * GEMV arm.  Fused pass: 8-wave workgroups of 16-row tasks while a 256-CU launch has fewer
+//    than 5 of them per CU (each task's inputs then split over two waves), 16-wave workgroups of
+//    16-row tasks from there, and 8 waves of 32-row tasks once those give each of the 2048 wave
+//    slots of a 256-CU, 8-wave launch one; down pass: 16-wave workgroups of 16-row tasks below
+//    1536 32-row tasks (batches of one and two tokens), of 32-row tasks from there.
 int kernel_arm(int32_t arm) {
   return arm == QTIP_ARM_GROUPED ? kArmGrouped : (arm == QTIP_ARM_DEQUANT ? kArmDense : kArmGemv);
 }
@@ -110,6 +112,7 @@ int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_to
       if (lut) return tall_tasks < 1536.0 ? 1 : 3;
       return tall_tasks < 6144.0 ? 1 : 4;
     }
+    if (!lut) return tall_tasks < 14000.0 ? 11 : 4;
     if (tall_tasks >= 2048.0) return 4;
     return woken * rows / 16.0 >= 5.0 * 256.0 ? 1 : 2;
   }

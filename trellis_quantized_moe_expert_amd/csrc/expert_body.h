@@ -1222,7 +1222,7 @@ struct ExpertCfg {
   // GEMV arm: look-ahead dwords loaded two blocks ahead (gemv_range) where the registers allow it:
   // the fused pass at 8 waves and 16 rows, the single-matrix pass up to 12 waves and 8 row-pair
   // products per lane (larger tasks spill).
-  static constexpr bool kDeepGemvGateUp = WAVES <= 8 && NT == 1;
+  static constexpr bool kDeepGemvGateUp = WAVES <= 12 && NT == 1;
   static constexpr bool kDeepGemvDown = NT == 1 || (WAVES <= 12 && NT * GPAIRS <= 8);
   // The fused grouped task of 64 rows x three 16-pair blocks would spill heavily at 12 waves;
   // that configuration serves the down pass only (the plan runs the fused pass as 32-row tasks).
