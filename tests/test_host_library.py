@@ -278,12 +278,13 @@ def test_default_kernel_shapes_follow_the_measured_rules():
 
 
 def test_lut_rung_default_kernel_shapes_follow_its_own_sweep():
-    # The LUT rung on the same V4 layer (GEMV up to 4 tokens, grouped from 5).  GEMV fused pass as on
-    # the bitshift rung; GEMV down pass: 32-row tasks from 1536 of them (n >= 3).  Grouped fused
+    # The LUT rung on the same V4 layer (GEMV up to 4 tokens, grouped from 5).  GEMV fused pass: 12
+    # waves of 16-row tasks below 5 of them per CU (n=1), 16 waves from there; GEMV down pass: 32-row
+    # tasks from 1536 of them (n >= 3).  Grouped fused
     # pass: 6 (12 waves, 32-row tasks) from 1.15 pairs per woken expert, 5 (8 waves, 64-row
     # tasks) from 8; grouped down pass: 7 (12 waves, 64-row tasks) throughout.
     plan = q.qtip_moe_plan_for_arch(q.make_desc(**V4, rung=q.QTIP_RUNG_LUT), "gfx950")
-    want = {1: (2, 1), 2: (1, 1), 4: (1, 3), 8: (1, 7), 16: (6, 7), 32: (6, 7), 128: (6, 7), 256: (6, 7),
+    want = {1: (11, 1), 2: (1, 1), 4: (1, 3), 8: (1, 7), 16: (6, 7), 32: (6, 7), 128: (6, 7), 256: (6, 7),
             512: (5, 7), 1024: (5, 7)}
     for n, (gu, dn) in want.items():
         s = q.qtip_moe_plan_schedule(plan, n)

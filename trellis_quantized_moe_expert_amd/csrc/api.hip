@@ -85,10 +85,11 @@ namespace {
 //    waves of 32-row tasks below 8, 8 waves of 64-row tasks from 8.  Down pass: 12 waves of
 //    64-row tasks (two 16-pair blocks per decode) throughout (level with three blocks per
 //    decode at n = 1024, ahead below).
-//  * GEMV arm.  Fused pass: 8-wave workgroups of 16-row tasks while a 256-CU launch has fewer
-//    than 5 of them per CU (each task's inputs then split over two waves), 16-wave workgroups of
-//    16-row tasks from there, and 8 waves of 32-row tasks once those give each of the 2048 wave
-//    slots of a 256-CU, 8-wave launch one; down pass: 16-wave workgroups of 16-row tasks below
+//  * GEMV arm.  Fused pass: 12-wave workgroups of 16-row tasks while a 256-CU launch has fewer
+//    than 5 of them per CU (their inputs split over several waves; n=1 24 against 27 us with
+//    8 waves), 16-wave workgroups of 16-row tasks from there, and 8 waves of 32-row tasks once
+//    those give each of the 2048 wave slots of a 256-CU, 8-wave launch one; down pass: 16-wave
+//    workgroups of 16-row tasks below
 //    1536 32-row tasks (batches of one and two tokens), of 32-row tasks from there.
 int kernel_arm(int32_t arm) {
   return arm == QTIP_ARM_GROUPED ? kArmGrouped : (arm == QTIP_ARM_DEQUANT ? kArmDense : kArmGemv);
@@ -114,7 +115,7 @@ int resolve_variant(const qtip_moe_plan_s* plan, int arm, int mode, int32_t n_to
     }
     if (!lut) return tall_tasks < 14000.0 ? 11 : 4;
     if (tall_tasks >= 2048.0) return 4;
-    return woken * rows / 16.0 >= 5.0 * 256.0 ? 1 : 2;
+    return woken * rows / 16.0 >= 5.0 * 256.0 ? 1 : 11;
   }
   const double ppe = fill_pairs_per_woken_expert(n, k, E);
   if (lut) {
