@@ -312,7 +312,7 @@ __device__ inline int out_row(const ExpertParams& p, int s) {
 
 template <int MODE>
 __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int r, int pi, float a0, float a1,
-                                      float s0, float s1) {
+                                      float s0, float s1, int orow) {
   const int s = un.start + pi;
   if (MODE == kModeGateUp) {
     const float g = a0 * s0, u = a1 * s1;
@@ -328,7 +328,7 @@ __device__ inline void epilogue_store(const ExpertParams& p, const Unit& un, int
     }
     reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_to_bf16_bits(h);
   } else {
-    const int orow = out_row(p, s);
+    // orow: out_row(p, s), loaded when the task started
     if (orow >= 0) reinterpret_cast<float*>(p.out)[(size_t)orow * p.rows + r] = a0 * s0;
   }
 }
@@ -475,23 +475,46 @@ __device__ inline RunSet<NT> load_runs_blk(const uint8_t* __restrict__ base, uin
 __device__ inline int block_at(int i, int kblocks) { return i == 0 ? kblocks - 1 : i - 1; }
 
 // Grouped and dequantize arms: scale and store one task's 16-pair x 16-row MFMA tiles.
+// What a task's epilogue reads from memory, requested when the task starts so that the loads
+// are not a round trip of their own after the last block: lane i holds the scale(s) of the
+// task's row r0 + i (i < 16 NT <= 64) and, in the single-matrix pass, the output row of the
+// unit's pair i (i < len <= 64); the epilogue moves them across lanes.
+struct EpiPre {
+  float s0, s1;
+  int orow;
+};
+
+template <int MODE, int NT>
+__device__ inline EpiPre epilogue_prefetch(const ExpertParams& p, const Unit& un, int r0) {
+  const int lane = threadIdx.x & 63;
+  EpiPre e{0.f, 0.f, -1};
+  if (lane < 16 * NT) {
+    const size_t o = (size_t)un.e * p.rows + r0 + lane;
+    e.s0 = f16_to_f32(p.scale0[o]);
+    if (MODE == kModeGateUp) e.s1 = f16_to_f32(p.scale1[o]);
+  }
+  if (MODE == kModeSingle && lane < un.len) e.orow = out_row(p, un.start + lane);
+  return e;
+}
+
 // D layout: lane holds rows 4*(lane/16)+t (pairs) of column lane%16 (output row).
 template <int MODE, int NS, int NT>
 __device__ inline void grouped_epilogue(const ExpertParams& p, const Unit& un, int r0, const f32x4 (&acc0)[NS][NT],
-                                        const f32x4 (&acc1)[NS][NT]) {
+                                        const f32x4 (&acc1)[NS][NT], const EpiPre& pre) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = r0 + 16 * nt + j;
-    const float s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
-    const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
+    const float s0 = __shfl(pre.s0, 16 * nt + j, 64);
+    const float s1 = (MODE == kModeGateUp) ? __shfl(pre.s1, 16 * nt + j, 64) : 0.f;
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int pi = m * 16 + 4 * g + t;
-        if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][nt][t], acc1[m][nt][t], s0, s1);
+        const int orow = (MODE == kModeSingle) ? __shfl(pre.orow, pi & 63, 64) : -1;
+        if (pi < un.len) epilogue_store<MODE>(p, un, r, pi, acc0[m][nt][t], acc1[m][nt][t], s0, s1, orow);
       }
     }
   }
@@ -548,6 +571,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
   const uint16_t* w0 = p.dense0 + slot * mat;
   const uint16_t* w1 = (MODE == kModeGateUp) ? p.dense1 + slot * mat : w0;
   const int rb0 = r0 / 16;
+  const EpiPre pre = epilogue_prefetch<MODE, NT>(p, un, r0);
 
   uint32_t aoff[NS];
   act_rows<NS>(p, un, j, 16, g, aoff);
@@ -581,7 +605,7 @@ __device__ void task_dense(const ExpertParams& p, const Unit& un, int r0) {
       }
     }
   }
-  grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1);
+  grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1, pre);
 }
 
 // Grouped arm: NS row blocks of 16 pairs x NT row blocks of 16 outputs share one decode of
@@ -601,6 +625,7 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
   const int tc = DEC::kPipelined ? code_chunk(lane) : g;
   const uint32_t roff = code_blk_row(r0 + (DEC::kPipelined ? code_row(lane) : j), row_bytes);
   const uint32_t nt_stride = 16u * (uint32_t)row_bytes;
+  const EpiPre pre = epilogue_prefetch<MODE, NT>(p, un, r0);
 
   uint32_t aoff[NS];  // A operand row i = lane%16 of each 16-pair block
   if (FRAG) {
@@ -780,7 +805,7 @@ __device__ void task_grouped(const ExpertParams& p, const DEC& lut, const Unit& 
     if (s < kblocks) step(Later{}, s, B0, B1, aB, pB0, pB1, A0, A1, aA, pA0, pA1);
   }
 
-  grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1);
+  grouped_epilogue<MODE, NS, NT>(p, un, r0, acc0, acc1, pre);
 }
 
 // GEMV arm: NQ pairs x NT row blocks of 16 outputs share one decode; VALU bf16 dot products.
@@ -1011,7 +1036,8 @@ __device__ inline void gemv_epilogue(const ExpertParams& p, const Unit& un, int 
         a1 += __shfl_xor(a1, 16, 64);
         a1 += __shfl_xor(a1, 32, 64);
       }
-      if (q < un.len && (q & 3) == g) epilogue_store<MODE>(p, un, r, q, a0, a1, s0, s1);
+      if (q < un.len && (q & 3) == g)
+        epilogue_store<MODE>(p, un, r, q, a0, a1, s0, s1, MODE == kModeSingle ? out_row(p, un.start + q) : -1);
     }
   }
 }
