@@ -475,25 +475,25 @@ __device__ inline RunSet<NT> load_runs_blk(const uint8_t* __restrict__ base, uin
 __device__ inline int block_at(int i, int kblocks) { return i == 0 ? kblocks - 1 : i - 1; }
 
 // Grouped and dequantize arms: scale and store one task's 16-pair x 16-row MFMA tiles.
-// What a task's epilogue reads from memory, requested when the task starts so that the loads
-// are not a round trip of their own after the last block: lane i holds the scale(s) of the
-// task's row r0 + i (i < 16 NT <= 64) and, in the single-matrix pass, the output row of the
-// unit's pair i (i < len <= 64); the epilogue moves them across lanes.
+// What the single-matrix pass's epilogue reads from memory, requested when the task starts so
+// that the loads are not a round trip of their own after the last block (there the output row
+// is a dependent lookup through the binned order): lane i holds the scale of the task's row
+// r0 + i (i < 16 NT <= 64) and the output row of the unit's pair i (i < len <= 64); the epilogue
+// moves them across lanes.  The fused pass loads its two scales in the epilogue (prefetching
+// them measured no gain there and costs registers its kernels do not have).
 struct EpiPre {
-  float s0, s1;
+  float s0;
   int orow;
 };
 
 template <int MODE, int NT>
 __device__ inline EpiPre epilogue_prefetch(const ExpertParams& p, const Unit& un, int r0) {
   const int lane = threadIdx.x & 63;
-  EpiPre e{0.f, 0.f, -1};
-  if (lane < 16 * NT) {
-    const size_t o = (size_t)un.e * p.rows + r0 + lane;
-    e.s0 = f16_to_f32(p.scale0[o]);
-    if (MODE == kModeGateUp) e.s1 = f16_to_f32(p.scale1[o]);
+  EpiPre e{0.f, -1};
+  if constexpr (MODE == kModeSingle) {
+    if (lane < 16 * NT) e.s0 = f16_to_f32(p.scale0[(size_t)un.e * p.rows + r0 + lane]);
+    if (lane < un.len) e.orow = out_row(p, un.start + lane);
   }
-  if (MODE == kModeSingle && lane < un.len) e.orow = out_row(p, un.start + lane);
   return e;
 }
 
@@ -506,8 +506,9 @@ __device__ inline void grouped_epilogue(const ExpertParams& p, const Unit& un, i
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = r0 + 16 * nt + j;
-    const float s0 = __shfl(pre.s0, 16 * nt + j, 64);
-    const float s1 = (MODE == kModeGateUp) ? __shfl(pre.s1, 16 * nt + j, 64) : 0.f;
+    const float s0 = (MODE == kModeSingle) ? __shfl(pre.s0, 16 * nt + j, 64)
+                                           : f16_to_f32(p.scale0[(size_t)un.e * p.rows + r]);
+    const float s1 = (MODE == kModeGateUp) ? f16_to_f32(p.scale1[(size_t)un.e * p.rows + r]) : 0.f;
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
 #pragma unroll
