@@ -74,3 +74,28 @@ def test_every_token_matches_the_oracle(name, out_dtype, v4_inputs, oracle_out):
         ok, stats = parity.check_bf16(got, numerics.f64_to_bf16_bits(ref))
     say(f"  {stats}")
     assert ok, stats
+
+
+@pytest.mark.timeout(1500)
+@pytest.mark.parametrize("name", ["v4_decode_n32", "v4_mid_n128"])
+def test_gemv_arm_every_token_matches_the_oracle(name, v4_inputs, oracle_out):
+    """The same layers forced onto the GEMV arm: its default configurations there are 12-wave
+    workgroups of 16-row tasks with up to three pairs per decode (n=32) and 8-wave workgroups of
+    32-row tasks (n=128)."""
+    layers, dw = v4_inputs
+    inp = layers[name]
+    n = inp.shape.n_tokens
+    say(f"V4 full parity on the GEMV arm {name} n={n}")
+    layer = Layer(inp, arm=q.QTIP_ARM_GEMV, weights=dw)
+    sched = q.qtip_moe_plan_schedule(layer.plan, n)
+    got = layer.forward(inp)
+    st = q.qtip_moe_stats(layer.plan)
+    layer.close()
+    assert st["last_arm"] == sched["arm"] == q.QTIP_ARM_GEMV
+    assert sched["gate_up"]["variant"] == {"v4_decode_n32": 11, "v4_mid_n128": 4}[name]
+    counts = st["gemv_variant_launches"]
+    want = {sched["gate_up"]["variant"], sched["down"]["variant"]}
+    assert sum(counts) == 2 and all(counts[v] >= 1 for v in want), (counts, sched)
+    ok, stats = parity.check_f32(got, oracle_out[name])
+    say(f"  {stats}")
+    assert ok, stats
