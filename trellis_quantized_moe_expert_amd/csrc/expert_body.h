@@ -1247,8 +1247,8 @@ struct ExpertCfg {
   // per decode, would spill).
   static constexpr bool kAPre = WAVES <= 8 || (NT <= 2 && NSUB <= 2);
   // GEMV arm: look-ahead dwords loaded two blocks ahead (gemv_range) where the registers allow it:
-  // the fused pass at 8 waves and 16 rows, the single-matrix pass up to 12 waves and 8 row-pair
-  // products per lane (larger tasks spill).
+  // the fused pass at up to 12 waves and 16 rows, the single-matrix pass up to 12 waves and 8
+  // row-pair products per lane (larger tasks spill).
   static constexpr bool kDeepGemvGateUp = WAVES <= 12 && NT == 1;
   static constexpr bool kDeepGemvDown = NT == 1 || (WAVES <= 12 && NT * GPAIRS <= 8);
   // The fused grouped task of 64 rows x three 16-pair blocks would spill heavily at 12 waves;
@@ -1505,95 +1505,93 @@ __global__ __launch_bounds__(kDequantWaves * 64, 1) void dequant_kernel(DequantP
     const int r0 = rb * 16;
     if (e < 0) continue;  // counts changed under the launch: not reached
     const size_t slot = by_slot ? (size_t)s : (q.counts ? (size_t)dense_slot(q.counts, e) : (size_t)e);
-    {
-      const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
-      uint16_t* out = (m ? q.out1 : q.out0) + slot * (size_t)q.out_expert_stride;
-      // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
-      const int tc = Dec::kPipelined ? code_chunk(lane) : g;
-      const uint32_t roff = code_blk_row(r0 + (Dec::kPipelined ? code_row(lane) : j), row_bytes);
-      if constexpr (!Dec::kPipelined) {
-        auto rows = [&](auto frag) {
-          constexpr bool FRAG = decltype(frag)::value;
-          auto store_block = [&](const RunCodes& c, int kb) {
-            u32x4 w[4];
-            dec.decode16(c.d0, c.d1, w[0], w[1]);
-            dec.decode16(c.d1, c.la, w[2], w[3]);
-            if constexpr (FRAG) {
+    const uint8_t* base = (m ? q.codes1 : q.codes0) + (size_t)e * mat_bytes;
+    uint16_t* out = (m ? q.out1 : q.out0) + slot * (size_t)q.out_expert_stride;
+    // this lane's code chunk and row: transposed for a pipelined decoder, the MFMA layout otherwise
+    const int tc = Dec::kPipelined ? code_chunk(lane) : g;
+    const uint32_t roff = code_blk_row(r0 + (Dec::kPipelined ? code_row(lane) : j), row_bytes);
+    if constexpr (!Dec::kPipelined) {
+      auto rows = [&](auto frag) {
+        constexpr bool FRAG = decltype(frag)::value;
+        auto store_block = [&](const RunCodes& c, int kb) {
+          u32x4 w[4];
+          dec.decode16(c.d0, c.d1, w[0], w[1]);
+          dec.decode16(c.d1, c.la, w[2], w[3]);
+          if constexpr (FRAG) {
 #pragma unroll
-              for (int st = 0; st < 4; ++st)
-                __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)));
-            } else {
-              uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
+            for (int st = 0; st < 4; ++st)
+              __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)));
+          } else {
+            uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
 #pragma unroll
-              for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
-            }
-          };
-          constexpr int B = kDqBatch;
-          if (kblocks % (4 * B) != 0) {
-            RunCodes nx = load_run_blk(base, roff, kblocks - 1, tc, kblocks);
-            for (int i = 0; i < kblocks; ++i) {
-              const RunCodes rc = nx;
-              if (i + 1 < kblocks) nx = load_run_blk(base, roff, i, tc, kblocks);
-              store_block(rc, block_at(i, kblocks));
-            }
-            return;
-          }
-          // One counter covers loads and stores, so a wait for codes also waits for every store
-          // issued before their load.  Batches of B blocks in two register sets: the next
-          // batch's codes are requested before this batch's stores, so a store is waited for a
-          // batch later, not on the next block.  Four batches per iteration: at the loop head
-          // the compiler's wait covers the previous batch's stores too.  (The last batch's loads
-          // re-read the row's first blocks, unused.)
-          auto load_batch = [&](RunCodes (&c)[B], int i0) {
-#pragma unroll
-            for (int b = 0; b < B; ++b)
-              c[b] = load_run_blk(base, roff, block_at(i0 + b < kblocks ? i0 + b : 0, kblocks), tc, kblocks);
-          };
-          RunCodes cA[B], cB[B];
-          load_batch(cA, 0);
-          for (int i = 0; i < kblocks; i += 4 * B) {
-#pragma unroll
-            for (int h = 0; h < 4; h += 2) {
-              load_batch(cB, i + (h + 1) * B);
-#pragma unroll
-              for (int b = 0; b < B; ++b) store_block(cA[b], block_at(i + h * B + b, kblocks));
-              load_batch(cA, i + (h + 2) * B);
-#pragma unroll
-              for (int b = 0; b < B; ++b) store_block(cB[b], block_at(i + (h + 1) * B + b, kblocks));
-            }
+            for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
           }
         };
-        if (q.fragment_order) rows(std::true_type{});
-        else rows(std::false_type{});
-        continue;
-      }
-      RunCodes cA = load_run_blk(base, roff, kblocks - 1, tc, kblocks), cB{};
-      keep_apart(cA);
-      auto step = [&](int i, const RunCodes& rc, RunCodes& nx) {
-        const int kb = block_at(i, kblocks);
-        if (i + 1 < kblocks) nx = load_run_blk(base, roff, i, tc, kblocks);
-        const RunCodes mc = to_mfma_layout(rc);
-        u32x4 w[4];
-        dec.decode16(mc.d0, mc.d1, w[0], w[1]);
-        dec.decode16(mc.d1, mc.la, w[2], w[3]);
-        if (q.fragment_order) {
-#pragma unroll
-          for (int st = 0; st < 4; ++st)
-            __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)));
-        } else {
-          uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
-#pragma unroll
-          for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+        constexpr int B = kDqBatch;
+        if (kblocks % (4 * B) != 0) {
+          RunCodes nx = load_run_blk(base, roff, kblocks - 1, tc, kblocks);
+          for (int i = 0; i < kblocks; ++i) {
+            const RunCodes rc = nx;
+            if (i + 1 < kblocks) nx = load_run_blk(base, roff, i, tc, kblocks);
+            store_block(rc, block_at(i, kblocks));
+          }
+          return;
         }
-        __builtin_amdgcn_sched_barrier(0);  // as in task_grouped
+        // One counter covers loads and stores, so a wait for codes also waits for every store
+        // issued before their load.  Batches of B blocks in two register sets: the next
+        // batch's codes are requested before this batch's stores, so a store is waited for a
+        // batch later, not on the next block.  Four batches per iteration: at the loop head
+        // the compiler's wait covers the previous batch's stores too.  (The last batch's loads
+        // re-read the row's first blocks, unused.)
+        auto load_batch = [&](RunCodes (&c)[B], int i0) {
+#pragma unroll
+          for (int b = 0; b < B; ++b)
+            c[b] = load_run_blk(base, roff, block_at(i0 + b < kblocks ? i0 + b : 0, kblocks), tc, kblocks);
+        };
+        RunCodes cA[B], cB[B];
+        load_batch(cA, 0);
+        for (int i = 0; i < kblocks; i += 4 * B) {
+#pragma unroll
+          for (int h = 0; h < 4; h += 2) {
+            load_batch(cB, i + (h + 1) * B);
+#pragma unroll
+            for (int b = 0; b < B; ++b) store_block(cA[b], block_at(i + h * B + b, kblocks));
+            load_batch(cA, i + (h + 2) * B);
+#pragma unroll
+            for (int b = 0; b < B; ++b) store_block(cB[b], block_at(i + (h + 1) * B + b, kblocks));
+          }
+        }
       };
-      int i = 0;
-      for (; i + 1 < kblocks; i += 2) {
-        step(i, cA, cB);
-        step(i + 1, cB, cA);
-      }
-      if (i < kblocks) step(i, cA, cB);
+      if (q.fragment_order) rows(std::true_type{});
+      else rows(std::false_type{});
+      continue;
     }
+    RunCodes cA = load_run_blk(base, roff, kblocks - 1, tc, kblocks), cB{};
+    keep_apart(cA);
+    auto step = [&](int i, const RunCodes& rc, RunCodes& nx) {
+      const int kb = block_at(i, kblocks);
+      if (i + 1 < kblocks) nx = load_run_blk(base, roff, i, tc, kblocks);
+      const RunCodes mc = to_mfma_layout(rc);
+      u32x4 w[4];
+      dec.decode16(mc.d0, mc.d1, w[0], w[1]);
+      dec.decode16(mc.d1, mc.la, w[2], w[3]);
+      if (q.fragment_order) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          __builtin_nontemporal_store(w[st], reinterpret_cast<u32x4*>(out + dense_fragment_offset(rb, kb, st, lane, kblocks)));
+      } else {
+        uint16_t* row = out + (size_t)(r0 + j) * q.cols + kb * kKBlock + 32 * g;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) *reinterpret_cast<u32x4*>(row + 8 * st) = w[st];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // as in task_grouped
+    };
+    int i = 0;
+    for (; i + 1 < kblocks; i += 2) {
+      step(i, cA, cB);
+      step(i + 1, cB, cA);
+    }
+    if (i < kblocks) step(i, cA, cB);
   }
 }
 
