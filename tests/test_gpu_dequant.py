@@ -7,6 +7,8 @@ when the automatic dispatch picks the arm inside a dequantize window, and the la
 show the arm that ran.  Shapes span several tiles with ragged tails, a full V4 expert, and the
 V4 decode layer with sampled tokens.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -91,15 +93,16 @@ def test_mid_layer_on_the_dequantize_arm_ragged(n):
 WIDE = moe_inputs.MoEShape(num_experts=150, top_k=4, hidden=256, inter=128, n_tokens=40)
 
 
+@pytest.mark.parametrize("rung", ["bitshift", "lut"])
 @pytest.mark.parametrize("n", [3, 40])
-def test_dequantize_arm_over_a_wide_router(n):
+def test_dequantize_arm_over_a_wide_router(n, rung):
     """150 experts: the woken ones spread over three 64-expert chunks, the last one partly past E.
     The materialise tasks cover the woken experts only (slot s is the s-th woken expert), so a wrong
     slot-to-expert walk would put another expert's weights under a pair."""
-    inp = moe_inputs.make_inputs(WIDE, seed=5, n_tokens=n)
+    inp = moe_inputs.make_inputs(dataclasses.replace(WIDE, rung=rung), seed=5, n_tokens=n)
     ref = moe.moe_forward(inp)
     woken = np.flatnonzero(ref["bins"]["counts"] > 0)
-    say(f"dequantize arm E=150 n={n}: {woken.size} woken, first {woken[0]}, last {woken[-1]}")
+    say(f"dequantize arm E=150 {rung} n={n}: {woken.size} woken, first {woken[0]}, last {woken[-1]}")
     layer = dequant_layer(inp, max_tokens=n)
     got = layer.forward(inp)
     st = q.qtip_moe_stats(layer.plan)
